@@ -1,0 +1,173 @@
+"""CPU oracle of the MoE layer forward (numpy front end over moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package.  The product library never does,
+and this package never imports the product library.
+
+Every function returns float64 results (or exact integers) computed by the
+plain C loops in ``moe_oracle.c``; see that file for which passage of the
+pages each step follows.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c with gcc into libmoe_oracle.so (next to it)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-Wall", "-Werror", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_route.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_moe_cumsum.argtypes = [vp, i64, i32, i32, vp]
+        lib.oracle_align.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp]
+        lib.oracle_indices_to_multihot.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+        lib.oracle_multihot_to_indices.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        lib.oracle_expert_ffn.argtypes = [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                          vp, i64, vp, i32]
+        for f in (lib.oracle_route, lib.oracle_moe_cumsum, lib.oracle_align,
+                  lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
+                  lib.oracle_expert_ffn):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def route(logits: np.ndarray, k: int, norm_topk_prob: bool = True):
+    """Top-k experts per row and their softmax weights -> (w [T,k] f64, ids [T,k] i32)."""
+    x = _c(logits, np.float32)
+    T, E = x.shape
+    w = np.empty((T, k), np.float64)
+    ids = np.empty((T, k), np.int32)
+    _check(_load().oracle_route(_p(x), T, E, k, int(bool(norm_topk_prob)), _p(w), _p(ids)), "route")
+    return w, ids
+
+
+def moe_cumsum(ids: np.ndarray, E: int) -> np.ndarray:
+    """The dense transposed inclusive cumsum of the expert mask, [E*T] int32."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    cs = np.empty(E * T, np.int32)
+    _check(_load().oracle_moe_cumsum(_p(ids), T, k, E, _p(cs)), "moe_cumsum")
+    return cs
+
+
+def align(ids: np.ndarray, E: int) -> dict:
+    """Expert counts, exclusive offsets, sorted token / slot ids and the inverse map."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    n = T * k
+    out = {
+        "counts": np.empty(E, np.int32),
+        "offsets": np.empty(E + 1, np.int32),
+        "sorted_token_ids": np.empty(n, np.int32),
+        "sorted_slot_ids": np.empty(n, np.int32),
+        "slot_to_sorted": np.empty(n, np.int32),
+    }
+    _check(_load().oracle_align(_p(ids), T, k, E, _p(out["counts"]), _p(out["offsets"]),
+                                _p(out["sorted_token_ids"]), _p(out["sorted_slot_ids"]),
+                                _p(out["slot_to_sorted"])), "align")
+    return out
+
+
+def indices_to_multihot(ids: np.ndarray, probs: np.ndarray, E: int):
+    """-> (multihot [T,E] u8, probs_in_multihot [T,E] f32, position_map [T,E] i32)."""
+    ids = _c(ids, np.int32)
+    probs = _c(probs, np.float32)
+    T, k = ids.shape
+    mh = np.empty((T, E), np.uint8)
+    pim = np.empty((T, E), np.float32)
+    pos = np.empty((T, E), np.int32)
+    _check(_load().oracle_indices_to_multihot(_p(ids), _p(probs), T, k, E, _p(mh), _p(pim),
+                                              _p(pos)), "indices_to_multihot")
+    return mh, pim, pos
+
+
+def multihot_to_indices(probs_in_multihot: np.ndarray, position_map: np.ndarray, k: int):
+    """-> (probs_indices [T,k] f32, ids [T,k] i32)."""
+    pim = _c(probs_in_multihot, np.float32)
+    pos = _c(position_map, np.int32)
+    T, E = pim.shape
+    probs = np.empty((T, k), np.float32)
+    ids = np.empty((T, k), np.int32)
+    _check(_load().oracle_multihot_to_indices(_p(pim), _p(pos), T, E, k, _p(probs), _p(ids)),
+           "multihot_to_indices")
+    return probs, ids
+
+
+def expert_ffn(hidden: np.ndarray, w13: np.ndarray, w2: np.ndarray, topk_w: np.ndarray,
+               topk_ids: np.ndarray, dtype: str, tokens=None, threads: int | None = None):
+    """Expert FFN + weighted combine in float64 -> out [len(tokens) or T, H].
+
+    dtype "f32": hidden / weights are float32 arrays; "bf16": uint16 bit patterns.
+    """
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    npdt = np.float32 if dt == 0 else np.uint16
+    hidden = _c(hidden, npdt)
+    w13 = _c(w13, npdt)
+    w2 = _c(w2, npdt)
+    T, H = hidden.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (E, H, I)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_w, np.float64)
+    k = ids.shape[1]
+    if tokens is None:
+        tok = None
+        ntok = T
+    else:
+        tok = _c(tokens, np.int64)
+        ntok = len(tok)
+    out = np.empty((ntok, H), np.float64)
+    nthr = threads if threads else (os.cpu_count() or 1)
+    _check(_load().oracle_expert_ffn(dt, _p(hidden), _p(w13), _p(w2), _p(w), _p(ids), T, H, I,
+                                     E, k, _p(tok) if tok is not None else None, ntok, _p(out),
+                                     nthr), "expert_ffn")
+    return out
+
+
+def layer(inp: dict, k: int, norm_topk_prob: bool, dtype: str, tokens=None,
+          threads: int | None = None) -> dict:
+    """Route + align + FFN/combine on one workload's inputs (float64 results)."""
+    w, ids = route(inp["logits"], k, norm_topk_prob)
+    out = {"topk_w": w, "topk_ids": ids}
+    if "hidden" in inp:
+        out["out"] = expert_ffn(inp["hidden"], inp["w13"], inp["w2"], w, ids, dtype,
+                                tokens=tokens, threads=threads)
+    return out

@@ -1,0 +1,337 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * Every floating-point step runs in double precision from inputs converted
+ * exactly (float32, or bfloat16 bit patterns).  Loops follow the pages' own
+ * formulations, not the GPU's: top-k by in-order insertion, alignment through
+ * the dense transposed cumulative sum, converters by init-then-scatter, and
+ * the expert FFN one token and one selected expert at a time.
+ *
+ * Sources (the three pages this method is described on):
+ *   [mlc]  mlc-llm, python/mlc_llm/op/moe_misc.py ("Mixture of Experts
+ *          operators"): gating_topk, _gating_topk_process_value,
+ *          gating_softmax_topk, moe_cumsum, get_indices, get_indptr,
+ *          scatter_output, moe_sum.
+ *   [mgt]  Megatron-LM, megatron/core/fusions/fused_indices_converter.py:
+ *          _indices_to_multihot_kernel, _multihot_to_indices_kernel,
+ *          IndicesToMultihot.forward / backward.
+ *   [p6]   project_6, ex_engine/csrc/moe_expert_gemm.cpp:
+ *          moe_decode_experts, moe_prefill_experts.
+ *
+ * Readings where the pages are silent or garbled are listed in the design
+ * notes; the ones that shape code here are restated at each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+int oracle_version(void) { return 1; }
+
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Element h of a float32 (dt=0) or bfloat16-bits (dt=1) array, as double. */
+static double load_elem(int dt, const void *base, int64_t i)
+{
+    if (dt == 0)
+        return (double)((const float *)base)[i];
+    return bf16_bits_to_double(((const uint16_t *)base)[i]);
+}
+
+/*
+ * Gating top-k with softmax weights.
+ *
+ * [mlc] gating_topk / _gating_topk_process_value: scan the experts of a row
+ * in ascending order and insert each score into a descending k-list at the
+ * first place where it is strictly greater than the held value, shifting the
+ * rest down.  Equal scores therefore keep the lower expert index first.  The
+ * pages' initialisation of the list is garbled; read here as "empty slots
+ * lose to every value", which makes the selection a total order (value
+ * descending, then index ascending) and needs k <= E.
+ *
+ * [mlc] gating_softmax_topk: with norm_topk_prob the weights are the softmax
+ * of the k selected logits (max-subtracted, summed in slot order).  Without
+ * it they are the full softmax over the E logits, taken at the selected
+ * experts.  Selection always runs on the logits: softmax is strictly
+ * increasing, so this picks the same experts as selecting on probabilities
+ * in exact arithmetic.
+ */
+int oracle_route(const float *logits, int64_t T, int32_t E, int32_t k,
+                 int32_t norm_topk_prob, double *topk_w, int32_t *topk_ids)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return ORACLE_EINVAL;
+    double *val = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    if (!val || !idx) {
+        free(val);
+        free(idx);
+        return ORACLE_ENOMEM;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *x = logits + t * E;
+        int filled = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            double v = (double)x[e];
+            for (int i = 0; i < k; ++i) {
+                if (i == filled || v > val[i]) {
+                    int last = filled < k ? filled : k - 1;
+                    for (int j = last; j > i; --j) {
+                        val[j] = val[j - 1];
+                        idx[j] = idx[j - 1];
+                    }
+                    val[i] = v;
+                    idx[i] = e;
+                    if (filled < k)
+                        ++filled;
+                    break;
+                }
+            }
+        }
+        double m, s = 0.0;
+        if (norm_topk_prob) {
+            m = val[0];
+            for (int i = 1; i < k; ++i)
+                m = fmax(m, val[i]);
+            for (int i = 0; i < k; ++i)
+                s += exp(val[i] - m);
+        } else {
+            m = (double)x[0];
+            for (int32_t e = 1; e < E; ++e)
+                m = fmax(m, (double)x[e]);
+            for (int32_t e = 0; e < E; ++e)
+                s += exp((double)x[e] - m);
+        }
+        for (int i = 0; i < k; ++i) {
+            topk_w[t * k + i] = exp(val[i] - m) / s;
+            topk_ids[t * k + i] = idx[i];
+        }
+    }
+    free(val);
+    free(idx);
+    return ORACLE_OK;
+}
+
+/*
+ * [mlc] moe_cumsum: expert_mask[t][e] = 1 when any of row t's k ids equals e;
+ * transpose to [E, T], flatten, inclusive int32 prefix sum.  An id outside
+ * [0, E) matches no column, so it is dropped.  cs must hold E*T entries.
+ */
+int oracle_moe_cumsum(const int32_t *ids, int64_t T, int32_t k, int32_t E, int32_t *cs)
+{
+    if (T < 0 || E < 1 || k < 1)
+        return ORACLE_EINVAL;
+    int64_t run = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        for (int64_t t = 0; t < T; ++t) {
+            int hit = 0;
+            for (int32_t j = 0; j < k; ++j)
+                hit |= ids[t * k + j] == e;
+            run += hit;
+            cs[(int64_t)e * T + t] = (int32_t)run;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Expert alignment from the cumulative sum.
+ *
+ * [mlc] get_indptr, exclusive form (the code, not the swapped docstring):
+ *   offsets[0] = 0, offsets[i] = cs[i*T - 1] for i in 1..E.
+ * [mlc] get_indices: for slot (t, j) with expert e, position
+ *   p = cs[e*T + t] - 1; reverse_indices[p] = t*k + j, token_indices[p] = t.
+ * The inverse map slot_to_sorted[t*k+j] = p is the same scatter read the
+ * other way; slots with an id outside [0, E) get -1 there, and entries of
+ * the sorted arrays past offsets[E] stay -1.
+ */
+int oracle_align(const int32_t *ids, int64_t T, int32_t k, int32_t E,
+                 int32_t *counts, int32_t *offsets, int32_t *sorted_token_ids,
+                 int32_t *sorted_slot_ids, int32_t *slot_to_sorted)
+{
+    if (T < 0 || E < 1 || k < 1)
+        return ORACLE_EINVAL;
+    int64_t n = T * k;
+    for (int64_t i = 0; i < n; ++i) {
+        sorted_token_ids[i] = -1;
+        sorted_slot_ids[i] = -1;
+        slot_to_sorted[i] = -1;
+    }
+    offsets[0] = 0;
+    if (T == 0) {
+        for (int32_t e = 0; e < E; ++e) {
+            offsets[e + 1] = 0;
+            counts[e] = 0;
+        }
+        return ORACLE_OK;
+    }
+    int32_t *cs = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E * T));
+    if (!cs)
+        return ORACLE_ENOMEM;
+    oracle_moe_cumsum(ids, T, k, E, cs);
+    for (int32_t i = 1; i <= E; ++i)
+        offsets[i] = cs[(int64_t)i * T - 1];
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = offsets[e + 1] - offsets[e];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = ids[t * k + j];
+            if (e < 0 || e >= E)
+                continue;
+            int32_t p = cs[(int64_t)e * T + t] - 1;
+            sorted_slot_ids[p] = (int32_t)(t * k + j);
+            sorted_token_ids[p] = (int32_t)t;
+            slot_to_sorted[t * k + j] = p;
+        }
+    }
+    free(cs);
+    return ORACLE_OK;
+}
+
+/*
+ * [mgt] _indices_to_multihot_kernel: per row, first initialise
+ * multihot = 0, probs_in_multihot = 0, position_map = -1 over all E columns,
+ * then for each slot j whose id is valid (not -1, below E; read here as
+ * 0 <= id < E) set multihot[id] = 1, probs_in_multihot[id] = probs[j] (bits
+ * copied) and position_map[id] = j.
+ */
+int oracle_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T, int32_t k,
+                               int32_t E, uint8_t *multihot, float *probs_in_multihot,
+                               int32_t *position_map)
+{
+    if (T < 0 || E < 1 || k < 1)
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            multihot[t * E + e] = 0;
+            probs_in_multihot[t * E + e] = 0.0f;
+            position_map[t * E + e] = -1;
+        }
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t id = ids[t * k + j];
+            if (id < 0 || id >= E)
+                continue;
+            multihot[t * E + id] = 1;
+            probs_in_multihot[t * E + id] = probs[t * k + j];
+            position_map[t * E + id] = j;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * [mgt] _multihot_to_indices_kernel: per row, initialise probs_indices = 0
+ * over the k slots, then for every expert e with position_map[e] != -1 write
+ * probs_indices[position_map[e]] = probs_in_multihot[e].  The id each slot
+ * came from is recovered the same way (ids_out[pos] = e, else -1).  Positions
+ * outside [0, k) are ignored.  With two experts naming one slot (not produced
+ * by the forward conversion) the later expert wins, as in this loop.
+ */
+int oracle_multihot_to_indices(const float *probs_in_multihot, const int32_t *position_map,
+                               int64_t T, int32_t E, int32_t k, float *probs_indices,
+                               int32_t *ids_out)
+{
+    if (T < 0 || E < 1 || k < 1)
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            probs_indices[t * k + j] = 0.0f;
+            if (ids_out)
+                ids_out[t * k + j] = -1;
+        }
+        for (int32_t e = 0; e < E; ++e) {
+            int32_t p = position_map[t * E + e];
+            if (p < 0 || p >= k)
+                continue;
+            probs_indices[t * k + p] = probs_in_multihot[t * E + e];
+            if (ids_out)
+                ids_out[t * k + p] = e;
+        }
+    }
+    return ORACLE_OK;
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * Expert FFN and weighted combine for a list of tokens.
+ *
+ * [p6] moe_decode_experts / moe_prefill_experts: for each selected expert of
+ * a token, gate_up = x . w13[e]^T (weights are [out, in]), act =
+ * silu(gate) * up with rows [0, I) of w13 read as the gate and rows [I, 2I)
+ * as the up projection, y = act . w2[e]^T, and out += weight * y.
+ * [mlc] moe_sum: the k expert outputs of a token are summed; here in slot
+ * order j = 0..k-1.  Slots with an id outside [0, E) contribute nothing.
+ *
+ * dt: 0 = float32 inputs, 1 = bfloat16 bit patterns.  tokens[0..ntok) lists
+ * which rows to evaluate (NULL = all T rows in order); out is [ntok, H]
+ * double.  Nothing is rounded on the way.
+ */
+int oracle_expert_ffn(int32_t dt, const void *hidden, const void *w13, const void *w2,
+                      const double *topk_w, const int32_t *topk_ids, int64_t T, int32_t H,
+                      int32_t I, int32_t E, int32_t k, const int64_t *tokens, int64_t ntok,
+                      double *out, int32_t nthreads)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || (dt != 0 && dt != 1))
+        return ORACLE_EINVAL;
+    if (!tokens)
+        ntok = T;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < ntok; ++r) {
+        int64_t t = tokens ? tokens[r] : r;
+        double *x = (double *)malloc(sizeof(double) * (size_t)H);
+        double *act = (double *)malloc(sizeof(double) * (size_t)I);
+        if (!x || !act || t < 0 || t >= T) {
+            free(x);
+            free(act);
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            x[h] = load_elem(dt, hidden, t * H + h);
+            out[r * H + h] = 0.0;
+        }
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = topk_ids[t * k + j];
+            if (e < 0 || e >= E)
+                continue;
+            double w = topk_w[t * k + j];
+            int64_t base13 = (int64_t)e * 2 * I * H;
+            for (int32_t i = 0; i < I; ++i) {
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    g += x[h] * load_elem(dt, w13, base13 + (int64_t)i * H + h);
+                    u += x[h] * load_elem(dt, w13, base13 + (int64_t)(I + i) * H + h);
+                }
+                act[i] = silu(g) * u;
+            }
+            int64_t base2 = (int64_t)e * H * I;
+            for (int32_t h = 0; h < H; ++h) {
+                double y = 0.0;
+                for (int32_t i = 0; i < I; ++i)
+                    y += act[i] * load_elem(dt, w2, base2 + (int64_t)h * I + i);
+                out[r * H + h] += w * y;
+            }
+        }
+        free(x);
+        free(act);
+    }
+    return fail ? ORACLE_EINVAL : ORACLE_OK;
+}

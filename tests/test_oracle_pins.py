@@ -1,0 +1,364 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every expected value is either
+printed on a page (fixtures under tests/golden/, each citing its passage), a
+closed form, a textbook / library routine on a special case, an invariant, or
+a brute force that computes the same quantity a different way.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moe_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Route (top-k + softmax weights)
+# --------------------------------------------------------------------------
+
+def _sort_topk(x, k):
+    """Full stable sort: value descending, ties by ascending index."""
+    E = x.shape[1]
+    out = np.empty((x.shape[0], k), np.int32)
+    for t in range(x.shape[0]):
+        order = np.lexsort((np.arange(E), -x[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (50, 64, 8), (17, 5, 5), (9, 1, 1), (33, 130, 7)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_ids_match_full_sort(T, E, k, ties):
+    g = np.random.Generator(np.random.PCG64(T * 131 + E + k))
+    x = g.standard_normal((T, E)).astype(np.float32)
+    if ties:  # few distinct values -> many equal pairs per row
+        x = np.round(x * 2).astype(np.float32)
+    for norm in (True, False):
+        _, ids = oracle.route(x, k, norm)
+        np.testing.assert_array_equal(ids, _sort_topk(x, k))
+
+
+def test_route_crafted_rows():
+    _, ids = oracle.route(np.zeros((1, 6), np.float32), 3)
+    assert ids.tolist() == [[0, 1, 2]]  # all equal -> lowest indices, ascending
+    _, ids = oracle.route(np.array([[1, 3, 3, 2]], np.float32), 2)
+    assert ids.tolist() == [[1, 2]]  # tie at the top: lower index first
+    _, ids = oracle.route(np.array([[-5, -1, -3, -1e30]], np.float32), 4)
+    assert ids.tolist() == [[1, 2, 0, 3]]
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (16, 16), (7, 1)])
+def test_route_norm_weights(E, k):
+    g = np.random.Generator(np.random.PCG64(E * 7 + k))
+    x = (g.standard_normal((40, E)) * 3).astype(np.float32)
+    w, ids = oracle.route(x, k, True)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0)  # descending with the logits
+    sel = np.take_along_axis(x.astype(np.float64), ids, 1)
+    ref = scipy.special.softmax(sel, axis=1)  # library softmax over the k picked
+    np.testing.assert_allclose(w, ref, rtol=1e-13, atol=0)
+    if k == 1:
+        assert np.all(w == 1.0)
+    if k == E:  # renormalised top-E == full softmax, reordered
+        full = scipy.special.softmax(x.astype(np.float64), axis=1)
+        np.testing.assert_allclose(w, np.take_along_axis(full, ids, 1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (5, 5)])
+def test_route_full_softmax_weights(E, k):
+    g = np.random.Generator(np.random.PCG64(100 + E))
+    x = (g.standard_normal((40, E)) * 2).astype(np.float32)
+    w, ids = oracle.route(x, k, False)
+    full = scipy.special.softmax(x.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(full, ids, 1), rtol=1e-13)
+    if k == E:
+        assert np.all(np.abs(w.sum(1) - 1) < 1e-12)
+
+
+def test_route_shift_invariance():
+    # Adding a constant to a row changes neither selection nor weights.
+    g = np.random.Generator(np.random.PCG64(5))
+    x = g.standard_normal((30, 16)).astype(np.float32)
+    w0, i0 = oracle.route(x, 4, True)
+    w1, i1 = oracle.route((x + np.float32(0.5)).astype(np.float32), 4, True)
+    np.testing.assert_array_equal(i0, i1)
+    np.testing.assert_allclose(w0, w1, rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Alignment (cumsum, indptr, indices)
+# --------------------------------------------------------------------------
+
+def test_cumsum_worked_example():
+    ex = _golden("mlc_moe_cumsum_example.json")
+    ids = np.array(ex["expert_indices"], np.int32)
+    cs = oracle.moe_cumsum(ids, ex["E"])
+    assert cs.reshape(ex["E"], ex["T"]).tolist() == ex["cumsum_E_by_T"]
+
+
+def test_align_worked_example():
+    ex = _golden("mlc_moe_cumsum_example.json")
+    ids = np.array(ex["expert_indices"], np.int32)
+    T, k, E = ex["T"], ex["k"], ex["E"]
+    cs = np.array(ex["cumsum_E_by_T"], np.int64).reshape(-1)
+    a = oracle.align(ids, E)
+    # get_indptr's documented numpy equivalent, applied to the printed cumsum
+    indptr = [0] + [int(cs[i * T - 1]) for i in range(1, E + 1)]
+    assert a["offsets"].tolist() == indptr == [0, 1, 3, 5, 6, 7, 8]
+    assert a["counts"].tolist() == [1, 2, 2, 1, 1, 1]
+    # get_indices' scatter rule, applied to the printed cumsum
+    rev = [None] * (T * k)
+    tok = [None] * (T * k)
+    for b in range(T):
+        for j in range(k):
+            p = int(cs[ids[b, j] * T + b]) - 1
+            rev[p] = b * k + j
+            tok[p] = b
+    assert a["sorted_slot_ids"].tolist() == rev == [0, 1, 2, 3, 6, 4, 5, 7]
+    assert a["sorted_token_ids"].tolist() == tok == [0, 0, 1, 1, 3, 2, 2, 3]
+
+
+def _check_align_against_stable_sort(ids, E, a):
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    valid = np.nonzero((flat >= 0) & (flat < E))[0]
+    order = valid[np.argsort(flat[valid], kind="stable")]  # library stable sort
+    nv = len(valid)
+    np.testing.assert_array_equal(a["counts"], np.bincount(flat[valid], minlength=E))
+    assert a["offsets"][0] == 0 and a["offsets"][-1] == nv
+    np.testing.assert_array_equal(np.diff(a["offsets"]), a["counts"])
+    np.testing.assert_array_equal(a["sorted_slot_ids"][:nv], order)
+    np.testing.assert_array_equal(a["sorted_token_ids"][:nv], order // k)
+    assert np.all(a["sorted_slot_ids"][nv:] == -1) and np.all(a["sorted_token_ids"][nv:] == -1)
+    s2s = np.full(T * k, -1, np.int64)
+    s2s[order] = np.arange(nv)
+    np.testing.assert_array_equal(a["slot_to_sorted"], s2s)
+    for e in range(E):  # ascending tokens inside every segment
+        seg = a["sorted_token_ids"][a["offsets"][e]:a["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+@pytest.mark.parametrize("T,E,k,inv", [(1000, 64, 8, 0.0), (333, 8, 2, 0.0), (257, 13, 3, 0.1),
+                                       (1, 4, 4, 0.0), (50, 1, 1, 0.0), (64, 200, 6, 0.2)])
+def test_align_matches_stable_sort(T, E, k, inv):
+    ids = mi.random_ids(T * 10 + E, T, E, k, invalid_frac=inv)
+    a = oracle.align(ids, E)
+    _check_align_against_stable_sort(ids, E, a)
+    if inv == 0:
+        assert a["offsets"][-1] == T * k
+        for t in range(T):  # every token appears exactly k times
+            assert np.count_nonzero(a["sorted_token_ids"] == t) == k
+
+
+def test_align_skewed_with_zero_counts():
+    ids = np.tile(np.array([[3, 0, 5]], np.int32), (20, 1))
+    a = oracle.align(ids, 8)
+    assert a["counts"].tolist() == [20, 0, 0, 20, 0, 20, 0, 0]
+    _check_align_against_stable_sort(ids, 8, a)
+
+
+def test_align_empty():
+    a = oracle.align(np.zeros((0, 4), np.int32), 6)
+    assert a["offsets"].tolist() == [0] * 7 and a["counts"].tolist() == [0] * 6
+
+
+def test_align_routing_workload_invariants():
+    w = mi.WORKLOADS["routing"]
+    _, ids = oracle.route(mi.gating_logits(w), w.k, True)
+    a = oracle.align(ids, w.E)
+    assert a["offsets"][-1] == w.T * w.k
+    _check_align_against_stable_sort(ids, w.E, a)
+
+
+# --------------------------------------------------------------------------
+# Multihot conversion and its inverse
+# --------------------------------------------------------------------------
+
+def test_multihot_worked_example():
+    ex = _golden("megatron_indices_to_multihot_example.json")
+    ids = np.array(ex["indices"], np.int32)
+    probs = np.array(ex["probs_in_indices"], np.float32)
+    mh, pim, pos = oracle.indices_to_multihot(ids, probs, ex["E"])
+    assert mh.tolist() == ex["multihot"]
+    np.testing.assert_array_equal(pim, np.array(ex["probs_in_multihot"], np.float32))
+    printed = np.array(ex["multihot_indices_printed"])
+    assert np.array_equal(mh == 1, printed == 1)
+    assert pos.tolist() == [[0, 1, -1, -1], [-1, 0, 1, -1]]
+
+
+def test_inverse_worked_example():
+    ex = _golden("megatron_multihot_to_indices_example.json")
+    pim = np.array(ex["probs_in_multihot"], np.float32)
+    pos = np.array(ex["position_map"], np.int32)
+    probs, ids = oracle.multihot_to_indices(pim, pos, ex["k"])
+    np.testing.assert_array_equal(probs, np.array(ex["probs_indices"], np.float32))
+    assert ids.tolist() == [[0, 1], [1, 2]]
+    assert np.array_equal(np.array(ex["position_map_printed"]) != -1, pos != -1)
+
+
+@pytest.mark.parametrize("T,E,k,inv", [(300, 64, 8, 0.0), (100, 6, 2, 0.25), (20, 300, 9, 0.1)])
+def test_multihot_roundtrip_and_dense(T, E, k, inv):
+    ids = mi.random_ids(T + E, T, E, k, invalid_frac=inv)
+    probs = mi.random_probs(T + k, T, k)
+    mh, pim, pos = oracle.indices_to_multihot(ids, probs, E)
+    valid = (ids >= 0) & (ids < E)
+    # dense brute force: column e of row t is set iff e is a valid id of the row
+    for t in range(T):
+        for e in range(E):
+            js = [j for j in range(k) if ids[t, j] == e]
+            assert mh[t, e] == (1 if js else 0)
+            assert pos[t, e] == (js[0] if js else -1)
+            assert pim[t, e] == (probs[t, js[0]] if js else 0.0)
+    back, ids_back = oracle.multihot_to_indices(pim, pos, k)
+    np.testing.assert_array_equal(back, np.where(valid, probs, 0).astype(np.float32))
+    np.testing.assert_array_equal(ids_back, np.where(valid, ids, -1))
+
+
+# --------------------------------------------------------------------------
+# Expert FFN + weighted combine
+# --------------------------------------------------------------------------
+
+def _dense_bruteforce(x, w13, w2, gate):
+    """Every expert on every token, combined through a dense [T,E] gate (0 off top-k)."""
+    E, I2, H = w13.shape
+    I = I2 // 2
+    gu = np.einsum("th,eih->tei", x, w13)  # [T,E,2I]
+    act = gu[..., :I] / (1 + np.exp(-gu[..., :I])) * gu[..., I:]
+    y = np.einsum("tei,ehi->teh", act, w2)
+    return np.einsum("te,teh->th", gate, y)
+
+
+def _tiny(seed, T, H, I, E, k, norm=True):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal((T, H)).astype(np.float32)
+    w13 = (g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32)
+    w2 = (g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32)
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    w, ids = oracle.route(logits, k, norm)
+    return x, w13, w2, w, ids
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(4, 64, 128, 8, 2), (9, 16, 24, 5, 3), (3, 8, 8, 4, 4)])
+def test_ffn_matches_dense_bruteforce(T, H, I, E, k):
+    x, w13, w2, w, ids = _tiny(T + H + I, T, H, I, E, k)
+    out = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    gate = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            gate[t, ids[t, j]] = w[t, j]
+    ref = _dense_bruteforce(x.astype(np.float64), w13.astype(np.float64), w2.astype(np.float64), gate)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_ffn_single_expert_is_swiglu_mlp():
+    x, w13, w2, w, ids = _tiny(11, 6, 32, 48, 1, 1)
+    assert np.all(w == 1.0) and np.all(ids == 0)
+    out = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    xt = torch.from_numpy(x.astype(np.float64))
+    gu = torch.nn.functional.linear(xt, torch.from_numpy(w13[0].astype(np.float64)))
+    a = torch.nn.functional.silu(gu[:, :48]) * gu[:, 48:]
+    ref = torch.nn.functional.linear(a, torch.from_numpy(w2[0].astype(np.float64))).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_ffn_shared_weights_reduce_to_one_mlp():
+    # All experts equal + renormalised weights (sum 1) -> out = FFN(x).
+    x, w13, w2, w, ids = _tiny(12, 5, 16, 32, 6, 3)
+    w13[:] = w13[0]
+    w2[:] = w2[0]
+    out = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    single = oracle.expert_ffn(x, w13[:1], w2[:1], np.ones((5, 1)), np.zeros((5, 1), np.int32), "f32")
+    np.testing.assert_allclose(out, single, rtol=1e-11, atol=1e-12)
+
+
+def test_ffn_unselected_experts_are_not_read():
+    x, w13, w2, w, ids = _tiny(13, 4, 16, 16, 8, 2)
+    used = set(ids.reshape(-1).tolist())
+    ref = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    for e in range(8):
+        if e not in used:
+            w13[e] = np.nan
+            w2[e] = np.nan
+    out = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    np.testing.assert_array_equal(out, ref)
+    # invalid ids contribute nothing
+    ids2 = ids.copy()
+    ids2[:, 1] = -1
+    out2 = oracle.expert_ffn(x, w13, w2, w, ids2, "f32")
+    ids3 = ids.copy()[:, :1]
+    out3 = oracle.expert_ffn(x, w13, w2, w[:, :1], ids3, "f32")
+    np.testing.assert_array_equal(out2, out3)
+
+
+def test_ffn_duplicate_rows_and_token_subset():
+    x, w13, w2, w, ids = _tiny(14, 6, 16, 16, 4, 2)
+    x[3] = x[1]
+    ids[3] = ids[1]
+    w[3] = w[1]
+    out = oracle.expert_ffn(x, w13, w2, w, ids, "f32")
+    np.testing.assert_array_equal(out[3], out[1])
+    sub = oracle.expert_ffn(x, w13, w2, w, ids, "f32", tokens=[5, 0, 3])
+    np.testing.assert_array_equal(sub, out[[5, 0, 3]])
+
+
+def test_ffn_bf16_inputs_decode_exactly():
+    x, w13, w2, w, ids = _tiny(15, 3, 32, 64, 4, 2)
+    xb, w13b, w2b = (mi.f32_to_bf16_bits(a) for a in (x, w13, w2))
+    out = oracle.expert_ffn(xb, w13b, w2b, w, ids, "bf16")
+    ref = oracle.expert_ffn(mi.bf16_bits_to_f32(xb), mi.bf16_bits_to_f32(w13b),
+                            mi.bf16_bits_to_f32(w2b), w, ids, "f32")
+    np.testing.assert_array_equal(out, ref)
+    gate = np.zeros((3, 4))
+    for t in range(3):
+        for j in range(2):
+            gate[t, ids[t, j]] = w[t, j]
+    dense = _dense_bruteforce(mi.bf16_bits_to_f32(xb).astype(np.float64),
+                              mi.bf16_bits_to_f32(w13b).astype(np.float64),
+                              mi.bf16_bits_to_f32(w2b).astype(np.float64), gate)
+    np.testing.assert_allclose(out, dense, rtol=1e-11, atol=1e-12)
+
+
+def test_tiny_workload_layer():
+    w = mi.WORKLOADS["tiny"]
+    inp = mi.layer_inputs(w)
+    res = oracle.layer(inp, w.k, w.norm, w.dtype)
+    assert res["out"].shape == (w.T, w.H)
+    for t in range(w.T):  # "ties rejected" rows
+        assert len(np.unique(inp["logits"][t])) == w.E
+    rms = math.sqrt(float(np.mean(res["out"] ** 2)))
+    assert 0.05 < rms < 5
+
+
+# --------------------------------------------------------------------------
+# Input generator
+# --------------------------------------------------------------------------
+
+def test_inputs_deterministic_and_thread_independent():
+    a = mi.normal_bf16(9, 2, 3 * mi.CHUNK + 5, 0.1, threads=1)
+    b = mi.normal_bf16(9, 2, 3 * mi.CHUNK + 5, 0.1, threads=8)
+    np.testing.assert_array_equal(a, b)
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3], np.float32)
+    # RNE: 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> 1+2^-6
+    assert mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(x)).tolist()[:4] == [1.0, 1.0, 1.015625, -2.5]
+
+
+def test_finegrained_bias_gives_zero_count_experts():
+    w = mi.WORKLOADS["finegrained"]
+    _, ids = oracle.route(mi.gating_logits(w), w.k, True)
+    counts = np.bincount(ids.reshape(-1), minlength=w.E)
+    assert np.count_nonzero(counts == 0) >= 2
+    assert counts.max() > 4 * counts.mean()
