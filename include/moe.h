@@ -1,0 +1,228 @@
+/*
+ * moe.h -- C ABI of libmoe, the Mixture-of-Experts layer forward on AMD
+ * Instinct MI355X (CDNA4, gfx950).
+ *
+ * The layer forward is split the way the method is stated:
+ *
+ *   moe_route                 gating softmax + top-k (optionally renormalised)
+ *   moe_align                 per-expert histogram, exclusive offsets, stable
+ *                             expert-major order of the (token, slot) pairs
+ *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
+ *   moe_multihot_to_indices   the inverse conversion
+ *   moe_expert_ffn            grouped w13 GEMM + SiLU-and-mul, grouped w2 GEMM,
+ *                             weighted combine (prefill, any T)
+ *   moe_expert_ffn_decode     the same for T <= MOE_DECODE_MAX_T, streaming only
+ *                             the selected experts' weights
+ *
+ * plus the three phases of moe_expert_ffn as separate calls, so a caller can
+ * place its own events between them.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers to row-major, contiguous memory
+ *   owned by the caller.  The library never allocates or frees device memory,
+ *   never synchronises the host and never reads device memory from the host.
+ *   Scratch memory is passed in as a workspace whose size comes from the
+ *   matching *_workspace_size query.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is
+ *   enqueued on it asynchronously; results are ready when the stream reaches
+ *   that point.  Calls that share a workspace on different streams race.
+ * - Shapes: T tokens, E experts, k experts per token, H hidden size,
+ *   I expert intermediate size.  Ids are int32.  Expert weights are stored
+ *   [out, in]: w13 is [E, 2I, H] (rows [0,I) = gate, rows [I,2I) = up) and w2
+ *   is [E, H, I]; a linear layer computes y = x . W^T.
+ * - An expert id is valid iff 0 <= id < E.  Invalid ids (e.g. -1 for a
+ *   dropped slot) are skipped by every call that consumes ids.
+ * - Errors are reported by return value only.  Argument checks (null
+ *   pointers, sizes, alignment, workspace size) happen on the host BEFORE any
+ *   launch; on error nothing is enqueued and outputs are untouched.  Device
+ *   preconditions (finite logits, distinct valid ids within a row, offsets
+ *   produced by moe_align for the same ids) are documented, not checked.
+ *   moe_last_error() returns a message for the last failing call on the
+ *   calling thread.
+ * - T = 0 is a valid no-op for every call.
+ *
+ * Method sources (cited per call below):
+ *   [mlc] mlc-llm, python/mlc_llm/op/moe_misc.py ("Mixture of Experts operators")
+ *   [mgt] Megatron-LM, megatron/core/fusions/fused_indices_converter.py
+ *   [p6]  project_6, ex_engine/csrc/moe_expert_gemm.cpp
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+#define MOE_DECODE_MAX_T 64
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, k > E, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle */
+    MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or too small */
+    MOE_ERR_HIP = 4          /* a HIP launch failed; see moe_last_error() */
+} moe_status_t;
+
+typedef enum {
+    MOE_F32 = 0, /* float32 hidden / weights / activations / output */
+    MOE_BF16 = 1 /* bfloat16 hidden / weights / activations / output, fp32 accumulation */
+} moe_dtype_t;
+
+/* Library version (MOE_VERSION). */
+int moe_version(void);
+/* Static text for a status code. */
+const char *moe_status_string(moe_status_t s);
+/* Detail of the last failing call on this thread ("" if none).  Thread-local,
+ * valid until the next failing call on the same thread. */
+const char *moe_last_error(void);
+
+/*
+ * moe_route -- gating top-k with softmax weights.
+ * [mlc] gating_topk, _gating_topk_process_value, gating_softmax_topk.
+ *
+ * logits    [T, E] float32, finite.
+ * topk_w    [T, k] float32 out: the weights of the selected experts.
+ * topk_ids  [T, k] int32 out: selected expert ids, per row in descending
+ *           logit order; equal logits keep the lower expert id first.
+ * norm_topk_prob != 0: weights = softmax over the k selected logits (they sum
+ *           to 1).  == 0: weights = full softmax over all E logits, taken at
+ *           the selected ids.  Selection is on the logits in both modes.
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS.
+ */
+moe_status_t moe_route(const float *logits, int64_t T, int32_t E, int32_t k,
+                       int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids, void *stream);
+
+/*
+ * moe_align -- expert alignment of the T*k (token, slot) pairs.
+ * [mlc] moe_cumsum, get_indices, get_indptr (exclusive form).
+ *
+ * topk_ids         [T, k] int32 in.  Valid ids within a row must be distinct.
+ * expert_counts    [E]    int32 out: number of valid slots routed to each expert.
+ * expert_offsets   [E+1]  int32 out: exclusive prefix sum of the counts;
+ *                  offsets[0] = 0, offsets[E] = number of valid slots.
+ * sorted_token_ids [T*k]  int32 out: token of each position p, expert-major,
+ *                  ascending token inside each expert's segment
+ *                  [offsets[e], offsets[e+1]).
+ * sorted_slot_ids  [T*k]  int32 out: flat slot t*k + j of each position p.
+ * slot_to_sorted   [T*k]  int32 out: position p of each flat slot (inverse of
+ *                  sorted_slot_ids), -1 for slots with an invalid id.
+ * Entries of sorted_token_ids / sorted_slot_ids at p >= offsets[E] are -1.
+ * workspace        >= moe_align_workspace_size(T, k, E) bytes of device memory,
+ *                  any content; clobbered.
+ * The result is identical bit for bit on every run (no order-dependent atomics).
+ */
+size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E);
+moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                       int32_t *expert_counts, int32_t *expert_offsets,
+                       int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                       int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * moe_indices_to_multihot -- [T,k] routing to [T,E] multihot form.
+ * [mgt] _indices_to_multihot_kernel, IndicesToMultihot.forward.
+ *
+ * ids               [T, k] int32 in; probs [T, k] float32 in.
+ * multihot          [T, E] uint8 out: 1 where expert e is a valid id of row t, else 0.
+ * probs_in_multihot [T, E] float32 out: probs[t, j] (bit copy) at e = ids[t, j], else 0.
+ * position_map      [T, E] int32 out: slot j at e = ids[t, j], else -1.
+ */
+moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,
+                                     int32_t k, int32_t E, uint8_t *multihot,
+                                     float *probs_in_multihot, int32_t *position_map,
+                                     void *stream);
+
+/*
+ * moe_multihot_to_indices -- inverse of moe_indices_to_multihot.
+ * [mgt] _multihot_to_indices_kernel, IndicesToMultihot.backward.
+ *
+ * probs_in_multihot [T, E] float32 in; position_map [T, E] int32 in (-1 = none).
+ * probs_indices     [T, k] float32 out: probs_in_multihot[t, e] at slot
+ *                   position_map[t, e], 0 for slots no expert names.
+ * ids_out           [T, k] int32 out, may be NULL: the expert e that named the
+ *                   slot, -1 if none.
+ * Positions outside [0, k) are ignored.  If two experts of a row name the same
+ * slot (never produced by the forward conversion), the higher expert id wins.
+ */
+moe_status_t moe_multihot_to_indices(const float *probs_in_multihot,
+                                     const int32_t *position_map, int64_t T, int32_t E,
+                                     int32_t k, float *probs_indices, int32_t *ids_out,
+                                     void *stream);
+
+/*
+ * moe_expert_ffn -- expert FFN over the aligned slots and weighted combine.
+ * [p6] moe_prefill_experts (per-expert FC1, SiLU-and-mul, FC2, weighted
+ * index_add), [mlc] scatter_output + moe_sum (un-permute and k-sum).
+ *
+ * For every valid slot (t, j) with expert e = topk_ids[t, j]:
+ *   gu  = hidden[t] . w13[e]^T                         (2I values)
+ *   act = silu(gu[0:I]) * gu[I:2I]                     (stored in `dt`)
+ *   y   = act . w2[e]^T                                (H values, float32)
+ * and out[t] = sum over j = 0..k-1 of topk_w[t, j] * y(t, j), accumulated in
+ * float32 in slot order and rounded once to `dt`.  A token with no valid slot
+ * gets 0.  Accumulation is float32 throughout; for MOE_BF16 the only
+ * roundings are act (the second GEMM's input) and out, once each.  The result
+ * is deterministic.
+ *
+ * hidden [T, H], w13 [E, 2I, H], w2 [E, H, I], out [T, H] in `dt`;
+ * topk_w [T, k] float32; expert_offsets [E+1], sorted_token_ids [T*k] and
+ * slot_to_sorted [T*k] as written by moe_align for the same ids.
+ * workspace >= moe_expert_ffn_workspace_size(dt, T, H, I, E, k) bytes.
+ * Requires H % 64 == 0, I % 64 == 0; device pointers 16-byte aligned.
+ */
+size_t moe_expert_ffn_workspace_size(moe_dtype_t dt, int64_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t k);
+moe_status_t moe_expert_ffn(moe_dtype_t dt, const void *hidden, const void *w13,
+                            const void *w2, const float *topk_w,
+                            const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                            const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t I,
+                            int32_t E, int32_t k, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * moe_expert_ffn_decode -- moe_expert_ffn for T <= MOE_DECODE_MAX_T.
+ * [p6] moe_decode_experts.  Same arguments and result.  Each distinct
+ * selected expert's w13 / w2 slice is read from memory once and applied to
+ * every token routed to it; unselected experts are never read.
+ */
+moe_status_t moe_expert_ffn_decode(moe_dtype_t dt, const void *hidden, const void *w13,
+                                   const void *w2, const float *topk_w,
+                                   const int32_t *expert_offsets,
+                                   const int32_t *sorted_token_ids,
+                                   const int32_t *slot_to_sorted, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k, void *out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The three phases of moe_expert_ffn (same kernels, same arguments).
+ *
+ * moe_ffn_gate_up: act [T*k, I] in `dt`, row p = position p of the aligned
+ *   order: act[p] = silu(gate) * up for token sorted_token_ids[p] and the
+ *   expert whose segment holds p.  Rows p >= offsets[E] are not written.
+ * moe_ffn_down:   y [T*k, H] float32: y[p] = act[p] . w2[e]^T, same rows.
+ * moe_combine:    out [T, H] in `dt` from y (float32), topk_w and slot_to_sorted.
+ * `decode` != 0 selects the decode kernels (T <= MOE_DECODE_MAX_T).
+ */
+moe_status_t moe_ffn_gate_up(moe_dtype_t dt, int32_t decode, const void *hidden,
+                             const void *w13, const int32_t *expert_offsets,
+                             const int32_t *sorted_token_ids, int64_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k, void *act, void *stream);
+moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const void *w2,
+                          const int32_t *expert_offsets, int64_t T, int32_t H, int32_t I,
+                          int32_t E, int32_t k, float *y, void *stream);
+moe_status_t moe_combine(moe_dtype_t dt, const float *y, const float *topk_w,
+                         const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t k,
+                         void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H */

@@ -1,0 +1,20 @@
+"""libmoe: the Mixture-of-Experts layer forward on AMD MI355X (gfx950).
+
+The compute lives in libmoe.so (hand-written HIP kernels behind the C ABI of
+include/moe.h); this package only binds it to torch tensors.
+"""
+
+from ._lib import MOE_BF16, MOE_F32, MoeError, lib  # noqa: F401
+from .moe import (  # noqa: F401
+    moe_align,
+    moe_align_workspace_size,
+    moe_combine,
+    moe_expert_ffn,
+    moe_expert_ffn_workspace_size,
+    moe_ffn_down,
+    moe_ffn_gate_up,
+    moe_indices_to_multihot,
+    moe_layer,
+    moe_multihot_to_indices,
+    moe_route,
+)

@@ -1,0 +1,301 @@
+// C ABI of libmoe: host-side argument checks and kernel dispatch.
+//
+// Every entry point validates its arguments before enqueuing anything, then
+// launches on the caller's stream and returns without synchronising.  Nothing
+// here allocates device memory or reads it back.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+#define CHECK(cond, status, ...)                      \
+    do {                                              \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+moe_status_t check_routing_dims(int64_t T, int32_t E, int32_t k, const char *fn) {
+    CHECK(T >= 0, MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+    CHECK(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_INVALID_ARG,
+          "%s: E = %d outside [1, %d]", fn, E, MOE_MAX_EXPERTS);
+    CHECK(k >= 1 && k <= MOE_MAX_TOPK, MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, %d]", fn, k,
+          MOE_MAX_TOPK);
+    CHECK(T * (int64_t)k < (int64_t)1 << 31, MOE_ERR_INVALID_ARG,
+          "%s: T*k = %lld does not fit int32", fn, (long long)(T * k));
+    return MOE_OK;
+}
+
+// act [T*k, I] in the layer dtype, then y [T*k, H] float32.
+size_t ffn_act_bytes(moe_dtype_t dt, int64_t T, int32_t I, int32_t k) {
+    const size_t es = dt == MOE_BF16 ? 2 : 4;
+    return round_up((size_t)T * (size_t)k * (size_t)I * es, 256);
+}
+size_t ffn_scratch_bytes(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t k) {
+    return ffn_act_bytes(dt, T, I, k) + round_up((size_t)T * (size_t)k * (size_t)H * 4, 256);
+}
+
+moe_status_t check_ffn_dims(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t E,
+                            int32_t k, const char *fn) {
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn,
+          (int)dt);
+    CHECK(H >= 1 && I >= 1, MOE_ERR_INVALID_ARG, "%s: H = %d, I = %d must be >= 1", fn, H, I);
+    CHECK(H % 64 == 0 && I % 64 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: H = %d and I = %d must be multiples of 64", fn, H, I);
+    CHECK((int64_t)E * 2 * I * (int64_t)H < (int64_t)1 << 62, MOE_ERR_INVALID_ARG,
+          "%s: weights too large", fn);
+    if (dt == MOE_F32)
+        CHECK(T * k <= 2147483647LL, MOE_ERR_UNSUPPORTED, "%s: float32 path needs T*k < 2^31",
+              fn);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_VERSION; }
+
+const char *moe_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+moe_status_t moe_route(const float *logits, int64_t T, int32_t E, int32_t k,
+                       int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids, void *stream) {
+    moe_status_t st = check_routing_dims(T, E, k, "moe_route");
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "moe_route: k = %d > E = %d", k, E);
+    if (T == 0) return MOE_OK;
+    CHECK(logits && topk_w && topk_ids, MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+    return hip_status(moe::launch_route(logits, T, E, k, norm_topk_prob != 0, topk_w, topk_ids,
+                                        static_cast<hipStream_t>(stream)),
+                      "moe_route");
+}
+
+size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    const int nb = moe::align_num_blocks(T * k, E);
+    return round_up((size_t)nb * (size_t)E * sizeof(int32_t), 256);
+}
+
+moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                       int32_t *expert_counts, int32_t *expert_offsets,
+                       int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                       int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    moe_status_t st = check_routing_dims(T, E, k, "moe_align");
+    if (st != MOE_OK) return st;
+    CHECK(expert_counts && expert_offsets, MOE_ERR_INVALID_ARG, "moe_align: null pointer");
+    CHECK(T == 0 || (topk_ids && sorted_token_ids && sorted_slot_ids && slot_to_sorted),
+          MOE_ERR_INVALID_ARG, "moe_align: null pointer");
+    const size_t need = moe_align_workspace_size(T, k, E);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "moe_align: workspace %zu bytes, need %zu", workspace_bytes, need);
+    return hip_status(moe::launch_align(topk_ids, T, k, E, expert_counts, expert_offsets,
+                                        sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                                        static_cast<int32_t *>(workspace),
+                                        static_cast<hipStream_t>(stream)),
+                      "moe_align");
+}
+
+moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,
+                                     int32_t k, int32_t E, uint8_t *multihot,
+                                     float *probs_in_multihot, int32_t *position_map,
+                                     void *stream) {
+    moe_status_t st = check_routing_dims(T, E, k, "moe_indices_to_multihot");
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    CHECK(ids && probs && multihot && probs_in_multihot && position_map, MOE_ERR_INVALID_ARG,
+          "moe_indices_to_multihot: null pointer");
+    return hip_status(moe::launch_to_multihot(ids, probs, T, k, E, multihot, probs_in_multihot,
+                                              position_map, static_cast<hipStream_t>(stream)),
+                      "moe_indices_to_multihot");
+}
+
+moe_status_t moe_multihot_to_indices(const float *probs_in_multihot,
+                                     const int32_t *position_map, int64_t T, int32_t E,
+                                     int32_t k, float *probs_indices, int32_t *ids_out,
+                                     void *stream) {
+    moe_status_t st = check_routing_dims(T, E, k, "moe_multihot_to_indices");
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    CHECK(probs_in_multihot && position_map && probs_indices, MOE_ERR_INVALID_ARG,
+          "moe_multihot_to_indices: null pointer");
+    return hip_status(moe::launch_to_indices(probs_in_multihot, position_map, T, E, k,
+                                             probs_indices, ids_out,
+                                             static_cast<hipStream_t>(stream)),
+                      "moe_multihot_to_indices");
+}
+
+size_t moe_expert_ffn_workspace_size(moe_dtype_t dt, int64_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t k) {
+    (void)E;
+    if (T < 0 || H < 1 || I < 1 || k < 1) return 0;
+    return ffn_scratch_bytes(dt, T, H, I, k);
+}
+
+moe_status_t moe_ffn_gate_up(moe_dtype_t dt, int32_t decode, const void *hidden,
+                             const void *w13, const int32_t *expert_offsets,
+                             const int32_t *sorted_token_ids, int64_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k, void *act, void *stream) {
+    const char *fn = "moe_ffn_gate_up";
+    moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    CHECK(hidden && w13 && expert_offsets && sorted_token_ids && act, MOE_ERR_INVALID_ARG,
+          "%s: null pointer", fn);
+    CHECK(aligned16(hidden) && aligned16(w13) && aligned16(act), MOE_ERR_INVALID_ARG,
+          "%s: hidden, w13 and act must be 16-byte aligned", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == MOE_F32) {
+        e = moe::launch_gate_up_f32(static_cast<const float *>(hidden),
+                                    static_cast<const float *>(w13), expert_offsets,
+                                    sorted_token_ids, T, H, I, E, k, static_cast<float *>(act), s);
+    } else if (decode) {
+        CHECK(T <= MOE_DECODE_MAX_T, MOE_ERR_UNSUPPORTED, "%s: decode needs T <= %d", fn,
+              MOE_DECODE_MAX_T);
+        e = moe::launch_decode_gate_up_bf16(static_cast<const uint16_t *>(hidden),
+                                            static_cast<const uint16_t *>(w13), expert_offsets,
+                                            sorted_token_ids, T, H, I, E, k,
+                                            static_cast<uint16_t *>(act), s);
+    } else {
+        e = moe::launch_gate_up_bf16(static_cast<const uint16_t *>(hidden),
+                                     static_cast<const uint16_t *>(w13), expert_offsets,
+                                     sorted_token_ids, T, H, I, E, k,
+                                     static_cast<uint16_t *>(act), s);
+    }
+    return hip_status(e, fn);
+}
+
+moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const void *w2,
+                          const int32_t *expert_offsets, int64_t T, int32_t H, int32_t I,
+                          int32_t E, int32_t k, float *y, void *stream) {
+    const char *fn = "moe_ffn_down";
+    moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    CHECK(act && w2 && expert_offsets && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(aligned16(act) && aligned16(w2) && aligned16(y), MOE_ERR_INVALID_ARG,
+          "%s: act, w2 and y must be 16-byte aligned", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == MOE_F32) {
+        e = moe::launch_down_f32(static_cast<const float *>(act), static_cast<const float *>(w2),
+                                 expert_offsets, T, H, I, E, k, y, s);
+    } else if (decode) {
+        CHECK(T <= MOE_DECODE_MAX_T, MOE_ERR_UNSUPPORTED, "%s: decode needs T <= %d", fn,
+              MOE_DECODE_MAX_T);
+        e = moe::launch_decode_down_bf16(static_cast<const uint16_t *>(act),
+                                         static_cast<const uint16_t *>(w2), expert_offsets, T, H,
+                                         I, E, k, y, s);
+    } else {
+        e = moe::launch_down_bf16(static_cast<const uint16_t *>(act),
+                                  static_cast<const uint16_t *>(w2), expert_offsets, T, H, I, E,
+                                  k, y, s);
+    }
+    return hip_status(e, fn);
+}
+
+moe_status_t moe_combine(moe_dtype_t dt, const float *y, const float *topk_w,
+                         const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t k,
+                         void *out, void *stream) {
+    const char *fn = "moe_combine";
+    CHECK(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && H >= 1, MOE_ERR_INVALID_ARG,
+          "%s: bad sizes T = %lld, H = %d, k = %d", fn, (long long)T, H, k);
+    CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    CHECK(H % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: H = %d must be a multiple of 64", fn, H);
+    if (T == 0) return MOE_OK;
+    CHECK(y && topk_w && slot_to_sorted && out, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(aligned16(y) && aligned16(out), MOE_ERR_INVALID_ARG,
+          "%s: y and out must be 16-byte aligned", fn);
+    return hip_status(moe::launch_combine(dt, y, topk_w, slot_to_sorted, T, H, k, out,
+                                          static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+static moe_status_t expert_ffn_impl(int32_t decode, moe_dtype_t dt, const void *hidden,
+                                    const void *w13, const void *w2, const float *topk_w,
+                                    const int32_t *expert_offsets,
+                                    const int32_t *sorted_token_ids,
+                                    const int32_t *slot_to_sorted, int64_t T, int32_t H,
+                                    int32_t I, int32_t E, int32_t k, void *out, void *workspace,
+                                    size_t workspace_bytes, void *stream, const char *fn) {
+    moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    if (decode)
+        CHECK(T <= MOE_DECODE_MAX_T, MOE_ERR_UNSUPPORTED, "%s: T = %lld > %d", fn, (long long)T,
+              MOE_DECODE_MAX_T);
+    if (T == 0) return MOE_OK;
+    CHECK(hidden && w13 && w2 && topk_w && expert_offsets && sorted_token_ids &&
+              slot_to_sorted && out,
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    const size_t need = ffn_scratch_bytes(dt, T, H, I, k);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
+          fn);
+    char *act = static_cast<char *>(workspace);
+    float *y = reinterpret_cast<float *>(act + ffn_act_bytes(dt, T, I, k));
+    st = moe_ffn_gate_up(dt, decode, hidden, w13, expert_offsets, sorted_token_ids, T, H, I, E,
+                         k, act, stream);
+    if (st != MOE_OK) return st;
+    st = moe_ffn_down(dt, decode, act, w2, expert_offsets, T, H, I, E, k, y, stream);
+    if (st != MOE_OK) return st;
+    return moe_combine(dt, y, topk_w, slot_to_sorted, T, H, k, out, stream);
+}
+
+moe_status_t moe_expert_ffn(moe_dtype_t dt, const void *hidden, const void *w13,
+                            const void *w2, const float *topk_w,
+                            const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                            const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t I,
+                            int32_t E, int32_t k, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return expert_ffn_impl(0, dt, hidden, w13, w2, topk_w, expert_offsets, sorted_token_ids,
+                           slot_to_sorted, T, H, I, E, k, out, workspace, workspace_bytes, stream,
+                           "moe_expert_ffn");
+}
+
+moe_status_t moe_expert_ffn_decode(moe_dtype_t dt, const void *hidden, const void *w13,
+                                   const void *w2, const float *topk_w,
+                                   const int32_t *expert_offsets,
+                                   const int32_t *sorted_token_ids,
+                                   const int32_t *slot_to_sorted, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k, void *out, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    return expert_ffn_impl(1, dt, hidden, w13, w2, topk_w, expert_offsets, sorted_token_ids,
+                           slot_to_sorted, T, H, I, E, k, out, workspace, workspace_bytes, stream,
+                           "moe_expert_ffn_decode");
+}
+
+}  // extern "C"

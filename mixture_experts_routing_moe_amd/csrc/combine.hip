@@ -1,0 +1,74 @@
+// Weighted combine back to token order.
+//
+// Method: project_6 moe_expert_gemm.cpp, moe_prefill_experts (scale each
+// expert output by its routing weight and add it into the token's row) and
+// mlc-llm moe_misc.py scatter_output + moe_sum (un-permute, then sum the k
+// expert outputs of a token).  Instead of a scatter-add, each token row
+// gathers its k expert rows through the inverse map and sums them in slot
+// order j = 0..k-1 in float32: one rounding at the end, no atomics, the same
+// bits on every run.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+struct Vec;
+constexpr int V = 8;  // columns per thread: 32 bytes of y
+
+__device__ __forceinline__ void store8(uint16_t *p, const float *f) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = to_bf16(f[i]);
+    *reinterpret_cast<bf16x8 *>(p) = v;
+}
+__device__ __forceinline__ void store8(float *p, const float *f) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// y is float32 [rows, H]; out is bf16 (uint16_t) or float32 [T, H].
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const float *__restrict__ y, const float *__restrict__ w, const int32_t *__restrict__ s2s,
+    int64_t ntok, int H, int k, OutT *__restrict__ out) {
+    for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
+        for (int h = threadIdx.x * V; h < H; h += kThreads * V) {
+            float acc[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int p = s2s[t * k + j];
+                if (p < 0) continue;
+                const float wj = w[t * k + j];
+                const float4 *src = reinterpret_cast<const float4 *>(y + (int64_t)p * H + h);
+                const float4 a = src[0], b = src[1];
+                const float v[V] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+            }
+            store8(out + t * H + h, acc);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(moe_dtype_t dt, const float *y, const float *w,
+                          const int32_t *slot_to_sorted, int64_t T, int H, int k, void *out,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(T < 65536 ? T : 65536);
+    if (dt == MOE_BF16) {
+        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, y, w,
+                           slot_to_sorted, T, H, k, static_cast<uint16_t *>(out));
+    } else {
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kThreads), 0, s, y, w,
+                           slot_to_sorted, T, H, k, static_cast<float *>(out));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

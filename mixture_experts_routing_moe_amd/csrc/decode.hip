@@ -1,0 +1,241 @@
+// Decode expert FFN (few tokens): weight-streaming kernels.
+//
+// Method: project_6 moe_expert_gemm.cpp, moe_decode_experts: for each
+// selected expert, gate_up = x . w13[e]^T, act = silu(gate) * up,
+// y = act . w2[e]^T, then a weighted sum over the token's experts.  The page
+// loops over the k experts of one token on the host, reading each id and
+// weight back to the host first.  Here the expert set comes from the aligned
+// offsets on the device: block row d serves the d-th expert with a non-empty
+// segment, so every selected expert's weights are streamed from memory
+// exactly once and applied to all tokens routed to it (up to 64), and
+// unselected experts are never touched.
+//
+// Each block owns 16 weight rows (16 gate + 16 up rows for FC1) of one
+// expert; its 4 waves split k and stream 256 contiguous bytes per row per
+// step into MFMA 16x16x32 bf16 (weights as the A operand, up to 4 chunks of
+// 16 tokens as B).  The 4 partial accumulators are summed through LDS.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 16;   // weight rows per block
+constexpr int kKB = 128;    // k elements per wave step (4 MFMA k-steps)
+
+// The d-th expert (in id order) whose segment is non-empty.
+__device__ bool nth_nonempty_expert(const int32_t *__restrict__ offsets, int E, int d, int &e,
+                                    int &base, int &cnt) {
+    const int lane = lane_id();
+    int seen = 0;
+    for (int c = 0; c < E; c += kWave) {
+        const int ee = c + lane;
+        int off = 0, cn = 0;
+        if (ee < E) {
+            off = offsets[ee];
+            cn = offsets[ee + 1] - off;
+        }
+        const uint64_t nz = __ballot(cn > 0);
+        const int pc = __popcll(nz);
+        if (d < seen + pc) {
+            const int before = __popcll(nz & lanemask_lt());
+            const uint64_t sel = __ballot(cn > 0 && before == d - seen);
+            const int L = __ffsll((unsigned long long)sel) - 1;
+            e = c + L;
+            base = readlane_i(off, L);
+            cnt = readlane_i(cn, L);
+            return true;
+        }
+        seen += pc;
+    }
+    return false;
+}
+
+// FC1 + SiLU-and-mul.  act[p, n] for n in this block's 16 rows and every
+// position p of the expert's segment.
+template <int MC>
+__global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
+    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w13,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_tok, int H, int I,
+    int E, uint16_t *__restrict__ act) {
+    __shared__ f32x4 red[3][2][MC][kWave];
+    int e, base, cnt;
+    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+    const int n0 = blockIdx.x * kRows;
+
+    const uint16_t *wg = w13 + ((int64_t)e * 2 * I + n0 + i) * H + kq * 8;
+    const uint16_t *wu = wg + (int64_t)I * H;
+    const uint16_t *xr[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        // Token columns past the segment read a valid row and are never stored.
+        const int m = min(mc * 16 + i, cnt - 1);
+        xr[mc] = hidden + (int64_t)sorted_tok[base + m] * H + kq * 8;
+    }
+    f32x4 ag[MC], au[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        ag[mc] = f32x4{};
+        au[mc] = f32x4{};
+    }
+    const int nkb = (H + kKB - 1) / kKB;
+    for (int kb = wave; kb < nkb; kb += 4) {
+#pragma unroll
+        for (int s = 0; s < kKB / 32; ++s) {
+            const int k0 = kb * kKB + s * 32;
+            if (k0 >= H) break;
+            const bf16x8 g = *reinterpret_cast<const bf16x8 *>(wg + k0);
+            const bf16x8 u = *reinterpret_cast<const bf16x8 *>(wu + k0);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
+                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g, x, ag[mc], 0, 0, 0);
+                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u, x, au[mc], 0, 0, 0);
+            }
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            red[wave - 1][0][mc][lane] = ag[mc];
+            red[wave - 1][1][mc][lane] = au[mc];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            ag[mc] += red[w][0][mc][lane];
+            au[mc] += red[w][1][mc][lane];
+        }
+    // Accumulator r holds weight row 4 kq + r and token column i.
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        const int m = mc * 16 + i;
+        if (m >= cnt) continue;
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = to_bf16(silu_f(ag[mc][r]) * au[mc][r]);
+        *reinterpret_cast<bf16x4 *>(act + (int64_t)(base + m) * I + n0 + kq * 4) = o;
+    }
+}
+
+// FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p of the
+// expert's segment.
+template <int MC>
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+    const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
+    const int32_t *__restrict__ offsets, int H, int I, int E, float *__restrict__ y) {
+    __shared__ f32x4 red[3][MC][kWave];
+    int e, base, cnt;
+    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+    const int h0 = blockIdx.x * kRows;
+
+    const uint16_t *wr = w2 + ((int64_t)e * H + h0 + i) * I + kq * 8;
+    const uint16_t *ar[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        const int m = min(mc * 16 + i, cnt - 1);
+        ar[mc] = act + (int64_t)(base + m) * I + kq * 8;
+    }
+    f32x4 acc[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{};
+    const int nkb = (I + kKB - 1) / kKB;
+    for (int kb = wave; kb < nkb; kb += 4) {
+#pragma unroll
+        for (int s = 0; s < kKB / 32; ++s) {
+            const int k0 = kb * kKB + s * 32;
+            if (k0 >= I) break;
+            const bf16x8 w = *reinterpret_cast<const bf16x8 *>(wr + k0);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
+                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc[mc], 0, 0, 0);
+            }
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) red[wave - 1][mc][lane] = acc[mc];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) acc[mc] += red[w][mc][lane];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        const int m = mc * 16 + i;
+        if (m >= cnt) continue;
+        *reinterpret_cast<float4 *>(y + (int64_t)(base + m) * H + h0 + kq * 4) =
+            make_float4(acc[mc][0], acc[mc][1], acc[mc][2], acc[mc][3]);
+    }
+}
+
+int token_chunks(int64_t T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+
+unsigned expert_rows(int64_t T, int E, int k) {
+    const int64_t d = T * k < E ? T * k : E;
+    return (unsigned)d;
+}
+
+}  // namespace
+
+hipError_t launch_decode_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
+                                      const int32_t *offsets, const int32_t *sorted_tok,
+                                      int64_t T, int H, int I, int E, int k, uint16_t *act,
+                                      hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid(I / kRows, expert_rows(T, E, k));
+    switch (token_chunks(T)) {
+        case 1:
+            hipLaunchKernelGGL(decode_gate_up_kernel<1>, grid, dim3(kThreads), 0, s, hidden, w13,
+                               offsets, sorted_tok, H, I, E, act);
+            break;
+        case 2:
+            hipLaunchKernelGGL(decode_gate_up_kernel<2>, grid, dim3(kThreads), 0, s, hidden, w13,
+                               offsets, sorted_tok, H, I, E, act);
+            break;
+        default:
+            hipLaunchKernelGGL(decode_gate_up_kernel<4>, grid, dim3(kThreads), 0, s, hidden, w13,
+                               offsets, sorted_tok, H, I, E, act);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
+                                   const int32_t *offsets, int64_t T, int H, int I, int E, int k,
+                                   float *y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid(H / kRows, expert_rows(T, E, k));
+    switch (token_chunks(T)) {
+        case 1:
+            hipLaunchKernelGGL(decode_down_kernel<1>, grid, dim3(kThreads), 0, s, act, w2,
+                               offsets, H, I, E, y);
+            break;
+        case 2:
+            hipLaunchKernelGGL(decode_down_kernel<2>, grid, dim3(kThreads), 0, s, act, w2,
+                               offsets, H, I, E, y);
+            break;
+        default:
+            hipLaunchKernelGGL(decode_down_kernel<4>, grid, dim3(kThreads), 0, s, act, w2,
+                               offsets, H, I, E, y);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

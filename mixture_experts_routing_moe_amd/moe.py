@@ -1,0 +1,213 @@
+"""torch-tensor front end of libmoe (same names as the C ABI in include/moe.h).
+
+Tensors must live on the current HIP device and be contiguous; outputs are
+allocated here with torch when not given.  Work is enqueued on torch's current
+stream and nothing synchronises.  bfloat16 tensors are passed as torch.bfloat16
+(their bits are the library's bf16 values).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, check, lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libmoe works on device tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def moe_route(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, topk_w=None,
+              topk_ids=None):
+    """Top-k experts per row + softmax weights -> (topk_w [T,k] f32, topk_ids [T,k] i32)."""
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be [T, E] float32")
+    T, E = logits.shape
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    _dev(logits, topk_w, topk_ids)
+    check(lib().moe_route(_ptr(logits), T, E, k, int(bool(norm_topk_prob)), _ptr(topk_w),
+                          _ptr(topk_ids), _stream()), "moe_route")
+    return topk_w, topk_ids
+
+
+def moe_align_workspace_size(T: int, k: int, E: int) -> int:
+    return int(lib().moe_align_workspace_size(T, k, E))
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, out: dict | None = None,
+              workspace: torch.Tensor | None = None) -> dict:
+    """Expert counts, offsets, sorted token / slot ids and the inverse map (all int32)."""
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k] int32")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    n = T * k
+    if out is None:
+        out = {
+            "counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_token_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "sorted_slot_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "slot_to_sorted": torch.empty(n, dtype=torch.int32, device=dev),
+        }
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                                device=dev)
+    _dev(topk_ids, workspace, *out.values())
+    check(lib().moe_align(_ptr(topk_ids), T, k, E, _ptr(out["counts"]), _ptr(out["offsets"]),
+                          _ptr(out["sorted_token_ids"]), _ptr(out["sorted_slot_ids"]),
+                          _ptr(out["slot_to_sorted"]), _ptr(workspace), workspace.numel(),
+                          _stream()), "moe_align")
+    return out
+
+
+def moe_indices_to_multihot(ids: torch.Tensor, probs: torch.Tensor, E: int, out=None):
+    """-> (multihot [T,E] u8, probs_in_multihot [T,E] f32, position_map [T,E] i32)."""
+    if ids.dtype != torch.int32 or probs.dtype != torch.float32 or ids.shape != probs.shape:
+        raise ValueError("ids [T,k] int32 and probs [T,k] float32 of the same shape")
+    T, k = ids.shape
+    dev = ids.device
+    if out is None:
+        out = (torch.empty((T, E), dtype=torch.uint8, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.int32, device=dev))
+    mh, pim, pos = out
+    _dev(ids, probs, mh, pim, pos)
+    check(lib().moe_indices_to_multihot(_ptr(ids), _ptr(probs), T, k, E, _ptr(mh), _ptr(pim),
+                                        _ptr(pos), _stream()), "moe_indices_to_multihot")
+    return mh, pim, pos
+
+
+def moe_multihot_to_indices(probs_in_multihot: torch.Tensor, position_map: torch.Tensor, k: int,
+                            with_ids: bool = True, out=None):
+    """-> (probs_indices [T,k] f32, ids [T,k] i32 or None)."""
+    if probs_in_multihot.dtype != torch.float32 or position_map.dtype != torch.int32 or \
+            probs_in_multihot.shape != position_map.shape:
+        raise ValueError("probs_in_multihot [T,E] float32 and position_map [T,E] int32")
+    T, E = probs_in_multihot.shape
+    dev = probs_in_multihot.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev) if with_ids else None)
+    probs, ids = out
+    _dev(probs_in_multihot, position_map, probs, ids)
+    check(lib().moe_multihot_to_indices(_ptr(probs_in_multihot), _ptr(position_map), T, E, k,
+                                        _ptr(probs), _ptr(ids), _stream()),
+          "moe_multihot_to_indices")
+    return probs, ids
+
+
+def moe_expert_ffn_workspace_size(dtype: int, T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_expert_ffn_workspace_size(dtype, T, H, I, E, k))
+
+
+def _ffn_shapes(hidden, w13, w2):
+    if hidden.dim() != 2 or w13.dim() != 3 or w2.dim() != 3:
+        raise ValueError("hidden [T,H], w13 [E,2I,H], w2 [E,H,I]")
+    T, H = hidden.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    if H2 != H or I2 != 2 * I or tuple(w2.shape) != (E, H, I):
+        raise ValueError("inconsistent FFN shapes")
+    if not (hidden.dtype == w13.dtype == w2.dtype):
+        raise ValueError("hidden, w13, w2 must share a dtype")
+    return T, H, I, E
+
+
+def moe_expert_ffn(hidden, w13, w2, topk_w, aligned: dict, decode: bool = False, out=None,
+                   workspace=None):
+    """Grouped FC1 + SiLU-and-mul, FC2, weighted combine -> out [T, H] in hidden's dtype."""
+    T, H, I, E = _ffn_shapes(hidden, w13, w2)
+    k = topk_w.shape[1]
+    dt = _dtype_code(hidden)
+    if out is None:
+        out = torch.empty((T, H), dtype=hidden.dtype, device=hidden.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_expert_ffn_workspace_size(dt, T, H, I, E, k)),
+                                dtype=torch.uint8, device=hidden.device)
+    _dev(hidden, w13, w2, topk_w, out, workspace, aligned["offsets"],
+         aligned["sorted_token_ids"], aligned["slot_to_sorted"])
+    fn = lib().moe_expert_ffn_decode if decode else lib().moe_expert_ffn
+    check(fn(dt, _ptr(hidden), _ptr(w13), _ptr(w2), _ptr(topk_w), _ptr(aligned["offsets"]),
+             _ptr(aligned["sorted_token_ids"]), _ptr(aligned["slot_to_sorted"]), T, H, I, E, k,
+             _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+          "moe_expert_ffn_decode" if decode else "moe_expert_ffn")
+    return out
+
+
+def moe_ffn_gate_up(hidden, w13, aligned: dict, k: int, decode: bool = False, act=None):
+    """act [T*k, I] in the aligned order."""
+    T, H = hidden.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if act is None:
+        act = torch.empty((T * k, I), dtype=hidden.dtype, device=hidden.device)
+    _dev(hidden, w13, act, aligned["offsets"], aligned["sorted_token_ids"])
+    check(lib().moe_ffn_gate_up(_dtype_code(hidden), int(decode), _ptr(hidden), _ptr(w13),
+                                _ptr(aligned["offsets"]), _ptr(aligned["sorted_token_ids"]), T,
+                                H, I, E, k, _ptr(act), _stream()), "moe_ffn_gate_up")
+    return act
+
+
+def moe_ffn_down(act, w2, aligned: dict, T: int, k: int, decode: bool = False, y=None):
+    """y [T*k, H] float32 in the aligned order."""
+    E, H, I = w2.shape
+    if y is None:
+        y = torch.empty((T * k, H), dtype=torch.float32, device=act.device)
+    _dev(act, w2, y, aligned["offsets"])
+    check(lib().moe_ffn_down(_dtype_code(act), int(decode), _ptr(act), _ptr(w2),
+                             _ptr(aligned["offsets"]), T, H, I, E, k, _ptr(y), _stream()),
+          "moe_ffn_down")
+    return y
+
+
+def moe_combine(y, topk_w, slot_to_sorted, out_dtype=torch.bfloat16, out=None):
+    """out [T, H] = sum_j topk_w[t, j] * y[slot_to_sorted[t*k + j]] (y float32)."""
+    if y.dtype != torch.float32:
+        raise ValueError("y must be float32")
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    _dev(y, topk_w, slot_to_sorted, out)
+    check(lib().moe_combine(_dtype_code(out), _ptr(y), _ptr(topk_w), _ptr(slot_to_sorted), T, H,
+                            k, _ptr(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_layer(hidden, w13, w2, logits, k: int, norm_topk_prob: bool = True,
+              decode: bool | None = None):
+    """route -> align -> expert FFN + combine.  Returns (out, topk_w, topk_ids, aligned)."""
+    E = w13.shape[0]
+    topk_w, topk_ids = moe_route(logits, k, norm_topk_prob)
+    aligned = moe_align(topk_ids, E)
+    if decode is None:
+        decode = hidden.dtype == torch.bfloat16 and hidden.shape[0] <= _lib.MOE_DECODE_MAX_T
+    out = moe_expert_ffn(hidden, w13, w2, topk_w, aligned, decode=decode)
+    return out, topk_w, topk_ids, aligned

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: exports, version, status strings, workspace sizes
+and host-side argument checks (every call here fails validation before any
+HIP call, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_routing_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import mixture_experts_routing_moe_amd.build as b
+        b.build()
+    return _lib.lib()
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_align", "moe_indices_to_multihot", "moe_multihot_to_indices",
+              "moe_expert_ffn", "moe_expert_ffn_decode"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_version() == 1
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    assert lib.moe_align_workspace_size(16384, 8, 64) >= 64 * 4
+    assert lib.moe_align_workspace_size(-1, 8, 64) == 0
+    assert lib.moe_align_workspace_size(0, 8, 64) > 0
+    n = lib.moe_expert_ffn_workspace_size(_lib.MOE_BF16, 4096, 4096, 14336, 8, 2)
+    assert n >= 8192 * (14336 + 4096) * 2
+    assert lib.moe_expert_ffn_workspace_size(_lib.MOE_F32, 4, 64, 128, 8, 2) >= 8 * (128 + 64) * 4
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def status(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_route_validation(lib):
+    I = _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, "moe_route", FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == I  # k > E
+    assert b"k = 9 > E = 8" in lib.moe_last_error()
+    assert status(lib, "moe_route", FAKE, 4, 0, 1, 1, FAKE, FAKE, None) == I  # E < 1
+    assert status(lib, "moe_route", FAKE, 4, 2000, 8, 1, FAKE, FAKE, None) == I  # E too big
+    assert status(lib, "moe_route", FAKE, 4, 128, 65, 1, FAKE, FAKE, None) == I  # k > 64
+    assert status(lib, "moe_route", FAKE, -1, 8, 2, 1, FAKE, FAKE, None) == I
+    assert status(lib, "moe_route", None, 4, 8, 2, 1, FAKE, FAKE, None) == I  # null
+    assert status(lib, "moe_route", None, 0, 8, 2, 1, None, None, None) == _lib.MOE_OK  # T=0
+
+
+def test_align_validation(lib):
+    ws = lib.moe_align_workspace_size(100, 2, 8)
+    assert status(lib, "moe_align", FAKE, 100, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1,
+                  None) == _lib.MOE_ERR_WORKSPACE
+    assert status(lib, "moe_align", FAKE, 100, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws,
+                  None) == _lib.MOE_ERR_WORKSPACE
+    assert status(lib, "moe_align", FAKE, 100, 2, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, "moe_align", FAKE, 1 << 30, 4, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                  None) == _lib.MOE_ERR_INVALID_ARG  # T*k overflows int32
+
+
+def test_converter_validation(lib):
+    I = _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, "moe_indices_to_multihot", FAKE, FAKE, 4, 2, 8, None, FAKE, FAKE,
+                  None) == I
+    assert status(lib, "moe_indices_to_multihot", FAKE, FAKE, 4, 0, 8, FAKE, FAKE, FAKE,
+                  None) == I
+    assert status(lib, "moe_multihot_to_indices", FAKE, None, 4, 8, 2, FAKE, None, None) == I
+    assert status(lib, "moe_multihot_to_indices", None, None, 0, 8, 2, None, None,
+                  None) == _lib.MOE_OK
+
+
+def test_ffn_validation(lib):
+    bf = _lib.MOE_BF16
+    ws = lib.moe_expert_ffn_workspace_size(bf, 16, 128, 128, 8, 2)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    # H not a multiple of 64
+    assert status(lib, "moe_expert_ffn", bf, *args, 16, 96, 128, 8, 2, FAKE, FAKE, ws,
+                  None) == _lib.MOE_ERR_UNSUPPORTED
+    # workspace too small
+    assert status(lib, "moe_expert_ffn", bf, *args, 16, 128, 128, 8, 2, FAKE, FAKE, ws - 1,
+                  None) == _lib.MOE_ERR_WORKSPACE
+    # decode beyond its token limit
+    assert status(lib, "moe_expert_ffn_decode", bf, *args, 65, 128, 128, 8, 2, FAKE, FAKE,
+                  1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED
+    # misaligned workspace
+    assert status(lib, "moe_expert_ffn", bf, *args, 16, 128, 128, 8, 2, FAKE,
+                  ctypes.c_void_p(0x1008), ws, None) == _lib.MOE_ERR_INVALID_ARG
+    # unknown dtype
+    assert status(lib, "moe_expert_ffn", 7, *args, 16, 128, 128, 8, 2, FAKE, FAKE, ws,
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    # misaligned act for a phase call
+    assert status(lib, "moe_ffn_gate_up", bf, 0, FAKE, FAKE, FAKE, FAKE, 16, 128, 128, 8, 2,
+                  ctypes.c_void_p(0x1002), None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, "moe_combine", bf, FAKE, FAKE, FAKE, 4, 100, 2, FAKE,
+                  None) == _lib.MOE_ERR_UNSUPPORTED
+    assert status(lib, "moe_expert_ffn", bf, None, None, None, None, None, None, None, 0, 128,
+                  128, 8, 2, None, None, 0, None) == _lib.MOE_OK  # T = 0
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    status(lib, "moe_route", FAKE, 4, 8, 9, 1, FAKE, FAKE, None)
+    seen = []
+
+    def other():
+        seen.append(lib.moe_last_error())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"k = 9" in lib.moe_last_error()
