@@ -1,0 +1,231 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+
+One step is one pass of the whole path over one batch of synthetic input:
+route -> align -> indices->multihot -> multihot->indices -> grouped FC1 +
+SiLU-and-mul -> grouped FC2 -> combine (decode workloads use the decode FFN
+kernels).  Inputs are resident in HBM before timing starts; nothing is
+allocated inside the timed region.  Each phase is bracketed by HIP events on
+the stream the library launches on (torch's current stream), so per-kernel
+durations are measured live.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = {
+    "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
+    "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral",
+                   choices=["mixtral", "finegrained", "decode1", "decode32", "routing"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SRC[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
+    """The oracle (route + align + expert FFN per token, fp64) on a growing
+    prefix of the workload's tokens until ~10 s of CPU work."""
+    import numpy as np
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    n, spent, done = 1, 0.0, 0
+    t_total = 0.0
+    while True:
+        n = min(n, w.T)
+        toks = np.arange(n)
+        t0 = time.perf_counter()
+        tw, ids = oracle.route(inp["logits"][:n], w.k, w.norm)
+        oracle.align(ids, w.E)
+        if "hidden" in inp:
+            oracle.expert_ffn(inp["hidden"][:n], inp["w13"], inp["w2"], tw, ids,
+                              "bf16" if w.dtype == "bf16" else "f32", threads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if dt >= budget_s[0] or n >= w.T or spent >= budget_s[1]:
+            done, t_total = n, dt
+            break
+        grow = max(2, int(budget_s[0] / max(dt, 1e-3)))
+        n = n * min(grow, 8)
+    return {"value": done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} of {w.T} tokens: route + align + expert FFN + combine in "
+                      f"float64, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
+                                   f"--gpus {args.gpus} is not supported"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_moe_amd as moe
+    import moe_inputs as mi
+
+    w = mi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = mi.layer_inputs(w)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    T, E, k = w.T, w.E, w.k
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    has_ffn = "hidden" in inp
+    decode = w.name.startswith("decode")
+    lib = moe.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    # --- every buffer allocated up front -------------------------------------
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    aligned = {
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "sorted_token_ids": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "sorted_slot_ids": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "slot_to_sorted": torch.empty(T * k, dtype=torch.int32, device=dev),
+    }
+    align_ws = torch.empty(max(1, moe.moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                           device=dev)
+    mh = torch.empty((T, E), dtype=torch.uint8, device=dev)
+    pim = torch.empty((T, E), dtype=torch.float32, device=dev)
+    pos = torch.empty((T, E), dtype=torch.int32, device=dev)
+    back_p = torch.empty((T, k), dtype=torch.float32, device=dev)
+    back_i = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if has_ffn:
+        H, I = w.H, w.I
+        hidden, w13, w2 = bf(inp["hidden"]), bf(inp["w13"]), bf(inp["w2"])
+        act = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    phases = ["route", "align", "to_multihot", "to_indices"]
+    if has_ffn:
+        phases += ["gate_up", "down", "combine"]
+
+    def run_phase(name):
+        if name == "route":
+            moe.moe_route(logits, k, w.norm, topk_w, topk_ids)
+        elif name == "align":
+            moe.moe_align(topk_ids, E, aligned, align_ws)
+        elif name == "to_multihot":
+            moe.moe_indices_to_multihot(topk_ids, topk_w, E, (mh, pim, pos))
+        elif name == "to_indices":
+            moe.moe_multihot_to_indices(pim, pos, k, out=(back_p, back_i))
+        elif name == "gate_up":
+            moe.moe_ffn_gate_up(hidden, w13, aligned, k, decode, act)
+        elif name == "down":
+            moe.moe_ffn_down(act, w2, aligned, T, k, decode, y)
+        elif name == "combine":
+            moe.moe_combine(y, topk_w, aligned["slot_to_sorted"], torch.bfloat16, out)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(args.steps)]
+
+    for _ in range(args.warmup):
+        for ph in phases:
+            run_phase(ph)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, ph in enumerate(phases):
+            run_phase(ph)
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase_ms = {ph: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) /
+                args.steps for i, ph in enumerate(phases)}
+    ms_per_step = wall * 1e3 / args.steps
+    value = T * args.steps / wall
+
+    cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm}
+    if has_ffn:
+        cfg.update({"H": w.H, "I": w.I})
+        n_valid = int(aligned["offsets"][-1].item())
+    roofline = None
+    if has_ffn and not decode:
+        # Algorithmic FLOPs of FC1 per launch: 2 * rows * (2I) * H.
+        flops = 2.0 * n_valid * 2 * w.I * w.H
+        achieved = flops / (phase_ms["gate_up"] * 1e-3) / 1e12
+        roofline = {"kernel": "grouped_gemm_bf16_kernel<gate_up>", "bound": "mfma",
+                    "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic("gate_up", w.name)}
+        layer_flops = 2.0 * n_valid * 3 * w.I * w.H
+        cfg["layer_tflops_per_s"] = round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1)
+    elif has_ffn and decode:
+        # Algorithmic bytes of decode FC1 per launch: the selected experts' w13.
+        n_exp = int((aligned["counts"] > 0).sum().item())
+        nbytes = n_exp * 2 * w.I * w.H * 2 + T * w.H * 2 + n_valid * w.I * 2
+        achieved = nbytes / (phase_ms["gate_up"] * 1e-3) / 1e9
+        roofline = {"kernel": "decode_gate_up_kernel", "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic("decode_gate_up", w.name)}
+        cfg["distinct_experts"] = n_exp
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators, random-init weights)", "config": cfg,
+        "roofline": roofline,
+        "phase_ms": {k_: round(v, 4) for k_, v in phase_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,10 +10,11 @@
 //
 // Tile: 256 (rows) x 256 (weight rows) x 64 (k), 4 waves in a 2 x 2 layout,
 // each wave 128 x 128 = 4 x 4 MFMA 32x32x16 bf16 tiles with float32
-// accumulators.  Operand tiles are staged through LDS, double buffered
-// (2 x 64 KB), with the next k-tile's global loads in flight while the
-// current one feeds the matrix cores; 16-byte chunks are XOR-swizzled by row
-// so both the stores and the fragment reads are free of bank conflicts.
+// accumulators.  Operand tiles go from global memory straight into LDS
+// (global_load_lds, no staging registers), double buffered (2 x 64 KB), the
+// next k-tile in flight while the current one feeds the matrix cores; 16-byte
+// chunks are XOR-swizzled by row so the fragment reads are free of bank
+// conflicts.
 //
 // The weight tile is the MFMA "A" operand and the token tile the "B" operand,
 // so each lane's accumulators hold 4 consecutive output columns of one row
@@ -79,6 +80,51 @@ __device__ bool find_m_tile(const int32_t *__restrict__ offsets, int E, int ms, 
     return false;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue one k-tile of both operands straight into an LDS stage (gfx950
+// global_load_lds_dwordx4: lane L's 16 bytes land at base + 16 L).  Wave w
+// fills rows [64 w, 64 w + 64) of each tile, 8 rows per instruction; the
+// source chunk of each lane is pre-permuted so that the stage comes out
+// XOR-swizzled (chunk c of row r at position c ^ (r & 7)).
+__device__ __forceinline__ void issue_stage(uint16_t *stage, const uint16_t *const (&aptr)[8],
+                                            const uint16_t *const (&bptr)[8], int k0,
+                                            int wave) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint16_t *da = stage + (wave * 64 + i * 8) * BK;
+        uint16_t *db = stage + (BM + wave * 64 + i * 8) * BK;
+        __builtin_amdgcn_global_load_lds(aptr[i] + k0, (lds_void *)da, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(bptr[i] + k0, (lds_void *)db, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One LDS stage through the matrix cores: 4 k-steps of 16, each 4 weight
+// fragments x 4 token fragments of MFMA 32x32x16.
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[4][4], const uint16_t *s,
+                                          const int (&nrow)[4], int xrow, int lr, int lk,
+                                          int lane) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+        const int ch = ((ks * 2 + lk) ^ (lane & 7)) * 8;
+        bf16x8 wf[4], xf[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            wf[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            xf[g] = *reinterpret_cast<const bf16x8 *>(s + (xrow + g * 32) * BK + ch);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[f], xf[g], acc[f][g], 0,
+                                                                    0, 0);
+    }
+}
+
 // kGateUp: A = hidden [T, K] gathered through `gather`, W = w13 [E, 2N, K],
 //          C = act [rows, N] bf16 = silu(gate) * up.
 // else:    A = act [rows, K], W = w2 [E, N, K], C = y [rows, N] float32.
@@ -113,16 +159,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // Global -> LDS assignment: thread handles the 16-byte chunk (tid & 7)
-    // of rows (tid >> 3) + 32 i, i = 0..7, of both tiles.
-    const int rsub = tid >> 3;
-    const int c8 = (tid & 7) * 8;
-    const int sw8 = ((tid & 7) ^ (rsub & 7)) * 8;
+    // Operand rows of this lane: row 64 wave + 8 i + (lane >> 3) of each tile,
+    // global chunk (lane & 7) ^ (lane >> 3) of that row (see issue_stage).
+    const int rr = lane >> 3;
+    const int c8 = ((lane & 7) ^ rr) * 8;
     const uint16_t *aptr[8];
     const uint16_t *bptr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int r = rsub + 32 * i;
+        const int r = wave * 64 + i * 8 + rr;
         const int p = min(tile.row0 + r, tile.row_end - 1);
         const int arow = kGateUp ? gather[p] : p;
         aptr[i] = A + (int64_t)arow * K + c8;
@@ -136,27 +181,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         bptr[i] = W + ((int64_t)tile.e * (kGateUp ? 2 * N : N) + wrow) * K + c8;
     }
 
-    uint4 ra[8], rb[8];
-    auto gload = [&](int k0) {
+    f32x16 acc[4][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ra[i] = *reinterpret_cast<const uint4 *>(aptr[i] + k0);
-            rb[i] = *reinterpret_cast<const uint4 *>(bptr[i] + k0);
-        }
-    };
-    auto lstore = [&](int st) {
-        uint16_t *s = smem + st * kStage;
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *reinterpret_cast<uint4 *>(s + (rsub + 32 * i) * BK + sw8) = ra[i];
-            *reinterpret_cast<uint4 *>(s + (BM + rsub + 32 * i) * BK + sw8) = rb[i];
-        }
-    };
+        for (int g = 0; g < 4; ++g) acc[f][g] = f32x16{};
 
     const int wn = wave & 1;
     const int wm = wave >> 1;
     const int lr = lane & 31;
     const int lk = lane >> 5;
+    // LDS rows (within the weight tile) of this wave's 4 weight fragments.
     int nrow[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -165,38 +200,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         else
             nrow[f] = wn * 128 + f * 32;
     }
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) acc[f][g] = f32x16{};
+    const int xrow = wm * 128 + lr;
 
     const int nk = K / BK;
-    gload(0);
-    lstore(0);
+    issue_stage(smem, aptr, bptr, 0, wave);
+    wait_loads();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const uint16_t *s = smem + (kt & 1) * kStage;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = (((ks * 2 + lk) ^ (lane & 7)) * 8);
-            bf16x8 wf[4], xf[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-                wf[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                xf[g] = *reinterpret_cast<const bf16x8 *>(s + (wm * 128 + g * 32 + lr) * BK + ch);
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[f], xf[g], acc[f][g],
-                                                                        0, 0, 0);
-        }
-        if (kt + 1 < nk) lstore((kt + 1) & 1);
+        // The next k-tile streams into the other stage while this one feeds
+        // the matrix cores; sched_barrier keeps the issue ahead of the math.
+        if (kt + 1 < nk) issue_stage(smem + ((kt + 1) & 1) * kStage, aptr, bptr, (kt + 1) * BK,
+                                     wave);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage(acc, smem + (kt & 1) * kStage, nrow, xrow, lr, lk, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_loads();
         __syncthreads();
     }
 

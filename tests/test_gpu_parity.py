@@ -1,10 +1,20 @@
 """GPU parity: libmoe (HIP, through the C ABI) against the CPU oracle.
 
 Integer outputs (ids, counts, offsets, sorted ids, multihot, position maps)
-must match bit for bit; routing weights within 1e-6 relative; the layer
-output within max-abs <= 2e-2 x RMS (bf16) or 1e-4 x RMS (fp32), where RMS is
-that of the oracle's output.  Full-size prefill layers are checked on sampled
-tokens (the oracle is evaluated per token) plus properties of every token.
+must match bit for bit; routing weights within 1e-6 relative.  Layer output,
+with RMS that of the oracle's output:
+
+* float32 layers: max-abs error <= 1e-4 x RMS.
+* bfloat16 layers: the combine is run a second time writing float32 from the
+  same y, and that pre-rounding output must be within max-abs 2e-2 x RMS of
+  the oracle; the bf16 output must equal its round-to-nearest-even bit for
+  bit; and the bf16 output itself must be within 2e-2 x RMS plus half a bf16
+  ulp of the oracle value (rounding an exact result to bf16 already moves
+  these heavy-tailed outputs by up to ~2.4% of RMS, so the final rounding is
+  allowed on top of the budget).
+
+Full-size prefill layers are checked on sampled tokens (the oracle is
+evaluated per token) plus properties of every token.
 """
 
 import math
@@ -51,6 +61,37 @@ def assert_layer_close(out_gpu, out_ref, tol):
     assert np.all(np.isfinite(out_gpu))
     assert err <= tol * rms, f"max abs err {err:.4e} > {tol} x rms {rms:.4e}"
     return err / rms
+
+
+def half_ulp_bf16(v):
+    """Half a bfloat16 ulp at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(v), np.finfo(np.float32).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 8)
+
+
+def assert_bf16_layer(out_bf16, out_f32, out_ref):
+    """The three bf16 checks of the module docstring."""
+    rel = assert_layer_close(out_f32, out_ref, TOL_BF16)
+    rne = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(out_f32))
+    np.testing.assert_array_equal(out_bf16.view(np.uint32), rne.view(np.uint32))
+    rms = math.sqrt(float(np.mean(out_ref ** 2)))
+    excess = np.abs(out_bf16.astype(np.float64) - out_ref) - half_ulp_bf16(out_ref)
+    assert excess.max() <= TOL_BF16 * rms, f"bf16 output off by {excess.max():.3e} + 1/2 ulp"
+    return rel
+
+
+def run_ffn(x, w13, w2, tw, a, k, decode):
+    """All FFN phases through the C ABI -> (out bf16 as f32, pre-rounding out f32)."""
+    T = x.shape[0]
+    act = moe.moe_ffn_gate_up(x, w13, a, k, decode)
+    y = moe.moe_ffn_down(act, w2, a, T, k, decode)
+    out = moe.moe_combine(y, tw, a["slot_to_sorted"], x.dtype)
+    out32 = moe.moe_combine(y, tw, a["slot_to_sorted"], torch.float32)
+    one_call = moe.moe_expert_ffn(x, w13, w2, tw, a, decode=decode)
+    torch.cuda.synchronize()
+    assert torch.equal(one_call.view(torch.int16) if one_call.dtype == torch.bfloat16 else one_call,
+                       out.view(torch.int16) if out.dtype == torch.bfloat16 else out)
+    return host(out), host(out32)
 
 
 # --------------------------------------------------------------------------
@@ -221,12 +262,11 @@ def _rand_layer(seed, T, H, I, E, k, dtype="bf16", skew=0.0, inv=0.0):
 
 
 def _ffn_gpu(x, w13, w2, w32, ids, dtype, decode=False):
+    """-> (out, pre-rounding float32 out)."""
     E = w13.shape[0]
     td = dev_bf16 if dtype == "bf16" else dev
     a = moe.moe_align(dev(ids), E)
-    out = moe.moe_expert_ffn(td(x), td(w13), td(w2), dev(w32), a, decode=decode)
-    torch.cuda.synchronize()
-    return host(out)
+    return run_ffn(td(x), td(w13), td(w2), dev(w32), a, ids.shape[1], decode)
 
 
 @pytest.mark.parametrize("T,H,I,E,k,skew,inv", [
@@ -241,9 +281,9 @@ def _ffn_gpu(x, w13, w2, w32, ids, dtype, decode=False):
 ])
 def test_ffn_bf16_prefill(T, H, I, E, k, skew, inv):
     x, w13, w2, w32, ids = _rand_layer(T + H + I + E, T, H, I, E, k, skew=skew, inv=inv)
-    out = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
+    out, out32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
     ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "bf16")
-    assert_layer_close(out, ref, TOL_BF16)
+    assert_bf16_layer(out, out32, ref)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(1, 128, 128, 8, 2), (5, 256, 192, 16, 4),
@@ -251,15 +291,15 @@ def test_ffn_bf16_prefill(T, H, I, E, k, skew, inv):
                                        (20, 192, 320, 6, 2)])
 def test_ffn_bf16_decode(T, H, I, E, k):
     x, w13, w2, w32, ids = _rand_layer(T * 5 + H + I, T, H, I, E, k)
-    out = _ffn_gpu(x, w13, w2, w32, ids, "bf16", decode=True)
+    out, out32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16", decode=True)
     ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "bf16")
-    assert_layer_close(out, ref, TOL_BF16)
+    assert_bf16_layer(out, out32, ref)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(4, 64, 128, 8, 2), (50, 128, 64, 5, 3), (1, 64, 64, 1, 1)])
 def test_ffn_f32(T, H, I, E, k):
     x, w13, w2, w32, ids = _rand_layer(T + 3 * H, T, H, I, E, k, dtype="f32")
-    out = _ffn_gpu(x, w13, w2, w32, ids, "f32")
+    out, _ = _ffn_gpu(x, w13, w2, w32, ids, "f32")
     ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "f32")
     assert_layer_close(out, ref, TOL_F32)
 
@@ -268,26 +308,26 @@ def test_tiny_workload_layer_f32():
     w = mi.WORKLOADS["tiny"]
     inp = mi.layer_inputs(w)
     out, tw, tids, _ = moe.moe_layer(dev(inp["hidden"]), dev(inp["w13"]), dev(inp["w2"]),
-                                     dev(inp["logits"]), w.k, w.norm)
+                                     dev(inp["logits"]), w.k, w.norm, decode=False)
     torch.cuda.synchronize()
     ref = oracle.layer(inp, w.k, w.norm, "f32")
     np.testing.assert_array_equal(tids.cpu().numpy(), ref["topk_ids"])
     assert_layer_close(host(out), ref["out"], TOL_F32)
 
 
-def _full_layer(name, decode=None, sample=None):
+def _full_layer(name, decode, sample=None):
     w = mi.WORKLOADS[name]
     inp = mi.layer_inputs(w)
     x, w13, w2 = dev_bf16(inp["hidden"]), dev_bf16(inp["w13"]), dev_bf16(inp["w2"])
-    out, tw, tids, a = moe.moe_layer(x, w13, w2, dev(inp["logits"]), w.k, w.norm, decode=decode)
-    torch.cuda.synchronize()
+    tw, tids = moe.moe_route(dev(inp["logits"]), w.k, w.norm)
+    a = moe.moe_align(tids, w.E)
+    got, got32 = run_ffn(x, w13, w2, tw, a, w.k, decode)
     ow, oids = oracle.route(inp["logits"], w.k, w.norm)
     np.testing.assert_array_equal(tids.cpu().numpy(), oids)
     assert_weights_close(tw.cpu().numpy(), ow)
     toks = np.arange(w.T) if sample is None else sample(w.T, oids)
     ref = oracle.expert_ffn(inp["hidden"], inp["w13"], inp["w2"], ow, oids, "bf16", tokens=toks)
-    got = host(out)
-    rel = assert_layer_close(got[toks], ref, TOL_BF16)
+    rel = assert_bf16_layer(got[toks], got32[toks], ref)
     assert np.all(np.isfinite(got))
     return got, rel
 
@@ -305,23 +345,24 @@ def _sample_tokens(T, ids, n=12):
 
 
 def test_mixtral_layer_full_size():
-    _full_layer("mixtral", sample=_sample_tokens)
+    _full_layer("mixtral", False, sample=_sample_tokens)
 
 
 def test_finegrained_layer_full_size():
-    _full_layer("finegrained", sample=_sample_tokens)
+    _full_layer("finegrained", False, sample=_sample_tokens)
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode32"])
 def test_decode_layer_full_size(name):
-    got, _ = _full_layer(name, decode=True)
-    got_prefill, _ = _full_layer(name, decode=False)
+    got, _ = _full_layer(name, True)
+    got_prefill, _ = _full_layer(name, False)
     # Both paths round act and y once to bf16 from fp32 sums of the same terms.
     np.testing.assert_allclose(got, got_prefill, rtol=0, atol=2e-2 * np.sqrt(np.mean(got ** 2)))
 
 
 def test_layer_deterministic():
     x, w13, w2, w32, ids = _rand_layer(9, 700, 256, 256, 16, 4, skew=0.5)
-    a = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
-    b = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
+    a, a32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
+    b, b32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
     np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    np.testing.assert_array_equal(a32.view(np.uint32), b32.view(np.uint32))
