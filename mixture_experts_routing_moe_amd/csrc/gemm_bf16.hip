@@ -8,13 +8,14 @@
 // each block finds its expert and row range on the device from the aligned
 // offsets, so nothing is read back and empty experts cost nothing.
 //
-// Tile: 256 (rows) x 256 (weight rows) x 64 (k), 4 waves in a 2 x 2 layout,
-// each wave 128 x 128 = 4 x 4 MFMA 32x32x16 bf16 tiles with float32
-// accumulators.  Operand tiles go from global memory straight into LDS
-// (global_load_lds, no staging registers), double buffered (2 x 64 KB), the
-// next k-tile in flight while the current one feeds the matrix cores; 16-byte
-// chunks are XOR-swizzled by row so the fragment reads are free of bank
-// conflicts.
+// Tile: 256 token rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
+// waits hide behind the other's matrix-core work) in a 4 x 2 layout, each
+// wave 64 weight rows x 128 token rows = 2 x 4 MFMA 32x32x16 bf16 tiles with
+// float32 accumulators.  Operands go from global memory straight into LDS
+// (gfx950 global_load_lds_dwordx4, no staging registers) through a ring of
+// kStages k-tiles, so each load has kStages - 1 k-tiles of matrix-core work to
+// land; 16-byte chunks are XOR-swizzled so fragment reads are bank-conflict
+// free.
 //
 // The weight tile is the MFMA "A" operand and the token tile the "B" operand,
 // so each lane's accumulators hold 4 consecutive output columns of one row
@@ -25,27 +26,58 @@
 // output is rounded once, in the combine.
 //
 // Rows of a partial tile past the expert's segment load a clamped row and
-// are never stored; weight rows past N are clamped the same way.
+// are never stored, and the MFMAs of token fragments that hold none of the
+// expert's rows are not issued (the loop is instantiated per count of valid
+// fragments, so the hot loop carries no branches); weight rows past N are
+// clamped the same way.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64  // k elements per LDS stage
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2  // LDS stages in flight
+#endif
+
 constexpr int BM = 256;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
-constexpr int BK = 64;   // k per stage
-constexpr int kGroupM = 4;
-constexpr int kStage = (BM + BN) * BK;  // bf16 elements per LDS stage
+constexpr int BK = MOE_GEMM_BK;
+constexpr int kStages = MOE_GEMM_STAGES;
+constexpr int WN = 4;  // waves along the weight rows
+constexpr int WM = 2;  // waves along the token rows
+constexpr int kWaves = WN * WM;
+constexpr int kThreads = 64 * kWaves;
+constexpr int NF = BN / WN / 32;  // weight fragments per wave
+constexpr int MF = BM / WM / 32;  // token fragments per wave
+constexpr int kXcdChunk = 32;  // CUs per XCD: tiles an XCD runs at once
+constexpr int kStage = (BM + BN) * BK;         // bf16 elements per LDS stage
+constexpr int kChunks = BK / 8;                // 16-byte chunks per row
+constexpr int kRowsPerLoad = 64 / kChunks;     // rows one wave instruction fills
+constexpr int kRowsPerWave = BM / kWaves;      // rows each wave loads per tile
+constexpr int NL = kRowsPerWave / kRowsPerLoad;  // load instructions per tile per wave
+constexpr int kRowsPerWindow = 128 / BK;       // rows sharing one 256-byte bank window
+static_assert(kStages * kStage * 2 <= 160 * 1024, "LDS ring exceeds 160 KB");
+static_assert(NF % 2 == 0, "gate and up fragments come in pairs");
+static_assert(MF == 4, "the k loop is dispatched on 0..4 valid token fragments");
+static_assert(BK % 16 == 0 && kChunks <= 8, "k-steps of 16, at most 8 chunks per row");
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct MTile {
     int e, row0, row_end;
 };
 
-// m-slot -> (expert, rows): expert e owns ceil(count_e / BM) consecutive
-// m-slots; a running sum over the experts (64 per pass, one per lane) finds
-// the owner.  Every wave computes the same answer, so no LDS is needed.
-__device__ bool find_m_tile(const int32_t *__restrict__ offsets, int E, int ms, MTile &t) {
+// Tile index -> (expert, rows, n-tile).  Expert e owns mt_e = ceil(count_e /
+// BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
+// tile index, ordered n-tile-major: consecutive tiles are the expert's
+// m-tiles under one weight n-tile.  A running sum of mt_e over the experts
+// (64 per pass, one per lane) finds the owner.  Every wave computes the same
+// answer, so no LDS is needed.
+__device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int n_tiles,
+                          MTile &t, int &nt) {
     const int lane = lane_id();
     int carry = 0;
     for (int c = 0; c < E; c += kWave) {
@@ -64,14 +96,18 @@ __device__ bool find_m_tile(const int32_t *__restrict__ offsets, int E, int ms, 
         }
         incl += carry;
         const int excl = incl - tiles;
-        const uint64_t hit = __ballot(tiles > 0 && ms >= excl && ms < incl);
+        const uint64_t hit =
+            __ballot(tiles > 0 && L >= excl * n_tiles && L < incl * n_tiles);
         if (hit) {
-            const int L = __ffsll((unsigned long long)hit) - 1;
-            const int ex = readlane_i(excl, L);
-            const int o0 = readlane_i(off, L);
-            const int cn = readlane_i(cnt, L);
-            t.e = c + L;
-            t.row0 = o0 + (ms - ex) * BM;
+            const int src = __ffsll((unsigned long long)hit) - 1;
+            const int ex = readlane_i(excl, src);
+            const int mt = readlane_i(tiles, src);
+            const int o0 = readlane_i(off, src);
+            const int cn = readlane_i(cnt, src);
+            const int j = L - ex * n_tiles;
+            nt = j / mt;
+            t.e = c + src;
+            t.row0 = o0 + (j - nt * mt) * BM;
             t.row_end = min(t.row0 + BM, o0 + cn);
             return true;
         }
@@ -80,48 +116,91 @@ __device__ bool find_m_tile(const int32_t *__restrict__ offsets, int E, int ms, 
     return false;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// LDS layout of a stage: token rows [0, BM) then weight rows [BM, BM + BN),
+// each BK bf16 = kChunks chunks of 16 bytes; chunk c of row r is stored at
+// position c ^ swz(r).  A ds_read_b128 serves 16 lanes per cycle from 64
+// banks (a 256-byte window); a fragment read has 16 consecutive rows at one
+// logical chunk, and rows r, r + kRowsPerWindow, ... share window offsets, so
+// swz must differ across them: swz(r) = (r / kRowsPerWindow) % kChunks.
+__device__ __forceinline__ int swz(int r) { return (r / kRowsPerWindow) % kChunks; }
 
-// Issue one k-tile of both operands straight into an LDS stage (gfx950
-// global_load_lds_dwordx4: lane L's 16 bytes land at base + 16 L).  Wave w
-// fills rows [64 w, 64 w + 64) of each tile, 8 rows per instruction; the
-// source chunk of each lane is pre-permuted so that the stage comes out
-// XOR-swizzled (chunk c of row r at position c ^ (r & 7)).
-__device__ __forceinline__ void issue_stage(uint16_t *stage, const uint16_t *const (&aptr)[8],
-                                            const uint16_t *const (&bptr)[8], int k0,
-                                            int wave) {
+// Issue one k-tile of both operands straight into an LDS stage
+// (global_load_lds_dwordx4: lane L's 16 bytes land at base + 16 L, i.e. row
+// L / kChunks, position L % kChunks of the instruction's rows).
+__device__ __forceinline__ void issue_stage(uint16_t *stage, const uint16_t *const *aptr,
+                                            const uint16_t *const *bptr, int k0, int row_base) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint16_t *da = stage + (wave * 64 + i * 8) * BK;
-        uint16_t *db = stage + (BM + wave * 64 + i * 8) * BK;
+    for (int i = 0; i < NL; ++i) {
+        uint16_t *da = stage + (row_base + i * kRowsPerLoad) * BK;
+        uint16_t *db = stage + (BM + row_base + i * kRowsPerLoad) * BK;
         __builtin_amdgcn_global_load_lds(aptr[i] + k0, (lds_void *)da, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(bptr[i] + k0, (lds_void *)db, 16, 0, 0);
     }
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most `n` load instructions of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
 
-// One LDS stage through the matrix cores: 4 k-steps of 16, each 4 weight
-// fragments x 4 token fragments of MFMA 32x32x16.
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[4][4], const uint16_t *s,
-                                          const int (&nrow)[4], int xrow, int lr, int lk,
-                                          int lane) {
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also drain the loads still in flight for later stages).  Callers wait for
+// the loads they need first; every LDS read of the previous stage has
+// completed because the MFMAs that consume it were issued before.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One LDS stage through the matrix cores: BK / 16 k-steps, each NF weight
+// fragments x MV token fragments of MFMA 32x32x16 (one ds_read_b128 per
+// fragment: row + lr, chunk 2 ks + lk, swizzled; fragment rows start at
+// multiples of 32, so swz(row) = swz(lr)).  Token fragments MV..MF-1 hold no
+// row of the expert and are skipped entirely.
+template <int MV>
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[NF][MF], const uint16_t *s,
+                                          const int (&nrow)[NF], int xrow, int lr, int lk) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ((ks * 2 + lk) ^ (lane & 7)) * 8;
-        bf16x8 wf[4], xf[4];
+        const int ch = ((ks * 2 + lk) ^ swz(lr)) * 8;
+        bf16x8 wf[NF], xf[MV > 0 ? MV : 1];
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < NF; ++f)
             wf[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < MV; ++g)
             xf[g] = *reinterpret_cast<const bf16x8 *>(s + (xrow + g * 32) * BK + ch);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int g = 0; g < MV; ++g)
                 acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[f], xf[g], acc[f][g], 0,
                                                                     0, 0);
+    }
+}
+
+// The k loop over a ring of kStages LDS stages.  Iteration kt waits for its
+// own k-tile (the kStages - 2 newer ones may still be in flight), then one
+// barrier makes that stage visible to every wave and guarantees that every
+// wave is done with the stage of iteration kt - 1, which is refilled with
+// k-tile kt + kStages - 1 before the math starts.
+template <int MV>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
+                                       const uint16_t *const *aptr, const uint16_t *const *bptr,
+                                       int nk, int row_base, const int (&nrow)[NF], int xrow,
+                                       int lr, int lk) {
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) issue_stage(smem + s * kStage, aptr, bptr, s * BK, row_base);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + kStages - 2 < nk)
+            wait_loads<(kStages - 2) * 2 * NL>();
+        else
+            wait_loads<0>();
+        stage_barrier();
+        const int nxt = kt + kStages - 1;
+        if (nxt < nk) issue_stage(smem + (nxt % kStages) * kStage, aptr, bptr, nxt * BK, row_base);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage<MV>(acc, smem + (kt % kStages) * kStage, nrow, xrow, lr, lk);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -132,42 +211,38 @@ template <bool kGateUp>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
-    int E, int K, int N, int m_slots, int n_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+    int E, int K, int N, int n_tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStage];
 
-    // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs, so
-    // block b is given tile index (b % 8) * (grid / 8) + b / 8: each XCD
-    // works through one contiguous range of tiles, and within it groups of
-    // kGroupM m-slots sweep the n-tiles together, sharing weight tiles (and
-    // token tiles) in that XCD's L2.
-    const int nblk = gridDim.x;
+    // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs (block b
+    // runs on XCD b % 8), and each XCD has 32 CUs.  Tiles are handed out in
+    // chunks of 32 consecutive tile indices per XCD, chunks round-robin over
+    // the XCDs: the 32 tiles an XCD runs together are a few weight n-tiles of
+    // one expert with all of its m-tiles under each, so they share weight and
+    // token tiles in that XCD's L2, and the surplus blocks past the last tile
+    // are spread evenly over the XCDs.
     const int bid = blockIdx.x;
-    const int L = (bid & 7) * (nblk >> 3) + (bid >> 3);
-    if (L >= m_slots * n_tiles) return;
-    const int per_group = kGroupM * n_tiles;
-    const int group = L / per_group;
-    const int first_m = group * kGroupM;
-    const int gsz = min(m_slots - first_m, kGroupM);
-    const int within = L - group * per_group;
-    const int ms = first_m + within % gsz;
-    const int nt = within / gsz;
-
+    const int slot = bid >> 3;
+    const int L = ((slot / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + slot % kXcdChunk;
     MTile tile;
-    if (!find_m_tile(offsets, E, ms, tile)) return;
+    int nt;
+    if (!find_tile(offsets, E, L, n_tiles, tile, nt)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // Operand rows of this lane: row 64 wave + 8 i + (lane >> 3) of each tile,
-    // global chunk (lane & 7) ^ (lane >> 3) of that row (see issue_stage).
-    const int rr = lane >> 3;
-    const int c8 = ((lane & 7) ^ rr) * 8;
-    const uint16_t *aptr[8];
-    const uint16_t *bptr[8];
+    // Operand rows this lane loads: row row_base + kRowsPerLoad i + lane /
+    // kChunks of each tile; it lands at position lane % kChunks, so it fetches
+    // global chunk (lane % kChunks) ^ swz(row) of that row.
+    const int row_base = wave * kRowsPerWave;
+    const int rr = lane / kChunks;
+    const uint16_t *aptr[NL];
+    const uint16_t *bptr[NL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wave * 64 + i * 8 + rr;
+    for (int i = 0; i < NL; ++i) {
+        const int r = row_base + i * kRowsPerLoad + rr;
+        const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         const int p = min(tile.row0 + r, tile.row_end - 1);
         const int arow = kGateUp ? gather[p] : p;
         aptr[i] = A + (int64_t)arow * K + c8;
@@ -181,60 +256,59 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         bptr[i] = W + ((int64_t)tile.e * (kGateUp ? 2 * N : N) + wrow) * K + c8;
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[NF][MF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[f][g] = f32x16{};
+        for (int g = 0; g < MF; ++g) acc[f][g] = f32x16{};
 
-    const int wn = wave & 1;
-    const int wm = wave >> 1;
+    const int wn = wave % WN;
+    const int wm = wave / WN;
     const int lr = lane & 31;
     const int lk = lane >> 5;
-    // LDS rows (within the weight tile) of this wave's 4 weight fragments.
-    int nrow[4];
+    // LDS rows (within the weight tile) of this wave's weight fragments.  For
+    // FC1 the first NF/2 are gate rows and the rest the matching up rows.
+    int nrow[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < NF; ++f) {
         if (kGateUp)
-            nrow[f] = f < 2 ? wn * 64 + f * 32 : BN / 2 + wn * 64 + (f - 2) * 32;
+            nrow[f] = (f < NF / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (f % (NF / 2)) * 32;
         else
-            nrow[f] = wn * 128 + f * 32;
+            nrow[f] = wn * (BN / WN) + f * 32;
     }
-    const int xrow = wm * 128 + lr;
+    const int xrow = wm * (BM / WM) + lr;
 
+    // Token fragments of this wave that hold at least one row of the expert
+    // (wave-uniform); a wave with none still takes part in loads and barriers.
+    const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     const int nk = K / BK;
-    issue_stage(smem, aptr, bptr, 0, wave);
-    wait_loads();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        // The next k-tile streams into the other stage while this one feeds
-        // the matrix cores; sched_barrier keeps the issue ahead of the math.
-        if (kt + 1 < nk) issue_stage(smem + ((kt + 1) & 1) * kStage, aptr, bptr, (kt + 1) * BK,
-                                     wave);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_stage(acc, smem + (kt & 1) * kStage, nrow, xrow, lr, lk, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_loads();
-        __syncthreads();
+    switch (mvalid) {
+        case 4: k_loop<4>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
+        case 3: k_loop<3>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
+        case 2: k_loop<2>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
+        case 1: k_loop<1>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
+        default: k_loop<0>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
     }
 
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
     // the weight side and column lr of the token side.
+    const int prow = tile.row0 + wm * (BM / WM) + lr;
     if (kGateUp) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < NF / 2; ++f) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int p = tile.row0 + wm * 128 + g * 32 + lr;
+            for (int g = 0; g < MF; ++g) {
+                const int p = prow + g * 32;
                 if (p >= tile.row_end) continue;
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int n = nt * (BN / 2) + wn * 64 + f * 32 + rg * 8 + lk * 4;
+                    const int n = nt * (BN / 2) + wn * (BN / 2 / WN) + f * 32 + rg * 8 + lk * 4;
                     if (n >= N) continue;
                     bf16x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        o[q] = to_bf16(silu_f(acc[f][g][rg * 4 + q]) * acc[f + 2][g][rg * 4 + q]);
+                        o[q] = to_bf16(silu_f(acc[f][g][rg * 4 + q]) *
+                                       acc[f + NF / 2][g][rg * 4 + q]);
                     *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(Cv) + (int64_t)p * N +
                                                 n) = o;
                 }
@@ -242,14 +316,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         }
     } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < NF; ++f) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int p = tile.row0 + wm * 128 + g * 32 + lr;
+            for (int g = 0; g < MF; ++g) {
+                const int p = prow + g * 32;
                 if (p >= tile.row_end) continue;
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int n = nt * BN + wn * 128 + f * 32 + rg * 8 + lk * 4;
+                    const int n = nt * BN + wn * (BN / WN) + f * 32 + rg * 8 + lk * 4;
                     if (n >= N) continue;
                     const f32x16 &a = acc[f][g];
                     *reinterpret_cast<float4 *>(static_cast<float *>(Cv) + (int64_t)p * N + n) =
@@ -265,9 +339,12 @@ int m_slot_bound(int64_t rows, int E) {
     return (int)((rows + BM - 1) / BM + nz);
 }
 
+// Blocks for an upper bound of m_slots * n_tiles tiles, rounded up to whole
+// rounds of 8 XCDs x kXcdChunk so the block -> tile map is a bijection.
 unsigned grid_of(int m_slots, int n_tiles) {
+    const int64_t round = 8 * kXcdChunk;
     const int64_t total = (int64_t)m_slots * n_tiles;
-    return (unsigned)((total + 7) / 8 * 8);
+    return (unsigned)((total + round - 1) / round * round);
 }
 
 }  // namespace
@@ -281,7 +358,7 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
     const int n_tiles = (I + BN / 2 - 1) / (BN / 2);
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(grid_of(m_slots, n_tiles)),
                        dim3(kThreads), 0, s, hidden, sorted_tok, w13, offsets, act, E, H, I,
-                       m_slots, n_tiles);
+                       n_tiles);
     return hipGetLastError();
 }
 
@@ -292,8 +369,7 @@ hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32
     const int m_slots = m_slot_bound(rows, E);
     const int n_tiles = (H + BN - 1) / BN;
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(grid_of(m_slots, n_tiles)),
-                       dim3(kThreads), 0, s, act, nullptr, w2, offsets, y, E, I, H, m_slots,
-                       n_tiles);
+                       dim3(kThreads), 0, s, act, nullptr, w2, offsets, y, E, I, H, n_tiles);
     return hipGetLastError();
 }
 
