@@ -42,6 +42,14 @@ def parse():
     p.add_argument("--workload", default="mixtral",
                    choices=["mixtral", "finegrained", "decode1", "decode32", "routing"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--draws", type=int, default=None,
+                   help="distinct routing draws rotated over the steps (default: 32 for "
+                        "decode workloads, else 1)")
+    p.add_argument("--flush", type=int, default=None,
+                   help="1: overwrite a 512 MiB buffer before every step (outside the "
+                        "per-kernel events) so weights come from HBM, not the Infinity "
+                        "Cache; ms_per_step is then the sum of the kernel phases "
+                        "(default: 1 for decode workloads, else 0)")
     return p.parse_args()
 
 
@@ -116,11 +124,13 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     T, E, k = w.T, w.E, w.k
-    logits = torch.from_numpy(inp["logits"]).to(dev)
-    has_ffn = "hidden" in inp
     decode = w.name.startswith("decode")
-    lib = moe.lib()
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    draws = args.draws if args.draws is not None else (32 if decode else 1)
+    flush = bool(args.flush if args.flush is not None else decode)
+    logits_draws = [torch.from_numpy(inp["logits"] if r == 0 else mi.gating_logits_draw(w, r))
+                    .to(dev) for r in range(draws)]
+    flush_buf = torch.empty(128 << 20, dtype=torch.float32, device=dev) if flush else None
+    has_ffn = "hidden" in inp
 
     # --- every buffer allocated up front -------------------------------------
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -150,9 +160,11 @@ def main():
     if has_ffn:
         phases += ["gate_up", "down", "combine"]
 
+    cur = {"logits": logits_draws[0]}
+
     def run_phase(name):
         if name == "route":
-            moe.moe_route(logits, k, w.norm, topk_w, topk_ids)
+            moe.moe_route(cur["logits"], k, w.norm, topk_w, topk_ids)
         elif name == "align":
             moe.moe_align(topk_ids, E, aligned, align_ws)
         elif name == "to_multihot":
@@ -169,26 +181,43 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
           for _ in range(args.steps)]
 
-    for _ in range(args.warmup):
+    for it in range(args.warmup):
+        cur["logits"] = logits_draws[it % draws]
         for ph in phases:
             run_phase(ph)
     torch.cuda.synchronize()
 
+    n_distinct = []
     t0 = time.perf_counter()
     for s in range(args.steps):
+        cur["logits"] = logits_draws[s % draws]
+        if flush:
+            flush_buf.fill_(float(s))
         ev[s][0].record()
         for i, ph in enumerate(phases):
             run_phase(ph)
             ev[s][i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if decode:
+        # Distinct experts per routing draw (outside the timed region).
+        for r in range(min(draws, args.steps)):
+            cur["logits"] = logits_draws[r]
+            run_phase("route")
+            run_phase("align")
+            n_distinct.append(int((aligned["counts"] > 0).sum().item()))
 
     phase_ms = {ph: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) /
                 args.steps for i, ph in enumerate(phases)}
-    ms_per_step = wall * 1e3 / args.steps
-    value = T * args.steps / wall
+    if flush:
+        # The cache flush between steps is not part of the layer.
+        ms_per_step = sum(phase_ms.values())
+    else:
+        ms_per_step = wall * 1e3 / args.steps
+    value = T * 1e3 / ms_per_step
 
-    cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm}
+    cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm,
+           "routing_draws": draws, "cache_flush_between_steps": flush}
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I})
         n_valid = int(aligned["offsets"][-1].item())
@@ -204,15 +233,19 @@ def main():
         layer_flops = 2.0 * n_valid * 3 * w.I * w.H
         cfg["layer_tflops_per_s"] = round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1)
     elif has_ffn and decode:
-        # Algorithmic bytes of decode FC1 per launch: the selected experts' w13.
-        n_exp = int((aligned["counts"] > 0).sum().item())
+        # Algorithmic bytes of decode FC1 per launch: the selected experts' w13
+        # (mean over the routing draws) + the token rows + the activations.
+        n_exp = sum(n_distinct) / len(n_distinct)
         nbytes = n_exp * 2 * w.I * w.H * 2 + T * w.H * 2 + n_valid * w.I * 2
         achieved = nbytes / (phase_ms["gate_up"] * 1e-3) / 1e9
         roofline = {"kernel": "decode_gate_up_kernel", "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic("decode_gate_up", w.name)}
-        cfg["distinct_experts"] = n_exp
+        cfg["distinct_experts_mean"] = round(n_exp, 2)
+        w2_bytes = n_exp * w.H * w.I * 2
+        cfg["down_hbm_gbs"] = round((w2_bytes + n_valid * w.I * 2 + n_valid * w.H * 4) /
+                                    (phase_ms["down"] * 1e-3) / 1e9, 1)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

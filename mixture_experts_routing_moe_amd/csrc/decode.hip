@@ -11,9 +11,10 @@
 // unselected experts are never touched.
 //
 // Each block owns 16 weight rows (16 gate + 16 up rows for FC1) of one
-// expert; its 4 waves split k and stream 256 contiguous bytes per row per
-// step into MFMA 16x16x32 bf16 (weights as the A operand, up to 4 chunks of
-// 16 tokens as B).  The 4 partial accumulators are summed through LDS.
+// expert; its 4 waves split k into contiguous quarters, load their whole
+// share of the weight rows up front and feed MFMA 16x16x32 bf16 (weights as
+// the A operand, up to 4 chunks of 16 tokens as B).  The 4 partial
+// accumulators are summed through LDS.
 #include "moe_internal.h"
 
 namespace moe {
@@ -21,7 +22,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 16;   // weight rows per block
-constexpr int kKB = 128;    // k elements per wave step (4 MFMA k-steps)
 
 // The d-th expert (in id order) whose segment is non-empty.
 __device__ bool nth_nonempty_expert(const int32_t *__restrict__ offsets, int E, int d, int &e,
@@ -49,6 +49,23 @@ __device__ bool nth_nonempty_expert(const int32_t *__restrict__ offsets, int E, 
         seen += pc;
     }
     return false;
+}
+
+// Streamed weight load: read once, so non-temporal.
+__device__ __forceinline__ bf16x8 ld_stream(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
+}
+
+// Each wave owns a contiguous quarter of the k range of the block's weight
+// rows and issues every load of a batch of kBatch MFMA k-steps (weights and
+// token fragments) before the first MFMA of the batch, so each lane keeps
+// kBatch x 16 bytes per weight row group in flight (these kernels are bound
+// by the bytes in flight).  k-steps past the wave's range load a clamped
+// address and multiply a zeroed fragment, so the math carries no branches.
+constexpr int kBatch = 8;
+
+__device__ __forceinline__ bf16x8 zero_unless(bool keep, bf16x8 v) {
+    return keep ? v : bf16x8{};
 }
 
 // FC1 + SiLU-and-mul.  act[p, n] for n in this block's 16 rows and every
@@ -82,21 +99,33 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
         ag[mc] = f32x4{};
         au[mc] = f32x4{};
     }
-    const int nkb = (H + kKB - 1) / kKB;
-    for (int kb = wave; kb < nkb; kb += 4) {
+    const int nks = H / 32;
+    const int per = (nks + 3) / 4;
+    const int s0 = wave * per;
+    const int s1 = min(nks, s0 + per);
+    for (int b = s0; b < s1; b += kBatch) {
+        bf16x8 g[kBatch], u[kBatch], x[MC][kBatch];
 #pragma unroll
-        for (int s = 0; s < kKB / 32; ++s) {
-            const int k0 = kb * kKB + s * 32;
-            if (k0 >= H) break;
-            const bf16x8 g = *reinterpret_cast<const bf16x8 *>(wg + k0);
-            const bf16x8 u = *reinterpret_cast<const bf16x8 *>(wu + k0);
+        for (int s = 0; s < kBatch; ++s) {
+            const int k0 = min(b + s, nks - 1) * 32;
+            g[s] = ld_stream(wg + k0);
+            u[s] = ld_stream(wu + k0);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+                x[mc][s] = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+            const bool in = b + s < s1;
+            const bf16x8 gs = zero_unless(in, g[s]), us = zero_unless(in, u[s]);
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc) {
-                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
-                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g, x, ag[mc], 0, 0, 0);
-                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u, x, au[mc], 0, 0, 0);
+                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gs, x[mc][s], ag[mc], 0, 0, 0);
+                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(us, x[mc][s], au[mc], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (wave > 0) {
 #pragma unroll
@@ -126,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
     }
 }
 
-// FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p of the
-// expert's segment.
+// FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p
+// of the expert's segment.
 template <int MC>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
@@ -151,19 +180,29 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     f32x4 acc[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{};
-    const int nkb = (I + kKB - 1) / kKB;
-    for (int kb = wave; kb < nkb; kb += 4) {
+    const int nks = I / 32;
+    const int per = (nks + 3) / 4;
+    const int s0 = wave * per;
+    const int s1 = min(nks, s0 + per);
+    for (int b = s0; b < s1; b += kBatch) {
+        bf16x8 wv[kBatch], x[MC][kBatch];
 #pragma unroll
-        for (int s = 0; s < kKB / 32; ++s) {
-            const int k0 = kb * kKB + s * 32;
-            if (k0 >= I) break;
-            const bf16x8 w = *reinterpret_cast<const bf16x8 *>(wr + k0);
+        for (int s = 0; s < kBatch; ++s) {
+            const int k0 = min(b + s, nks - 1) * 32;
+            wv[s] = ld_stream(wr + k0);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
-                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc[mc], 0, 0, 0);
-            }
+            for (int mc = 0; mc < MC; ++mc)
+                x[mc][s] = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+            const bf16x8 ws = zero_unless(b + s < s1, wv[s]);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws, x[mc][s], acc[mc], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (wave > 0) {
 #pragma unroll

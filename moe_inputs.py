@@ -162,6 +162,18 @@ def gating_logits(w: Workload, T: int | None = None, reject_ties: bool | None = 
     return np.ascontiguousarray(x)
 
 
+def gating_logits_draw(w: Workload, draw: int) -> np.ndarray:
+    """Extra independent [T, E] logits for the same workload (draw >= 1; draw 0
+    is gating_logits): N(0,1) from stream 100 + draw, plus the same bias."""
+    if draw == 0:
+        return gating_logits(w)
+    g = generator(w.wid, 100 + draw)
+    x = g.standard_normal((w.T, w.E)).astype(np.float32)
+    if w.bias != "none":
+        x = (x + expert_bias(w)[None, :]).astype(np.float32)
+    return np.ascontiguousarray(x)
+
+
 def layer_inputs(w: Workload, T: int | None = None, weights: bool = True) -> dict:
     """Every input of the layer forward for a workload.
 
