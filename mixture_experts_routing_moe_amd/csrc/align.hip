@@ -8,15 +8,15 @@
 //
 //   1. align_hist:    each block counts the ids of its contiguous chunk of
 //                     flat slots into an LDS histogram -> partial[b][e].
-//   2. align_scan:    one block turns the partials into per-expert totals,
-//                     exclusive offsets (the indptr) and, for every (b, e),
-//                     the first position block b may write for expert e.
-//   3. align_scatter: each block walks its chunk in order, 256 slots at a
-//                     time; a slot's rank among earlier slots of the same
-//                     expert comes from ballots inside its wave plus the
-//                     counts of the waves before it, so positions follow the
-//                     flat slot order t*k+j -- ascending token inside each
-//                     expert, exactly the order of the pages' cumsum.
+//   2. align_scatter: each block sums the partials into per-expert totals,
+//                     the exclusive offsets (the indptr) and the first
+//                     position it may write for each expert, then walks its
+//                     chunk in order, 256 slots at a time; a slot's rank among
+//                     earlier slots of the same expert comes from ballots
+//                     inside its wave plus the counts of the waves before it,
+//                     so positions follow the flat slot order t*k+j --
+//                     ascending token inside each expert, exactly the order
+//                     of the pages' cumsum.
 //
 // Only integer LDS atomics on private counters are used, and no result
 // depends on their order, so the output is identical on every run.
@@ -26,8 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kAlignThreads = 256;
-constexpr int kScanThreads = 1024;
-constexpr int kPartialBudget = 12288;  // nb * E partial counts kept in LDS by the scan
+constexpr int kPartialBudget = 12288;  // cap on nb * E partial counts each scatter block sums
 
 int64_t align_chunk(int64_t n, int nb) {
     int64_t c = (n + nb - 1) / nb;
@@ -51,86 +50,115 @@ __global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(
         partial[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-__global__ __launch_bounds__(kScanThreads) void align_scan_kernel(
-    int32_t *__restrict__ partial, int nb, int E, int64_t n, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
-    int32_t *__restrict__ sorted_slot) {
-    extern __shared__ int32_t sm[];
-    int32_t *P = sm;                 // [nb][E]
-    int32_t *base = sm + nb * E;     // [E]
-    int32_t *wtot = base + E;        // [kScanThreads / 64]
-    int32_t *total = wtot + kScanThreads / kWave;
+// Block-wide exclusive scan of v[0..n) in LDS (n <= 4 * kAlignThreads),
+// written to out[0..n); returns the total.  All threads must call it.
+__device__ int block_exclusive_scan(const int32_t *v, int32_t *out, int n, int32_t *wsum) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
-
-    for (int i = tid; i < nb * E; i += kScanThreads) P[i] = partial[i];
-    __syncthreads();
-    // Per expert: exclusive prefix over blocks (in place) and the total.
-    for (int e = tid; e < E; e += kScanThreads) {
-        int run = 0;
-        for (int b = 0; b < nb; ++b) {
-            const int c = P[b * E + e];
-            P[b * E + e] = run;
-            run += c;
-        }
-        base[e] = run;
+    int x[4];
+    int tsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        x[i] = e < n ? v[e] : 0;
+        tsum += x[i];
     }
-    __syncthreads();
-    // Exclusive prefix over experts (E <= kScanThreads: one per thread).
-    const int x = tid < E ? base[tid] : 0;
-    int incl = x;
+    int incl = tsum;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const int y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
     }
-    if (lane == kWave - 1) wtot[wave] = incl;
+    if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    if (wave == 0) {
-        int w = lane < kScanThreads / kWave ? wtot[lane] : 0;
-        int wi = w;
+    int before = 0, total = 0;
 #pragma unroll
-        for (int o = 1; o < kScanThreads / kWave; o <<= 1) {
-            const int y = __shfl_up(wi, o, kWave);
-            if (lane >= o) wi += y;
-        }
-        if (lane < kScanThreads / kWave) wtot[lane] = wi - w;  // exclusive wave prefix
+    for (int w = 0; w < kAlignThreads / kWave; ++w) {
+        const int ws = wsum[w];
+        if (w < wave) before += ws;
+        total += ws;
+    }
+    int run = before + incl - tsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        if (e < n) out[e] = run;
+        run += x[i];
     }
     __syncthreads();
-    const int excl = incl - x + wtot[wave];
-    if (tid < E) {
-        counts[tid] = x;
-        offsets[tid] = excl;
-        base[tid] = excl;
-        if (tid == E - 1) {
-            offsets[E] = excl + x;
-            *total = excl + x;
+    return total;
+}
+
+// Scan + scatter.  Every block first turns the per-block histograms into the
+// expert totals, the exclusive expert offsets and its own first position per
+// expert (block 0 also writes counts and offsets); then it walks its chunk
+// in order, 256 slots at a time: a slot's rank among earlier slots of the
+// same expert comes from ballots inside its wave plus the counts of the
+// waves before it, so positions follow the flat slot order.
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
+    const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
+    extern __shared__ int32_t sm[];
+    // LDS: run[E] | wcnt[4][E] | tot[E] | off[E] | tot_part[P][E] | pre_part[P][E] | wsum[4]
+    const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
+    int32_t *run = sm;
+    int32_t *wcnt = run + E;
+    int32_t *tot = wcnt + 4 * E;
+    int32_t *off = tot + E;
+    int32_t *tot_part = off + E;
+    int32_t *pre_part = tot_part + parts * E;
+    int32_t *wsum = pre_part + parts * E;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int b = blockIdx.x;
+
+    // Per (part, expert): sums over the blocks part, part + parts, ... -- all
+    // of them and those before b.  Threads of one pass read consecutive
+    // experts of one block row (coalesced), and the loads are independent.
+    for (int idx = tid; idx < parts * E; idx += kAlignThreads) {
+        const int e = idx % E, part = idx / E;
+        int all = 0, pre = 0;
+#pragma unroll 8
+        for (int bb = part; bb < nb; bb += parts) {
+            const int c = partial[(int64_t)bb * E + e];
+            all += c;
+            pre += bb < b ? c : 0;
         }
+        tot_part[part * E + e] = all;
+        pre_part[part * E + e] = pre;
     }
     __syncthreads();
-    for (int i = tid; i < nb * E; i += kScanThreads) partial[i] = base[i % E] + P[i];
+    for (int e = tid; e < E; e += kAlignThreads) {
+        int all = 0, pre = 0;
+        for (int part = 0; part < parts; ++part) {
+            all += tot_part[part * E + e];
+            pre += pre_part[part * E + e];
+        }
+        tot[e] = all;
+        run[e] = pre;
+    }
+    for (int i = tid; i < 4 * E; i += kAlignThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int total = block_exclusive_scan(tot, off, E, wsum);
+    for (int e = tid; e < E; e += kAlignThreads) {
+        run[e] += off[e];
+        if (b == 0) {
+            counts[e] = tot[e];
+            offsets[e] = off[e];
+        }
+    }
+    if (b == 0 && tid == 0) offsets[E] = total;
     // Positions past the valid slots (ids outside [0, E)) read -1.
-    for (int64_t p = *total + tid; p < n; p += kScanThreads) {
+    for (int p = total + b * kAlignThreads + tid; p < n; p += nb * kAlignThreads) {
         sorted_tok[p] = -1;
         sorted_slot[p] = -1;
     }
-}
-
-__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits,
-    const int32_t *__restrict__ start, int32_t *__restrict__ sorted_tok,
-    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
-    extern __shared__ int32_t sm[];
-    int32_t *run = sm;        // [E]   next free position per expert for this block
-    int32_t *wcnt = sm + E;   // [4][E] per-wave counts of the current 256 slots
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    for (int e = tid; e < E; e += kAlignThreads) run[e] = start[(int64_t)blockIdx.x * E + e];
-    for (int i = tid; i < 4 * E; i += kAlignThreads) wcnt[i] = 0;
     __syncthreads();
 
-    const int lo = blockIdx.x * chunk;
+    const int lo = b * chunk;
     const int hi = lo + chunk < n ? lo + chunk : n;
     for (int it = lo; it < hi; it += kAlignThreads) {
         const int s = it + tid;
@@ -139,10 +167,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         const bool ok = (unsigned)e < (unsigned)E;
         // Lanes of this wave holding the same expert: filter by each id bit.
         uint64_t peers = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(ok && bit);
-            peers &= bit ? m : ~m;
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool set = (e >> bit) & 1;
+            const uint64_t m = __ballot(ok && set);
+            peers &= set ? m : ~m;
         }
         const int rank = __popcll(peers & lanemask_lt());
         const int cnt = __popcll(peers);
@@ -186,20 +214,17 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
 
-    // With no slots the histogram is all zeros and the scan still writes
-    // zero counts and offsets.
+    // With no slots the histogram is all zeros and the scatter kernel still
+    // writes zero counts and offsets.
     hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(kAlignThreads), E * sizeof(int32_t), s,
                        ids, n, E, chunk, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t scan_lds = (size_t)(nb * E + E + kScanThreads / kWave + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, s, ws, nb, E, n,
-                       counts, offsets, sorted_tok, sorted_slot);
-    err = hipGetLastError();
-    if (err != hipSuccess || n == 0) return err;
-    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads),
-                       5 * E * sizeof(int32_t), s, ids, (int)n, k, E, (int)chunk, nbits, ws,
-                       sorted_tok, sorted_slot, slot_to_sorted);
+    const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
+    const size_t lds = (size_t)(7 * E + 2 * parts * E + kAlignThreads / kWave) * sizeof(int32_t);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
+                       k, E, (int)chunk, nbits, nb, ws, counts, offsets, sorted_tok, sorted_slot,
+                       slot_to_sorted);
     return hipGetLastError();
 }
 

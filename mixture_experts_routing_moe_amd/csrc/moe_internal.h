@@ -46,6 +46,53 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// 16-lane row reductions with DPP (VALU lane permutes, no LDS crossbar): after
+// xor-1, xor-2, half-row mirror and row mirror steps every lane of each
+// 16-lane row holds the row's result.
+// ---------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, true);
+}
+template <int ctrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = dpp_u32<ctrl>((uint32_t)u), hi = dpp_u32<ctrl>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    return v;
+}
+__device__ __forceinline__ double row16_sum_f64(double v) {
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    return v;
+}
+
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key; every finite or infinite value maps above 0).  -0.0 and +0.0 compare
+// equal as floats, so both map to the key of +0.0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // SiLU in float32: z / (1 + e^-z).
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 

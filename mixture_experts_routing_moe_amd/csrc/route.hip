@@ -1,13 +1,14 @@
-// Gating top-k + softmax weights: one wavefront per token row.
+// Gating top-k + softmax weights: 16 lanes (E <= 64, k <= 16) or a whole
+// wavefront per token row.
 //
 // Method: mlc-llm moe_misc.py, gating_topk / _gating_topk_process_value /
 // gating_softmax_topk.  The selection order is value descending with equal
 // values keeping the lower expert id first (the pages' strict-greater
 // insertion over ascending expert ids).  The pages give one thread per row
-// with a serial loop over E; here a 64-lane wave holds the row (VPL
-// consecutive experts per lane) and runs k rounds of a wave-wide argmax, so
-// the row is read once, coalesced, and every round costs six cross-lane max
-// steps plus one ballot.
+// with a serial loop over E; here lanes hold consecutive experts of a row and
+// run k rounds of a cross-lane argmax, so the row is read once, coalesced.
+// The general kernel gives a row a whole wave (VPL experts per lane); the fast
+// path packs 4 rows into a wave with 16 lanes per row and DPP reductions.
 #include "moe_internal.h"
 
 namespace moe {
@@ -88,6 +89,96 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
+// Fast path for E <= 64 and k <= 16: a wave holds 4 rows, 16 lanes per row,
+// lane q of a row holding experts 4q .. 4q+3.  Every round of the top-k is a
+// 4-step DPP max over the row's 16 lanes on an order-preserving unsigned key
+// plus one ballot; the lowest lane holding the maximum wins, which is the
+// lowest expert id among equal logits.  A second 4-step max broadcasts the
+// winner's local slot.
+__global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
+    const float *__restrict__ logits, int64_t T, int E, int k, int norm, int vec4,
+    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids) {
+    const int lane = lane_id();
+    const int g = lane >> 4;
+    const int q = lane & 15;
+    const int64_t wave = (int64_t)blockIdx.x * (kRouteThreads / kWave) + threadIdx.x / kWave;
+    const int64_t nwaves = (int64_t)gridDim.x * (kRouteThreads / kWave);
+
+    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
+        const int64_t t = t0 + g;
+        const bool row_ok = t < T;
+        float v[4];
+        uint32_t avail = 0;
+        if (row_ok && vec4) {  // E == 64 and 16-byte aligned rows
+            const float4 x = *reinterpret_cast<const float4 *>(logits + t * 64 + 4 * q);
+            v[0] = x.x;
+            v[1] = x.y;
+            v[2] = x.z;
+            v[3] = x.w;
+            avail = 0xFu;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * q + i;
+                v[i] = 0.0f;
+                if (row_ok && e < E) {
+                    v[i] = logits[t * E + e];
+                    avail |= 1u << i;
+                }
+            }
+        }
+        const uint32_t valid = avail;
+        uint32_t key[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) key[i] = float_key(v[i]);
+
+        uint32_t sel_key = 0, kmax = 0;
+        int sel_e = -1;
+        for (int r = 0; r < k; ++r) {
+            // Lane-local best; strict > keeps the lowest local slot on ties.
+            uint32_t bk = 0;
+            int bi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (((avail >> i) & 1u) && key[i] > bk) {
+                    bk = key[i];
+                    bi = i;
+                }
+            }
+            const uint32_t rmax = row16_max_u32(bk);
+            const uint64_t cand = __ballot(bk != 0 && bk == rmax);
+            const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
+            const int wl = __ffs((int)mrow) - 1;  // -1 only for rows past T
+            const bool is_w = q == wl;
+            if (is_w) avail &= ~(1u << bi);
+            const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
+            if (q == r) {
+                sel_key = rmax;
+                sel_e = wl * 4 + (int)wbi;
+            }
+            if (r == 0) kmax = rmax;
+        }
+
+        // Weights in double, rounded once to float.
+        const double mx = (double)key_float(kmax);
+        const double ex = q < k ? exp((double)key_float(sel_key) - mx) : 0.0;
+        double part;
+        if (norm) {
+            part = ex;
+        } else {
+            part = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((valid >> i) & 1u) part += exp((double)v[i] - mx);
+        }
+        const double sum = row16_sum_f64(part);
+        if (row_ok && q < k) {
+            topk_w[t * k + q] = (float)(ex / sum);
+            topk_ids[t * k + q] = sel_e;
+        }
+    }
+}
+
 template <int VPL>
 hipError_t launch_vpl(const float *logits, int64_t T, int E, int k, int norm, float *w,
                       int32_t *ids, hipStream_t s) {
@@ -104,6 +195,14 @@ hipError_t launch_vpl(const float *logits, int64_t T, int E, int k, int norm, fl
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int norm, float *w,
                         int32_t *ids, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (E <= 64 && k <= 16) {
+        int64_t blocks = (T + 15) / 16;  // 4 waves x 4 rows per block
+        if (blocks > 8192) blocks = 8192;
+        const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+        hipLaunchKernelGGL(route_rows16_kernel, dim3((unsigned)blocks), dim3(kRouteThreads), 0, s,
+                           logits, T, E, k, norm, vec4, w, ids);
+        return hipGetLastError();
+    }
     if (E <= 64) return launch_vpl<1>(logits, T, E, k, norm, w, ids, s);
     if (E <= 128) return launch_vpl<2>(logits, T, E, k, norm, w, ids, s);
     if (E <= 256) return launch_vpl<4>(logits, T, E, k, norm, w, ids, s);
