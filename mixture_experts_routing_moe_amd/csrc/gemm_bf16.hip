@@ -12,10 +12,11 @@
 // waits hide behind the other's matrix-core work) in a 4 x 2 layout, each
 // wave 64 weight rows x 128 token rows = 2 x 4 MFMA 32x32x16 bf16 tiles with
 // float32 accumulators.  Operands go from global memory straight into LDS
-// (gfx950 global_load_lds_dwordx4, no staging registers) through a ring of
-// kStages k-tiles, so each load has kStages - 1 k-tiles of matrix-core work to
-// land; 16-byte chunks are XOR-swizzled so fragment reads are bank-conflict
-// free.
+// (gfx950 global_load_lds_dwordx4, no staging registers), double buffered, the
+// next k-tile in flight while the current one feeds the matrix cores;
+// fragments are double buffered in registers and their LDS reads interleaved
+// with the MFMAs; 16-byte chunks are XOR-swizzled so fragment reads are
+// bank-conflict free.
 //
 // The weight tile is the MFMA "A" operand and the token tile the "B" operand,
 // so each lane's accumulators hold 4 consecutive output columns of one row
@@ -35,19 +36,20 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64  // k elements per LDS stage
-#endif
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 2  // LDS stages in flight
-#endif
+
 
 constexpr int BM = 256;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
-constexpr int BK = MOE_GEMM_BK;
-constexpr int kStages = MOE_GEMM_STAGES;
-constexpr int WN = 4;  // waves along the weight rows
-constexpr int WM = 2;  // waves along the token rows
+constexpr int BK = 64;   // k elements per LDS stage
+constexpr int kStages = 2;  // LDS stages (double buffer)
+#ifndef MOE_GEMM_WN
+#define MOE_GEMM_WN 4
+#endif
+#ifndef MOE_GEMM_WM
+#define MOE_GEMM_WM 2
+#endif
+constexpr int WN = MOE_GEMM_WN;  // waves along the weight rows
+constexpr int WM = MOE_GEMM_WM;  // waves along the token rows
 constexpr int kWaves = WN * WM;
 constexpr int kThreads = 64 * kWaves;
 constexpr int NF = BN / WN / 32;  // weight fragments per wave
@@ -150,57 +152,95 @@ __device__ __forceinline__ void wait_loads() {
 // completed because the MFMAs that consume it were issued before.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// One LDS stage through the matrix cores: BK / 16 k-steps, each NF weight
-// fragments x MV token fragments of MFMA 32x32x16 (one ds_read_b128 per
-// fragment: row + lr, chunk 2 ks + lk, swizzled; fragment rows start at
-// multiples of 32, so swz(row) = swz(lr)).  Token fragments MV..MF-1 hold no
-// row of the expert and are skipped entirely.
+// Fragments of one 16-wide k-step: NF weight fragments and MV token
+// fragments, one ds_read_b128 each (row + lr, 16-byte chunk 2 ks + lk,
+// swizzled; fragment rows start at multiples of 32, so swz(row) = swz(lr)).
+// Token fragments MV..MF-1 hold no row of the expert and are skipped.
 template <int MV>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[NF][MF], const uint16_t *s,
-                                          const int (&nrow)[NF], int xrow, int lr, int lk) {
+struct Frags {
+    bf16x8 w[NF], x[MV > 0 ? MV : 1];
+};
+
+template <int MV>
+__device__ __forceinline__ void load_frags(Frags<MV> &fr, const uint16_t *s, const int (&nrow)[NF],
+                                           int xrow, int lr, int ch) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ((ks * 2 + lk) ^ swz(lr)) * 8;
-        bf16x8 wf[NF], xf[MV > 0 ? MV : 1];
+    for (int f = 0; f < NF; ++f)
+        fr.w[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-            wf[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
-#pragma unroll
-        for (int g = 0; g < MV; ++g)
-            xf[g] = *reinterpret_cast<const bf16x8 *>(s + (xrow + g * 32) * BK + ch);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-            for (int g = 0; g < MV; ++g)
-                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[f], xf[g], acc[f][g], 0,
-                                                                    0, 0);
-    }
+    for (int g = 0; g < MV; ++g)
+        fr.x[g] = *reinterpret_cast<const bf16x8 *>(s + (xrow + g * 32) * BK + ch);
 }
 
-// The k loop over a ring of kStages LDS stages.  Iteration kt waits for its
-// own k-tile (the kStages - 2 newer ones may still be in flight), then one
-// barrier makes that stage visible to every wave and guarantees that every
-// wave is done with the stage of iteration kt - 1, which is refilled with
-// k-tile kt + kStages - 1 before the math starts.
+template <int MV>
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[NF][MF], const Frags<MV> &fr) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int g = 0; g < MV; ++g)
+            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.w[f], fr.x[g], acc[f][g], 0, 0,
+                                                                0);
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Order the code since the last sched_barrier as: one fragment read, then
+// NF*MV/(NF+MV) MFMAs, repeated, then the remaining MFMAs -- the reads of the
+// next k-step travel behind this k-step's matrix-core work.
+template <int MV>
+__device__ __forceinline__ void interleave() {
+    constexpr int nr = NF + MV, nm = NF * MV;
+#pragma unroll
+    for (int i = 0; i < nr; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, nm / nr > 0 ? nm / nr : 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, nm, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The k loop over two LDS stages.  Per k-tile kt (stage cur): the next
+// k-tile is issued into the other stage, then the four 16-wide k-steps run
+// with fragments double-buffered in registers (the reads for k-step ks+1 are
+// issued during the MFMAs of k-step ks).  Before the last k-step every wave
+// waits for its own loads and its LDS reads, and one barrier makes the next
+// stage visible and frees this one; the fragments of the next k-tile's first
+// k-step are then read under the last k-step's MFMAs.  The last iteration
+// re-reads its own stage instead, so the loop has a single path.
 template <int MV>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
                                        const uint16_t *const *aptr, const uint16_t *const *bptr,
                                        int nk, int row_base, const int (&nrow)[NF], int xrow,
                                        int lr, int lk) {
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < nk) issue_stage(smem + s * kStage, aptr, bptr, s * BK, row_base);
+    static_assert(BK == 64, "four 16-wide k-steps per stage");
+    const int sw = swz(lr);
+    issue_stage(smem, aptr, bptr, 0, row_base);
+    wait_loads<0>();
+    stage_barrier();
+    Frags<MV> fa, fb;
+    load_frags(fa, smem, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + kStages - 2 < nk)
-            wait_loads<(kStages - 2) * 2 * NL>();
-        else
-            wait_loads<0>();
+        uint16_t *cur = smem + (kt & 1) * kStage;
+        const bool more = kt + 1 < nk;
+        uint16_t *nxt = more ? smem + ((kt + 1) & 1) * kStage : cur;
+        if (more) issue_stage(nxt, aptr, bptr, (kt + 1) * BK, row_base);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(fb, cur, nrow, xrow, lr, ((2 + lk) ^ sw) * 8);
+        mma_frags(acc, fa);
+        interleave<MV>();
+        load_frags(fa, cur, nrow, xrow, lr, ((4 + lk) ^ sw) * 8);
+        mma_frags(acc, fb);
+        interleave<MV>();
+        load_frags(fb, cur, nrow, xrow, lr, ((6 + lk) ^ sw) * 8);
+        mma_frags(acc, fa);
+        interleave<MV>();
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         stage_barrier();
-        const int nxt = kt + kStages - 1;
-        if (nxt < nk) issue_stage(smem + (nxt % kStages) * kStage, aptr, bptr, nxt * BK, row_base);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_stage<MV>(acc, smem + (kt % kStages) * kStage, nrow, xrow, lr, lk);
-        __builtin_amdgcn_sched_barrier(0);
+        load_frags(fa, nxt, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
+        mma_frags(acc, fb);
+        interleave<MV>();
     }
 }
 
