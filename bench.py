@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--workload", default="mixtral",
                    choices=["mixtral", "finegrained", "decode1", "decode32", "routing"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy 5 times and exit: the "
+                        "known-size kernel that calibrates the HBM byte counters")
     p.add_argument("--draws", type=int, default=None,
                    help="distinct routing draws rotated over the steps (default: 32 for "
                         "decode workloads, else 1)")
@@ -111,6 +114,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": src.numel() * 4,
+                          "copy_probe_bytes_written": dst.numel() * 4}), flush=True)
+        return
 
     import mixture_experts_routing_moe_amd as moe
     import moe_inputs as mi

@@ -40,8 +40,15 @@ namespace {
 
 constexpr int BM = 256;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
-constexpr int BK = 64;   // k elements per LDS stage
-constexpr int kStages = 2;  // LDS stages (double buffer)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2
+#endif
+constexpr int BK = MOE_GEMM_BK;           // k elements per LDS stage
+constexpr int kStages = MOE_GEMM_STAGES;  // LDS stages in the ring
+constexpr int KS = BK / 16;               // 16-wide k-steps per stage
 #ifndef MOE_GEMM_WN
 #define MOE_GEMM_WN 4
 #endif
@@ -64,7 +71,10 @@ constexpr int kRowsPerWindow = 128 / BK;       // rows sharing one 256-byte bank
 static_assert(kStages * kStage * 2 <= 160 * 1024, "LDS ring exceeds 160 KB");
 static_assert(NF % 2 == 0, "gate and up fragments come in pairs");
 static_assert(MF == 4, "the k loop is dispatched on 0..4 valid token fragments");
-static_assert(BK % 16 == 0 && kChunks <= 8, "k-steps of 16, at most 8 chunks per row");
+static_assert(BK % 32 == 0 && kChunks <= 8, "an even number of 16-wide k-steps, at most 8 chunks per row");
+static_assert(kStages >= 2, "at least a double buffer");
+constexpr int kLoadsPerStage = 2 * NL;  // load instructions per lane per stage
+static_assert((kStages - 2) * kLoadsPerStage <= 63, "vmcnt holds at most 63");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -140,12 +150,6 @@ __device__ __forceinline__ void issue_stage(uint16_t *stage, const uint16_t *con
     }
 }
 
-// Wait until at most `n` load instructions of this wave are outstanding.
-template <int n>
-__device__ __forceinline__ void wait_loads() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-}
-
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also drain the loads still in flight for later stages).  Callers wait for
 // the loads they need first; every LDS read of the previous stage has
@@ -201,46 +205,68 @@ __device__ __forceinline__ void interleave() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The k loop over two LDS stages.  Per k-tile kt (stage cur): the next
-// k-tile is issued into the other stage, then the four 16-wide k-steps run
-// with fragments double-buffered in registers (the reads for k-step ks+1 are
-// issued during the MFMAs of k-step ks).  Before the last k-step every wave
-// waits for its own loads and its LDS reads, and one barrier makes the next
-// stage visible and frees this one; the fragments of the next k-tile's first
-// k-step are then read under the last k-step's MFMAs.  The last iteration
-// re-reads its own stage instead, so the loop has a single path.
+// Wait until at most `later` k-tiles' loads of this wave are in flight
+// (later <= kStages - 2, wave-uniform; negative means none) and every LDS
+// read of this wave has returned.
+template <int n>
+__device__ __forceinline__ void wait_landed(int later) {
+    if constexpr (n > 0) {
+        if (later >= n) {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(n * kLoadsPerStage) : "memory");
+            return;
+        }
+        wait_landed<n - 1>(later);
+    } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
+}
+
+// The k loop over a ring of kStages LDS stages, k-tile kt in stage
+// kt % kStages.  Before the loop k-tiles 0 .. kStages-2 are issued.  Per
+// k-tile kt: k-tile kt + kStages - 1 is issued into the stage freed by the
+// previous iteration, then the KS k-steps run with fragments double-buffered
+// in registers (the reads for k-step j+1 are issued during the MFMAs of
+// k-step j).  Before the last k-step every wave waits until k-tile kt + 1 has
+// landed (later k-tiles stay in flight) and its own LDS reads are back, and
+// one barrier makes k-tile kt + 1 visible to all waves and frees stage kt; the
+// fragments of k-tile kt + 1's first k-step are then read under the last
+// k-step's MFMAs.  The last iteration re-reads its own stage instead, so the
+// loop has a single path.
 template <int MV>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
                                        const uint16_t *const *aptr, const uint16_t *const *bptr,
                                        int nk, int row_base, const int (&nrow)[NF], int xrow,
                                        int lr, int lk) {
-    static_assert(BK == 64, "four 16-wide k-steps per stage");
     const int sw = swz(lr);
-    issue_stage(smem, aptr, bptr, 0, row_base);
-    wait_loads<0>();
+#pragma unroll
+    for (int s = 0; s + 1 < kStages; ++s)
+        if (s < nk) issue_stage(smem + s * kStage, aptr, bptr, s * BK, row_base);
+    wait_landed<kStages - 2>(min(nk - 1, kStages - 2));
     stage_barrier();
-    Frags<MV> fa, fb;
-    load_frags(fa, smem, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
+    Frags<MV> fr[2];
+    load_frags(fr[0], smem, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
+    int cs = 0;  // stage of k-tile kt
     for (int kt = 0; kt < nk; ++kt) {
-        uint16_t *cur = smem + (kt & 1) * kStage;
-        const bool more = kt + 1 < nk;
-        uint16_t *nxt = more ? smem + ((kt + 1) & 1) * kStage : cur;
-        if (more) issue_stage(nxt, aptr, bptr, (kt + 1) * BK, row_base);
+        uint16_t *cur = smem + cs * kStage;
+        if (kt + kStages - 1 < nk) {
+            const int is = cs == 0 ? kStages - 1 : cs - 1;
+            issue_stage(smem + is * kStage, aptr, bptr, (kt + kStages - 1) * BK, row_base);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(fb, cur, nrow, xrow, lr, ((2 + lk) ^ sw) * 8);
-        mma_frags(acc, fa);
-        interleave<MV>();
-        load_frags(fa, cur, nrow, xrow, lr, ((4 + lk) ^ sw) * 8);
-        mma_frags(acc, fb);
-        interleave<MV>();
-        load_frags(fb, cur, nrow, xrow, lr, ((6 + lk) ^ sw) * 8);
-        mma_frags(acc, fa);
-        interleave<MV>();
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j + 1 < KS; ++j) {
+            load_frags(fr[(j + 1) & 1], cur, nrow, xrow, lr, ((2 * (j + 1) + lk) ^ sw) * 8);
+            mma_frags(acc, fr[j & 1]);
+            interleave<MV>();
+        }
+        const int ns = cs + 1 == kStages ? 0 : cs + 1;
+        uint16_t *nxt = kt + 1 < nk ? smem + ns * kStage : cur;
+        wait_landed<kStages - 2>(min(nk - 2 - kt, kStages - 2));
         stage_barrier();
-        load_frags(fa, nxt, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
-        mma_frags(acc, fb);
+        load_frags(fr[0], nxt, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
+        mma_frags(acc, fr[(KS - 1) & 1]);
         interleave<MV>();
+        cs = ns;
     }
 }
 
