@@ -166,7 +166,8 @@ def main():
         H, I = w.H, w.I
         hidden, w13, w2 = bf(inp["hidden"]), bf(inp["w13"]), bf(inp["w2"])
         act = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-        y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+        splits = moe.moe_ffn_down_splits(moe.MOE_BF16, T, H, I, E, k, decode)
+        y = torch.empty((splits, T * k, H), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     phases = ["route", "align", "to_multihot", "to_indices"]
@@ -187,7 +188,7 @@ def main():
         elif name == "gate_up":
             moe.moe_ffn_gate_up(hidden, w13, aligned, k, decode, act)
         elif name == "down":
-            moe.moe_ffn_down(act, w2, aligned, T, k, decode, y)
+            moe.moe_ffn_down(act, w2, aligned, T, k, decode, y, splits)
         elif name == "combine":
             moe.moe_combine(y, topk_w, aligned["slot_to_sorted"], torch.bfloat16, out)
 
@@ -232,7 +233,7 @@ def main():
     cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm,
            "routing_draws": draws, "cache_flush_between_steps": flush}
     if has_ffn:
-        cfg.update({"H": w.H, "I": w.I})
+        cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())
     roofline = None
     if has_ffn and not decode:

@@ -57,10 +57,11 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 1
+#define MOE_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
 #define MOE_DECODE_MAX_T 64
+#define MOE_MAX_SPLITS 8
 
 typedef enum {
     MOE_OK = 0,
@@ -206,18 +207,32 @@ moe_status_t moe_expert_ffn_decode(moe_dtype_t dt, const void *hidden, const voi
  * moe_ffn_gate_up: act [T*k, I] in `dt`, row p = position p of the aligned
  *   order: act[p] = silu(gate) * up for token sorted_token_ids[p] and the
  *   expert whose segment holds p.  Rows p >= offsets[E] are not written.
- * moe_ffn_down:   y [T*k, H] float32: y[p] = act[p] . w2[e]^T, same rows.
- * moe_combine:    out [T, H] in `dt` from y (float32), topk_w and slot_to_sorted.
+ * moe_ffn_down:   y [splits, T*k, H] float32: the product act[p] . w2[e]^T
+ *   of the same rows with its K = I terms cut into `splits` equal slices,
+ *   plane s holding the partial sum over slice s (one plane, the whole
+ *   product, when splits = 1).  Slices let a product with few output tiles
+ *   fill every compute unit; moe_ffn_down_splits gives the count the library
+ *   uses for a shape (1 for decode and float32).  splits > 1 needs the
+ *   bfloat16 prefill path and I % (64 * splits) == 0, else
+ *   MOE_ERR_UNSUPPORTED; splits outside [1, MOE_MAX_SPLITS] is
+ *   MOE_ERR_INVALID_ARG.
+ * moe_combine:    out [T, H] in `dt` from y (float32, `splits` planes),
+ *   topk_w and slot_to_sorted: each expert row is summed over the planes in
+ *   plane order, then weighted and summed over j = 0..k-1 in float32.
  * `decode` != 0 selects the decode kernels (T <= MOE_DECODE_MAX_T).
+ * moe_expert_ffn runs the three with splits = moe_ffn_down_splits(dt, decode,
+ * ...), and its workspace holds act and the y planes.
  */
+int32_t moe_ffn_down_splits(moe_dtype_t dt, int32_t decode, int64_t T, int32_t H, int32_t I,
+                            int32_t E, int32_t k);
 moe_status_t moe_ffn_gate_up(moe_dtype_t dt, int32_t decode, const void *hidden,
                              const void *w13, const int32_t *expert_offsets,
                              const int32_t *sorted_token_ids, int64_t T, int32_t H, int32_t I,
                              int32_t E, int32_t k, void *act, void *stream);
 moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const void *w2,
                           const int32_t *expert_offsets, int64_t T, int32_t H, int32_t I,
-                          int32_t E, int32_t k, float *y, void *stream);
-moe_status_t moe_combine(moe_dtype_t dt, const float *y, const float *topk_w,
+                          int32_t E, int32_t k, int32_t splits, float *y, void *stream);
+moe_status_t moe_combine(moe_dtype_t dt, const float *y, int32_t splits, const float *topk_w,
                          const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t k,
                          void *out, void *stream);
 

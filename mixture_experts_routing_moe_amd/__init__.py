@@ -12,6 +12,7 @@ from .moe import (  # noqa: F401
     moe_expert_ffn,
     moe_expert_ffn_workspace_size,
     moe_ffn_down,
+    moe_ffn_down_splits,
     moe_ffn_gate_up,
     moe_indices_to_multihot,
     moe_layer,

@@ -24,6 +24,8 @@ MOE_BF16 = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_DECODE_MAX_T = 64
+MOE_MAX_SPLITS = 8
+MOE_VERSION = 2
 
 # name -> (restype, argtypes), mirroring include/moe.h
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -44,8 +46,10 @@ SIGNATURES = {
                                     _i32, _i32, _vp, _vp, _sz, _vp]),
     "moe_ffn_gate_up": (_st, [_st, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                               _vp]),
-    "moe_ffn_down": (_st, [_st, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
-    "moe_combine": (_st, [_st, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_ffn_down_splits": (_i32, [_st, _i32, _i64, _i32, _i32, _i32, _i32]),
+    "moe_ffn_down": (_st, [_st, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
+                           _vp]),
+    "moe_combine": (_st, [_st, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
 }
 
 _lib = None

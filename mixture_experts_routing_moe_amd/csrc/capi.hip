@@ -50,8 +50,18 @@ size_t ffn_act_bytes(moe_dtype_t dt, int64_t T, int32_t I, int32_t k) {
     const size_t es = dt == MOE_BF16 ? 2 : 4;
     return round_up((size_t)T * (size_t)k * (size_t)I * es, 256);
 }
-size_t ffn_scratch_bytes(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t k) {
-    return ffn_act_bytes(dt, T, I, k) + round_up((size_t)T * (size_t)k * (size_t)H * 4, 256);
+// K slices of the FC2 product for a prefill shape (1 for float32).
+int32_t prefill_splits(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+    if (dt != MOE_BF16 || T <= 0) return 1;
+    return moe::down_splits(T, H, I, E, k);
+}
+size_t ffn_y_bytes(int64_t T, int32_t H, int32_t k, int32_t splits) {
+    return round_up((size_t)splits * (size_t)T * (size_t)k * (size_t)H * 4, 256);
+}
+size_t ffn_scratch_bytes(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t E,
+                         int32_t k, int32_t splits) {
+    (void)E;
+    return ffn_act_bytes(dt, T, I, k) + ffn_y_bytes(T, H, k, splits);
 }
 
 moe_status_t check_ffn_dims(moe_dtype_t dt, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -159,9 +169,14 @@ moe_status_t moe_multihot_to_indices(const float *probs_in_multihot,
 
 size_t moe_expert_ffn_workspace_size(moe_dtype_t dt, int64_t T, int32_t H, int32_t I,
                                      int32_t E, int32_t k) {
-    (void)E;
-    if (T < 0 || H < 1 || I < 1 || k < 1) return 0;
-    return ffn_scratch_bytes(dt, T, H, I, k);
+    if (T < 0 || H < 1 || I < 1 || k < 1 || E < 1) return 0;
+    return ffn_scratch_bytes(dt, T, H, I, E, k, prefill_splits(dt, T, H, I, E, k));
+}
+
+int32_t moe_ffn_down_splits(moe_dtype_t dt, int32_t decode, int64_t T, int32_t H, int32_t I,
+                            int32_t E, int32_t k) {
+    if (decode || T < 0 || H < 1 || I < 1 || k < 1 || E < 1) return 1;
+    return prefill_splits(dt, T, H, I, E, k);
 }
 
 moe_status_t moe_ffn_gate_up(moe_dtype_t dt, int32_t decode, const void *hidden,
@@ -200,10 +215,16 @@ moe_status_t moe_ffn_gate_up(moe_dtype_t dt, int32_t decode, const void *hidden,
 
 moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const void *w2,
                           const int32_t *expert_offsets, int64_t T, int32_t H, int32_t I,
-                          int32_t E, int32_t k, float *y, void *stream) {
+                          int32_t E, int32_t k, int32_t splits, float *y, void *stream) {
     const char *fn = "moe_ffn_down";
     moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
     if (st != MOE_OK) return st;
+    CHECK(splits >= 1 && splits <= MOE_MAX_SPLITS, MOE_ERR_INVALID_ARG,
+          "%s: splits = %d outside [1, %d]", fn, splits, MOE_MAX_SPLITS);
+    CHECK(splits == 1 || (dt == MOE_BF16 && !decode), MOE_ERR_UNSUPPORTED,
+          "%s: K slices need the bfloat16 prefill path", fn);
+    CHECK(I % (64 * splits) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: I = %d is not a multiple of 64 * splits = %d", fn, I, 64 * splits);
     if (T == 0) return MOE_OK;
     CHECK(act && w2 && expert_offsets && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     CHECK(aligned16(act) && aligned16(w2) && aligned16(y), MOE_ERR_INVALID_ARG,
@@ -222,15 +243,17 @@ moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const
     } else {
         e = moe::launch_down_bf16(static_cast<const uint16_t *>(act),
                                   static_cast<const uint16_t *>(w2), expert_offsets, T, H, I, E,
-                                  k, y, s);
+                                  k, splits, y, s);
     }
     return hip_status(e, fn);
 }
 
-moe_status_t moe_combine(moe_dtype_t dt, const float *y, const float *topk_w,
+moe_status_t moe_combine(moe_dtype_t dt, const float *y, int32_t splits, const float *topk_w,
                          const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t k,
                          void *out, void *stream) {
     const char *fn = "moe_combine";
+    CHECK(splits >= 1 && splits <= MOE_MAX_SPLITS, MOE_ERR_INVALID_ARG,
+          "%s: splits = %d outside [1, %d]", fn, splits, MOE_MAX_SPLITS);
     CHECK(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && H >= 1, MOE_ERR_INVALID_ARG,
           "%s: bad sizes T = %lld, H = %d, k = %d", fn, (long long)T, H, k);
     CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_ARG, "%s: unknown dtype", fn);
@@ -239,7 +262,7 @@ moe_status_t moe_combine(moe_dtype_t dt, const float *y, const float *topk_w,
     CHECK(y && topk_w && slot_to_sorted && out, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     CHECK(aligned16(y) && aligned16(out), MOE_ERR_INVALID_ARG,
           "%s: y and out must be 16-byte aligned", fn);
-    return hip_status(moe::launch_combine(dt, y, topk_w, slot_to_sorted, T, H, k, out,
+    return hip_status(moe::launch_combine(dt, y, splits, topk_w, slot_to_sorted, T, H, k, out,
                                           static_cast<hipStream_t>(stream)),
                       fn);
 }
@@ -260,7 +283,8 @@ static moe_status_t expert_ffn_impl(int32_t decode, moe_dtype_t dt, const void *
     CHECK(hidden && w13 && w2 && topk_w && expert_offsets && sorted_token_ids &&
               slot_to_sorted && out,
           MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-    const size_t need = ffn_scratch_bytes(dt, T, H, I, k);
+    const int32_t splits = decode ? 1 : prefill_splits(dt, T, H, I, E, k);
+    const size_t need = ffn_scratch_bytes(dt, T, H, I, E, k, splits);
     CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
     CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
@@ -270,9 +294,9 @@ static moe_status_t expert_ffn_impl(int32_t decode, moe_dtype_t dt, const void *
     st = moe_ffn_gate_up(dt, decode, hidden, w13, expert_offsets, sorted_token_ids, T, H, I, E,
                          k, act, stream);
     if (st != MOE_OK) return st;
-    st = moe_ffn_down(dt, decode, act, w2, expert_offsets, T, H, I, E, k, y, stream);
+    st = moe_ffn_down(dt, decode, act, w2, expert_offsets, T, H, I, E, k, splits, y, stream);
     if (st != MOE_OK) return st;
-    return moe_combine(dt, y, topk_w, slot_to_sorted, T, H, k, out, stream);
+    return moe_combine(dt, y, splits, topk_w, slot_to_sorted, T, H, k, out, stream);
 }
 
 moe_status_t moe_expert_ffn(moe_dtype_t dt, const void *hidden, const void *w13,

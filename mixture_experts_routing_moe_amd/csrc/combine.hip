@@ -6,7 +6,9 @@
 // expert outputs of a token).  Instead of a scatter-add, each token row
 // gathers its k expert rows through the inverse map and sums them in slot
 // order j = 0..k-1 in float32: one rounding at the end, no atomics, the same
-// bits on every run.
+// bits on every run.  When the FC2 product was cut into K slices, y holds one
+// partial plane per slice and each expert row is first summed over the planes
+// in slice order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,11 +31,11 @@ __device__ __forceinline__ void store8(float *p, const float *f) {
     reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-// y is float32 [rows, H]; out is bf16 (uint16_t) or float32 [T, H].
+// y is float32 [splits, rows, H]; out is bf16 (uint16_t) or float32 [T, H].
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
-    const float *__restrict__ y, const float *__restrict__ w, const int32_t *__restrict__ s2s,
-    int64_t ntok, int H, int k, OutT *__restrict__ out) {
+    const float *__restrict__ y, int splits, int64_t plane, const float *__restrict__ w,
+    const int32_t *__restrict__ s2s, int64_t ntok, int H, int k, OutT *__restrict__ out) {
     for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
         for (int h = threadIdx.x * V; h < H; h += kThreads * V) {
             float acc[V];
@@ -45,7 +47,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
                 const float wj = w[t * k + j];
                 const float4 *src = reinterpret_cast<const float4 *>(y + (int64_t)p * H + h);
                 const float4 a = src[0], b = src[1];
-                const float v[V] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float v[V] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                for (int sp = 1; sp < splits; ++sp) {
+                    const float4 *q = reinterpret_cast<const float4 *>(
+                        y + sp * plane + (int64_t)p * H + h);
+                    const float4 c = q[0], d = q[1];
+                    const float u[V] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+#pragma unroll
+                    for (int i = 0; i < V; ++i) v[i] += u[i];
+                }
 #pragma unroll
                 for (int i = 0; i < V; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
             }
@@ -56,17 +66,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(moe_dtype_t dt, const float *y, const float *w,
+hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const float *w,
                           const int32_t *slot_to_sorted, int64_t T, int H, int k, void *out,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
+    const int64_t plane = T * k * H;
     const unsigned grid = (unsigned)(T < 65536 ? T : 65536);
     if (dt == MOE_BF16) {
-        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, y, w,
-                           slot_to_sorted, T, H, k, static_cast<uint16_t *>(out));
+        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, y, splits,
+                           plane, w, slot_to_sorted, T, H, k, static_cast<uint16_t *>(out));
     } else {
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kThreads), 0, s, y, w,
-                           slot_to_sorted, T, H, k, static_cast<float *>(out));
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kThreads), 0, s, y, splits,
+                           plane, w, slot_to_sorted, T, H, k, static_cast<float *>(out));
     }
     return hipGetLastError();
 }

@@ -31,6 +31,8 @@
 // expert's rows are not issued (the loop is instantiated per count of valid
 // fragments, so the hot loop carries no branches); weight rows past N are
 // clamped the same way.
+#include <cmath>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -85,9 +87,13 @@ struct MTile {
 // Tile index -> (expert, rows, n-tile).  Expert e owns mt_e = ceil(count_e /
 // BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
 // tile index, ordered n-tile-major: consecutive tiles are the expert's
-// m-tiles under one weight n-tile.  A running sum of mt_e over the experts
+// m-tiles under one weight n-tile.  With kEven the segment is dealt to the
+// m-tiles in near-equal whole fragments (1040 rows: 4 x 224 + 144) instead of
+// 4 x 256 + 16, so the tiles sharing a weight tile do similar work (measured
+// faster for FC1; FC2 keeps 256-row tiles, which measured faster there).  A running sum of mt_e over the experts
 // (64 per pass, one per lane) finds the owner.  Every wave computes the same
 // answer, so no LDS is needed.
+template <bool kEven>
 __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int n_tiles,
                           MTile &t, int &nt) {
     const int lane = lane_id();
@@ -118,14 +124,35 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             const int cn = readlane_i(cnt, src);
             const int j = L - ex * n_tiles;
             nt = j / mt;
+            const int i = j - nt * mt;
             t.e = c + src;
-            t.row0 = o0 + (j - nt * mt) * BM;
-            t.row_end = min(t.row0 + BM, o0 + cn);
-            return true;
+            // Rows per m-tile: BM, or with kEven the expert's rows dealt in
+            // equal shares rounded up to whole 32-row fragments (at most BM;
+            // never an empty tile, since q mt >= cn and q < cn / (mt - 1)
+            // whenever mt > 1).
+            const int q = kEven ? (cn + 32 * mt - 1) / (32 * mt) * 32 : BM;
+            t.row0 = o0 + min(i * q, cn);
+            t.row_end = o0 + min((i + 1) * q, cn);
+            return t.row0 < t.row_end;
         }
         carry = readlane_i(incl, kWave - 1);
     }
     return false;
+}
+
+// Total m-tiles sum_e ceil(count_e / BM) (every lane gets it).
+__device__ int count_mtiles(const int32_t *__restrict__ offsets, int E) {
+    const int lane = lane_id();
+    int total = 0;
+    for (int c = 0; c < E; c += kWave) {
+        const int e = c + lane;
+        const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+        int tiles = (cnt + BM - 1) / BM;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) tiles += __shfl_xor(tiles, o, kWave);
+        total += tiles;
+    }
+    return total;
 }
 
 // LDS layout of a stage: token rows [0, BM) then weight rows [BM, BM + BN),
@@ -272,12 +299,15 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
 
 // kGateUp: A = hidden [T, K] gathered through `gather`, W = w13 [E, 2N, K],
 //          C = act [rows, N] bf16 = silu(gate) * up.
-// else:    A = act [rows, K], W = w2 [E, N, K], C = y [rows, N] float32.
+// else:    A = act [rows, K], W = w2 [E, N, K], C = y [rows, N] float32;
+//          with ksplit > 1, K is cut into ksplit equal slices and slice s
+//          writes its partial sums to plane s of y (planes `plane` floats
+//          apart).
 template <bool kGateUp>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
-    int E, int K, int N, int n_tiles) {
+    int E, int K, int N, int n_tiles, int ksplit, int64_t plane) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStage];
 
     // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs (block b
@@ -289,10 +319,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     // are spread evenly over the XCDs.
     const int bid = blockIdx.x;
     const int slot = bid >> 3;
-    const int L = ((slot / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + slot % kXcdChunk;
+    int L = ((slot / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + slot % kXcdChunk;
+    // K slices are enumerated slice-major, so the tiles an XCD runs together
+    // belong to one slice and still share operands.
+    int ks = 0;
+    if (ksplit > 1) {
+        const int total = count_mtiles(offsets, E) * n_tiles;
+        ks = L / total;
+        if (ks >= ksplit) return;
+        L -= ks * total;
+    }
     MTile tile;
     int nt;
-    if (!find_tile(offsets, E, L, n_tiles, tile, nt)) return;
+    if (!find_tile<kGateUp>(offsets, E, L, n_tiles, tile, nt)) return;
+    const int kper = K / ksplit;  // a multiple of BK (checked by the host)
+    const int kbeg = ks * kper;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -311,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         const int p = min(tile.row0 + r, tile.row_end - 1);
         const int arow = kGateUp ? gather[p] : p;
-        aptr[i] = A + (int64_t)arow * K + c8;
+        aptr[i] = A + (int64_t)arow * K + kbeg + c8;
         int wrow;
         if (kGateUp) {
             const int n = min(nt * (BN / 2) + (r & (BN / 2 - 1)), N - 1);
@@ -319,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         } else {
             wrow = min(nt * BN + r, N - 1);
         }
-        bptr[i] = W + ((int64_t)tile.e * (kGateUp ? 2 * N : N) + wrow) * K + c8;
+        bptr[i] = W + ((int64_t)tile.e * (kGateUp ? 2 * N : N) + wrow) * K + kbeg + c8;
     }
 
     f32x16 acc[NF][MF];
@@ -347,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     // Token fragments of this wave that hold at least one row of the expert
     // (wave-uniform); a wave with none still takes part in loads and barriers.
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
-    const int nk = K / BK;
+    const int nk = kper / BK;
     switch (mvalid) {
         case 4: k_loop<4>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
         case 3: k_loop<3>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
@@ -392,7 +433,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
                     const int n = nt * BN + wn * (BN / WN) + f * 32 + rg * 8 + lk * 4;
                     if (n >= N) continue;
                     const f32x16 &a = acc[f][g];
-                    *reinterpret_cast<float4 *>(static_cast<float *>(Cv) + (int64_t)p * N + n) =
+                    *reinterpret_cast<float4 *>(static_cast<float *>(Cv) + ks * plane +
+                                                (int64_t)p * N + n) =
                         make_float4(a[rg * 4], a[rg * 4 + 1], a[rg * 4 + 2], a[rg * 4 + 3]);
                 }
             }
@@ -424,18 +466,44 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
     const int n_tiles = (I + BN / 2 - 1) / (BN / 2);
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(grid_of(m_slots, n_tiles)),
                        dim3(kThreads), 0, s, hidden, sorted_tok, w13, offsets, act, E, H, I,
-                       n_tiles);
+                       n_tiles, 1, (int64_t)0);
     return hipGetLastError();
 }
 
+int down_splits(int64_t T, int H, int I, int E, int k) {
+    // Expected tiles: every full BM rows plus about half a partial m-tile per
+    // expert that has rows.  A slice count is worth its extra y plane (written
+    // here, read again by the combine: measured at about 8% of the FC2 time
+    // each on the Mixtral-shaped layer) when it fills the last round of 256
+    // CUs better; slices keep K / ksplit >= 1024 and a multiple of BK.
+    const int64_t rows = T * k;
+    if (rows == 0) return 1;
+    const int64_t nz = rows < E ? rows : E;
+    const double tiles = (double)((rows + BM - 1) / BM + nz / 2) * ((H + BN - 1) / BN);
+    int best = 1;
+    double best_score = 0.0;
+    for (int sp = 1; sp <= 4; ++sp) {
+        if (sp > 1 && (I % (sp * BK) != 0 || I / sp < 1024)) continue;
+        const double rounds = tiles * sp / 256.0;
+        const double score = rounds / std::ceil(rounds) - 0.08 * (sp - 1);
+        if (score > best_score + 1e-9) {
+            best_score = score;
+            best = sp;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32_t *offsets,
-                            int64_t T, int H, int I, int E, int k, float *y, hipStream_t s) {
+                            int64_t T, int H, int I, int E, int k, int ksplit, float *y,
+                            hipStream_t s) {
     const int64_t rows = T * k;
     if (rows == 0) return hipSuccess;
     const int m_slots = m_slot_bound(rows, E);
     const int n_tiles = (H + BN - 1) / BN;
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(grid_of(m_slots, n_tiles)),
-                       dim3(kThreads), 0, s, act, nullptr, w2, offsets, y, E, I, H, n_tiles);
+    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>,
+                       dim3(grid_of(m_slots * ksplit, n_tiles)), dim3(kThreads), 0, s, act,
+                       nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H);
     return hipGetLastError();
 }
 

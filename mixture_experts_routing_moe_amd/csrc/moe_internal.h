@@ -116,7 +116,10 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
                                const int32_t *offsets, const int32_t *sorted_tok, int64_t T,
                                int H, int I, int E, int k, uint16_t *act, hipStream_t s);
 hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32_t *offsets,
-                            int64_t T, int H, int I, int E, int k, float *y, hipStream_t s);
+                            int64_t T, int H, int I, int E, int k, int ksplit, float *y,
+                            hipStream_t s);
+// K slices the prefill FC2 uses for this shape (1 .. 4).
+int down_splits(int64_t T, int H, int I, int E, int k);
 
 hipError_t launch_gate_up_f32(const float *hidden, const float *w13, const int32_t *offsets,
                               const int32_t *sorted_tok, int64_t T, int H, int I, int E, int k,
@@ -132,7 +135,7 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
                                    const int32_t *offsets, int64_t T, int H, int I, int E, int k,
                                    float *y, hipStream_t s);
 
-hipError_t launch_combine(moe_dtype_t dt, const float *y, const float *w,
+hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const float *w,
                           const int32_t *slot_to_sorted, int64_t T, int H, int k, void *out,
                           hipStream_t s);
 

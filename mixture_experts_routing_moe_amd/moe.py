@@ -175,29 +175,50 @@ def moe_ffn_gate_up(hidden, w13, aligned: dict, k: int, decode: bool = False, ac
     return act
 
 
-def moe_ffn_down(act, w2, aligned: dict, T: int, k: int, decode: bool = False, y=None):
-    """y [T*k, H] float32 in the aligned order."""
+def moe_ffn_down_splits(dtype: int, T: int, H: int, I: int, E: int, k: int,
+                        decode: bool = False) -> int:
+    """K slices the library uses for the FC2 product of this shape."""
+    return int(lib().moe_ffn_down_splits(dtype, int(decode), T, H, I, E, k))
+
+
+def moe_ffn_down(act, w2, aligned: dict, T: int, k: int, decode: bool = False, y=None,
+                 splits: int | None = None):
+    """y float32 in the aligned order: [T*k, H] for one K slice, else [splits, T*k, H]
+    partial planes (summed by moe_combine).  splits defaults to the library's choice
+    (moe_ffn_down_splits), or to what an explicit y's shape holds."""
     E, H, I = w2.shape
+    dt = _dtype_code(act)
+    if splits is None:
+        if y is not None:
+            splits = y.shape[0] if y.dim() == 3 else 1
+        else:
+            splits = moe_ffn_down_splits(dt, T, H, I, E, k, decode)
     if y is None:
-        y = torch.empty((T * k, H), dtype=torch.float32, device=act.device)
+        shape = (T * k, H) if splits == 1 else (splits, T * k, H)
+        y = torch.empty(shape, dtype=torch.float32, device=act.device)
+    if y.numel() != splits * T * k * H:
+        raise ValueError(f"y holds {y.numel()} floats, need {splits} x {T * k} x {H}")
     _dev(act, w2, y, aligned["offsets"])
-    check(lib().moe_ffn_down(_dtype_code(act), int(decode), _ptr(act), _ptr(w2),
-                             _ptr(aligned["offsets"]), T, H, I, E, k, _ptr(y), _stream()),
-          "moe_ffn_down")
+    check(lib().moe_ffn_down(dt, int(decode), _ptr(act), _ptr(w2), _ptr(aligned["offsets"]), T,
+                             H, I, E, k, splits, _ptr(y), _stream()), "moe_ffn_down")
     return y
 
 
 def moe_combine(y, topk_w, slot_to_sorted, out_dtype=torch.bfloat16, out=None):
-    """out [T, H] = sum_j topk_w[t, j] * y[slot_to_sorted[t*k + j]] (y float32)."""
+    """out [T, H] = sum_j topk_w[t, j] * (sum_s y[s, slot_to_sorted[t*k + j]]) (y float32,
+    [T*k, H] or [splits, T*k, H])."""
     if y.dtype != torch.float32:
         raise ValueError("y must be float32")
     T, k = topk_w.shape
-    H = y.shape[1]
+    splits = y.shape[0] if y.dim() == 3 else 1
+    H = y.shape[-1]
+    if y.shape[-2] != T * k:
+        raise ValueError("y must have T*k rows per plane")
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y.device)
     _dev(y, topk_w, slot_to_sorted, out)
-    check(lib().moe_combine(_dtype_code(out), _ptr(y), _ptr(topk_w), _ptr(slot_to_sorted), T, H,
-                            k, _ptr(out), _stream()), "moe_combine")
+    check(lib().moe_combine(_dtype_code(out), _ptr(y), splits, _ptr(topk_w), _ptr(slot_to_sorted),
+                            T, H, k, _ptr(out), _stream()), "moe_combine")
     return out
 
 

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_version() == 1
+    assert lib.moe_version() == 2
     for s in range(5):
         assert lib.moe_status_string(s)
     assert lib.moe_status_string(99) == b"unknown status"
@@ -122,10 +122,47 @@ def test_ffn_validation(lib):
     # misaligned act for a phase call
     assert status(lib, "moe_ffn_gate_up", bf, 0, FAKE, FAKE, FAKE, FAKE, 16, 128, 128, 8, 2,
                   ctypes.c_void_p(0x1002), None) == _lib.MOE_ERR_INVALID_ARG
-    assert status(lib, "moe_combine", bf, FAKE, FAKE, FAKE, 4, 100, 2, FAKE,
+    assert status(lib, "moe_combine", bf, FAKE, 1, FAKE, FAKE, 4, 100, 2, FAKE,
                   None) == _lib.MOE_ERR_UNSUPPORTED
     assert status(lib, "moe_expert_ffn", bf, None, None, None, None, None, None, None, 0, 128,
                   128, 8, 2, None, None, 0, None) == _lib.MOE_OK  # T = 0
+
+
+def test_down_splits(lib):
+    bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
+    f = lib.moe_ffn_down_splits
+    # Mixtral-shaped FC2: 36 x 16 = 576 expected tiles fill 2.25 rounds of
+    # 256 CUs; two K slices of 7168 make 4.5 rounds, and more slices cost
+    # more in y traffic than they save.
+    assert f(bf, 0, 4096, 4096, 14336, 8, 2) == 2
+    # Fine-grained FC2: ~2300 tiles already fill the chip; K = 1408 is too
+    # short to cut.
+    assert f(bf, 0, 8192, 2048, 1408, 64, 8) == 1
+    assert f(f32, 0, 4096, 4096, 14336, 8, 2) == 1
+    assert f(bf, 1, 32, 2048, 1408, 64, 8) == 1
+    for T in (1, 7, 100, 1000, 5000, 20000):
+        for I in (1408, 4096, 14336):
+            sp = f(bf, 0, T, 4096, I, 8, 2)
+            assert 1 <= sp <= _lib.MOE_MAX_SPLITS and I % (64 * sp) == 0
+    # the one-call workspace holds act plus every y plane
+    n1 = lib.moe_expert_ffn_workspace_size(bf, 8192, 2048, 1408, 64, 8)
+    assert n1 >= 65536 * (1408 * 2 + 2048 * 4)
+    n2 = lib.moe_expert_ffn_workspace_size(bf, 4096, 4096, 14336, 8, 2)
+    assert n2 >= 8192 * 14336 * 2 + 2 * 8192 * 4096 * 4
+
+
+def test_down_split_validation(lib):
+    bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
+    a = (FAKE, FAKE, FAKE, 16, 128, 256, 8, 2)
+    assert status(lib, "moe_ffn_down", bf, 0, *a, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, "moe_ffn_down", bf, 0, *a, _lib.MOE_MAX_SPLITS + 1, FAKE,
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    # I = 256 cuts into at most 4 slices of 64
+    assert status(lib, "moe_ffn_down", bf, 0, *a, 8, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert status(lib, "moe_ffn_down", bf, 1, *a, 2, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert status(lib, "moe_ffn_down", f32, 0, *a, 2, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert status(lib, "moe_combine", bf, FAKE, 0, FAKE, FAKE, 4, 128, 2, FAKE,
+                  None) == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_last_error_is_thread_local(lib):

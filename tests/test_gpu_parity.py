@@ -360,6 +360,35 @@ def test_decode_layer_full_size(name):
     np.testing.assert_allclose(got, got_prefill, rtol=0, atol=2e-2 * np.sqrt(np.mean(got ** 2)))
 
 
+@pytest.mark.parametrize("T,H,I,E,k,skew", [(700, 256, 1024, 8, 2, 0.0),
+                                            (300, 512, 2048, 16, 4, 1.0)])
+def test_ffn_bf16_down_k_slices(T, H, I, E, k, skew):
+    """FC2 cut into K slices: the planes sum to the one-slice product (up to
+    float32 reassociation), the combined output meets the oracle bar, and
+    the result is the same on every run."""
+    x, w13, w2, w32, ids = _rand_layer(T + 11 * I, T, H, I, E, k, skew=skew)
+    xd, w13d, w2d, twd = dev_bf16(x), dev_bf16(w13), dev_bf16(w2), dev(w32)
+    a = moe.moe_align(dev(ids), E)
+    act = moe.moe_ffn_gate_up(xd, w13d, a, k)
+    y1 = moe.moe_ffn_down(act, w2d, a, T, k, splits=1)
+    ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "bf16")
+    rows = int(a["offsets"][-1])
+    base = y1[:rows].double()
+    scale = float(base.pow(2).mean().sqrt())
+    for sp in (2, 4):
+        y = moe.moe_ffn_down(act, w2d, a, T, k, splits=sp)
+        assert y.shape == (sp, T * k, H)
+        err = float((y[:, :rows].double().sum(0) - base).abs().max())
+        assert err <= 1e-5 * scale, f"{sp} slices: {err:.3e} vs rms {scale:.3e}"
+        out = moe.moe_combine(y, twd, a["slot_to_sorted"], torch.bfloat16)
+        out32 = moe.moe_combine(y, twd, a["slot_to_sorted"], torch.float32)
+        again = moe.moe_combine(moe.moe_ffn_down(act, w2d, a, T, k, splits=sp), twd,
+                                a["slot_to_sorted"], torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out32, again)
+        assert_bf16_layer(host(out), host(out32), ref)
+
+
 def test_layer_deterministic():
     x, w13, w2, w32, ids = _rand_layer(9, 700, 256, 256, 16, 4, skew=0.5)
     a, a32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
