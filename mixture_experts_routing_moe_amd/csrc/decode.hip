@@ -15,6 +15,17 @@
 // share of the weight rows up front and feed MFMA 16x16x32 bf16 (weights as
 // the A operand, up to 4 chunks of 16 tokens as B).  The 4 partial
 // accumulators are summed through LDS.
+//
+// Weight loads come in pairs of k-steps.  The MFMA A operand of one k-step
+// gives each of 16 rows 64 bytes (4 lanes x 16), so loading it directly
+// makes every instruction touch 16 half cache lines; instead, instruction P
+// reads rows 0-7 and instruction Q rows 8-15, each row's whole 128-byte line
+// of the pair (lane i of a 16-lane row reads row i & 7, half i >> 3).  The
+// two k-steps' operands are then rebuilt in registers: lanes i < 8 take P
+// for the first k-step and lane i ^ 8's P for the second, lanes i >= 8 take
+// lane i ^ 8's Q for the first and Q for the second (one DPP row rotate by 8
+// and a select per dword).  Measured on the part: whole-line reads stream
+// from HBM about 25 % faster than half-line reads of the same bytes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,16 +67,33 @@ __device__ __forceinline__ bf16x8 ld_stream(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
 }
 
-// Each wave owns a contiguous quarter of the k range of the block's weight
-// rows and issues every load of a batch of kBatch MFMA k-steps (weights and
+// Each wave owns a contiguous quarter of the k-step pairs of the block's
+// weight rows and issues every load of a batch of kPairs pairs (weights and
 // token fragments) before the first MFMA of the batch, so each lane keeps
-// kBatch x 16 bytes per weight row group in flight (these kernels are bound
-// by the bytes in flight).  k-steps past the wave's range load a clamped
-// address and multiply a zeroed fragment, so the math carries no branches.
-constexpr int kBatch = 8;
+// kPairs x 32 bytes per weight row group in flight (these kernels are bound
+// by HBM).  Pairs past the wave's range load a clamped address and multiply
+// a zeroed fragment, so the math carries no branches.
+constexpr int kPairs = 4;
 
 __device__ __forceinline__ bf16x8 zero_unless(bool keep, bf16x8 v) {
     return keep ? v : bf16x8{};
+}
+
+// The A operands of k-steps 2p and 2p+1 from the paired loads P (rows 0-7)
+// and Q (rows 8-15); `lo` = this lane's row is below 8.
+__device__ __forceinline__ void unpair(bool lo, const bf16x8 &P, const bf16x8 &Q, bf16x8 &a0,
+                                       bf16x8 &a1) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 p = __builtin_bit_cast(u32x4, P), q = __builtin_bit_cast(u32x4, Q);
+    u32x4 r0, r1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t pr = dpp_u32<kDppRor8>(p[d]), qr = dpp_u32<kDppRor8>(q[d]);
+        r0[d] = lo ? p[d] : qr;
+        r1[d] = lo ? pr : q[d];
+    }
+    a0 = __builtin_bit_cast(bf16x8, r0);
+    a1 = __builtin_bit_cast(bf16x8, r1);
 }
 
 // FC1 + SiLU-and-mul.  act[p, n] for n in this block's 16 rows and every
@@ -84,8 +112,13 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
     const int kq = lane >> 4;
     const int n0 = blockIdx.x * kRows;
 
-    const uint16_t *wg = w13 + ((int64_t)e * 2 * I + n0 + i) * H + kq * 8;
-    const uint16_t *wu = wg + (int64_t)I * H;
+    // Paired-load addresses: row (i & 7) of the gate (up) rows 0-7 for P,
+    // 8 rows further for Q, half (i >> 3) of each 128-byte line.
+    const bool lo = i < 8;
+    const uint16_t *wgP = w13 + ((int64_t)e * 2 * I + n0 + (i & 7)) * H + (i >> 3) * 32 + kq * 8;
+    const uint16_t *wgQ = wgP + (int64_t)8 * H;
+    const uint16_t *wuP = wgP + (int64_t)I * H;
+    const uint16_t *wuQ = wuP + (int64_t)8 * H;
     const uint16_t *xr[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
@@ -99,30 +132,40 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
         ag[mc] = f32x4{};
         au[mc] = f32x4{};
     }
-    const int nks = H / 32;
-    const int per = (nks + 3) / 4;
-    const int s0 = wave * per;
-    const int s1 = min(nks, s0 + per);
-    for (int b = s0; b < s1; b += kBatch) {
-        bf16x8 g[kBatch], u[kBatch], x[MC][kBatch];
+    const int npairs = H / 64;
+    const int per = (npairs + 3) / 4;
+    const int p0 = wave * per;
+    const int p1 = min(npairs, p0 + per);
+    for (int b = p0; b < p1; b += kPairs) {
+        bf16x8 gP[kPairs], gQ[kPairs], uP[kPairs], uQ[kPairs], x[MC][2 * kPairs];
 #pragma unroll
-        for (int s = 0; s < kBatch; ++s) {
-            const int k0 = min(b + s, nks - 1) * 32;
-            g[s] = ld_stream(wg + k0);
-            u[s] = ld_stream(wu + k0);
+        for (int q = 0; q < kPairs; ++q) {
+            const int k0 = min(b + q, npairs - 1) * 64;
+            gP[q] = ld_stream(wgP + k0);
+            gQ[q] = ld_stream(wgQ + k0);
+            uP[q] = ld_stream(wuP + k0);
+            uQ[q] = ld_stream(wuQ + k0);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
-                x[mc][s] = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
+            for (int mc = 0; mc < MC; ++mc) {
+                x[mc][2 * q] = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
+                x[mc][2 * q + 1] = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0 + 32);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < kBatch; ++s) {
-            const bool in = b + s < s1;
-            const bf16x8 gs = zero_unless(in, g[s]), us = zero_unless(in, u[s]);
+        for (int q = 0; q < kPairs; ++q) {
+            const bool in = b + q < p1;
+            bf16x8 g0, g1, u0, u1;
+            unpair(lo, zero_unless(in, gP[q]), zero_unless(in, gQ[q]), g0, g1);
+            unpair(lo, zero_unless(in, uP[q]), zero_unless(in, uQ[q]), u0, u1);
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc) {
-                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gs, x[mc][s], ag[mc], 0, 0, 0);
-                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(us, x[mc][s], au[mc], 0, 0, 0);
+                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g0, x[mc][2 * q], ag[mc], 0, 0, 0);
+                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u0, x[mc][2 * q], au[mc], 0, 0, 0);
+                ag[mc] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(g1, x[mc][2 * q + 1], ag[mc], 0, 0, 0);
+                au[mc] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(u1, x[mc][2 * q + 1], au[mc], 0, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -170,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const int kq = lane >> 4;
     const int h0 = blockIdx.x * kRows;
 
-    const uint16_t *wr = w2 + ((int64_t)e * H + h0 + i) * I + kq * 8;
+    const bool lo = i < 8;
+    const uint16_t *wP = w2 + ((int64_t)e * H + h0 + (i & 7)) * I + (i >> 3) * 32 + kq * 8;
+    const uint16_t *wQ = wP + (int64_t)8 * I;
     const uint16_t *ar[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
@@ -180,27 +225,35 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     f32x4 acc[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{};
-    const int nks = I / 32;
-    const int per = (nks + 3) / 4;
-    const int s0 = wave * per;
-    const int s1 = min(nks, s0 + per);
-    for (int b = s0; b < s1; b += kBatch) {
-        bf16x8 wv[kBatch], x[MC][kBatch];
+    const int npairs = I / 64;
+    const int per = (npairs + 3) / 4;
+    const int p0 = wave * per;
+    const int p1 = min(npairs, p0 + per);
+    for (int b = p0; b < p1; b += kPairs) {
+        bf16x8 wPv[kPairs], wQv[kPairs], x[MC][2 * kPairs];
 #pragma unroll
-        for (int s = 0; s < kBatch; ++s) {
-            const int k0 = min(b + s, nks - 1) * 32;
-            wv[s] = ld_stream(wr + k0);
+        for (int q = 0; q < kPairs; ++q) {
+            const int k0 = min(b + q, npairs - 1) * 64;
+            wPv[q] = ld_stream(wP + k0);
+            wQv[q] = ld_stream(wQ + k0);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
-                x[mc][s] = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
+            for (int mc = 0; mc < MC; ++mc) {
+                x[mc][2 * q] = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
+                x[mc][2 * q + 1] = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0 + 32);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < kBatch; ++s) {
-            const bf16x8 ws = zero_unless(b + s < s1, wv[s]);
+        for (int q = 0; q < kPairs; ++q) {
+            const bool in = b + q < p1;
+            bf16x8 w0, w1;
+            unpair(lo, zero_unless(in, wPv[q]), zero_unless(in, wQv[q]), w0, w1);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
-                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws, x[mc][s], acc[mc], 0, 0, 0);
+            for (int mc = 0; mc < MC; ++mc) {
+                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x[mc][2 * q], acc[mc], 0, 0, 0);
+                acc[mc] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x[mc][2 * q + 1], acc[mc], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }

@@ -55,6 +55,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
+constexpr int kDppRor8 = 0x128;       // row_ror:8 (lane i of a row reads lane i ^ 8)
 
 template <int ctrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
