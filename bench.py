@@ -42,6 +42,10 @@ def parse():
     p.add_argument("--workload", default="mixtral",
                    choices=["mixtral", "finegrained", "decode1", "decode32", "routing"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", type=int, default=None,
+                   help="1: time the whole step as one captured HIP graph replay (the "
+                        "per-phase breakdown still comes from eager launches); default 1 "
+                        "for decode workloads, whose steps are launch-bound, else 0")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy 5 times and exit: the "
                         "known-size kernel that calibrates the HBM byte counters")
@@ -140,6 +144,7 @@ def main():
     decode = w.name.startswith("decode")
     draws = args.draws if args.draws is not None else (32 if decode else 1)
     flush = bool(args.flush if args.flush is not None else decode)
+    use_graph = bool(args.graph if args.graph is not None else decode)
     logits_draws = [torch.from_numpy(inp["logits"] if r == 0 else mi.gating_logits_draw(w, r))
                     .to(dev) for r in range(draws)]
     flush_buf = torch.empty(128 << 20, dtype=torch.float32, device=dev) if flush else None
@@ -213,6 +218,41 @@ def main():
             ev[s][i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    graph_ms = None
+    if use_graph:
+        # The same step captured once and replayed: the input logits live in
+        # one static buffer that each routing draw is copied into before its
+        # replay (outside the timed events, like the cache flush).
+        static_logits = torch.empty_like(logits_draws[0])
+        static_logits.copy_(logits_draws[0])
+        cur["logits"] = static_logits
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for ph in phases:
+                run_phase(ph)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for ph in phases:
+                run_phase(ph)
+        for it in range(args.warmup):
+            static_logits.copy_(logits_draws[it % draws])
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for st in range(args.steps):
+            static_logits.copy_(logits_draws[st % draws])
+            if flush:
+                flush_buf.fill_(float(st))
+            gev[st][0].record()
+            graph.replay()
+            gev[st][1].record()
+        torch.cuda.synchronize()
+        graph_ms = sum(a.elapsed_time(b) for a, b in gev) / args.steps
+
     if decode:
         # Distinct experts per routing draw (outside the timed region).
         for r in range(min(draws, args.steps)):
@@ -223,15 +263,17 @@ def main():
 
     phase_ms = {ph: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) /
                 args.steps for i, ph in enumerate(phases)}
-    if flush:
-        # The cache flush between steps is not part of the layer.
-        ms_per_step = sum(phase_ms.values())
-    else:
-        ms_per_step = wall * 1e3 / args.steps
+    eager_ms = sum(phase_ms.values()) if flush else wall * 1e3 / args.steps
+    # With a cache flush between steps the wall clock would include it, so the
+    # step time is then the sum of the event-timed phases (or the graph
+    # replay, bracketed by its own events).
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = T * 1e3 / ms_per_step
 
     cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm,
-           "routing_draws": draws, "cache_flush_between_steps": flush}
+           "routing_draws": draws, "cache_flush_between_steps": flush,
+           "step_timing": "hip_graph_replay" if graph_ms is not None else "eager",
+           "eager_ms_per_step": round(eager_ms, 4)}
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())

@@ -395,3 +395,71 @@ def test_layer_deterministic():
     b, b32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
     np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
     np.testing.assert_array_equal(a32.view(np.uint32), b32.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# One layer step captured as a HIP graph (the library allocates, syncs and
+# memsets nothing, so every call is capturable)
+# --------------------------------------------------------------------------
+
+def _layer_into(bufs, logits, x, w13, w2, k, decode):
+    T, E = logits.shape
+    moe.moe_route(logits, k, True, bufs["tw"], bufs["ids"])
+    moe.moe_align(bufs["ids"], E, bufs["aligned"], bufs["ws"])
+    moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
+    moe.moe_ffn_down(bufs["act"], w2, bufs["aligned"], T, k, decode, bufs["y"])
+    moe.moe_combine(bufs["y"], bufs["tw"], bufs["aligned"]["slot_to_sorted"], torch.bfloat16,
+                    bufs["out"])
+
+
+def _layer_bufs(T, H, I, E, k, decode):
+    sp = moe.moe_ffn_down_splits(moe.MOE_BF16, T, H, I, E, k, decode)
+    return {
+        "tw": torch.empty((T, k), dtype=torch.float32, device=DEV),
+        "ids": torch.empty((T, k), dtype=torch.int32, device=DEV),
+        "aligned": {n: torch.empty(m, dtype=torch.int32, device=DEV) for n, m in
+                    (("counts", E), ("offsets", E + 1), ("sorted_token_ids", T * k),
+                     ("sorted_slot_ids", T * k), ("slot_to_sorted", T * k))},
+        "ws": torch.empty(max(1, moe.moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                          device=DEV),
+        "act": torch.empty((T * k, I), dtype=torch.bfloat16, device=DEV),
+        "y": torch.empty((sp, T * k, H), dtype=torch.float32, device=DEV),
+        "out": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+    }
+
+
+@pytest.mark.parametrize("T,H,I,E,k,decode", [(1, 256, 256, 16, 4, True),
+                                              (32, 512, 384, 64, 8, True),
+                                              (300, 256, 2048, 8, 2, False)])
+def test_layer_graph_replay(T, H, I, E, k, decode):
+    """Replays of a captured step, with other GPU work between them, equal
+    eager runs of the same step bit for bit, for several inputs."""
+    x, w13, w2, _, _ = _rand_layer(T * 3 + I, T, H, I, E, k)
+    xd, w13d, w2d = dev_bf16(x), dev_bf16(w13), dev_bf16(w2)
+    g = np.random.Generator(np.random.PCG64(T + E))
+    draws = [dev(g.standard_normal((T, E)).astype(np.float32)) for _ in range(4)]
+    static = torch.empty_like(draws[0])
+    static.copy_(draws[0])
+    bufs = _layer_bufs(T, H, I, E, k, decode)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _layer_into(bufs, static, xd, w13d, w2d, k, decode)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _layer_into(bufs, static, xd, w13d, w2d, k, decode)
+    eager = _layer_bufs(T, H, I, E, k, decode)
+    for r in (1, 2, 0, 3, 1):
+        static.copy_(draws[r])
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bufs["out"].clone()
+        got_ids = bufs["ids"].clone()
+        # unrelated eager work, then the eager step on the same input
+        torch.matmul(xd.float(), xd.float().t()).sum().item()
+        _layer_into(eager, draws[r], xd, w13d, w2d, k, decode)
+        torch.cuda.synchronize()
+        assert torch.equal(got_ids, eager["ids"])
+        assert torch.equal(got.view(torch.int16), eager["out"].view(torch.int16))
