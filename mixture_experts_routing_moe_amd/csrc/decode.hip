@@ -199,8 +199,9 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
 }
 
 // FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p
-// of the expert's segment.
-template <int MC>
+// of the expert's segment.  KP pairs per batch: 6 for up to 32 tokens (one
+// batch covers each wave's share of k = 1408), 4 for more.
+template <int MC, int KP>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
     const int32_t *__restrict__ offsets, int H, int I, int E, float *__restrict__ y) {
@@ -229,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const int per = (npairs + 3) / 4;
     const int p0 = wave * per;
     const int p1 = min(npairs, p0 + per);
-    for (int b = p0; b < p1; b += kPairs) {
-        bf16x8 wPv[kPairs], wQv[kPairs], x[MC][2 * kPairs];
+    for (int b = p0; b < p1; b += KP) {
+        bf16x8 wPv[KP], wQv[KP], x[MC][2 * KP];
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
+        for (int q = 0; q < KP; ++q) {
             const int k0 = min(b + q, npairs - 1) * 64;
             wPv[q] = ld_stream(wP + k0);
             wQv[q] = ld_stream(wQ + k0);
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
+        for (int q = 0; q < KP; ++q) {
             const bool in = b + q < p1;
             bf16x8 w0, w1;
             unpair(lo, zero_unless(in, wPv[q]), zero_unless(in, wQv[q]), w0, w1);
@@ -315,15 +316,15 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
     const dim3 grid(H / kRows, expert_rows(T, E, k));
     switch (token_chunks(T)) {
         case 1:
-            hipLaunchKernelGGL(decode_down_kernel<1>, grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<1, 6>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
         case 2:
-            hipLaunchKernelGGL(decode_down_kernel<2>, grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<2, 6>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
         default:
-            hipLaunchKernelGGL(decode_down_kernel<4>, grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<4, 4>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
     }
