@@ -32,6 +32,7 @@
 // fragments, so the hot loop carries no branches); weight rows past N are
 // clamped the same way.
 #include <cmath>
+#include <cstdlib>
 
 #include "moe_internal.h"
 
@@ -163,17 +164,50 @@ __device__ int count_mtiles(const int32_t *__restrict__ offsets, int E) {
 // swz must differ across them: swz(r) = (r / kRowsPerWindow) % kChunks.
 __device__ __forceinline__ int swz(int r) { return (r / kRowsPerWindow) % kChunks; }
 
-// Issue one k-tile of both operands straight into an LDS stage
-// (global_load_lds_dwordx4: lane L's 16 bytes land at base + 16 L, i.e. row
-// L / kChunks, position L % kChunks of the instruction's rows).
-__device__ __forceinline__ void issue_stage(uint16_t *stage, const uint16_t *const *aptr,
-                                            const uint16_t *const *bptr, int k0, int row_base) {
+// Operand addressing.  kBuf: a buffer resource per operand (scalar
+// registers), a 32-bit byte offset per lane and row, and the k position as the
+// scalar offset, so issuing a k-tile's loads takes no vector arithmetic (the
+// load path measured 2-8 % faster than with 64-bit per-lane pointers).  It
+// needs each operand under 2^31 bytes; larger ones take the pointer path.
+template <bool kBuf>
+struct Ops;
+template <>
+struct Ops<true> {
+    __amdgpu_buffer_rsrc_t a, b;  // token / weight operand (this expert)
+    int kb;                       // first k of this K slice
+    uint32_t aoff[NL], boff[NL];  // byte offsets of this lane's rows and chunk
+};
+template <>
+struct Ops<false> {
+    const uint16_t *a[NL], *b[NL];  // this lane's rows and chunk, from the slice's first k
+};
+
+// Buffer resource word 3 for raw (unstructured) buffer access on gfx9-class
+// parts: 32-bit data format, no swizzle or index stride.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Issue one k-tile of both operands straight into an LDS stage (global /
+// buffer load to LDS, 16 bytes per lane: lane L's bytes land at base + 16 L,
+// i.e. row L / kChunks, position L % kChunks of the instruction's rows).
+__device__ __forceinline__ void issue_stage(uint16_t *stage, const Ops<true> &op, int k0,
+                                            int row_base) {
+    const uint32_t so = 2u * (uint32_t)(op.kb + k0);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         uint16_t *da = stage + (row_base + i * kRowsPerLoad) * BK;
         uint16_t *db = stage + (BM + row_base + i * kRowsPerLoad) * BK;
-        __builtin_amdgcn_global_load_lds(aptr[i] + k0, (lds_void *)da, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(bptr[i] + k0, (lds_void *)db, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], so, 0, 0);
+    }
+}
+__device__ __forceinline__ void issue_stage(uint16_t *stage, const Ops<false> &op, int k0,
+                                            int row_base) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        uint16_t *da = stage + (row_base + i * kRowsPerLoad) * BK;
+        uint16_t *db = stage + (BM + row_base + i * kRowsPerLoad) * BK;
+        __builtin_amdgcn_global_load_lds(op.a[i] + k0, (lds_void *)da, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(op.b[i] + k0, (lds_void *)db, 16, 0, 0);
     }
 }
 
@@ -259,15 +293,14 @@ __device__ __forceinline__ void wait_landed(int later) {
 // fragments of k-tile kt + 1's first k-step are then read under the last
 // k-step's MFMAs.  The last iteration re-reads its own stage instead, so the
 // loop has a single path.
-template <int MV>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
-                                       const uint16_t *const *aptr, const uint16_t *const *bptr,
+template <int MV, bool kBuf>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const Ops<kBuf> &op,
                                        int nk, int row_base, const int (&nrow)[NF], int xrow,
                                        int lr, int lk) {
     const int sw = swz(lr);
 #pragma unroll
     for (int s = 0; s + 1 < kStages; ++s)
-        if (s < nk) issue_stage(smem + s * kStage, aptr, bptr, s * BK, row_base);
+        if (s < nk) issue_stage(smem + s * kStage, op, s * BK, row_base);
     wait_landed<kStages - 2>(min(nk - 1, kStages - 2));
     stage_barrier();
     Frags<MV> fr[2];
@@ -277,7 +310,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
         uint16_t *cur = smem + cs * kStage;
         if (kt + kStages - 1 < nk) {
             const int is = cs == 0 ? kStages - 1 : cs - 1;
-            issue_stage(smem + is * kStage, aptr, bptr, (kt + kStages - 1) * BK, row_base);
+            issue_stage(smem + is * kStage, op, (kt + kStages - 1) * BK, row_base);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -303,11 +336,14 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem,
 //          with ksplit > 1, K is cut into ksplit equal slices and slice s
 //          writes its partial sums to plane s of y (planes `plane` floats
 //          apart).
-template <bool kGateUp>
+//
+// kBuf selects the operand addressing (Ops); a_bytes is the token operand's
+// size in bytes (used by kBuf only).
+template <bool kGateUp, bool kBuf>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
-    int E, int K, int N, int n_tiles, int ksplit, int64_t plane) {
+    int E, int K, int N, int n_tiles, int ksplit, int64_t plane, int a_bytes) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStage];
 
     // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs (block b
@@ -341,18 +377,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 
     // Operand rows this lane loads: row row_base + kRowsPerLoad i + lane /
     // kChunks of each tile; it lands at position lane % kChunks, so it fetches
-    // global chunk (lane % kChunks) ^ swz(row) of that row.
-    const int row_base = wave * kRowsPerWave;
+    // global chunk (lane % kChunks) ^ swz(row) of that row.  The wave index is
+    // made scalar so the LDS destinations (M0) need no per-load conversion.
+    const int row_base = __builtin_amdgcn_readfirstlane(wave) * kRowsPerWave;
     const int rr = lane / kChunks;
-    const uint16_t *aptr[NL];
-    const uint16_t *bptr[NL];
+    const int rows_w = kGateUp ? 2 * N : N;
+    const uint16_t *We = W + (int64_t)tile.e * rows_w * K;
+    Ops<kBuf> op;
+    if constexpr (kBuf) {
+        op.a = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, a_bytes, kBufferWord3);
+        op.b = __builtin_amdgcn_make_buffer_rsrc((void *)We, (short)0, rows_w * K * 2,
+                                                 kBufferWord3);
+        op.kb = __builtin_amdgcn_readfirstlane(kbeg);
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int r = row_base + i * kRowsPerLoad + rr;
         const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         const int p = min(tile.row0 + r, tile.row_end - 1);
         const int arow = kGateUp ? gather[p] : p;
-        aptr[i] = A + (int64_t)arow * K + kbeg + c8;
         int wrow;
         if (kGateUp) {
             const int n = min(nt * (BN / 2) + (r & (BN / 2 - 1)), N - 1);
@@ -360,7 +403,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         } else {
             wrow = min(nt * BN + r, N - 1);
         }
-        bptr[i] = W + ((int64_t)tile.e * (kGateUp ? 2 * N : N) + wrow) * K + kbeg + c8;
+        if constexpr (kBuf) {
+            op.aoff[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)c8) * 2u;
+            op.boff[i] = ((uint32_t)wrow * (uint32_t)K + (uint32_t)c8) * 2u;
+        } else {
+            op.a[i] = A + (int64_t)arow * K + kbeg + c8;
+            op.b[i] = We + (int64_t)wrow * K + kbeg + c8;
+        }
     }
 
     f32x16 acc[NF][MF];
@@ -390,11 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     const int nk = kper / BK;
     switch (mvalid) {
-        case 4: k_loop<4>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
-        case 3: k_loop<3>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
-        case 2: k_loop<2>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
-        case 1: k_loop<1>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
-        default: k_loop<0>(acc, smem, aptr, bptr, nk, row_base, nrow, xrow, lr, lk); break;
+        case 4: k_loop<4>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
+        case 3: k_loop<3>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
+        case 2: k_loop<2>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
+        case 1: k_loop<1>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
+        default: k_loop<0>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
     }
 
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
@@ -457,6 +506,16 @@ unsigned grid_of(int m_slots, int n_tiles) {
 
 }  // namespace
 
+// The buffer-addressed kernels need every operand byte offset to fit in a
+// signed 32-bit value.  MOE_GEMM_POINTER_PATH=1 in the environment forces the
+// 64-bit pointer path (tests use it to cover that path at small sizes).
+bool use_buffer_path(int64_t a_bytes, int64_t w_bytes) {
+    const char *v = std::getenv("MOE_GEMM_POINTER_PATH");  // read per launch (host only)
+    const bool forced = v != nullptr && v[0] == '1';
+    const int64_t lim = (int64_t)1 << 31;
+    return !forced && a_bytes < lim && w_bytes < lim;
+}
+
 hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
                                const int32_t *offsets, const int32_t *sorted_tok, int64_t T,
                                int H, int I, int E, int k, uint16_t *act, hipStream_t s) {
@@ -464,9 +523,16 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
     if (rows == 0) return hipSuccess;
     const int m_slots = m_slot_bound(rows, E);
     const int n_tiles = (I + BN / 2 - 1) / (BN / 2);
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(grid_of(m_slots, n_tiles)),
-                       dim3(kThreads), 0, s, hidden, sorted_tok, w13, offsets, act, E, H, I,
-                       n_tiles, 1, (int64_t)0);
+    const int64_t a_bytes = T * H * 2, w_bytes = (int64_t)2 * I * H * 2;
+    const dim3 grid(grid_of(m_slots, n_tiles));
+    if (use_buffer_path(a_bytes, w_bytes))
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s,
+                           hidden, sorted_tok, w13, offsets, act, E, H, I, n_tiles, 1, (int64_t)0,
+                           (int)a_bytes);
+    else
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s,
+                           hidden, sorted_tok, w13, offsets, act, E, H, I, n_tiles, 1, (int64_t)0,
+                           0);
     return hipGetLastError();
 }
 
@@ -501,9 +567,15 @@ hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32
     if (rows == 0) return hipSuccess;
     const int m_slots = m_slot_bound(rows, E);
     const int n_tiles = (H + BN - 1) / BN;
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>,
-                       dim3(grid_of(m_slots * ksplit, n_tiles)), dim3(kThreads), 0, s, act,
-                       nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H);
+    const int64_t a_bytes = rows * I * 2, w_bytes = (int64_t)H * I * 2;
+    const dim3 grid(grid_of(m_slots * ksplit, n_tiles));
+    if (use_buffer_path(a_bytes, w_bytes))
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s,
+                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H,
+                           (int)a_bytes);
+    else
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s,
+                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H, 0);
     return hipGetLastError();
 }
 

@@ -360,6 +360,22 @@ def test_decode_layer_full_size(name):
     np.testing.assert_allclose(got, got_prefill, rtol=0, atol=2e-2 * np.sqrt(np.mean(got ** 2)))
 
 
+@pytest.mark.parametrize("T,H,I,E,k,skew,inv", [(300, 128, 192, 8, 2, 0.0, 0.0),
+                                                (513, 512, 384, 64, 8, 0.3, 0.0),
+                                                (260, 192, 256, 12, 3, 0.0, 0.2)])
+def test_ffn_bf16_prefill_pointer_path(monkeypatch, T, H, I, E, k, skew, inv):
+    """The grouped GEMMs' 64-bit pointer path (taken for operands of 2 GiB or
+    more; forced here) against the oracle, and equal to the default path."""
+    x, w13, w2, w32, ids = _rand_layer(T + H + I + E, T, H, I, E, k, skew=skew, inv=inv)
+    base, base32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
+    monkeypatch.setenv("MOE_GEMM_POINTER_PATH", "1")
+    out, out32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16")
+    monkeypatch.delenv("MOE_GEMM_POINTER_PATH")
+    ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "bf16")
+    assert_bf16_layer(out, out32, ref)
+    np.testing.assert_array_equal(out32.view(np.uint32), base32.view(np.uint32))
+
+
 @pytest.mark.parametrize("T,H,I,E,k,skew", [(700, 256, 1024, 8, 2, 0.0),
                                             (300, 512, 2048, 16, 4, 1.0)])
 def test_ffn_bf16_down_k_slices(T, H, I, E, k, skew):
