@@ -43,15 +43,8 @@ namespace {
 
 constexpr int BM = 256;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 2
-#endif
-constexpr int BK = MOE_GEMM_BK;           // k elements per LDS stage
-constexpr int kStages = MOE_GEMM_STAGES;  // LDS stages in the ring
-constexpr int KS = BK / 16;               // 16-wide k-steps per stage
+constexpr int BK = 64;   // k elements per LDS stage (two stages)
+constexpr int KS = BK / 16;  // 16-wide k-steps per stage
 #ifndef MOE_GEMM_WN
 #define MOE_GEMM_WN 4
 #endif
@@ -65,19 +58,22 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int NF = BN / WN / 32;  // weight fragments per wave
 constexpr int MF = BM / WM / 32;  // token fragments per wave
 constexpr int kXcdChunk = 32;  // CUs per XCD: tiles an XCD runs at once
-constexpr int kStage = (BM + BN) * BK;         // bf16 elements per LDS stage
+// LDS: the two token stages, then the two weight stages, so every fragment
+// address is a per-lane base plus a constant below 64 KiB (the ds_read offset
+// field).
+constexpr int kTokStage = BM * BK;          // bf16 elements per token stage
+constexpr int kWStage = BN * BK;            // bf16 elements per weight stage
+constexpr int kWOff = 2 * kTokStage;        // first weight stage
+constexpr int kLds = kWOff + 2 * kWStage;   // bf16 elements in all
 constexpr int kChunks = BK / 8;                // 16-byte chunks per row
 constexpr int kRowsPerLoad = 64 / kChunks;     // rows one wave instruction fills
 constexpr int kRowsPerWave = BM / kWaves;      // rows each wave loads per tile
 constexpr int NL = kRowsPerWave / kRowsPerLoad;  // load instructions per tile per wave
 constexpr int kRowsPerWindow = 128 / BK;       // rows sharing one 256-byte bank window
-static_assert(kStages * kStage * 2 <= 160 * 1024, "LDS ring exceeds 160 KB");
+static_assert(kLds * 2 <= 160 * 1024, "LDS exceeds 160 KB");
 static_assert(NF % 2 == 0, "gate and up fragments come in pairs");
 static_assert(MF == 4, "the k loop is dispatched on 0..4 valid token fragments");
-static_assert(BK % 32 == 0 && kChunks <= 8, "an even number of 16-wide k-steps, at most 8 chunks per row");
-static_assert(kStages >= 2, "at least a double buffer");
-constexpr int kLoadsPerStage = 2 * NL;  // load instructions per lane per stage
-static_assert((kStages - 2) * kLoadsPerStage <= 63, "vmcnt holds at most 63");
+static_assert(BM == BN, "token and weight stages have the same shape");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -189,23 +185,25 @@ constexpr int kBufferWord3 = 0x00020000;
 // Issue one k-tile of both operands straight into an LDS stage (global /
 // buffer load to LDS, 16 bytes per lane: lane L's bytes land at base + 16 L,
 // i.e. row L / kChunks, position L % kChunks of the instruction's rows).
-__device__ __forceinline__ void issue_stage(uint16_t *stage, const Ops<true> &op, int k0,
+template <int S>
+__device__ __forceinline__ void issue_stage(uint16_t *smem, const Ops<true> &op, int k0,
                                             int row_base) {
     const uint32_t so = 2u * (uint32_t)(op.kb + k0);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        uint16_t *da = stage + (row_base + i * kRowsPerLoad) * BK;
-        uint16_t *db = stage + (BM + row_base + i * kRowsPerLoad) * BK;
+        uint16_t *da = smem + S * kTokStage + (row_base + i * kRowsPerLoad) * BK;
+        uint16_t *db = smem + kWOff + S * kWStage + (row_base + i * kRowsPerLoad) * BK;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], so, 0, 0);
     }
 }
-__device__ __forceinline__ void issue_stage(uint16_t *stage, const Ops<false> &op, int k0,
+template <int S>
+__device__ __forceinline__ void issue_stage(uint16_t *smem, const Ops<false> &op, int k0,
                                             int row_base) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        uint16_t *da = stage + (row_base + i * kRowsPerLoad) * BK;
-        uint16_t *db = stage + (BM + row_base + i * kRowsPerLoad) * BK;
+        uint16_t *da = smem + S * kTokStage + (row_base + i * kRowsPerLoad) * BK;
+        uint16_t *db = smem + kWOff + S * kWStage + (row_base + i * kRowsPerLoad) * BK;
         __builtin_amdgcn_global_load_lds(op.a[i] + k0, (lds_void *)da, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(op.b[i] + k0, (lds_void *)db, 16, 0, 0);
     }
@@ -226,15 +224,29 @@ struct Frags {
     bf16x8 w[NF], x[MV > 0 ? MV : 1];
 };
 
-template <int MV>
-__device__ __forceinline__ void load_frags(Frags<MV> &fr, const uint16_t *s, const int (&nrow)[NF],
-                                           int xrow, int lr, int ch) {
+// Per-lane byte addresses in LDS of this lane's first weight and token
+// fragment rows at k-step j of stage 0; the stage, the fragment and the
+// weight half are compile-time offsets on top.
+struct FragAddr {
+    uint32_t w[KS], x[KS];
+};
+
+// Row of weight fragment f within the wave's rows: FC1 holds gate fragments
+// then the matching up fragments BN/2 rows further.
+template <bool kGateUp>
+constexpr int frag_row(int f) {
+    return kGateUp ? (f < NF / 2 ? 0 : BN / 2) + (f % (NF / 2)) * 32 : f * 32;
+}
+
+template <int S, int J, int MV, bool kGateUp>
+__device__ __forceinline__ void load_frags(Frags<MV> &fr, const char *lds, const FragAddr &fa) {
 #pragma unroll
     for (int f = 0; f < NF; ++f)
-        fr.w[f] = *reinterpret_cast<const bf16x8 *>(s + (BM + nrow[f] + lr) * BK + ch);
+        fr.w[f] = *reinterpret_cast<const bf16x8 *>(
+            lds + fa.w[J] + (S * kWStage + frag_row<kGateUp>(f) * BK) * 2);
 #pragma unroll
     for (int g = 0; g < MV; ++g)
-        fr.x[g] = *reinterpret_cast<const bf16x8 *>(s + (xrow + g * 32) * BK + ch);
+        fr.x[g] = *reinterpret_cast<const bf16x8 *>(lds + fa.x[J] + (S * kTokStage + g * 32 * BK) * 2);
 }
 
 template <int MV>
@@ -266,68 +278,53 @@ __device__ __forceinline__ void interleave() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Wait until at most `later` k-tiles' loads of this wave are in flight
-// (later <= kStages - 2, wave-uniform; negative means none) and every LDS
-// read of this wave has returned.
-template <int n>
-__device__ __forceinline__ void wait_landed(int later) {
-    if constexpr (n > 0) {
-        if (later >= n) {
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(n * kLoadsPerStage) : "memory");
-            return;
-        }
-        wait_landed<n - 1>(later);
-    } else {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    }
+// Half of the k loop: k-tile kt from stage S.  k-tile kt + 1 is issued into
+// the other stage (freed by the previous half's barrier), then the KS k-steps
+// run with fragments double-buffered in registers (the reads for k-step j+1
+// are issued during the MFMAs of k-step j).  Before the last k-step every wave
+// waits for its own loads and LDS reads, and one barrier makes k-tile kt + 1
+// visible to all waves and frees stage S; the fragments of k-tile kt + 1's
+// first k-step are then read from the other stage under the last k-step's
+// MFMAs (after the last k-tile that stage holds stale data nobody uses).
+// Stage indices are compile-time, so the loop computes no addresses.
+template <int S, int MV, bool kGateUp, typename OpsT>
+__device__ __forceinline__ void k_half(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
+                                       const OpsT &op, int kt, int nk, int row_base,
+                                       const FragAddr &fa) {
+    const char *lds = reinterpret_cast<const char *>(smem);
+    if (kt + 1 < nk) issue_stage<1 - S>(smem, op, (kt + 1) * BK, row_base);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<S, 1, MV, kGateUp>(fr[1], lds, fa);
+    mma_frags(acc, fr[0]);
+    interleave<MV>();
+    load_frags<S, 2, MV, kGateUp>(fr[0], lds, fa);
+    mma_frags(acc, fr[1]);
+    interleave<MV>();
+    load_frags<S, 3, MV, kGateUp>(fr[1], lds, fa);
+    mma_frags(acc, fr[0]);
+    interleave<MV>();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    load_frags<1 - S, 0, MV, kGateUp>(fr[0], lds, fa);
+    mma_frags(acc, fr[1]);
+    interleave<MV>();
 }
 
-// The k loop over a ring of kStages LDS stages, k-tile kt in stage
-// kt % kStages.  Before the loop k-tiles 0 .. kStages-2 are issued.  Per
-// k-tile kt: k-tile kt + kStages - 1 is issued into the stage freed by the
-// previous iteration, then the KS k-steps run with fragments double-buffered
-// in registers (the reads for k-step j+1 are issued during the MFMAs of
-// k-step j).  Before the last k-step every wave waits until k-tile kt + 1 has
-// landed (later k-tiles stay in flight) and its own LDS reads are back, and
-// one barrier makes k-tile kt + 1 visible to all waves and frees stage kt; the
-// fragments of k-tile kt + 1's first k-step are then read under the last
-// k-step's MFMAs.  The last iteration re-reads its own stage instead, so the
-// loop has a single path.
-template <int MV, bool kBuf>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const Ops<kBuf> &op,
-                                       int nk, int row_base, const int (&nrow)[NF], int xrow,
-                                       int lr, int lk) {
-    const int sw = swz(lr);
-#pragma unroll
-    for (int s = 0; s + 1 < kStages; ++s)
-        if (s < nk) issue_stage(smem + s * kStage, op, s * BK, row_base);
-    wait_landed<kStages - 2>(min(nk - 1, kStages - 2));
+template <int MV, bool kGateUp, typename OpsT>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const OpsT &op,
+                                       int nk, int row_base, const FragAddr &fa) {
+    static_assert(KS == 4, "four 16-wide k-steps per stage");
+    issue_stage<0>(smem, op, 0, row_base);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     stage_barrier();
     Frags<MV> fr[2];
-    load_frags(fr[0], smem, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
-    int cs = 0;  // stage of k-tile kt
-    for (int kt = 0; kt < nk; ++kt) {
-        uint16_t *cur = smem + cs * kStage;
-        if (kt + kStages - 1 < nk) {
-            const int is = cs == 0 ? kStages - 1 : cs - 1;
-            issue_stage(smem + is * kStage, op, (kt + kStages - 1) * BK, row_base);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j + 1 < KS; ++j) {
-            load_frags(fr[(j + 1) & 1], cur, nrow, xrow, lr, ((2 * (j + 1) + lk) ^ sw) * 8);
-            mma_frags(acc, fr[j & 1]);
-            interleave<MV>();
-        }
-        const int ns = cs + 1 == kStages ? 0 : cs + 1;
-        uint16_t *nxt = kt + 1 < nk ? smem + ns * kStage : cur;
-        wait_landed<kStages - 2>(min(nk - 2 - kt, kStages - 2));
-        stage_barrier();
-        load_frags(fr[0], nxt, nrow, xrow, lr, ((0 + lk) ^ sw) * 8);
-        mma_frags(acc, fr[(KS - 1) & 1]);
-        interleave<MV>();
-        cs = ns;
+    load_frags<0, 0, MV, kGateUp>(fr[0], reinterpret_cast<const char *>(smem), fa);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        k_half<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
+        k_half<1, MV, kGateUp>(acc, fr, smem, op, kt + 1, nk, row_base, fa);
     }
+    if (kt < nk) k_half<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
 }
 
 // kGateUp: A = hidden [T, K] gathered through `gather`, W = w13 [E, 2N, K],
@@ -344,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
     int E, int K, int N, int n_tiles, int ksplit, int64_t plane, int a_bytes) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStage];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
 
     // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs (block b
     // runs on XCD b % 8), and each XCD has 32 CUs.  Tiles are handed out in
@@ -422,28 +419,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int wm = wave / WN;
     const int lr = lane & 31;
     const int lk = lane >> 5;
-    // LDS rows (within the weight tile) of this wave's weight fragments.  For
-    // FC1 the first NF/2 are gate rows and the rest the matching up rows.
-    int nrow[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        if (kGateUp)
-            nrow[f] = (f < NF / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (f % (NF / 2)) * 32;
-        else
-            nrow[f] = wn * (BN / WN) + f * 32;
-    }
+    // LDS byte addresses of this lane's fragment rows at each k-step of stage
+    // 0: weight row wn * (rows per wave) + lr (FC1: of the gate half), token
+    // row wm * (BM / WM) + lr, 16-byte chunk 2 j + lk swizzled.
+    const int sw = swz(lr);
+    const int wrow0 = kGateUp ? wn * (BN / 2 / WN) : wn * (BN / WN);
     const int xrow = wm * (BM / WM) + lr;
+    FragAddr fa;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const uint32_t ch = (uint32_t)(((2 * j + lk) ^ sw) * 16);
+        fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
+        fa.x[j] = (uint32_t)(xrow * BK * 2) + ch;
+    }
 
     // Token fragments of this wave that hold at least one row of the expert
     // (wave-uniform); a wave with none still takes part in loads and barriers.
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     const int nk = kper / BK;
     switch (mvalid) {
-        case 4: k_loop<4>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
-        case 3: k_loop<3>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
-        case 2: k_loop<2>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
-        case 1: k_loop<1>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
-        default: k_loop<0>(acc, smem, op, nk, row_base, nrow, xrow, lr, lk); break;
+        case 4: k_loop<4, kGateUp>(acc, smem, op, nk, row_base, fa); break;
+        case 3: k_loop<3, kGateUp>(acc, smem, op, nk, row_base, fa); break;
+        case 2: k_loop<2, kGateUp>(acc, smem, op, nk, row_base, fa); break;
+        case 1: k_loop<1, kGateUp>(acc, smem, op, nk, row_base, fa); break;
+        default: k_loop<0, kGateUp>(acc, smem, op, nk, row_base, fa); break;
     }
 
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
