@@ -43,8 +43,15 @@ namespace {
 
 constexpr int BM = 256;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
-constexpr int BK = 64;   // k elements per LDS stage (two stages)
-constexpr int KS = BK / 16;  // 16-wide k-steps per stage
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2
+#endif
+constexpr int BK = MOE_GEMM_BK;           // k elements per LDS stage
+constexpr int NS = MOE_GEMM_STAGES;       // LDS stages in the ring
+constexpr int KS = BK / 16;               // 16-wide k-steps per stage
 #ifndef MOE_GEMM_WN
 #define MOE_GEMM_WN 4
 #endif
@@ -58,13 +65,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int NF = BN / WN / 32;  // weight fragments per wave
 constexpr int MF = BM / WM / 32;  // token fragments per wave
 constexpr int kXcdChunk = 32;  // CUs per XCD: tiles an XCD runs at once
-// LDS: the two token stages, then the two weight stages, so every fragment
+// LDS: the NS token stages, then the NS weight stages, so every fragment
 // address is a per-lane base plus a constant below 64 KiB (the ds_read offset
 // field).
 constexpr int kTokStage = BM * BK;          // bf16 elements per token stage
 constexpr int kWStage = BN * BK;            // bf16 elements per weight stage
-constexpr int kWOff = 2 * kTokStage;        // first weight stage
-constexpr int kLds = kWOff + 2 * kWStage;   // bf16 elements in all
+constexpr int kWOff = NS * kTokStage;       // first weight stage
+constexpr int kLds = kWOff + NS * kWStage;  // bf16 elements in all
 constexpr int kChunks = BK / 8;                // 16-byte chunks per row
 constexpr int kRowsPerLoad = 64 / kChunks;     // rows one wave instruction fills
 constexpr int kRowsPerWave = BM / kWaves;      // rows each wave loads per tile
@@ -74,6 +81,10 @@ static_assert(kLds * 2 <= 160 * 1024, "LDS exceeds 160 KB");
 static_assert(NF % 2 == 0, "gate and up fragments come in pairs");
 static_assert(MF == 4, "the k loop is dispatched on 0..4 valid token fragments");
 static_assert(BM == BN, "token and weight stages have the same shape");
+static_assert(NS >= 2 && KS % 2 == 0, "a ring of at least two stages, an even count of k-steps");
+static_assert(((NS - 1) * kWStage + BN * BK) * 2 <= 65536, "fragment offsets fit the ds_read field");
+constexpr int kLoadsPerStage = 2 * NL;  // load instructions per lane per stage
+static_assert((NS - 2) * kLoadsPerStage <= 63, "vmcnt holds at most 63");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -278,53 +289,94 @@ __device__ __forceinline__ void interleave() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Half of the k loop: k-tile kt from stage S.  k-tile kt + 1 is issued into
-// the other stage (freed by the previous half's barrier), then the KS k-steps
-// run with fragments double-buffered in registers (the reads for k-step j+1
-// are issued during the MFMAs of k-step j).  Before the last k-step every wave
-// waits for its own loads and LDS reads, and one barrier makes k-tile kt + 1
-// visible to all waves and frees stage S; the fragments of k-tile kt + 1's
-// first k-step are then read from the other stage under the last k-step's
-// MFMAs (after the last k-tile that stage holds stale data nobody uses).
-// Stage indices are compile-time, so the loop computes no addresses.
+// Wait until at most `later` k-tiles' loads of this wave are in flight
+// (0 <= later <= NS - 2, wave-uniform; negative means none) and every LDS
+// read of this wave has returned.
+template <int n>
+__device__ __forceinline__ void wait_landed(int later) {
+    if constexpr (n > 0) {
+        if (later >= n) {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(n * kLoadsPerStage) : "memory");
+            return;
+        }
+        wait_landed<n - 1>(later);
+    } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
+}
+
+// k-steps 1 .. KS-1 of stage S but the last: the reads for k-step j+1 are
+// issued during the MFMAs of k-step j (fragments double-buffered).
+template <int S, int J, int MV, bool kGateUp>
+__device__ __forceinline__ void k_steps(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], const char *lds,
+                                        const FragAddr &fa) {
+    if constexpr (J + 1 < KS) {
+        load_frags<S, J + 1, MV, kGateUp>(fr[(J + 1) & 1], lds, fa);
+        mma_frags(acc, fr[J & 1]);
+        interleave<MV>();
+        k_steps<S, J + 1, MV, kGateUp>(acc, fr, lds, fa);
+    }
+}
+
+// One k-tile of the k loop: k-tile kt from stage S.  k-tile kt + NS - 1 is
+// issued into the stage freed by the previous k-tile's barrier, then the KS
+// k-steps run; before the last k-step every wave waits until k-tile kt + 1
+// has landed (later k-tiles stay in flight) and its own LDS reads are back,
+// and one barrier makes k-tile kt + 1 visible to all waves and frees stage S;
+// the fragments of k-tile kt + 1's first k-step are then read from its stage
+// under the last k-step's MFMAs (after the last k-tile that stage holds data
+// nobody uses).  Stage indices are compile-time, so the loop computes no
+// addresses.
 template <int S, int MV, bool kGateUp, typename OpsT>
-__device__ __forceinline__ void k_half(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
+__device__ __forceinline__ void k_tile(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
                                        const OpsT &op, int kt, int nk, int row_base,
                                        const FragAddr &fa) {
     const char *lds = reinterpret_cast<const char *>(smem);
-    if (kt + 1 < nk) issue_stage<1 - S>(smem, op, (kt + 1) * BK, row_base);
+    if (kt + NS - 1 < nk) issue_stage<(S + NS - 1) % NS>(smem, op, (kt + NS - 1) * BK, row_base);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags<S, 1, MV, kGateUp>(fr[1], lds, fa);
-    mma_frags(acc, fr[0]);
-    interleave<MV>();
-    load_frags<S, 2, MV, kGateUp>(fr[0], lds, fa);
-    mma_frags(acc, fr[1]);
-    interleave<MV>();
-    load_frags<S, 3, MV, kGateUp>(fr[1], lds, fa);
-    mma_frags(acc, fr[0]);
-    interleave<MV>();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    k_steps<S, 0, MV, kGateUp>(acc, fr, lds, fa);
+    wait_landed<NS - 2>(min(nk - 2 - kt, NS - 2));
     stage_barrier();
-    load_frags<1 - S, 0, MV, kGateUp>(fr[0], lds, fa);
-    mma_frags(acc, fr[1]);
+    load_frags<(S + 1) % NS, 0, MV, kGateUp>(fr[0], lds, fa);
+    mma_frags(acc, fr[(KS - 1) & 1]);
     interleave<MV>();
+}
+
+template <int S, int MV, bool kGateUp, typename OpsT>
+__device__ __forceinline__ void k_tiles(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
+                                        const OpsT &op, int kt, int nk, int row_base,
+                                        const FragAddr &fa) {
+    if constexpr (S < NS) {
+        if (kt < nk) {
+            k_tile<S, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
+            k_tiles<S + 1, MV, kGateUp>(acc, fr, smem, op, kt + 1, nk, row_base, fa);
+        }
+    }
+}
+
+template <int S, bool kBuf>
+__device__ __forceinline__ void issue_first(uint16_t *smem, const Ops<kBuf> &op, int nk,
+                                            int row_base) {
+    if constexpr (S + 1 < NS) {
+        if (S < nk) issue_stage<S>(smem, op, S * BK, row_base);
+        issue_first<S + 1>(smem, op, nk, row_base);
+    }
 }
 
 template <int MV, bool kGateUp, typename OpsT>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const OpsT &op,
                                        int nk, int row_base, const FragAddr &fa) {
-    static_assert(KS == 4, "four 16-wide k-steps per stage");
-    issue_stage<0>(smem, op, 0, row_base);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue_first<0>(smem, op, nk, row_base);
+    wait_landed<NS - 2>(min(nk - 1, NS - 2));
     stage_barrier();
     Frags<MV> fr[2];
     load_frags<0, 0, MV, kGateUp>(fr[0], reinterpret_cast<const char *>(smem), fa);
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        k_half<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
-        k_half<1, MV, kGateUp>(acc, fr, smem, op, kt + 1, nk, row_base, fa);
-    }
-    if (kt < nk) k_half<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
+    // Whole rounds of the ring with every stage index a constant, then the
+    // remaining k-tiles.
+    for (; kt + NS <= nk; kt += NS)
+        k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
+    k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
 }
 
 // kGateUp: A = hidden [T, K] gathered through `gather`, W = w13 [E, 2N, K],
