@@ -379,6 +379,68 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
     k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
 }
 
+// The k loop and the epilogue of one tile whose waves hold MV valid token
+// fragments.  Each MV has its accumulators to itself: declared outside the
+// dispatch on MV, one set shared by the five loop versions measured slower
+// (the register allocator copies it between them).
+template <int MV, bool kGateUp, typename OpsT>
+__device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int row_base,
+                                         const FragAddr &fa, const MTile &tile, int nt, int wn,
+                                         int wm, int lr, int lk, int N, int ks, int64_t plane,
+                                         void *__restrict__ Cv) {
+    f32x16 acc[NF][MF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int g = 0; g < MF; ++g) acc[f][g] = f32x16{};
+
+    k_loop<MV, kGateUp>(acc, smem, op, nk, row_base, fa);
+
+    // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
+    // the weight side and column lr of the token side.
+    const int prow = tile.row0 + wm * (BM / WM) + lr;
+    if (kGateUp) {
+#pragma unroll
+        for (int f = 0; f < NF / 2; ++f) {
+#pragma unroll
+            for (int g = 0; g < MV; ++g) {
+                const int p = prow + g * 32;
+                if (p >= tile.row_end) continue;
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int n = nt * (BN / 2) + wn * (BN / 2 / WN) + f * 32 + rg * 8 + lk * 4;
+                    if (n >= N) continue;
+                    bf16x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = to_bf16(silu_f(acc[f][g][rg * 4 + q]) *
+                                       acc[f + NF / 2][g][rg * 4 + q]);
+                    *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(Cv) + (int64_t)p * N +
+                                                n) = o;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+#pragma unroll
+            for (int g = 0; g < MV; ++g) {
+                const int p = prow + g * 32;
+                if (p >= tile.row_end) continue;
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int n = nt * BN + wn * (BN / WN) + f * 32 + rg * 8 + lk * 4;
+                    if (n >= N) continue;
+                    const f32x16 &a = acc[f][g];
+                    *reinterpret_cast<float4 *>(static_cast<float *>(Cv) + ks * plane +
+                                                (int64_t)p * N + n) =
+                        make_float4(a[rg * 4], a[rg * 4 + 1], a[rg * 4 + 2], a[rg * 4 + 3]);
+                }
+            }
+        }
+    }
+}
+
 // kGateUp: A = hidden [T, K] gathered through `gather`, W = w13 [E, 2N, K],
 //          C = act [rows, N] bf16 = silu(gate) * up.
 // else:    A = act [rows, K], W = w2 [E, N, K], C = y [rows, N] float32;
@@ -461,12 +523,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         }
     }
 
-    f32x16 acc[NF][MF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int g = 0; g < MF; ++g) acc[f][g] = f32x16{};
-
     const int wn = wave % WN;
     const int wm = wave / WN;
     const int lr = lane & 31;
@@ -490,55 +546,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     const int nk = kper / BK;
     switch (mvalid) {
-        case 4: k_loop<4, kGateUp>(acc, smem, op, nk, row_base, fa); break;
-        case 3: k_loop<3, kGateUp>(acc, smem, op, nk, row_base, fa); break;
-        case 2: k_loop<2, kGateUp>(acc, smem, op, nk, row_base, fa); break;
-        case 1: k_loop<1, kGateUp>(acc, smem, op, nk, row_base, fa); break;
-        default: k_loop<0, kGateUp>(acc, smem, op, nk, row_base, fa); break;
-    }
-
-    // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
-    // the weight side and column lr of the token side.
-    const int prow = tile.row0 + wm * (BM / WM) + lr;
-    if (kGateUp) {
-#pragma unroll
-        for (int f = 0; f < NF / 2; ++f) {
-#pragma unroll
-            for (int g = 0; g < MF; ++g) {
-                const int p = prow + g * 32;
-                if (p >= tile.row_end) continue;
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int n = nt * (BN / 2) + wn * (BN / 2 / WN) + f * 32 + rg * 8 + lk * 4;
-                    if (n >= N) continue;
-                    bf16x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        o[q] = to_bf16(silu_f(acc[f][g][rg * 4 + q]) *
-                                       acc[f + NF / 2][g][rg * 4 + q]);
-                    *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(Cv) + (int64_t)p * N +
-                                                n) = o;
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-#pragma unroll
-            for (int g = 0; g < MF; ++g) {
-                const int p = prow + g * 32;
-                if (p >= tile.row_end) continue;
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int n = nt * BN + wn * (BN / WN) + f * 32 + rg * 8 + lk * 4;
-                    if (n >= N) continue;
-                    const f32x16 &a = acc[f][g];
-                    *reinterpret_cast<float4 *>(static_cast<float *>(Cv) + ks * plane +
-                                                (int64_t)p * N + n) =
-                        make_float4(a[rg * 4], a[rg * 4 + 1], a[rg * 4 + 2], a[rg * 4 + 3]);
-                }
-            }
-        }
+        case 4:
+            run_tile<4, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv);
+            break;
+        case 3:
+            run_tile<3, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv);
+            break;
+        case 2:
+            run_tile<2, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv);
+            break;
+        case 1:
+            run_tile<1, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv);
+            break;
+        default:
+            run_tile<0, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv);
+            break;
     }
 }
 
