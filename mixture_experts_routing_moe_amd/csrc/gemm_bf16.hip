@@ -8,10 +8,13 @@
 // each block finds its expert and row range on the device from the aligned
 // offsets, so nothing is read back and empty experts cost nothing.
 //
-// Tile: 256 token rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
+// Tile: 320 token rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
 // waits hide behind the other's matrix-core work) in a 4 x 2 layout, each
-// wave 64 weight rows x 128 token rows = 2 x 4 MFMA 32x32x16 bf16 tiles with
-// float32 accumulators.  Operands go from global memory straight into LDS
+// wave 64 weight rows x 160 token rows = 2 x 5 MFMA 32x32x16 bf16 tiles with
+// float32 accumulators.  320 rows rather than 256: the operand loads bound
+// these kernels, and an expert with a little over 1024 rows (the Mixtral
+// shape's typical count) then takes 4 m-tiles instead of 5, so its weights
+// are streamed through the chip 4 times instead of 5.  Operands go from global memory straight into LDS
 // (gfx950 global_load_lds_dwordx4, no staging registers), double buffered, the
 // next k-tile in flight while the current one feeds the matrix cores;
 // fragments are double buffered in registers and their LDS reads interleaved
@@ -39,9 +42,10 @@
 namespace moe {
 namespace {
 
-
-
-constexpr int BM = 256;  // token rows per tile
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 320
+#endif
+constexpr int BM = MOE_GEMM_BM;  // token rows per tile
 constexpr int BN = 256;  // weight rows per tile
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
@@ -74,16 +78,21 @@ constexpr int kWOff = NS * kTokStage;       // first weight stage
 constexpr int kLds = kWOff + NS * kWStage;  // bf16 elements in all
 constexpr int kChunks = BK / 8;                // 16-byte chunks per row
 constexpr int kRowsPerLoad = 64 / kChunks;     // rows one wave instruction fills
-constexpr int kRowsPerWave = BM / kWaves;      // rows each wave loads per tile
-constexpr int NL = kRowsPerWave / kRowsPerLoad;  // load instructions per tile per wave
+constexpr int kTokRowsPerWave = BM / kWaves;   // token rows each wave loads per k-tile
+constexpr int kWRowsPerWave = BN / kWaves;     // weight rows each wave loads per k-tile
+constexpr int NLA = kTokRowsPerWave / kRowsPerLoad;  // token load instructions per wave
+constexpr int NLB = kWRowsPerWave / kRowsPerLoad;    // weight load instructions per wave
 constexpr int kRowsPerWindow = 128 / BK;       // rows sharing one 256-byte bank window
 static_assert(kLds * 2 <= 160 * 1024, "LDS exceeds 160 KB");
 static_assert(NF % 2 == 0, "gate and up fragments come in pairs");
-static_assert(MF == 4, "the k loop is dispatched on 0..4 valid token fragments");
-static_assert(BM == BN, "token and weight stages have the same shape");
+static_assert(MF >= 1 && MF <= 5, "the k loop is dispatched on 0..5 valid token fragments");
+static_assert(NLA * kRowsPerLoad * kWaves == BM && NLB * kRowsPerLoad * kWaves == BN,
+              "whole load instructions per wave");
 static_assert(NS >= 2 && KS % 2 == 0, "a ring of at least two stages, an even count of k-steps");
-static_assert(((NS - 1) * kWStage + BN * BK) * 2 <= 65536, "fragment offsets fit the ds_read field");
-constexpr int kLoadsPerStage = 2 * NL;  // load instructions per lane per stage
+static_assert(((NS - 1) * kWStage + BN * BK) * 2 <= 65536 &&
+                  ((NS - 1) * kTokStage + (MF - 1) * 32 * BK) * 2 < 65536,
+              "fragment offsets fit the ds_read field");
+constexpr int kLoadsPerStage = NLA + NLB;  // load instructions per lane per stage
 static_assert((NS - 2) * kLoadsPerStage <= 63, "vmcnt holds at most 63");
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -96,9 +105,9 @@ struct MTile {
 // BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
 // tile index, ordered n-tile-major: consecutive tiles are the expert's
 // m-tiles under one weight n-tile.  With kEven the segment is dealt to the
-// m-tiles in near-equal whole fragments (1040 rows: 4 x 224 + 144) instead of
-// 4 x 256 + 16, so the tiles sharing a weight tile do similar work (measured
-// faster for FC1; FC2 keeps 256-row tiles, which measured faster there).  A running sum of mt_e over the experts
+// m-tiles in near-equal whole fragments (1040 rows: 3 x 288 + 176) instead of
+// 3 x 320 + 80, so the tiles sharing a weight tile do similar work (measured
+// faster for FC1; FC2 keeps full-height tiles, which measured faster there).  A running sum of mt_e over the experts
 // (64 per pass, one per lane) finds the owner.  Every wave computes the same
 // answer, so no LDS is needed.
 template <bool kEven>
@@ -180,14 +189,26 @@ template <bool kBuf>
 struct Ops;
 template <>
 struct Ops<true> {
-    __amdgpu_buffer_rsrc_t a, b;  // token / weight operand (this expert)
-    int kb;                       // first k of this K slice
-    uint32_t aoff[NL], boff[NL];  // byte offsets of this lane's rows and chunk
+    __amdgpu_buffer_rsrc_t a, b;    // token / weight operand (this expert)
+    int kb;                         // first k of this K slice
+    int na;                         // token loads that hold a row of the tile
+    uint32_t aoff[NLA], boff[NLB];  // byte offsets of this lane's rows and chunk
 };
 template <>
 struct Ops<false> {
-    const uint16_t *a[NL], *b[NL];  // this lane's rows and chunk, from the slice's first k
+    const uint16_t *a[NLA], *b[NLB];  // this lane's rows and chunk, from the slice's first k
+    int na;                           // token loads that hold a row of the tile
 };
+
+// Token load i of a wave is issued only if its rows reach into the tile
+// (i < na, wave-uniform): rows past the expert's segment are never stored, so
+// their LDS rows may hold anything, and skipping them cuts the load traffic
+// that bounds these kernels (a partial m-tile's rows).  With more than two
+// stages the waits count loads per stage, so every load is issued.
+template <typename OpsT>
+__device__ __forceinline__ bool tok_load(const OpsT &op, int i) {
+    return i < NLA && (NS > 2 || i < op.na);
+}
 
 // Buffer resource word 3 for raw (unstructured) buffer access on gfx9-class
 // parts: 32-bit data format, no swizzle or index stride.
@@ -196,27 +217,41 @@ constexpr int kBufferWord3 = 0x00020000;
 // Issue one k-tile of both operands straight into an LDS stage (global /
 // buffer load to LDS, 16 bytes per lane: lane L's bytes land at base + 16 L,
 // i.e. row L / kChunks, position L % kChunks of the instruction's rows).
+// `wave` is the (scalar) wave index: the wave's rows of each operand start
+// at wave * k{Tok,W}RowsPerWave.
 template <int S>
 __device__ __forceinline__ void issue_stage(uint16_t *smem, const Ops<true> &op, int k0,
-                                            int row_base) {
+                                            int wave) {
     const uint32_t so = 2u * (uint32_t)(op.kb + k0);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        uint16_t *da = smem + S * kTokStage + (row_base + i * kRowsPerLoad) * BK;
-        uint16_t *db = smem + kWOff + S * kWStage + (row_base + i * kRowsPerLoad) * BK;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], so, 0, 0);
+    for (int i = 0; i < (NLA > NLB ? NLA : NLB); ++i) {
+        if (tok_load(op, i)) {
+            uint16_t *da = smem + S * kTokStage + (wave * kTokRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0,
+                                                     0);
+        }
+        if (i < NLB) {
+            uint16_t *db =
+                smem + kWOff + S * kWStage + (wave * kWRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], so, 0,
+                                                     0);
+        }
     }
 }
 template <int S>
 __device__ __forceinline__ void issue_stage(uint16_t *smem, const Ops<false> &op, int k0,
-                                            int row_base) {
+                                            int wave) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        uint16_t *da = smem + S * kTokStage + (row_base + i * kRowsPerLoad) * BK;
-        uint16_t *db = smem + kWOff + S * kWStage + (row_base + i * kRowsPerLoad) * BK;
-        __builtin_amdgcn_global_load_lds(op.a[i] + k0, (lds_void *)da, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(op.b[i] + k0, (lds_void *)db, 16, 0, 0);
+    for (int i = 0; i < (NLA > NLB ? NLA : NLB); ++i) {
+        if (tok_load(op, i)) {
+            uint16_t *da = smem + S * kTokStage + (wave * kTokRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_global_load_lds(op.a[i] + k0, (lds_void *)da, 16, 0, 0);
+        }
+        if (i < NLB) {
+            uint16_t *db =
+                smem + kWOff + S * kWStage + (wave * kWRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_global_load_lds(op.b[i] + k0, (lds_void *)db, 16, 0, 0);
+        }
     }
 }
 
@@ -329,10 +364,10 @@ __device__ __forceinline__ void k_steps(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2
 // addresses.
 template <int S, int MV, bool kGateUp, typename OpsT>
 __device__ __forceinline__ void k_tile(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
-                                       const OpsT &op, int kt, int nk, int row_base,
+                                       const OpsT &op, int kt, int nk, int wv,
                                        const FragAddr &fa) {
     const char *lds = reinterpret_cast<const char *>(smem);
-    if (kt + NS - 1 < nk) issue_stage<(S + NS - 1) % NS>(smem, op, (kt + NS - 1) * BK, row_base);
+    if (kt + NS - 1 < nk) issue_stage<(S + NS - 1) % NS>(smem, op, (kt + NS - 1) * BK, wv);
     __builtin_amdgcn_sched_barrier(0);
     k_steps<S, 0, MV, kGateUp>(acc, fr, lds, fa);
     wait_landed<NS - 2>(min(nk - 2 - kt, NS - 2));
@@ -344,29 +379,29 @@ __device__ __forceinline__ void k_tile(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2]
 
 template <int S, int MV, bool kGateUp, typename OpsT>
 __device__ __forceinline__ void k_tiles(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
-                                        const OpsT &op, int kt, int nk, int row_base,
+                                        const OpsT &op, int kt, int nk, int wv,
                                         const FragAddr &fa) {
     if constexpr (S < NS) {
         if (kt < nk) {
-            k_tile<S, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
-            k_tiles<S + 1, MV, kGateUp>(acc, fr, smem, op, kt + 1, nk, row_base, fa);
+            k_tile<S, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
+            k_tiles<S + 1, MV, kGateUp>(acc, fr, smem, op, kt + 1, nk, wv, fa);
         }
     }
 }
 
 template <int S, bool kBuf>
 __device__ __forceinline__ void issue_first(uint16_t *smem, const Ops<kBuf> &op, int nk,
-                                            int row_base) {
+                                            int wv) {
     if constexpr (S + 1 < NS) {
-        if (S < nk) issue_stage<S>(smem, op, S * BK, row_base);
-        issue_first<S + 1>(smem, op, nk, row_base);
+        if (S < nk) issue_stage<S>(smem, op, S * BK, wv);
+        issue_first<S + 1>(smem, op, nk, wv);
     }
 }
 
 template <int MV, bool kGateUp, typename OpsT>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const OpsT &op,
-                                       int nk, int row_base, const FragAddr &fa) {
-    issue_first<0>(smem, op, nk, row_base);
+                                       int nk, int wv, const FragAddr &fa) {
+    issue_first<0>(smem, op, nk, wv);
     wait_landed<NS - 2>(min(nk - 1, NS - 2));
     stage_barrier();
     Frags<MV> fr[2];
@@ -375,8 +410,8 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
     // Whole rounds of the ring with every stage index a constant, then the
     // remaining k-tiles.
     for (; kt + NS <= nk; kt += NS)
-        k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
-    k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, row_base, fa);
+        k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
+    k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
 }
 
 // The k loop and the epilogue of one tile whose waves hold MV valid token
@@ -384,7 +419,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
 // dispatch on MV, one set shared by the five loop versions measured slower
 // (the register allocator copies it between them).
 template <int MV, bool kGateUp, typename OpsT>
-__device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int row_base,
+__device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int wv,
                                          const FragAddr &fa, const MTile &tile, int nt, int wn,
                                          int wm, int lr, int lk, int N, int ks, int64_t plane,
                                          void *__restrict__ Cv) {
@@ -394,7 +429,7 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 #pragma unroll
         for (int g = 0; g < MF; ++g) acc[f][g] = f32x16{};
 
-    k_loop<MV, kGateUp>(acc, smem, op, nk, row_base, fa);
+    k_loop<MV, kGateUp>(acc, smem, op, nk, wv, fa);
 
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
     // the weight side and column lr of the token side.
@@ -486,11 +521,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // Operand rows this lane loads: row row_base + kRowsPerLoad i + lane /
-    // kChunks of each tile; it lands at position lane % kChunks, so it fetches
-    // global chunk (lane % kChunks) ^ swz(row) of that row.  The wave index is
-    // made scalar so the LDS destinations (M0) need no per-load conversion.
-    const int row_base = __builtin_amdgcn_readfirstlane(wave) * kRowsPerWave;
+    // Operand rows this lane loads: row wave * k{Tok,W}RowsPerWave +
+    // kRowsPerLoad i + lane / kChunks of each tile; it lands at position
+    // lane % kChunks, so it fetches global chunk (lane % kChunks) ^ swz(row)
+    // of that row.  The wave index is made scalar so the LDS destinations (M0)
+    // need no per-load conversion.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int rr = lane / kChunks;
     const int rows_w = kGateUp ? 2 * N : N;
     const uint16_t *We = W + (int64_t)tile.e * rows_w * K;
@@ -501,12 +537,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
                                                  kBufferWord3);
         op.kb = __builtin_amdgcn_readfirstlane(kbeg);
     }
+    op.na = __builtin_amdgcn_readfirstlane(
+        min(NLA, max(0, (tile.row_end - tile.row0 - wv * kTokRowsPerWave + kRowsPerLoad - 1) /
+                            kRowsPerLoad)));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int r = row_base + i * kRowsPerLoad + rr;
+    for (int i = 0; i < NLA; ++i) {
+        const int r = wv * kTokRowsPerWave + i * kRowsPerLoad + rr;
         const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         const int p = min(tile.row0 + r, tile.row_end - 1);
         const int arow = kGateUp ? gather[p] : p;
+        if constexpr (kBuf)
+            op.aoff[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)c8) * 2u;
+        else
+            op.a[i] = A + (int64_t)arow * K + kbeg + c8;
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+        const int r = wv * kWRowsPerWave + i * kRowsPerLoad + rr;
+        const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         int wrow;
         if (kGateUp) {
             const int n = min(nt * (BN / 2) + (r & (BN / 2 - 1)), N - 1);
@@ -514,13 +562,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         } else {
             wrow = min(nt * BN + r, N - 1);
         }
-        if constexpr (kBuf) {
-            op.aoff[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)c8) * 2u;
+        if constexpr (kBuf)
             op.boff[i] = ((uint32_t)wrow * (uint32_t)K + (uint32_t)c8) * 2u;
-        } else {
-            op.a[i] = A + (int64_t)arow * K + kbeg + c8;
+        else
             op.b[i] = We + (int64_t)wrow * K + kbeg + c8;
-        }
     }
 
     const int wn = wave % WN;
@@ -546,24 +591,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     const int nk = kper / BK;
     switch (mvalid) {
+        case 5:
+            if constexpr (MF >= 5)
+                run_tile<5, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks, plane,
+                                     Cv);
+            break;
         case 4:
-            run_tile<4, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+            run_tile<4, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
                                  plane, Cv);
             break;
         case 3:
-            run_tile<3, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+            run_tile<3, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
                                  plane, Cv);
             break;
         case 2:
-            run_tile<2, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+            run_tile<2, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
                                  plane, Cv);
             break;
         case 1:
-            run_tile<1, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+            run_tile<1, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
                                  plane, Cv);
             break;
         default:
-            run_tile<0, kGateUp>(smem, op, nk, row_base, fa, tile, nt, wn, wm, lr, lk, N, ks,
+            run_tile<0, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
                                  plane, Cv);
             break;
     }

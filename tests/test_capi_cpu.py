@@ -131,10 +131,13 @@ def test_ffn_validation(lib):
 def test_down_splits(lib):
     bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
     f = lib.moe_ffn_down_splits
-    # Mixtral-shaped FC2: 36 x 16 = 576 expected tiles fill 2.25 rounds of
-    # 256 CUs; two K slices of 7168 make 4.5 rounds, and more slices cost
-    # more in y traffic than they save.
-    assert f(bf, 0, 4096, 4096, 14336, 8, 2) == 2
+    # Mixtral-shaped FC2: 30 x 16 = 480 expected tiles fill 1.9 rounds of
+    # 256 CUs; two K slices of 7168 make 3.75 rounds, which does not pay for
+    # the extra y plane.
+    assert f(bf, 0, 4096, 4096, 14336, 8, 2) == 1
+    # 4 experts of ~4096 rows: 54 x 16 = 864 expected tiles leave the last of
+    # 3.4 rounds 40 % full; two slices make 6.75 rounds.
+    assert f(bf, 0, 8192, 4096, 14336, 4, 2) == 2
     # Fine-grained FC2: ~2300 tiles already fill the chip; K = 1408 is too
     # short to cut.
     assert f(bf, 0, 8192, 2048, 1408, 64, 8) == 1
@@ -148,7 +151,8 @@ def test_down_splits(lib):
     n1 = lib.moe_expert_ffn_workspace_size(bf, 8192, 2048, 1408, 64, 8)
     assert n1 >= 65536 * (1408 * 2 + 2048 * 4)
     n2 = lib.moe_expert_ffn_workspace_size(bf, 4096, 4096, 14336, 8, 2)
-    assert n2 >= 8192 * 14336 * 2 + 2 * 8192 * 4096 * 4
+    sp = f(bf, 0, 4096, 4096, 14336, 8, 2)
+    assert n2 >= 8192 * 14336 * 2 + sp * 8192 * 4096 * 4
 
 
 def test_down_split_validation(lib):

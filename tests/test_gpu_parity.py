@@ -278,6 +278,8 @@ def _ffn_gpu(x, w13, w2, w32, ids, dtype, decode=False):
     (600, 320, 448, 4, 1, 2.0, 0.0),
     (260, 192, 256, 12, 3, 0.0, 0.2),
     (2048, 1024, 256, 8, 2, 1.0, 0.0),
+    (1400, 128, 256, 2, 1, 0.0, 0.0),
+    (2600, 64, 128, 4, 2, 0.5, 0.1),
 ])
 def test_ffn_bf16_prefill(T, H, I, E, k, skew, inv):
     x, w13, w2, w32, ids = _rand_layer(T + H + I + E, T, H, I, E, k, skew=skew, inv=inv)
