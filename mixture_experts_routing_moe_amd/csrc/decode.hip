@@ -13,8 +13,9 @@
 // Each block owns 16 weight rows (16 gate + 16 up rows for FC1) of one
 // expert; its 4 waves split k into contiguous quarters, load their whole
 // share of the weight rows up front and feed MFMA 16x16x32 bf16 (weights as
-// the A operand, up to 4 chunks of 16 tokens as B).  The 4 partial
-// accumulators are summed through LDS.
+// the A operand, up to 4 chunks of 16 tokens as B; the chunk count follows
+// the expert's own row count).  The 4 partial accumulators are summed
+// through LDS.
 //
 // Weight loads come in pairs of k-steps.  The MFMA A operand of one k-step
 // gives each of 16 rows 64 bytes (4 lanes x 16), so loading it directly
@@ -97,15 +98,15 @@ __device__ __forceinline__ void unpair(bool lo, const bf16x8 &P, const bf16x8 &Q
 }
 
 // FC1 + SiLU-and-mul.  act[p, n] for n in this block's 16 rows and every
-// position p of the expert's segment.
+// position p of expert e's segment [base, base + cnt), in MC chunks of 16
+// token columns.
 template <int MC>
-__global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
-    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w13,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_tok, int H, int I,
-    int E, uint16_t *__restrict__ act) {
+__device__ __forceinline__ void gate_up_rows(const uint16_t *__restrict__ hidden,
+                                             const uint16_t *__restrict__ w13,
+                                             const int32_t *__restrict__ sorted_tok, int H, int I,
+                                             int e, int base, int cnt,
+                                             uint16_t *__restrict__ act) {
     __shared__ f32x4 red[3][2][MC][kWave];
-    int e, base, cnt;
-    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int i = lane & 15;
@@ -199,15 +200,15 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
 }
 
 // FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p
-// of the expert's segment.  KP pairs per batch: 6 for up to 32 tokens (one
-// batch covers each wave's share of k = 1408), 4 for more.
-template <int MC, int KP>
-__global__ __launch_bounds__(kThreads) void decode_down_kernel(
-    const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
-    const int32_t *__restrict__ offsets, int H, int I, int E, float *__restrict__ y) {
+// of expert e's segment, in MC chunks of 16 token columns.  KP pairs per
+// batch: 6 for up to 32 tokens (one batch covers each wave's share of
+// k = 1408), 4 for more.
+template <int MC>
+__device__ __forceinline__ void down_rows(const uint16_t *__restrict__ act,
+                                          const uint16_t *__restrict__ w2, int H, int I, int e,
+                                          int base, int cnt, float *__restrict__ y) {
+    constexpr int KP = MC <= 2 ? 6 : 4;
     __shared__ f32x4 red[3][MC][kWave];
-    int e, base, cnt;
-    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int i = lane & 15;
@@ -277,6 +278,39 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     }
 }
 
+// One block per (16 weight rows, non-empty expert).  The number of 16-token
+// chunks is chosen per block from the expert's own row count (at most MCmax,
+// which the launch sets from T): with T = 32 most experts hold 16 rows or
+// fewer and take the one-chunk path.
+template <int MCmax>
+__global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
+    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w13,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_tok, int H, int I,
+    int E, uint16_t *__restrict__ act) {
+    int e, base, cnt;
+    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
+    if (MCmax == 1 || cnt <= 16)
+        gate_up_rows<1>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+    else if (MCmax == 2 || cnt <= 32)
+        gate_up_rows<(MCmax > 1 ? 2 : 1)>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+    else
+        gate_up_rows<MCmax>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+}
+
+template <int MCmax>
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+    const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
+    const int32_t *__restrict__ offsets, int H, int I, int E, float *__restrict__ y) {
+    int e, base, cnt;
+    if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
+    if (MCmax == 1 || cnt <= 16)
+        down_rows<1>(act, w2, H, I, e, base, cnt, y);
+    else if (MCmax == 2 || cnt <= 32)
+        down_rows<(MCmax > 1 ? 2 : 1)>(act, w2, H, I, e, base, cnt, y);
+    else
+        down_rows<MCmax>(act, w2, H, I, e, base, cnt, y);
+}
+
 int token_chunks(int64_t T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
 unsigned expert_rows(int64_t T, int E, int k) {
@@ -316,15 +350,15 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
     const dim3 grid(H / kRows, expert_rows(T, E, k));
     switch (token_chunks(T)) {
         case 1:
-            hipLaunchKernelGGL((decode_down_kernel<1, 6>), grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<1>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
         case 2:
-            hipLaunchKernelGGL((decode_down_kernel<2, 6>), grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<2>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
         default:
-            hipLaunchKernelGGL((decode_down_kernel<4, 4>), grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<4>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
     }
