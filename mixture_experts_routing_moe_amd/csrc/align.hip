@@ -18,6 +18,9 @@
 //                     ascending token inside each expert, exactly the order
 //                     of the pages' cumsum.
 //
+//   With at most 1024 slots one scatter block does it all, counting the ids
+//   itself, and the histogram kernel is skipped.
+//
 // Only integer LDS atomics on private counters are used, and no result
 // depends on their order, so the output is identical on every run.
 #include "moe_internal.h"
@@ -96,9 +99,12 @@ __device__ int block_exclusive_scan(const int32_t *v, int32_t *out, int n, int32
 // in order, 256 slots at a time: a slot's rank among earlier slots of the
 // same expert comes from ballots inside its wave plus the counts of the
 // waves before it, so positions follow the flat slot order.
+//
+// With one block (n <= 1024 slots: decode batches) the block counts the ids
+// itself (fused_hist) and the histogram kernel is not launched.
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
-    const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
+    int fused_hist, const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
     int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
     extern __shared__ int32_t sm[];
@@ -115,10 +121,21 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int wave = tid / kWave;
     const int b = blockIdx.x;
 
+    if (fused_hist) {
+        for (int idx = tid; idx < parts * E; idx += kAlignThreads) {
+            tot_part[idx] = 0;
+            pre_part[idx] = 0;
+        }
+        __syncthreads();
+        for (int s = tid; s < n; s += kAlignThreads) {
+            const int e = ids[s];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&tot_part[e], 1);
+        }
+    }
     // Per (part, expert): sums over the blocks part, part + parts, ... -- all
     // of them and those before b.  Threads of one pass read consecutive
     // experts of one block row (coalesced), and the loads are independent.
-    for (int idx = tid; idx < parts * E; idx += kAlignThreads) {
+    for (int idx = tid; idx < (fused_hist ? 0 : parts * E); idx += kAlignThreads) {
         const int e = idx % E, part = idx / E;
         int all = 0, pre = 0;
 #pragma unroll 8
@@ -216,15 +233,18 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
 
     // With no slots the histogram is all zeros and the scatter kernel still
     // writes zero counts and offsets.
-    hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(kAlignThreads), E * sizeof(int32_t), s,
-                       ids, n, E, chunk, ws);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    const int fused = nb == 1;
+    if (!fused) {
+        hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(kAlignThreads), E * sizeof(int32_t),
+                           s, ids, n, E, chunk, ws);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
     const size_t lds = (size_t)(7 * E + 2 * parts * E + kAlignThreads / kWave) * sizeof(int32_t);
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
-                       k, E, (int)chunk, nbits, nb, ws, counts, offsets, sorted_tok, sorted_slot,
-                       slot_to_sorted);
+                       k, E, (int)chunk, nbits, nb, fused, ws, counts, offsets, sorted_tok,
+                       sorted_slot, slot_to_sorted);
     return hipGetLastError();
 }
 
