@@ -104,13 +104,12 @@ struct MTile {
 // Tile index -> (expert, rows, n-tile).  Expert e owns mt_e = ceil(count_e /
 // BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
 // tile index, ordered n-tile-major: consecutive tiles are the expert's
-// m-tiles under one weight n-tile.  With kEven the segment is dealt to the
-// m-tiles in near-equal whole fragments (1040 rows: 3 x 288 + 176) instead of
-// 3 x 320 + 80, so the tiles sharing a weight tile do similar work (measured
-// faster for FC1; FC2 keeps full-height tiles, which measured faster there).  A running sum of mt_e over the experts
-// (64 per pass, one per lane) finds the owner.  Every wave computes the same
-// answer, so no LDS is needed.
-template <bool kEven>
+// m-tiles under one weight n-tile.  The segment is dealt to the m-tiles in
+// near-equal whole fragments (1040 rows: 3 x 288 + 176) instead of
+// 3 x 320 + 80, so the tiles sharing a weight tile do similar work and stay
+// in step (measured faster for both GEMMs).  A running sum of mt_e over the
+// experts (64 per pass, one per lane) finds the owner.  Every wave computes
+// the same answer, so no LDS is needed.
 __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int n_tiles,
                           MTile &t, int &nt) {
     const int lane = lane_id();
@@ -143,11 +142,10 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             nt = j / mt;
             const int i = j - nt * mt;
             t.e = c + src;
-            // Rows per m-tile: BM, or with kEven the expert's rows dealt in
-            // equal shares rounded up to whole 32-row fragments (at most BM;
-            // never an empty tile, since q mt >= cn and q < cn / (mt - 1)
-            // whenever mt > 1).
-            const int q = kEven ? (cn + 32 * mt - 1) / (32 * mt) * 32 : BM;
+            // Rows per m-tile: the expert's rows dealt in equal shares
+            // rounded up to whole 32-row fragments (at most BM; never an
+            // empty tile: (mt - 1) q < cn, checked for every cn < 200000).
+            const int q = (cn + 32 * mt - 1) / (32 * mt) * 32;
             t.row0 = o0 + min(i * q, cn);
             t.row_end = o0 + min((i + 1) * q, cn);
             return t.row0 < t.row_end;
@@ -513,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     }
     MTile tile;
     int nt;
-    if (!find_tile<kGateUp>(offsets, E, L, n_tiles, tile, nt)) return;
+    if (!find_tile(offsets, E, L, n_tiles, tile, nt)) return;
     const int kper = K / ksplit;  // a multiple of BK (checked by the host)
     const int kbeg = ks * kper;
 

@@ -95,7 +95,13 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }
 
 // SiLU in float32: z / (1 + e^-z).
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about
+// 1 ulp) instead of an IEEE division: the result is rounded to bf16 next,
+// and the division's fix-up sequence tripled the size of the GEMM epilogues.
+// z -> -inf gives -0 (the reciprocal of inf is 0), z -> +inf gives z.
+__device__ __forceinline__ float silu_f(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (each returns hipSuccess or the launch error).

@@ -182,3 +182,14 @@ def test_last_error_is_thread_local(lib):
     t.join()
     assert seen == [b""]
     assert b"k = 9" in lib.moe_last_error()
+
+
+def test_even_mtile_split_never_empty():
+    """The grouped GEMMs deal an expert's cn rows to mt = ceil(cn / 320)
+    m-tiles in equal shares rounded up to whole 32-row fragments; every tile
+    must get at least one row and none more than 320."""
+    bm = 320
+    for cn in range(1, 200000):
+        mt = -(-cn // bm)
+        q = -(-cn // (32 * mt)) * 32
+        assert q <= bm and (mt - 1) * q < cn <= mt * q, cn
