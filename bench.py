@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
 
 One step is one pass of the whole path over one batch of synthetic input:
-route -> align -> indices->multihot -> multihot->indices -> grouped FC1 +
-SiLU-and-mul -> grouped FC2 -> combine (decode workloads use the decode FFN
-kernels).  Inputs are resident in HBM before timing starts; nothing is
+route + indices->multihot (one call, fused in one kernel for E <= 64) ->
+align -> multihot->indices -> grouped FC1 + SiLU-and-mul -> grouped FC2 ->
+combine (decode workloads use the decode FFN kernels).  Inputs are resident in HBM before timing starts; nothing is
 allocated inside the timed region.  Each phase is bracketed by HIP events on
 the stream the library launches on (torch's current stream), so per-kernel
 durations are measured live.  Prints one JSON line.
@@ -193,19 +193,19 @@ def main():
         y = torch.empty((splits, T * k, H), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    phases = ["route", "align", "to_multihot", "to_indices"]
+    # Route and the indices->multihot conversion of its output run as one
+    # call (one kernel where the library fuses them, see config).
+    phases = ["route_multihot", "align", "to_indices"]
     if has_ffn:
         phases += ["gate_up", "down", "combine"]
 
     cur = {"logits": logits_draws[0]}
 
     def run_phase(name):
-        if name == "route":
-            moe.moe_route(cur["logits"], k, w.norm, topk_w, topk_ids)
+        if name == "route_multihot":
+            moe.moe_route_multihot(cur["logits"], k, w.norm, (topk_w, topk_ids, mh, pim, pos))
         elif name == "align":
             moe.moe_align(topk_ids, E, aligned, align_ws)
-        elif name == "to_multihot":
-            moe.moe_indices_to_multihot(topk_ids, topk_w, E, (mh, pim, pos))
         elif name == "to_indices":
             moe.moe_multihot_to_indices(pim, pos, k, out=(back_p, back_i))
         elif name == "gate_up":
@@ -275,7 +275,7 @@ def main():
         # Distinct experts per routing draw (outside the timed region).
         for r in range(min(draws, args.steps)):
             cur["logits"] = logits_draws[r]
-            run_phase("route")
+            run_phase("route_multihot")
             run_phase("align")
             n_distinct.append(int((aligned["counts"] > 0).sum().item()))
 
@@ -291,7 +291,8 @@ def main():
     cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm,
            "routing_draws": draws, "cache_flush_between_steps": flush,
            "step_timing": "hip_graph_replay" if graph_ms is not None else "eager",
-           "eager_ms_per_step": round(eager_ms, 4)}
+           "eager_ms_per_step": round(eager_ms, 4),
+           "route_multihot_fused": moe.moe_route_multihot_fused(E, k)}
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())
@@ -324,13 +325,13 @@ def main():
     if routing_only:
         # Algorithmic HBM bytes per phase: every input read once, every output
         # written once.
-        nb = {"route": T * E * 4 + T * k * 8,
+        nb = {"route_multihot": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
-              "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "to_indices": T * E * 8 + T * k * 8}
         dom = max(phase_ms, key=phase_ms.get)
-        names = {"route": "route_rows16_kernel", "align": "align_hist_kernel + align_scatter_kernel",
-                 "to_multihot": "to_multihot_rows16_kernel", "to_indices": "to_indices_rows16_kernel"}
+        names = {"route_multihot": "route_rows16_kernel (route + multihot)",
+                 "align": "align_hist_kernel + align_scatter_kernel",
+                 "to_indices": "to_indices_rows16_kernel"}
         achieved = nb[dom] / (phase_ms[dom] * 1e-3) / 1e9
         roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -5,6 +5,7 @@
  * The layer forward is split the way the method is stated:
  *
  *   moe_route                 gating softmax + top-k (optionally renormalised)
+ *   moe_route_multihot        moe_route + moe_indices_to_multihot in one pass
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 2
+#define MOE_VERSION 3
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
 #define MOE_DECODE_MAX_T 64
@@ -99,6 +100,27 @@ const char *moe_last_error(void);
  */
 moe_status_t moe_route(const float *logits, int64_t T, int32_t E, int32_t k,
                        int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids, void *stream);
+
+/*
+ * moe_route_multihot -- moe_route followed by moe_indices_to_multihot of its
+ * own output, in one pass where moe_route_multihot_fused(E, k) is true (and
+ * probs_in_multihot / position_map are 16-byte aligned, multihot 4-byte
+ * aligned); otherwise the same two launches as the separate calls.
+ * [mlc] gating_topk, gating_softmax_topk; [mgt] _indices_to_multihot_kernel.
+ *
+ * Arguments as moe_route, plus the [T, E] outputs of moe_indices_to_multihot
+ * (multihot uint8, probs_in_multihot float32, position_map int32).  Every
+ * output is bit-identical to moe_route then moe_indices_to_multihot on the
+ * same logits.  All pointers non-null when T > 0.
+ */
+moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32_t k,
+                                int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                uint8_t *multihot, float *probs_in_multihot,
+                                int32_t *position_map, void *stream);
+
+/* 1 if moe_route_multihot runs as one kernel for this E and k (E <= 64,
+ * E % 4 == 0, k <= 16, k <= E), else 0. */
+int32_t moe_route_multihot_fused(int32_t E, int32_t k);
 
 /*
  * moe_align -- expert alignment of the T*k (token, slot) pairs.

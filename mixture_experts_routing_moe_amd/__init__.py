@@ -18,4 +18,6 @@ from .moe import (  # noqa: F401
     moe_layer,
     moe_multihot_to_indices,
     moe_route,
+    moe_route_multihot,
+    moe_route_multihot_fused,
 )

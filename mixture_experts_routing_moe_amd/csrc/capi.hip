@@ -112,6 +112,26 @@ moe_status_t moe_route(const float *logits, int64_t T, int32_t E, int32_t k,
                       "moe_route");
 }
 
+moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32_t k,
+                                int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                uint8_t *multihot, float *probs_in_multihot,
+                                int32_t *position_map, void *stream) {
+    moe_status_t st = check_routing_dims(T, E, k, "moe_route_multihot");
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "moe_route_multihot: k = %d > E = %d", k, E);
+    if (T == 0) return MOE_OK;
+    CHECK(logits && topk_w && topk_ids && multihot && probs_in_multihot && position_map,
+          MOE_ERR_INVALID_ARG, "moe_route_multihot: null pointer");
+    return hip_status(moe::launch_route_multihot(logits, T, E, k, norm_topk_prob != 0, topk_w,
+                                                 topk_ids, multihot, probs_in_multihot,
+                                                 position_map, static_cast<hipStream_t>(stream)),
+                      "moe_route_multihot");
+}
+
+int32_t moe_route_multihot_fused(int32_t E, int32_t k) {
+    return E >= 1 && k >= 1 && k <= E && E <= 64 && E % 4 == 0 && k <= 16;
+}
+
 size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E) {
     if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
     const int nb = moe::align_num_blocks(T * k, E);

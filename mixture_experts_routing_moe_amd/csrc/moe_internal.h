@@ -108,6 +108,12 @@ __device__ __forceinline__ float silu_f(float z) {
 // ---------------------------------------------------------------------------
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int norm, float *w,
                         int32_t *ids, hipStream_t s);
+// Route and indices->multihot in one pass where the fused kernel applies
+// (route_multihot_fused), else the two launches.
+bool route_multihot_fused(int E, int k, const uint8_t *mh, const float *pim, const int32_t *pos);
+hipError_t launch_route_multihot(const float *logits, int64_t T, int E, int k, int norm,
+                                 float *w, int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                                 hipStream_t s);
 
 int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,

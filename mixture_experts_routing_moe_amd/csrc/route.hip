@@ -95,9 +95,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 // plus one ballot; the lowest lane holding the maximum wins, which is the
 // lowest expert id among equal logits.  A second 4-step max broadcasts the
 // winner's local slot.
+//
+// With multihot != nullptr (E % 4 == 0, 16-byte aligned rows) the same pass
+// also writes the row's [E] multihot, probability and position-map entries
+// (the indices->multihot conversion of the selection just made): each lane
+// records which round picked each of its 4 experts, fetches that slot's
+// weight from the lane that computed it, and writes its 4 columns, so the
+// conversion costs no second read of the ids and weights and no launch.
 __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
     const float *__restrict__ logits, int64_t T, int E, int k, int norm, int vec4,
-    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids) {
+    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot,
+    float *__restrict__ pim, int32_t *__restrict__ pos) {
     const int lane = lane_id();
     const int g = lane >> 4;
     const int q = lane & 15;
@@ -134,6 +142,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
 
         uint32_t sel_key = 0, kmax = 0;
         int sel_e = -1;
+        uint32_t slot_of = 0xFFFFFFFFu;  // byte i: round that picked local expert i
         for (int r = 0; r < k; ++r) {
             // Lane-local best; strict > keeps the lowest local slot on ties.
             uint32_t bk = 0;
@@ -150,7 +159,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
             const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
             const int wl = __ffs((int)mrow) - 1;  // -1 only for rows past T
             const bool is_w = q == wl;
-            if (is_w) avail &= ~(1u << bi);
+            if (is_w) {
+                avail &= ~(1u << bi);
+                slot_of = (slot_of & ~(0xFFu << (8 * bi))) | ((uint32_t)r << (8 * bi));
+            }
             const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
             if (q == r) {
                 sel_key = rmax;
@@ -172,9 +184,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
                 if ((valid >> i) & 1u) part += exp((double)v[i] - mx);
         }
         const double sum = row16_sum_f64(part);
+        const float wq = (float)(ex / sum);
         if (row_ok && q < k) {
-            topk_w[t * k + q] = (float)(ex / sum);
+            topk_w[t * k + q] = wq;
             topk_ids[t * k + q] = sel_e;
+        }
+        if (multihot != nullptr) {
+            int pj[4];
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (int)((slot_of >> (8 * i)) & 0xFFu);
+                pj[i] = r == 0xFF ? -1 : r;
+                // Every lane takes part in the shuffle; unpicked columns read
+                // their own lane and are zeroed.
+                const float w = __shfl(wq, pj[i] >= 0 ? (lane & ~15) + pj[i] : lane, kWave);
+                pv[i] = pj[i] >= 0 ? w : 0.0f;
+            }
+            if (row_ok && 4 * q < E) {
+                const uint32_t m = (uint32_t)(pj[0] >= 0) | (uint32_t)(pj[1] >= 0) << 8 |
+                                   (uint32_t)(pj[2] >= 0) << 16 | (uint32_t)(pj[3] >= 0) << 24;
+                *reinterpret_cast<uint32_t *>(multihot + t * E + 4 * q) = m;
+                *reinterpret_cast<float4 *>(pim + t * E + 4 * q) =
+                    make_float4(pv[0], pv[1], pv[2], pv[3]);
+                *reinterpret_cast<int4 *>(pos + t * E + 4 * q) = make_int4(pj[0], pj[1], pj[2], pj[3]);
+            }
         }
     }
 }
@@ -192,17 +226,43 @@ hipError_t launch_vpl(const float *logits, int64_t T, int E, int k, int norm, fl
 
 }  // namespace
 
+namespace {
+
+hipError_t launch_rows16(const float *logits, int64_t T, int E, int k, int norm, float *w,
+                         int32_t *ids, uint8_t *mh, float *pim, int32_t *pos, hipStream_t s) {
+    int64_t blocks = (T + 15) / 16;  // 4 waves x 4 rows per block
+    if (blocks > 8192) blocks = 8192;
+    const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+    hipLaunchKernelGGL(route_rows16_kernel, dim3((unsigned)blocks), dim3(kRouteThreads), 0, s,
+                       logits, T, E, k, norm, vec4, w, ids, mh, pim, pos);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool route_multihot_fused(int E, int k, const uint8_t *mh, const float *pim,
+                          const int32_t *pos) {
+    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    return E <= 64 && E % 4 == 0 && k <= 16 && a16(pim) && a16(pos) &&
+           (reinterpret_cast<uintptr_t>(mh) & 3u) == 0;
+}
+
+hipError_t launch_route_multihot(const float *logits, int64_t T, int E, int k, int norm,
+                                 float *w, int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                                 hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (route_multihot_fused(E, k, mh, pim, pos))
+        return launch_rows16(logits, T, E, k, norm, w, ids, mh, pim, pos, s);
+    const hipError_t err = launch_route(logits, T, E, k, norm, w, ids, s);
+    if (err != hipSuccess) return err;
+    return launch_to_multihot(ids, w, T, k, E, mh, pim, pos, s);
+}
+
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int norm, float *w,
                         int32_t *ids, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64 && k <= 16) {
-        int64_t blocks = (T + 15) / 16;  // 4 waves x 4 rows per block
-        if (blocks > 8192) blocks = 8192;
-        const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
-        hipLaunchKernelGGL(route_rows16_kernel, dim3((unsigned)blocks), dim3(kRouteThreads), 0, s,
-                           logits, T, E, k, norm, vec4, w, ids);
-        return hipGetLastError();
-    }
+    if (E <= 64 && k <= 16)
+        return launch_rows16(logits, T, E, k, norm, w, ids, nullptr, nullptr, nullptr, s);
     if (E <= 64) return launch_vpl<1>(logits, T, E, k, norm, w, ids, s);
     if (E <= 128) return launch_vpl<2>(logits, T, E, k, norm, w, ids, s);
     if (E <= 256) return launch_vpl<4>(logits, T, E, k, norm, w, ids, s);

@@ -56,6 +56,32 @@ def moe_route(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, topk_w=
     return topk_w, topk_ids
 
 
+def moe_route_multihot(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, out=None):
+    """moe_route + moe_indices_to_multihot of its output, one pass where the
+    library fuses them -> (topk_w, topk_ids, multihot, probs_in_multihot,
+    position_map)."""
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be [T, E] float32")
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, E), dtype=torch.uint8, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.int32, device=dev))
+    tw, ti, mh, pim, pos = out
+    _dev(logits, tw, ti, mh, pim, pos)
+    check(lib().moe_route_multihot(_ptr(logits), T, E, k, int(bool(norm_topk_prob)), _ptr(tw),
+                                   _ptr(ti), _ptr(mh), _ptr(pim), _ptr(pos), _stream()),
+          "moe_route_multihot")
+    return tw, ti, mh, pim, pos
+
+
+def moe_route_multihot_fused(E: int, k: int) -> bool:
+    return bool(lib().moe_route_multihot_fused(E, k))
+
+
 def moe_align_workspace_size(T: int, k: int, E: int) -> int:
     return int(lib().moe_align_workspace_size(T, k, E))
 

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_version() == 2
+    assert lib.moe_version() == 3
     for s in range(5):
         assert lib.moe_status_string(s)
     assert lib.moe_status_string(99) == b"unknown status"
@@ -75,6 +75,18 @@ def test_route_validation(lib):
     assert status(lib, "moe_route", FAKE, -1, 8, 2, 1, FAKE, FAKE, None) == I
     assert status(lib, "moe_route", None, 4, 8, 2, 1, FAKE, FAKE, None) == I  # null
     assert status(lib, "moe_route", None, 0, 8, 2, 1, None, None, None) == _lib.MOE_OK  # T=0
+
+
+def test_route_multihot_validation(lib):
+    I = _lib.MOE_ERR_INVALID_ARG
+    f = "moe_route_multihot"
+    assert status(lib, f, FAKE, 4, 8, 9, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == I  # k > E
+    assert status(lib, f, FAKE, 4, 8, 2, 1, FAKE, FAKE, None, FAKE, FAKE, None) == I  # null
+    assert status(lib, f, FAKE, 4, 2000, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == I
+    assert status(lib, f, None, 0, 8, 2, 1, None, None, None, None, None, None) == _lib.MOE_OK
+    fused = lib.moe_route_multihot_fused
+    assert fused(64, 8) == 1 and fused(8, 2) == 1 and fused(4, 4) == 1
+    assert fused(6, 2) == 0 and fused(128, 8) == 0 and fused(64, 17) == 0 and fused(8, 9) == 0
 
 
 def test_align_validation(lib):

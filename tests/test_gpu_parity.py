@@ -229,6 +229,37 @@ def test_multihot_random(T, E, k, inv):
                     E)
 
 
+@pytest.mark.parametrize("T,E,k,norm,ties", [(16384, 64, 8, True, False), (1, 64, 8, True, False),
+                                             (37, 8, 2, False, True), (1000, 64, 16, True, True),
+                                             (5, 4, 4, True, False), (301, 12, 3, False, False),
+                                             (60, 6, 2, True, False), (33, 130, 7, True, False)])
+def test_route_multihot_fused(T, E, k, norm, ties):
+    """moe_route_multihot: every output bit-identical to moe_route followed by
+    moe_indices_to_multihot (fused kernel where E <= 64, E % 4 == 0, k <= 16;
+    the two launches otherwise), ids equal to the oracle's, multihot equal to
+    the oracle's conversion of the weights."""
+    g = np.random.Generator(np.random.PCG64(T * 131 + E * 7 + k))
+    x = g.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        x = np.round(x * 2) / 2  # many equal logits per row
+    tw, ti, mh, pim, pos = moe.moe_route_multihot(dev(x), k, norm)
+    rw, ri = moe.moe_route(dev(x), k, norm)
+    rmh, rpim, rpos = moe.moe_indices_to_multihot(ri, rw, E)
+    torch.cuda.synchronize()
+    assert moe.moe_route_multihot_fused(E, k) == (E <= 64 and E % 4 == 0 and k <= 16)
+    assert torch.equal(ti, ri)
+    assert torch.equal(tw.view(torch.int32), rw.view(torch.int32))
+    assert torch.equal(mh, rmh)
+    assert torch.equal(pim.view(torch.int32), rpim.view(torch.int32))
+    assert torch.equal(pos, rpos)
+    _, oids = oracle.route(x, k, norm)
+    np.testing.assert_array_equal(ti.cpu().numpy(), oids)
+    omh, opim, opos = oracle.indices_to_multihot(ti.cpu().numpy(), tw.cpu().numpy(), E)
+    np.testing.assert_array_equal(mh.cpu().numpy(), omh)
+    np.testing.assert_array_equal(pim.cpu().numpy().view(np.int32), opim.view(np.int32))
+    np.testing.assert_array_equal(pos.cpu().numpy(), opos)
+
+
 def test_multihot_worked_examples():
     ids = np.array([[0, 1], [1, 2]], np.int32)
     probs = np.array([[0.1, 0.2], [0.3, 0.4]], np.float32)
