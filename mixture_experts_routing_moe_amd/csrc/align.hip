@@ -11,14 +11,14 @@
 //   2. align_scatter: each block sums the partials into per-expert totals,
 //                     the exclusive offsets (the indptr) and the first
 //                     position it may write for each expert, then walks its
-//                     chunk in order, 256 slots at a time; a slot's rank among
+//                     chunk in order, 512 slots at a time; a slot's rank among
 //                     earlier slots of the same expert comes from ballots
 //                     inside its wave plus the counts of the waves before it,
 //                     so positions follow the flat slot order t*k+j --
 //                     ascending token inside each expert, exactly the order
 //                     of the pages' cumsum.
 //
-//   With at most 1024 slots one scatter block does it all, counting the ids
+//   With at most 512 slots one scatter block does it all, counting the ids
 //   itself, and the histogram kernel is skipped.
 //
 // Only integer LDS atomics on private counters are used, and no result
@@ -28,8 +28,19 @@
 namespace moe {
 namespace {
 
-constexpr int kAlignThreads = 256;
-constexpr int kPartialBudget = 12288;  // cap on nb * E partial counts each scatter block sums
+#ifndef MOE_ALIGN_THREADS
+#define MOE_ALIGN_THREADS 512
+#endif
+constexpr int kAlignThreads = MOE_ALIGN_THREADS;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+#ifndef MOE_ALIGN_BUDGET
+#define MOE_ALIGN_BUDGET 16384
+#endif
+#ifndef MOE_ALIGN_SLOTS
+#define MOE_ALIGN_SLOTS 512
+#endif
+constexpr int kPartialBudget = MOE_ALIGN_BUDGET;  // cap on nb * E partial counts each scatter block sums
+constexpr int kSlotsPerBlock = MOE_ALIGN_SLOTS;   // slots per block before the cap
 
 int64_t align_chunk(int64_t n, int nb) {
     int64_t c = (n + nb - 1) / nb;
@@ -96,11 +107,11 @@ __device__ int block_exclusive_scan(const int32_t *v, int32_t *out, int n, int32
 // Scan + scatter.  Every block first turns the per-block histograms into the
 // expert totals, the exclusive expert offsets and its own first position per
 // expert (block 0 also writes counts and offsets); then it walks its chunk
-// in order, 256 slots at a time: a slot's rank among earlier slots of the
+// in order, 512 slots at a time: a slot's rank among earlier slots of the
 // same expert comes from ballots inside its wave plus the counts of the
 // waves before it, so positions follow the flat slot order.
 //
-// With one block (n <= 1024 slots: decode batches) the block counts the ids
+// With one block (n <= 512 slots: decode batches) the block counts the ids
 // itself (fused_hist) and the histogram kernel is not launched.
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
@@ -108,11 +119,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
     int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
     extern __shared__ int32_t sm[];
-    // LDS: run[E] | wcnt[4][E] | tot[E] | off[E] | tot_part[P][E] | pre_part[P][E] | wsum[4]
+    // LDS: run[E] | wcnt[W][E] | tot[E] | off[E] | tot_part[P][E] | pre_part[P][E] | wsum[W]
+    // (W waves, P parts)
     const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
     int32_t *run = sm;
     int32_t *wcnt = run + E;
-    int32_t *tot = wcnt + 4 * E;
+    int32_t *tot = wcnt + kAlignWaves * E;
     int32_t *off = tot + E;
     int32_t *tot_part = off + E;
     int32_t *pre_part = tot_part + parts * E;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         tot[e] = all;
         run[e] = pre;
     }
-    for (int i = tid; i < 4 * E; i += kAlignThreads) wcnt[i] = 0;
+    for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wcnt[i] = 0;
     __syncthreads();
     const int total = block_exclusive_scan(tot, off, E, wsum);
     for (int e = tid; e < E; e += kAlignThreads) {
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
 }  // namespace
 
 int align_num_blocks(int64_t n, int E) {
-    int64_t nb = (n + 1023) / 1024;
+    int64_t nb = (n + kSlotsPerBlock - 1) / kSlotsPerBlock;
     int64_t cap = kPartialBudget / E;
     if (cap < 1) cap = 1;
     if (nb > cap) nb = cap;
@@ -241,7 +253,8 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
         if (err != hipSuccess) return err;
     }
     const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
-    const size_t lds = (size_t)(7 * E + 2 * parts * E + kAlignThreads / kWave) * sizeof(int32_t);
+    const size_t lds =
+        (size_t)((3 + kAlignWaves) * E + 2 * parts * E + kAlignWaves) * sizeof(int32_t);
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
                        k, E, (int)chunk, nbits, nb, fused, ws, counts, offsets, sorted_tok,
                        sorted_slot, slot_to_sorted);
