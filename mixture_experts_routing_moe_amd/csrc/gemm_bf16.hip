@@ -69,6 +69,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int NF = BN / WN / 32;  // weight fragments per wave
 constexpr int MF = BM / WM / 32;  // token fragments per wave
 constexpr int kXcdChunk = 32;  // CUs per XCD: tiles an XCD runs at once
+constexpr int kBandMTiles = 4;  // m-tiles per band of the tile order (at least)
 // LDS: the NS token stages, then the NS weight stages, so every fragment
 // address is a per-lane base plus a constant below 64 KiB (the ds_read offset
 // field).
@@ -103,13 +104,12 @@ struct MTile {
 
 // Tile index -> (expert, rows, n-tile).  Expert e owns mt_e = ceil(count_e /
 // BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
-// tile index, ordered n-tile-major: consecutive tiles are the expert's
-// m-tiles under one weight n-tile.  The segment is dealt to the m-tiles in
-// near-equal whole fragments (1040 rows: 3 x 288 + 176) instead of
-// 3 x 320 + 80, so the tiles sharing a weight tile do similar work and stay
-// in step (measured faster for both GEMMs).  A running sum of mt_e over the
-// experts (64 per pass, one per lane) finds the owner.  Every wave computes
-// the same answer, so no LDS is needed.
+// tile index, in bands of m-tiles (below).  The segment is dealt to the
+// m-tiles in near-equal whole fragments (1040 rows: 3 x 288 + 176) instead
+// of 3 x 320 + 80, so the tiles sharing a weight tile do similar work and
+// stay in step (measured faster for both GEMMs).  A running sum of mt_e over
+// the experts (64 per pass, one per lane) finds the owner.  Every wave
+// computes the same answer, so no LDS is needed.
 __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int n_tiles,
                           MTile &t, int &nt) {
     const int lane = lane_id();
@@ -138,9 +138,18 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             const int mt = readlane_i(tiles, src);
             const int o0 = readlane_i(off, src);
             const int cn = readlane_i(cnt, src);
+            // Tile j of the expert: bands of a m-tiles, each band's tiles
+            // n-tile-major, so the kXcdChunk tiles an XCD runs together span
+            // about a m-tiles x kXcdChunk / a n-tiles and share both operands
+            // in its L2 (with all m-tiles of a big expert under one n-tile,
+            // its token rows were re-read for every n-tile).
             const int j = L - ex * n_tiles;
-            nt = j / mt;
-            const int i = j - nt * mt;
+            const int a = min(mt, max(kBandMTiles, kXcdChunk / n_tiles));
+            const int b = j / (a * n_tiles);
+            const int r = j - b * a * n_tiles;
+            const int ab = min(a, mt - b * a);
+            nt = r / ab;
+            const int i = b * a + (r - nt * ab);
             t.e = c + src;
             // Rows per m-tile: the expert's rows dealt in equal shares
             // rounded up to whole 32-row fragments (at most BM; never an
