@@ -22,6 +22,13 @@ Workloads (ids as used in seeds):
 3. Mixtral-shaped   T=4096,  H=4096, I=14336, E=8,  k=2  (bf16)
 4. fine-grained     T=8192,  H=2048, I=1408,  E=64, k=8  (bf16, skewed)
 5. decode           T=1|32,  H=2048, I=1408,  E=64, k=8  (bf16, skewed)
+6. grouped routing, noaux_tc              T=16384, E=256, 8 groups, 4 kept, k=8
+7. grouped routing, group_limited_greedy  T=16384, E=160, 8 groups, 3 kept, k=6
+
+The grouped-routing scores are the logistic function of N(0,1) draws
+(computed in float64, rounded to float32), i.e. values in (0, 1) as a
+sigmoid gate gives them; noaux_tc's correction bias is N(0, 0.1^2) per
+expert, float32.
 """
 
 from __future__ import annotations
@@ -59,6 +66,26 @@ WORKLOADS = {
                             bias="zipf1.1"),
     "decode1": Workload(5, "decode1", T=1, E=64, k=8, H=2048, I=1408, bias="zipf1.1"),
     "decode32": Workload(5, "decode32", T=32, E=64, k=8, H=2048, I=1408, bias="zipf1.1"),
+}
+
+
+@dataclass(frozen=True)
+class GroupedWorkload:
+    wid: int
+    name: str
+    T: int
+    E: int
+    k: int
+    n_group: int
+    topk_group: int
+    method: str  # "noaux_tc" | "group_limited_greedy"
+
+
+GROUPED = {
+    "grouped_noaux": GroupedWorkload(6, "grouped_noaux", T=16384, E=256, k=8, n_group=8,
+                                     topk_group=4, method="noaux_tc"),
+    "grouped_greedy": GroupedWorkload(7, "grouped_greedy", T=16384, E=160, k=6, n_group=8,
+                                      topk_group=3, method="group_limited_greedy"),
 }
 
 
@@ -212,3 +239,19 @@ def random_ids(seed: int, T: int, E: int, k: int, invalid_frac: float = 0.0) -> 
 def random_probs(seed: int, T: int, k: int) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(seed))
     return np.ascontiguousarray(g.random((T, k)).astype(np.float32))
+
+
+def grouped_scores(w: GroupedWorkload, T: int | None = None, draw: int = 0) -> np.ndarray:
+    """[T, E] float32 scores in (0, 1): the logistic function of N(0,1) draws."""
+    T = w.T if T is None else T
+    g = generator(w.wid, S_LOGITS if draw == 0 else 100 + draw)
+    x = g.standard_normal((T, w.E))
+    return np.ascontiguousarray((1.0 / (1.0 + np.exp(-x))).astype(np.float32))
+
+
+def correction_bias(w: GroupedWorkload) -> np.ndarray | None:
+    """noaux_tc's per-expert score correction bias, N(0, 0.1^2) float32 (None otherwise)."""
+    if w.method != "noaux_tc":
+        return None
+    g = generator(w.wid, S_BIAS)
+    return np.ascontiguousarray((g.standard_normal(w.E) * 0.1).astype(np.float32))

@@ -41,13 +41,14 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_route.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_route_grouped.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
         lib.oracle_moe_cumsum.argtypes = [vp, i64, i32, i32, vp]
         lib.oracle_align.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp]
         lib.oracle_indices_to_multihot.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
         lib.oracle_multihot_to_indices.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_expert_ffn.argtypes = [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                           vp, i64, vp, i32]
-        for f in (lib.oracle_route, lib.oracle_moe_cumsum, lib.oracle_align,
+        for f in (lib.oracle_route, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
                   lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
                   lib.oracle_expert_ffn):
             f.restype = ctypes.c_int
@@ -75,6 +76,26 @@ def route(logits: np.ndarray, k: int, norm_topk_prob: bool = True):
     w = np.empty((T, k), np.float64)
     ids = np.empty((T, k), np.int32)
     _check(_load().oracle_route(_p(x), T, E, k, int(bool(norm_topk_prob)), _p(w), _p(ids)), "route")
+    return w, ids
+
+
+GROUP_METHODS = {"group_limited_greedy": 0, "noaux_tc": 1}
+
+
+def route_grouped(scores: np.ndarray, k: int, n_group: int, topk_group: int, method: str,
+                  bias: np.ndarray | None = None, renormalize: bool = False):
+    """Group-limited top-k (greedy or noaux_tc) -> (w [T,k] f64, ids [T,k] i32)."""
+    x = _c(scores, np.float32)
+    T, E = x.shape
+    m = GROUP_METHODS[method]
+    b = None if bias is None else _c(bias, np.float32)
+    if b is not None:
+        assert b.shape == (E,)
+    w = np.empty((T, k), np.float64)
+    ids = np.empty((T, k), np.int32)
+    _check(_load().oracle_route_grouped(_p(x), _p(b) if b is not None else None, T, E, k,
+                                        n_group, topk_group, m, int(bool(renormalize)), _p(w),
+                                        _p(ids)), "route_grouped")
     return w, ids
 
 

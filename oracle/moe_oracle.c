@@ -128,6 +128,126 @@ int oracle_route(const float *logits, int64_t T, int32_t E, int32_t k,
 }
 
 /*
+ * Insertion top-k over the entries of v[0..n) that have use[e] != 0, taken in
+ * ascending e: each entry goes to the first place where the list is unfilled
+ * or the entry is strictly greater than the held value, shifting the rest
+ * down ([mlc] _gating_topk_process_value; empty places lose to everything).
+ * Returns how many places were filled (min(k, number of usable entries)).
+ */
+static int insert_topk(const float *v, const unsigned char *use, int32_t n, int32_t k,
+                       float *val, int32_t *idx)
+{
+    int filled = 0;
+    for (int32_t e = 0; e < n; ++e) {
+        if (use && !use[e])
+            continue;
+        for (int i = 0; i < k; ++i) {
+            if (i == filled || v[e] > val[i]) {
+                int last = filled < k ? filled : k - 1;
+                for (int j = last; j > i; --j) {
+                    val[j] = val[j - 1];
+                    idx[j] = idx[j - 1];
+                }
+                val[i] = v[e];
+                idx[i] = e;
+                if (filled < k)
+                    ++filled;
+                break;
+            }
+        }
+    }
+    return filled;
+}
+
+/*
+ * Group-limited expert selection, [mlc] group_limited_greedy_topk.
+ *
+ * The E experts of a row form n_group groups of E / n_group consecutive
+ * experts.  The score used for choosing is the float32 score, plus (method 1,
+ * "noaux_tc") the float32 per-expert correction bias, added in float32 as
+ * the page adds two float32 tensors.  A group's score is its largest choice
+ * score (method 0, "group_limited_greedy") or the float32 sum of its two
+ * largest (method 1; the page's top-2 then sum).  The topk_group best groups
+ * are kept (top-k order: value descending, lower group first on ties), the
+ * experts of the other groups are masked out, and the k best remaining
+ * experts are selected in the same order.  The page fills masked entries
+ * with float32's lowest finite value, which its strict-greater insertion
+ * never takes; here they are simply skipped (the two agree whenever at least
+ * k experts remain, which is required: k <= topk_group * group size).
+ *
+ * Weights: method 0 returns the selected choice scores (the scores
+ * themselves); method 1 gathers the scores WITHOUT the bias at the selected
+ * experts.  renormalize != 0 divides them by their sum (not on the page;
+ * the optional renormalisation callers apply to these weights), in double.
+ *
+ * Every comparison is between float32 values, as on the page, so the
+ * selection is exactly the page's; only the renormalisation runs in double.
+ */
+int oracle_route_grouped(const float *scores, const float *bias, int64_t T, int32_t E,
+                         int32_t k, int32_t n_group, int32_t topk_group, int32_t method,
+                         int32_t renormalize, double *topk_w, int32_t *topk_ids)
+{
+    if (T < 0 || E < 1 || k < 1 || n_group < 1 || E % n_group != 0 || topk_group < 1 ||
+        topk_group > n_group || (method != 0 && method != 1))
+        return ORACLE_EINVAL;
+    const int32_t gs = E / n_group;
+    if (k > topk_group * gs || (method == 1 && (gs < 2 || bias == NULL)))
+        return ORACLE_EINVAL;
+    float *choice = (float *)malloc(sizeof(float) * (size_t)E);
+    float *gscore = (float *)malloc(sizeof(float) * (size_t)n_group);
+    unsigned char *use = (unsigned char *)malloc((size_t)E);
+    float *val = (float *)malloc(sizeof(float) * (size_t)(k > topk_group ? k : topk_group));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k > topk_group ? k : topk_group));
+    if (!choice || !gscore || !use || !val || !idx) {
+        free(choice);
+        free(gscore);
+        free(use);
+        free(val);
+        free(idx);
+        return ORACLE_ENOMEM;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *s = scores + t * E;
+        for (int32_t e = 0; e < E; ++e)
+            choice[e] = method == 1 ? s[e] + bias[e] : s[e];
+        for (int32_t g = 0; g < n_group; ++g) {
+            const float *c = choice + (int64_t)g * gs;
+            if (method == 1) {
+                float top2[2];
+                int32_t at[2];
+                insert_topk(c, NULL, gs, 2, top2, at);
+                gscore[g] = top2[0] + top2[1];
+            } else {
+                float m = c[0];
+                for (int32_t j = 1; j < gs; ++j)
+                    if (c[j] > m)
+                        m = c[j];
+                gscore[g] = m;
+            }
+        }
+        insert_topk(gscore, NULL, n_group, topk_group, val, idx);
+        memset(use, 0, (size_t)E);
+        for (int32_t i = 0; i < topk_group; ++i)
+            memset(use + (int64_t)idx[i] * gs, 1, (size_t)gs);
+        insert_topk(choice, use, E, k, val, idx);
+        double sum = 0.0;
+        for (int32_t i = 0; i < k; ++i)
+            sum += (double)s[idx[i]];
+        for (int32_t i = 0; i < k; ++i) {
+            double w = (double)s[idx[i]];
+            topk_w[t * k + i] = renormalize ? w / sum : w;
+            topk_ids[t * k + i] = idx[i];
+        }
+    }
+    free(choice);
+    free(gscore);
+    free(use);
+    free(val);
+    free(idx);
+    return ORACLE_OK;
+}
+
+/*
  * [mlc] moe_cumsum: expert_mask[t][e] = 1 when any of row t's k ids equals e;
  * transpose to [E, T], flatten, inclusive int32 prefix sum.  An id outside
  * [0, E) matches no column, so it is dropped.  cs must hold E*T entries.

@@ -100,6 +100,147 @@ def test_route_shift_invariance():
 
 
 # --------------------------------------------------------------------------
+# Group-limited routing (group_limited_greedy / noaux_tc)
+# --------------------------------------------------------------------------
+
+def _grouped_bruteforce(scores, bias, k, n_group, topk_group, method):
+    """Same selection by whole-array sorting instead of insertion: group scores
+    from a sort of each group, groups and experts ranked with np.lexsort
+    (value descending, lower index first)."""
+    T, E = scores.shape
+    gs = E // n_group
+    choice = scores if bias is None else (scores + bias[None, :]).astype(np.float32)
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        grp = choice[t].reshape(n_group, gs)
+        if method == "noaux_tc":
+            srt = np.sort(grp, axis=1)
+            gsc = (srt[:, -1] + srt[:, -2]).astype(np.float32)  # float32 add
+        else:
+            gsc = grp.max(axis=1)
+        keep = np.lexsort((np.arange(n_group), -gsc.astype(np.float64)))[:topk_group]
+        cand = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in keep])
+        order = np.lexsort((cand, -choice[t, cand].astype(np.float64)))
+        ids[t] = cand[order[:k]]
+    return ids
+
+
+def test_grouped_crafted_rows_tell_the_methods_apart():
+    # Four groups of two.  Group maxima: 0.9, 0.5, 0.2, 0.3 -> greedy keeps
+    # group 0 and selects experts 0, 1.  Sums of the top two: 0.9, 1.0, 0.3,
+    # 0.35 -> noaux_tc keeps group 1; its two equal scores come out lower id
+    # first.
+    s = np.array([[0.90, 0.00, 0.50, 0.50, 0.10, 0.20, 0.30, 0.05]], np.float32)
+    w, ids = oracle.route_grouped(s, 2, 4, 1, "group_limited_greedy")
+    assert ids.tolist() == [[0, 1]]
+    assert w.tolist() == [[float(np.float32(0.9)), 0.0]]
+    w, ids = oracle.route_grouped(s, 2, 4, 1, "noaux_tc", bias=np.zeros(8, np.float32))
+    assert ids.tolist() == [[2, 3]] and w.tolist() == [[0.5, 0.5]]
+    # With two groups kept greedy takes groups 0 and 1 and then the best two
+    # experts of those: 0 (0.9), then 2 and 3 tie at 0.5 -> 2.
+    _, ids = oracle.route_grouped(s, 2, 4, 2, "group_limited_greedy")
+    assert ids.tolist() == [[0, 2]]
+
+
+def test_grouped_bias_steers_choice_but_not_weights():
+    # Two groups of four.  Unbiased top-two sums: 1.1 vs 1.07 -> group 0.  A
+    # +0.1 bias on experts 4, 5 lifts group 1 to 1.27 -> experts 4, 5, whose
+    # weights are their UNbiased scores; renormalised they sum to 1.
+    s = np.array([[0.6, 0.5, 0.1, 0.1, 0.55, 0.52, 0.2, 0.2]], np.float32)
+    zero = np.zeros(8, np.float32)
+    b = np.array([0, 0, 0, 0, 0.1, 0.1, 0, 0], np.float32)
+    w, ids = oracle.route_grouped(s, 2, 2, 1, "noaux_tc", bias=zero)
+    assert ids.tolist() == [[0, 1]]
+    w, ids = oracle.route_grouped(s, 2, 2, 1, "noaux_tc", bias=b)
+    assert ids.tolist() == [[4, 5]]
+    assert w.tolist() == [[float(np.float32(0.55)), float(np.float32(0.52))]]
+    w, _ = oracle.route_grouped(s, 2, 2, 1, "noaux_tc", bias=b, renormalize=True)
+    a, c = float(np.float32(0.55)), float(np.float32(0.52))
+    np.testing.assert_allclose(w[0], [a / (a + c), c / (a + c)], rtol=1e-15)
+
+
+@pytest.mark.parametrize("method", ["group_limited_greedy", "noaux_tc"])
+def test_grouped_all_groups_kept_is_plain_topk(method):
+    # topk_group = n_group masks nothing: the selection is the plain top-k of
+    # the choice scores (full sort), the weights the scores at those ids.
+    g = np.random.Generator(np.random.PCG64(71))
+    s = g.random((40, 64)).astype(np.float32)
+    b = (g.standard_normal(64) * 0.1).astype(np.float32) if method == "noaux_tc" else None
+    w, ids = oracle.route_grouped(s, 6, 8, 8, method, bias=b)
+    choice = s if b is None else (s + b[None, :]).astype(np.float32)
+    np.testing.assert_array_equal(ids, _sort_topk(choice, 6))
+    np.testing.assert_array_equal(w, np.take_along_axis(s, ids, 1).astype(np.float64))
+
+
+def test_grouped_singleton_groups_is_plain_topk():
+    # Groups of one expert: greedy's group scores are the scores themselves,
+    # so keeping the k best groups and then the k best experts is plain top-k.
+    g = np.random.Generator(np.random.PCG64(72))
+    s = g.random((30, 16)).astype(np.float32)
+    _, ids = oracle.route_grouped(s, 4, 16, 4, "group_limited_greedy")
+    np.testing.assert_array_equal(ids, _sort_topk(s, 4))
+
+
+def test_grouped_all_equal_row():
+    s = np.full((1, 32), 0.25, np.float32)
+    for method, b in (("group_limited_greedy", None), ("noaux_tc", np.zeros(32, np.float32))):
+        _, ids = oracle.route_grouped(s, 5, 8, 3, method, bias=b)
+        assert ids.tolist() == [[0, 1, 2, 3, 4]]  # groups 0..2 kept, lowest ids first
+
+
+@pytest.mark.parametrize("method,E,n_group,topk_group,k", [
+    ("noaux_tc", 256, 8, 4, 8), ("group_limited_greedy", 160, 8, 3, 6),
+    ("noaux_tc", 64, 4, 2, 6), ("group_limited_greedy", 64, 16, 5, 9)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_grouped_matches_sort_bruteforce(method, E, n_group, topk_group, k, ties):
+    g = np.random.Generator(np.random.PCG64(E + n_group * 7 + k))
+    s = g.random((48, E)).astype(np.float32)
+    if ties:
+        s = (np.round(s * 6) / 6).astype(np.float32)
+    b = (g.standard_normal(E) * 0.1).astype(np.float32) if method == "noaux_tc" else None
+    if ties and b is not None:
+        b = (np.round(b * 8) / 8).astype(np.float32)
+    for renorm in (False, True):
+        w, ids = oracle.route_grouped(s, k, n_group, topk_group, method, bias=b,
+                                      renormalize=renorm)
+        np.testing.assert_array_equal(ids, _grouped_bruteforce(s, b, k, n_group, topk_group,
+                                                               method))
+        raw = np.take_along_axis(s, ids, 1).astype(np.float64)
+        if renorm:
+            np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(w, raw / raw.sum(1, keepdims=True), rtol=1e-15)
+        else:
+            np.testing.assert_array_equal(w, raw)
+        # Every selected expert lies in one of at most topk_group groups.
+        assert max(len(set((ids[t] // (E // n_group)).tolist())) for t in range(len(ids))) \
+            <= topk_group
+
+
+def test_grouped_rejects_bad_shapes():
+    s = np.zeros((2, 12), np.float32)
+    with pytest.raises(ValueError):
+        oracle.route_grouped(s, 2, 5, 1, "group_limited_greedy")  # 12 % 5 != 0
+    with pytest.raises(ValueError):
+        oracle.route_grouped(s, 7, 4, 2, "group_limited_greedy")  # k > 2 groups x 3
+    with pytest.raises(ValueError):
+        oracle.route_grouped(s, 2, 4, 2, "noaux_tc")  # noaux_tc needs the bias
+    with pytest.raises(ValueError):
+        oracle.route_grouped(s, 1, 12, 2, "noaux_tc", bias=np.zeros(12, np.float32))  # groups of 1
+
+
+def test_grouped_workload_inputs():
+    for w in mi.GROUPED.values():
+        s = mi.grouped_scores(w, T=64)
+        assert s.shape == (64, w.E) and s.dtype == np.float32
+        assert (s > 0).all() and (s < 1).all()
+        b = mi.correction_bias(w)
+        assert (b is None) == (w.method != "noaux_tc")
+        _, ids = oracle.route_grouped(s, w.k, w.n_group, w.topk_group, w.method, bias=b)
+        np.testing.assert_array_equal(ids, _grouped_bruteforce(s, b, w.k, w.n_group,
+                                                               w.topk_group, w.method))
+
+
+# --------------------------------------------------------------------------
 # Alignment (cumsum, indptr, indices)
 # --------------------------------------------------------------------------
 
