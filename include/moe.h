@@ -6,6 +6,7 @@
  *
  *   moe_route                 gating softmax + top-k (optionally renormalised)
  *   moe_route_multihot        moe_route + moe_indices_to_multihot in one pass
+ *   moe_route_grouped         group-limited top-k (group_limited_greedy, noaux_tc)
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
@@ -58,11 +59,16 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 3
+#define MOE_VERSION 4
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
 #define MOE_DECODE_MAX_T 64
 #define MOE_MAX_SPLITS 8
+#define MOE_MAX_GROUPS 64
+
+/* moe_route_grouped methods */
+#define MOE_GROUP_LIMITED_GREEDY 0
+#define MOE_NOAUX_TC 1
 
 typedef enum {
     MOE_OK = 0,
@@ -117,6 +123,35 @@ moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32
                                 int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
                                 uint8_t *multihot, float *probs_in_multihot,
                                 int32_t *position_map, void *stream);
+
+/*
+ * moe_route_grouped -- group-limited top-k expert selection.
+ * [mlc] group_limited_greedy_topk (methods "group_limited_greedy", "noaux_tc").
+ *
+ * scores    [T, E] float32 routing scores (e.g. a softmax or sigmoid of the
+ *           gating logits, computed by the caller), finite and greater than
+ *           float32's lowest finite value.
+ * e_score_correction_bias
+ *           [E] float32, read only by MOE_NOAUX_TC (may be NULL for
+ *           MOE_GROUP_LIMITED_GREEDY).
+ * The E experts form n_group groups of E / n_group consecutive experts.  The
+ * choice score of an expert is its score (greedy) or score + bias, added in
+ * float32 (noaux_tc).  A group's score is its largest choice score (greedy)
+ * or the float32 sum of its two largest (noaux_tc).  The topk_group best
+ * groups are kept and the k best experts among them selected; both rankings
+ * are value descending, equal values keeping the lower index first.
+ * topk_ids  [T, k] int32 out: selected experts in descending choice order.
+ * topk_w    [T, k] float32 out: the scores (without the bias) of the selected
+ *           experts; renormalize != 0 divides them by their sum.
+ * Requires E % n_group == 0, 1 <= n_group <= MOE_MAX_GROUPS,
+ * 1 <= topk_group <= n_group, 1 <= k <= min(MOE_MAX_TOPK,
+ * topk_group * E / n_group), E <= MOE_MAX_EXPERTS, and groups of at least
+ * two experts for noaux_tc.  Pointers 4-byte aligned.
+ */
+moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
+                               int64_t T, int32_t E, int32_t k, int32_t n_group,
+                               int32_t topk_group, int32_t method, int32_t renormalize,
+                               float *topk_w, int32_t *topk_ids, void *stream);
 
 /* 1 if moe_route_multihot runs as one kernel for this E and k (E <= 64,
  * E % 4 == 0, k <= 16, k <= E), else 0. */

@@ -25,7 +25,10 @@ MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_DECODE_MAX_T = 64
 MOE_MAX_SPLITS = 8
-MOE_VERSION = 3
+MOE_VERSION = 4
+MOE_MAX_GROUPS = 64
+MOE_GROUP_LIMITED_GREEDY = 0
+MOE_NOAUX_TC = 1
 
 # name -> (restype, argtypes), mirroring include/moe.h
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -37,6 +40,8 @@ SIGNATURES = {
     "moe_route": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_route_multihot": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_multihot_fused": (_i32, [_i32, _i32]),
+    "moe_route_grouped": (_st, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                _vp]),
     "moe_align_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_align": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_indices_to_multihot": (_st, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),

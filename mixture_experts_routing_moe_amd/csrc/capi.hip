@@ -128,6 +128,43 @@ moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32
                       "moe_route_multihot");
 }
 
+moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
+                               int64_t T, int32_t E, int32_t k, int32_t n_group,
+                               int32_t topk_group, int32_t method, int32_t renormalize,
+                               float *topk_w, int32_t *topk_ids, void *stream) {
+    const char *fn = "moe_route_grouped";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(method == MOE_GROUP_LIMITED_GREEDY || method == MOE_NOAUX_TC, MOE_ERR_INVALID_ARG,
+          "%s: unknown method %d", fn, method);
+    CHECK(n_group >= 1 && n_group <= MOE_MAX_GROUPS, MOE_ERR_INVALID_ARG,
+          "%s: n_group = %d outside [1, %d]", fn, n_group, MOE_MAX_GROUPS);
+    CHECK(E % n_group == 0, MOE_ERR_INVALID_ARG, "%s: E = %d not a multiple of n_group = %d", fn,
+          E, n_group);
+    CHECK(topk_group >= 1 && topk_group <= n_group, MOE_ERR_INVALID_ARG,
+          "%s: topk_group = %d outside [1, n_group = %d]", fn, topk_group, n_group);
+    const int32_t gs = E / n_group;
+    CHECK(k <= topk_group * gs, MOE_ERR_INVALID_ARG,
+          "%s: k = %d > topk_group * group size = %d", fn, k, topk_group * gs);
+    CHECK(method != MOE_NOAUX_TC || gs >= 2, MOE_ERR_INVALID_ARG,
+          "%s: noaux_tc needs groups of at least 2 experts (E / n_group = %d)", fn, gs);
+    if (T == 0) return MOE_OK;
+    CHECK(scores && topk_w && topk_ids, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(method != MOE_NOAUX_TC || e_score_correction_bias, MOE_ERR_INVALID_ARG,
+          "%s: noaux_tc needs e_score_correction_bias", fn);
+    const auto a4 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    CHECK(a4(scores) && a4(topk_w) && a4(topk_ids) &&
+              (method != MOE_NOAUX_TC || a4(e_score_correction_bias)),
+          MOE_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+    return hip_status(moe::launch_route_grouped(scores,
+                                                method == MOE_NOAUX_TC ? e_score_correction_bias
+                                                                       : nullptr,
+                                                T, E, k, n_group, topk_group,
+                                                method == MOE_NOAUX_TC, renormalize != 0, topk_w,
+                                                topk_ids, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 int32_t moe_route_multihot_fused(int32_t E, int32_t k) {
     return E >= 1 && k >= 1 && k <= E && E <= 64 && E % 4 == 0 && k <= 16;
 }

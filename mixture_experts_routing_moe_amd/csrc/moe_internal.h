@@ -115,6 +115,10 @@ hipError_t launch_route_multihot(const float *logits, int64_t T, int E, int k, i
                                  float *w, int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
                                  hipStream_t s);
 
+hipError_t launch_route_grouped(const float *scores, const float *bias, int64_t T, int E, int k,
+                                int n_group, int topk_group, int noaux, int renorm, float *w,
+                                int32_t *ids, hipStream_t s);
+
 int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,

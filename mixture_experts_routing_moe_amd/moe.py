@@ -56,6 +56,34 @@ def moe_route(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, topk_w=
     return topk_w, topk_ids
 
 
+GROUP_METHODS = {"group_limited_greedy": _lib.MOE_GROUP_LIMITED_GREEDY,
+                 "noaux_tc": _lib.MOE_NOAUX_TC}
+
+
+def moe_route_grouped(scores: torch.Tensor, k: int, n_group: int, topk_group: int,
+                      method: str = "noaux_tc", e_score_correction_bias=None,
+                      renormalize: bool = False, topk_w=None, topk_ids=None):
+    """Group-limited top-k (group_limited_greedy / noaux_tc) over [T, E] float32
+    scores -> (topk_w [T,k] f32, topk_ids [T,k] i32)."""
+    if scores.dtype != torch.float32 or scores.dim() != 2:
+        raise ValueError("scores must be [T, E] float32")
+    if method not in GROUP_METHODS:
+        raise ValueError(f"method must be one of {sorted(GROUP_METHODS)}")
+    T, E = scores.shape
+    b = e_score_correction_bias
+    if b is not None and (b.dtype != torch.float32 or b.shape != (E,)):
+        raise ValueError("e_score_correction_bias must be [E] float32")
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    _dev(scores, b, topk_w, topk_ids)
+    check(lib().moe_route_grouped(_ptr(scores), _ptr(b), T, E, k, n_group, topk_group,
+                                  GROUP_METHODS[method], int(bool(renormalize)), _ptr(topk_w),
+                                  _ptr(topk_ids), _stream()), "moe_route_grouped")
+    return topk_w, topk_ids
+
+
 def moe_route_multihot(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, out=None):
     """moe_route + moe_indices_to_multihot of its output, one pass where the
     library fuses them -> (topk_w, topk_ids, multihot, probs_in_multihot,

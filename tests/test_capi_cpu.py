@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_version() == 3
+    assert lib.moe_version() == 4
     for s in range(5):
         assert lib.moe_status_string(s)
     assert lib.moe_status_string(99) == b"unknown status"
@@ -75,6 +75,28 @@ def test_route_validation(lib):
     assert status(lib, "moe_route", FAKE, -1, 8, 2, 1, FAKE, FAKE, None) == I
     assert status(lib, "moe_route", None, 4, 8, 2, 1, FAKE, FAKE, None) == I  # null
     assert status(lib, "moe_route", None, 0, 8, 2, 1, None, None, None) == _lib.MOE_OK  # T=0
+
+
+def test_route_grouped_validation(lib):
+    I = _lib.MOE_ERR_INVALID_ARG
+    G, N = _lib.MOE_GROUP_LIMITED_GREEDY, _lib.MOE_NOAUX_TC
+
+    def rg(T, E, k, ng, tg, m, scores=FAKE, bias=FAKE, w=FAKE, ids=FAKE):
+        return lib.moe_route_grouped(scores, bias, T, E, k, ng, tg, m, 0, w, ids, None)
+
+    assert rg(4, 250, 8, 8, 4, N) == I  # E % n_group != 0
+    assert b"not a multiple" in lib.moe_last_error()
+    assert rg(4, 256, 8, 8, 9, N) == I  # topk_group > n_group
+    assert rg(4, 256, 8, 8, 0, N) == I  # topk_group < 1
+    assert rg(4, 256, 8, 128, 4, G) == I  # n_group > 64
+    assert rg(4, 64, 9, 8, 1, G) == I  # k > topk_group * group size
+    assert b"group size" in lib.moe_last_error()
+    assert rg(4, 64, 2, 64, 4, N) == I  # noaux_tc with groups of one
+    assert rg(4, 64, 2, 8, 2, 7) == I  # unknown method
+    assert rg(4, 64, 2, 8, 2, N, bias=None) == I  # noaux_tc without the bias
+    assert rg(4, 64, 2, 8, 2, G, scores=None) == I
+    assert rg(4, 64, 2, 8, 2, G, scores=ctypes.c_void_p(0x1002)) == I  # misaligned
+    assert rg(0, 64, 2, 8, 2, N, scores=None, bias=None, w=None, ids=None) == _lib.MOE_OK
 
 
 def test_route_multihot_validation(lib):

@@ -140,6 +140,73 @@ def test_route_empty():
 
 
 # --------------------------------------------------------------------------
+# Group-limited routing (group_limited_greedy / noaux_tc)
+# --------------------------------------------------------------------------
+
+def _grouped_check(s, k, n_group, topk_group, method, bias, renorm, scores_dev=None):
+    sd = dev(s) if scores_dev is None else scores_dev
+    bd = None if bias is None else dev(bias)
+    w, ids = moe.moe_route_grouped(sd, k, n_group, topk_group, method, bd, renorm)
+    torch.cuda.synchronize()
+    ow, oids = oracle.route_grouped(s, k, n_group, topk_group, method, bias=bias,
+                                    renormalize=renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    if renorm:
+        assert_weights_close(w.cpu().numpy(), ow)
+    else:  # the scores themselves, copied
+        np.testing.assert_array_equal(w.cpu().numpy().astype(np.float64), ow)
+
+
+@pytest.mark.parametrize("name", sorted(mi.GROUPED))
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_grouped_workloads(name, renorm):
+    w = mi.GROUPED[name]
+    print(f"grouped routing workload {name} T={w.T} E={w.E} renorm={renorm}", flush=True)
+    _grouped_check(mi.grouped_scores(w), w.k, w.n_group, w.topk_group, w.method,
+                   mi.correction_bias(w), renorm)
+
+
+@pytest.mark.parametrize("T,E,n_group,topk_group,k", [
+    (333, 16, 4, 2, 3), (70, 64, 8, 3, 8), (1, 64, 64, 64, 64), (129, 90, 9, 4, 7),
+    (257, 96, 4, 1, 24), (200, 160, 8, 3, 6), (64, 256, 1, 1, 8), (100, 256, 8, 8, 64),
+    (77, 384, 12, 5, 16), (40, 1024, 64, 7, 14), (33, 1000, 8, 2, 50)])
+@pytest.mark.parametrize("method", ["group_limited_greedy", "noaux_tc"])
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_grouped_shapes(T, E, n_group, topk_group, k, method, ties):
+    if method == "noaux_tc" and E // n_group < 2:
+        pytest.skip("noaux_tc needs groups of two or more")
+    g = np.random.Generator(np.random.PCG64(T * 7 + E + n_group + k))
+    s = g.random((T, E)).astype(np.float32)
+    b = (g.standard_normal(E) * 0.1).astype(np.float32) if method == "noaux_tc" else None
+    if ties:  # few distinct values: equal scores, equal group scores
+        s = (np.round(s * 4) / 4).astype(np.float32)
+        if b is not None:
+            b = (np.round(b * 4) / 4).astype(np.float32)
+    print(f"grouped T={T} E={E} n_group={n_group} topk_group={topk_group} k={k} {method} "
+          f"ties={ties}", flush=True)
+    for renorm in (False, True):
+        _grouped_check(s, k, n_group, topk_group, method, b, renorm)
+
+
+def test_route_grouped_unaligned_rows():
+    # Scores starting 4 bytes past a 16-byte boundary take the scalar loads.
+    w = mi.GROUPED["grouped_noaux"]
+    s = mi.grouped_scores(w, T=300)
+    flat = torch.zeros(s.size + 1, dtype=torch.float32, device=DEV)
+    flat[1:] = dev(s.reshape(-1))
+    sd = flat[1:].view(300, w.E)
+    assert sd.data_ptr() % 16 == 4
+    _grouped_check(s, w.k, w.n_group, w.topk_group, w.method, mi.correction_bias(w), True,
+                   scores_dev=sd)
+
+
+def test_route_grouped_empty():
+    w, ids = moe.moe_route_grouped(torch.empty((0, 64), dtype=torch.float32, device=DEV), 4, 8,
+                                   2, "group_limited_greedy")
+    assert w.shape == (0, 4) and ids.shape == (0, 4)
+
+
+# --------------------------------------------------------------------------
 # Align
 # --------------------------------------------------------------------------
 
