@@ -41,6 +41,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_route.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_router_logits.argtypes = [i32, vp, vp, i64, i32, i32, vp]
         lib.oracle_route_grouped.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp]
         lib.oracle_moe_cumsum.argtypes = [vp, i64, i32, i32, vp]
         lib.oracle_align.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp]
@@ -48,7 +49,7 @@ def _load():
         lib.oracle_multihot_to_indices.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_expert_ffn.argtypes = [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                           vp, i64, vp, i32]
-        for f in (lib.oracle_route, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
+        for f in (lib.oracle_route, lib.oracle_router_logits, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
                   lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
                   lib.oracle_expert_ffn):
             f.restype = ctypes.c_int
@@ -77,6 +78,21 @@ def route(logits: np.ndarray, k: int, norm_topk_prob: bool = True):
     ids = np.empty((T, k), np.int32)
     _check(_load().oracle_route(_p(x), T, E, k, int(bool(norm_topk_prob)), _p(w), _p(ids)), "route")
     return w, ids
+
+
+def router_logits(hidden: np.ndarray, w_gate: np.ndarray, dtype: str) -> np.ndarray:
+    """logits [T,E] f64 = hidden [T,H] . w_gate[E,H]^T ("f32": float32 arrays,
+    "bf16": uint16 bit patterns)."""
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    npdt = np.float32 if dt == 0 else np.uint16
+    x = _c(hidden, npdt)
+    w = _c(w_gate, npdt)
+    T, H = x.shape
+    E, H2 = w.shape
+    assert H2 == H
+    out = np.empty((T, E), np.float64)
+    _check(_load().oracle_router_logits(dt, _p(x), _p(w), T, H, E, _p(out)), "router_logits")
+    return out
 
 
 GROUP_METHODS = {"group_limited_greedy": 0, "noaux_tc": 1}

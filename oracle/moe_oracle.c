@@ -128,6 +128,30 @@ int oracle_route(const float *logits, int64_t T, int32_t E, int32_t k,
 }
 
 /*
+ * Router logits, the step before gating: logits[t][e] = sum over h of
+ * hidden[t][h] * w_gate[e][h], i.e. a linear layer y = x . W^T with W stored
+ * [out, in] ([p6] moe_decode_experts / moe_prefill_experts apply their
+ * expert weights the same way).  The pages take the logits as given; this is
+ * the plain definition, one dot product per (token, expert), in double from
+ * float32 (dt=0) or bfloat16-bits (dt=1) inputs, summed in ascending h.
+ */
+int oracle_router_logits(int32_t dt, const void *hidden, const void *w_gate, int64_t T,
+                         int32_t H, int32_t E, double *logits)
+{
+    if (T < 0 || H < 1 || E < 1 || (dt != 0 && dt != 1))
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                acc += load_elem(dt, hidden, t * H + h) * load_elem(dt, w_gate, (int64_t)e * H + h);
+            logits[t * E + e] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Insertion top-k over the entries of v[0..n) that have use[e] != 0, taken in
  * ascending e: each entry goes to the first place where the list is unfilled
  * or the entry is strictly greater than the held value, shifting the rest

@@ -100,6 +100,37 @@ def test_route_shift_invariance():
 
 
 # --------------------------------------------------------------------------
+# Router logits (the linear gate before routing)
+# --------------------------------------------------------------------------
+
+def test_router_logits_one_hot_rows_pick_weight_columns():
+    # A token that is the unit vector e_h has logits W[:, h], exactly.
+    g = np.random.Generator(np.random.PCG64(81))
+    H, E = 64, 12
+    w = mi.f32_to_bf16_bits(g.standard_normal((E, H)).astype(np.float32))
+    x = np.zeros((H, H), np.float32)
+    x[np.arange(H), np.arange(H)] = 1.0
+    got = oracle.router_logits(mi.f32_to_bf16_bits(x), w, "bf16")
+    np.testing.assert_array_equal(got, mi.bf16_bits_to_f32(w).astype(np.float64).T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_logits_match_library_matmul(dtype):
+    g = np.random.Generator(np.random.PCG64(82))
+    T, H, E = 37, 256, 20
+    x = g.standard_normal((T, H)).astype(np.float32)
+    w = (g.standard_normal((E, H)) / 16).astype(np.float32)
+    if dtype == "bf16":
+        xb, wb = mi.f32_to_bf16_bits(x), mi.f32_to_bf16_bits(w)
+        x, w = mi.bf16_bits_to_f32(xb), mi.bf16_bits_to_f32(wb)
+        got = oracle.router_logits(xb, wb, "bf16")
+    else:
+        got = oracle.router_logits(x, w, "f32")
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+# --------------------------------------------------------------------------
 # Group-limited routing (group_limited_greedy / noaux_tc)
 # --------------------------------------------------------------------------
 
