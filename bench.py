@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral",
-                   choices=["mixtral", "finegrained", "decode1", "decode32", "routing"])
+                   choices=["mixtral", "finegrained", "decode1", "decode32", "routing",
+                            "grouped_noaux", "grouped_greedy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", type=int, default=None,
                    help="1: time the whole step as one captured HIP graph replay (the "
@@ -90,9 +91,15 @@ def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
 
     threads = len(os.sched_getaffinity(0))
     has_ffn = "hidden" in inp
+    grouped = hasattr(w, "n_group")
+
     def run(n):
         t0 = time.perf_counter()
-        tw, ids = oracle.route(inp["logits"][:n], w.k, w.norm)
+        if grouped:
+            tw, ids = oracle.route_grouped(inp["logits"][:n], w.k, w.n_group, w.topk_group,
+                                           w.method, bias=inp["bias"], renormalize=w.renorm)
+        else:
+            tw, ids = oracle.route(inp["logits"][:n], w.k, w.norm)
         oracle.align(ids, w.E)
         if has_ffn:
             oracle.expert_ffn(inp["hidden"][:n], inp["w13"], inp["w2"], tw, ids,
@@ -119,7 +126,8 @@ def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
         passes += 1
         t_total += dt
     what = ("route + align + expert FFN + combine" if has_ffn else
-            "route + align + indices->multihot + multihot->indices")
+            f"{'grouped ' if grouped else ''}route + align + indices->multihot + "
+            "multihot->indices")
     return {"value": n * passes / t_total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens x {passes} pass(es): {what} in float64, "
@@ -149,10 +157,16 @@ def main():
     import mixture_experts_routing_moe_amd as moe
     import moe_inputs as mi
 
-    w = mi.WORKLOADS[args.workload]
+    grouped = args.workload in mi.GROUPED
+    w = mi.GROUPED[args.workload] if grouped else mi.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = mi.layer_inputs(w)
+    if grouped:
+        # Group-limited routing: [T, E] scores and (noaux_tc) the correction bias.
+        inp = {"logits": mi.grouped_scores(w), "bias": mi.correction_bias(w)}
+        bias_d = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev)
+    else:
+        inp = mi.layer_inputs(w)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -160,11 +174,15 @@ def main():
     T, E, k = w.T, w.E, w.k
     decode = w.name.startswith("decode")
     draws = args.draws if args.draws is not None else (32 if decode else 1)
-    routing_only = w.H == 0
+    routing_only = grouped or w.H == 0
     flush = bool(args.flush if args.flush is not None else (decode or routing_only))
     use_graph = bool(args.graph if args.graph is not None else (decode or routing_only))
-    logits_draws = [torch.from_numpy(inp["logits"] if r == 0 else mi.gating_logits_draw(w, r))
-                    .to(dev) for r in range(draws)]
+    def draw(r):
+        if r == 0:
+            return inp["logits"]
+        return mi.grouped_scores(w, draw=r) if grouped else mi.gating_logits_draw(w, r)
+
+    logits_draws = [torch.from_numpy(draw(r)).to(dev) for r in range(draws)]
     flush_buf = torch.empty(128 << 20, dtype=torch.float32, device=dev) if flush else None
     has_ffn = "hidden" in inp
 
@@ -196,6 +214,8 @@ def main():
     # Route and the indices->multihot conversion of its output run as one
     # call (one kernel where the library fuses them, see config).
     phases = ["route_multihot", "align", "to_indices"]
+    if grouped:  # group-limited selection, then the same conversions
+        phases = ["route_grouped", "align", "to_multihot", "to_indices"]
     if has_ffn:
         phases += ["gate_up", "down", "combine"]
 
@@ -204,6 +224,11 @@ def main():
     def run_phase(name):
         if name == "route_multihot":
             moe.moe_route_multihot(cur["logits"], k, w.norm, (topk_w, topk_ids, mh, pim, pos))
+        elif name == "route_grouped":
+            moe.moe_route_grouped(cur["logits"], k, w.n_group, w.topk_group, w.method, bias_d,
+                                  w.renorm, topk_w, topk_ids)
+        elif name == "to_multihot":
+            moe.moe_indices_to_multihot(topk_ids, topk_w, E, out=(mh, pim, pos))
         elif name == "align":
             moe.moe_align(topk_ids, E, aligned, align_ws)
         elif name == "to_indices":
@@ -288,11 +313,16 @@ def main():
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = T * 1e3 / ms_per_step
 
-    cfg = {"workload": w.name, "T": T, "E": E, "top_k": k, "norm_topk_prob": w.norm,
+    cfg = {"workload": w.name, "T": T, "E": E, "top_k": k,
            "routing_draws": draws, "cache_flush_between_steps": flush,
            "step_timing": "hip_graph_replay" if graph_ms is not None else "eager",
-           "eager_ms_per_step": round(eager_ms, 4),
-           "route_multihot_fused": moe.moe_route_multihot_fused(E, k)}
+           "eager_ms_per_step": round(eager_ms, 4)}
+    if grouped:
+        cfg.update({"method": w.method, "n_group": w.n_group, "topk_group": w.topk_group,
+                    "renormalize": w.renorm})
+    else:
+        cfg.update({"norm_topk_prob": w.norm,
+                    "route_multihot_fused": moe.moe_route_multihot_fused(E, k)})
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())
@@ -326,12 +356,17 @@ def main():
         # Algorithmic HBM bytes per phase: every input read once, every output
         # written once.
         nb = {"route_multihot": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
+              "route_grouped": T * E * 4 + E * 4 + T * k * 8,
+              "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
               "to_indices": T * E * 8 + T * k * 8}
+        nb = {ph: nb[ph] for ph in phases}
         dom = max(phase_ms, key=phase_ms.get)
         names = {"route_multihot": "route_rows16_kernel (route + multihot)",
+                 "route_grouped": "route_grouped_kernel",
+                 "to_multihot": "to_multihot kernel",
                  "align": "align_hist_kernel + align_scatter_kernel",
-                 "to_indices": "to_indices_rows16_kernel"}
+                 "to_indices": "to_indices kernel"}
         achieved = nb[dom] / (phase_ms[dom] * 1e-3) / 1e9
         roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

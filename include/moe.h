@@ -7,6 +7,7 @@
  *   moe_route                 gating softmax + top-k (optionally renormalised)
  *   moe_route_multihot        moe_route + moe_indices_to_multihot in one pass
  *   moe_route_grouped         group-limited top-k (group_limited_greedy, noaux_tc)
+ *   moe_router_route          router GEMM (hidden . w_gate^T) + moe_route, one pass
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
@@ -123,6 +124,28 @@ moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32
                                 int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
                                 uint8_t *multihot, float *probs_in_multihot,
                                 int32_t *position_map, void *stream);
+
+/*
+ * moe_router_route -- the router GEMM that produces the gating logits,
+ * followed by moe_route on them, in one pass where E <= 64 and k <= 16
+ * (otherwise the GEMM kernel, then moe_route's kernel).
+ * The logits are logits = hidden . w_gate^T (a linear layer, W stored
+ * [out, in] as in [p6]); the pages take them as given.  Routing as moe_route
+ * ([mlc] gating_topk, gating_softmax_topk).
+ *
+ * dt        MOE_BF16 (other dtypes return MOE_ERR_UNSUPPORTED).
+ * hidden    [T, H] bf16, w_gate [E, H] bf16; 16-byte aligned.
+ * logits    [T, E] float32 out: fp32 accumulation of the bf16 products (the
+ *           summation order is the kernel's, so values can differ from an
+ *           exact dot product by rounding).
+ * topk_w, topk_ids  [T, k] out: exactly moe_route(logits, ...) on the
+ *           logits written.
+ * Requires H % 64 == 0 (else MOE_ERR_UNSUPPORTED), 1 <= k <= min(E,
+ * MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS.
+ */
+moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_gate, int64_t T,
+                              int32_t H, int32_t E, int32_t k, int32_t norm_topk_prob,
+                              float *logits, float *topk_w, int32_t *topk_ids, void *stream);
 
 /*
  * moe_route_grouped -- group-limited top-k expert selection.

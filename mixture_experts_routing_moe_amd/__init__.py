@@ -21,4 +21,5 @@ from .moe import (  # noqa: F401
     moe_route_grouped,
     moe_route_multihot,
     moe_route_multihot_fused,
+    moe_router_route,
 )

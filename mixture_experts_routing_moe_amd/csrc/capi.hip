@@ -128,6 +128,33 @@ moe_status_t moe_route_multihot(const float *logits, int64_t T, int32_t E, int32
                       "moe_route_multihot");
 }
 
+moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_gate, int64_t T,
+                              int32_t H, int32_t E, int32_t k, int32_t norm_topk_prob,
+                              float *logits, float *topk_w, int32_t *topk_ids, void *stream) {
+    const char *fn = "moe_router_route";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
+    CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn,
+          (int)dt);
+    CHECK(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: only bf16 hidden / w_gate", fn);
+    CHECK(H >= 1, MOE_ERR_INVALID_ARG, "%s: H = %d < 1", fn, H);
+    CHECK(H % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: H = %d must be a multiple of 64", fn, H);
+    if (T == 0) return MOE_OK;
+    CHECK(hidden && w_gate && logits && topk_w && topk_ids, MOE_ERR_INVALID_ARG,
+          "%s: null pointer", fn);
+    CHECK(aligned16(hidden) && aligned16(w_gate), MOE_ERR_INVALID_ARG,
+          "%s: hidden and w_gate must be 16-byte aligned", fn);
+    const auto a4 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    CHECK(a4(logits) && a4(topk_w) && a4(topk_ids), MOE_ERR_INVALID_ARG,
+          "%s: outputs must be 4-byte aligned", fn);
+    return hip_status(moe::launch_router_route(static_cast<const uint16_t *>(hidden),
+                                               static_cast<const uint16_t *>(w_gate), T, H, E, k,
+                                               norm_topk_prob != 0, logits, topk_w, topk_ids,
+                                               static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
                                int64_t T, int32_t E, int32_t k, int32_t n_group,
                                int32_t topk_group, int32_t method, int32_t renormalize,

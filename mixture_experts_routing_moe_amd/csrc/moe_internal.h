@@ -94,6 +94,71 @@ __device__ __forceinline__ float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// One routing row held by a 16-lane DPP row (g = lane / 16, q = lane % 16):
+// lane q holds the logits v[0..3] of experts 4q .. 4q+3, `avail` marks which
+// of them exist.  Selects the row's top k (value descending, the lower expert
+// id first among equal values) in k rounds: a lane-local best, a 4-step DPP
+// maximum over the row on order-preserving keys, and one ballot (the lowest
+// lane holding the maximum wins); a second maximum broadcasts the winner's
+// local slot.  Returns the weight of slot q (lanes q < k; softmax over the k
+// selected logits if norm, else the full softmax at the selected expert),
+// computed in double and rounded once.  sel_e = expert of slot q; byte i of
+// slot_of = the round that picked local expert i (0xFF if none).  Rows with
+// no available expert (past T) select nothing; lanes q >= k get sel_e = -1.
+__device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, int k, int norm,
+                                             int g, int q, int &sel_e, uint32_t &slot_of) {
+    const uint32_t valid = avail;
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = float_key(v[i]);
+
+    uint32_t sel_key = 0, kmax = 0;
+    sel_e = -1;
+    slot_of = 0xFFFFFFFFu;
+    for (int r = 0; r < k; ++r) {
+        // Lane-local best; strict > keeps the lowest local slot on ties.
+        uint32_t bk = 0;
+        int bi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (((avail >> i) & 1u) && key[i] > bk) {
+                bk = key[i];
+                bi = i;
+            }
+        }
+        const uint32_t rmax = row16_max_u32(bk);
+        const uint64_t cand = __ballot(bk != 0 && bk == rmax);
+        const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
+        const int wl = __ffs((int)mrow) - 1;  // -1 only for rows without experts
+        const bool is_w = q == wl;
+        if (is_w) {
+            avail &= ~(1u << bi);
+            slot_of = (slot_of & ~(0xFFu << (8 * bi))) | ((uint32_t)r << (8 * bi));
+        }
+        const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
+        if (q == r) {
+            sel_key = rmax;
+            sel_e = wl * 4 + (int)wbi;
+        }
+        if (r == 0) kmax = rmax;
+    }
+
+    // Weights in double, rounded once to float.
+    const double mx = (double)key_float(kmax);
+    const double ex = q < k ? exp((double)key_float(sel_key) - mx) : 0.0;
+    double part;
+    if (norm) {
+        part = ex;
+    } else {
+        part = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((valid >> i) & 1u) part += exp((double)v[i] - mx);
+    }
+    const double sum = row16_sum_f64(part);
+    return (float)(ex / sum);
+}
+
 // SiLU in float32: z / (1 + e^-z).
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about
 // 1 ulp) instead of an IEEE division: the result is rounded to bf16 next,
@@ -118,6 +183,10 @@ hipError_t launch_route_multihot(const float *logits, int64_t T, int E, int k, i
 hipError_t launch_route_grouped(const float *scores, const float *bias, int64_t T, int E, int k,
                                 int n_group, int topk_group, int noaux, int renorm, float *w,
                                 int32_t *ids, hipStream_t s);
+
+hipError_t launch_router_route(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H,
+                               int E, int k, int norm, float *logits, float *w, int32_t *ids,
+                               hipStream_t s);
 
 int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,

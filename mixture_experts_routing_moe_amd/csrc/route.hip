@@ -135,56 +135,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
                 }
             }
         }
-        const uint32_t valid = avail;
-        uint32_t key[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) key[i] = float_key(v[i]);
-
-        uint32_t sel_key = 0, kmax = 0;
-        int sel_e = -1;
-        uint32_t slot_of = 0xFFFFFFFFu;  // byte i: round that picked local expert i
-        for (int r = 0; r < k; ++r) {
-            // Lane-local best; strict > keeps the lowest local slot on ties.
-            uint32_t bk = 0;
-            int bi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (((avail >> i) & 1u) && key[i] > bk) {
-                    bk = key[i];
-                    bi = i;
-                }
-            }
-            const uint32_t rmax = row16_max_u32(bk);
-            const uint64_t cand = __ballot(bk != 0 && bk == rmax);
-            const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
-            const int wl = __ffs((int)mrow) - 1;  // -1 only for rows past T
-            const bool is_w = q == wl;
-            if (is_w) {
-                avail &= ~(1u << bi);
-                slot_of = (slot_of & ~(0xFFu << (8 * bi))) | ((uint32_t)r << (8 * bi));
-            }
-            const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
-            if (q == r) {
-                sel_key = rmax;
-                sel_e = wl * 4 + (int)wbi;
-            }
-            if (r == 0) kmax = rmax;
-        }
-
-        // Weights in double, rounded once to float.
-        const double mx = (double)key_float(kmax);
-        const double ex = q < k ? exp((double)key_float(sel_key) - mx) : 0.0;
-        double part;
-        if (norm) {
-            part = ex;
-        } else {
-            part = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if ((valid >> i) & 1u) part += exp((double)v[i] - mx);
-        }
-        const double sum = row16_sum_f64(part);
-        const float wq = (float)(ex / sum);
+        uint32_t slot_of;  // byte i: round that picked local expert i (0xFF: none)
+        int sel_e;
+        const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
         if (row_ok && q < k) {
             topk_w[t * k + q] = wq;
             topk_ids[t * k + q] = sel_e;

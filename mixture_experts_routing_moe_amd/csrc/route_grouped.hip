@@ -13,12 +13,17 @@
 //
 // The pages run this as five separate operators (bias add, per-group top-2 or
 // max, top-k over groups, a masking pass that writes a full [T, E] copy, and a
-// top-k over that copy, plus a gather for noaux_tc).  Here one wave does a
-// whole row in one pass: the row is read once into registers (lane l holds
-// experts l*VPL .. l*VPL+VPL-1), the choice scores go to the wave's slice of
-// LDS, lane g reduces group g from there, and the group and expert rankings
-// are rounds of a cross-lane argmax on order-preserving integer keys.  The
-// masked [T, E] copy never exists.
+// top-k over that copy, plus a gather for noaux_tc).  Here each row is done in
+// one pass from registers, and the masked [T, E] copy never exists.  Two
+// kernels:
+//  * route_grouped_rows16_kernel (E % 16 == 0, E <= 256, n_group dividing 16,
+//    k <= 16): 4 rows per wave, 16 lanes per row, each group on whole lanes;
+//    group scores merge over the group's lanes with DPP.
+//  * route_grouped_kernel (any other shape): one wave per row (lane l holds
+//    experts l*VPL .. l*VPL+VPL-1); the choice scores go to the wave's slice
+//    of LDS and lane g reduces group g from there.
+// In both, the group and expert rankings are rounds of a cross-lane argmax on
+// order-preserving integer keys.
 #include "moe_internal.h"
 
 namespace moe {
@@ -195,6 +200,206 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_kernel(
     }
 }
 
+// Fast path: E % 16 == 0, E <= 256, n_group dividing 16, k <= 16.  A wave
+// holds 4 rows, 16 lanes per row; lane q of a row holds the vpl = E / 16
+// consecutive experts q*vpl .. q*vpl+vpl-1, so a group of E / n_group experts
+// is exactly LG = 16 / n_group lanes and group scores come from a DPP merge
+// over those lanes (no LDS).  Every round of either ranking is a 4-step DPP
+// maximum over the row's 16 lanes on order-preserving keys plus one ballot;
+// the lowest lane holding the maximum wins, which is the lowest group or
+// expert id among equal values.
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<ctrl>(__float_as_uint(v)));
+}
+
+// Merge the two largest values (m1 >= m2) of this lane and of its DPP partner.
+template <int ctrl>
+__device__ __forceinline__ void merge_top2(float &m1, float &m2) {
+    const float o1 = dpp_f32<ctrl>(m1), o2 = dpp_f32<ctrl>(m2);
+    m2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+    m1 = fmaxf(m1, o1);
+}
+
+// Order-preserving key of a choice score; adding +0.0 first turns -0.0 into
+// +0.0, so equal scores get equal keys.  Every float maps above 0.
+__device__ __forceinline__ uint32_t choice_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+template <int VPL, bool NOAUX>
+__global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
+    const float *__restrict__ scores, const float *__restrict__ bias, int64_t T, int k,
+    int lg_log2, int topk_group, int renorm, int vec, float *__restrict__ topk_w,
+    int32_t *__restrict__ topk_ids) {
+    constexpr int E = 16 * VPL;
+    constexpr int W = VPL % 4 == 0 ? 4 : (VPL % 2 == 0 ? 2 : 1);  // load width
+    const int lane = lane_id();
+    const int seg = lane >> 4;
+    const int q = lane & 15;
+    const int e0 = q * VPL;
+    const int n_group = 16 >> lg_log2;
+    const int my_group = q >> lg_log2;
+    const bool mask_groups = topk_group < n_group;
+
+    float b[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) b[i] = NOAUX ? bias[e0 + i] : 0.0f;
+
+    const int64_t wave = (int64_t)blockIdx.x * kGroupedWaves + threadIdx.x / kWave;
+    const int64_t nwaves = (int64_t)gridDim.x * kGroupedWaves;
+    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
+        const int64_t t = t0 + seg;
+        const bool row_ok = t < T;
+        const float *row = scores + t * E + e0;
+        float c[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) c[i] = 0.0f;
+        if (row_ok) {
+            if (W > 1 && vec) {  // rows aligned to the load width
+#pragma unroll
+                for (int j = 0; j < VPL / W; ++j) {
+                    if constexpr (W == 4) {
+                        const float4 x = reinterpret_cast<const float4 *>(row)[j];
+                        c[4 * j] = x.x;
+                        c[4 * j + 1] = x.y;
+                        c[4 * j + 2] = x.z;
+                        c[4 * j + 3] = x.w;
+                    } else if constexpr (W == 2) {
+                        const float2 x = reinterpret_cast<const float2 *>(row)[j];
+                        c[2 * j] = x.x;
+                        c[2 * j + 1] = x.y;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) c[i] = row[i];
+            }
+        }
+        uint32_t key[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            if (NOAUX) c[i] = c[i] + b[i];  // float32 add, as on the page
+            key[i] = row_ok ? choice_key(c[i]) : 0u;
+        }
+
+        if (mask_groups) {
+            // This lane's largest (greedy) or two largest (noaux_tc) choice
+            // scores, merged over the LG lanes of its group.
+            float m1 = c[0], m2 = -INFINITY;
+#pragma unroll
+            for (int i = 1; i < VPL; ++i) {
+                if (NOAUX) m2 = fmaxf(m2, fminf(m1, c[i]));
+                m1 = fmaxf(m1, c[i]);
+            }
+            if (NOAUX) {
+                if (lg_log2 >= 1) merge_top2<kDppXor1>(m1, m2);
+                if (lg_log2 >= 2) merge_top2<kDppXor2>(m1, m2);
+                if (lg_log2 >= 3) merge_top2<kDppHalfMirror>(m1, m2);
+                if (lg_log2 >= 4) merge_top2<kDppMirror>(m1, m2);
+            } else {
+                if (lg_log2 >= 1) m1 = fmaxf(m1, dpp_f32<kDppXor1>(m1));
+                if (lg_log2 >= 2) m1 = fmaxf(m1, dpp_f32<kDppXor2>(m1));
+                if (lg_log2 >= 3) m1 = fmaxf(m1, dpp_f32<kDppHalfMirror>(m1));
+                if (lg_log2 >= 4) m1 = fmaxf(m1, dpp_f32<kDppMirror>(m1));
+            }
+            uint32_t gkey = row_ok ? choice_key(NOAUX ? m1 + m2 : m1) : 0u;
+            bool kept = false;
+            for (int r = 0; r < topk_group; ++r) {
+                const uint32_t m = row16_max_u32(gkey);
+                const uint64_t cand = __ballot(gkey != 0 && gkey == m);
+                const uint32_t bits = (uint32_t)(cand >> (seg * 16)) & 0xFFFFu;
+                const int wg = (__ffs((int)bits) - 1) >> lg_log2;  // < 0 past T
+                if (bits != 0 && my_group == wg) {
+                    gkey = 0;
+                    kept = true;
+                }
+            }
+            if (!kept) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) key[i] = 0u;
+            }
+        }
+
+        int sel_e = -1;
+        for (int r = 0; r < k; ++r) {
+            // Lane-local best; strict > keeps the lowest local index on ties.
+            uint32_t bk = key[0];
+            int bi = 0;
+#pragma unroll
+            for (int i = 1; i < VPL; ++i) {
+                if (key[i] > bk) {
+                    bk = key[i];
+                    bi = i;
+                }
+            }
+            const uint32_t m = row16_max_u32(bk);
+            const uint64_t cand = __ballot(bk != 0 && bk == m);
+            const uint32_t bits = (uint32_t)(cand >> (seg * 16)) & 0xFFFFu;
+            const int wl = __ffs((int)bits) - 1;  // -1 only for rows past T
+            const bool is_w = q == wl;
+            const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
+            if (is_w) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i)
+                    if (i == bi) key[i] = 0u;
+            }
+            if (q == r) sel_e = wl * VPL + (int)wbi;
+        }
+
+        // The weight is the score (without the bias) of the selected expert,
+        // read back from the row just loaded.
+        const bool out = row_ok && q < k;
+        float w = 0.0f;
+        if (out) w = scores[t * E + sel_e];
+        float w_out = w;
+        if (renorm) {
+            const double s = row16_sum_f64(out ? (double)w : 0.0);
+            w_out = (float)((double)w / s);
+        }
+        if (out) {
+            topk_w[t * k + q] = w_out;
+            topk_ids[t * k + q] = sel_e;
+        }
+    }
+}
+
+template <int VPL, bool NOAUX>
+hipError_t launch_rows16_t(const float *scores, const float *bias, int64_t T, int k,
+                           int n_group, int topk_group, int renorm, float *w, int32_t *ids,
+                           hipStream_t s) {
+    int64_t blocks = (T + 4 * kGroupedWaves - 1) / (4 * kGroupedWaves);
+    if (blocks > 16384) blocks = 16384;
+    constexpr int W = VPL % 4 == 0 ? 4 : (VPL % 2 == 0 ? 2 : 1);
+    const int vec = (reinterpret_cast<uintptr_t>(scores) & (4u * W - 1)) == 0;
+    int lg_log2 = 0;
+    while ((16 >> lg_log2) > n_group) ++lg_log2;
+    hipLaunchKernelGGL((route_grouped_rows16_kernel<VPL, NOAUX>), dim3((unsigned)blocks),
+                       dim3(kGroupedThreads), 0, s, scores, bias, T, k, lg_log2, topk_group,
+                       renorm, vec, w, ids);
+    return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t launch_rows16(const float *scores, const float *bias, int64_t T, int E, int k,
+                         int n_group, int topk_group, int noaux, int renorm, float *w,
+                         int32_t *ids, hipStream_t s) {
+    if (E != 16 * VPL)
+        return launch_rows16<VPL + 1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm,
+                                      w, ids, s);
+    if (noaux)
+        return launch_rows16_t<VPL, true>(scores, bias, T, k, n_group, topk_group, renorm, w, ids,
+                                          s);
+    return launch_rows16_t<VPL, false>(scores, bias, T, k, n_group, topk_group, renorm, w, ids,
+                                       s);
+}
+template <>
+hipError_t launch_rows16<17>(const float *, const float *, int64_t, int, int, int, int, int,
+                             int, float *, int32_t *, hipStream_t) {
+    return hipErrorInvalidValue;  // unreachable: E <= 256 is checked by the caller
+}
+
 template <int VPL>
 hipError_t launch_vpl(const float *scores, const float *bias, int64_t T, int E, int k,
                       int n_group, int topk_group, int noaux, int renorm, float *w, int32_t *ids,
@@ -215,6 +420,9 @@ hipError_t launch_route_grouped(const float *scores, const float *bias, int64_t 
                                 int n_group, int topk_group, int noaux, int renorm, float *w,
                                 int32_t *ids, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (E % 16 == 0 && E <= 256 && 16 % n_group == 0 && k <= 16)
+        return launch_rows16<1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm, w, ids,
+                                s);
     if (E <= 64)
         return launch_vpl<1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm, w, ids, s);
     if (E <= 128)

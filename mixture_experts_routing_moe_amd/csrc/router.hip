@@ -1,0 +1,202 @@
+// Router GEMM + gating top-k in one kernel.
+//
+// The step before routing: logits = hidden . w_gate^T (a linear gate, W
+// stored [E, H] as every weight of this layer is stored [out, in]), then the
+// gating top-k of mlc-llm moe_misc.py (gating_topk, gating_softmax_topk) on
+// those logits.  The pages take the logits as given; fusing the gate into the
+// routing pass means the [T, E] logits are written once (they are an output)
+// and never read back.
+//
+// A block owns MC chunks of 16 tokens and EB blocks of 16 experts.  Its 4
+// waves split H into contiguous quarters and feed MFMA 16x16x32 bf16 (gate
+// rows as the A operand, tokens as B, fp32 accumulation), batching KB k-steps
+// of loads before their MFMAs; the 4 partial sums meet in LDS in a fixed
+// order.  Wave 0 writes the logits and an LDS copy of the tile, from which
+// all 4 waves route the block's rows with the same 16-lanes-per-row
+// selection as moe_route (so the ids and weights are exactly moe_route's on
+// these logits).  For E > 64 or k > 16 the kernel only computes logits
+// (blocks also split over experts) and moe_route's general kernel selects
+// from them.
+//
+// What bounds it is the bytes each CU loads: besides its token rows, every
+// block reads the whole gate matrix (E x H bf16, 256 KB at E = 64, H = 2048)
+// from L2, and one CU streams on the order of 40-60 GB/s.  Staging the token
+// tile in LDS with direct loads (all of it in flight at once), 8 or 16 waves
+// per block, or one 16-token chunk per block all measured slower on the
+// part.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouterThreads = 256;
+constexpr int kRouterKB = 4;  // k-steps of 32 per load batch
+
+__device__ __forceinline__ bf16x8 zero_unless(bool keep, bf16x8 v) {
+    return keep ? v : bf16x8{};
+}
+
+template <int MC, int EB>
+__global__ __launch_bounds__(kRouterThreads) void router_route_kernel(
+    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ wg, int64_t T, int H, int E,
+    int k, int norm, int do_route, float *__restrict__ logits, float *__restrict__ topk_w,
+    int32_t *__restrict__ topk_ids) {
+    __shared__ f32x4 red[3][MC][EB][kWave];
+    __shared__ float s_log[MC * 16][EB * 16];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * (MC * 16);
+    const int e_base = blockIdx.y * (EB * 16);
+
+    // Rows past T or E read a valid row; their results are never stored.
+    const uint16_t *xr[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+        const int64_t t = min(t0 + mc * 16 + i, T - 1);
+        xr[mc] = hidden + t * H + kq * 8;
+    }
+    const uint16_t *wr[EB];
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+        const int e = min(e_base + eb * 16 + i, E - 1);
+        wr[eb] = wg + (int64_t)e * H + kq * 8;
+    }
+    f32x4 acc[MC][EB];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) acc[mc][eb] = f32x4{};
+
+    const int ksteps = H / 32;
+    const int per = (ksteps + 3) / 4;
+    const int s0 = wave * per;
+    const int s1 = min(ksteps, s0 + per);
+    for (int s = s0; s < s1; s += kRouterKB) {
+        bf16x8 xa[kRouterKB][MC], wa[kRouterKB][EB];
+#pragma unroll
+        for (int j = 0; j < kRouterKB; ++j) {
+            const int ss = min(s + j, s1 - 1) * 32;
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+                xa[j][mc] = *reinterpret_cast<const bf16x8 *>(xr[mc] + ss);
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+                wa[j][eb] = *reinterpret_cast<const bf16x8 *>(wr[eb] + ss);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kRouterKB; ++j) {
+            const bool in = s + j < s1;
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb) {
+                const bf16x8 w = zero_unless(in, wa[j][eb]);
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc)
+                    acc[mc][eb] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xa[j][mc], acc[mc][eb], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (wave > 0) {
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb) red[wave - 1][mc][eb][lane] = acc[mc][eb];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // Accumulator r holds expert row 4 kq + r of the block and token column i.
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            const int tl = mc * 16 + i;
+            const int64_t t = t0 + tl;
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb) {
+                f32x4 a = acc[mc][eb];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) a += red[w][mc][eb][lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int el = eb * 16 + kq * 4 + r;
+                    const int e = e_base + el;
+                    s_log[tl][el] = a[r];
+                    if (t < T && e < E) logits[t * E + e] = a[r];
+                }
+            }
+        }
+    }
+    if (!do_route) return;  // uniform over the launch
+    __syncthreads();
+
+    const int g = lane >> 4;
+    const int q = lane & 15;
+#pragma unroll
+    for (int p = 0; p < MC; ++p) {
+        const int rl = p * 16 + wave * 4 + g;
+        const int64_t t = t0 + rl;
+        float v[4];
+        uint32_t avail = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * q + j;
+            v[j] = 0.0f;
+            if (t < T && e < E) {
+                v[j] = s_log[rl][e];
+                avail |= 1u << j;
+            }
+        }
+        uint32_t slot_of;
+        int sel_e;
+        const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
+        if (t < T && q < k) {
+            topk_w[t * k + q] = wq;
+            topk_ids[t * k + q] = sel_e;
+        }
+    }
+}
+
+template <int MC, int EB>
+hipError_t launch_mc_eb(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H, int E,
+                        int k, int norm, int do_route, float *logits, float *w, int32_t *ids,
+                        hipStream_t s) {
+    const int64_t bx = (T + MC * 16 - 1) / (MC * 16);
+    const int by = (E + EB * 16 - 1) / (EB * 16);
+    hipLaunchKernelGGL((router_route_kernel<MC, EB>), dim3((unsigned)bx, (unsigned)by),
+                       dim3(kRouterThreads), 0, s, hidden, wg, T, H, E, k, norm, do_route, logits,
+                       w, ids);
+    return hipGetLastError();
+}
+
+template <int MC>
+hipError_t launch_mc(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H, int E, int k,
+                     int norm, int do_route, float *logits, float *w, int32_t *ids,
+                     hipStream_t s) {
+    switch ((min(E, 64) + 15) / 16) {
+        case 1: return launch_mc_eb<MC, 1>(hidden, wg, T, H, E, k, norm, do_route, logits, w, ids, s);
+        case 2: return launch_mc_eb<MC, 2>(hidden, wg, T, H, E, k, norm, do_route, logits, w, ids, s);
+        case 3: return launch_mc_eb<MC, 3>(hidden, wg, T, H, E, k, norm, do_route, logits, w, ids, s);
+        default: return launch_mc_eb<MC, 4>(hidden, wg, T, H, E, k, norm, do_route, logits, w, ids, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_route(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H,
+                               int E, int k, int norm, float *logits, float *w, int32_t *ids,
+                               hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int fused = E <= 64 && k <= 16;
+    // Two 16-token chunks per block (half the gate-matrix reads) once that
+    // still gives a block per CU.
+    const bool two = T >= 256 * 32;
+    const hipError_t err = two ? launch_mc<2>(hidden, wg, T, H, E, k, norm, fused, logits, w, ids, s)
+                               : launch_mc<1>(hidden, wg, T, H, E, k, norm, fused, logits, w, ids, s);
+    if (err != hipSuccess || fused) return err;
+    return launch_route(logits, T, E, k, norm, w, ids, s);
+}
+
+}  // namespace moe

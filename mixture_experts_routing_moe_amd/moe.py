@@ -56,6 +56,30 @@ def moe_route(logits: torch.Tensor, k: int, norm_topk_prob: bool = True, topk_w=
     return topk_w, topk_ids
 
 
+def moe_router_route(hidden: torch.Tensor, w_gate: torch.Tensor, k: int,
+                     norm_topk_prob: bool = True, out=None):
+    """Router GEMM + gating top-k: logits = hidden . w_gate^T (bf16 in, fp32
+    out), then moe_route on them -> (logits [T,E] f32, topk_w [T,k] f32,
+    topk_ids [T,k] i32)."""
+    if hidden.dim() != 2 or w_gate.dim() != 2 or hidden.shape[1] != w_gate.shape[1]:
+        raise ValueError("hidden [T, H] and w_gate [E, H]")
+    if hidden.dtype != w_gate.dtype:
+        raise ValueError("hidden and w_gate must have the same dtype")
+    T, H = hidden.shape
+    E = w_gate.shape[0]
+    dev = hidden.device
+    if out is None:
+        out = (torch.empty((T, E), dtype=torch.float32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev))
+    logits, tw, ti = out
+    _dev(hidden, w_gate, logits, tw, ti)
+    check(lib().moe_router_route(_dtype_code(hidden), _ptr(hidden), _ptr(w_gate), T, H, E, k,
+                                 int(bool(norm_topk_prob)), _ptr(logits), _ptr(tw), _ptr(ti),
+                                 _stream()), "moe_router_route")
+    return logits, tw, ti
+
+
 GROUP_METHODS = {"group_limited_greedy": _lib.MOE_GROUP_LIMITED_GREEDY,
                  "noaux_tc": _lib.MOE_NOAUX_TC}
 

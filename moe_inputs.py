@@ -7,7 +7,9 @@ fed from here, so the two sides always read identical bits.
 Recipe (one generator per (workload, stream)):
 
 * seed = 1000 * workload_id + stream, streams: 0 gating logits, 1 hidden,
-  2 w13, 3 w2, 4 expert bias, 5 expert rank permutation.
+  2 w13, 3 w2, 4 expert bias, 5 expert rank permutation, 6 router gate
+  weights (w_gate [E, H], N(0, 1/H) bf16, so hidden . w_gate^T has unit
+  variance like the workloads' N(0,1) logits).
 * Large tensors are drawn in fixed-size chunks; chunk ``c`` of a stream uses
   ``PCG64(SeedSequence(seed, spawn_key=(c,)))``, so the bits do not depend on
   how many threads draw them.
@@ -41,7 +43,7 @@ import numpy as np
 
 CHUNK = 1 << 22  # elements per independently seeded chunk
 
-S_LOGITS, S_HIDDEN, S_W13, S_W2, S_BIAS, S_RANK = range(6)
+S_LOGITS, S_HIDDEN, S_W13, S_W2, S_BIAS, S_RANK, S_WGATE = range(7)
 
 
 @dataclass(frozen=True)
@@ -79,11 +81,12 @@ class GroupedWorkload:
     n_group: int
     topk_group: int
     method: str  # "noaux_tc" | "group_limited_greedy"
+    renorm: bool = False  # divide the selected scores by their sum
 
 
 GROUPED = {
     "grouped_noaux": GroupedWorkload(6, "grouped_noaux", T=16384, E=256, k=8, n_group=8,
-                                     topk_group=4, method="noaux_tc"),
+                                     topk_group=4, method="noaux_tc", renorm=True),
     "grouped_greedy": GroupedWorkload(7, "grouped_greedy", T=16384, E=160, k=6, n_group=8,
                                       topk_group=3, method="group_limited_greedy"),
 }
@@ -255,3 +258,8 @@ def correction_bias(w: GroupedWorkload) -> np.ndarray | None:
         return None
     g = generator(w.wid, S_BIAS)
     return np.ascontiguousarray((g.standard_normal(w.E) * 0.1).astype(np.float32))
+
+
+def router_weights(w: Workload) -> np.ndarray:
+    """The linear gate w_gate [E, H] (bf16 bits, N(0, 1/H)) for a layer workload."""
+    return normal_bf16(w.wid, S_WGATE, w.E * w.H, 1 / math.sqrt(w.H)).reshape(w.E, w.H)

@@ -77,6 +77,23 @@ def test_route_validation(lib):
     assert status(lib, "moe_route", None, 0, 8, 2, 1, None, None, None) == _lib.MOE_OK  # T=0
 
 
+def test_router_route_validation(lib):
+    I, U = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
+    B = _lib.MOE_BF16
+
+    def rr(dt, T, H, E, k, x=FAKE, w=FAKE, lg=FAKE, tw=FAKE, ti=FAKE):
+        return lib.moe_router_route(dt, x, w, T, H, E, k, 1, lg, tw, ti, None)
+
+    assert rr(_lib.MOE_F32, 4, 64, 8, 2) == U  # bf16 only
+    assert rr(B, 4, 96, 8, 2) == U  # H % 64
+    assert b"multiple of 64" in lib.moe_last_error()
+    assert rr(B, 4, 64, 8, 9) == I  # k > E
+    assert rr(7, 4, 64, 8, 2) == I  # unknown dtype
+    assert rr(B, 4, 64, 8, 2, lg=None) == I  # logits are an output, required
+    assert rr(B, 4, 64, 8, 2, x=ctypes.c_void_p(0x1008)) == I  # hidden not 16-byte aligned
+    assert rr(B, 0, 64, 8, 2, x=None, w=None, lg=None, tw=None, ti=None) == _lib.MOE_OK
+
+
 def test_route_grouped_validation(lib):
     I = _lib.MOE_ERR_INVALID_ARG
     G, N = _lib.MOE_GROUP_LIMITED_GREEDY, _lib.MOE_NOAUX_TC

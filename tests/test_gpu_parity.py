@@ -140,6 +140,68 @@ def test_route_empty():
 
 
 # --------------------------------------------------------------------------
+# Router GEMM + route
+# --------------------------------------------------------------------------
+
+def _router_check(x, wg, k, norm):
+    """x [T,H], wg [E,H] bf16 bits.  Logits within the fp32-accumulation bound
+    of the exact dot products; ids and weights exactly moe_route's selection on
+    the logits the kernel wrote (oracle route on them), and equal to the
+    oracle's selection on exact logits wherever the top-(k+1) gaps exceed
+    twice the bound."""
+    T, H = x.shape
+    logits, w, ids = moe.moe_router_route(dev_bf16(x), dev_bf16(wg), k, norm)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy()
+    ref = oracle.router_logits(x, wg, "bf16")
+    # bf16 x bf16 products are exact in fp32; at most H/32 + 8 roundings of
+    # partial sums, each <= 2^-24 of the running magnitude <= sum |x w|.
+    absdot = np.abs(mi.bf16_bits_to_f32(x)).astype(np.float64) @ \
+        np.abs(mi.bf16_bits_to_f32(wg)).astype(np.float64).T
+    bound = (H / 32 + 8) * 2.0 ** -24 * absdot
+    assert np.all(np.abs(gl - ref) <= bound), f"logit err {np.max(np.abs(gl - ref) / bound):.3f} x bound"
+    ow, oids = oracle.route(gl, k, norm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    assert_weights_close(w.cpu().numpy(), ow)
+    E = wg.shape[0]
+    if k < E:
+        srt = np.sort(ref, axis=1)[:, ::-1][:, :k + 1]
+        rb = bound.max(axis=1, keepdims=True)
+        clear = np.all(srt[:, :-1] - srt[:, 1:] > 2 * rb, axis=1)
+        _, eids = oracle.route(ref.astype(np.float32), k, norm)
+        np.testing.assert_array_equal(ids.cpu().numpy()[clear], eids[clear])
+        assert clear.mean() > 0.5, f"only {clear.mean():.2f} of rows have clear margins"
+
+
+@pytest.mark.parametrize("T,H,E,k", [(1, 64, 8, 2), (33, 128, 64, 8), (300, 256, 16, 4),
+                                     (515, 192, 40, 6), (100, 64, 30, 3), (64, 128, 100, 8),
+                                     (70, 256, 64, 20), (9000, 64, 64, 8), (8200, 128, 8, 2),
+                                     (40, 4160, 16, 4), (2100, 4224, 8, 2)])
+@pytest.mark.parametrize("norm", [True, False])
+def test_router_route_shapes(T, H, E, k, norm):
+    g = np.random.Generator(np.random.PCG64(T + H + E * 3 + k))
+    x = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    wg = mi.f32_to_bf16_bits((g.standard_normal((E, H)) / math.sqrt(H)).astype(np.float32))
+    print(f"router T={T} H={H} E={E} k={k} norm={norm}", flush=True)
+    _router_check(x, wg, k, norm)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "finegrained", "decode32"])
+def test_router_route_workloads(name):
+    w = mi.WORKLOADS[name]
+    print(f"router workload {name}", flush=True)
+    x = mi.normal_bf16(w.wid, mi.S_HIDDEN, w.T * w.H, 1.0).reshape(w.T, w.H)
+    _router_check(x, mi.router_weights(w), w.k, w.norm)
+
+
+def test_router_route_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    wg = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    lg, w, ids = moe.moe_router_route(x, wg, 2)
+    assert lg.shape == (0, 8) and ids.shape == (0, 2)
+
+
+# --------------------------------------------------------------------------
 # Group-limited routing (group_limited_greedy / noaux_tc)
 # --------------------------------------------------------------------------
 
@@ -169,7 +231,10 @@ def test_route_grouped_workloads(name, renorm):
 @pytest.mark.parametrize("T,E,n_group,topk_group,k", [
     (333, 16, 4, 2, 3), (70, 64, 8, 3, 8), (1, 64, 64, 64, 64), (129, 90, 9, 4, 7),
     (257, 96, 4, 1, 24), (200, 160, 8, 3, 6), (64, 256, 1, 1, 8), (100, 256, 8, 8, 64),
-    (77, 384, 12, 5, 16), (40, 1024, 64, 7, 14), (33, 1000, 8, 2, 50)])
+    (77, 384, 12, 5, 16), (40, 1024, 64, 7, 14), (33, 1000, 8, 2, 50),
+    # 16-lanes-per-row kernel: E % 16 == 0, E <= 256, n_group | 16, k <= 16
+    (500, 128, 16, 5, 16), (65, 48, 2, 1, 5), (301, 256, 4, 2, 8), (90, 32, 16, 3, 4),
+    (1031, 256, 8, 4, 8), (7, 160, 8, 3, 6), (130, 64, 2, 2, 16), (66, 208, 16, 16, 9)])
 @pytest.mark.parametrize("method", ["group_limited_greedy", "noaux_tc"])
 @pytest.mark.parametrize("ties", [False, True])
 def test_route_grouped_shapes(T, E, n_group, topk_group, k, method, ties):
