@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral",
                    choices=["mixtral", "finegrained", "decode1", "decode32", "routing",
-                            "grouped_noaux", "grouped_greedy"])
+                            "grouped_noaux", "grouped_greedy", "router_finegrained",
+                            "router_mixtral"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", type=int, default=None,
                    help="1: time the whole step as one captured HIP graph replay (the "
@@ -93,8 +94,14 @@ def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
     has_ffn = "hidden" in inp
     grouped = hasattr(w, "n_group")
 
+    router = "w_gate" in inp
+
     def run(n):
         t0 = time.perf_counter()
+        if router:
+            lg = oracle.router_logits(inp["hidden"][:n], inp["w_gate"], "bf16")
+            oracle.route(lg.astype(np.float32), w.k, w.norm)
+            return time.perf_counter() - t0
         if grouped:
             tw, ids = oracle.route_grouped(inp["logits"][:n], w.k, w.n_group, w.topk_group,
                                            w.method, bias=inp["bias"], renormalize=w.renorm)
@@ -125,13 +132,67 @@ def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
         spent += dt
         passes += 1
         t_total += dt
-    what = ("route + align + expert FFN + combine" if has_ffn else
+    what = ("route + align + expert FFN + combine" if has_ffn and not router else
+            "router logits + route" if router else
             f"{'grouped ' if grouped else ''}route + align + indices->multihot + "
             "multihot->indices")
     return {"value": n * passes / t_total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens x {passes} pass(es): {what} in float64, "
                       f"{t_total:.1f} s"}
+
+
+def bench_router(args, w, dev):
+    """Router GEMM + gating top-k (moe_router_route) on a layer workload's
+    hidden states and a seeded linear gate; HBM roofline over its bytes."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_moe_amd as moe
+    import moe_inputs as mi
+
+    T, H, E, k = w.T, w.H, w.E, w.k
+    hid = mi.normal_bf16(w.wid, mi.S_HIDDEN, T * H, 1.0).reshape(T, H)
+    wg = mi.router_weights(w)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, wgd = bf(hid), bf(wg)
+    out = (torch.empty((T, E), dtype=torch.float32, device=dev),
+           torch.empty((T, k), dtype=torch.float32, device=dev),
+           torch.empty((T, k), dtype=torch.int32, device=dev))
+    flush_buf = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        moe.moe_router_route(x, wgd, k, w.norm, out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for st in range(args.steps):
+        flush_buf.fill_(float(st))  # weights and tokens come from HBM
+        ev[st][0].record()
+        moe.moe_router_route(x, wgd, k, w.norm, out)
+        ev[st][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    nbytes = T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(T * 1e3 / ms, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators, random-init weights)",
+        "config": {"workload": f"router_{w.name}", "T": T, "H": H, "E": E, "top_k": k,
+                   "norm_topk_prob": w.norm, "cache_flush_between_steps": True,
+                   "step_timing": "eager", "path_bytes": nbytes},
+        "roofline": {"kernel": "router_route_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "phase_ms": {"router_route": round(ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, {"hidden": hid, "w_gate": wg})
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -158,9 +219,17 @@ def main():
     import moe_inputs as mi
 
     grouped = args.workload in mi.GROUPED
-    w = mi.GROUPED[args.workload] if grouped else mi.WORKLOADS[args.workload]
+    router = args.workload.startswith("router_")
+    if grouped:
+        w = mi.GROUPED[args.workload]
+    elif router:
+        w = mi.WORKLOADS[args.workload[len("router_"):]]
+    else:
+        w = mi.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if router:
+        return bench_router(args, w, dev)
     if grouped:
         # Group-limited routing: [T, E] scores and (noaux_tc) the correction bias.
         inp = {"logits": mi.grouped_scores(w), "bias": mi.correction_bias(w)}
