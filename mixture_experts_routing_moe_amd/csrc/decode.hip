@@ -97,29 +97,37 @@ __device__ __forceinline__ void unpair(bool lo, const bf16x8 &P, const bf16x8 &Q
     a1 = __builtin_bit_cast(bf16x8, r1);
 }
 
-// FC1 + SiLU-and-mul.  act[p, n] for n in this block's 16 rows and every
-// position p of expert e's segment [base, base + cnt), in MC chunks of 16
-// token columns.
-template <int MC>
+// FC1 + SiLU-and-mul.  act[p, n] for n in this block's RT x 16 rows and
+// every position p of expert e's segment [base, base + cnt), in MC chunks of
+// 16 token columns.  Two row tiles per block (from 16 tokens on) read the
+// token rows once for 32 gate and 32 up rows; they take batches of 2 pairs
+// instead of kPairs to stay within the registers.
+template <int MC, int RT>
 __device__ __forceinline__ void gate_up_rows(const uint16_t *__restrict__ hidden,
                                              const uint16_t *__restrict__ w13,
                                              const int32_t *__restrict__ sorted_tok, int H, int I,
                                              int e, int base, int cnt,
                                              uint16_t *__restrict__ act) {
-    __shared__ f32x4 red[3][2][MC][kWave];
+    constexpr int KP = RT == 1 ? kPairs : 2;
+    __shared__ f32x4 red[3][2][RT][MC][kWave];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int i = lane & 15;
     const int kq = lane >> 4;
-    const int n0 = blockIdx.x * kRows;
+    const int n0 = blockIdx.x * kRows * RT;
 
     // Paired-load addresses: row (i & 7) of the gate (up) rows 0-7 for P,
     // 8 rows further for Q, half (i >> 3) of each 128-byte line.
     const bool lo = i < 8;
-    const uint16_t *wgP = w13 + ((int64_t)e * 2 * I + n0 + (i & 7)) * H + (i >> 3) * 32 + kq * 8;
-    const uint16_t *wgQ = wgP + (int64_t)8 * H;
-    const uint16_t *wuP = wgP + (int64_t)I * H;
-    const uint16_t *wuQ = wuP + (int64_t)8 * H;
+    const uint16_t *wgP[RT], *wgQ[RT], *wuP[RT], *wuQ[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        wgP[rt] = w13 + ((int64_t)e * 2 * I + n0 + rt * kRows + (i & 7)) * H + (i >> 3) * 32 +
+                  kq * 8;
+        wgQ[rt] = wgP[rt] + (int64_t)8 * H;
+        wuP[rt] = wgP[rt] + (int64_t)I * H;
+        wuQ[rt] = wuP[rt] + (int64_t)8 * H;
+    }
     const uint16_t *xr[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
@@ -127,25 +135,30 @@ __device__ __forceinline__ void gate_up_rows(const uint16_t *__restrict__ hidden
         const int m = min(mc * 16 + i, cnt - 1);
         xr[mc] = hidden + (int64_t)sorted_tok[base + m] * H + kq * 8;
     }
-    f32x4 ag[MC], au[MC];
+    f32x4 ag[RT][MC], au[RT][MC];
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-        ag[mc] = f32x4{};
-        au[mc] = f32x4{};
-    }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            ag[rt][mc] = f32x4{};
+            au[rt][mc] = f32x4{};
+        }
     const int npairs = H / 64;
     const int per = (npairs + 3) / 4;
     const int p0 = wave * per;
     const int p1 = min(npairs, p0 + per);
-    for (int b = p0; b < p1; b += kPairs) {
-        bf16x8 gP[kPairs], gQ[kPairs], uP[kPairs], uQ[kPairs], x[MC][2 * kPairs];
+    for (int b = p0; b < p1; b += KP) {
+        bf16x8 gP[RT][KP], gQ[RT][KP], uP[RT][KP], uQ[RT][KP], x[MC][2 * KP];
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
+        for (int q = 0; q < KP; ++q) {
             const int k0 = min(b + q, npairs - 1) * 64;
-            gP[q] = ld_stream(wgP + k0);
-            gQ[q] = ld_stream(wgQ + k0);
-            uP[q] = ld_stream(wuP + k0);
-            uQ[q] = ld_stream(wuQ + k0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                gP[rt][q] = ld_stream(wgP[rt] + k0);
+                gQ[rt][q] = ld_stream(wgQ[rt] + k0);
+                uP[rt][q] = ld_stream(wuP[rt] + k0);
+                uQ[rt][q] = ld_stream(wuQ[rt] + k0);
+            }
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc) {
                 x[mc][2 * q] = *reinterpret_cast<const bf16x8 *>(xr[mc] + k0);
@@ -154,90 +167,116 @@ __device__ __forceinline__ void gate_up_rows(const uint16_t *__restrict__ hidden
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
+        for (int q = 0; q < KP; ++q) {
             const bool in = b + q < p1;
-            bf16x8 g0, g1, u0, u1;
-            unpair(lo, zero_unless(in, gP[q]), zero_unless(in, gQ[q]), g0, g1);
-            unpair(lo, zero_unless(in, uP[q]), zero_unless(in, uQ[q]), u0, u1);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g0, x[mc][2 * q], ag[mc], 0, 0, 0);
-                au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u0, x[mc][2 * q], au[mc], 0, 0, 0);
-                ag[mc] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(g1, x[mc][2 * q + 1], ag[mc], 0, 0, 0);
-                au[mc] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(u1, x[mc][2 * q + 1], au[mc], 0, 0, 0);
+            for (int rt = 0; rt < RT; ++rt) {
+                bf16x8 g0, g1, u0, u1;
+                unpair(lo, zero_unless(in, gP[rt][q]), zero_unless(in, gQ[rt][q]), g0, g1);
+                unpair(lo, zero_unless(in, uP[rt][q]), zero_unless(in, uQ[rt][q]), u0, u1);
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc) {
+                    ag[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g0, x[mc][2 * q],
+                                                                        ag[rt][mc], 0, 0, 0);
+                    au[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u0, x[mc][2 * q],
+                                                                        au[rt][mc], 0, 0, 0);
+                    ag[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g1, x[mc][2 * q + 1],
+                                                                        ag[rt][mc], 0, 0, 0);
+                    au[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u1, x[mc][2 * q + 1],
+                                                                        au[rt][mc], 0, 0, 0);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     if (wave > 0) {
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) {
-            red[wave - 1][0][mc][lane] = ag[mc];
-            red[wave - 1][1][mc][lane] = au[mc];
-        }
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                red[wave - 1][0][rt][mc][lane] = ag[rt][mc];
+                red[wave - 1][1][rt][mc][lane] = au[rt][mc];
+            }
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < 3; ++w)
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) {
-            ag[mc] += red[w][0][mc][lane];
-            au[mc] += red[w][1][mc][lane];
-        }
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                ag[rt][mc] += red[w][0][rt][mc][lane];
+                au[rt][mc] += red[w][1][rt][mc][lane];
+            }
     // Accumulator r holds weight row 4 kq + r and token column i.
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-        const int m = mc * 16 + i;
-        if (m >= cnt) continue;
-        bf16x4 o;
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = to_bf16(silu_f(ag[mc][r]) * au[mc][r]);
-        *reinterpret_cast<bf16x4 *>(act + (int64_t)(base + m) * I + n0 + kq * 4) = o;
+        for (int mc = 0; mc < MC; ++mc) {
+            const int m = mc * 16 + i;
+            if (m >= cnt) continue;
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[r] = to_bf16(silu_f(ag[rt][mc][r]) * au[rt][mc][r]);
+            *reinterpret_cast<bf16x4 *>(act + (int64_t)(base + m) * I + n0 + rt * kRows +
+                                        kq * 4) = o;
+        }
     }
 }
 
-// FC2.  y[p, h] (float32) for h in this block's 16 rows and every position p
-// of expert e's segment, in MC chunks of 16 token columns.  KP pairs per
-// batch: 6 for up to 32 tokens (one batch covers each wave's share of
-// k = 1408), 4 for more.
-template <int MC>
+// FC2.  y[p, h] (float32) for h in this block's RT x 16 rows and every
+// position p of expert e's segment, in MC chunks of 16 token columns.  KP
+// pairs per batch: with one row tile, 6 for up to 32 tokens (one batch covers
+// each wave's share of k = 1408), 4 for more; with two row tiles, 3.  Two row
+// tiles per block (used from 16 tokens on) read the expert's activation rows
+// once for 32 weight rows: at T = 32 those rows are otherwise close to half
+// of a block's bytes.
+template <int MC, int RT>
 __device__ __forceinline__ void down_rows(const uint16_t *__restrict__ act,
                                           const uint16_t *__restrict__ w2, int H, int I, int e,
                                           int base, int cnt, float *__restrict__ y) {
-    constexpr int KP = MC <= 2 ? 6 : 4;
-    __shared__ f32x4 red[3][MC][kWave];
+    constexpr int KP = RT == 1 ? (MC <= 2 ? 6 : 4) : 3;
+    __shared__ f32x4 red[3][RT][MC][kWave];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int i = lane & 15;
     const int kq = lane >> 4;
-    const int h0 = blockIdx.x * kRows;
+    const int h0 = blockIdx.x * kRows * RT;
 
     const bool lo = i < 8;
-    const uint16_t *wP = w2 + ((int64_t)e * H + h0 + (i & 7)) * I + (i >> 3) * 32 + kq * 8;
-    const uint16_t *wQ = wP + (int64_t)8 * I;
+    const uint16_t *wP[RT], *wQ[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        wP[rt] = w2 + ((int64_t)e * H + h0 + rt * kRows + (i & 7)) * I + (i >> 3) * 32 + kq * 8;
+        wQ[rt] = wP[rt] + (int64_t)8 * I;
+    }
     const uint16_t *ar[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
         const int m = min(mc * 16 + i, cnt - 1);
         ar[mc] = act + (int64_t)(base + m) * I + kq * 8;
     }
-    f32x4 acc[MC];
+    f32x4 acc[RT][MC];
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) acc[rt][mc] = f32x4{};
     const int npairs = I / 64;
     const int per = (npairs + 3) / 4;
     const int p0 = wave * per;
     const int p1 = min(npairs, p0 + per);
     for (int b = p0; b < p1; b += KP) {
-        bf16x8 wPv[KP], wQv[KP], x[MC][2 * KP];
+        bf16x8 wPv[RT][KP], wQv[RT][KP], x[MC][2 * KP];
 #pragma unroll
         for (int q = 0; q < KP; ++q) {
             const int k0 = min(b + q, npairs - 1) * 64;
-            wPv[q] = ld_stream(wP + k0);
-            wQv[q] = ld_stream(wQ + k0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                wPv[rt][q] = ld_stream(wP[rt] + k0);
+                wQv[rt][q] = ld_stream(wQ[rt] + k0);
+            }
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc) {
                 x[mc][2 * q] = *reinterpret_cast<const bf16x8 *>(ar[mc] + k0);
@@ -248,33 +287,44 @@ __device__ __forceinline__ void down_rows(const uint16_t *__restrict__ act,
 #pragma unroll
         for (int q = 0; q < KP; ++q) {
             const bool in = b + q < p1;
-            bf16x8 w0, w1;
-            unpair(lo, zero_unless(in, wPv[q]), zero_unless(in, wQv[q]), w0, w1);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x[mc][2 * q], acc[mc], 0, 0, 0);
-                acc[mc] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x[mc][2 * q + 1], acc[mc], 0, 0, 0);
+            for (int rt = 0; rt < RT; ++rt) {
+                bf16x8 w0, w1;
+                unpair(lo, zero_unless(in, wPv[rt][q]), zero_unless(in, wQv[rt][q]), w0, w1);
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc) {
+                    acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x[mc][2 * q],
+                                                                         acc[rt][mc], 0, 0, 0);
+                    acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x[mc][2 * q + 1],
+                                                                         acc[rt][mc], 0, 0, 0);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     if (wave > 0) {
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) red[wave - 1][mc][lane] = acc[mc];
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) red[wave - 1][rt][mc][lane] = acc[rt][mc];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < 3; ++w)
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) acc[mc] += red[w][mc][lane];
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-        const int m = mc * 16 + i;
-        if (m >= cnt) continue;
-        *reinterpret_cast<float4 *>(y + (int64_t)(base + m) * H + h0 + kq * 4) =
-            make_float4(acc[mc][0], acc[mc][1], acc[mc][2], acc[mc][3]);
+            for (int mc = 0; mc < MC; ++mc) acc[rt][mc] += red[w][rt][mc][lane];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            const int m = mc * 16 + i;
+            if (m >= cnt) continue;
+            *reinterpret_cast<float4 *>(y + (int64_t)(base + m) * H + h0 + rt * kRows + kq * 4) =
+                make_float4(acc[rt][mc][0], acc[rt][mc][1], acc[rt][mc][2], acc[rt][mc][3]);
+        }
     }
 }
 
@@ -282,7 +332,7 @@ __device__ __forceinline__ void down_rows(const uint16_t *__restrict__ act,
 // chunks is chosen per block from the expert's own row count (at most MCmax,
 // which the launch sets from T): with T = 32 most experts hold 16 rows or
 // fewer and take the one-chunk path.
-template <int MCmax>
+template <int MCmax, int RT>
 __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w13,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_tok, int H, int I,
@@ -290,25 +340,26 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
     int e, base, cnt;
     if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
     if (MCmax == 1 || cnt <= 16)
-        gate_up_rows<1>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+        gate_up_rows<1, RT>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
     else if (MCmax == 2 || cnt <= 32)
-        gate_up_rows<(MCmax > 1 ? 2 : 1)>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+        gate_up_rows<(MCmax > 1 ? 2 : 1), RT>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
     else
-        gate_up_rows<MCmax>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
+        gate_up_rows<MCmax, RT>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
 }
 
-template <int MCmax>
+// One block per (RT x 16 weight rows, non-empty expert).
+template <int MCmax, int RT>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
     const int32_t *__restrict__ offsets, int H, int I, int E, float *__restrict__ y) {
     int e, base, cnt;
     if (!nth_nonempty_expert(offsets, E, blockIdx.y, e, base, cnt)) return;
     if (MCmax == 1 || cnt <= 16)
-        down_rows<1>(act, w2, H, I, e, base, cnt, y);
+        down_rows<1, RT>(act, w2, H, I, e, base, cnt, y);
     else if (MCmax == 2 || cnt <= 32)
-        down_rows<(MCmax > 1 ? 2 : 1)>(act, w2, H, I, e, base, cnt, y);
+        down_rows<(MCmax > 1 ? 2 : 1), RT>(act, w2, H, I, e, base, cnt, y);
     else
-        down_rows<MCmax>(act, w2, H, I, e, base, cnt, y);
+        down_rows<MCmax, RT>(act, w2, H, I, e, base, cnt, y);
 }
 
 int token_chunks(int64_t T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
@@ -325,19 +376,26 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t *hidden, const uint16_t *w1
                                       int64_t T, int H, int I, int E, int k, uint16_t *act,
                                       hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const dim3 grid(I / kRows, expert_rows(T, E, k));
-    switch (token_chunks(T)) {
+    // Two row tiles per block from 16 tokens on (I % 64 == 0, so I / 32
+    // blocks cover I).
+    const bool two = T >= 16;
+    const dim3 grid(I / (kRows * (two ? 2 : 1)), expert_rows(T, E, k));
+    switch (token_chunks(T) * (two ? 10 : 1)) {
         case 1:
-            hipLaunchKernelGGL(decode_gate_up_kernel<1>, grid, dim3(kThreads), 0, s, hidden, w13,
-                               offsets, sorted_tok, H, I, E, act);
+            hipLaunchKernelGGL((decode_gate_up_kernel<1, 1>), grid, dim3(kThreads), 0, s, hidden,
+                               w13, offsets, sorted_tok, H, I, E, act);
             break;
-        case 2:
-            hipLaunchKernelGGL(decode_gate_up_kernel<2>, grid, dim3(kThreads), 0, s, hidden, w13,
-                               offsets, sorted_tok, H, I, E, act);
+        case 10:
+            hipLaunchKernelGGL((decode_gate_up_kernel<1, 2>), grid, dim3(kThreads), 0, s, hidden,
+                               w13, offsets, sorted_tok, H, I, E, act);
+            break;
+        case 20:
+            hipLaunchKernelGGL((decode_gate_up_kernel<2, 2>), grid, dim3(kThreads), 0, s, hidden,
+                               w13, offsets, sorted_tok, H, I, E, act);
             break;
         default:
-            hipLaunchKernelGGL(decode_gate_up_kernel<4>, grid, dim3(kThreads), 0, s, hidden, w13,
-                               offsets, sorted_tok, H, I, E, act);
+            hipLaunchKernelGGL((decode_gate_up_kernel<4, 2>), grid, dim3(kThreads), 0, s, hidden,
+                               w13, offsets, sorted_tok, H, I, E, act);
             break;
     }
     return hipGetLastError();
@@ -347,18 +405,25 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
                                    const int32_t *offsets, int64_t T, int H, int I, int E, int k,
                                    float *y, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const dim3 grid(H / kRows, expert_rows(T, E, k));
-    switch (token_chunks(T)) {
+    // Two row tiles per block once the experts hold enough tokens for their
+    // activation rows to matter (H % 64 == 0, so H / 32 blocks cover H).
+    const bool two = T >= 16;
+    const dim3 grid(H / (kRows * (two ? 2 : 1)), expert_rows(T, E, k));
+    switch (token_chunks(T) * (two ? 10 : 1)) {
         case 1:
-            hipLaunchKernelGGL((decode_down_kernel<1>), grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<1, 1>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
-        case 2:
-            hipLaunchKernelGGL((decode_down_kernel<2>), grid, dim3(kThreads), 0, s, act, w2,
+        case 10:
+            hipLaunchKernelGGL((decode_down_kernel<1, 2>), grid, dim3(kThreads), 0, s, act, w2,
+                               offsets, H, I, E, y);
+            break;
+        case 20:
+            hipLaunchKernelGGL((decode_down_kernel<2, 2>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
         default:
-            hipLaunchKernelGGL((decode_down_kernel<4>), grid, dim3(kThreads), 0, s, act, w2,
+            hipLaunchKernelGGL((decode_down_kernel<4, 2>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
     }

@@ -453,7 +453,8 @@ def test_ffn_bf16_prefill(T, H, I, E, k, skew, inv):
 
 @pytest.mark.parametrize("T,H,I,E,k", [(1, 128, 128, 8, 2), (5, 256, 192, 16, 4),
                                        (32, 512, 256, 64, 8), (64, 64, 64, 8, 8),
-                                       (20, 192, 320, 6, 2)])
+                                       (20, 192, 320, 6, 2), (15, 128, 192, 4, 2),
+                                       (16, 128, 192, 4, 2), (48, 256, 128, 32, 6)])
 def test_ffn_bf16_decode(T, H, I, E, k):
     x, w13, w2, w32, ids = _rand_layer(T * 5 + H + I, T, H, I, E, k)
     out, out32 = _ffn_gpu(x, w13, w2, w32, ids, "bf16", decode=True)
