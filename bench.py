@@ -3,9 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
 
 One step is one pass of the whole path over one batch of synthetic input:
-route + indices->multihot (one call, fused in one kernel for E <= 64) ->
-align -> multihot->indices -> grouped FC1 + SiLU-and-mul -> grouped FC2 ->
-combine (decode workloads use the decode FFN kernels).  Inputs are resident in HBM before timing starts; nothing is
+route + indices->multihot + align (one call, moe_route_align: one kernel for
+at most 512 routing slots, else a route kernel that also counts the
+alignment's histograms plus the scatter kernel) -> multihot->indices ->
+grouped FC1 + SiLU-and-mul -> grouped FC2 -> combine (decode workloads use
+the decode FFN kernels).  Inputs are resident in HBM before timing starts; nothing is
 allocated inside the timed region.  Each phase is bracketed by HIP events on
 the stream the library launches on (torch's current stream), so per-kernel
 durations are measured live.  Prints one JSON line.
@@ -280,9 +282,11 @@ def main():
         y = torch.empty((splits, T * k, H), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    # Route and the indices->multihot conversion of its output run as one
-    # call (one kernel where the library fuses them, see config).
-    phases = ["route_multihot", "align", "to_indices"]
+    # Route, the indices->multihot conversion of its output and the alignment
+    # run as one call (moe_route_align; its launches are in config).
+    phases = ["route_align", "to_indices"]
+    ra_out = {"topk_w": topk_w, "topk_ids": topk_ids, "multihot": mh, "probs_in_multihot": pim,
+              "position_map": pos, **aligned}
     if grouped:  # group-limited selection, then the same conversions
         phases = ["route_grouped", "align", "to_multihot", "to_indices"]
     if has_ffn:
@@ -291,8 +295,9 @@ def main():
     cur = {"logits": logits_draws[0]}
 
     def run_phase(name):
-        if name == "route_multihot":
-            moe.moe_route_multihot(cur["logits"], k, w.norm, (topk_w, topk_ids, mh, pim, pos))
+        if name == "route_align":
+            moe.moe_route_align(cur["logits"], k, w.norm, with_multihot=True, out=ra_out,
+                                workspace=align_ws)
         elif name == "route_grouped":
             moe.moe_route_grouped(cur["logits"], k, w.n_group, w.topk_group, w.method, bias_d,
                                   w.renorm, topk_w, topk_ids)
@@ -369,8 +374,7 @@ def main():
         # Distinct experts per routing draw (outside the timed region).
         for r in range(min(draws, args.steps)):
             cur["logits"] = logits_draws[r]
-            run_phase("route_multihot")
-            run_phase("align")
+            run_phase("route_align")
             n_distinct.append(int((aligned["counts"] > 0).sum().item()))
 
     phase_ms = {ph: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) /
@@ -391,7 +395,8 @@ def main():
                     "renormalize": w.renorm})
     else:
         cfg.update({"norm_topk_prob": w.norm,
-                    "route_multihot_fused": moe.moe_route_multihot_fused(E, k)})
+                    "route_align_launches": (1 if T * k <= 512 else 2)
+                    if moe.moe_route_align_fused(T, E, k) else 3})
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())
@@ -425,6 +430,8 @@ def main():
         # Algorithmic HBM bytes per phase: every input read once, every output
         # written once.
         nb = {"route_multihot": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
+              "route_align": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4) + T * k * 12 +
+              (2 * E + 1) * 4,
               "route_grouped": T * E * 4 + E * 4 + T * k * 8,
               "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
@@ -432,6 +439,8 @@ def main():
         nb = {ph: nb[ph] for ph in phases}
         dom = max(phase_ms, key=phase_ms.get)
         names = {"route_multihot": "route_rows16_kernel (route + multihot)",
+                 "route_align": "route_hist_kernel + align_scatter_kernel (route + multihot "
+                                "+ align)",
                  "route_grouped": "route_grouped_kernel",
                  "to_multihot": "to_multihot kernel",
                  "align": "align_hist_kernel + align_scatter_kernel",

@@ -8,6 +8,7 @@
  *   moe_route_multihot        moe_route + moe_indices_to_multihot in one pass
  *   moe_route_grouped         group-limited top-k (group_limited_greedy, noaux_tc)
  *   moe_router_route          router GEMM (hidden . w_gate^T) + moe_route, one pass
+ *   moe_route_align           moe_route(_multihot) + moe_align in fewer launches
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 4
+#define MOE_VERSION 5
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
 #define MOE_DECODE_MAX_T 64
@@ -215,6 +216,33 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
  * probs_in_multihot [T, E] float32 out: probs[t, j] (bit copy) at e = ids[t, j], else 0.
  * position_map      [T, E] int32 out: slot j at e = ids[t, j], else -1.
  */
+/*
+ * moe_route_align -- moe_route (moe_route_multihot when multihot,
+ * probs_in_multihot and position_map are all given; all NULL otherwise)
+ * followed by moe_align on the ids it produces.
+ * [mlc] gating_topk, gating_softmax_topk, moe_cumsum, get_indices, get_indptr;
+ * [mgt] _indices_to_multihot_kernel.
+ *
+ * Arguments as the separate calls; every output is bit-identical to them.
+ * Where moe_route_align_fused(T, E, k) is 1 (E <= 64, k <= 16, and for more
+ * than 512 slots alignment chunks of at most 64 whole rows) the calls take
+ * fewer launches: for at most 512 slots (decode batches) one kernel routes
+ * and aligns; beyond that the route kernel also counts each alignment
+ * chunk's ids, so the alignment's histogram kernel is not launched.  (With
+ * the multihot outputs the fused path also needs what moe_route_multihot's
+ * one-kernel path needs.)  workspace: moe_align_workspace_size(T, k, E)
+ * bytes.  T = 0 writes zero counts and offsets, as moe_align does.
+ */
+moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t k,
+                             int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                             uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
+                             int32_t *expert_counts, int32_t *expert_offsets,
+                             int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                             int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                             void *stream);
+/* 1 if moe_route_align takes the fused launches for this T, E and k. */
+int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k);
+
 moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,
                                      int32_t k, int32_t E, uint8_t *multihot,
                                      float *probs_in_multihot, int32_t *position_map,

@@ -18,6 +18,8 @@ from .moe import (  # noqa: F401
     moe_layer,
     moe_multihot_to_indices,
     moe_route,
+    moe_route_align,
+    moe_route_align_fused,
     moe_route_grouped,
     moe_route_multihot,
     moe_route_multihot_fused,

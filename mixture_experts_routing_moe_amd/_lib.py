@@ -25,7 +25,7 @@ MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_DECODE_MAX_T = 64
 MOE_MAX_SPLITS = 8
-MOE_VERSION = 4
+MOE_VERSION = 5
 MOE_MAX_GROUPS = 64
 MOE_GROUP_LIMITED_GREEDY = 0
 MOE_NOAUX_TC = 1
@@ -44,6 +44,9 @@ SIGNATURES = {
     "moe_route_grouped": (_st, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                 _vp]),
     "moe_align_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_route_align": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_align_fused": (_i32, [_i64, _i32, _i32]),
     "moe_align": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_indices_to_multihot": (_st, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_multihot_to_indices": (_st, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),

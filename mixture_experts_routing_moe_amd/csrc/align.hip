@@ -113,12 +113,11 @@ __device__ int block_exclusive_scan(const int32_t *v, int32_t *out, int n, int32
 //
 // With one block (n <= 512 slots: decode batches) the block counts the ids
 // itself (fused_hist) and the histogram kernel is not launched.
-__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
+__device__ __forceinline__ void align_scatter_block(
+    int b, const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
     int fused_hist, const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
-    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
-    extern __shared__ int32_t sm[];
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted, int32_t *sm) {
     // LDS: run[E] | wcnt[W][E] | tot[E] | off[E] | tot_part[P][E] | pre_part[P][E] | wsum[W]
     // (W waves, P parts)
     const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
@@ -131,7 +130,6 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     int32_t *wsum = pre_part + parts * E;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
-    const int b = blockIdx.x;
 
     if (fused_hist) {
         for (int idx = tid; idx < parts * E; idx += kAlignThreads) {
@@ -223,7 +221,79 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     }
 }
 
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
+    int fused_hist, const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
+    extern __shared__ int32_t sm[];
+    align_scatter_block(blockIdx.x, ids, n, k, E, chunk, nbits, nb, fused_hist, partial, counts,
+                        offsets, sorted_tok, sorted_slot, slot_to_sorted, sm);
+}
+
+// Route + align in one block (at most kAlignThreads slots, E <= 64, k <= 16):
+// the block's 8 waves route 4 rows each per pass with route16_row (the
+// moe_route / moe_route_multihot selection), then the block aligns the ids it
+// has just written, counting them itself.
+__global__ __launch_bounds__(kAlignThreads) void route_align_small_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int norm, int vec4,
+    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot,
+    float *__restrict__ pim, int32_t *__restrict__ pos, int chunk, int nbits,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_tok, int32_t *__restrict__ sorted_slot,
+    int32_t *__restrict__ slot_to_sorted) {
+    extern __shared__ int32_t sm[];
+    const int lane = lane_id();
+    const int g = lane >> 4;
+    const int q = lane & 15;
+    const int wave = threadIdx.x / kWave;
+    for (int t0 = wave * 4; t0 < T; t0 += kAlignWaves * 4)
+        route16_row(logits, T, t0 + g, E, k, norm, vec4, topk_w, topk_ids, multihot, pim, pos, g,
+                    q);
+    __syncthreads();  // every id of the batch is written before the block reads them
+    align_scatter_block(0, topk_ids, T * k, k, E, chunk, nbits, 1, 1, nullptr, counts, offsets,
+                        sorted_tok, sorted_slot, slot_to_sorted, sm);
+}
+
+// Route with the alignment's per-block histograms: block b routes the rows of
+// alignment chunk b (rows_per_block = chunk / k rows, slots [b chunk,
+// (b + 1) chunk)) and counts their ids into partial[b][e], exactly what
+// align_hist_kernel would count from the ids, so the scatter kernel follows
+// directly.  16 waves of 4 rows: a chunk of at most 64 rows in one pass.
+constexpr int kRouteHistThreads = 1024;
+constexpr int kRouteHistRows = kRouteHistThreads / kWave * 4;
+
+__global__ __launch_bounds__(kRouteHistThreads) void route_hist_kernel(
+    const float *__restrict__ logits, int64_t T, int E, int k, int norm, int vec4,
+    int64_t rows_per_block, float *__restrict__ topk_w, int32_t *__restrict__ topk_ids,
+    uint8_t *__restrict__ multihot, float *__restrict__ pim, int32_t *__restrict__ pos,
+    int32_t *__restrict__ partial) {
+    extern __shared__ int32_t hist[];
+    for (int e = threadIdx.x; e < E; e += kRouteHistThreads) hist[e] = 0;
+    __syncthreads();
+    const int lane = lane_id();
+    const int g = lane >> 4;
+    const int q = lane & 15;
+    const int wave = threadIdx.x / kWave;
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < T ? r0 + rows_per_block : T;
+    // Rows at or past r1 belong to the next block: r1 bounds the rows here.
+    for (int64_t t0 = r0 + wave * 4; t0 < r1; t0 += kRouteHistRows) {
+        const int e = route16_row(logits, r1, t0 + g, E, k, norm, vec4, topk_w, topk_ids, multihot,
+                                  pim, pos, g, q);
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRouteHistThreads)
+        partial[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
 }  // namespace
+
+size_t scatter_lds_bytes(int E) {
+    const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
+    return (size_t)((3 + kAlignWaves) * E + 2 * parts * E + kAlignWaves) * sizeof(int32_t);
+}
 
 int align_num_blocks(int64_t n, int E) {
     int64_t nb = (n + kSlotsPerBlock - 1) / kSlotsPerBlock;
@@ -252,12 +322,61 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const int parts = E < kAlignThreads ? kAlignThreads / E : 1;
-    const size_t lds =
-        (size_t)((3 + kAlignWaves) * E + 2 * parts * E + kAlignWaves) * sizeof(int32_t);
+    const size_t lds = scatter_lds_bytes(E);
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
                        k, E, (int)chunk, nbits, nb, fused, ws, counts, offsets, sorted_tok,
                        sorted_slot, slot_to_sorted);
+    return hipGetLastError();
+}
+
+bool route_align_fused(int64_t T, int E, int k, const float *logits, const uint8_t *mh,
+                       const float *pim, const int32_t *pos) {
+    (void)logits;
+    if (E > 64 || k > 16) return false;
+    if (mh != nullptr && !route_multihot_fused(E, k, mh, pim, pos)) return false;
+    const int64_t n = T * k;
+    const int nb = align_num_blocks(n, E);
+    if (nb == 1) return true;
+    // Chunks of whole rows, few enough that one pass of the route kernel's
+    // 16 waves covers a chunk (more rows per block measured slower than the
+    // separate launches: the route then runs on too few blocks).
+    const int64_t chunk = align_chunk(n, nb);
+    return chunk % k == 0 && chunk / k <= kRouteHistRows;
+}
+
+hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int norm, float *w,
+                              int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
+                              int32_t *sorted_slot, int32_t *slot_to_sorted, int32_t *ws,
+                              hipStream_t s) {
+    if (!route_align_fused(T, E, k, logits, mh, pim, pos)) {
+        hipError_t err = mh != nullptr
+                             ? launch_route_multihot(logits, T, E, k, norm, w, ids, mh, pim, pos, s)
+                             : launch_route(logits, T, E, k, norm, w, ids, s);
+        if (err != hipSuccess) return err;
+        return launch_align(ids, T, k, E, counts, offsets, sorted_tok, sorted_slot,
+                            slot_to_sorted, ws, s);
+    }
+    const int64_t n = T * k;
+    const int nb = align_num_blocks(n, E);
+    const int64_t chunk = align_chunk(n, nb);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+    if (nb == 1) {
+        hipLaunchKernelGGL(route_align_small_kernel, dim3(1), dim3(kAlignThreads),
+                           scatter_lds_bytes(E), s, logits, (int)T, E, k, norm, vec4, w, ids, mh,
+                           pim, pos, (int)chunk, nbits, counts, offsets, sorted_tok, sorted_slot,
+                           slot_to_sorted);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(kRouteHistThreads), E * sizeof(int32_t), s,
+                       logits, T, E, k, norm, vec4, chunk / k, w, ids, mh, pim, pos, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), scatter_lds_bytes(E),
+                       s, ids, (int)n, k, E, (int)chunk, nbits, nb, 0, ws, counts, offsets,
+                       sorted_tok, sorted_slot, slot_to_sorted);
     return hipGetLastError();
 }
 

@@ -222,6 +222,42 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                       "moe_align");
 }
 
+moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t k,
+                             int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                             uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
+                             int32_t *expert_counts, int32_t *expert_offsets,
+                             int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                             int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    const char *fn = "moe_route_align";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
+    const int n_mh = (multihot != nullptr) + (probs_in_multihot != nullptr) +
+                     (position_map != nullptr);
+    CHECK(n_mh == 0 || n_mh == 3, MOE_ERR_INVALID_ARG,
+          "%s: give all three multihot outputs or none", fn);
+    CHECK(expert_counts && expert_offsets, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(T == 0 || (logits && topk_w && topk_ids && sorted_token_ids && sorted_slot_ids &&
+                     slot_to_sorted),
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    const size_t need = moe_align_workspace_size(T, k, E);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    return hip_status(moe::launch_route_align(logits, T, E, k, norm_topk_prob != 0, topk_w,
+                                              topk_ids, multihot, probs_in_multihot,
+                                              position_map, expert_counts, expert_offsets,
+                                              sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                                              static_cast<int32_t *>(workspace),
+                                              static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k) {
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK) return 0;
+    return moe::route_align_fused(T, E, k, nullptr, nullptr, nullptr, nullptr);
+}
+
 moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,
                                      int32_t k, int32_t E, uint8_t *multihot,
                                      float *probs_in_multihot, int32_t *position_map,

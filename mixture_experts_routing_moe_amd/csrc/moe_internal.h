@@ -159,6 +159,74 @@ __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, i
     return (float)(ex / sum);
 }
 
+// One routing row on a 16-lane DPP row (g = lane / 16, q = lane % 16): row
+// t of logits [T, E] (E <= 64, k <= 16; rows t >= T write nothing), the
+// selection of route_row16, topk_w / topk_ids written by lanes q < k, and
+// with multihot != nullptr (E % 4 == 0, 16-byte aligned rows) the row's [E]
+// multihot, probability and position-map entries: each lane records which
+// round picked each of its 4 experts, fetches that slot's weight from the
+// lane that computed it, and writes its 4 columns.  vec4: E == 64 and
+// 16-byte aligned logits.  Returns the expert of slot q (-1 for q >= k or
+// rows past T).
+__device__ __forceinline__ int route16_row(const float *__restrict__ logits, int64_t T,
+                                           int64_t t, int E, int k, int norm, int vec4,
+                                           float *__restrict__ topk_w,
+                                           int32_t *__restrict__ topk_ids,
+                                           uint8_t *__restrict__ multihot, float *__restrict__ pim,
+                                           int32_t *__restrict__ pos, int g, int q) {
+    const int lane = lane_id();
+    const bool row_ok = t < T;
+    float v[4];
+    uint32_t avail = 0;
+    if (row_ok && vec4) {  // E == 64 and 16-byte aligned rows
+        const float4 x = *reinterpret_cast<const float4 *>(logits + t * 64 + 4 * q);
+        v[0] = x.x;
+        v[1] = x.y;
+        v[2] = x.z;
+        v[3] = x.w;
+        avail = 0xFu;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * q + i;
+            v[i] = 0.0f;
+            if (row_ok && e < E) {
+                v[i] = logits[t * E + e];
+                avail |= 1u << i;
+            }
+        }
+    }
+    uint32_t slot_of;  // byte i: round that picked local expert i (0xFF: none)
+    int sel_e;
+    const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
+    if (row_ok && q < k) {
+        topk_w[t * k + q] = wq;
+        topk_ids[t * k + q] = sel_e;
+    }
+    if (multihot != nullptr) {
+        int pj[4];
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (int)((slot_of >> (8 * i)) & 0xFFu);
+            pj[i] = r == 0xFF ? -1 : r;
+            // Every lane takes part in the shuffle; unpicked columns read
+            // their own lane and are zeroed.
+            const float w = __shfl(wq, pj[i] >= 0 ? (lane & ~15) + pj[i] : lane, kWave);
+            pv[i] = pj[i] >= 0 ? w : 0.0f;
+        }
+        if (row_ok && 4 * q < E) {
+            const uint32_t m = (uint32_t)(pj[0] >= 0) | (uint32_t)(pj[1] >= 0) << 8 |
+                               (uint32_t)(pj[2] >= 0) << 16 | (uint32_t)(pj[3] >= 0) << 24;
+            *reinterpret_cast<uint32_t *>(multihot + t * E + 4 * q) = m;
+            *reinterpret_cast<float4 *>(pim + t * E + 4 * q) =
+                make_float4(pv[0], pv[1], pv[2], pv[3]);
+            *reinterpret_cast<int4 *>(pos + t * E + 4 * q) = make_int4(pj[0], pj[1], pj[2], pj[3]);
+        }
+    }
+    return row_ok ? sel_e : -1;
+}
+
 // SiLU in float32: z / (1 + e^-z).
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (v_rcp_f32, about
 // 1 ulp) instead of an IEEE division: the result is rounded to bf16 next,
@@ -192,6 +260,17 @@ int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
                         int32_t *slot_to_sorted, int32_t *ws, hipStream_t s);
+
+// Route (+ indices->multihot when mh != nullptr) and align in fewer launches
+// where route_align_fused holds; otherwise the separate launches.  Outputs
+// are those of the separate calls, bit for bit.
+bool route_align_fused(int64_t T, int E, int k, const float *logits, const uint8_t *mh,
+                       const float *pim, const int32_t *pos);
+hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int norm, float *w,
+                              int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
+                              int32_t *sorted_slot, int32_t *slot_to_sorted, int32_t *ws,
+                              hipStream_t s);
 
 hipError_t launch_to_multihot(const int32_t *ids, const float *probs, int64_t T, int k, int E,
                               uint8_t *mh, float *pim, int32_t *pos, hipStream_t s);

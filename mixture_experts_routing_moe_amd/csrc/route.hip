@@ -112,58 +112,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_rows16_kernel(
     const int64_t wave = (int64_t)blockIdx.x * (kRouteThreads / kWave) + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * (kRouteThreads / kWave);
 
-    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
-        const int64_t t = t0 + g;
-        const bool row_ok = t < T;
-        float v[4];
-        uint32_t avail = 0;
-        if (row_ok && vec4) {  // E == 64 and 16-byte aligned rows
-            const float4 x = *reinterpret_cast<const float4 *>(logits + t * 64 + 4 * q);
-            v[0] = x.x;
-            v[1] = x.y;
-            v[2] = x.z;
-            v[3] = x.w;
-            avail = 0xFu;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * q + i;
-                v[i] = 0.0f;
-                if (row_ok && e < E) {
-                    v[i] = logits[t * E + e];
-                    avail |= 1u << i;
-                }
-            }
-        }
-        uint32_t slot_of;  // byte i: round that picked local expert i (0xFF: none)
-        int sel_e;
-        const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
-        if (row_ok && q < k) {
-            topk_w[t * k + q] = wq;
-            topk_ids[t * k + q] = sel_e;
-        }
-        if (multihot != nullptr) {
-            int pj[4];
-            float pv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = (int)((slot_of >> (8 * i)) & 0xFFu);
-                pj[i] = r == 0xFF ? -1 : r;
-                // Every lane takes part in the shuffle; unpicked columns read
-                // their own lane and are zeroed.
-                const float w = __shfl(wq, pj[i] >= 0 ? (lane & ~15) + pj[i] : lane, kWave);
-                pv[i] = pj[i] >= 0 ? w : 0.0f;
-            }
-            if (row_ok && 4 * q < E) {
-                const uint32_t m = (uint32_t)(pj[0] >= 0) | (uint32_t)(pj[1] >= 0) << 8 |
-                                   (uint32_t)(pj[2] >= 0) << 16 | (uint32_t)(pj[3] >= 0) << 24;
-                *reinterpret_cast<uint32_t *>(multihot + t * E + 4 * q) = m;
-                *reinterpret_cast<float4 *>(pim + t * E + 4 * q) =
-                    make_float4(pv[0], pv[1], pv[2], pv[3]);
-                *reinterpret_cast<int4 *>(pos + t * E + 4 * q) = make_int4(pj[0], pj[1], pj[2], pj[3]);
-            }
-        }
-    }
+    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4)
+        route16_row(logits, T, t0 + g, E, k, norm, vec4, topk_w, topk_ids, multihot, pim, pos, g,
+                    q);
 }
 
 template <int VPL>

@@ -165,6 +165,48 @@ def moe_align(topk_ids: torch.Tensor, E: int, out: dict | None = None,
     return out
 
 
+def moe_route_align_fused(T: int, E: int, k: int) -> bool:
+    return bool(lib().moe_route_align_fused(T, E, k))
+
+
+def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
+                    with_multihot: bool = False, out: dict | None = None,
+                    workspace: torch.Tensor | None = None) -> dict:
+    """moe_route (moe_route_multihot with with_multihot) + moe_align in one call ->
+    dict with topk_w, topk_ids, the alignment outputs of moe_align and, with
+    with_multihot, multihot / probs_in_multihot / position_map."""
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be [T, E] float32")
+    T, E = logits.shape
+    dev = logits.device
+    n = T * k
+    if out is None:
+        out = {
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+            "topk_ids": torch.empty((T, k), dtype=torch.int32, device=dev),
+            "counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_token_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "sorted_slot_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "slot_to_sorted": torch.empty(n, dtype=torch.int32, device=dev),
+        }
+        if with_multihot:
+            out["multihot"] = torch.empty((T, E), dtype=torch.uint8, device=dev)
+            out["probs_in_multihot"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+            out["position_map"] = torch.empty((T, E), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                                device=dev)
+    _dev(logits, workspace, *out.values())
+    check(lib().moe_route_align(
+        _ptr(logits), T, E, k, int(bool(norm_topk_prob)), _ptr(out["topk_w"]),
+        _ptr(out["topk_ids"]), _ptr(out.get("multihot")), _ptr(out.get("probs_in_multihot")),
+        _ptr(out.get("position_map")), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["sorted_token_ids"]), _ptr(out["sorted_slot_ids"]), _ptr(out["slot_to_sorted"]),
+        _ptr(workspace), workspace.numel(), _stream()), "moe_route_align")
+    return out
+
+
 def moe_indices_to_multihot(ids: torch.Tensor, probs: torch.Tensor, E: int, out=None):
     """-> (multihot [T,E] u8, probs_in_multihot [T,E] f32, position_map [T,E] i32)."""
     if ids.dtype != torch.int32 or probs.dtype != torch.float32 or ids.shape != probs.shape:

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_version() == 4
+    assert lib.moe_version() == 5
     for s in range(5):
         assert lib.moe_status_string(s)
     assert lib.moe_status_string(99) == b"unknown status"
@@ -92,6 +92,30 @@ def test_router_route_validation(lib):
     assert rr(B, 4, 64, 8, 2, lg=None) == I  # logits are an output, required
     assert rr(B, 4, 64, 8, 2, x=ctypes.c_void_p(0x1008)) == I  # hidden not 16-byte aligned
     assert rr(B, 0, 64, 8, 2, x=None, w=None, lg=None, tw=None, ti=None) == _lib.MOE_OK
+
+
+def test_route_align_validation(lib):
+    I, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE
+    ws_need = lib.moe_align_workspace_size(100, 8, 64)
+
+    def ra(T=100, E=64, k=8, mh=(None, None, None), ws=FAKE, wsb=None, logits=FAKE):
+        return lib.moe_route_align(logits, T, E, k, 1, FAKE, FAKE, *mh, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, ws, ws_need if wsb is None else wsb, None)
+
+    assert ra(k=65) == I
+    assert ra(E=4, k=5) == I  # k > E
+    assert ra(mh=(FAKE, None, None)) == I  # some multihot outputs but not all
+    assert b"all three" in lib.moe_last_error()
+    assert ra(wsb=ws_need - 1) == W
+    assert ra(ws=None) == W
+    assert ra(logits=None) == I
+    # fused-path predicate: E <= 64, k <= 16, chunks of whole rows
+    assert lib.moe_route_align_fused(1, 64, 8) == 1
+    assert lib.moe_route_align_fused(16384, 64, 8) == 1
+    assert lib.moe_route_align_fused(16384, 64, 6) == 0  # 512-slot chunks hold no whole rows
+    assert lib.moe_route_align_fused(4096, 8, 2) == 0  # 16 chunks of 256 rows: separate launches
+    assert lib.moe_route_align_fused(100, 128, 8) == 0
+    assert lib.moe_route_align_fused(100, 64, 20) == 0
 
 
 def test_route_grouped_validation(lib):

@@ -324,6 +324,64 @@ def test_align_deterministic():
 
 
 # --------------------------------------------------------------------------
+# Route + align in one call
+# --------------------------------------------------------------------------
+
+ALIGN_KEYS = ("counts", "offsets", "sorted_token_ids", "sorted_slot_ids", "slot_to_sorted")
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (32, 64, 8), (64, 64, 8), (0, 64, 8), (5, 8, 2),
+                                   (100, 60, 5), (16384, 64, 8), (4096, 8, 2), (3000, 64, 6),
+                                   (777, 100, 4), (300, 64, 20), (9000, 36, 4),
+                                   (4096, 64, 16), (12000, 62, 8), (8192, 64, 8)])
+@pytest.mark.parametrize("mh", [False, True])
+def test_route_align_matches_separate_calls(T, E, k, mh):
+    g = np.random.Generator(np.random.PCG64(T * 3 + E + k))
+    x = g.standard_normal((T, E)).astype(np.float32)
+    if T > 0:
+        x[:, : min(E, 5)] = np.round(x[:, : min(E, 5)])  # some equal logits
+    xd = dev(x)
+    print(f"route_align T={T} E={E} k={k} multihot={mh} "
+          f"fused={moe.moe_route_align_fused(T, E, k)}", flush=True)
+    got = moe.moe_route_align(xd, k, True, with_multihot=mh)
+    if mh:
+        sep = dict(zip(("topk_w", "topk_ids", "multihot", "probs_in_multihot", "position_map"),
+                       moe.moe_route_multihot(xd, k, True)))
+    else:
+        sep = dict(zip(("topk_w", "topk_ids"), moe.moe_route(xd, k, True)))
+    sep.update(moe.moe_align(sep["topk_ids"], E))
+    torch.cuda.synchronize()
+    for key in sep:
+        a, b = got[key], sep[key]
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), key
+    ow, oids = oracle.route(x, k, True)
+    np.testing.assert_array_equal(got["topk_ids"].cpu().numpy(), oids)
+    ref = oracle.align(oids, E)
+    for key in ALIGN_KEYS:
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+
+
+def test_route_align_routing_workload():
+    w = mi.WORKLOADS["routing"]
+    x = mi.gating_logits(w)
+    got = moe.moe_route_align(dev(x), w.k, w.norm, with_multihot=True)
+    torch.cuda.synchronize()
+    assert moe.moe_route_align_fused(w.T, w.E, w.k)
+    ow, oids = oracle.route(x, w.k, w.norm)
+    np.testing.assert_array_equal(got["topk_ids"].cpu().numpy(), oids)
+    assert_weights_close(got["topk_w"].cpu().numpy(), ow)
+    ref = oracle.align(oids, w.E)
+    for key in ALIGN_KEYS:
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    mh, pim, pos = oracle.indices_to_multihot(oids, got["topk_w"].cpu().numpy(), w.E)
+    np.testing.assert_array_equal(got["multihot"].cpu().numpy(), mh)
+    np.testing.assert_array_equal(got["position_map"].cpu().numpy(), pos)
+    np.testing.assert_array_equal(got["probs_in_multihot"].cpu().numpy().view(np.int32),
+                                  pim.view(np.int32))
+
+
+# --------------------------------------------------------------------------
 # Multihot conversion and inverse
 # --------------------------------------------------------------------------
 
