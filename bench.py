@@ -287,8 +287,8 @@ def main():
     phases = ["route_align", "to_indices"]
     ra_out = {"topk_w": topk_w, "topk_ids": topk_ids, "multihot": mh, "probs_in_multihot": pim,
               "position_map": pos, **aligned}
-    if grouped:  # group-limited selection, then the same conversions
-        phases = ["route_grouped", "align", "to_multihot", "to_indices"]
+    if grouped:  # group-limited selection (+ indices->multihot), then align and the inverse
+        phases = ["route_grouped", "align", "to_indices"]
     if has_ffn:
         phases += ["gate_up", "down", "combine"]
 
@@ -300,7 +300,7 @@ def main():
                                 workspace=align_ws)
         elif name == "route_grouped":
             moe.moe_route_grouped(cur["logits"], k, w.n_group, w.topk_group, w.method, bias_d,
-                                  w.renorm, topk_w, topk_ids)
+                                  w.renorm, topk_w, topk_ids, multihot=(mh, pim, pos))
         elif name == "to_multihot":
             moe.moe_indices_to_multihot(topk_ids, topk_w, E, out=(mh, pim, pos))
         elif name == "align":
@@ -432,7 +432,7 @@ def main():
         nb = {"route_multihot": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
               "route_align": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4) + T * k * 12 +
               (2 * E + 1) * 4,
-              "route_grouped": T * E * 4 + E * 4 + T * k * 8,
+              "route_grouped": T * E * 4 + E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
               "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
               "to_indices": T * E * 8 + T * k * 8}
@@ -441,7 +441,7 @@ def main():
         names = {"route_multihot": "route_rows16_kernel (route + multihot)",
                  "route_align": "route_hist_kernel + align_scatter_kernel (route + multihot "
                                 "+ align)",
-                 "route_grouped": "route_grouped_kernel",
+                 "route_grouped": "route_grouped_rows16_kernel (selection + multihot)",
                  "to_multihot": "to_multihot kernel",
                  "align": "align_hist_kernel + align_scatter_kernel",
                  "to_indices": "to_indices kernel"}

@@ -167,6 +167,11 @@ moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_
  * topk_ids  [T, k] int32 out: selected experts in descending choice order.
  * topk_w    [T, k] float32 out: the scores (without the bias) of the selected
  *           experts; renormalize != 0 divides them by their sum.
+ * multihot, probs_in_multihot, position_map
+ *           [T, E] outputs of moe_indices_to_multihot on (topk_ids, topk_w),
+ *           bit for bit: all three given, or all NULL for none.  On the
+ *           16-lanes-per-row path (E % 16 == 0, E <= 256, n_group dividing 16,
+ *           k <= 16) the same kernel writes them.
  * Requires E % n_group == 0, 1 <= n_group <= MOE_MAX_GROUPS,
  * 1 <= topk_group <= n_group, 1 <= k <= min(MOE_MAX_TOPK,
  * topk_group * E / n_group), E <= MOE_MAX_EXPERTS, and groups of at least
@@ -175,7 +180,8 @@ moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_
 moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
                                int64_t T, int32_t E, int32_t k, int32_t n_group,
                                int32_t topk_group, int32_t method, int32_t renormalize,
-                               float *topk_w, int32_t *topk_ids, void *stream);
+                               float *topk_w, int32_t *topk_ids, uint8_t *multihot,
+                               float *probs_in_multihot, int32_t *position_map, void *stream);
 
 /* 1 if moe_route_multihot runs as one kernel for this E and k (E <= 64,
  * E % 4 == 0, k <= 16, k <= E), else 0. */

@@ -42,7 +42,7 @@ SIGNATURES = {
     "moe_route_multihot_fused": (_i32, [_i32, _i32]),
     "moe_router_route": (_st, [_st, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_route_grouped": (_st, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
-                                _vp]),
+                                _vp, _vp, _vp, _vp]),
     "moe_align_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_route_align": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _sz, _vp]),

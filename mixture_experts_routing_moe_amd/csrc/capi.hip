@@ -158,7 +158,8 @@ moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_
 moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
                                int64_t T, int32_t E, int32_t k, int32_t n_group,
                                int32_t topk_group, int32_t method, int32_t renormalize,
-                               float *topk_w, int32_t *topk_ids, void *stream) {
+                               float *topk_w, int32_t *topk_ids, uint8_t *multihot,
+                               float *probs_in_multihot, int32_t *position_map, void *stream) {
     const char *fn = "moe_route_grouped";
     moe_status_t st = check_routing_dims(T, E, k, fn);
     if (st != MOE_OK) return st;
@@ -175,6 +176,10 @@ moe_status_t moe_route_grouped(const float *scores, const float *e_score_correct
           "%s: k = %d > topk_group * group size = %d", fn, k, topk_group * gs);
     CHECK(method != MOE_NOAUX_TC || gs >= 2, MOE_ERR_INVALID_ARG,
           "%s: noaux_tc needs groups of at least 2 experts (E / n_group = %d)", fn, gs);
+    const int n_mh = (multihot != nullptr) + (probs_in_multihot != nullptr) +
+                     (position_map != nullptr);
+    CHECK(n_mh == 0 || n_mh == 3, MOE_ERR_INVALID_ARG,
+          "%s: give all three multihot outputs or none", fn);
     if (T == 0) return MOE_OK;
     CHECK(scores && topk_w && topk_ids, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     CHECK(method != MOE_NOAUX_TC || e_score_correction_bias, MOE_ERR_INVALID_ARG,
@@ -188,7 +193,8 @@ moe_status_t moe_route_grouped(const float *scores, const float *e_score_correct
                                                                        : nullptr,
                                                 T, E, k, n_group, topk_group,
                                                 method == MOE_NOAUX_TC, renormalize != 0, topk_w,
-                                                topk_ids, static_cast<hipStream_t>(stream)),
+                                                topk_ids, multihot, probs_in_multihot,
+                                                position_map, static_cast<hipStream_t>(stream)),
                       fn);
 }
 

@@ -248,9 +248,13 @@ hipError_t launch_route_multihot(const float *logits, int64_t T, int E, int k, i
                                  float *w, int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
                                  hipStream_t s);
 
+// Group-limited selection; with mh != nullptr also the indices->multihot
+// conversion of its output (in the same kernel on the 16-lanes-per-row path).
+bool route_grouped_rows16(int E, int n_group, int k);
 hipError_t launch_route_grouped(const float *scores, const float *bias, int64_t T, int E, int k,
                                 int n_group, int topk_group, int noaux, int renorm, float *w,
-                                int32_t *ids, hipStream_t s);
+                                int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                                hipStream_t s);
 
 hipError_t launch_router_route(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H,
                                int E, int k, int norm, float *logits, float *w, int32_t *ids,

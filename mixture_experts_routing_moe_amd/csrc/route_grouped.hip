@@ -228,11 +228,18 @@ __device__ __forceinline__ uint32_t choice_key(float f) {
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-template <int VPL, bool NOAUX>
+// With MH the kernel also writes the row's [E] multihot, probability and
+// position-map entries (the indices->multihot conversion of its selection):
+// each lane records the round that picked each of its experts, and the
+// probability of a picked expert is its score, re-read from the row and
+// renormalised exactly as the slot's weight is.  mvec: 16-byte aligned maps
+// and VPL % 4 == 0 (vector stores), else scalar stores.
+template <int VPL, bool NOAUX, bool MH>
 __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
     const float *__restrict__ scores, const float *__restrict__ bias, int64_t T, int k,
     int lg_log2, int topk_group, int renorm, int vec, float *__restrict__ topk_w,
-    int32_t *__restrict__ topk_ids) {
+    int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot, float *__restrict__ pim,
+    int32_t *__restrict__ pos, int mvec) {
     constexpr int E = 16 * VPL;
     constexpr int W = VPL % 4 == 0 ? 4 : (VPL % 2 == 0 ? 2 : 1);  // load width
     const int lane = lane_id();
@@ -323,6 +330,9 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
         }
 
         int sel_e = -1;
+        int pr[VPL];  // round that picked local expert i, -1 if none
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) pr[i] = -1;
         for (int r = 0; r < k; ++r) {
             // Lane-local best; strict > keeps the lowest local index on ties.
             uint32_t bk = key[0];
@@ -342,8 +352,12 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
             const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
             if (is_w) {
 #pragma unroll
-                for (int i = 0; i < VPL; ++i)
-                    if (i == bi) key[i] = 0u;
+                for (int i = 0; i < VPL; ++i) {
+                    if (i == bi) {
+                        key[i] = 0u;
+                        if (MH) pr[i] = r;
+                    }
+                }
             }
             if (q == r) sel_e = wl * VPL + (int)wbi;
         }
@@ -354,49 +368,97 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
         float w = 0.0f;
         if (out) w = scores[t * E + sel_e];
         float w_out = w;
+        double s = 1.0;
         if (renorm) {
-            const double s = row16_sum_f64(out ? (double)w : 0.0);
+            s = row16_sum_f64(out ? (double)w : 0.0);
             w_out = (float)((double)w / s);
         }
         if (out) {
             topk_w[t * k + q] = w_out;
             topk_ids[t * k + q] = sel_e;
         }
+        if (MH && row_ok) {
+            float pv[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                pv[i] = 0.0f;
+                if (pr[i] >= 0) {
+                    const float v = row[i];
+                    pv[i] = renorm ? (float)((double)v / s) : v;
+                }
+            }
+            uint8_t *mrow = multihot + t * E + e0;
+            float *prow = pim + t * E + e0;
+            int32_t *qrow = pos + t * E + e0;
+            if constexpr (VPL % 4 == 0) {
+                if (mvec) {
+#pragma unroll
+                    for (int j = 0; j < VPL / 4; ++j) {
+                        const uint32_t m = (uint32_t)(pr[4 * j] >= 0) |
+                                           (uint32_t)(pr[4 * j + 1] >= 0) << 8 |
+                                           (uint32_t)(pr[4 * j + 2] >= 0) << 16 |
+                                           (uint32_t)(pr[4 * j + 3] >= 0) << 24;
+                        reinterpret_cast<uint32_t *>(mrow)[j] = m;
+                        reinterpret_cast<float4 *>(prow)[j] =
+                            make_float4(pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]);
+                        reinterpret_cast<int4 *>(qrow)[j] =
+                            make_int4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
+                    }
+                    continue;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                mrow[i] = pr[i] >= 0 ? 1 : 0;
+                prow[i] = pv[i];
+                qrow[i] = pr[i];
+            }
+        }
     }
 }
 
-template <int VPL, bool NOAUX>
+template <int VPL, bool NOAUX, bool MH>
 hipError_t launch_rows16_t(const float *scores, const float *bias, int64_t T, int k,
                            int n_group, int topk_group, int renorm, float *w, int32_t *ids,
-                           hipStream_t s) {
+                           uint8_t *mh, float *pim, int32_t *pos, hipStream_t s) {
     int64_t blocks = (T + 4 * kGroupedWaves - 1) / (4 * kGroupedWaves);
     if (blocks > 16384) blocks = 16384;
     constexpr int W = VPL % 4 == 0 ? 4 : (VPL % 2 == 0 ? 2 : 1);
     const int vec = (reinterpret_cast<uintptr_t>(scores) & (4u * W - 1)) == 0;
     int lg_log2 = 0;
     while ((16 >> lg_log2) > n_group) ++lg_log2;
-    hipLaunchKernelGGL((route_grouped_rows16_kernel<VPL, NOAUX>), dim3((unsigned)blocks),
+    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const int mvec = MH && VPL % 4 == 0 && a16(mh) && a16(pim) && a16(pos);
+    hipLaunchKernelGGL((route_grouped_rows16_kernel<VPL, NOAUX, MH>), dim3((unsigned)blocks),
                        dim3(kGroupedThreads), 0, s, scores, bias, T, k, lg_log2, topk_group,
-                       renorm, vec, w, ids);
+                       renorm, vec, w, ids, mh, pim, pos, mvec);
     return hipGetLastError();
 }
 
 template <int VPL>
 hipError_t launch_rows16(const float *scores, const float *bias, int64_t T, int E, int k,
                          int n_group, int topk_group, int noaux, int renorm, float *w,
-                         int32_t *ids, hipStream_t s) {
+                         int32_t *ids, uint8_t *mh, float *pim, int32_t *pos, hipStream_t s) {
     if (E != 16 * VPL)
         return launch_rows16<VPL + 1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm,
-                                      w, ids, s);
+                                      w, ids, mh, pim, pos, s);
+    if (mh != nullptr) {
+        if (noaux)
+            return launch_rows16_t<VPL, true, true>(scores, bias, T, k, n_group, topk_group,
+                                                    renorm, w, ids, mh, pim, pos, s);
+        return launch_rows16_t<VPL, false, true>(scores, bias, T, k, n_group, topk_group, renorm,
+                                                 w, ids, mh, pim, pos, s);
+    }
     if (noaux)
-        return launch_rows16_t<VPL, true>(scores, bias, T, k, n_group, topk_group, renorm, w, ids,
-                                          s);
-    return launch_rows16_t<VPL, false>(scores, bias, T, k, n_group, topk_group, renorm, w, ids,
-                                       s);
+        return launch_rows16_t<VPL, true, false>(scores, bias, T, k, n_group, topk_group, renorm,
+                                                 w, ids, nullptr, nullptr, nullptr, s);
+    return launch_rows16_t<VPL, false, false>(scores, bias, T, k, n_group, topk_group, renorm, w,
+                                              ids, nullptr, nullptr, nullptr, s);
 }
 template <>
 hipError_t launch_rows16<17>(const float *, const float *, int64_t, int, int, int, int, int,
-                             int, float *, int32_t *, hipStream_t) {
+                             int, float *, int32_t *, uint8_t *, float *, int32_t *,
+                             hipStream_t) {
     return hipErrorInvalidValue;  // unreachable: E <= 256 is checked by the caller
 }
 
@@ -416,13 +478,25 @@ hipError_t launch_vpl(const float *scores, const float *bias, int64_t T, int E, 
 
 }  // namespace
 
+bool route_grouped_rows16(int E, int n_group, int k) {
+    return E % 16 == 0 && E <= 256 && 16 % n_group == 0 && k <= 16;
+}
+
 hipError_t launch_route_grouped(const float *scores, const float *bias, int64_t T, int E, int k,
                                 int n_group, int topk_group, int noaux, int renorm, float *w,
-                                int32_t *ids, hipStream_t s) {
+                                int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
+                                hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E % 16 == 0 && E <= 256 && 16 % n_group == 0 && k <= 16)
+    if (route_grouped_rows16(E, n_group, k))
         return launch_rows16<1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm, w, ids,
-                                s);
+                                mh, pim, pos, s);
+    if (mh != nullptr) {
+        const hipError_t err = launch_route_grouped(scores, bias, T, E, k, n_group, topk_group,
+                                                    noaux, renorm, w, ids, nullptr, nullptr,
+                                                    nullptr, s);
+        if (err != hipSuccess) return err;
+        return launch_to_multihot(ids, w, T, k, E, mh, pim, pos, s);
+    }
     if (E <= 64)
         return launch_vpl<1>(scores, bias, T, E, k, n_group, topk_group, noaux, renorm, w, ids, s);
     if (E <= 128)

@@ -86,9 +86,11 @@ GROUP_METHODS = {"group_limited_greedy": _lib.MOE_GROUP_LIMITED_GREEDY,
 
 def moe_route_grouped(scores: torch.Tensor, k: int, n_group: int, topk_group: int,
                       method: str = "noaux_tc", e_score_correction_bias=None,
-                      renormalize: bool = False, topk_w=None, topk_ids=None):
+                      renormalize: bool = False, topk_w=None, topk_ids=None, multihot=None):
     """Group-limited top-k (group_limited_greedy / noaux_tc) over [T, E] float32
-    scores -> (topk_w [T,k] f32, topk_ids [T,k] i32)."""
+    scores -> (topk_w [T,k] f32, topk_ids [T,k] i32).  multihot: True (allocate)
+    or a (multihot, probs_in_multihot, position_map) tuple of [T, E] outputs,
+    which the call also fills and appends to the result."""
     if scores.dtype != torch.float32 or scores.dim() != 2:
         raise ValueError("scores must be [T, E] float32")
     if method not in GROUP_METHODS:
@@ -101,10 +103,18 @@ def moe_route_grouped(scores: torch.Tensor, k: int, n_group: int, topk_group: in
         topk_w = torch.empty((T, k), dtype=torch.float32, device=scores.device)
     if topk_ids is None:
         topk_ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
-    _dev(scores, b, topk_w, topk_ids)
+    if multihot is True:
+        multihot = (torch.empty((T, E), dtype=torch.uint8, device=scores.device),
+                    torch.empty((T, E), dtype=torch.float32, device=scores.device),
+                    torch.empty((T, E), dtype=torch.int32, device=scores.device))
+    mh = multihot if multihot else (None, None, None)
+    _dev(scores, b, topk_w, topk_ids, *mh)
     check(lib().moe_route_grouped(_ptr(scores), _ptr(b), T, E, k, n_group, topk_group,
                                   GROUP_METHODS[method], int(bool(renormalize)), _ptr(topk_w),
-                                  _ptr(topk_ids), _stream()), "moe_route_grouped")
+                                  _ptr(topk_ids), _ptr(mh[0]), _ptr(mh[1]), _ptr(mh[2]),
+                                  _stream()), "moe_route_grouped")
+    if multihot:
+        return (topk_w, topk_ids, *multihot)
     return topk_w, topk_ids
 
 

@@ -122,8 +122,8 @@ def test_route_grouped_validation(lib):
     I = _lib.MOE_ERR_INVALID_ARG
     G, N = _lib.MOE_GROUP_LIMITED_GREEDY, _lib.MOE_NOAUX_TC
 
-    def rg(T, E, k, ng, tg, m, scores=FAKE, bias=FAKE, w=FAKE, ids=FAKE):
-        return lib.moe_route_grouped(scores, bias, T, E, k, ng, tg, m, 0, w, ids, None)
+    def rg(T, E, k, ng, tg, m, scores=FAKE, bias=FAKE, w=FAKE, ids=FAKE, mh=(None, None, None)):
+        return lib.moe_route_grouped(scores, bias, T, E, k, ng, tg, m, 0, w, ids, *mh, None)
 
     assert rg(4, 250, 8, 8, 4, N) == I  # E % n_group != 0
     assert b"not a multiple" in lib.moe_last_error()
@@ -138,6 +138,7 @@ def test_route_grouped_validation(lib):
     assert rg(4, 64, 2, 8, 2, G, scores=None) == I
     assert rg(4, 64, 2, 8, 2, G, scores=ctypes.c_void_p(0x1002)) == I  # misaligned
     assert rg(0, 64, 2, 8, 2, N, scores=None, bias=None, w=None, ids=None) == _lib.MOE_OK
+    assert rg(4, 64, 2, 8, 2, G, mh=(FAKE, FAKE, None)) == I  # multihot outputs: all or none
 
 
 def test_route_multihot_validation(lib):

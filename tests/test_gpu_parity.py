@@ -253,6 +253,31 @@ def test_route_grouped_shapes(T, E, n_group, topk_group, k, method, ties):
         _grouped_check(s, k, n_group, topk_group, method, b, renorm)
 
 
+@pytest.mark.parametrize("T,E,n_group,topk_group,k,method", [
+    (1031, 256, 8, 4, 8, "noaux_tc"), (700, 160, 8, 3, 6, "group_limited_greedy"),
+    (65, 48, 2, 1, 5, "noaux_tc"), (90, 32, 16, 3, 4, "group_limited_greedy"),
+    (129, 90, 9, 4, 7, "noaux_tc"), (40, 384, 12, 5, 16, "group_limited_greedy")])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_grouped_multihot(T, E, n_group, topk_group, k, method, renorm):
+    """The selection's [T, E] maps, written by the selection kernel (or, off its
+    fast path, by the converter after it), equal moe_indices_to_multihot of the
+    selection's own ids and weights bit for bit."""
+    g = np.random.Generator(np.random.PCG64(T + E + k))
+    s = g.random((T, E)).astype(np.float32)
+    b = dev((g.standard_normal(E) * 0.1).astype(np.float32)) if method == "noaux_tc" else None
+    w, ids, mh, pim, pos = moe.moe_route_grouped(dev(s), k, n_group, topk_group, method, b,
+                                                 renorm, multihot=True)
+    w2, ids2 = moe.moe_route_grouped(dev(s), k, n_group, topk_group, method, b, renorm)
+    rmh, rpim, rpos = moe.moe_indices_to_multihot(ids, w, E)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(mh, rmh) and torch.equal(pos, rpos)
+    assert torch.equal(pim.view(torch.int32), rpim.view(torch.int32))
+    _, oids = oracle.route_grouped(s, k, n_group, topk_group, method,
+                                   bias=None if b is None else b.cpu().numpy(), renormalize=renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+
+
 def test_route_grouped_unaligned_rows():
     # Scores starting 4 bytes past a 16-byte boundary take the scalar loads.
     w = mi.GROUPED["grouped_noaux"]
