@@ -667,10 +667,16 @@ def test_layer_deterministic():
 # memsets nothing, so every call is capturable)
 # --------------------------------------------------------------------------
 
-def _layer_into(bufs, logits, x, w13, w2, k, decode):
+def _layer_into(bufs, logits, x, w13, w2, k, decode, fused=False):
     T, E = logits.shape
-    moe.moe_route(logits, k, True, bufs["tw"], bufs["ids"])
-    moe.moe_align(bufs["ids"], E, bufs["aligned"], bufs["ws"])
+    if fused:  # route + multihot + align in one call, as the benchmark step runs them
+        out = {"topk_w": bufs["tw"], "topk_ids": bufs["ids"], **bufs["aligned"],
+               "multihot": bufs["mh"], "probs_in_multihot": bufs["pim"],
+               "position_map": bufs["pos"]}
+        moe.moe_route_align(logits, k, True, with_multihot=True, out=out, workspace=bufs["ws"])
+    else:
+        moe.moe_route(logits, k, True, bufs["tw"], bufs["ids"])
+        moe.moe_align(bufs["ids"], E, bufs["aligned"], bufs["ws"])
     moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
     moe.moe_ffn_down(bufs["act"], w2, bufs["aligned"], T, k, decode, bufs["y"])
     moe.moe_combine(bufs["y"], bufs["tw"], bufs["aligned"]["slot_to_sorted"], torch.bfloat16,
@@ -690,13 +696,18 @@ def _layer_bufs(T, H, I, E, k, decode):
         "act": torch.empty((T * k, I), dtype=torch.bfloat16, device=DEV),
         "y": torch.empty((sp, T * k, H), dtype=torch.float32, device=DEV),
         "out": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+        "mh": torch.empty((T, E), dtype=torch.uint8, device=DEV),
+        "pim": torch.empty((T, E), dtype=torch.float32, device=DEV),
+        "pos": torch.empty((T, E), dtype=torch.int32, device=DEV),
     }
 
 
 @pytest.mark.parametrize("T,H,I,E,k,decode", [(1, 256, 256, 16, 4, True),
                                               (32, 512, 384, 64, 8, True),
-                                              (300, 256, 2048, 8, 2, False)])
-def test_layer_graph_replay(T, H, I, E, k, decode):
+                                              (300, 256, 2048, 8, 2, False),
+                                              (2048, 256, 256, 64, 8, False)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_layer_graph_replay(T, H, I, E, k, decode, fused):
     """Replays of a captured step, with other GPU work between them, equal
     eager runs of the same step bit for bit, for several inputs."""
     x, w13, w2, _, _ = _rand_layer(T * 3 + I, T, H, I, E, k)
@@ -709,12 +720,12 @@ def test_layer_graph_replay(T, H, I, E, k, decode):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        _layer_into(bufs, static, xd, w13d, w2d, k, decode)
+        _layer_into(bufs, static, xd, w13d, w2d, k, decode, fused)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _layer_into(bufs, static, xd, w13d, w2d, k, decode)
+        _layer_into(bufs, static, xd, w13d, w2d, k, decode, fused)
     eager = _layer_bufs(T, H, I, E, k, decode)
     for r in (1, 2, 0, 3, 1):
         static.copy_(draws[r])
@@ -724,7 +735,58 @@ def test_layer_graph_replay(T, H, I, E, k, decode):
         got_ids = bufs["ids"].clone()
         # unrelated eager work, then the eager step on the same input
         torch.matmul(xd.float(), xd.float().t()).sum().item()
-        _layer_into(eager, draws[r], xd, w13d, w2d, k, decode)
+        _layer_into(eager, draws[r], xd, w13d, w2d, k, decode, fused)
         torch.cuda.synchronize()
         assert torch.equal(got_ids, eager["ids"])
         assert torch.equal(got.view(torch.int16), eager["out"].view(torch.int16))
+
+
+def test_grouped_routing_graph_replay():
+    """The grouped routing step (selection with its multihot maps, align,
+    inverse) replayed from a captured graph equals eager runs bit for bit."""
+    w = mi.GROUPED["grouped_noaux"]
+    T, E, k = 2048, w.E, w.k
+    draws = [dev(mi.grouped_scores(w, T=T, draw=r)) for r in range(3)]
+    bias = dev(mi.correction_bias(w))
+
+    def bufs():
+        return {"tw": torch.empty((T, k), dtype=torch.float32, device=DEV),
+                "ids": torch.empty((T, k), dtype=torch.int32, device=DEV),
+                "mh": (torch.empty((T, E), dtype=torch.uint8, device=DEV),
+                       torch.empty((T, E), dtype=torch.float32, device=DEV),
+                       torch.empty((T, E), dtype=torch.int32, device=DEV)),
+                "ws": torch.empty(max(1, moe.moe_align_workspace_size(T, k, E)),
+                                  dtype=torch.uint8, device=DEV),
+                "back": (torch.empty((T, k), dtype=torch.float32, device=DEV),
+                         torch.empty((T, k), dtype=torch.int32, device=DEV))}
+
+    def step(b, scores):
+        moe.moe_route_grouped(scores, k, w.n_group, w.topk_group, w.method, bias, w.renorm,
+                              b["tw"], b["ids"], multihot=b["mh"])
+        b["aligned"] = moe.moe_align(b["ids"], E, b.get("aligned"), b["ws"])
+        moe.moe_multihot_to_indices(b["mh"][1], b["mh"][2], k, out=b["back"])
+
+    static = torch.empty_like(draws[0])
+    static.copy_(draws[0])
+    gb, eb = bufs(), bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(gb, static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gb, static)
+    for r in (1, 2, 0, 1):
+        static.copy_(draws[r])
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {key: gb["aligned"][key].clone() for key in ALIGN_KEYS}
+        got_back = gb["back"][1].clone()
+        step(eb, draws[r])
+        torch.cuda.synchronize()
+        for key in ALIGN_KEYS:
+            assert torch.equal(got[key], eb["aligned"][key]), key
+        assert torch.equal(got_back, eb["back"][1])
+        assert torch.equal(got_back, eb["ids"])
