@@ -265,6 +265,10 @@ moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int
  *                   slot, -1 if none.
  * Positions outside [0, k) are ignored.  If two experts of a row name the same
  * slot (never produced by the forward conversion), the higher expert id wins.
+ * With ids_out = NULL this is also the backward of moe_indices_to_multihot
+ * ([mgt] IndicesToMultihot.backward): given the gradient of probs_in_multihot
+ * (any values, also where position_map is -1) and the forward's position_map,
+ * probs_indices is the gradient of the forward's probs.
  */
 moe_status_t moe_multihot_to_indices(const float *probs_in_multihot,
                                      const int32_t *position_map, int64_t T, int32_t E,

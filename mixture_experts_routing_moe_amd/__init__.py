@@ -15,6 +15,7 @@ from .moe import (  # noqa: F401
     moe_ffn_down_splits,
     moe_ffn_gate_up,
     moe_indices_to_multihot,
+    moe_indices_to_multihot_backward,
     moe_layer,
     moe_multihot_to_indices,
     moe_route,

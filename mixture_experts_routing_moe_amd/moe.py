@@ -217,6 +217,17 @@ def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
     return out
 
 
+def moe_indices_to_multihot_backward(grad_probs_in_multihot: torch.Tensor,
+                                     position_map: torch.Tensor, k: int, out=None):
+    """Gradient of moe_indices_to_multihot's probs from the gradient of its
+    probs_in_multihot ([mgt] IndicesToMultihot.backward): moe_multihot_to_indices
+    without the ids -> grad_probs [T, k] float32."""
+    if out is not None:
+        out = (out, None)
+    return moe_multihot_to_indices(grad_probs_in_multihot, position_map, k, with_ids=False,
+                                   out=out)[0]
+
+
 def moe_indices_to_multihot(ids: torch.Tensor, probs: torch.Tensor, E: int, out=None):
     """-> (multihot [T,E] u8, probs_in_multihot [T,E] f32, position_map [T,E] i32)."""
     if ids.dtype != torch.int32 or probs.dtype != torch.float32 or ids.shape != probs.shape:

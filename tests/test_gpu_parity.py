@@ -348,6 +348,22 @@ def test_align_deterministic():
         assert torch.equal(a1[key], a2[key])
 
 
+@pytest.mark.parametrize("T,E,k,inv", [(300, 64, 8, 0.0), (1000, 8, 2, 0.05), (77, 256, 8, 0.1),
+                                       (33, 30, 3, 0.0)])
+def test_indices_to_multihot_backward(T, E, k, inv):
+    """The converter's backward on a dense random gradient (nonzero where no
+    expert was selected, unlike any forward output) equals the oracle's
+    inverse conversion of that gradient bit for bit."""
+    ids = mi.random_ids(T + E, T, E, k, invalid_frac=inv)
+    probs = mi.random_probs(T + 1, T, k)
+    _, _, pos = moe.moe_indices_to_multihot(dev(ids), dev(probs), E)
+    grad = np.random.Generator(np.random.PCG64(T * E)).standard_normal((T, E)).astype(np.float32)
+    got = moe.moe_indices_to_multihot_backward(dev(grad), pos, k)
+    torch.cuda.synchronize()
+    ref, _ = oracle.multihot_to_indices(grad, pos.cpu().numpy(), k)
+    np.testing.assert_array_equal(got.cpu().numpy().view(np.int32), ref.view(np.int32))
+
+
 # --------------------------------------------------------------------------
 # Route + align in one call
 # --------------------------------------------------------------------------

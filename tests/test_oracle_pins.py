@@ -400,6 +400,27 @@ def test_multihot_roundtrip_and_dense(T, E, k, inv):
     np.testing.assert_array_equal(ids_back, np.where(valid, ids, -1))
 
 
+@pytest.mark.parametrize("T,E,k,inv", [(37, 8, 2, 0.0), (64, 64, 8, 0.1), (9, 5, 5, 0.0)])
+def test_converter_backward_is_the_adjoint(T, E, k, inv):
+    # [mgt] IndicesToMultihot.backward runs the inverse conversion on the
+    # gradient.  For fixed ids the forward's probability map F: probs [T,k] ->
+    # probs_in_multihot [T,E] is linear, so its backward B must be the adjoint:
+    # <F(p), g> = <p, B(g)> for every p and every gradient g, including
+    # gradients that are nonzero where no expert was selected.
+    ids = mi.random_ids(T * 7 + E, T, E, k, invalid_frac=inv)
+    g = np.random.Generator(np.random.PCG64(T + 3 * E))
+    for _ in range(3):
+        p = g.standard_normal((T, k)).astype(np.float32)
+        grad = g.standard_normal((T, E)).astype(np.float32)
+        _, fp, pos = oracle.indices_to_multihot(ids, p, E)
+        bg, _ = oracle.multihot_to_indices(grad, pos, k)
+        lhs = float(np.sum(fp.astype(np.float64) * grad.astype(np.float64)))
+        rhs = float(np.sum(p.astype(np.float64) * bg.astype(np.float64)))
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+    # Slots with an invalid id receive no gradient.
+    assert np.all(bg[ids < 0] == 0) and np.all(bg[ids >= E] == 0)
+
+
 # --------------------------------------------------------------------------
 # Expert FFN + weighted combine
 # --------------------------------------------------------------------------
