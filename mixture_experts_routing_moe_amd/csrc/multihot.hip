@@ -4,7 +4,7 @@
 // and _multihot_to_indices_kernel.  The pages run one program per row that
 // first initialises the row, waits on a barrier, then scatters the k entries.
 // Here lanes own expert columns (one wave per row with a lane per column, or
-// for E <= 64 four rows per wave with 4 columns per lane), so every output
+// for E <= 256 four rows per wave with 4, 8 or 16 columns per lane), so every output
 // element is written exactly once by its owner: no initialisation pass, no
 // barrier, and every store is coalesced.
 #include "moe_internal.h"
@@ -87,68 +87,93 @@ __global__ __launch_bounds__(kThreads) void to_indices_kernel(
     }
 }
 
-// Fast paths for E <= 64 with E % 4 == 0, k <= 16 and 16-byte aligned rows:
-// a wave holds 4 rows, 16 lanes per row, lane q owning experts 4q .. 4q+3, so
-// each lane writes its 4 columns with one 4-byte, one 16-byte and one 16-byte
-// store.
+// Fast paths for E <= 16 * CPL (CPL = 4, 8 or 16, so E <= 256) with
+// E % 4 == 0, k <= 16 and 16-byte aligned rows: a wave holds 4 rows, 16 lanes
+// per row, lane q owning experts CPL q .. CPL q + CPL - 1, so each lane
+// writes its columns in groups of 4 with one 4-byte, one 16-byte and one
+// 16-byte store.
 constexpr int kKMax16 = 16;
 
+template <int CPL>
 __global__ __launch_bounds__(kThreads) void to_multihot_rows16_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ probs, int64_t T, int k, int E,
     uint8_t *__restrict__ multihot, float *__restrict__ pim, int32_t *__restrict__ pos) {
     const int lane = lane_id();
     const int g = lane >> 4;
     const int q = lane & 15;
+    const int c0 = CPL * q;
     const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
     for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
         const int64_t t = t0 + g;
-        if (t >= T || 4 * q >= E) continue;
-        int pj[4] = {-1, -1, -1, -1};
-        float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (t >= T || c0 >= E) continue;
+        int pj[CPL];
+        float pv[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            pj[i] = -1;
+            pv[i] = 0.0f;
+        }
         for (int j = 0; j < kKMax16 && j < k; ++j) {  // later slots win
             const int id = ids[t * k + j];
             const float p = probs[t * k + j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (id == 4 * q + i) {
+            for (int i = 0; i < CPL; ++i) {
+                if (id == c0 + i) {
                     pj[i] = j;
                     pv[i] = p;
                 }
             }
         }
-        const uint32_t m = (uint32_t)(pj[0] >= 0) | (uint32_t)(pj[1] >= 0) << 8 |
-                           (uint32_t)(pj[2] >= 0) << 16 | (uint32_t)(pj[3] >= 0) << 24;
-        *reinterpret_cast<uint32_t *>(multihot + t * E + 4 * q) = m;
-        *reinterpret_cast<float4 *>(pim + t * E + 4 * q) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-        *reinterpret_cast<int4 *>(pos + t * E + 4 * q) = make_int4(pj[0], pj[1], pj[2], pj[3]);
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c) {
+            if (c0 + 4 * c >= E) break;
+            const int *a = pj + 4 * c;
+            const float *b = pv + 4 * c;
+            const uint32_t m = (uint32_t)(a[0] >= 0) | (uint32_t)(a[1] >= 0) << 8 |
+                               (uint32_t)(a[2] >= 0) << 16 | (uint32_t)(a[3] >= 0) << 24;
+            *reinterpret_cast<uint32_t *>(multihot + t * E + c0 + 4 * c) = m;
+            *reinterpret_cast<float4 *>(pim + t * E + c0 + 4 * c) =
+                make_float4(b[0], b[1], b[2], b[3]);
+            *reinterpret_cast<int4 *>(pos + t * E + c0 + 4 * c) = make_int4(a[0], a[1], a[2], a[3]);
+        }
     }
 }
 
 // Slot j of a row is filled from the highest expert naming it: each lane
 // proposes 1 + its highest expert per slot, a 16-lane DPP max per slot picks
 // the row's, and lane j fetches that expert's probability.
+template <int CPL>
 __global__ __launch_bounds__(kThreads) void to_indices_rows16_kernel(
     const float *__restrict__ pim, const int32_t *__restrict__ pos, int64_t T, int E, int k,
     float *__restrict__ probs, int32_t *__restrict__ ids) {
     const int lane = lane_id();
     const int g = lane >> 4;
     const int q = lane & 15;
+    const int c0 = CPL * q;
     const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
     for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
         const int64_t t = t0 + g;
         const bool row_ok = t < T;
-        int4 p4 = make_int4(-1, -1, -1, -1);
-        if (row_ok && 4 * q < E) p4 = *reinterpret_cast<const int4 *>(pos + t * E + 4 * q);
-        const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+        int pp[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c) {
+            int4 p4 = make_int4(-1, -1, -1, -1);
+            if (row_ok && c0 + 4 * c < E)
+                p4 = *reinterpret_cast<const int4 *>(pos + t * E + c0 + 4 * c);
+            pp[4 * c] = p4.x;
+            pp[4 * c + 1] = p4.y;
+            pp[4 * c + 2] = p4.z;
+            pp[4 * c + 3] = p4.w;
+        }
         uint32_t best[kKMax16];
 #pragma unroll
         for (int j = 0; j < kKMax16; ++j) {
             best[j] = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (pp[i] == j) best[j] = (uint32_t)(4 * q + i + 1);
+            for (int i = 0; i < CPL; ++i)
+                if (pp[i] == j) best[j] = (uint32_t)(c0 + i + 1);
         }
         uint32_t mine = 0;
 #pragma unroll
@@ -187,10 +212,18 @@ unsigned grid_for_rows(int64_t T) {
 hipError_t launch_to_multihot(const int32_t *ids, const float *probs, int64_t T, int k, int E,
                               uint8_t *mh, float *pim, int32_t *pos, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64 && E % 4 == 0 && k <= kKMax16 && aligned16(pim) && aligned16(pos) &&
+    if (E <= 256 && E % 4 == 0 && k <= kKMax16 && aligned16(pim) && aligned16(pos) &&
         (reinterpret_cast<uintptr_t>(mh) & 3u) == 0) {
-        hipLaunchKernelGGL(to_multihot_rows16_kernel, dim3(grid_for_rows16(T)), dim3(kThreads), 0,
-                           s, ids, probs, T, k, E, mh, pim, pos);
+        const dim3 grid(grid_for_rows16(T));
+        if (E <= 64)
+            hipLaunchKernelGGL(to_multihot_rows16_kernel<4>, grid, dim3(kThreads), 0, s, ids,
+                               probs, T, k, E, mh, pim, pos);
+        else if (E <= 128)
+            hipLaunchKernelGGL(to_multihot_rows16_kernel<8>, grid, dim3(kThreads), 0, s, ids,
+                               probs, T, k, E, mh, pim, pos);
+        else
+            hipLaunchKernelGGL(to_multihot_rows16_kernel<16>, grid, dim3(kThreads), 0, s, ids,
+                               probs, T, k, E, mh, pim, pos);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(to_multihot_kernel, dim3(grid_for_rows(T)), dim3(kThreads), 0, s, ids,
@@ -201,9 +234,17 @@ hipError_t launch_to_multihot(const int32_t *ids, const float *probs, int64_t T,
 hipError_t launch_to_indices(const float *pim, const int32_t *pos, int64_t T, int E, int k,
                              float *probs, int32_t *ids, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64 && E % 4 == 0 && k <= kKMax16 && aligned16(pos)) {
-        hipLaunchKernelGGL(to_indices_rows16_kernel, dim3(grid_for_rows16(T)), dim3(kThreads), 0,
-                           s, pim, pos, T, E, k, probs, ids);
+    if (E <= 256 && E % 4 == 0 && k <= kKMax16 && aligned16(pos)) {
+        const dim3 grid(grid_for_rows16(T));
+        if (E <= 64)
+            hipLaunchKernelGGL(to_indices_rows16_kernel<4>, grid, dim3(kThreads), 0, s, pim, pos,
+                               T, E, k, probs, ids);
+        else if (E <= 128)
+            hipLaunchKernelGGL(to_indices_rows16_kernel<8>, grid, dim3(kThreads), 0, s, pim, pos,
+                               T, E, k, probs, ids);
+        else
+            hipLaunchKernelGGL(to_indices_rows16_kernel<16>, grid, dim3(kThreads), 0, s, pim, pos,
+                               T, E, k, probs, ids);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(to_indices_kernel, dim3(grid_for_rows(T)), dim3(kThreads), 0, s, pim,

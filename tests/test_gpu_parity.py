@@ -454,7 +454,9 @@ def test_multihot_routing_workload_roundtrip():
 
 @pytest.mark.parametrize("T,E,k,inv", [(1, 4, 2, 0.0), (300, 64, 8, 0.0), (100, 6, 2, 0.25),
                                        (20, 300, 9, 0.1), (7, 1024, 64, 0.0), (513, 130, 5, 0.3),
-                                       (64, 1, 1, 0.0)])
+                                       (64, 1, 1, 0.0), (333, 128, 8, 0.1), (1001, 256, 8, 0.05),
+                                       (77, 160, 6, 0.0), (50, 100, 16, 0.2), (9, 68, 3, 0.0),
+                                       (40, 252, 17, 0.0)])
 def test_multihot_random(T, E, k, inv):
     _multihot_check(mi.random_ids(T + E, T, E, k, invalid_frac=inv), mi.random_probs(T + k, T, k),
                     E)
