@@ -279,9 +279,11 @@ __global__ __launch_bounds__(kRouteHistThreads) void route_hist_kernel(
     const int64_t r1 = r0 + rows_per_block < T ? r0 + rows_per_block : T;
     // Rows at or past r1 belong to the next block: r1 bounds the rows here.
     for (int64_t t0 = r0 + wave * 4; t0 < r1; t0 += kRouteHistRows) {
-        const int e = route16_row(logits, r1, t0 + g, E, k, norm, vec4, topk_w, topk_ids, multihot,
-                                  pim, pos, g, q);
-        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+        const uint32_t slot_of = route16_row(logits, r1, t0 + g, E, k, norm, vec4, topk_w,
+                                             topk_ids, multihot, pim, pos, g, q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (((slot_of >> (8 * i)) & 0xFFu) != 0xFFu) atomicAdd(&hist[4 * q + i], 1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kRouteHistThreads)

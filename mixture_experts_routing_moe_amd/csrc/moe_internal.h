@@ -99,21 +99,20 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // of them exist.  Selects the row's top k (value descending, the lower expert
 // id first among equal values) in k rounds: a lane-local best, a 4-step DPP
 // maximum over the row on order-preserving keys, and one ballot (the lowest
-// lane holding the maximum wins); a second maximum broadcasts the winner's
-// local slot.  Returns the weight of slot q (lanes q < k; softmax over the k
-// selected logits if norm, else the full softmax at the selected expert),
-// computed in double and rounded once.  sel_e = expert of slot q; byte i of
-// slot_of = the round that picked local expert i (0xFF if none).  Rows with
-// no available expert (past T) select nothing; lanes q >= k get sel_e = -1.
+// lane holding the maximum wins).  Returns the weight of slot q (lanes q < k;
+// softmax over the k selected logits if norm, else the full softmax at the
+// selected expert), computed in double and rounded once.  Byte i of slot_of
+// = the round (= slot) that picked local expert i (0xFF if none): the lane
+// that owns an expert writes its id, so no round broadcasts the winner's
+// local index.  Rows with no available expert (past T) select nothing.
 __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, int k, int norm,
-                                             int g, int q, int &sel_e, uint32_t &slot_of) {
+                                             int g, int q, uint32_t &slot_of) {
     const uint32_t valid = avail;
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) key[i] = float_key(v[i]);
 
     uint32_t sel_key = 0, kmax = 0;
-    sel_e = -1;
     slot_of = 0xFFFFFFFFu;
     for (int r = 0; r < k; ++r) {
         // Lane-local best; strict > keeps the lowest local slot on ties.
@@ -130,16 +129,11 @@ __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, i
         const uint64_t cand = __ballot(bk != 0 && bk == rmax);
         const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
         const int wl = __ffs((int)mrow) - 1;  // -1 only for rows without experts
-        const bool is_w = q == wl;
-        if (is_w) {
+        if (q == wl) {
             avail &= ~(1u << bi);
             slot_of = (slot_of & ~(0xFFu << (8 * bi))) | ((uint32_t)r << (8 * bi));
         }
-        const uint32_t wbi = row16_max_u32(is_w ? (uint32_t)bi : 0u);
-        if (q == r) {
-            sel_key = rmax;
-            sel_e = wl * 4 + (int)wbi;
-        }
+        if (q == r) sel_key = rmax;
         if (r == 0) kmax = rmax;
     }
 
@@ -166,9 +160,9 @@ __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, i
 // multihot, probability and position-map entries: each lane records which
 // round picked each of its 4 experts, fetches that slot's weight from the
 // lane that computed it, and writes its 4 columns.  vec4: E == 64 and
-// 16-byte aligned logits.  Returns the expert of slot q (-1 for q >= k or
-// rows past T).
-__device__ __forceinline__ int route16_row(const float *__restrict__ logits, int64_t T,
+// 16-byte aligned logits.  Returns slot_of (byte i: the slot that picked
+// local expert i, 0xFF if none; all 0xFF for rows past T).
+__device__ __forceinline__ uint32_t route16_row(const float *__restrict__ logits, int64_t T,
                                            int64_t t, int E, int k, int norm, int vec4,
                                            float *__restrict__ topk_w,
                                            int32_t *__restrict__ topk_ids,
@@ -197,11 +191,14 @@ __device__ __forceinline__ int route16_row(const float *__restrict__ logits, int
         }
     }
     uint32_t slot_of;  // byte i: round that picked local expert i (0xFF: none)
-    int sel_e;
-    const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
-    if (row_ok && q < k) {
-        topk_w[t * k + q] = wq;
-        topk_ids[t * k + q] = sel_e;
+    const float wq = route_row16(v, avail, k, norm, g, q, slot_of);
+    if (row_ok) {
+        if (q < k) topk_w[t * k + q] = wq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r = (slot_of >> (8 * i)) & 0xFFu;
+            if (r != 0xFFu) topk_ids[t * k + r] = 4 * q + i;
+        }
     }
     if (multihot != nullptr) {
         int pj[4];
@@ -224,7 +221,7 @@ __device__ __forceinline__ int route16_row(const float *__restrict__ logits, int
             *reinterpret_cast<int4 *>(pos + t * E + 4 * q) = make_int4(pj[0], pj[1], pj[2], pj[3]);
         }
     }
-    return row_ok ? sel_e : -1;
+    return slot_of;
 }
 
 // SiLU in float32: z / (1 + e^-z).

@@ -150,11 +150,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_route_kernel(
             }
         }
         uint32_t slot_of;
-        int sel_e;
-        const float wq = route_row16(v, avail, k, norm, g, q, sel_e, slot_of);
-        if (t < T && q < k) {
-            topk_w[t * k + q] = wq;
-            topk_ids[t * k + q] = sel_e;
+        const float wq = route_row16(v, avail, k, norm, g, q, slot_of);
+        if (t < T) {
+            if (q < k) topk_w[t * k + q] = wq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t r = (slot_of >> (8 * j)) & 0xFFu;
+                if (r != 0xFFu) topk_ids[t * k + r] = 4 * q + j;
+            }
         }
     }
 }
