@@ -231,7 +231,7 @@ __device__ __forceinline__ uint32_t choice_key(float f) {
 // With MH the kernel also writes the row's [E] multihot, probability and
 // position-map entries (the indices->multihot conversion of its selection):
 // each lane records the round that picked each of its experts, and the
-// probability of a picked expert is its score, re-read from the row and
+// probability of a picked expert is its score (kept from the row's load) and
 // renormalised exactly as the slot's weight is.  mvec: 16-byte aligned maps
 // and VPL % 4 == 0 (vector stores), else scalar stores.
 template <int VPL, bool NOAUX, bool MH>
@@ -285,8 +285,10 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
             }
         }
         uint32_t key[VPL];
+        float raw[MH ? VPL : 1];  // the scores themselves, for the maps
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
+            if (MH) raw[i] = c[i];
             if (NOAUX) c[i] = c[i] + b[i];  // float32 add, as on the page
             key[i] = row_ok ? choice_key(c[i]) : 0u;
         }
@@ -382,10 +384,7 @@ __global__ __launch_bounds__(kGroupedThreads) void route_grouped_rows16_kernel(
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 pv[i] = 0.0f;
-                if (pr[i] >= 0) {
-                    const float v = row[i];
-                    pv[i] = renorm ? (float)((double)v / s) : v;
-                }
+                if (pr[i] >= 0) pv[i] = renorm ? (float)((double)raw[i] / s) : raw[i];
             }
             uint8_t *mrow = multihot + t * E + e0;
             float *prow = pim + t * E + e0;
