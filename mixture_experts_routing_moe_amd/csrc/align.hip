@@ -331,9 +331,8 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
     return hipGetLastError();
 }
 
-bool route_align_fused(int64_t T, int E, int k, const float *logits, const uint8_t *mh,
-                       const float *pim, const int32_t *pos) {
-    (void)logits;
+bool route_align_fused(int64_t T, int E, int k, const uint8_t *mh, const float *pim,
+                       const int32_t *pos) {
     if (E > 64 || k > 16) return false;
     if (mh != nullptr && !route_multihot_fused(E, k, mh, pim, pos)) return false;
     const int64_t n = T * k;
@@ -351,7 +350,7 @@ hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int 
                               int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
                               int32_t *sorted_slot, int32_t *slot_to_sorted, int32_t *ws,
                               hipStream_t s) {
-    if (!route_align_fused(T, E, k, logits, mh, pim, pos)) {
+    if (!route_align_fused(T, E, k, mh, pim, pos)) {
         hipError_t err = mh != nullptr
                              ? launch_route_multihot(logits, T, E, k, norm, w, ids, mh, pim, pos, s)
                              : launch_route(logits, T, E, k, norm, w, ids, s);

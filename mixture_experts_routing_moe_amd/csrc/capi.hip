@@ -261,7 +261,7 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
 
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k) {
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK) return 0;
-    return moe::route_align_fused(T, E, k, nullptr, nullptr, nullptr, nullptr);
+    return moe::route_align_fused(T, E, k, nullptr, nullptr, nullptr);
 }
 
 moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,

@@ -265,8 +265,8 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
 // Route (+ indices->multihot when mh != nullptr) and align in fewer launches
 // where route_align_fused holds; otherwise the separate launches.  Outputs
 // are those of the separate calls, bit for bit.
-bool route_align_fused(int64_t T, int E, int k, const float *logits, const uint8_t *mh,
-                       const float *pim, const int32_t *pos);
+bool route_align_fused(int64_t T, int E, int k, const uint8_t *mh, const float *pim,
+                       const int32_t *pos);
 hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int norm, float *w,
                               int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
                               int32_t *counts, int32_t *offsets, int32_t *sorted_tok,

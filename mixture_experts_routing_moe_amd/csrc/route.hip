@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 // lane q of a row holding experts 4q .. 4q+3.  Every round of the top-k is a
 // 4-step DPP max over the row's 16 lanes on an order-preserving unsigned key
 // plus one ballot; the lowest lane holding the maximum wins, which is the
-// lowest expert id among equal logits.  A second 4-step max broadcasts the
-// winner's local slot.
+// lowest expert id among equal logits.  The lane that owns a picked expert
+// writes its id; lane j computes and writes slot j's weight.
 //
 // With multihot != nullptr (E % 4 == 0, 16-byte aligned rows) the same pass
 // also writes the row's [E] multihot, probability and position-map entries
