@@ -32,32 +32,58 @@ __device__ __forceinline__ void store8(float *p, const float *f) {
 }
 
 // y is float32 [splits, rows, H]; out is bf16 (uint16_t) or float32 [T, H].
+// The k slots of a token are taken in batches of KB: every load of a batch
+// is issued before the first is used, so a token costs one memory round
+// trip per batch instead of one per slot (what bounds a decode batch, where
+// a handful of blocks have nothing else to overlap).  The sums run in the
+// same order as slot by slot: planes in plane order, then slots in slot
+// order.
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float *__restrict__ y, int splits, int64_t plane, const float *__restrict__ w,
     const int32_t *__restrict__ s2s, int64_t ntok, int H, int k, OutT *__restrict__ out) {
+    constexpr int KB = 8;
     for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
         for (int h = threadIdx.x * V; h < H; h += kThreads * V) {
             float acc[V];
 #pragma unroll
             for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-            for (int j = 0; j < k; ++j) {
-                const int p = s2s[t * k + j];
-                if (p < 0) continue;
-                const float wj = w[t * k + j];
-                const float4 *src = reinterpret_cast<const float4 *>(y + (int64_t)p * H + h);
-                const float4 a = src[0], b = src[1];
-                float v[V] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                for (int sp = 1; sp < splits; ++sp) {
-                    const float4 *q = reinterpret_cast<const float4 *>(
-                        y + sp * plane + (int64_t)p * H + h);
-                    const float4 c = q[0], d = q[1];
-                    const float u[V] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+            for (int j0 = 0; j0 < k; j0 += KB) {
+                int p[KB];
+                float wj[KB];
+                float4 lo[KB], hi[KB];
 #pragma unroll
-                    for (int i = 0; i < V; ++i) v[i] += u[i];
+                for (int jj = 0; jj < KB; ++jj) {
+                    const int j = j0 + jj;
+                    p[jj] = j < k ? s2s[t * k + j] : -1;
+                    wj[jj] = j < k ? w[t * k + j] : 0.0f;
                 }
 #pragma unroll
-                for (int i = 0; i < V; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+                for (int jj = 0; jj < KB; ++jj) {
+                    lo[jj] = hi[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (p[jj] >= 0) {
+                        const float4 *src =
+                            reinterpret_cast<const float4 *>(y + (int64_t)p[jj] * H + h);
+                        lo[jj] = src[0];
+                        hi[jj] = src[1];
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < KB; ++jj) {
+                    if (p[jj] < 0) continue;
+                    float v[V] = {lo[jj].x, lo[jj].y, lo[jj].z, lo[jj].w,
+                                  hi[jj].x, hi[jj].y, hi[jj].z, hi[jj].w};
+                    for (int sp = 1; sp < splits; ++sp) {
+                        const float4 *q = reinterpret_cast<const float4 *>(
+                            y + sp * plane + (int64_t)p[jj] * H + h);
+                        const float4 c = q[0], d = q[1];
+                        const float u[V] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+#pragma unroll
+                        for (int i = 0; i < V; ++i) v[i] += u[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < V; ++i) acc[i] = fmaf(wj[jj], v[i], acc[i]);
+                }
             }
             store8(out + t * H + h, acc);
         }
