@@ -233,7 +233,7 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
  * Where moe_route_align_fused(T, E, k) is 1 (E <= 64, k <= 16, and for more
  * than 512 slots alignment chunks of at most 64 whole rows) the calls take
  * fewer launches: for at most 512 slots (decode batches) one kernel routes
- * and aligns; beyond that the route kernel also counts each alignment
+ * and aligns (one wave for at most 64 slots); beyond that the route kernel also counts each alignment
  * chunk's ids, so the alignment's histogram kernel is not launched.  (With
  * the multihot outputs the fused path also needs what moe_route_multihot's
  * one-kernel path needs.)  workspace: moe_align_workspace_size(T, k, E)

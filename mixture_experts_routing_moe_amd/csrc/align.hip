@@ -255,6 +255,80 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_small_kernel(
                         sorted_tok, sorted_slot, slot_to_sorted, sm);
 }
 
+// Route + align in one wave (at most 64 slots, E <= 64, k <= 16: decode
+// batches of up to 64 / k tokens).  The wave routes its rows with
+// route16_row and keeps the ids in LDS; lane s then takes slot s: its rank
+// among the earlier slots of the same expert comes from ceil(log2 E) ballots
+// (as in the scatter), the expert leaders record the counts, and lane e
+// scans them into the exclusive offsets.  Same outputs as the block path.
+__global__ __launch_bounds__(kWave) void route_align_wave_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int norm, int vec4,
+    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot,
+    float *__restrict__ pim, int32_t *__restrict__ pos, int nbits, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
+    __shared__ int32_t s_ids[kWave];
+    __shared__ int32_t s_cnt[kWave];
+    __shared__ int32_t s_off[kWave];
+    const int lane = lane_id();
+    const int g = lane >> 4;
+    const int q = lane & 15;
+    const int n = T * k;
+    s_ids[lane] = -1;
+    s_cnt[lane] = 0;
+    __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += 4) {
+        const int t = t0 + g;
+        const uint32_t slot_of = route16_row(logits, T, t, E, k, norm, vec4, topk_w, topk_ids,
+                                             multihot, pim, pos, g, q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r = (slot_of >> (8 * i)) & 0xFFu;
+            if (r != 0xFFu) s_ids[t * k + (int)r] = 4 * q + i;
+        }
+    }
+    __syncthreads();
+    const int s = lane;
+    const int e = s < n ? s_ids[s] : -1;
+    const bool ok = (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t m = __ballot(ok && set);
+        peers &= set ? m : ~m;
+    }
+    const int rank = __popcll(peers & lanemask_lt());
+    if (ok && rank == 0) s_cnt[e] = __popcll(peers);
+    __syncthreads();
+    const int c = lane < E ? s_cnt[lane] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    s_off[lane] = incl - c;
+    if (lane < E) {
+        counts[lane] = c;
+        offsets[lane] = incl - c;
+    }
+    if (lane == 0) offsets[E] = total;
+    __syncthreads();
+    if (ok) {
+        const int p = s_off[e] + rank;
+        sorted_tok[p] = s / k;
+        sorted_slot[p] = s;
+        slot_to_sorted[s] = p;
+    } else if (s < n) {
+        slot_to_sorted[s] = -1;
+    }
+    for (int p = total + lane; p < n; p += kWave) {
+        sorted_tok[p] = -1;
+        sorted_slot[p] = -1;
+    }
+}
+
 // Route with the alignment's per-block histograms: block b routes the rows of
 // alignment chunk b (rows_per_block = chunk / k rows, slots [b chunk,
 // (b + 1) chunk)) and counts their ids into partial[b][e], exactly what
@@ -364,6 +438,12 @@ hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int 
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+    if (n <= kWave) {
+        hipLaunchKernelGGL(route_align_wave_kernel, dim3(1), dim3(kWave), 0, s, logits, (int)T, E,
+                           k, norm, vec4, w, ids, mh, pim, pos, nbits, counts, offsets, sorted_tok,
+                           sorted_slot, slot_to_sorted);
+        return hipGetLastError();
+    }
     if (nb == 1) {
         hipLaunchKernelGGL(route_align_small_kernel, dim3(1), dim3(kAlignThreads),
                            scatter_lds_bytes(E), s, logits, (int)T, E, k, norm, vec4, w, ids, mh,

@@ -374,7 +374,8 @@ ALIGN_KEYS = ("counts", "offsets", "sorted_token_ids", "sorted_slot_ids", "slot_
 @pytest.mark.parametrize("T,E,k", [(1, 64, 8), (32, 64, 8), (64, 64, 8), (0, 64, 8), (5, 8, 2),
                                    (100, 60, 5), (16384, 64, 8), (4096, 8, 2), (3000, 64, 6),
                                    (777, 100, 4), (300, 64, 20), (9000, 36, 4),
-                                   (4096, 64, 16), (12000, 62, 8), (8192, 64, 8)])
+                                   (4096, 64, 16), (12000, 62, 8), (8192, 64, 8),
+                                   (8, 64, 8), (64, 16, 1), (3, 64, 16), (9, 20, 7)])
 @pytest.mark.parametrize("mh", [False, True])
 def test_route_align_matches_separate_calls(T, E, k, mh):
     g = np.random.Generator(np.random.PCG64(T * 3 + E + k))
