@@ -269,3 +269,16 @@ def test_even_mtile_split_never_empty():
         mt = -(-cn // bm)
         q = -(-cn // (32 * mt)) * 32
         assert q <= bm and (mt - 1) * q < cn <= mt * q, cn
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asking for more exits with status 2 and a JSON
+    message before anything touches a GPU."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
