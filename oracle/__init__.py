@@ -1,4 +1,4 @@
-"""CPU oracle of the MoE layer forward (numpy front end over moe_oracle.c).
+"""CPU oracle of the MoE layer forward and backward (numpy front end over moe_oracle.c).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
 of the benchmark may import this package.  The product library never does,
@@ -49,9 +49,16 @@ def _load():
         lib.oracle_multihot_to_indices.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_expert_ffn.argtypes = [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                           vp, i64, vp, i32]
+        lib.oracle_route_backward.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_expert_ffn_backward.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
+                                                   i32, i32, vp, i64, vp, vp, vp, vp, i32]
+        lib.oracle_expert_wgrad_entries.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
+                                                    i32, i32, i64, vp, vp, vp, i64, vp, vp, vp,
+                                                    i32]
         for f in (lib.oracle_route, lib.oracle_router_logits, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
                   lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
-                  lib.oracle_expert_ffn):
+                  lib.oracle_expert_ffn, lib.oracle_route_backward,
+                  lib.oracle_expert_ffn_backward, lib.oracle_expert_wgrad_entries):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -208,3 +215,80 @@ def layer(inp: dict, k: int, norm_topk_prob: bool, dtype: str, tokens=None,
         out["out"] = expert_ffn(inp["hidden"], inp["w13"], inp["w2"], w, ids, dtype,
                                 tokens=tokens, threads=threads)
     return out
+
+
+def route_backward(logits: np.ndarray, topk_ids: np.ndarray, grad_topk_w: np.ndarray,
+                   norm_topk_prob: bool = True) -> np.ndarray:
+    """Gradient of the gating softmax weights w.r.t. the logits -> [T, E] float64."""
+    x = _c(logits, np.float32)
+    ids = _c(topk_ids, np.int32)
+    g = _c(grad_topk_w, np.float64)
+    T, E = x.shape
+    k = ids.shape[1]
+    out = np.empty((T, E), np.float64)
+    _check(_load().oracle_route_backward(_p(x), _p(ids), T, E, k, int(bool(norm_topk_prob)),
+                                         _p(g), _p(out)), "route_backward")
+    return out
+
+
+def _ffn_operands(hidden, w13, w2, topk_w, topk_ids, grad_out, dtype):
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    npdt = np.float32 if dt == 0 else np.uint16
+    hidden, w13, w2, grad_out = (_c(a, npdt) for a in (hidden, w13, w2, grad_out))
+    T, H = hidden.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (E, H, I) and grad_out.shape == (T, H)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_w, np.float64)
+    return dt, hidden, w13, w2, w, ids, grad_out, T, H, I, E, ids.shape[1]
+
+
+def expert_ffn_backward(hidden, w13, w2, topk_w, topk_ids, grad_out, dtype: str,
+                        tokens=None, weights: bool = False, threads: int | None = None) -> dict:
+    """Backward of expert_ffn in float64.
+
+    Returns grad_hidden [n, H] and grad_topk_w [n, k] for the listed tokens (all T if
+    None); with weights=True (all tokens only) also grad_w13 [E, 2I, H] and
+    grad_w2 [E, H, I].
+    """
+    dt, hidden, w13, w2, w, ids, dy, T, H, I, E, k = _ffn_operands(
+        hidden, w13, w2, topk_w, topk_ids, grad_out, dtype)
+    assert not (weights and tokens is not None)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    out = {"grad_hidden": np.empty((n, H), np.float64),
+           "grad_topk_w": np.empty((n, k), np.float64)}
+    if weights:
+        out["grad_w13"] = np.empty((E, 2 * I, H), np.float64)
+        out["grad_w2"] = np.empty((E, H, I), np.float64)
+    nthr = threads if threads else (os.cpu_count() or 1)
+    _check(_load().oracle_expert_ffn_backward(
+        dt, _p(hidden), _p(w13), _p(w2), _p(w), _p(ids), _p(dy), T, H, I, E, k,
+        _p(tok) if tok is not None else None, n, _p(out["grad_hidden"]),
+        _p(out["grad_topk_w"]), _p(out["grad_w13"]) if weights else None,
+        _p(out["grad_w2"]) if weights else None, nthr), "expert_ffn_backward")
+    return out
+
+
+def expert_wgrad_entries(hidden, w13, w2, topk_w, topk_ids, grad_out, dtype: str,
+                         rows13=(), cols2=(), threads: int | None = None):
+    """Rows of grad_w13 and columns of grad_w2 from their definitions.
+
+    rows13: (e, c) pairs -> [len, H] rows c of grad_w13[e]; cols2: (e, i) pairs ->
+    [len, H] columns i of grad_w2[e].
+    """
+    dt, hidden, w13, w2, w, ids, dy, T, H, I, E, k = _ffn_operands(
+        hidden, w13, w2, topk_w, topk_ids, grad_out, dtype)
+    r13 = _c(np.array(rows13, np.int32).reshape(-1, 2), np.int32)
+    c2 = _c(np.array(cols2, np.int32).reshape(-1, 2), np.int32)
+    e13, cc13 = _c(r13[:, 0], np.int32), _c(r13[:, 1], np.int32)
+    e2, ii2 = _c(c2[:, 0], np.int32), _c(c2[:, 1], np.int32)
+    row13 = np.empty((len(r13), H), np.float64)
+    col2 = np.empty((len(c2), H), np.float64)
+    nthr = threads if threads else (os.cpu_count() or 1)
+    _check(_load().oracle_expert_wgrad_entries(
+        dt, _p(hidden), _p(w13), _p(w2), _p(w), _p(ids), _p(dy), T, H, I, E, k,
+        len(r13), _p(e13), _p(cc13), _p(row13), len(c2), _p(e2), _p(ii2), _p(col2), nthr),
+        "expert_wgrad_entries")
+    return row13, col2

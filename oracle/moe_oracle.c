@@ -1,5 +1,6 @@
 /*
- * moe_oracle.c -- plain, slow CPU oracle of the MoE layer forward.
+ * moe_oracle.c -- plain, slow CPU oracle of the MoE layer forward and of its
+ * backward (the chain rule on the same definitions).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the smoke check and the CPU-baseline leg of
@@ -476,6 +477,262 @@ int oracle_expert_ffn(int32_t dt, const void *hidden, const void *w13, const voi
         }
         free(x);
         free(act);
+    }
+    return fail ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/*
+ * Backward of the gating softmax of oracle_route, by the chain rule (the
+ * pages give only the forward).  grad_topk_w [T, k] is the gradient of the
+ * routing weights; the selection is piecewise constant and passes none.
+ * topk_ids are the forward's (valid and distinct within a row).  The weights
+ * are recomputed from the logits in double.
+ *   norm_topk_prob:  w = softmax of the k selected logits, so
+ *                    grad_logits[e_j] = w_j (g_j - sum_i w_i g_i), 0 elsewhere.
+ *   otherwise:       w_j = p[e_j] of the softmax p over all E logits, so
+ *                    grad_logits[e] = p[e] (g(e) - sum_j w_j g_j), where
+ *                    g(e) = g_j if e = e_j, else 0.
+ */
+int oracle_route_backward(const float *logits, const int32_t *topk_ids, int64_t T, int32_t E,
+                          int32_t k, int32_t norm_topk_prob, const double *grad_topk_w,
+                          double *grad_logits)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return ORACLE_EINVAL;
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    if (!p)
+        return ORACLE_ENOMEM;
+    int fail = 0;
+    for (int64_t t = 0; t < T && !fail; ++t) {
+        const float *x = logits + t * E;
+        const int32_t *ids = topk_ids + t * k;
+        const double *g = grad_topk_w + t * k;
+        double *out = grad_logits + t * E;
+        for (int32_t j = 0; j < k; ++j)
+            if (ids[j] < 0 || ids[j] >= E)
+                fail = 1;
+        if (fail)
+            break;
+        /* p[e]: the probability the forward assigns (selected experts only
+         * under norm_topk_prob). */
+        double m = -INFINITY, s = 0.0;
+        if (norm_topk_prob) {
+            for (int32_t j = 0; j < k; ++j)
+                m = fmax(m, (double)x[ids[j]]);
+            for (int32_t j = 0; j < k; ++j)
+                s += exp((double)x[ids[j]] - m);
+        } else {
+            for (int32_t e = 0; e < E; ++e)
+                m = fmax(m, (double)x[e]);
+            for (int32_t e = 0; e < E; ++e)
+                s += exp((double)x[e] - m);
+        }
+        for (int32_t e = 0; e < E; ++e)
+            p[e] = exp((double)x[e] - m) / s;
+        double dot = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            dot += p[ids[j]] * g[j];
+        for (int32_t e = 0; e < E; ++e)
+            out[e] = norm_topk_prob ? 0.0 : -p[e] * dot;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = ids[j];
+            if (norm_topk_prob)
+                out[e] = p[e] * (g[j] - dot);
+            else
+                out[e] += p[e] * g[j];
+        }
+    }
+    free(p);
+    return fail ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/*
+ * Backward of oracle_expert_ffn (same inputs), by the chain rule; the pages
+ * print only the forward.  grad_out [T, H] is the gradient of the layer
+ * output (dt as the other inputs).  For a token t and a slot j with a valid
+ * expert e and weight w, with w1 = rows [0, I) of w13[e], w3 = rows [I, 2I),
+ * gate = x . w1^T, up = x . w3^T, s = sigmoid(gate), act = gate s up and
+ * y = act . w2[e]^T:
+ *   grad_topk_w[t, j] = <grad_out[t], y>
+ *   d_act  = w (grad_out[t] . w2[e])                       (I values)
+ *   d_gate = d_act up s (1 + gate (1 - s)),   d_up = d_act gate s
+ *   grad_hidden[t] = sum over j of d_gate . w1 + d_up . w3
+ *   grad_w2[e]  += w grad_out[t]^T act                     ([H, I])
+ *   grad_w13[e] += [d_gate ; d_up]^T x                     ([2I, H])
+ * Invalid slots give grad_topk_w 0 and add nothing; experts no slot names get
+ * zero weight gradients.
+ *
+ * tokens[0..ntok) lists the rows whose grad_hidden [ntok, H] and grad_topk_w
+ * [ntok, k] are wanted (NULL = all T in order).  grad_w13 [E, 2I, H] and
+ * grad_w2 [E, H, I] may be NULL; when given, tokens must be NULL and the
+ * tokens run one after another in ascending order (so every sum has a fixed
+ * order); otherwise tokens are spread over nthreads.  All outputs double.
+ */
+int oracle_expert_ffn_backward(int32_t dt, const void *hidden, const void *w13, const void *w2,
+                               const double *topk_w, const int32_t *topk_ids,
+                               const void *grad_out, int64_t T, int32_t H, int32_t I, int32_t E,
+                               int32_t k, const int64_t *tokens, int64_t ntok,
+                               double *grad_hidden, double *grad_topk_w, double *grad_w13,
+                               double *grad_w2, int32_t nthreads)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || (dt != 0 && dt != 1))
+        return ORACLE_EINVAL;
+    const int weights = grad_w13 != NULL || grad_w2 != NULL;
+    if (weights && (tokens || !grad_w13 || !grad_w2))
+        return ORACLE_EINVAL;
+    if (!tokens)
+        ntok = T;
+    if (weights) {
+        for (int64_t q = 0; q < (int64_t)E * 2 * I * H; ++q)
+            grad_w13[q] = 0.0;
+        for (int64_t q = 0; q < (int64_t)E * H * I; ++q)
+            grad_w2[q] = 0.0;
+    }
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(weights ? 1 : (nthreads > 0 ? nthreads : 1))
+    for (int64_t r = 0; r < ntok; ++r) {
+        int64_t t = tokens ? tokens[r] : r;
+        double *x = (double *)malloc(sizeof(double) * (size_t)H);
+        double *dy = (double *)malloc(sizeof(double) * (size_t)H);
+        double *v = (double *)malloc(sizeof(double) * (size_t)I * 5);
+        if (!x || !dy || !v || t < 0 || t >= T) {
+            free(x);
+            free(dy);
+            free(v);
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        double *gate = v, *up = v + I, *act = v + 2 * I, *dgate = v + 3 * I, *dup = v + 4 * I;
+        for (int32_t h = 0; h < H; ++h) {
+            x[h] = load_elem(dt, hidden, t * H + h);
+            dy[h] = load_elem(dt, grad_out, t * H + h);
+            grad_hidden[r * H + h] = 0.0;
+        }
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = topk_ids[t * k + j];
+            grad_topk_w[r * k + j] = 0.0;
+            if (e < 0 || e >= E)
+                continue;
+            double w = topk_w[t * k + j];
+            int64_t base13 = (int64_t)e * 2 * I * H;
+            int64_t base2 = (int64_t)e * H * I;
+            for (int32_t i = 0; i < I; ++i) {
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    g += x[h] * load_elem(dt, w13, base13 + (int64_t)i * H + h);
+                    u += x[h] * load_elem(dt, w13, base13 + (int64_t)(I + i) * H + h);
+                }
+                gate[i] = g;
+                up[i] = u;
+                act[i] = silu(g) * u;
+            }
+            /* grad_topk_w = <grad_out, y> with y = act . w2^T */
+            double dw = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                double y = 0.0;
+                for (int32_t i = 0; i < I; ++i)
+                    y += act[i] * load_elem(dt, w2, base2 + (int64_t)h * I + i);
+                dw += dy[h] * y;
+            }
+            grad_topk_w[r * k + j] = dw;
+            for (int32_t i = 0; i < I; ++i) {
+                double da = 0.0;
+                for (int32_t h = 0; h < H; ++h)
+                    da += dy[h] * load_elem(dt, w2, base2 + (int64_t)h * I + i);
+                da *= w;
+                double s = 1.0 / (1.0 + exp(-gate[i]));
+                dgate[i] = da * up[i] * s * (1.0 + gate[i] * (1.0 - s));
+                dup[i] = da * gate[i] * s;
+            }
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t i = 0; i < I; ++i)
+                    acc += dgate[i] * load_elem(dt, w13, base13 + (int64_t)i * H + h) +
+                           dup[i] * load_elem(dt, w13, base13 + (int64_t)(I + i) * H + h);
+                grad_hidden[r * H + h] += acc;
+            }
+            if (weights) {
+                for (int32_t h = 0; h < H; ++h)
+                    for (int32_t i = 0; i < I; ++i)
+                        grad_w2[base2 + (int64_t)h * I + i] += w * dy[h] * act[i];
+                for (int32_t i = 0; i < I; ++i)
+                    for (int32_t h = 0; h < H; ++h) {
+                        grad_w13[base13 + (int64_t)i * H + h] += dgate[i] * x[h];
+                        grad_w13[base13 + (int64_t)(I + i) * H + h] += dup[i] * x[h];
+                    }
+            }
+        }
+        free(x);
+        free(dy);
+        free(v);
+    }
+    return fail ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/*
+ * Single rows and columns of the weight gradients of
+ * oracle_expert_ffn_backward, each from its definition, for checks at sizes
+ * where the whole gradient is too slow on a CPU.  Row c of grad_w13[e] sums
+ * d_c x[t] over the slots of e (d_c = d_gate or d_up of unit c mod I), and
+ * column i of grad_w2[e] sums w act_i grad_out[t] over them; each needs only
+ * gate and up of one unit per slot.  Slots are visited in ascending (t, j).
+ * row13 [n13, H] gets row c13[q] of grad_w13[e13[q]]; col2 [n2, H] gets
+ * column i2[q] of grad_w2[e2[q]].
+ */
+int oracle_expert_wgrad_entries(int32_t dt, const void *hidden, const void *w13, const void *w2,
+                                const double *topk_w, const int32_t *topk_ids,
+                                const void *grad_out, int64_t T, int32_t H, int32_t I,
+                                int32_t E, int32_t k, int64_t n13, const int32_t *e13,
+                                const int32_t *c13, double *row13, int64_t n2,
+                                const int32_t *e2, const int32_t *i2, double *col2,
+                                int32_t nthreads)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || (dt != 0 && dt != 1))
+        return ORACLE_EINVAL;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t q = 0; q < n13 + n2; ++q) {
+        const int is13 = q < n13;
+        const int32_t e = is13 ? e13[q] : e2[q - n13];
+        const int32_t c = is13 ? c13[q] : i2[q - n13];
+        double *out = is13 ? row13 + q * H : col2 + (q - n13) * H;
+        if (e < 0 || e >= E || c < 0 || c >= (is13 ? 2 * I : I)) {
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        const int32_t i = is13 ? c % I : c;
+        const int64_t base13 = (int64_t)e * 2 * I * H;
+        const int64_t base2 = (int64_t)e * H * I;
+        for (int32_t h = 0; h < H; ++h)
+            out[h] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            for (int32_t j = 0; j < k; ++j) {
+                if (topk_ids[t * k + j] != e)
+                    continue;
+                double w = topk_w[t * k + j];
+                double g = 0.0, u = 0.0, da = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    double xh = load_elem(dt, hidden, t * H + h);
+                    g += xh * load_elem(dt, w13, base13 + (int64_t)i * H + h);
+                    u += xh * load_elem(dt, w13, base13 + (int64_t)(I + i) * H + h);
+                    da += load_elem(dt, grad_out, t * H + h) *
+                          load_elem(dt, w2, base2 + (int64_t)h * I + i);
+                }
+                da *= w;
+                double s = 1.0 / (1.0 + exp(-g));
+                if (is13) {
+                    double d = c < I ? da * u * s * (1.0 + g * (1.0 - s)) : da * g * s;
+                    for (int32_t h = 0; h < H; ++h)
+                        out[h] += d * load_elem(dt, hidden, t * H + h);
+                } else {
+                    double a = silu(g) * u;
+                    for (int32_t h = 0; h < H; ++h)
+                        out[h] += w * load_elem(dt, grad_out, t * H + h) * a;
+                }
+            }
+        }
     }
     return fail ? ORACLE_EINVAL : ORACLE_OK;
 }
