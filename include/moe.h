@@ -17,6 +17,9 @@
  *                             weighted combine (prefill, any T)
  *   moe_expert_ffn_decode     the same for T <= MOE_DECODE_MAX_T, streaming only
  *                             the selected experts' weights
+ *   moe_route_backward        gradient of the gating softmax weights w.r.t. the logits
+ *   moe_expert_ffn_backward   gradients of moe_expert_ffn w.r.t. hidden, w13, w2
+ *                             and the routing weights
  *
  * plus the three phases of moe_expert_ffn as separate calls, so a caller can
  * place its own events between them.
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 5
+#define MOE_VERSION 6
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 64
 #define MOE_DECODE_MAX_T 64
@@ -318,6 +321,68 @@ moe_status_t moe_expert_ffn_decode(moe_dtype_t dt, const void *hidden, const voi
                                    const int32_t *slot_to_sorted, int64_t T, int32_t H,
                                    int32_t I, int32_t E, int32_t k, void *out,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_route_backward -- backward of moe_route's weights.
+ * The chain rule applied to [mlc] gating_softmax_topk (the pages give only
+ * the forward); the selection is piecewise constant and passes no gradient.
+ *
+ * logits      [T, E] float32 in: the forward's logits.
+ * topk_ids    [T, k] int32 in, topk_w [T, k] float32 in: the forward's outputs
+ *             (ids valid and distinct within a row, as moe_route writes them).
+ * grad_topk_w [T, k] float32 in: gradient of the weights.
+ * grad_logits [T, E] float32 out.  With dot = sum_j topk_w[j] grad_topk_w[j]:
+ *   norm_topk_prob != 0: grad[e_j] = topk_w[j] (grad_topk_w[j] - dot), 0 for
+ *                        unselected experts;
+ *   norm_topk_prob == 0: grad[e] = p_e (g(e) - dot), p = softmax of the row's
+ *                        E logits, g(e) = grad_topk_w[j] if e = e_j, else 0.
+ * Requires k <= E.  Pointers 4-byte aligned.
+ */
+moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
+                                const float *topk_w, const float *grad_topk_w, int64_t T,
+                                int32_t E, int32_t k, int32_t norm_topk_prob,
+                                float *grad_logits, void *stream);
+
+/*
+ * moe_expert_ffn_backward -- backward of moe_expert_ffn (bfloat16 layer).
+ * The chain rule applied to [p6] moe_prefill_experts and [mlc] moe_sum (the
+ * pages give only the forward).  For each valid slot (t, j) with expert e and
+ * weight w, with gate/up = hidden[t] . w13[e]^T halves, s = sigmoid(gate),
+ * act = gate s up, dy = grad_out[t] and G = dy . w2[e]:
+ *   grad_topk_w[t, j] = <G, act>                    (= <dy, y(t, j)>)
+ *   d_gate = w G up s (1 + gate (1 - s)),  d_up = w G gate s
+ *   grad_hidden[t]    = sum over j of [d_gate ; d_up] . w13[e]
+ *   grad_w2[e]        = sum over the slots of e of (w dy)^T act
+ *   grad_w13[e]       = sum over the slots of e of [d_gate ; d_up]^T hidden[t]
+ * Slots with an invalid id get grad_topk_w = 0 and add nothing; an expert no
+ * slot names gets zero weight gradients (every element of every output is
+ * written).  gate/up are recomputed (one grouped product); w act and
+ * d_gate/d_up are rounded to bfloat16 as the inputs of the bf16 products,
+ * everything else accumulates in float32.  Results are deterministic.
+ *
+ * dt must be MOE_BF16.  hidden [T, H], w13 [E, 2I, H], w2 [E, H, I],
+ * grad_out [T, H] bfloat16; topk_w [T, k] float32; expert_offsets [E+1],
+ * sorted_token_ids, sorted_slot_ids and slot_to_sorted [T*k] as written by
+ * moe_align for the forward's ids.  Outputs float32: grad_hidden [T, H],
+ * grad_w13 [E, 2I, H], grad_w2 [E, H, I], grad_topk_w [T, k].
+ * workspace >= moe_expert_ffn_backward_workspace_size(T, H, I, E, k) bytes
+ * (T*k*(18 I + 4 H) bytes, rounded), 16-byte aligned, clobbered.
+ * Requires H % 64 == 0, I % 64 == 0; hidden, weights, grad_out and the
+ * gradients 16-byte aligned.  T = 0 enqueues nothing, as for every call, so
+ * the weight gradients are then left as they were.
+ */
+size_t moe_expert_ffn_backward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
+                                              int32_t k);
+moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const void *w13,
+                                     const void *w2, const float *topk_w,
+                                     const int32_t *expert_offsets,
+                                     const int32_t *sorted_token_ids,
+                                     const int32_t *sorted_slot_ids,
+                                     const int32_t *slot_to_sorted, const void *grad_out,
+                                     int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                     float *grad_hidden, float *grad_w13, float *grad_w2,
+                                     float *grad_topk_w, void *workspace,
+                                     size_t workspace_bytes, void *stream);
 
 /*
  * The three phases of moe_expert_ffn (same kernels, same arguments).

@@ -1,4 +1,4 @@
-"""libmoe: the Mixture-of-Experts layer forward on AMD MI355X (gfx950).
+"""libmoe: the Mixture-of-Experts layer forward (and its backward) on AMD MI355X (gfx950).
 
 The compute lives in libmoe.so (hand-written HIP kernels behind the C ABI of
 include/moe.h); this package only binds it to torch tensors.
@@ -10,6 +10,8 @@ from .moe import (  # noqa: F401
     moe_align_workspace_size,
     moe_combine,
     moe_expert_ffn,
+    moe_expert_ffn_backward,
+    moe_expert_ffn_backward_workspace_size,
     moe_expert_ffn_workspace_size,
     moe_ffn_down,
     moe_ffn_down_splits,
@@ -21,6 +23,7 @@ from .moe import (  # noqa: F401
     moe_route,
     moe_route_align,
     moe_route_align_fused,
+    moe_route_backward,
     moe_route_grouped,
     moe_route_multihot,
     moe_route_multihot_fused,

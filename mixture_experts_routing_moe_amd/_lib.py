@@ -25,7 +25,7 @@ MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
 MOE_DECODE_MAX_T = 64
 MOE_MAX_SPLITS = 8
-MOE_VERSION = 5
+MOE_VERSION = 6
 MOE_MAX_GROUPS = 64
 MOE_GROUP_LIMITED_GREEDY = 0
 MOE_NOAUX_TC = 1
@@ -61,6 +61,11 @@ SIGNATURES = {
     "moe_ffn_down": (_st, [_st, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
                            _vp]),
     "moe_combine": (_st, [_st, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_route_backward": (_st, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "moe_expert_ffn_backward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn_backward": (_st, [_st, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                      _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                      _vp]),
 }
 
 _lib = None

@@ -31,7 +31,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS
 
-SOURCES = ["capi.hip", "route.hip", "route_grouped.hip", "router.hip", "align.hip", "multihot.hip", "combine.hip", "ffn_f32.hip",
+SOURCES = ["capi.hip", "route.hip", "route_grouped.hip", "router.hip", "align.hip", "multihot.hip", "combine.hip", "ffn_f32.hip", "backward.hip",
            "gemm_bf16.hip", "decode.hip"]
 
 

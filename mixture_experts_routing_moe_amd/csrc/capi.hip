@@ -448,4 +448,70 @@ moe_status_t moe_expert_ffn_decode(moe_dtype_t dt, const void *hidden, const voi
                            "moe_expert_ffn_decode");
 }
 
+moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
+                                const float *topk_w, const float *grad_topk_w, int64_t T,
+                                int32_t E, int32_t k, int32_t norm_topk_prob,
+                                float *grad_logits, void *stream) {
+    const char *fn = "moe_route_backward";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
+    if (T == 0) return MOE_OK;
+    CHECK(logits && topk_ids && topk_w && grad_topk_w && grad_logits, MOE_ERR_INVALID_ARG,
+          "%s: null pointer", fn);
+    return hip_status(moe::launch_route_backward(logits, topk_ids, topk_w, grad_topk_w, T, E, k,
+                                                 norm_topk_prob ? 1 : 0, grad_logits,
+                                                 static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+size_t moe_expert_ffn_backward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
+                                              int32_t k) {
+    (void)E;
+    if (T <= 0 || H < 1 || I < 1 || k < 1) return 0;
+    return moe::ffn_backward_scratch_bytes(T, H, I, k);
+}
+
+moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const void *w13,
+                                     const void *w2, const float *topk_w,
+                                     const int32_t *expert_offsets,
+                                     const int32_t *sorted_token_ids,
+                                     const int32_t *sorted_slot_ids,
+                                     const int32_t *slot_to_sorted, const void *grad_out,
+                                     int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                     float *grad_hidden, float *grad_w13, float *grad_w2,
+                                     float *grad_topk_w, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    const char *fn = "moe_expert_ffn_backward";
+    moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: only the bfloat16 path has a backward", fn);
+    if (T == 0) return MOE_OK;
+    CHECK(hidden && w13 && w2 && topk_w && expert_offsets && sorted_token_ids &&
+              sorted_slot_ids && slot_to_sorted && grad_out && grad_hidden && grad_w13 &&
+              grad_w2 && grad_topk_w,
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(grad_out) &&
+              aligned16(grad_hidden) && aligned16(grad_w13) && aligned16(grad_w2),
+          MOE_ERR_INVALID_ARG, "%s: hidden, weights, gradients must be 16-byte aligned", fn);
+    const size_t need = moe::ffn_backward_scratch_bytes(T, H, I, k);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
+          fn);
+    // Grid limits of the grouped products: one block row per 128 positions
+    // plus one per expert; 128-column tiles of at most 2I columns.
+    CHECK(T * (int64_t)k / 128 + E < (int64_t)1 << 31 && 2 * (int64_t)I / 128 < 65535 &&
+              (int64_t)H / 128 < 65535 && (2 * (int64_t)I / 128 + 1) * ((int64_t)H / 128 + 1) < (int64_t)1 << 31,
+          MOE_ERR_UNSUPPORTED, "%s: shape exceeds the launch grid", fn);
+    return hip_status(moe::launch_ffn_backward_bf16(
+                          static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(w13),
+                          static_cast<const uint16_t *>(w2), topk_w, expert_offsets,
+                          sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                          static_cast<const uint16_t *>(grad_out), T, H, I, E, k, grad_hidden,
+                          grad_w13, grad_w2, grad_topk_w, workspace,
+                          static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 }  // extern "C"

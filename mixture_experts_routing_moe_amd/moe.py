@@ -373,3 +373,50 @@ def moe_layer(hidden, w13, w2, logits, k: int, norm_topk_prob: bool = True,
         decode = hidden.dtype == torch.bfloat16 and hidden.shape[0] <= _lib.MOE_DECODE_MAX_T
     out = moe_expert_ffn(hidden, w13, w2, topk_w, aligned, decode=decode)
     return out, topk_w, topk_ids, aligned
+
+
+def moe_route_backward(logits, topk_ids, topk_w, grad_topk_w, norm_topk_prob: bool = True,
+                       grad_logits=None):
+    """Gradient of moe_route's weights w.r.t. the logits -> grad_logits [T, E] float32."""
+    T, E = logits.shape
+    k = topk_ids.shape[1]
+    if grad_logits is None:
+        grad_logits = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    _dev(logits, topk_ids, topk_w, grad_topk_w, grad_logits)
+    check(lib().moe_route_backward(_ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(grad_topk_w), T, E, k, int(bool(norm_topk_prob)),
+                                   _ptr(grad_logits), _stream()), "moe_route_backward")
+    return grad_logits
+
+
+def moe_expert_ffn_backward_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_expert_ffn_backward_workspace_size(T, H, I, E, k))
+
+
+def moe_expert_ffn_backward(hidden, w13, w2, topk_w, aligned: dict, grad_out, out=None,
+                            workspace=None):
+    """Backward of moe_expert_ffn (bf16) -> dict of float32 grad_hidden [T, H],
+    grad_w13 [E, 2I, H], grad_w2 [E, H, I], grad_topk_w [T, k]."""
+    T, H, I, E = _ffn_shapes(hidden, w13, w2)
+    k = topk_w.shape[1]
+    dev = hidden.device
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = {"grad_hidden": torch.empty((T, H), **f32),
+               "grad_w13": torch.empty((E, 2 * I, H), **f32),
+               "grad_w2": torch.empty((E, H, I), **f32),
+               "grad_topk_w": torch.empty((T, k), **f32)}
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_expert_ffn_backward_workspace_size(T, H, I, E, k)),
+                                dtype=torch.uint8, device=dev)
+    _dev(hidden, w13, w2, topk_w, grad_out, workspace, aligned["offsets"],
+         aligned["sorted_token_ids"], aligned["sorted_slot_ids"], aligned["slot_to_sorted"],
+         *out.values())
+    check(lib().moe_expert_ffn_backward(
+        _dtype_code(hidden), _ptr(hidden), _ptr(w13), _ptr(w2), _ptr(topk_w),
+        _ptr(aligned["offsets"]), _ptr(aligned["sorted_token_ids"]),
+        _ptr(aligned["sorted_slot_ids"]), _ptr(aligned["slot_to_sorted"]), _ptr(grad_out),
+        T, H, I, E, k, _ptr(out["grad_hidden"]), _ptr(out["grad_w13"]), _ptr(out["grad_w2"]),
+        _ptr(out["grad_topk_w"]), _ptr(workspace), workspace.numel(), _stream()),
+        "moe_expert_ffn_backward")
+    return out

@@ -43,7 +43,7 @@ import numpy as np
 
 CHUNK = 1 << 22  # elements per independently seeded chunk
 
-S_LOGITS, S_HIDDEN, S_W13, S_W2, S_BIAS, S_RANK, S_WGATE = range(7)
+S_LOGITS, S_HIDDEN, S_W13, S_W2, S_BIAS, S_RANK, S_WGATE, S_GRAD = range(8)
 
 
 @dataclass(frozen=True)
@@ -263,3 +263,12 @@ def correction_bias(w: GroupedWorkload) -> np.ndarray | None:
 def router_weights(w: Workload) -> np.ndarray:
     """The linear gate w_gate [E, H] (bf16 bits, N(0, 1/H)) for a layer workload."""
     return normal_bf16(w.wid, S_WGATE, w.E * w.H, 1 / math.sqrt(w.H)).reshape(w.E, w.H)
+
+
+def grad_output(w: Workload, T: int | None = None) -> np.ndarray:
+    """Gradient of the layer output for backward runs: [T, H] N(0, 1) in the layer dtype
+    (bf16 as uint16 bits)."""
+    T = w.T if T is None else T
+    if w.dtype == "f32":
+        return normal_f32(w.wid, S_GRAD, T * w.H, 1.0).reshape(T, w.H)
+    return normal_bf16(w.wid, S_GRAD, T * w.H, 1.0).reshape(T, w.H)

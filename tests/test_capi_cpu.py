@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_version() == 5
+    assert lib.moe_version() == 6
     for s in range(5):
         assert lib.moe_status_string(s)
     assert lib.moe_status_string(99) == b"unknown status"
@@ -282,3 +282,42 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_route_backward_validation(lib):
+    I = _lib.MOE_ERR_INVALID_ARG
+
+    def rb(T=4, E=8, k=2, lg=FAKE, ids=FAKE, w=FAKE, g=FAKE, out=FAKE):
+        return lib.moe_route_backward(lg, ids, w, g, T, E, k, 1, out, None)
+
+    assert rb(k=9) == I  # k > E
+    assert rb(E=0) == I
+    assert rb(T=-1) == I
+    assert rb(out=None) == I
+    assert rb(g=None) == I
+    assert rb(T=0, lg=None, ids=None, w=None, g=None, out=None) == _lib.MOE_OK
+
+
+def test_ffn_backward_validation(lib):
+    I, U, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+    B = _lib.MOE_BF16
+    T, H, Im, E, k = 100, 128, 192, 8, 2
+    need = lib.moe_expert_ffn_backward_workspace_size(T, H, Im, E, k)
+    assert need >= T * k * (18 * Im + 4 * H)
+    assert lib.moe_expert_ffn_backward_workspace_size(0, H, Im, E, k) == 0
+
+    def fb(dt=B, T=T, H=H, I=Im, E=E, k=k, x=FAKE, dx=FAKE, ws=FAKE, wsb=need):
+        return lib.moe_expert_ffn_backward(dt, x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           T, H, I, E, k, dx, FAKE, FAKE, FAKE, ws, wsb, None)
+
+    assert fb(dt=_lib.MOE_F32) == U  # bf16 only
+    assert b"bfloat16" in lib.moe_last_error()
+    assert fb(H=96) == U  # H % 64
+    assert fb(I=100) == U
+    assert fb(k=65) == I  # k > MOE_MAX_TOPK
+    assert fb(x=None) == I
+    assert fb(dx=None) == I
+    assert fb(x=ctypes.c_void_p(0x1008)) == I  # not 16-byte aligned
+    assert fb(wsb=need - 1) == W
+    assert fb(ws=None) == W
+    assert fb(T=0, x=None, dx=None, ws=None, wsb=0) == _lib.MOE_OK

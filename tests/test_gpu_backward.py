@@ -1,0 +1,156 @@
+"""GPU parity of the backward calls against the CPU oracle (through the C ABI).
+
+Tolerances (derived from the arithmetic): the bf16 backward rounds exactly one
+operand of each bf16 product to bfloat16 (w act for the w2 gradient,
+d_gate/d_up for the w13 and hidden gradients; grad_out, hidden and the weights
+are exact bf16 inputs) and accumulates in float32.  That rounding moves each
+product term by at most u = 2^-9 relative, which gives an error RMS of about
+1.7e-3 of the output's RMS and a largest error near u x the largest output
+(a normwise bound: elements whose terms cancel can carry several percent of
+the RMS, so no element-wise bound at the RMS scale holds).  Each gradient
+must satisfy
+    RMS(error) <= 4e-3 x RMS(oracle)   and   max |error| <= 4u x max |oracle|.
+grad_topk_w = <G, act> is formed from exact inputs with float32 sums:
+max |error| <= 1e-4 x max |oracle|.  The gating backward is float32
+throughout: max |error| <= 1e-5 x max |oracle|.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+
+import mixture_experts_routing_moe_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+RMS_TOL = 4e-3
+MAX_TOL = 4 * 2.0 ** -9
+TOPKW_TOL = 1e-4
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def check_grad(name, got, ref, max_tol=MAX_TOL, rms_tol=RMS_TOL):
+    """max |err| <= max_tol x max |ref| and RMS(err) <= rms_tol x RMS(ref)."""
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), name
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = got - ref
+    emax = float(np.abs(err).max()) / float(np.abs(ref).max())
+    erms = math.sqrt(float(np.mean(err ** 2))) / rms
+    assert emax <= max_tol and erms <= rms_tol, \
+        f"{name}: max err {emax:.3e} x max|ref|, rms err {erms:.3e} x RMS"
+    return emax, erms
+
+
+# --------------------------------------------------------------------------
+# Gating softmax backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1000, 64, 8), (37, 8, 2), (5, 130, 6), (16, 256, 8),
+                                   (3, 1024, 64), (2, 1, 1), (64, 70, 64)])
+@pytest.mark.parametrize("norm", [True, False])
+def test_route_backward(T, E, k, norm):
+    g = np.random.Generator(np.random.PCG64(T * 7 + E + k))
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    gw = g.standard_normal((T, k)).astype(np.float32)
+    ld = dev(logits)
+    tw, tids = moe.moe_route(ld, k, norm)
+    ow, oids = oracle.route(logits, k, norm)
+    np.testing.assert_array_equal(tids.cpu().numpy(), oids)
+    got = moe.moe_route_backward(ld, tids, tw, dev(gw), norm).cpu().numpy().astype(np.float64)
+    ref = oracle.route_backward(logits, oids, gw.astype(np.float64), norm)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    assert np.abs(got - ref).max() <= 1e-5 * scale
+    if norm:  # unselected experts get exactly zero
+        sel = np.zeros((T, E), bool)
+        np.put_along_axis(sel, oids, True, axis=1)
+        assert np.all(got[~sel] == 0)
+
+
+def test_route_backward_empty():
+    z = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    zi = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    zw = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    out = moe.moe_route_backward(z, zi, zw, zw, True)
+    assert out.shape == (0, 8)
+
+
+# --------------------------------------------------------------------------
+# Expert FFN backward
+# --------------------------------------------------------------------------
+
+def _rand_case(seed, T, H, I, E, k, skew=0.0, inv=0.0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    w13 = mi.f32_to_bf16_bits((g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32))
+    w2 = mi.f32_to_bf16_bits((g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32))
+    dy = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    logits += (skew * np.arange(E, dtype=np.float32))[None, :]
+    w, ids = oracle.route(logits, k, True)
+    if inv > 0:
+        ids = np.where(g.random(ids.shape) < inv, -1, ids).astype(np.int32)
+    return x, w13, w2, w.astype(np.float32), ids, dy
+
+
+def _bwd_gpu(x, w13, w2, w32, ids, dy):
+    E = w13.shape[0]
+    a = moe.moe_align(dev(ids), E)
+    out = moe.moe_expert_ffn_backward(dev_bf16(x), dev_bf16(w13), dev_bf16(w2), dev(w32), a,
+                                      dev_bf16(dy))
+    return {n: t.cpu().numpy() for n, t in out.items()}
+
+
+@pytest.mark.parametrize("T,H,I,E,k,skew,inv", [
+    (300, 128, 192, 8, 2, 0.0, 0.0),
+    (200, 256, 64, 5, 3, 0.0, 0.0),
+    (77, 64, 64, 3, 3, 0.0, 0.0),
+    (513, 192, 320, 16, 4, 0.5, 0.0),   # skew: experts with no row
+    (260, 128, 128, 12, 3, 0.0, 0.2),   # dropped slots (id -1)
+    (1, 128, 128, 8, 2, 0.0, 0.0),
+    (400, 64, 256, 2, 1, 2.0, 0.0),
+])
+def test_ffn_backward(T, H, I, E, k, skew, inv):
+    x, w13, w2, w32, ids, dy = _rand_case(T + H + I + E, T, H, I, E, k, skew, inv)
+    got = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    ref = oracle.expert_ffn_backward(x, w13, w2, w32.astype(np.float64), ids, dy, "bf16",
+                                     weights=True)
+    for name in ("grad_hidden", "grad_w13", "grad_w2"):
+        check_grad(name, got[name], ref[name])
+    check_grad("grad_topk_w", got["grad_topk_w"], ref["grad_topk_w"], TOPKW_TOL, TOPKW_TOL)
+    # Slots with an invalid id get exactly 0; experts no slot names get zero gradients.
+    assert np.all(got["grad_topk_w"][ids < 0] == 0)
+    used = np.zeros(E, bool)
+    used[ids[ids >= 0]] = True
+    assert np.all(got["grad_w13"][~used] == 0) and np.all(got["grad_w2"][~used] == 0)
+
+
+def test_ffn_backward_deterministic():
+    x, w13, w2, w32, ids, dy = _rand_case(5, 300, 128, 192, 8, 2)
+    a = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    b = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    for name in a:
+        np.testing.assert_array_equal(a[name], b[name])
+
+
+def test_ffn_backward_empty():
+    E, H, I = 4, 64, 64
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    w13 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=DEV)
+    w2 = torch.zeros((E, H, I), dtype=torch.bfloat16, device=DEV)
+    tw = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    a = moe.moe_align(torch.empty((0, 2), dtype=torch.int32, device=DEV), E)
+    out = moe.moe_expert_ffn_backward(x, w13, w2, tw, a, x)
+    assert out["grad_hidden"].shape == (0, H)
