@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--workload", default="mixtral",
                    choices=["mixtral", "finegrained", "decode1", "decode32", "routing",
                             "grouped_noaux", "grouped_greedy", "router_finegrained",
-                            "router_mixtral"])
+                            "router_mixtral", "backward_mixtral", "backward_finegrained"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", type=int, default=None,
                    help="1: time the whole step as one captured HIP graph replay (the "
@@ -197,6 +197,112 @@ def bench_router(args, w, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(args, w, dev):
+    """Layer backward on a layer workload: moe_expert_ffn_backward (gradients of
+    hidden, w13, w2 and the routing weights) then moe_route_backward (the
+    logits' gradient), from the saved forward routing and a seeded grad_out.
+    MFMA roofline over the five grouped products of the FFN backward."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_moe_amd as moe
+    import moe_inputs as mi
+
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+    inp = mi.layer_inputs(w)
+    gout = mi.grad_output(w)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w13, w2, dy = bf(inp["hidden"]), bf(inp["w13"]), bf(inp["w2"]), bf(gout)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    # The forward's routing and alignment, saved (outside the timed steps).
+    topk_w, topk_ids = moe.moe_route(logits, k, w.norm)
+    aligned = moe.moe_align(topk_ids, E)
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = {"grad_hidden": torch.empty((T, H), **f32),
+             "grad_w13": torch.empty((E, 2 * I, H), **f32),
+             "grad_w2": torch.empty((E, H, I), **f32),
+             "grad_topk_w": torch.empty((T, k), **f32)}
+    grad_logits = torch.empty((T, E), **f32)
+    ws = torch.empty(moe.moe_expert_ffn_backward_workspace_size(T, H, I, E, k),
+                     dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        moe.moe_expert_ffn_backward(x, w13, w2, topk_w, aligned, dy, grads, ws)
+        if ev:
+            ev[1].record()
+        moe.moe_route_backward(logits, topk_ids, topk_w, grads["grad_topk_w"], w.norm,
+                               grad_logits)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step(ev[st])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ffn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    route_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms = sum(e[0].elapsed_time(e[2]) for e in ev) / args.steps
+    P = T * k
+    flops = 16.0 * P * H * I  # gate/up recompute 4PHI, G 2PHI, dx 4PHI, dw2 2PHI, dw13 4PHI
+    achieved = flops / (ffn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(T * 1e3 / ms, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators, random-init weights)",
+        "config": {"workload": f"backward_{w.name}", "T": T, "H": H, "I": I, "E": E,
+                   "top_k": k, "norm_topk_prob": w.norm, "step_timing": "eager",
+                   "wall_ms_per_step": round(wall_ms, 4),
+                   "backward_tflop_per_step": round(flops / 1e12, 3)},
+        "roofline": {"kernel": "moe_expert_ffn_backward (5 grouped bf16 GEMMs + 2 row kernels)",
+                     "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "phase_ms": {"ffn_backward": round(ffn_ms, 4), "route_backward": round(route_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_backward(w, inp, gout)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_backward(w, inp, gout, budget_s=(10.0, 30.0)):
+    """The oracle's layer backward (route, FFN backward with weight gradients,
+    gating backward; float64) on a growing prefix of the tokens.  With weight
+    gradients the oracle visits tokens one after another on one thread."""
+    import numpy as np
+
+    import oracle
+
+    def run(n):
+        t0 = time.perf_counter()
+        tw, ids = oracle.route(inp["logits"][:n], w.k, w.norm)
+        g = oracle.expert_ffn_backward(inp["hidden"][:n], inp["w13"], inp["w2"], tw, ids,
+                                       gout[:n], "bf16", weights=True)
+        oracle.route_backward(inp["logits"][:n], ids, g["grad_topk_w"], w.norm)
+        return time.perf_counter() - t0
+
+    n, spent = 1, 0.0
+    while True:
+        dt = run(n)
+        spent += dt
+        if dt >= budget_s[0] or n >= w.T or spent >= budget_s[1]:
+            break
+        n = min(w.T, n * min(8, max(2, int(budget_s[0] / max(dt, 1e-3)))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens: route + expert FFN backward with weight "
+                      f"gradients + gating backward in float64, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -222,16 +328,19 @@ def main():
 
     grouped = args.workload in mi.GROUPED
     router = args.workload.startswith("router_")
+    backward = args.workload.startswith("backward_")
     if grouped:
         w = mi.GROUPED[args.workload]
-    elif router:
-        w = mi.WORKLOADS[args.workload[len("router_"):]]
+    elif router or backward:
+        w = mi.WORKLOADS[args.workload.split("_", 1)[1]]
     else:
         w = mi.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if router:
         return bench_router(args, w, dev)
+    if backward:
+        return bench_backward(args, w, dev)
     if grouped:
         # Group-limited routing: [T, E] scores and (noaux_tc) the correction bias.
         inp = {"logits": mi.grouped_scores(w), "bias": mi.correction_bias(w)}

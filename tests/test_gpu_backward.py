@@ -154,3 +154,64 @@ def test_ffn_backward_empty():
     a = moe.moe_align(torch.empty((0, 2), dtype=torch.int32, device=DEV), E)
     out = moe.moe_expert_ffn_backward(x, w13, w2, tw, a, x)
     assert out["grad_hidden"].shape == (0, H)
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, in the configuration bench.py times (backward_<name>):
+# sampled tokens, sampled weight-gradient rows and columns, plus properties of
+# every element.
+# --------------------------------------------------------------------------
+
+def _sample(T, ids, E, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    toks = set(g.choice(T, size=6, replace=False).tolist()) | {0, T - 1}
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    used = np.nonzero(counts)[0]
+    # the most and the least loaded experts that have rows, and two random ones
+    picks = {int(used[np.argmax(counts[used])]), int(used[np.argmin(counts[used])])}
+    picks |= set(int(e) for e in g.choice(used, size=min(2, len(used)), replace=False))
+    return np.array(sorted(toks), np.int64), sorted(picks), counts
+
+
+@pytest.mark.parametrize("name", ["mixtral", "finegrained"])
+def test_backward_full_size(name):
+    w = mi.WORKLOADS[name]
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+    inp = mi.layer_inputs(w)
+    gout = mi.grad_output(w)
+    ld = dev(inp["logits"])
+    tw, tids = moe.moe_route(ld, k, w.norm)
+    ow, oids = oracle.route(inp["logits"], k, w.norm)
+    np.testing.assert_array_equal(tids.cpu().numpy(), oids)
+    a = moe.moe_align(tids, E)
+    g = moe.moe_expert_ffn_backward(dev_bf16(inp["hidden"]), dev_bf16(inp["w13"]),
+                                    dev_bf16(inp["w2"]), tw, a, dev_bf16(gout))
+    gl = moe.moe_route_backward(ld, tids, tw, g["grad_topk_w"], w.norm)
+    toks, experts, counts = _sample(T, oids, E, T + E)
+    # Every element finite; experts no slot names get exactly zero gradients.
+    for n in ("grad_hidden", "grad_topk_w"):
+        assert bool(torch.isfinite(g[n]).all()), n
+    unused = torch.from_numpy(counts == 0).to(DEV)
+    for n in ("grad_w13", "grad_w2"):
+        assert bool(torch.isfinite(g[n]).all()), n
+        if bool(unused.any()):
+            assert bool((g[n][unused] == 0).all()), n
+    assert bool(torch.isfinite(gl).all())
+
+    ref = oracle.expert_ffn_backward(inp["hidden"], inp["w13"], inp["w2"], ow, oids, gout,
+                                     "bf16", tokens=toks)
+    check_grad("grad_hidden", g["grad_hidden"][toks].cpu().numpy(), ref["grad_hidden"])
+    check_grad("grad_topk_w", g["grad_topk_w"][toks].cpu().numpy(), ref["grad_topk_w"],
+               TOPKW_TOL, TOPKW_TOL)
+    rows13 = [(e, c) for e in experts for c in (0, I - 1, I, 2 * I - 1, I // 3)]
+    cols2 = [(e, i) for e in experts for i in (0, I - 1, I // 2)]
+    r13, c2 = oracle.expert_wgrad_entries(inp["hidden"], inp["w13"], inp["w2"], ow, oids, gout,
+                                          "bf16", rows13, cols2)
+    got13 = np.stack([g["grad_w13"][e, c].cpu().numpy() for e, c in rows13])
+    got2 = np.stack([g["grad_w2"][e, :, i].cpu().numpy() for e, i in cols2])
+    check_grad("grad_w13 rows", got13, r13)
+    check_grad("grad_w2 columns", got2, c2)
+    # The gating backward on the sampled rows, from the oracle's own weight gradient.
+    rl = oracle.route_backward(inp["logits"][toks], oids[toks], ref["grad_topk_w"], w.norm)
+    gl_s = gl[torch.from_numpy(toks).to(DEV)].cpu().numpy().astype(np.float64)
+    assert np.abs(gl_s - rl).max() <= 1e-3 * np.abs(rl).max()
