@@ -358,7 +358,9 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
  * slot names gets zero weight gradients (every element of every output is
  * written).  gate/up are recomputed (one grouped product); w act and
  * d_gate/d_up are rounded to bfloat16 as the inputs of the bf16 products,
- * everything else accumulates in float32.  Results are deterministic.
+ * everything else accumulates in float32.  Results are deterministic.  The
+ * call writes w13 and w2 transposed per expert into the workspace (weights
+ * change between training steps, so nothing is cached).
  *
  * dt must be MOE_BF16.  hidden [T, H], w13 [E, 2I, H], w2 [E, H, I],
  * grad_out [T, H] bfloat16; topk_w [T, k] float32; expert_offsets [E+1],
@@ -366,7 +368,7 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
  * moe_align for the forward's ids.  Outputs float32: grad_hidden [T, H],
  * grad_w13 [E, 2I, H], grad_w2 [E, H, I], grad_topk_w [T, k].
  * workspace >= moe_expert_ffn_backward_workspace_size(T, H, I, E, k) bytes
- * (T*k*(18 I + 4 H) bytes, rounded), 16-byte aligned, clobbered.
+ * (about T*k*(24 I + 12 H) + 6 E H I), 16-byte aligned, clobbered.
  * Requires H % 64 == 0, I % 64 == 0; hidden, weights, grad_out and the
  * gradients 16-byte aligned.  T = 0 enqueues nothing, as for every call, so
  * the weight gradients are then left as they were.

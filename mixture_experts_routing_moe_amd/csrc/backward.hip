@@ -11,173 +11,69 @@
 //   grad_w2[e]  = sum over slots of dy^T (w act)
 //   grad_w13[e] = sum over slots of [d_gate ; d_up]^T x
 //
-// The products are grouped GEMMs over the aligned (expert-major) slot order.
-// One kernel serves them all: C[m, n] = sum_k A(m, k) B(n, k) on the bf16
-// matrix cores (MFMA 16x16x32, float32 accumulation), 128 x 128 tiles, 4
-// waves of 64 x 64.  Operands are either stored with k contiguous (a row per
-// m or n, optionally gathered through sorted_token_ids) or with k as the row
-// index (m or n contiguous); the second kind is transposed on its way into
-// LDS, so fragment reads are the same for both.  The expert segments lie
-// either on the M side (the dgrad-style products: rows of one expert against
-// that expert's weight matrix) or on the K side (the weight gradients: a
-// ragged sum over the expert's rows; an expert with no row gets zeros).
-//
-// This is a plain, single-buffered tiling (register prefetch of the next
-// k-tile, two barriers per k-tile), not the forward GEMM's tuned pipeline.
+// Layout for the matrix cores.  Every product is arranged so that both of its
+// operands are stored with the contracted index contiguous ("NT"), which is
+// what the MFMA fragments read:
+// * The three row-segment products (gate/up recomputed = x . w13^T,
+//   G = dy . w2, d_hidden = [d_gate ; d_up] . w13) run on the forward's tuned
+//   grouped kernel (the FC2 variant: A rows in the aligned order, one weight
+//   matrix per expert, float32 out).  Its A rows are the tokens' rows gathered
+//   into the aligned order, and its weights for G and d_hidden are w2 and w13
+//   transposed per expert ([E, I, H] and [E, H, 2I], written each call).
+// * The two weight gradients contract over each expert's rows.  Their
+//   operands (dy, x, w act, [d_gate ; d_up]) are transposed into [columns,
+//   positions] with every expert's segment padded to a multiple of 32
+//   positions (zeros in the padding), so the k loop of a segment runs over
+//   whole, aligned 32-wide tiles; one block computes a 128 x 128 tile of one
+//   expert's gradient (zero for an expert with no rows).
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kBT = 256;          // threads per GEMM block: 4 waves in 2 x 2
-constexpr int kBM = 128;          // tile rows (m)
-constexpr int kBN = 128;          // tile columns (n)
+constexpr int kSegPad = 32;       // positions per padded segment unit
+constexpr int kBT = 256;          // threads per wgrad block: 4 waves in 2 x 2
+constexpr int kBM = 128;          // wgrad tile rows (m)
+constexpr int kBN = 128;          // wgrad tile columns (n)
 constexpr int kBK = 32;           // k per LDS tile (one MFMA k-step)
 constexpr int kLdsW = kBK + 8;    // bf16 per LDS row: 80 bytes, 16-byte aligned rows
 
-struct BwdGemm {
-    const uint16_t *A;
-    int64_t lda;
-    const int32_t *a_gather;  // A row (M-segment mode) or k row (K-segment) of position p
-    const uint16_t *B;
-    int64_t ldb;
-    int64_t b_estride;        // M-segment mode: expert e's B starts at B + e * b_estride
-    const int32_t *b_gather;  // K-segment mode: B row of position p is b_gather[p]
-    float *C;
-    int64_t ldc;
-    int64_t c_estride;        // K-segment mode: expert e's C starts at C + e * c_estride
-    const int32_t *offsets;   // [E + 1] aligned segment offsets
-    int E, M, N, K;
-    int n_tiles;
-};
-
-// Block s of the M-segment grid -> expert e and its rows [row0, min(row0 +
-// kBM, row_end)).  Expert e owns ceil(count_e / kBM) consecutive blocks; a
-// running sum over the experts (64 per pass, one per lane) finds the owner.
-// Every wave computes the same answer.
-__device__ bool find_mslot(const int32_t *__restrict__ off, int E, int s, int &e_out, int &row0,
-                           int &row_end) {
-    const int lane = lane_id();
-    int carry = 0;
-    for (int c = 0; c < E; c += kWave) {
-        const int e = c + lane;
-        int o = 0, cnt = 0;
-        if (e < E) {
-            o = off[e];
-            cnt = off[e + 1] - o;
-        }
-        const int mt = (cnt + kBM - 1) / kBM;
-        int incl = mt;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        const int lo = carry + incl - mt;
-        const uint64_t b = __ballot(e < E && s >= lo && s < carry + incl);
-        if (b) {
-            const int l = __builtin_ctzll(b);
-            const int lo_l = __shfl(lo, l);
-            const int o_l = __shfl(o, l);
-            const int cnt_l = __shfl(cnt, l);
-            e_out = c + l;
-            row0 = o_l + (s - lo_l) * kBM;
-            row_end = o_l + cnt_l;
-            return true;
-        }
-        carry += __shfl(incl, kWave - 1);
-    }
-    return false;
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, to_bf16(f));
 }
 
-__device__ __forceinline__ uint16_t elem16(const uint4 &v, int j) {
-    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-    return (uint16_t)(w >> (16 * (j & 1)));
-}
-
-// Tile of one operand: kBM (or kBN) rows x kBK k values into LDS row-major
-// [row][k].  Two 16-byte chunks per thread.
-//   KC (k contiguous):  chunk c = row (c / 4), k-group (c % 4).
-//   otherwise (k rows): chunk c = k row (c / 16), 8 consecutive rows (c % 16)
-//                       of the tile, written transposed.
-template <bool KC>
-__device__ __forceinline__ void lds_store(uint16_t *s, const uint4 (&r)[2]) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = threadIdx.x + kBT * q;
-        if (KC) {
-            *reinterpret_cast<uint4 *>(s + (c >> 2) * kLdsW + 8 * (c & 3)) = r[q];
-        } else {
-            const int kr = c >> 4, x0 = 8 * (c & 15);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s[(x0 + j) * kLdsW + kr] = elem16(r[q], j);
-        }
-    }
-}
-
-template <bool KSEG, bool BKM>
-__global__ __launch_bounds__(kBT) void bwd_gemm_kernel(BwdGemm g) {
+// Weight gradient of one expert, C_e[m, n] = sum over k in the expert's padded
+// segment [poff[e], poff[e+1]) of A[m, k] B[n, k]; A [M, ld] and B [N, ld] bf16
+// with k contiguous, C_e float32 [M, N] at C + e M N.  Block (tile, e): a
+// 128 x 128 tile, 4 waves of 64 x 64 = 4 x 4 MFMA 16x16x32 fragments; the next
+// k-tile is loaded into registers while the current one is multiplied.
+__global__ __launch_bounds__(kBT) void wgrad_kernel(const uint16_t *__restrict__ A,
+                                                    const uint16_t *__restrict__ B, int64_t ld,
+                                                    const int32_t *__restrict__ poff, int M,
+                                                    int N, int n_tiles, float *__restrict__ C) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[kBM * kLdsW];
     __shared__ __attribute__((aligned(16))) uint16_t sB[kBN * kLdsW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int e = blockIdx.y;
+    const int m0 = (int)(blockIdx.x / n_tiles) * kBM;
+    const int n0 = (int)(blockIdx.x % n_tiles) * kBN;
+    const int k0 = poff[e], k_end = poff[e + 1];
+    float *Ce = C + (int64_t)e * M * N;
 
-    int e, m0, m_end, k0, k_end, n0;
-    const uint16_t *Bb;
-    float *Cb;
-    if (KSEG) {
-        e = blockIdx.y;
-        m0 = (int)(blockIdx.x / g.n_tiles) * kBM;
-        n0 = (int)(blockIdx.x % g.n_tiles) * kBN;
-        m_end = g.M;
-        k0 = g.offsets[e];
-        k_end = g.offsets[e + 1];
-        Bb = g.B;
-        Cb = g.C + (int64_t)e * g.c_estride;
-    } else {
-        n0 = blockIdx.y * kBN;
-        if (!find_mslot(g.offsets, g.E, blockIdx.x, e, m0, m_end)) return;  // uniform
-        k0 = 0;
-        k_end = g.K;
-        Bb = g.B + (int64_t)e * g.b_estride;
-        Cb = g.C;
-    }
-
+    // Chunk c (two per thread) = row c / 4 of the tile, k-group c % 4.
     uint4 ra[2], rb[2];
     auto load = [&](int kt) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = tid + kBT * q;
+            const int r = c >> 2, kc = 8 * (c & 3);
             ra[q] = uint4{0, 0, 0, 0};
             rb[q] = uint4{0, 0, 0, 0};
-            if (!KSEG) {  // A: rows of the segment, k contiguous
-                const int p = m0 + (c >> 2);
-                if (p < m_end) {
-                    const int64_t row = g.a_gather ? g.a_gather[p] : p;
-                    ra[q] = *reinterpret_cast<const uint4 *>(g.A + row * g.lda + kt + 8 * (c & 3));
-                }
-            } else {  // A: k rows (positions of the segment), m contiguous
-                const int p = kt + (c >> 4);
-                const int m = m0 + 8 * (c & 15);
-                if (p < k_end && m < g.M) {
-                    const int64_t row = g.a_gather ? g.a_gather[p] : p;
-                    ra[q] = *reinterpret_cast<const uint4 *>(g.A + row * g.lda + m);
-                }
-            }
-            if (!BKM) {  // B: rows n, k contiguous
-                const int n = n0 + (c >> 2);
-                if (n < g.N)
-                    rb[q] = *reinterpret_cast<const uint4 *>(Bb + (int64_t)n * g.ldb + kt + 8 * (c & 3));
-            } else {  // B: k rows, n contiguous
-                const int p = kt + (c >> 4);
-                const int n = n0 + 8 * (c & 15);
-                if (p < k_end && n < g.N) {
-                    const int64_t row = (KSEG && g.b_gather) ? g.b_gather[p] : p;
-                    rb[q] = *reinterpret_cast<const uint4 *>(Bb + row * g.ldb + n);
-                }
-            }
+            if (m0 + r < M) ra[q] = *reinterpret_cast<const uint4 *>(A + (int64_t)(m0 + r) * ld + kt + kc);
+            if (n0 + r < N) rb[q] = *reinterpret_cast<const uint4 *>(B + (int64_t)(n0 + r) * ld + kt + kc);
         }
     };
 
@@ -191,8 +87,12 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(BwdGemm g) {
     if (k0 < k_end) load(k0);
     for (int kt = k0; kt < k_end; kt += kBK) {
         __syncthreads();  // the previous tile's fragment reads are done
-        lds_store<!KSEG>(sA, ra);
-        lds_store<!BKM>(sB, rb);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = tid + kBT * q;
+            *reinterpret_cast<uint4 *>(sA + (c >> 2) * kLdsW + 8 * (c & 3)) = ra[q];
+            *reinterpret_cast<uint4 *>(sB + (c >> 2) * kLdsW + 8 * (c & 3)) = rb[q];
+        }
         __syncthreads();
         if (kt + kBK < k_end) load(kt + kBK);
         bf16x8 af[4], bf[4];
@@ -217,13 +117,101 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + a * 16 + 4 * kq + r;
-                if (m < m_end && n < g.N) Cb[(int64_t)m * g.ldc + n] = acc[a][b][r];
+                if (m < M && n < N) Ce[(int64_t)m * N + n] = acc[a][b][r];
             }
         }
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    return __builtin_bit_cast(uint16_t, to_bf16(f));
+// dst[p] = src[tok[p]] (rows of L bf16) for every aligned position p, for
+// two sources at once (x and grad_out).  One block per position.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ dy,
+                                                          const int32_t *__restrict__ tok,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int E, int L, uint16_t *__restrict__ xs,
+                                                          uint16_t *__restrict__ dys) {
+    const int p = blockIdx.x;
+    if (p >= offsets[E]) return;
+    const int64_t t = tok[p];
+    for (int c = threadIdx.x; c < L / 8; c += blockDim.x) {
+        *reinterpret_cast<uint4 *>(xs + (int64_t)p * L + 8 * c) =
+            *reinterpret_cast<const uint4 *>(x + t * L + 8 * c);
+        *reinterpret_cast<uint4 *>(dys + (int64_t)p * L + 8 * c) =
+            *reinterpret_cast<const uint4 *>(dy + t * L + 8 * c);
+    }
+}
+
+// Padded segment offsets: poff[0] = 0, poff[e+1] = poff[e] + count_e rounded
+// up to kSegPad.  One thread (E <= 1024).
+__global__ void seg_offsets_kernel(const int32_t *__restrict__ offsets, int E,
+                                   int32_t *__restrict__ poff) {
+    if (threadIdx.x != 0) return;
+    int acc = 0;
+    poff[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        const int cnt = offsets[e + 1] - offsets[e];
+        acc += (cnt + kSegPad - 1) / kSegPad * kSegPad;
+        poff[e + 1] = acc;
+    }
+}
+
+// For each padded position q < nq: the aligned position it holds, or -1 for
+// padding (and for q past the last segment).
+__global__ __launch_bounds__(256) void seg_src_kernel(const int32_t *__restrict__ offsets,
+                                                      const int32_t *__restrict__ poff, int E,
+                                                      int nq, int32_t *__restrict__ src) {
+    const int q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nq) return;
+    int r = -1;
+    if (q < poff[E]) {
+        int lo = 0, hi = E - 1;  // the last e with poff[e] <= q
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (poff[mid] <= q) lo = mid;
+            else hi = mid - 1;
+        }
+        const int local = q - poff[lo];
+        if (local < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + local;
+    }
+    src[q] = r;
+}
+
+// Batched bf16 transpose through LDS: for batch b = blockIdx.y / (L / 64),
+// out_b[l][q] = in_b[row(q)][l] with row(q) = src[q] (0 where src[q] < 0) or q
+// when src is null; q < nq (a multiple of 8), l < L (a multiple of 64).  A
+// block moves a 64 x 64 tile.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(
+    const uint16_t *__restrict__ in, int64_t ld_in, int64_t in_bs, const int32_t *__restrict__ src,
+    int nq, int L, uint16_t *__restrict__ out, int64_t ld_out, int64_t out_bs) {
+    constexpr int kTW = 72;  // LDS row stride (bf16): 144 bytes keeps 16-byte stores aligned
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kTW];
+    const int lt = L / 64;
+    const int b = blockIdx.y / lt;
+    const int q0 = blockIdx.x * 64, l0 = (blockIdx.y % lt) * 64;
+    in += (int64_t)b * in_bs;
+    out += (int64_t)b * out_bs;
+    for (int c = threadIdx.x; c < 512; c += blockDim.x) {
+        const int qq = c >> 3, lc = 8 * (c & 7);
+        const int q = q0 + qq;
+        uint4 v = uint4{0, 0, 0, 0};
+        if (q < nq) {
+            const int64_t r = src ? (int64_t)src[q] : (int64_t)q;
+            if (r >= 0) v = *reinterpret_cast<const uint4 *>(in + r * ld_in + l0 + lc);
+        }
+        *reinterpret_cast<uint4 *>(tile + qq * kTW + lc) = v;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 512; c += blockDim.x) {
+        const int ll = c >> 3, qc = 8 * (c & 7);
+        if (q0 + qc >= nq) continue;
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            o[h] = (uint32_t)tile[(qc + 2 * h) * kTW + ll] |
+                   ((uint32_t)tile[(qc + 2 * h + 1) * kTW + ll] << 16);
+        *reinterpret_cast<uint4 *>(out + (int64_t)(l0 + ll) * ld_out + q0 + qc) =
+            uint4{o[0], o[1], o[2], o[3]};
+    }
 }
 
 __device__ __forceinline__ float wave_sum_f(float v) {
@@ -365,39 +353,62 @@ hipError_t launch_route_backward(const float *logits, const int32_t *ids, const 
     return hipGetLastError();
 }
 
-size_t ffn_backward_part_bytes(int64_t T, int H, int I, int k, int part) {
+namespace {
+
+// Padded positions (a multiple of 64, so the transposes' tiles are whole).
+int64_t padded_positions(int64_t T, int E, int k) {
+    return (T * k + (int64_t)kSegPad * E + 63) / 64 * 64;
+}
+
+size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
     const size_t P = (size_t)T * (size_t)k;
+    const size_t Pp = (size_t)padded_positions(T, E, k);
     size_t b = 0;
     switch (part) {
-        case 0: b = P * 2 * I * 4; break;  // h13   f32  [P, 2I]
-        case 1: b = P * I * 4; break;      // G     f32  [P, I]
-        case 2: b = P * I * 2; break;      // wact  bf16 [P, I]
-        case 3: b = P * 2 * I * 2; break;  // dh13  bf16 [P, 2I]
-        case 4: b = P * H * 4; break;      // dxs   f32  [P, H]
+        case 0: b = P * 2 * I * 4; break;               // h13    f32  [P, 2I]
+        case 1: b = P * I * 4; break;                   // G      f32  [P, I]
+        case 2: b = P * I * 2; break;                   // wact   bf16 [P, I]
+        case 3: b = P * 2 * I * 2; break;               // dh13   bf16 [P, 2I]
+        case 4: b = P * H * 4; break;                   // dxs    f32  [P, H]
+        case 5: b = P * H * 2; break;                   // xs     bf16 [P, H]
+        case 6: b = P * H * 2; break;                   // dys    bf16 [P, H]
+        case 7: b = (size_t)E * 2 * I * H * 2; break;   // w13t   bf16 [E, H, 2I]
+        case 8: b = (size_t)E * H * I * 2; break;       // w2t    bf16 [E, I, H]
+        case 9: b = (size_t)H * Pp * 2; break;          // dyT    bf16 [H, Pp]
+        case 10: b = (size_t)I * Pp * 2; break;         // wactT  bf16 [I, Pp]
+        case 11: b = (size_t)2 * I * Pp * 2; break;     // dh13T  bf16 [2I, Pp]
+        case 12: b = (size_t)H * Pp * 2; break;         // xT     bf16 [H, Pp]
+        case 13: b = (size_t)(E + 1) * 4; break;        // poff   int32 [E+1]
+        case 14: b = Pp * 4; break;                     // src    int32 [Pp]
     }
     return (b + 255) / 256 * 256;
 }
+constexpr int kParts = 15;
 
-size_t ffn_backward_scratch_bytes(int64_t T, int H, int I, int k) {
-    size_t b = 0;
-    for (int part = 0; part < 5; ++part) b += ffn_backward_part_bytes(T, H, I, k, part);
-    return b;
-}
-
-namespace {
-template <bool KSEG, bool BKM>
-hipError_t launch_bwd_gemm(const BwdGemm &g, int64_t P, hipStream_t s) {
-    dim3 grid;
-    if (KSEG) {
-        const int m_tiles = (g.M + kBM - 1) / kBM;
-        grid = dim3((unsigned)(m_tiles * g.n_tiles), (unsigned)g.E);
-    } else {
-        grid = dim3((unsigned)((P + kBM - 1) / kBM + g.E), (unsigned)g.n_tiles);
-    }
-    hipLaunchKernelGGL((bwd_gemm_kernel<KSEG, BKM>), grid, dim3(kBT), 0, s, g);
+hipError_t transpose(const uint16_t *in, int64_t ld_in, int64_t in_bs, const int32_t *src,
+                     int nq, int L, uint16_t *out, int64_t ld_out, int64_t out_bs, int batch,
+                     hipStream_t s) {
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((nq + 63) / 64), (unsigned)(L / 64 * batch)),
+                       dim3(256), 0, s, in, ld_in, in_bs, src, nq, L, out, ld_out, out_bs);
     return hipGetLastError();
 }
+
+hipError_t wgrad(const uint16_t *A, const uint16_t *B, int64_t ld, const int32_t *poff, int E,
+                 int M, int N, float *C, hipStream_t s) {
+    const int n_tiles = (N + kBN - 1) / kBN;
+    const int m_tiles = (M + kBM - 1) / kBM;
+    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(m_tiles * n_tiles), (unsigned)E), dim3(kBT),
+                       0, s, A, B, ld, poff, M, N, n_tiles, C);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t ffn_backward_scratch_bytes(int64_t T, int H, int I, int E, int k) {
+    size_t b = 0;
+    for (int part = 0; part < kParts; ++part) b += part_bytes(T, H, I, E, k, part);
+    return b;
+}
 
 hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, const uint16_t *w2,
                                     const float *topk_w, const int32_t *offsets,
@@ -408,63 +419,68 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
                                     hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int64_t P = T * k;
+    const int Pp = (int)padded_positions(T, E, k);
+    char *part[kParts];
     char *base = static_cast<char *>(ws);
-    float *h13 = reinterpret_cast<float *>(base);
-    base += ffn_backward_part_bytes(T, H, I, k, 0);
-    float *G = reinterpret_cast<float *>(base);
-    base += ffn_backward_part_bytes(T, H, I, k, 1);
-    uint16_t *wact = reinterpret_cast<uint16_t *>(base);
-    base += ffn_backward_part_bytes(T, H, I, k, 2);
-    uint16_t *dh13 = reinterpret_cast<uint16_t *>(base);
-    base += ffn_backward_part_bytes(T, H, I, k, 3);
-    float *dxs = reinterpret_cast<float *>(base);
-
+    for (int i = 0; i < kParts; ++i) {
+        part[i] = base;
+        base += part_bytes(T, H, I, E, k, i);
+    }
+    float *h13 = reinterpret_cast<float *>(part[0]);
+    float *G = reinterpret_cast<float *>(part[1]);
+    uint16_t *wact = reinterpret_cast<uint16_t *>(part[2]);
+    uint16_t *dh13 = reinterpret_cast<uint16_t *>(part[3]);
+    float *dxs = reinterpret_cast<float *>(part[4]);
+    uint16_t *xs = reinterpret_cast<uint16_t *>(part[5]);
+    uint16_t *dys = reinterpret_cast<uint16_t *>(part[6]);
+    uint16_t *w13t = reinterpret_cast<uint16_t *>(part[7]);
+    uint16_t *w2t = reinterpret_cast<uint16_t *>(part[8]);
+    uint16_t *dyT = reinterpret_cast<uint16_t *>(part[9]);
+    uint16_t *wactT = reinterpret_cast<uint16_t *>(part[10]);
+    uint16_t *dh13T = reinterpret_cast<uint16_t *>(part[11]);
+    uint16_t *xT = reinterpret_cast<uint16_t *>(part[12]);
+    int32_t *poff = reinterpret_cast<int32_t *>(part[13]);
+    int32_t *src = reinterpret_cast<int32_t *>(part[14]);
     hipError_t err;
-    BwdGemm g{};
-    g.offsets = offsets;
-    g.E = E;
-    // h13[p] = x[tok p] . w13[e]^T   (gate and up recomputed)
-    g.A = x; g.lda = H; g.a_gather = sorted_tok;
-    g.B = w13; g.ldb = H; g.b_estride = (int64_t)2 * I * H; g.b_gather = nullptr;
-    g.C = h13; g.ldc = 2 * I; g.c_estride = 0;
-    g.M = 0; g.N = 2 * I; g.K = H; g.n_tiles = (g.N + kBN - 1) / kBN;
-    if ((err = launch_bwd_gemm<false, false>(g, P, s)) != hipSuccess) return err;
-    // G[p] = dy[tok p] . w2[e]   (w2[e] is [H, I]: k = h rows, n = i contiguous)
-    g.A = dy; g.lda = H; g.a_gather = sorted_tok;
-    g.B = w2; g.ldb = I; g.b_estride = (int64_t)H * I;
-    g.C = G; g.ldc = I;
-    g.N = I; g.K = H; g.n_tiles = (g.N + kBN - 1) / kBN;
-    if ((err = launch_bwd_gemm<false, true>(g, P, s)) != hipSuccess) return err;
+#define MOE_TRY(x)                                   \
+    do {                                             \
+        if ((err = (x)) != hipSuccess) return err;   \
+    } while (0)
 
+    // Layout preparation: gathered rows, per-expert transposed weights, the
+    // padded segment map.
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)P), dim3(256), 0, s, x, dy, sorted_tok,
+                       offsets, E, H, xs, dys);
+    MOE_TRY(hipGetLastError());
+    MOE_TRY(transpose(w13, H, (int64_t)2 * I * H, nullptr, 2 * I, H, w13t, 2 * I,
+                      (int64_t)2 * I * H, E, s));
+    MOE_TRY(transpose(w2, I, (int64_t)H * I, nullptr, H, I, w2t, H, (int64_t)H * I, E, s));
+    hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, E, poff);
+    MOE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(seg_src_kernel, dim3((unsigned)((Pp + 255) / 256)), dim3(256), 0, s,
+                       offsets, poff, E, Pp, src);
+    MOE_TRY(hipGetLastError());
+
+    // Row-segment products on the forward's grouped kernel (FC2 form).
+    MOE_TRY(launch_down_bf16(xs, w13, offsets, T, 2 * I, H, E, k, 1, h13, s));  // gate/up
+    MOE_TRY(launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));       // G
     hipLaunchKernelGGL(bwd_act_kernel, dim3((unsigned)P), dim3(256), 0, s, h13, G, topk_w,
                        offsets, sorted_slot, E, I, wact, dh13, dw);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-
-    // dxs[p] = dh13[p] . w13[e]   (w13[e] is [2I, H]: k = c rows, n = h contiguous)
-    g.A = dh13; g.lda = 2 * I; g.a_gather = nullptr;
-    g.B = w13; g.ldb = H; g.b_estride = (int64_t)2 * I * H;
-    g.C = dxs; g.ldc = H;
-    g.N = H; g.K = 2 * I; g.n_tiles = (g.N + kBN - 1) / kBN;
-    if ((err = launch_bwd_gemm<false, true>(g, P, s)) != hipSuccess) return err;
+    MOE_TRY(hipGetLastError());
+    MOE_TRY(launch_down_bf16(dh13, w13t, offsets, T, H, 2 * I, E, k, 1, dxs, s));  // d_hidden
     hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
                        H, dx, dw);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    MOE_TRY(hipGetLastError());
 
-    // dw2[e][h, i] = sum over the segment of dy[tok p, h] (w act)[p, i]
-    BwdGemm w{};
-    w.offsets = offsets;
-    w.E = E;
-    w.A = dy; w.lda = H; w.a_gather = sorted_tok;
-    w.B = wact; w.ldb = I; w.b_gather = nullptr;
-    w.C = dw2; w.ldc = I; w.c_estride = (int64_t)H * I;
-    w.M = H; w.N = I; w.n_tiles = (w.N + kBN - 1) / kBN;
-    if ((err = launch_bwd_gemm<true, true>(w, P, s)) != hipSuccess) return err;
-    // dw13[e][c, h] = sum over the segment of dh13[p, c] x[tok p, h]
-    w.A = dh13; w.lda = 2 * I; w.a_gather = nullptr;
-    w.B = x; w.ldb = H; w.b_gather = sorted_tok;
-    w.C = dw13; w.ldc = H; w.c_estride = (int64_t)2 * I * H;
-    w.M = 2 * I; w.N = H; w.n_tiles = (w.N + kBN - 1) / kBN;
-    return launch_bwd_gemm<true, true>(w, P, s);
+    // Weight gradients over the padded, transposed segments.
+    MOE_TRY(transpose(dys, H, 0, src, Pp, H, dyT, Pp, 0, 1, s));
+    MOE_TRY(transpose(wact, I, 0, src, Pp, I, wactT, Pp, 0, 1, s));
+    MOE_TRY(transpose(dh13, 2 * I, 0, src, Pp, 2 * I, dh13T, Pp, 0, 1, s));
+    MOE_TRY(transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
+    MOE_TRY(wgrad(dyT, wactT, Pp, poff, E, H, I, dw2, s));       // dw2[e]  [H, I]
+    MOE_TRY(wgrad(dh13T, xT, Pp, poff, E, 2 * I, H, dw13, s));   // dw13[e] [2I, H]
+#undef MOE_TRY
+    return hipSuccess;
 }
 
 }  // namespace moe

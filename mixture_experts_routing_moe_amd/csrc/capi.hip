@@ -467,9 +467,8 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
 
 size_t moe_expert_ffn_backward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
                                               int32_t k) {
-    (void)E;
-    if (T <= 0 || H < 1 || I < 1 || k < 1) return 0;
-    return moe::ffn_backward_scratch_bytes(T, H, I, k);
+    if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
+    return moe::ffn_backward_scratch_bytes(T, H, I, E, k);
 }
 
 moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const void *w13,
@@ -494,16 +493,19 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
     CHECK(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(grad_out) &&
               aligned16(grad_hidden) && aligned16(grad_w13) && aligned16(grad_w2),
           MOE_ERR_INVALID_ARG, "%s: hidden, weights, gradients must be 16-byte aligned", fn);
-    const size_t need = moe::ffn_backward_scratch_bytes(T, H, I, k);
+    const size_t need = moe::ffn_backward_scratch_bytes(T, H, I, E, k);
     CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
     CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
           fn);
-    // Grid limits of the grouped products: one block row per 128 positions
-    // plus one per expert; 128-column tiles of at most 2I columns.
-    CHECK(T * (int64_t)k / 128 + E < (int64_t)1 << 31 && 2 * (int64_t)I / 128 < 65535 &&
-              (int64_t)H / 128 < 65535 && (2 * (int64_t)I / 128 + 1) * ((int64_t)H / 128 + 1) < (int64_t)1 << 31,
-          MOE_ERR_UNSUPPORTED, "%s: shape exceeds the launch grid", fn);
+    // Launch grids: 64 x 64 transpose tiles (the weight transposes put E times
+    // H / 64 or I / 64 block rows in one grid dimension), weight-gradient
+    // tiles of 128 x 128, padded positions within int32.
+    const int64_t Pp = T * k + 32 * (int64_t)E + 64;
+    CHECK(Pp < (int64_t)1 << 31 && (int64_t)E * H / 64 <= 65535 &&
+              (int64_t)E * I / 64 <= 65535 &&
+              (2 * (int64_t)I / 128 + 1) * ((int64_t)H / 128 + 1) < (int64_t)1 << 31,
+          MOE_ERR_UNSUPPORTED, "%s: shape exceeds the launch grids", fn);
     return hip_status(moe::launch_ffn_backward_bf16(
                           static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(w13),
                           static_cast<const uint16_t *>(w2), topk_w, expert_offsets,

@@ -309,9 +309,8 @@ hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const floa
 hipError_t launch_route_backward(const float *logits, const int32_t *ids, const float *w,
                                  const float *gw, int64_t T, int E, int k, int norm, float *out,
                                  hipStream_t s);
-// Expert FFN backward (bf16): scratch layout and size, then the launches.
-size_t ffn_backward_part_bytes(int64_t T, int H, int I, int k, int part);
-size_t ffn_backward_scratch_bytes(int64_t T, int H, int I, int k);
+// Expert FFN backward (bf16): scratch size, then the launches.
+size_t ffn_backward_scratch_bytes(int64_t T, int H, int I, int E, int k);
 hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, const uint16_t *w2,
                                     const float *topk_w, const int32_t *offsets,
                                     const int32_t *sorted_tok, const int32_t *sorted_slot,
