@@ -501,7 +501,7 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
     // Launch grids: 64 x 64 transpose tiles (the weight transposes put E times
     // H / 64 or I / 64 block rows in one grid dimension), weight-gradient
     // tiles of 128 x 128, padded positions within int32.
-    const int64_t Pp = T * k + 32 * (int64_t)E + 64;
+    const int64_t Pp = T * k + 64 * (int64_t)E + 64;
     CHECK(Pp < (int64_t)1 << 31 && (int64_t)E * H / 64 <= 65535 &&
               (int64_t)E * I / 64 <= 65535 &&
               (2 * (int64_t)I / 128 + 1) * ((int64_t)H / 128 + 1) < (int64_t)1 << 31,
