@@ -24,20 +24,22 @@
 //   operands (dy, x, w act, [d_gate ; d_up]) are transposed into [columns,
 //   positions] with every expert's segment padded to a whole number of
 //   k-tiles (zeros in the padding), so the k loop of a segment runs over
-//   whole, aligned tiles; one block computes a 128 x 128 tile of one expert's
-//   gradient (zero for an expert with no rows).  k-tiles of 32 in two LDS
-//   stages measured 4 % faster than 64 on the Mixtral shape and 5 % slower on
-//   the fine-grained one.
+//   whole, aligned tiles; one block computes a 256 x 256 tile of one expert's
+//   gradient (zero for an expert with no rows), 8 waves of 64 x 128, k-tiles
+//   of 64 in two LDS stages (144 KB).  Measured against 128 x 128 tiles and
+//   32-wide k-tiles: 4 % (Mixtral shape) and 10 % (fine-grained) faster
+//   backward.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kBT = 256;          // threads per wgrad block: 4 waves in 2 x 2
-constexpr int kBM = 128;          // wgrad tile rows (m)
-constexpr int kBN = 128;          // wgrad tile columns (n)
+#ifndef MOE_WGRAD_TILE
+#define MOE_WGRAD_TILE 256
+#endif
+constexpr int kWT = MOE_WGRAD_TILE;  // wgrad tile rows and columns (128 or 256)
 #ifndef MOE_WGRAD_BK
-#define MOE_WGRAD_BK 32
+#define MOE_WGRAD_BK 64
 #endif
 #ifndef MOE_WGRAD_STAGES
 #define MOE_WGRAD_STAGES 2
@@ -46,10 +48,9 @@ constexpr int kBK = MOE_WGRAD_BK;       // k per LDS stage (MFMA k-steps of 32)
 constexpr int kNS = MOE_WGRAD_STAGES;   // LDS stages (1 or 2)
 constexpr int kSegPad = kBK;      // positions per padded segment unit: whole k-tiles
 constexpr int kLdsW = kBK + 8;    // bf16 per LDS row: 144 bytes, 16-byte aligned rows
-constexpr int kChunks = kBM * kBK / 8 / kBT;  // 16-byte chunks per thread and operand
 constexpr int kCPR = kBK / 8;                  // 16-byte chunks per tile row
-static_assert(kBK % 32 == 0 && (kNS == 1 || kNS == 2) && kChunks * kBT * 8 == kBM * kBK,
-              "whole MFMA k-steps, one or two stages, whole chunks per thread");
+static_assert(kBK % 32 == 0 && (kNS == 1 || kNS == 2) && (kWT == 128 || kWT == 256),
+              "whole MFMA k-steps, one or two stages, 128 or 256 tiles");
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, to_bf16(f));
@@ -58,55 +59,70 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 // Weight gradient of one expert, C_e[m, n] = sum over k in the expert's padded
 // segment [poff[e], poff[e+1]) of A[m, k] B[n, k]; A [M, ld] and B [N, ld] bf16
 // with k contiguous, C_e float32 [M, N] at C + e M N.  Block (tile, e): a
-// 128 x 128 tile, 4 waves of 64 x 64 = 4 x 4 MFMA 16x16x32 fragments.  The
-// next k-tile is loaded into registers while the current LDS stage is
-// multiplied, then written into the other stage (one barrier per k-tile) or,
-// with a single stage, into the same one after a second barrier.
-__global__ __launch_bounds__(kBT) void wgrad_kernel(const uint16_t *__restrict__ A,
-                                                    const uint16_t *__restrict__ B, int64_t ld,
-                                                    const int32_t *__restrict__ poff, int M,
-                                                    int N, int n_tiles, float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kNS][kBM * kLdsW];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[kNS][kBN * kLdsW];
+// BM x BN tile, WM x WN waves of (BM / WM) x (BN / WN), each a grid of MFMA
+// 16x16x32 fragments.  The next k-tile is loaded into registers while the
+// current LDS stage is multiplied, then written into the other stage (one
+// barrier per k-tile) or, with a single stage, into the same one after a
+// second barrier.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t ld,
+    const int32_t *__restrict__ poff, int M, int N, int n_tiles, float *__restrict__ C) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int FA = BM / WM / 16, FB = BN / WN / 16;  // fragments per wave
+    constexpr int CA = BM * kBK / 8 / NT, CB = BN * kBK / 8 / NT;  // chunks per thread
+    static_assert(CA * NT * 8 == BM * kBK && CB * NT * 8 == BN * kBK, "whole chunks per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kNS][BM * kLdsW];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[kNS][BN * kLdsW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int e = blockIdx.y;
-    const int m0 = (int)(blockIdx.x / n_tiles) * kBM;
-    const int n0 = (int)(blockIdx.x % n_tiles) * kBN;
+    const int m0 = (int)(blockIdx.x / n_tiles) * BM;
+    const int n0 = (int)(blockIdx.x % n_tiles) * BN;
     const int k0 = poff[e], k_end = poff[e + 1];
     float *Ce = C + (int64_t)e * M * N;
 
-    // Chunk c (kChunks per thread) = row c / kCPR of the tile, k-group c % kCPR.
-    uint4 ra[kChunks], rb[kChunks];
+    // Chunk c = row c / kCPR of the tile, k-group c % kCPR.
+    uint4 ra[CA], rb[CB];
     auto load = [&](int kt) {
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-            const int c = tid + kBT * q;
+        for (int q = 0; q < CA; ++q) {
+            const int c = tid + NT * q;
             const int r = c / kCPR, kc = 8 * (c % kCPR);
             ra[q] = uint4{0, 0, 0, 0};
-            rb[q] = uint4{0, 0, 0, 0};
             if (m0 + r < M) ra[q] = *reinterpret_cast<const uint4 *>(A + (int64_t)(m0 + r) * ld + kt + kc);
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int c = tid + NT * q;
+            const int r = c / kCPR, kc = 8 * (c % kCPR);
+            rb[q] = uint4{0, 0, 0, 0};
             if (n0 + r < N) rb[q] = *reinterpret_cast<const uint4 *>(B + (int64_t)(n0 + r) * ld + kt + kc);
         }
     };
     auto store = [&](int st) {
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-            const int c = tid + kBT * q;
+        for (int q = 0; q < CA; ++q) {
+            const int c = tid + NT * q;
             *reinterpret_cast<uint4 *>(&sA[st][(c / kCPR) * kLdsW + 8 * (c % kCPR)]) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int c = tid + NT * q;
             *reinterpret_cast<uint4 *>(&sB[st][(c / kCPR) * kLdsW + 8 * (c % kCPR)]) = rb[q];
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[FA][FB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int i = lane & 15, kq = lane >> 4;
+    const int wr = wm * (BM / WM), wc = wn * (BN / WN);
     int st = 0;
     if (k0 < k_end) {
         load(k0);
@@ -118,16 +134,17 @@ __global__ __launch_bounds__(kBT) void wgrad_kernel(const uint16_t *__restrict__
         if (more) load(kt + kBK);
 #pragma unroll
         for (int ks = 0; ks < kBK; ks += 32) {
-            bf16x8 af[4], bf[4];
+            bf16x8 af[FA], bf[FB];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                af[f] = *reinterpret_cast<const bf16x8 *>(&sA[st][(wm * 64 + f * 16 + i) * kLdsW + ks + 8 * kq]);
-                bf[f] = *reinterpret_cast<const bf16x8 *>(&sB[st][(wn * 64 + f * 16 + i) * kLdsW + ks + 8 * kq]);
-            }
+            for (int f = 0; f < FA; ++f)
+                af[f] = *reinterpret_cast<const bf16x8 *>(&sA[st][(wr + f * 16 + i) * kLdsW + ks + 8 * kq]);
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int f = 0; f < FB; ++f)
+                bf[f] = *reinterpret_cast<const bf16x8 *>(&sB[st][(wc + f * 16 + i) * kLdsW + ks + 8 * kq]);
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int b = 0; b < FB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
         }
         // With two stages the other one was last read before the previous
@@ -140,13 +157,13 @@ __global__ __launch_bounds__(kBT) void wgrad_kernel(const uint16_t *__restrict__
 
     // Accumulator r of fragment (a, b): row 4 kq + r of A's fragment, column i of B's.
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int n = n0 + wn * 64 + b * 16 + i;
+        for (int b = 0; b < FB; ++b) {
+            const int n = n0 + wc + b * 16 + i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + a * 16 + 4 * kq + r;
+                const int m = m0 + wr + a * 16 + 4 * kq + r;
                 if (m < M && n < N) Ce[(int64_t)m * N + n] = acc[a][b][r];
             }
         }
@@ -425,10 +442,12 @@ hipError_t transpose(const uint16_t *in, int64_t ld_in, int64_t in_bs, const int
 
 hipError_t wgrad(const uint16_t *A, const uint16_t *B, int64_t ld, const int32_t *poff, int E,
                  int M, int N, float *C, hipStream_t s) {
-    const int n_tiles = (N + kBN - 1) / kBN;
-    const int m_tiles = (M + kBM - 1) / kBM;
-    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(m_tiles * n_tiles), (unsigned)E), dim3(kBT),
-                       0, s, A, B, ld, poff, M, N, n_tiles, C);
+    // kWT = 256: 8 waves of 64 x 128; kWT = 128: 4 waves of 64 x 64.
+    constexpr int WM = kWT == 256 ? 4 : 2, WN = 2;
+    const int n_tiles = (N + kWT - 1) / kWT;
+    const int m_tiles = (M + kWT - 1) / kWT;
+    hipLaunchKernelGGL((wgrad_kernel<kWT, kWT, WM, WN>), dim3((unsigned)(m_tiles * n_tiles), (unsigned)E),
+                       dim3(WM * WN * 64), 0, s, A, B, ld, poff, M, N, n_tiles, C);
     return hipGetLastError();
 }
 
