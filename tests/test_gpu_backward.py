@@ -121,6 +121,8 @@ def _bwd_gpu(x, w13, w2, w32, ids, dy):
     (260, 128, 128, 12, 3, 0.0, 0.2),   # dropped slots (id -1)
     (1, 128, 128, 8, 2, 0.0, 0.0),
     (400, 64, 256, 2, 1, 2.0, 0.0),
+    (50, 64, 64, 1, 1, 0.0, 0.0),       # one expert
+    (100, 64, 128, 256, 8, 0.0, 0.0),   # many experts, most with a few rows or none
 ])
 def test_ffn_backward(T, H, I, E, k, skew, inv):
     x, w13, w2, w32, ids, dy = _rand_case(T + H + I + E, T, H, I, E, k, skew, inv)
