@@ -344,7 +344,7 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
                                 float *grad_logits, void *stream);
 
 /*
- * moe_expert_ffn_backward -- backward of moe_expert_ffn (bfloat16 layer).
+ * moe_expert_ffn_backward -- backward of moe_expert_ffn.
  * The chain rule applied to [p6] moe_prefill_experts and [mlc] moe_sum (the
  * pages give only the forward).  For each valid slot (t, j) with expert e and
  * weight w, with gate/up = hidden[t] . w13[e]^T halves, s = sigmoid(gate),
@@ -356,19 +356,22 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
  *   grad_w13[e]       = sum over the slots of e of [d_gate ; d_up]^T hidden[t]
  * Slots with an invalid id get grad_topk_w = 0 and add nothing; an expert no
  * slot names gets zero weight gradients (every element of every output is
- * written).  gate/up are recomputed (one grouped product); w act and
- * d_gate/d_up are rounded to bfloat16 as the inputs of the bf16 products,
- * everything else accumulates in float32.  Results are deterministic.  The
+ * written).  gate/up are recomputed.  MOE_BF16: five grouped bf16 products
+ * on the matrix cores; w act and d_gate/d_up are rounded to bfloat16 as the
+ * inputs of those products, everything else accumulates in float32, and the
  * call writes w13 and w2 transposed per expert into the workspace (weights
- * change between training steps, so nothing is cached).
+ * change between training steps, so nothing is cached).  MOE_F32 (small
+ * layers): float32 throughout, one thread per output element.  Results are
+ * deterministic.
  *
- * dt must be MOE_BF16.  hidden [T, H], w13 [E, 2I, H], w2 [E, H, I],
- * grad_out [T, H] bfloat16; topk_w [T, k] float32; expert_offsets [E+1],
+ * hidden [T, H], w13 [E, 2I, H], w2 [E, H, I], grad_out [T, H] in `dt`;
+ * topk_w [T, k] float32; expert_offsets [E+1],
  * sorted_token_ids, sorted_slot_ids and slot_to_sorted [T*k] as written by
  * moe_align for the forward's ids.  Outputs float32: grad_hidden [T, H],
  * grad_w13 [E, 2I, H], grad_w2 [E, H, I], grad_topk_w [T, k].
  * workspace >= moe_expert_ffn_backward_workspace_size(T, H, I, E, k) bytes
- * (about T*k*(24 I + 12 H) + 6 E H I), 16-byte aligned, clobbered.
+ * (about T*k*(24 I + 12 H) + 6 E H I: the bfloat16 path's need, which also
+ * covers the float32 path's T*k*(6 I + H)*4), 16-byte aligned, clobbered.
  * Requires H % 64 == 0, I % 64 == 0; hidden, weights, grad_out and the
  * gradients 16-byte aligned.  T = 0 enqueues nothing, as for every call, so
  * the weight gradients are then left as they were.

@@ -339,6 +339,123 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
     }
 }
 
+// ---------------------------------------------------------------------------
+// Float32 layers (small; no matrix cores): one thread per output element,
+// float32 dot products in a fixed order, as the float32 forward.
+// ---------------------------------------------------------------------------
+
+// Expert whose segment [offsets[e], offsets[e+1]) holds position p.
+__device__ int expert_at(const int32_t *__restrict__ offsets, int E, int p) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= p) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// h13[p] = [x . w1^T, x . w3^T] and G[p] = dy . w2[e] for unit i of position p.
+__global__ __launch_bounds__(256) void f32_gate_up_g_kernel(
+    const float *__restrict__ x, const float *__restrict__ w13, const float *__restrict__ w2,
+    const float *__restrict__ dy, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ tok, int H, int I, int E, float *__restrict__ h13,
+    float *__restrict__ G) {
+    const int p = blockIdx.x;
+    if (p >= offsets[E]) return;
+    const int i = blockIdx.y * blockDim.x + threadIdx.x;
+    if (i >= I) return;
+    const int e = expert_at(offsets, E, p);
+    const int64_t t = tok[p];
+    const float *xr = x + t * H, *dr = dy + t * H;
+    const float *wg = w13 + ((int64_t)e * 2 * I + i) * H;
+    const float *wu = w13 + ((int64_t)e * 2 * I + I + i) * H;
+    const float *wd = w2 + (int64_t)e * H * I + i;
+    float g = 0.f, u = 0.f, gd = 0.f;
+    for (int h = 0; h < H; ++h) {
+        g = fmaf(xr[h], wg[h], g);
+        u = fmaf(xr[h], wu[h], u);
+        gd = fmaf(dr[h], wd[(int64_t)h * I], gd);
+    }
+    h13[(int64_t)p * 2 * I + i] = g;
+    h13[(int64_t)p * 2 * I + I + i] = u;
+    G[(int64_t)p * I + i] = gd;
+}
+
+// Per position: act (float32), [d_gate ; d_up] and grad_topk_w = <G, act>
+// (fixed-order sum: strided per thread, then a fixed tree).
+__global__ __launch_bounds__(256) void f32_act_kernel(const float *__restrict__ h13,
+                                                      const float *__restrict__ G,
+                                                      const float *__restrict__ topk_w,
+                                                      const int32_t *__restrict__ offsets,
+                                                      const int32_t *__restrict__ sorted_slot,
+                                                      int E, int I, float *__restrict__ act,
+                                                      float *__restrict__ d13,
+                                                      float *__restrict__ grad_w) {
+    __shared__ float part[4];
+    const int p = blockIdx.x;
+    if (p >= offsets[E]) return;
+    const int slot = sorted_slot[p];
+    const float w = topk_w[slot];
+    float sum = 0.f;
+    for (int i = threadIdx.x; i < I; i += blockDim.x) {
+        const float z = h13[(int64_t)p * 2 * I + i], u = h13[(int64_t)p * 2 * I + I + i];
+        const float s = 1.0f / (1.0f + expf(-z));
+        const float a = z * s * u;
+        const float gi = G[(int64_t)p * I + i];
+        act[(int64_t)p * I + i] = a;
+        sum += gi * a;
+        const float da = w * gi;
+        d13[(int64_t)p * 2 * I + i] = da * u * s * (1.0f + z * (1.0f - s));
+        d13[(int64_t)p * 2 * I + I + i] = da * z * s;
+    }
+    sum = wave_sum_f(sum);
+    if (lane_id() == 0) part[threadIdx.x / kWave] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) grad_w[slot] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// dxs[p][h] = sum over c < 2I of d13[p][c] w13[e][c][h].
+__global__ __launch_bounds__(256) void f32_dx_kernel(const float *__restrict__ d13,
+                                                     const float *__restrict__ w13,
+                                                     const int32_t *__restrict__ offsets, int H,
+                                                     int I, int E, float *__restrict__ dxs) {
+    const int p = blockIdx.x;
+    if (p >= offsets[E]) return;
+    const int h = blockIdx.y * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    const int e = expert_at(offsets, E, p);
+    const float *d = d13 + (int64_t)p * 2 * I;
+    const float *w = w13 + (int64_t)e * 2 * I * H + h;
+    float acc = 0.f;
+    for (int c = 0; c < 2 * I; ++c) acc = fmaf(d[c], w[(int64_t)c * H], acc);
+    dxs[(int64_t)p * H + h] = acc;
+}
+
+// dw2[e][h][i] = sum over the segment of (w dy[tok p][h]) act[p][i], and
+// dw13[e][c][h] = sum over the segment of d13[p][c] x[tok p][h]; positions in
+// ascending order.  blockIdx.x = e * rows + row, threads over the columns.
+__global__ __launch_bounds__(256) void f32_wgrad_kernel(
+    const float *__restrict__ x, const float *__restrict__ dy, const float *__restrict__ act,
+    const float *__restrict__ d13, const float *__restrict__ topk_w,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tok,
+    const int32_t *__restrict__ sorted_slot, int H, int I, int which, float *__restrict__ out) {
+    const int rows = which == 2 ? H : 2 * I;  // rows of dw2[e] / dw13[e]
+    const int cols = which == 2 ? I : H;
+    const int e = blockIdx.x / rows, r = blockIdx.x % rows;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
+    if (c >= cols) return;
+    float acc = 0.f;
+    for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+        const int64_t t = tok[p];
+        if (which == 2)
+            acc = fmaf(topk_w[sorted_slot[p]] * dy[t * H + r], act[(int64_t)p * I + c], acc);
+        else
+            acc = fmaf(d13[(int64_t)p * 2 * I + r], x[t * H + c], acc);
+    }
+    out[((int64_t)e * rows + r) * cols + c] = acc;
+}
+
 // Gating softmax backward, one wave per row.  dot = sum_j w_j g_j over the
 // forward's weights.  norm: grad[e_j] = w_j (g_j - dot), 0 elsewhere.
 // Otherwise grad[e] = p_e (g(e) - dot) with p the softmax over all E logits
@@ -530,6 +647,47 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
     MOE_TRY(wgrad(dh13T, xT, Pp, poff, E, 2 * I, H, dw13, s));   // dw13[e] [2I, H]
 #undef MOE_TRY
     return hipSuccess;
+}
+
+
+hipError_t launch_ffn_backward_f32(const float *x, const float *w13, const float *w2,
+                                   const float *topk_w, const int32_t *offsets,
+                                   const int32_t *sorted_tok, const int32_t *sorted_slot,
+                                   const int32_t *slot_to_sorted, const float *dy, int64_t T,
+                                   int H, int I, int E, int k, float *dx, float *dw13,
+                                   float *dw2, float *dw, void *ws, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int64_t P = T * k;
+    float *h13 = static_cast<float *>(ws);   // [P, 2I]
+    float *G = h13 + P * 2 * I;              // [P, I]
+    float *act = G + P * I;                  // [P, I]
+    float *d13 = act + P * I;                // [P, 2I]
+    float *dxs = d13 + P * 2 * I;            // [P, H]
+    hipError_t err;
+    hipLaunchKernelGGL(f32_gate_up_g_kernel, dim3((unsigned)P, (unsigned)((I + 255) / 256)),
+                       dim3(256), 0, s, x, w13, w2, dy, offsets, sorted_tok, H, I, E, h13, G);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(f32_act_kernel, dim3((unsigned)P), dim3(256), 0, s, h13, G, topk_w,
+                       offsets, sorted_slot, E, I, act, d13, dw);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(f32_dx_kernel, dim3((unsigned)P, (unsigned)((H + 255) / 256)), dim3(256),
+                       0, s, d13, w13, offsets, H, I, E, dxs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
+                       H, dx, dw);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(f32_wgrad_kernel, dim3((unsigned)(E * H), (unsigned)((I + 255) / 256)),
+                       dim3(256), 0, s, x, dy, act, d13, topk_w, offsets, sorted_tok, sorted_slot,
+                       H, I, 2, dw2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(f32_wgrad_kernel, dim3((unsigned)(E * 2 * I), (unsigned)((H + 255) / 256)),
+                       dim3(256), 0, s, x, dy, act, d13, topk_w, offsets, sorted_tok, sorted_slot,
+                       H, I, 13, dw13);
+    return hipGetLastError();
+}
+
+size_t ffn_backward_f32_scratch_bytes(int64_t T, int H, int I, int k) {
+    return (size_t)T * k * (6 * (size_t)I + H) * 4;
 }
 
 }  // namespace moe

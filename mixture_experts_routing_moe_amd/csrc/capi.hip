@@ -484,7 +484,6 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
     const char *fn = "moe_expert_ffn_backward";
     moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
     if (st != MOE_OK) return st;
-    CHECK(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: only the bfloat16 path has a backward", fn);
     if (T == 0) return MOE_OK;
     CHECK(hidden && w13 && w2 && topk_w && expert_offsets && sorted_token_ids &&
               sorted_slot_ids && slot_to_sorted && grad_out && grad_hidden && grad_w13 &&
@@ -493,7 +492,8 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
     CHECK(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(grad_out) &&
               aligned16(grad_hidden) && aligned16(grad_w13) && aligned16(grad_w2),
           MOE_ERR_INVALID_ARG, "%s: hidden, weights, gradients must be 16-byte aligned", fn);
-    const size_t need = moe::ffn_backward_scratch_bytes(T, H, I, E, k);
+    const size_t need = dt == MOE_F32 ? moe::ffn_backward_f32_scratch_bytes(T, H, I, k)
+                                      : moe::ffn_backward_scratch_bytes(T, H, I, E, k);
     CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
     CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
@@ -506,13 +506,24 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
               (int64_t)E * I / 64 <= 65535 &&
               (2 * (int64_t)I / 128 + 1) * ((int64_t)H / 128 + 1) < (int64_t)1 << 31,
           MOE_ERR_UNSUPPORTED, "%s: shape exceeds the launch grids", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dt == MOE_F32) {
+        CHECK((int64_t)E * 2 * I < (int64_t)1 << 31 && (int64_t)E * H < (int64_t)1 << 31,
+              MOE_ERR_UNSUPPORTED, "%s: shape exceeds the launch grids", fn);
+        return hip_status(moe::launch_ffn_backward_f32(
+                              static_cast<const float *>(hidden), static_cast<const float *>(w13),
+                              static_cast<const float *>(w2), topk_w, expert_offsets,
+                              sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                              static_cast<const float *>(grad_out), T, H, I, E, k, grad_hidden,
+                              grad_w13, grad_w2, grad_topk_w, workspace, s),
+                          fn);
+    }
     return hip_status(moe::launch_ffn_backward_bf16(
                           static_cast<const uint16_t *>(hidden), static_cast<const uint16_t *>(w13),
                           static_cast<const uint16_t *>(w2), topk_w, expert_offsets,
                           sorted_token_ids, sorted_slot_ids, slot_to_sorted,
                           static_cast<const uint16_t *>(grad_out), T, H, I, E, k, grad_hidden,
-                          grad_w13, grad_w2, grad_topk_w, workspace,
-                          static_cast<hipStream_t>(stream)),
+                          grad_w13, grad_w2, grad_topk_w, workspace, s),
                       fn);
 }
 

@@ -309,8 +309,16 @@ hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const floa
 hipError_t launch_route_backward(const float *logits, const int32_t *ids, const float *w,
                                  const float *gw, int64_t T, int E, int k, int norm, float *out,
                                  hipStream_t s);
-// Expert FFN backward (bf16): scratch size, then the launches.
+// Expert FFN backward: scratch sizes (bf16; float32, always the smaller), then
+// the launches.
 size_t ffn_backward_scratch_bytes(int64_t T, int H, int I, int E, int k);
+size_t ffn_backward_f32_scratch_bytes(int64_t T, int H, int I, int k);
+hipError_t launch_ffn_backward_f32(const float *x, const float *w13, const float *w2,
+                                   const float *topk_w, const int32_t *offsets,
+                                   const int32_t *sorted_tok, const int32_t *sorted_slot,
+                                   const int32_t *slot_to_sorted, const float *dy, int64_t T,
+                                   int H, int I, int E, int k, float *dx, float *dw13,
+                                   float *dw2, float *dw, void *ws, hipStream_t s);
 hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, const uint16_t *w2,
                                     const float *topk_w, const int32_t *offsets,
                                     const int32_t *sorted_tok, const int32_t *sorted_slot,

@@ -310,8 +310,10 @@ def test_ffn_backward_validation(lib):
         return lib.moe_expert_ffn_backward(dt, x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                            T, H, I, E, k, dx, FAKE, FAKE, FAKE, ws, wsb, None)
 
-    assert fb(dt=_lib.MOE_F32) == U  # bf16 only
-    assert b"bfloat16" in lib.moe_last_error()
+    need32 = T * k * (6 * Im + H) * 4  # the float32 path needs less
+    assert need32 < need
+    assert fb(dt=_lib.MOE_F32, wsb=need32 - 1) == W
+    assert fb(dt=7) == I  # unknown dtype
     assert fb(H=96) == U  # H % 64
     assert fb(I=100) == U
     assert fb(k=65) == I  # k > MOE_MAX_TOPK

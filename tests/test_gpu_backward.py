@@ -139,6 +139,29 @@ def test_ffn_backward(T, H, I, E, k, skew, inv):
     assert np.all(got["grad_w13"][~used] == 0) and np.all(got["grad_w2"][~used] == 0)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,inv", [(4, 64, 128, 8, 2, 0.0), (50, 128, 64, 5, 3, 0.0),
+                                            (30, 64, 64, 3, 3, 0.2), (1, 64, 64, 1, 1, 0.0)])
+def test_ffn_backward_f32(T, H, I, E, k, inv):
+    """float32 layers: float32 throughout, so RMS(err) <= 1e-5 x RMS and
+    max |err| <= 1e-4 x max |oracle| for every gradient."""
+    g = np.random.Generator(np.random.PCG64(T * 11 + E))
+    x = g.standard_normal((T, H)).astype(np.float32)
+    w13 = (g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32)
+    w2 = (g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32)
+    dy = g.standard_normal((T, H)).astype(np.float32)
+    w, ids = oracle.route(g.standard_normal((T, E)).astype(np.float32), k, True)
+    if inv > 0:
+        ids = np.where(g.random(ids.shape) < inv, -1, ids).astype(np.int32)
+    w32 = w.astype(np.float32)
+    a = moe.moe_align(dev(ids), E)
+    got = moe.moe_expert_ffn_backward(dev(x), dev(w13), dev(w2), dev(w32), a, dev(dy))
+    ref = oracle.expert_ffn_backward(x, w13, w2, w32.astype(np.float64), ids, dy, "f32",
+                                     weights=True)
+    for name in ("grad_hidden", "grad_w13", "grad_w2", "grad_topk_w"):
+        check_grad(name, got[name].cpu().numpy(), ref[name], 1e-4, 1e-5)
+    assert np.all(got["grad_topk_w"].cpu().numpy()[ids < 0] == 0)
+
+
 def test_ffn_backward_deterministic():
     x, w13, w2, w32, ids, dy = _rand_case(5, 300, 128, 192, 8, 2)
     a = _bwd_gpu(x, w13, w2, w32, ids, dy)
@@ -217,3 +240,68 @@ def test_backward_full_size(name):
     rl = oracle.route_backward(inp["logits"][toks], oids[toks], ref["grad_topk_w"], w.norm)
     gl_s = gl[torch.from_numpy(toks).to(DEV)].cpu().numpy().astype(np.float64)
     assert np.abs(gl_s - rl).max() <= 1e-3 * np.abs(rl).max()
+
+
+def test_backward_graph_replay():
+    """Route + align + layer backward captured as one HIP graph: replays with
+    different grad_out, with other GPU work between them, equal eager runs
+    of the same calls bit for bit (the calls allocate, sync and memset
+    nothing)."""
+    T, H, I, E, k = 300, 128, 192, 8, 2
+    x, w13, w2, _, _, _ = _rand_case(77, T, H, I, E, k)
+    xd, w13d, w2d = dev_bf16(x), dev_bf16(w13), dev_bf16(w2)
+    g = np.random.Generator(np.random.PCG64(78))
+    logits = dev(g.standard_normal((T, E)).astype(np.float32))
+    dys = [dev_bf16(mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32)))
+           for _ in range(3)]
+    static_dy = dys[0].clone()
+
+    def bufs():
+        f32 = dict(dtype=torch.float32, device=DEV)
+        a = {"counts": torch.empty(E, dtype=torch.int32, device=DEV),
+             "offsets": torch.empty(E + 1, dtype=torch.int32, device=DEV),
+             "sorted_token_ids": torch.empty(T * k, dtype=torch.int32, device=DEV),
+             "sorted_slot_ids": torch.empty(T * k, dtype=torch.int32, device=DEV),
+             "slot_to_sorted": torch.empty(T * k, dtype=torch.int32, device=DEV)}
+        return {"tw": torch.empty((T, k), **f32),
+                "ids": torch.empty((T, k), dtype=torch.int32, device=DEV),
+                "aligned": a,
+                "align_ws": torch.empty(moe.moe_align_workspace_size(T, k, E), dtype=torch.uint8,
+                                        device=DEV),
+                "grads": {"grad_hidden": torch.empty((T, H), **f32),
+                          "grad_w13": torch.empty((E, 2 * I, H), **f32),
+                          "grad_w2": torch.empty((E, H, I), **f32),
+                          "grad_topk_w": torch.empty((T, k), **f32)},
+                "gl": torch.empty((T, E), **f32),
+                "ws": torch.empty(moe.moe_expert_ffn_backward_workspace_size(T, H, I, E, k),
+                                  dtype=torch.uint8, device=DEV)}
+
+    def step(b, dy):
+        moe.moe_route(logits, k, True, b["tw"], b["ids"])
+        moe.moe_align(b["ids"], E, b["aligned"], b["align_ws"])
+        moe.moe_expert_ffn_backward(xd, w13d, w2d, b["tw"], b["aligned"], dy, b["grads"], b["ws"])
+        moe.moe_route_backward(logits, b["ids"], b["tw"], b["grads"]["grad_topk_w"], True, b["gl"])
+
+    cap = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(cap, static_dy)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(cap, static_dy)
+    eager = bufs()
+    for r in (1, 2, 0, 1):
+        static_dy.copy_(dys[r])
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {n: t.clone() for n, t in cap["grads"].items()}
+        got_gl = cap["gl"].clone()
+        torch.matmul(xd.float(), xd.float().t()).sum().item()
+        step(eager, dys[r])
+        torch.cuda.synchronize()
+        for n in got:
+            assert torch.equal(got[n], eager["grads"][n]), (r, n)
+        assert torch.equal(got_gl, eager["gl"]), r
