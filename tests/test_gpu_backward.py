@@ -305,3 +305,31 @@ def test_backward_graph_replay():
         for n in got:
             assert torch.equal(got[n], eager["grads"][n]), (r, n)
         assert torch.equal(got_gl, eager["gl"]), r
+
+
+@pytest.mark.parametrize("counts", [(63, 64, 65, 128, 0, 1), (64, 0, 0, 129, 191, 2)])
+def test_ffn_backward_segment_boundaries(counts):
+    """Expert row counts on and around the weight gradients' 64-position
+    segment padding (and empty experts between them), k = 1."""
+    E, H, I, k = len(counts), 128, 192, 1
+    T = sum(counts)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])[:, None]
+    g = np.random.Generator(np.random.PCG64(T))
+    ids = ids[g.permutation(T)]  # tokens of one expert are not contiguous
+    x = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    w13 = mi.f32_to_bf16_bits((g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32))
+    w2 = mi.f32_to_bf16_bits((g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32))
+    dy = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    w32 = g.uniform(0.2, 1.0, (T, k)).astype(np.float32)
+    got = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    ref = oracle.expert_ffn_backward(x, w13, w2, w32.astype(np.float64), ids, dy, "bf16",
+                                     weights=True)
+    for name in ("grad_hidden", "grad_w13", "grad_w2"):
+        check_grad(name, got[name], ref[name])
+    check_grad("grad_topk_w", got["grad_topk_w"], ref["grad_topk_w"], TOPKW_TOL, TOPKW_TOL)
+    for e, c in enumerate(counts):
+        if c == 0:
+            assert np.all(got["grad_w13"][e] == 0) and np.all(got["grad_w2"][e] == 0)
+        else:  # each expert's slice on its own scale
+            check_grad(f"grad_w13[{e}]", got["grad_w13"][e], ref["grad_w13"][e])
+            check_grad(f"grad_w2[{e}]", got["grad_w2"][e], ref["grad_w2"][e])
