@@ -50,6 +50,7 @@ def _load():
         lib.oracle_expert_ffn.argtypes = [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                           vp, i64, vp, i32]
         lib.oracle_route_backward.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_route_grouped_backward.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
         lib.oracle_expert_ffn_backward.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
                                                    i32, i32, vp, i64, vp, vp, vp, vp, i32]
         lib.oracle_expert_wgrad_entries.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
@@ -58,6 +59,7 @@ def _load():
         for f in (lib.oracle_route, lib.oracle_router_logits, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
                   lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
                   lib.oracle_expert_ffn, lib.oracle_route_backward,
+                  lib.oracle_route_grouped_backward,
                   lib.oracle_expert_ffn_backward, lib.oracle_expert_wgrad_entries):
             f.restype = ctypes.c_int
         _lib = lib
@@ -228,6 +230,20 @@ def route_backward(logits: np.ndarray, topk_ids: np.ndarray, grad_topk_w: np.nda
     out = np.empty((T, E), np.float64)
     _check(_load().oracle_route_backward(_p(x), _p(ids), T, E, k, int(bool(norm_topk_prob)),
                                          _p(g), _p(out)), "route_backward")
+    return out
+
+
+def route_grouped_backward(scores: np.ndarray, topk_ids: np.ndarray, grad_topk_w: np.ndarray,
+                           renormalize: bool = False) -> np.ndarray:
+    """Gradient of the group-limited selection's weights w.r.t. the scores -> [T, E] f64."""
+    x = _c(scores, np.float32)
+    ids = _c(topk_ids, np.int32)
+    g = _c(grad_topk_w, np.float64)
+    T, E = x.shape
+    k = ids.shape[1]
+    out = np.empty((T, E), np.float64)
+    _check(_load().oracle_route_grouped_backward(_p(x), _p(ids), T, E, k, int(bool(renormalize)),
+                                                 _p(g), _p(out)), "route_grouped_backward")
     return out
 
 

@@ -736,3 +736,40 @@ int oracle_expert_wgrad_entries(int32_t dt, const void *hidden, const void *w13,
     }
     return fail ? ORACLE_EINVAL : ORACLE_OK;
 }
+
+/*
+ * Backward of the weights of oracle_route_grouped, by the chain rule (the
+ * pages give only the forward).  The weights are the selected experts'
+ * scores (the correction bias moves only the selection, which is piecewise
+ * constant and passes no gradient), divided by their sum S when
+ * renormalize != 0.  With g = grad_topk_w:
+ *   plain:        grad_scores[e_j] = g_j
+ *   renormalized: grad_scores[e_j] = (g_j - sum_i w_i g_i) / S
+ * and 0 for every unselected expert.  topk_ids are the forward's (valid and
+ * distinct within a row).
+ */
+int oracle_route_grouped_backward(const float *scores, const int32_t *topk_ids, int64_t T,
+                                  int32_t E, int32_t k, int32_t renormalize,
+                                  const double *grad_topk_w, double *grad_scores)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t *ids = topk_ids + t * k;
+        const double *g = grad_topk_w + t * k;
+        double *out = grad_scores + t * E;
+        for (int32_t e = 0; e < E; ++e)
+            out[e] = 0.0;
+        double S = 0.0, dot = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            if (ids[j] < 0 || ids[j] >= E)
+                return ORACLE_EINVAL;
+            S += (double)scores[t * E + ids[j]];
+        }
+        for (int32_t j = 0; j < k; ++j)
+            dot += (double)scores[t * E + ids[j]] / S * g[j];
+        for (int32_t j = 0; j < k; ++j)
+            out[ids[j]] = renormalize ? (g[j] - dot) / S : g[j];
+    }
+    return ORACLE_OK;
+}

@@ -209,3 +209,46 @@ def test_route_backward_invariants(norm):
         np.put_along_axis(sel, ids, True, axis=1)
         assert np.all(grad[~sel] == 0)
         np.testing.assert_allclose(same, 0.0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Group-limited selection backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("method", ["group_limited_greedy", "noaux_tc"])
+def test_route_grouped_backward_matches_finite_differences(method, renorm):
+    g = np.random.Generator(np.random.PCG64(31 + renorm))
+    T, E, k, ng, tg = 6, 16, 3, 4, 2
+    scores = (1.0 / (1.0 + np.exp(-g.standard_normal((T, E))))).astype(np.float32)
+    bias = (0.1 * g.standard_normal(E)).astype(np.float32)
+    w, ids = oracle.route_grouped(scores, k, ng, tg, method, bias=bias, renormalize=renorm)
+    gw = g.standard_normal((T, k))
+    grad = oracle.route_grouped_backward(scores, ids, gw, renorm)
+
+    def f(a):
+        w2, ids2 = oracle.route_grouped(a, k, ng, tg, method, bias=bias, renormalize=renorm)
+        assert np.array_equal(ids2, ids)  # the selection is fixed under tiny steps
+        return float(np.sum(w2 * gw))
+
+    for idx in np.ndindex(scores.shape):
+        fd = _fd(f, scores, idx, h=2.0 ** -14)
+        assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(grad[idx])), idx
+
+
+def test_route_grouped_backward_invariants():
+    g = np.random.Generator(np.random.PCG64(33))
+    T, E, k = 8, 32, 4
+    scores = (1.0 / (1.0 + np.exp(-g.standard_normal((T, E))))).astype(np.float32)
+    w, ids = oracle.route_grouped(scores, k, 8, 3, "noaux_tc", bias=np.zeros(E, np.float32),
+                                  renormalize=True)
+    gw = g.standard_normal((T, k))
+    grad = oracle.route_grouped_backward(scores, ids, gw, True)
+    # Renormalised weights are scale invariant, so the gradient is orthogonal
+    # to the scores (Euler); unselected experts get exactly zero.
+    np.testing.assert_allclose(np.sum(grad * scores, axis=1), 0.0, atol=1e-12)
+    sel = np.zeros((T, E), bool)
+    np.put_along_axis(sel, ids, True, axis=1)
+    assert np.all(grad[~sel] == 0)
+    plain = oracle.route_grouped_backward(scores, ids, gw, False)
+    np.testing.assert_array_equal(np.take_along_axis(plain, ids, axis=1), gw)
