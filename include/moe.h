@@ -18,6 +18,7 @@
  *   moe_expert_ffn_decode     the same for T <= MOE_DECODE_MAX_T, streaming only
  *                             the selected experts' weights
  *   moe_route_backward        gradient of the gating softmax weights w.r.t. the logits
+ *   moe_route_grouped_backward gradient of the group-limited weights w.r.t. the scores
  *   moe_expert_ffn_backward   gradients of moe_expert_ffn w.r.t. hidden, w13, w2
  *                             and the routing weights
  *
@@ -342,6 +343,27 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
                                 const float *topk_w, const float *grad_topk_w, int64_t T,
                                 int32_t E, int32_t k, int32_t norm_topk_prob,
                                 float *grad_logits, void *stream);
+
+/*
+ * moe_route_grouped_backward -- backward of moe_route_grouped's weights.
+ * The chain rule applied to [mlc] group_limited_greedy_topk (the pages give
+ * only the forward).  The weights are the selected scores, divided by their
+ * sum S when renormalize != 0; the correction bias and the group masking
+ * only move the selection, which passes no gradient.
+ *
+ * scores      [T, E] float32 in: the forward's scores.
+ * topk_ids    [T, k] int32 in, topk_w [T, k] float32 in: the forward's outputs
+ *             (ids valid and distinct within a row).
+ * grad_topk_w [T, k] float32 in.
+ * grad_scores [T, E] float32 out: grad[e_j] = grad_topk_w[j], or with
+ *             renormalize (grad_topk_w[j] - sum_i topk_w[i] grad_topk_w[i]) / S;
+ *             0 for unselected experts.
+ * Requires k <= E.  Pointers 4-byte aligned.
+ */
+moe_status_t moe_route_grouped_backward(const float *scores, const int32_t *topk_ids,
+                                        const float *topk_w, const float *grad_topk_w, int64_t T,
+                                        int32_t E, int32_t k, int32_t renormalize,
+                                        float *grad_scores, void *stream);
 
 /*
  * moe_expert_ffn_backward -- backward of moe_expert_ffn.

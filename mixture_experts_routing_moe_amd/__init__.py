@@ -19,11 +19,13 @@ from .moe import (  # noqa: F401
     moe_indices_to_multihot,
     moe_indices_to_multihot_backward,
     moe_layer,
+    moe_layer_backward,
     moe_multihot_to_indices,
     moe_route,
     moe_route_align,
     moe_route_align_fused,
     moe_route_backward,
+    moe_route_grouped_backward,
     moe_route_grouped,
     moe_route_multihot,
     moe_route_multihot_fused,

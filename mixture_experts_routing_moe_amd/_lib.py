@@ -62,6 +62,7 @@ SIGNATURES = {
                            _vp]),
     "moe_combine": (_st, [_st, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_route_backward": (_st, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "moe_route_grouped_backward": (_st, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "moe_expert_ffn_backward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_backward": (_st, [_st, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                       _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,

@@ -505,7 +505,51 @@ __global__ __launch_bounds__(256) void route_backward_kernel(
     }
 }
 
+
+// Group-limited selection backward, one wave per row: the weights are the
+// selected scores (over their sum S when renormalised), so grad[e_j] = g_j,
+// or (g_j - sum_i w_i g_i) / S; 0 for unselected experts.  The bias moves
+// only the selection.
+__global__ __launch_bounds__(256) void route_grouped_backward_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ ids,
+    const float *__restrict__ topk_w, const float *__restrict__ gw, int64_t T, int E, int k,
+    int renorm, float *__restrict__ out) {
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= T) return;
+    const float *x = scores + t * E;
+    const int my_id = lane < k ? ids[t * k + lane] : -1;
+    const float my_g = lane < k ? gw[t * k + lane] : 0.f;
+    const float my_w = lane < k ? topk_w[t * k + lane] : 0.f;
+    const float dot = wave_sum_f(my_w * my_g);
+    const float S = wave_sum_f(my_id >= 0 ? x[my_id] : 0.f);
+    for (int e0 = 0; e0 < E; e0 += kWave) {  // same trip count on every lane
+        const int e = e0 + lane;
+        int j_sel = -1;
+        float ge = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int idj = __shfl(my_id, j);
+            const float gj = __shfl(my_g, j);
+            if (idj == e) {
+                j_sel = j;
+                ge = gj;
+            }
+        }
+        if (e < E) out[t * E + e] = j_sel < 0 ? 0.f : renorm ? (ge - dot) / S : ge;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_route_grouped_backward(const float *scores, const int32_t *ids, const float *w,
+                                         const float *gw, int64_t T, int E, int k, int renorm,
+                                         float *out, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int rows = 256 / kWave;
+    hipLaunchKernelGGL(route_grouped_backward_kernel, dim3((unsigned)((T + rows - 1) / rows)),
+                       dim3(256), 0, s, scores, ids, w, gw, T, E, k, renorm, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_route_backward(const float *logits, const int32_t *ids, const float *w,
                                  const float *gw, int64_t T, int E, int k, int norm, float *out,

@@ -465,6 +465,23 @@ moe_status_t moe_route_backward(const float *logits, const int32_t *topk_ids,
                       fn);
 }
 
+moe_status_t moe_route_grouped_backward(const float *scores, const int32_t *topk_ids,
+                                        const float *topk_w, const float *grad_topk_w, int64_t T,
+                                        int32_t E, int32_t k, int32_t renormalize,
+                                        float *grad_scores, void *stream) {
+    const char *fn = "moe_route_grouped_backward";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
+    if (T == 0) return MOE_OK;
+    CHECK(scores && topk_ids && topk_w && grad_topk_w && grad_scores, MOE_ERR_INVALID_ARG,
+          "%s: null pointer", fn);
+    return hip_status(moe::launch_route_grouped_backward(scores, topk_ids, topk_w, grad_topk_w, T,
+                                                         E, k, renormalize ? 1 : 0, grad_scores,
+                                                         static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 size_t moe_expert_ffn_backward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
                                               int32_t k) {
     if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;

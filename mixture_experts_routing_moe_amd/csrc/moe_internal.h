@@ -305,6 +305,10 @@ hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const floa
                           const int32_t *slot_to_sorted, int64_t T, int H, int k, void *out,
                           hipStream_t s);
 
+// Backward of the group-limited selection's weights (one wave per row).
+hipError_t launch_route_grouped_backward(const float *scores, const int32_t *ids, const float *w,
+                                         const float *gw, int64_t T, int E, int k, int renorm,
+                                         float *out, hipStream_t s);
 // Backward of the gating softmax (one wave per row).
 hipError_t launch_route_backward(const float *logits, const int32_t *ids, const float *w,
                                  const float *gw, int64_t T, int E, int k, int norm, float *out,

@@ -389,6 +389,21 @@ def moe_route_backward(logits, topk_ids, topk_w, grad_topk_w, norm_topk_prob: bo
     return grad_logits
 
 
+def moe_route_grouped_backward(scores, topk_ids, topk_w, grad_topk_w, renormalize: bool = False,
+                               grad_scores=None):
+    """Gradient of moe_route_grouped's weights w.r.t. the scores -> [T, E] float32."""
+    T, E = scores.shape
+    k = topk_ids.shape[1]
+    if grad_scores is None:
+        grad_scores = torch.empty((T, E), dtype=torch.float32, device=scores.device)
+    _dev(scores, topk_ids, topk_w, grad_topk_w, grad_scores)
+    check(lib().moe_route_grouped_backward(_ptr(scores), _ptr(topk_ids), _ptr(topk_w),
+                                           _ptr(grad_topk_w), T, E, k, int(bool(renormalize)),
+                                           _ptr(grad_scores), _stream()),
+          "moe_route_grouped_backward")
+    return grad_scores
+
+
 def moe_expert_ffn_backward_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
     return int(lib().moe_expert_ffn_backward_workspace_size(T, H, I, E, k))
 
@@ -420,3 +435,14 @@ def moe_expert_ffn_backward(hidden, w13, w2, topk_w, aligned: dict, grad_out, ou
         _ptr(out["grad_topk_w"]), _ptr(workspace), workspace.numel(), _stream()),
         "moe_expert_ffn_backward")
     return out
+
+
+def moe_layer_backward(hidden, w13, w2, logits, topk_w, topk_ids, aligned: dict, grad_out,
+                       norm_topk_prob: bool = True):
+    """Backward of moe_layer from its saved routing: moe_expert_ffn_backward then
+    moe_route_backward.  Returns grad_hidden, grad_w13, grad_w2, grad_topk_w and
+    grad_logits (float32)."""
+    g = moe_expert_ffn_backward(hidden, w13, w2, topk_w, aligned, grad_out)
+    g["grad_logits"] = moe_route_backward(logits, topk_ids, topk_w, g["grad_topk_w"],
+                                          norm_topk_prob)
+    return g

@@ -333,3 +333,58 @@ def test_ffn_backward_segment_boundaries(counts):
         else:  # each expert's slice on its own scale
             check_grad(f"grad_w13[{e}]", got["grad_w13"][e], ref["grad_w13"][e])
             check_grad(f"grad_w2[{e}]", got["grad_w2"][e], ref["grad_w2"][e])
+
+
+# --------------------------------------------------------------------------
+# Group-limited selection backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", sorted(mi.GROUPED))
+def test_route_grouped_backward_workloads(name):
+    """Full-size group-limited workloads: float32 throughout, max |err| <= 1e-5 x max."""
+    w = mi.GROUPED[name]
+    scores = mi.grouped_scores(w)
+    bias = mi.correction_bias(w)
+    sd = dev(scores)
+    bd = None if bias is None else dev(bias)
+    tw, tids = moe.moe_route_grouped(sd, w.k, w.n_group, w.topk_group, w.method, bd, w.renorm)
+    ow, oids = oracle.route_grouped(scores, w.k, w.n_group, w.topk_group, w.method, bias=bias,
+                                    renormalize=w.renorm)
+    np.testing.assert_array_equal(tids.cpu().numpy(), oids)
+    g = np.random.Generator(np.random.PCG64(w.wid)).standard_normal((w.T, w.k)).astype(np.float32)
+    got = moe.moe_route_grouped_backward(sd, tids, tw, dev(g), w.renorm).cpu().numpy()
+    ref = oracle.route_grouped_backward(scores, oids, g.astype(np.float64), w.renorm)
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+    sel = np.zeros(ref.shape, bool)
+    np.put_along_axis(sel, oids, True, axis=1)
+    assert np.all(got[~sel] == 0)
+
+
+@pytest.mark.parametrize("T,E,k,renorm", [(5, 130, 6, True), (77, 8, 8, False), (3, 256, 64, True)])
+def test_route_grouped_backward_shapes(T, E, k, renorm):
+    g = np.random.Generator(np.random.PCG64(T + E + k))
+    scores = (1.0 / (1.0 + np.exp(-g.standard_normal((T, E))))).astype(np.float32)
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = np.take_along_axis(scores, ids, axis=1).astype(np.float64)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    gw = g.standard_normal((T, k)).astype(np.float32)
+    got = moe.moe_route_grouped_backward(dev(scores), dev(ids), dev(w.astype(np.float32)),
+                                         dev(gw), renorm).cpu().numpy()
+    ref = oracle.route_grouped_backward(scores, ids, gw.astype(np.float64), renorm)
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_layer_backward_chains_the_two_calls():
+    """moe_layer_backward = moe_expert_ffn_backward then moe_route_backward."""
+    T, H, I, E, k = 64, 128, 128, 8, 2
+    x, w13, w2, _, _, dy = _rand_case(91, T, H, I, E, k)
+    logits = np.random.Generator(np.random.PCG64(92)).standard_normal((T, E)).astype(np.float32)
+    xd, w13d, w2d, dyd = dev_bf16(x), dev_bf16(w13), dev_bf16(w2), dev_bf16(dy)
+    out, tw, tids, a = moe.moe_layer(xd, w13d, w2d, dev(logits), k, True, decode=False)
+    g = moe.moe_layer_backward(xd, w13d, w2d, dev(logits), tw, tids, a, dyd, True)
+    ref = moe.moe_expert_ffn_backward(xd, w13d, w2d, tw, a, dyd)
+    for n in ref:
+        assert torch.equal(g[n], ref[n]), n
+    rl = moe.moe_route_backward(dev(logits), tids, tw, ref["grad_topk_w"], True)
+    assert torch.equal(g["grad_logits"], rl)
