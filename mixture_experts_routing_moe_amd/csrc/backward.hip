@@ -1,4 +1,5 @@
-// Backward of the MoE layer: gating softmax and expert FFN.
+// Backward of the MoE layer: gating softmax, group-limited selection weights
+// and expert FFN (bfloat16 on the matrix cores; float32 for small layers).
 //
 // The pages describe the forward (the multihot converters' backward aside,
 // which moe_multihot_to_indices already is); these kernels apply the chain
@@ -47,7 +48,7 @@ constexpr int kWT = MOE_WGRAD_TILE;  // wgrad tile rows and columns (128 or 256)
 constexpr int kBK = MOE_WGRAD_BK;       // k per LDS stage (MFMA k-steps of 32)
 constexpr int kNS = MOE_WGRAD_STAGES;   // LDS stages (1 or 2)
 constexpr int kSegPad = kBK;      // positions per padded segment unit: whole k-tiles
-constexpr int kLdsW = kBK + 8;    // bf16 per LDS row: 144 bytes, 16-byte aligned rows
+constexpr int kLdsW = kBK + 8;    // bf16 per LDS row: 16-byte aligned, rows staggered over banks
 constexpr int kCPR = kBK / 8;                  // 16-byte chunks per tile row
 static_assert(kBK % 32 == 0 && (kNS == 1 || kNS == 2) && (kWT == 128 || kWT == 256),
               "whole MFMA k-steps, one or two stages, 128 or 256 tiles");
