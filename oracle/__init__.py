@@ -51,6 +51,7 @@ def _load():
                                           vp, i64, vp, i32]
         lib.oracle_route_backward.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
         lib.oracle_route_grouped_backward.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
+        lib.oracle_router_backward.argtypes = [i32, vp, vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_expert_ffn_backward.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
                                                    i32, i32, vp, i64, vp, vp, vp, vp, i32]
         lib.oracle_expert_wgrad_entries.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, i32,
@@ -59,7 +60,7 @@ def _load():
         for f in (lib.oracle_route, lib.oracle_router_logits, lib.oracle_route_grouped, lib.oracle_moe_cumsum, lib.oracle_align,
                   lib.oracle_indices_to_multihot, lib.oracle_multihot_to_indices,
                   lib.oracle_expert_ffn, lib.oracle_route_backward,
-                  lib.oracle_route_grouped_backward,
+                  lib.oracle_route_grouped_backward, lib.oracle_router_backward,
                   lib.oracle_expert_ffn_backward, lib.oracle_expert_wgrad_entries):
             f.restype = ctypes.c_int
         _lib = lib
@@ -245,6 +246,23 @@ def route_grouped_backward(scores: np.ndarray, topk_ids: np.ndarray, grad_topk_w
     _check(_load().oracle_route_grouped_backward(_p(x), _p(ids), T, E, k, int(bool(renormalize)),
                                                  _p(g), _p(out)), "route_grouped_backward")
     return out
+
+
+def router_backward(hidden: np.ndarray, w_gate: np.ndarray, grad_logits: np.ndarray,
+                    dtype: str):
+    """Backward of router_logits -> (grad_hidden [T, H], grad_w_gate [E, H]) float64."""
+    dt = {"f32": 0, "bf16": 1}[dtype]
+    npdt = np.float32 if dt == 0 else np.uint16
+    x = _c(hidden, npdt)
+    w = _c(w_gate, npdt)
+    g = _c(grad_logits, np.float64)
+    T, H = x.shape
+    E = w.shape[0]
+    gh = np.empty((T, H), np.float64)
+    gw = np.empty((E, H), np.float64)
+    _check(_load().oracle_router_backward(dt, _p(x), _p(w), _p(g), T, H, E, _p(gh), _p(gw)),
+           "router_backward")
+    return gh, gw
 
 
 def _ffn_operands(hidden, w13, w2, topk_w, topk_ids, grad_out, dtype):

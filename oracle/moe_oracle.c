@@ -773,3 +773,33 @@ int oracle_route_grouped_backward(const float *scores, const int32_t *topk_ids, 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Backward of oracle_router_logits (logits = hidden . w_gate^T), by the chain
+ * rule: with g = grad_logits [T, E],
+ *   grad_hidden[t][h] = sum over e of g[t][e] w_gate[e][h]
+ *   grad_w_gate[e][h] = sum over t of g[t][e] hidden[t][h]
+ * in double, sums in ascending e and t.  dt as in oracle_router_logits.
+ */
+int oracle_router_backward(int32_t dt, const void *hidden, const void *w_gate,
+                           const double *grad_logits, int64_t T, int32_t H, int32_t E,
+                           double *grad_hidden, double *grad_w_gate)
+{
+    if (T < 0 || H < 1 || E < 1 || (dt != 0 && dt != 1))
+        return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t e = 0; e < E; ++e)
+                acc += grad_logits[t * E + e] * load_elem(dt, w_gate, (int64_t)e * H + h);
+            grad_hidden[t * H + h] = acc;
+        }
+    for (int32_t e = 0; e < E; ++e)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                acc += grad_logits[t * E + e] * load_elem(dt, hidden, t * H + h);
+            grad_w_gate[(int64_t)e * H + h] = acc;
+        }
+    return ORACLE_OK;
+}

@@ -252,3 +252,30 @@ def test_route_grouped_backward_invariants():
     assert np.all(grad[~sel] == 0)
     plain = oracle.route_grouped_backward(scores, ids, gw, False)
     np.testing.assert_array_equal(np.take_along_axis(plain, ids, axis=1), gw)
+
+
+# --------------------------------------------------------------------------
+# Router GEMM backward
+# --------------------------------------------------------------------------
+
+def test_router_backward_matches_finite_differences_and_matmul():
+    g = np.random.Generator(np.random.PCG64(41))
+    T, H, E = 5, 8, 6
+    x = g.standard_normal((T, H)).astype(np.float32)
+    wg = (g.standard_normal((E, H)) / math.sqrt(H)).astype(np.float32)
+    gl = g.standard_normal((T, E))
+    gh, gw = oracle.router_backward(x, wg, gl, "f32")
+
+    def f_x(a):
+        return float(np.sum(oracle.router_logits(a, wg, "f32") * gl))
+
+    def f_w(a):
+        return float(np.sum(oracle.router_logits(x, a, "f32") * gl))
+
+    for idx in np.ndindex(x.shape):
+        assert abs(_fd(f_x, x, idx) - gh[idx]) <= 1e-7, idx
+    for idx in np.ndindex(wg.shape):
+        assert abs(_fd(f_w, wg, idx) - gw[idx]) <= 1e-7, idx
+    # the plain definitions as float64 library products
+    np.testing.assert_allclose(gh, gl @ wg.astype(np.float64), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gw, gl.T @ x.astype(np.float64), rtol=1e-12, atol=1e-13)
