@@ -19,6 +19,7 @@
  *                             the selected experts' weights
  *   moe_route_backward        gradient of the gating softmax weights w.r.t. the logits
  *   moe_route_grouped_backward gradient of the group-limited weights w.r.t. the scores
+ *   moe_router_backward       gradients of the gate's hidden states and weights
  *   moe_expert_ffn_backward   gradients of moe_expert_ffn w.r.t. hidden, w13, w2
  *                             and the routing weights
  *
@@ -364,6 +365,27 @@ moe_status_t moe_route_grouped_backward(const float *scores, const int32_t *topk
                                         const float *topk_w, const float *grad_topk_w, int64_t T,
                                         int32_t E, int32_t k, int32_t renormalize,
                                         float *grad_scores, void *stream);
+
+/*
+ * moe_router_backward -- backward of moe_router_route's gate (the linear
+ * layer logits = hidden . w_gate^T; the top-k part's backward is
+ * moe_route_backward).  The chain rule on the [p6] linear-layer convention:
+ *   grad_hidden [T, H] float32 out = grad_logits . w_gate
+ *   grad_w_gate [E, H] float32 out = grad_logits^T . hidden
+ * hidden [T, H] and w_gate [E, H] bfloat16 (dt must be MOE_BF16);
+ * grad_logits [T, E] float32 (e.g. from moe_route_backward).  float32
+ * arithmetic, sums over e and over t in ascending order (t in chunks of 256
+ * whose partial sums are added in chunk order): deterministic.
+ * workspace >= moe_router_backward_workspace_size(T, H, E) bytes
+ * (ceil(T / 256) * E * H * 4), 16-byte aligned, clobbered.  Requires
+ * H % 64 == 0; hidden, w_gate and the gradients 16-byte aligned.  T = 0
+ * enqueues nothing (grad_w_gate is then left as it was).
+ */
+size_t moe_router_backward_workspace_size(int64_t T, int32_t H, int32_t E);
+moe_status_t moe_router_backward(moe_dtype_t dt, const void *hidden, const void *w_gate,
+                                 const float *grad_logits, int64_t T, int32_t H, int32_t E,
+                                 float *grad_hidden, float *grad_w_gate, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * moe_expert_ffn_backward -- backward of moe_expert_ffn.

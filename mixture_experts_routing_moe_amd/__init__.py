@@ -29,5 +29,6 @@ from .moe import (  # noqa: F401
     moe_route_grouped,
     moe_route_multihot,
     moe_route_multihot_fused,
+    moe_router_backward,
     moe_router_route,
 )

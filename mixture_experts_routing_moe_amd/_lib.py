@@ -63,6 +63,8 @@ SIGNATURES = {
     "moe_combine": (_st, [_st, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_route_backward": (_st, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "moe_route_grouped_backward": (_st, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "moe_router_backward_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_router_backward": (_st, [_st, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_backward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_backward": (_st, [_st, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                       _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,

@@ -155,6 +155,46 @@ moe_status_t moe_router_route(moe_dtype_t dt, const void *hidden, const void *w_
                       fn);
 }
 
+size_t moe_router_backward_workspace_size(int64_t T, int32_t H, int32_t E) {
+    if (T <= 0 || H < 1 || E < 1) return 0;
+    return moe::router_backward_scratch_bytes(T, H, E);
+}
+
+moe_status_t moe_router_backward(moe_dtype_t dt, const void *hidden, const void *w_gate,
+                                 const float *grad_logits, int64_t T, int32_t H, int32_t E,
+                                 float *grad_hidden, float *grad_w_gate, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    const char *fn = "moe_router_backward";
+    CHECK(T >= 0, MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+    CHECK(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, %d]", fn,
+          E, MOE_MAX_EXPERTS);
+    CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn,
+          (int)dt);
+    CHECK(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: only bf16 hidden / w_gate", fn);
+    CHECK(H >= 1, MOE_ERR_INVALID_ARG, "%s: H = %d < 1", fn, H);
+    CHECK(H % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: H = %d must be a multiple of 64", fn, H);
+    CHECK(T / 256 < 65535, MOE_ERR_UNSUPPORTED, "%s: T = %lld exceeds the launch grid", fn,
+          (long long)T);
+    if (T == 0) return MOE_OK;
+    CHECK(hidden && w_gate && grad_logits && grad_hidden && grad_w_gate, MOE_ERR_INVALID_ARG,
+          "%s: null pointer", fn);
+    CHECK(aligned16(hidden) && aligned16(w_gate) && aligned16(grad_hidden) &&
+              aligned16(grad_w_gate),
+          MOE_ERR_INVALID_ARG, "%s: hidden, w_gate and the gradients must be 16-byte aligned",
+          fn);
+    const size_t need = moe::router_backward_scratch_bytes(T, H, E);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    CHECK(aligned16(workspace), MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned",
+          fn);
+    return hip_status(moe::launch_router_backward(static_cast<const uint16_t *>(hidden),
+                                                  static_cast<const uint16_t *>(w_gate),
+                                                  grad_logits, T, H, E, grad_hidden,
+                                                  grad_w_gate, workspace,
+                                                  static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 moe_status_t moe_route_grouped(const float *scores, const float *e_score_correction_bias,
                                int64_t T, int32_t E, int32_t k, int32_t n_group,
                                int32_t topk_group, int32_t method, int32_t renormalize,

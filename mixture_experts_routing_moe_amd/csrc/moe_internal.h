@@ -257,6 +257,12 @@ hipError_t launch_router_route(const uint16_t *hidden, const uint16_t *wg, int64
                                int E, int k, int norm, float *logits, float *w, int32_t *ids,
                                hipStream_t s);
 
+// Gate backward: grad_hidden = g . w_gate, grad_w_gate = g^T . hidden (f32).
+size_t router_backward_scratch_bytes(int64_t T, int H, int E);
+hipError_t launch_router_backward(const uint16_t *hidden, const uint16_t *wg, const float *g,
+                                  int64_t T, int H, int E, float *gh, float *gw, void *ws,
+                                  hipStream_t s);
+
 int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,

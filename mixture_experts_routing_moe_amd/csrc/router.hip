@@ -186,7 +186,138 @@ hipError_t launch_mc(const uint16_t *hidden, const uint16_t *wg, int64_t T, int 
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward of the gate (logits = hidden . w_gate^T), float32 arithmetic on
+// the bf16 operands: grad_hidden = g . w_gate, grad_w_gate = g^T . hidden with
+// g = grad_logits [T, E].  E is small (tens of experts), so these are
+// streaming kernels, not matrix-core products.
+// ---------------------------------------------------------------------------
+
+constexpr int kBwdTok = 8;      // tokens per grad_hidden block
+constexpr int kBwdChunk = 256;  // tokens per grad_w_gate partial plane
+
+__device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = bf16_bits_to_f32((uint16_t)w[j]);
+        f[2 * j + 1] = bf16_bits_to_f32((uint16_t)(w[j] >> 16));
+    }
+}
+
+// grad_hidden[t][h] = sum over e (ascending) of g[t][e] w_gate[e][h].  Block:
+// kBwdTok tokens (their g rows staged in LDS); thread: 8 consecutive h.
+__global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t *__restrict__ wg,
+                                                        const float *__restrict__ g, int64_t T,
+                                                        int H, int E, float *__restrict__ gh) {
+    extern __shared__ float sg[];  // [kBwdTok][E]
+    const int64_t t0 = (int64_t)blockIdx.x * kBwdTok;
+    for (int i = threadIdx.x; i < kBwdTok * E; i += blockDim.x) {
+        const int tt = i / E, e = i % E;
+        sg[i] = t0 + tt < T ? g[(t0 + tt) * E + e] : 0.f;
+    }
+    __syncthreads();
+    for (int hc = threadIdx.x; hc < H / 8; hc += blockDim.x) {
+        float acc[kBwdTok][8];
+#pragma unroll
+        for (int tt = 0; tt < kBwdTok; ++tt)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[tt][j] = 0.f;
+        for (int e = 0; e < E; ++e) {
+            float wf[8];
+            unpack8(*reinterpret_cast<const uint4 *>(wg + (int64_t)e * H + 8 * hc), wf);
+#pragma unroll
+            for (int tt = 0; tt < kBwdTok; ++tt) {
+                const float ge = sg[tt * E + e];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[tt][j] = fmaf(ge, wf[j], acc[tt][j]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kBwdTok; ++tt) {
+            if (t0 + tt >= T) break;
+            float *o = gh + (t0 + tt) * H + 8 * hc;
+            *reinterpret_cast<f32x4 *>(o) = f32x4{acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
+            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{acc[tt][4], acc[tt][5], acc[tt][6], acc[tt][7]};
+        }
+    }
+}
+
+// part[c][e][h] = sum over the tokens t of chunk c (ascending) of
+// g[t][e] hidden[t][h].  Block (h block, chunk c): 32 h-chunks of 8 x 8
+// groups of 8 experts (groups beyond the eighth loop).
+__global__ __launch_bounds__(256) void router_dw_partial_kernel(const uint16_t *__restrict__ x,
+                                                                const float *__restrict__ g,
+                                                                int64_t T, int H, int E,
+                                                                float *__restrict__ part) {
+    const int hc = blockIdx.x * 32 + (threadIdx.x & 31);
+    if (hc >= H / 8) return;
+    const int64_t t0 = (int64_t)blockIdx.y * kBwdChunk;
+    const int64_t t1 = min(T, t0 + kBwdChunk);
+    for (int eg = threadIdx.x >> 5; eg * 8 < E; eg += 8) {
+        float acc[8][8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+        for (int64_t t = t0; t < t1; ++t) {
+            float xf[8];
+            unpack8(*reinterpret_cast<const uint4 *>(x + t * H + 8 * hc), xf);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int e = eg * 8 + j;
+                const float ge = e < E ? g[t * E + e] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(ge, xf[i], acc[j][i]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = eg * 8 + j;
+            if (e >= E) break;
+            float *o = part + ((int64_t)blockIdx.y * E + e) * H + 8 * hc;
+            *reinterpret_cast<f32x4 *>(o) = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
+        }
+    }
+}
+
+// grad_w_gate[e][h] = sum over chunks c = 0, 1, ... of part[c][e][h].
+__global__ __launch_bounds__(256) void router_dw_sum_kernel(const float *__restrict__ part,
+                                                            int nc, int64_t n4,
+                                                            float *__restrict__ gw) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 acc = reinterpret_cast<const f32x4 *>(part)[i];
+    for (int c = 1; c < nc; ++c) acc += reinterpret_cast<const f32x4 *>(part)[(int64_t)c * n4 + i];
+    reinterpret_cast<f32x4 *>(gw)[i] = acc;
+}
 }  // namespace
+
+size_t router_backward_scratch_bytes(int64_t T, int H, int E) {
+    const int64_t nc = (T + kBwdChunk - 1) / kBwdChunk;
+    return (size_t)nc * E * H * 4;
+}
+
+hipError_t launch_router_backward(const uint16_t *hidden, const uint16_t *wg, const float *g,
+                                  int64_t T, int H, int E, float *gh, float *gw, void *ws,
+                                  hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    hipError_t err;
+    hipLaunchKernelGGL(router_dx_kernel, dim3((unsigned)((T + kBwdTok - 1) / kBwdTok)), dim3(256),
+                       kBwdTok * E * sizeof(float), s, wg, g, T, H, E, gh);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int nc = (int)((T + kBwdChunk - 1) / kBwdChunk);
+    float *part = static_cast<float *>(ws);
+    hipLaunchKernelGGL(router_dw_partial_kernel, dim3((unsigned)((H / 8 + 31) / 32), (unsigned)nc),
+                       dim3(256), 0, s, hidden, g, T, H, E, part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t n4 = (int64_t)E * H / 4;
+    hipLaunchKernelGGL(router_dw_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       part, nc, n4, gw);
+    return hipGetLastError();
+}
 
 hipError_t launch_router_route(const uint16_t *hidden, const uint16_t *wg, int64_t T, int H,
                                int E, int k, int norm, float *logits, float *w, int32_t *ids,

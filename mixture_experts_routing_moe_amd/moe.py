@@ -404,6 +404,25 @@ def moe_route_grouped_backward(scores, topk_ids, topk_w, grad_topk_w, renormaliz
     return grad_scores
 
 
+def moe_router_backward(hidden, w_gate, grad_logits, out=None, workspace=None):
+    """Backward of the gate logits = hidden . w_gate^T -> (grad_hidden [T, H],
+    grad_w_gate [E, H]) float32."""
+    T, H = hidden.shape
+    E = w_gate.shape[0]
+    if out is None:
+        out = (torch.empty((T, H), dtype=torch.float32, device=hidden.device),
+               torch.empty((E, H), dtype=torch.float32, device=hidden.device))
+    if workspace is None:
+        workspace = torch.empty(max(1, int(lib().moe_router_backward_workspace_size(T, H, E))),
+                                dtype=torch.uint8, device=hidden.device)
+    _dev(hidden, w_gate, grad_logits, *out, workspace)
+    check(lib().moe_router_backward(_dtype_code(hidden), _ptr(hidden), _ptr(w_gate),
+                                    _ptr(grad_logits), T, H, E, _ptr(out[0]), _ptr(out[1]),
+                                    _ptr(workspace), workspace.numel(), _stream()),
+          "moe_router_backward")
+    return out
+
+
 def moe_expert_ffn_backward_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
     return int(lib().moe_expert_ffn_backward_workspace_size(T, H, I, E, k))
 

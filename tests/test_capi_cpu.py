@@ -323,3 +323,24 @@ def test_ffn_backward_validation(lib):
     assert fb(wsb=need - 1) == W
     assert fb(ws=None) == W
     assert fb(T=0, x=None, dx=None, ws=None, wsb=0) == _lib.MOE_OK
+
+
+def test_router_backward_validation(lib):
+    I, U, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+    B = _lib.MOE_BF16
+    T, H, E = 300, 128, 64
+    need = lib.moe_router_backward_workspace_size(T, H, E)
+    assert need == 2 * E * H * 4  # two chunks of 256 tokens
+    assert lib.moe_router_backward_workspace_size(0, H, E) == 0
+
+    def rb(dt=B, T=T, H=H, E=E, x=FAKE, gh=FAKE, ws=FAKE, wsb=need):
+        return lib.moe_router_backward(dt, x, FAKE, FAKE, T, H, E, gh, FAKE, ws, wsb, None)
+
+    assert rb(dt=_lib.MOE_F32) == U
+    assert rb(H=96) == U
+    assert rb(E=0) == I
+    assert rb(E=2000) == I
+    assert rb(x=None) == I
+    assert rb(gh=ctypes.c_void_p(0x1008)) == I
+    assert rb(wsb=need - 1) == W
+    assert rb(T=0, x=None, gh=None, ws=None, wsb=0) == _lib.MOE_OK

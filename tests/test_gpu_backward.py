@@ -388,3 +388,38 @@ def test_layer_backward_chains_the_two_calls():
         assert torch.equal(g[n], ref[n]), n
     rl = moe.moe_route_backward(dev(logits), tids, tw, ref["grad_topk_w"], True)
     assert torch.equal(g["grad_logits"], rl)
+
+
+# --------------------------------------------------------------------------
+# Router GEMM backward
+# --------------------------------------------------------------------------
+
+def _router_bwd_check(x, wg, gl):
+    gh, gw = moe.moe_router_backward(dev_bf16(x), dev_bf16(wg), dev(gl))
+    rh, rw = oracle.router_backward(x, wg, gl.astype(np.float64), "bf16")
+    # float32 sums of exact bf16 x float32 products: relative error ~ E or T ulps
+    for name, got, ref in (("grad_hidden", gh, rh), ("grad_w_gate", gw, rw)):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), name
+        assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max(), name
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 64, 1), (300, 128, 64), (77, 192, 130), (513, 64, 8)])
+def test_router_backward_shapes(T, H, E):
+    g = np.random.Generator(np.random.PCG64(T + H + E))
+    x = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    wg = mi.f32_to_bf16_bits((g.standard_normal((E, H)) / math.sqrt(H)).astype(np.float32))
+    gl = g.standard_normal((T, E)).astype(np.float32)
+    _router_bwd_check(x, wg, gl)
+
+
+@pytest.mark.parametrize("name", ["finegrained", "mixtral"])
+def test_router_backward_workloads(name):
+    """The router workloads' full shapes, with the logits' gradient of a
+    routing-weight gradient through moe_route_backward."""
+    w = mi.WORKLOADS[name]
+    x = mi.normal_bf16(w.wid, mi.S_HIDDEN, w.T * w.H, 1.0).reshape(w.T, w.H)
+    wg = mi.router_weights(w)
+    g = np.random.Generator(np.random.PCG64(w.wid))
+    gl = g.standard_normal((w.T, w.E)).astype(np.float32)
+    _router_bwd_check(x, wg, gl)
