@@ -83,6 +83,18 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
     """The oracle on a growing prefix of the workload's tokens until ~10 s of
     CPU work (or the whole workload): route + align, then the expert FFN and
@@ -141,7 +153,7 @@ def cpu_baseline(w, inp, budget_s=(10.0, 30.0)):
     return {"value": n * passes / t_total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens x {passes} pass(es): {what} in float64, "
-                      f"{t_total:.1f} s"}
+                      f"{t_total:.1f} s on {cpu_model()}"}
 
 
 def bench_router(args, w, dev):
@@ -300,7 +312,7 @@ def cpu_baseline_backward(w, inp, gout, budget_s=(10.0, 30.0)):
         n = min(w.T, n * min(8, max(2, int(budget_s[0] / max(dt, 1e-3)))))
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens: route + expert FFN backward with weight "
-                      f"gradients + gating backward in float64, {dt:.1f} s"}
+                      f"gradients + gating backward in float64, {dt:.1f} s on {cpu_model()}"}
 
 
 def main():
