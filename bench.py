@@ -506,11 +506,18 @@ def main():
     # replay, bracketed by its own events).
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = T * 1e3 / ms_per_step
+    # Median over the timed steps of the event-timed step (the graph replay,
+    # or the first to the last phase event of an eager step).
+    if graph_ms is not None:
+        per_step = [a.elapsed_time(b) for a, b in gev]
+    else:
+        per_step = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]
+    median_ms = float(np.median(per_step))
 
     cfg = {"workload": w.name, "T": T, "E": E, "top_k": k,
            "routing_draws": draws, "cache_flush_between_steps": flush,
            "step_timing": "hip_graph_replay" if graph_ms is not None else "eager",
-           "eager_ms_per_step": round(eager_ms, 4)}
+           "eager_ms_per_step": round(eager_ms, 4), "median_event_ms_per_step": round(median_ms, 4)}
     if grouped:
         cfg.update({"method": w.method, "n_group": w.n_group, "topk_group": w.topk_group,
                     "renormalize": w.renorm})
