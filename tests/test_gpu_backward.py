@@ -423,3 +423,27 @@ def test_router_backward_workloads(name):
     g = np.random.Generator(np.random.PCG64(w.wid))
     gl = g.standard_normal((w.T, w.E)).astype(np.float32)
     _router_bwd_check(x, wg, gl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ffn_backward_all_slots_dropped(dtype):
+    """Every id -1: no aligned position; every gradient is exactly zero."""
+    T, H, I, E, k = 10, 64, 64, 4, 2
+    g = np.random.Generator(np.random.PCG64(5))
+    ids = np.full((T, k), -1, np.int32)
+    x, w13, w2, dy = (g.standard_normal(s).astype(np.float32)
+                      for s in ((T, H), (E, 2 * I, H), (E, H, I), (T, H)))
+    if dtype == "bf16":
+        x, w13, w2, dy = (dev_bf16(mi.f32_to_bf16_bits(a)) for a in (x, w13, w2, dy))
+    else:
+        x, w13, w2, dy = (dev(a) for a in (x, w13, w2, dy))
+    a = moe.moe_align(dev(ids), E)
+    # Fill the outputs with NaN first: every element must be written.
+    f32 = dict(dtype=torch.float32, device=DEV)
+    out = {"grad_hidden": torch.full((T, H), float("nan"), **f32),
+           "grad_w13": torch.full((E, 2 * I, H), float("nan"), **f32),
+           "grad_w2": torch.full((E, H, I), float("nan"), **f32),
+           "grad_topk_w": torch.full((T, k), float("nan"), **f32)}
+    got = moe.moe_expert_ffn_backward(x, w13, w2, dev(np.ones((T, k), np.float32)), a, dy, out)
+    for n, t in got.items():
+        assert bool((t == 0).all()), n
