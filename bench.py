@@ -33,6 +33,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
     "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
+    "ffn_backward": ["mixture_experts_routing_moe_amd/csrc/backward.hip",
+                     "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip"],
 }
 
 
@@ -65,9 +67,13 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(rel) -> str:
+    """First 16 hex digits of the SHA-256 of one source file, or of several in order."""
+    h = hashlib.sha256()
+    for r in [rel] if isinstance(rel, str) else rel:
+        with open(os.path.join(ROOT, r), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -279,7 +285,8 @@ def bench_backward(args, w, dev):
         "roofline": {"kernel": "moe_expert_ffn_backward (5 grouped bf16 GEMMs + 2 row kernels)",
                      "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("ffn_backward", w.name)},
         "phase_ms": {"ffn_backward": round(ffn_ms, 4), "route_backward": round(route_ms, 4)},
     }
     if not args.no_cpu_baseline:
