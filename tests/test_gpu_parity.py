@@ -80,14 +80,33 @@ def assert_bf16_layer(out_bf16, out_f32, out_ref):
     return rel
 
 
+def _nan_filled(shape, dtype):
+    """A device buffer whose every element is NaN (bf16 / f32 all-ones bits), so an
+    element the library fails to write shows up downstream as a non-finite output."""
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
 def run_ffn(x, w13, w2, tw, a, k, decode):
-    """All FFN phases through the C ABI -> (out bf16 as f32, pre-rounding out f32)."""
-    T = x.shape[0]
-    act = moe.moe_ffn_gate_up(x, w13, a, k, decode)
-    y = moe.moe_ffn_down(act, w2, a, T, k, decode)
-    out = moe.moe_combine(y, tw, a["slot_to_sorted"], x.dtype)
-    out32 = moe.moe_combine(y, tw, a["slot_to_sorted"], torch.float32)
-    one_call = moe.moe_expert_ffn(x, w13, w2, tw, a, decode=decode)
+    """All FFN phases through the C ABI -> (out bf16 as f32, pre-rounding out f32).
+
+    Every intermediate (act, y, the one-call workspace) and every output starts
+    as NaN, so a tile the GEMMs leave unwritten reaches the output as NaN."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    act = moe.moe_ffn_gate_up(x, w13, a, k, decode, act=_nan_filled((T * k, I), x.dtype))
+    sp = moe.moe_ffn_down_splits(moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32,
+                                 T, H, I, E, k, decode)
+    yshape = (T * k, H) if sp == 1 else (sp, T * k, H)
+    y = moe.moe_ffn_down(act, w2, a, T, k, decode, y=_nan_filled(yshape, torch.float32))
+    out = moe.moe_combine(y, tw, a["slot_to_sorted"], x.dtype, out=_nan_filled((T, H), x.dtype))
+    out32 = moe.moe_combine(y, tw, a["slot_to_sorted"], torch.float32,
+                            out=_nan_filled((T, H), torch.float32))
+    dt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
+    ws = torch.full((max(1, moe.moe_expert_ffn_workspace_size(dt, T, H, I, E, k)),), 0xFF,
+                    dtype=torch.uint8, device=DEV)
+    one_call = moe.moe_expert_ffn(x, w13, w2, tw, a, decode=decode,
+                                  out=_nan_filled((T, H), x.dtype), workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(one_call.view(torch.int16) if one_call.dtype == torch.bfloat16 else one_call,
                        out.view(torch.int16) if out.dtype == torch.bfloat16 else out)
@@ -228,18 +247,21 @@ def test_route_grouped_workloads(name, renorm):
                    mi.correction_bias(w), renorm)
 
 
-@pytest.mark.parametrize("T,E,n_group,topk_group,k", [
+_GROUPED_SHAPES = [
     (333, 16, 4, 2, 3), (70, 64, 8, 3, 8), (1, 64, 64, 64, 64), (129, 90, 9, 4, 7),
     (257, 96, 4, 1, 24), (200, 160, 8, 3, 6), (64, 256, 1, 1, 8), (100, 256, 8, 8, 64),
     (77, 384, 12, 5, 16), (40, 1024, 64, 7, 14), (33, 1000, 8, 2, 50),
     # 16-lanes-per-row kernel: E % 16 == 0, E <= 256, n_group | 16, k <= 16
     (500, 128, 16, 5, 16), (65, 48, 2, 1, 5), (301, 256, 4, 2, 8), (90, 32, 16, 3, 4),
-    (1031, 256, 8, 4, 8), (7, 160, 8, 3, 6), (130, 64, 2, 2, 16), (66, 208, 16, 16, 9)])
-@pytest.mark.parametrize("method", ["group_limited_greedy", "noaux_tc"])
+    (1031, 256, 8, 4, 8), (7, 160, 8, 3, 6), (130, 64, 2, 2, 16), (66, 208, 16, 16, 9)]
+
+
+# noaux_tc scores a group by its two best experts, so it needs groups of two or more.
+@pytest.mark.parametrize("T,E,n_group,topk_group,k,method", [
+    (*shape, m) for shape in _GROUPED_SHAPES for m in ("group_limited_greedy", "noaux_tc")
+    if m == "group_limited_greedy" or shape[1] // shape[2] >= 2])
 @pytest.mark.parametrize("ties", [False, True])
 def test_route_grouped_shapes(T, E, n_group, topk_group, k, method, ties):
-    if method == "noaux_tc" and E // n_group < 2:
-        pytest.skip("noaux_tc needs groups of two or more")
     g = np.random.Generator(np.random.PCG64(T * 7 + E + n_group + k))
     s = g.random((T, E)).astype(np.float32)
     b = (g.standard_normal(E) * 0.1).astype(np.float32) if method == "noaux_tc" else None
@@ -545,6 +567,10 @@ def _ffn_gpu(x, w13, w2, w32, ids, dtype, decode=False):
     (2048, 1024, 256, 8, 2, 1.0, 0.0),
     (1400, 128, 256, 2, 1, 0.0, 0.0),
     (2600, 64, 128, 4, 2, 0.5, 0.1),
+    # An expert with more m-tiles than one band of the tile order holds, in
+    # both products (8 n-tiles each): every token checked.
+    (2000, 2048, 1024, 2, 1, 3.0, 0.0),
+    (3000, 1024, 1408, 4, 2, 2.0, 0.05),
 ])
 def test_ffn_bf16_prefill(T, H, I, E, k, skew, inv):
     x, w13, w2, w32, ids = _rand_layer(T + H + I + E, T, H, I, E, k, skew=skew, inv=inv)
@@ -593,31 +619,43 @@ def _full_layer(name, decode, sample=None):
     ow, oids = oracle.route(inp["logits"], w.k, w.norm)
     np.testing.assert_array_equal(tids.cpu().numpy(), oids)
     assert_weights_close(tw.cpu().numpy(), ow)
-    toks = np.arange(w.T) if sample is None else sample(w.T, oids)
+    toks = np.arange(w.T) if sample is None else sample(w.T, oids, w.E)
+    print(f"{name}: oracle on {len(toks)} of {w.T} tokens", flush=True)
     ref = oracle.expert_ffn(inp["hidden"], inp["w13"], inp["w2"], ow, oids, "bf16", tokens=toks)
     rel = assert_bf16_layer(got[toks], got32[toks], ref)
     assert np.all(np.isfinite(got))
     return got, rel
 
 
-def _sample_tokens(T, ids, n=12):
-    g = np.random.Generator(np.random.PCG64(T))
-    picks = set(g.choice(T, size=n, replace=False).tolist()) | {0, T - 1}
-    # one token for each of the least-loaded experts
-    counts = np.bincount(ids.reshape(-1), minlength=ids.max() + 1)
-    for e in np.argsort(counts)[:4]:
-        hit = np.nonzero((ids == e).any(1))[0]
-        if len(hit):
-            picks.add(int(hit[0]))
+def _fragment_tokens(T, ids, E):
+    """Tokens whose rows cover every 32-row fragment of every expert segment.
+
+    The grouped GEMMs cut an expert's segment of the aligned order into m-tiles
+    whose first rows sit at multiples of 32 from the segment start, and a tile's
+    waves own 32-row fragments from there; whatever the tile height, each
+    fragment of each (expert, m-tile, n-tile) is then hit by the rows at
+    segment offsets 32 j and 32 j + 31 (and the segment's last row).  A token's
+    output row spans every n-tile of both products, so these tokens check every
+    tile of FC1 and FC2.  Plus the first and last token."""
+    a = oracle.align(ids, E)
+    off, sti = a["offsets"], a["sorted_token_ids"]
+    picks = {0, T - 1}
+    for e in range(E):
+        o0, o1 = int(off[e]), int(off[e + 1])
+        if o1 == o0:
+            continue
+        pos = np.arange(o0, o1, 32)
+        pos = np.concatenate([pos, np.minimum(pos + 31, o1 - 1), [o1 - 1]])
+        picks.update(int(t) for t in sti[pos])
     return np.array(sorted(picks), np.int64)
 
 
 def test_mixtral_layer_full_size():
-    _full_layer("mixtral", False, sample=_sample_tokens)
+    _full_layer("mixtral", False, sample=_fragment_tokens)
 
 
 def test_finegrained_layer_full_size():
-    _full_layer("finegrained", False, sample=_sample_tokens)
+    _full_layer("finegrained", False, sample=_fragment_tokens)
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode32"])
