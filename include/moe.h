@@ -219,15 +219,6 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                        void *stream);
 
 /*
- * moe_indices_to_multihot -- [T,k] routing to [T,E] multihot form.
- * [mgt] _indices_to_multihot_kernel, IndicesToMultihot.forward.
- *
- * ids               [T, k] int32 in; probs [T, k] float32 in.
- * multihot          [T, E] uint8 out: 1 where expert e is a valid id of row t, else 0.
- * probs_in_multihot [T, E] float32 out: probs[t, j] (bit copy) at e = ids[t, j], else 0.
- * position_map      [T, E] int32 out: slot j at e = ids[t, j], else -1.
- */
-/*
  * moe_route_align -- moe_route (moe_route_multihot when multihot,
  * probs_in_multihot and position_map are all given; all NULL otherwise)
  * followed by moe_align on the ids it produces.
@@ -254,6 +245,15 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
 /* 1 if moe_route_align takes the fused launches for this T, E and k. */
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k);
 
+/*
+ * moe_indices_to_multihot -- [T,k] routing to [T,E] multihot form.
+ * [mgt] _indices_to_multihot_kernel, IndicesToMultihot.forward.
+ *
+ * ids               [T, k] int32 in; probs [T, k] float32 in.
+ * multihot          [T, E] uint8 out: 1 where expert e is a valid id of row t, else 0.
+ * probs_in_multihot [T, E] float32 out: probs[t, j] (bit copy) at e = ids[t, j], else 0.
+ * position_map      [T, E] int32 out: slot j at e = ids[t, j], else -1.
+ */
 moe_status_t moe_indices_to_multihot(const int32_t *ids, const float *probs, int64_t T,
                                      int32_t k, int32_t E, uint8_t *multihot,
                                      float *probs_in_multihot, int32_t *position_map,
