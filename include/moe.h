@@ -246,6 +246,29 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k);
 
 /*
+ * moe_route_align_noalloc -- moe_route_align for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * launches and bit-identical outputs.  The alignment's scratch (per-block
+ * expert counts, moe_align_workspace_size(T, k, E) bytes, at most 64 KiB for
+ * any valid T, k, E) lives in a 256 KiB array that the library holds in
+ * device memory, one copy per GPU, until the process ends; a shape whose
+ * scratch would exceed it returns MOE_ERR_WORKSPACE before any launch.  The
+ * device's address of that array is looked up on the first call on each
+ * device (make that first call outside graph capture).  Nothing in the array
+ * needs to start at zero.  Every call on a GPU shares that GPU's array, so
+ * calls that overlap on one GPU (different streams, or several host threads)
+ * race: order them on one stream.
+ */
+moe_status_t moe_route_align_noalloc(const float *logits, int64_t T, int32_t E, int32_t k,
+                                     int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                     uint8_t *multihot, float *probs_in_multihot,
+                                     int32_t *position_map, int32_t *expert_counts,
+                                     int32_t *expert_offsets, int32_t *sorted_token_ids,
+                                     int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                                     void *stream);
+
+/*
  * moe_indices_to_multihot -- [T,k] routing to [T,E] multihot form.
  * [mgt] _indices_to_multihot_kernel, IndicesToMultihot.forward.
  *

@@ -6,6 +6,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace {
@@ -268,14 +271,19 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                       "moe_align");
 }
 
-moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t k,
-                             int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
-                             uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
-                             int32_t *expert_counts, int32_t *expert_offsets,
-                             int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
-                             int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
-                             void *stream) {
-    const char *fn = "moe_route_align";
+}  // extern "C"
+
+namespace {
+
+// moe_route_align's checks and launches, with the alignment scratch given as
+// a device pointer (the caller's workspace, or the library's static array).
+moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, int32_t E,
+                              int32_t k, int32_t norm_topk_prob, float *topk_w,
+                              int32_t *topk_ids, uint8_t *multihot, float *probs_in_multihot,
+                              int32_t *position_map, int32_t *expert_counts,
+                              int32_t *expert_offsets, int32_t *sorted_token_ids,
+                              int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                              void *workspace, size_t workspace_bytes, void *stream) {
     moe_status_t st = check_routing_dims(T, E, k, fn);
     if (st != MOE_OK) return st;
     CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
@@ -297,6 +305,80 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
                                               static_cast<int32_t *>(workspace),
                                               static_cast<hipStream_t>(stream)),
                       fn);
+}
+
+// The allocation-free variant's scratch: a file-scope device array, one copy
+// per GPU, zero at load and held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// symbol): each device's address is looked up once, with that device
+// current, and kept in scratch_ptr.
+constexpr size_t kStaticScratchBytes = 256 * 1024;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+moe_status_t static_scratch(const char *fn, void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    CHECK(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "%s: device %d >= %d", fn, dev,
+          kMaxDevices);
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+            CHECK(p != nullptr, MOE_ERR_HIP, "%s: no device address for the static scratch",
+                  fn);
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t k,
+                             int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                             uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
+                             int32_t *expert_counts, int32_t *expert_offsets,
+                             int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                             int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return route_align_impl("moe_route_align", logits, T, E, k, norm_topk_prob, topk_w, topk_ids,
+                            multihot, probs_in_multihot, position_map, expert_counts,
+                            expert_offsets, sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                            workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_route_align_noalloc(const float *logits, int64_t T, int32_t E, int32_t k,
+                                     int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                     uint8_t *multihot, float *probs_in_multihot,
+                                     int32_t *position_map, int32_t *expert_counts,
+                                     int32_t *expert_offsets, int32_t *sorted_token_ids,
+                                     int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                                     void *stream) {
+    const char *fn = "moe_route_align_noalloc";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    const size_t need = moe_align_workspace_size(T, k, E);
+    CHECK(need <= kStaticScratchBytes, MOE_ERR_WORKSPACE,
+          "%s: needs %zu bytes of scratch, the static array holds %zu", fn, need,
+          kStaticScratchBytes);
+    void *ws = nullptr;
+    st = static_scratch(fn, &ws);
+    if (st != MOE_OK) return st;
+    return route_align_impl(fn, logits, T, E, k, norm_topk_prob, topk_w, topk_ids, multihot,
+                            probs_in_multihot, position_map, expert_counts, expert_offsets,
+                            sorted_token_ids, sorted_slot_ids, slot_to_sorted, ws,
+                            kStaticScratchBytes, stream);
 }
 
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k) {

@@ -179,12 +179,7 @@ def moe_route_align_fused(T: int, E: int, k: int) -> bool:
     return bool(lib().moe_route_align_fused(T, E, k))
 
 
-def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
-                    with_multihot: bool = False, out: dict | None = None,
-                    workspace: torch.Tensor | None = None) -> dict:
-    """moe_route (moe_route_multihot with with_multihot) + moe_align in one call ->
-    dict with topk_w, topk_ids, the alignment outputs of moe_align and, with
-    with_multihot, multihot / probs_in_multihot / position_map."""
+def _route_align_outputs(logits, k, with_multihot, out):
     if logits.dtype != torch.float32 or logits.dim() != 2:
         raise ValueError("logits must be [T, E] float32")
     T, E = logits.shape
@@ -204,16 +199,43 @@ def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
             out["multihot"] = torch.empty((T, E), dtype=torch.uint8, device=dev)
             out["probs_in_multihot"] = torch.empty((T, E), dtype=torch.float32, device=dev)
             out["position_map"] = torch.empty((T, E), dtype=torch.int32, device=dev)
+    return T, E, out
+
+
+def _route_align_ptrs(out):
+    return (_ptr(out["topk_w"]), _ptr(out["topk_ids"]), _ptr(out.get("multihot")),
+            _ptr(out.get("probs_in_multihot")), _ptr(out.get("position_map")),
+            _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sorted_token_ids"]),
+            _ptr(out["sorted_slot_ids"]), _ptr(out["slot_to_sorted"]))
+
+
+def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
+                    with_multihot: bool = False, out: dict | None = None,
+                    workspace: torch.Tensor | None = None) -> dict:
+    """moe_route (moe_route_multihot with with_multihot) + moe_align in one call ->
+    dict with topk_w, topk_ids, the alignment outputs of moe_align and, with
+    with_multihot, multihot / probs_in_multihot / position_map."""
+    T, E, out = _route_align_outputs(logits, k, with_multihot, out)
     if workspace is None:
         workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
-                                device=dev)
+                                device=logits.device)
     _dev(logits, workspace, *out.values())
-    check(lib().moe_route_align(
-        _ptr(logits), T, E, k, int(bool(norm_topk_prob)), _ptr(out["topk_w"]),
-        _ptr(out["topk_ids"]), _ptr(out.get("multihot")), _ptr(out.get("probs_in_multihot")),
-        _ptr(out.get("position_map")), _ptr(out["counts"]), _ptr(out["offsets"]),
-        _ptr(out["sorted_token_ids"]), _ptr(out["sorted_slot_ids"]), _ptr(out["slot_to_sorted"]),
-        _ptr(workspace), workspace.numel(), _stream()), "moe_route_align")
+    check(lib().moe_route_align(_ptr(logits), T, E, k, int(bool(norm_topk_prob)),
+                                *_route_align_ptrs(out), _ptr(workspace), workspace.numel(),
+                                _stream()), "moe_route_align")
+    return out
+
+
+def moe_route_align_noalloc(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
+                            with_multihot: bool = False, out: dict | None = None) -> dict:
+    """moe_route_align without a workspace: the library's own device scratch
+    (shared by every call on the GPU) stands in for it.  With `out` given this
+    allocates nothing."""
+    T, E, out = _route_align_outputs(logits, k, with_multihot, out)
+    _dev(logits, *out.values())
+    check(lib().moe_route_align_noalloc(_ptr(logits), T, E, k, int(bool(norm_topk_prob)),
+                                        *_route_align_ptrs(out), _stream()),
+          "moe_route_align_noalloc")
     return out
 
 
