@@ -560,6 +560,14 @@ def main():
         w2_bytes = n_exp * w.H * w.I * 2
         cfg["down_hbm_gbs"] = round((w2_bytes + n_valid * w.I * 2 + n_valid * w.H * 4) /
                                     (phase_ms["down"] * 1e-3) / 1e9, 1)
+        # The whole step against HBM: its algorithmic bytes (every selected
+        # expert's w13 and w2 once, the logits, the routing and multihot
+        # outputs, the inverse's reads and writes, the token rows and the
+        # output) over the step time.
+        step_bytes = n_exp * 3 * w.I * w.H * 2 + T * E * 4 + T * k * 8 + T * k * 12 + \
+            T * E * 9 + T * E * 8 + T * k * 8 + T * w.H * 2 * 2
+        cfg["step_hbm_gbs"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)
+        cfg["step_hbm_frac"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
 
     if routing_only:
         # Algorithmic HBM bytes per phase: every input read once, every output

@@ -41,6 +41,8 @@ constexpr int kAlignWaves = kAlignThreads / kWave;
 #endif
 constexpr int kPartialBudget = MOE_ALIGN_BUDGET;  // cap on nb * E partial counts each scatter block sums
 constexpr int kSlotsPerBlock = MOE_ALIGN_SLOTS;   // slots per block before the cap
+// Partial-count rows a scatter thread loads per batch (all in flight at once).
+constexpr int kRowBatch = kPartialBudget / kAlignThreads;
 
 int64_t align_chunk(int64_t n, int nb) {
     int64_t c = (n + nb - 1) / nb;
@@ -142,17 +144,34 @@ __device__ __forceinline__ void align_scatter_block(
             if ((unsigned)e < (unsigned)E) atomicAdd(&tot_part[e], 1);
         }
     }
+    // The first ids of the chunk, loaded before the partial sums below so
+    // that both loads are in flight together.
+    const int lo = b * chunk;
+    const int hi = lo + chunk < n ? lo + chunk : n;
+    int e_first = -1;
+    if (lo + tid < hi) e_first = ids[lo + tid];
+
     // Per (part, expert): sums over the blocks part, part + parts, ... -- all
     // of them and those before b.  Threads of one pass read consecutive
-    // experts of one block row (coalesced), and the loads are independent.
+    // experts of one block row (coalesced).  The loads go out in batches of
+    // kRowBatch, each issued whole before its first value is used: when E
+    // divides 512 a thread sums at most kRowBatch blocks (nb <= 16384 / E
+    // over parts = 512 / E threads), so that is one memory round trip.
     for (int idx = tid; idx < (fused_hist ? 0 : parts * E); idx += kAlignThreads) {
         const int e = idx % E, part = idx / E;
         int all = 0, pre = 0;
-#pragma unroll 8
-        for (int bb = part; bb < nb; bb += parts) {
-            const int c = partial[(int64_t)bb * E + e];
-            all += c;
-            pre += bb < b ? c : 0;
+        for (int r0 = part; r0 < nb; r0 += kRowBatch * parts) {
+            int c[kRowBatch];
+#pragma unroll
+            for (int i = 0; i < kRowBatch; ++i) {
+                const int bb = r0 + i * parts;
+                c[i] = bb < nb ? partial[(int64_t)bb * E + e] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < kRowBatch; ++i) {
+                all += c[i];
+                pre += r0 + i * parts < b ? c[i] : 0;
+            }
         }
         tot_part[part * E + e] = all;
         pre_part[part * E + e] = pre;
@@ -185,12 +204,10 @@ __device__ __forceinline__ void align_scatter_block(
     }
     __syncthreads();
 
-    const int lo = b * chunk;
-    const int hi = lo + chunk < n ? lo + chunk : n;
     for (int it = lo; it < hi; it += kAlignThreads) {
         const int s = it + tid;
-        int e = -1;
-        if (s < hi) e = ids[s];
+        int e = e_first;
+        if (it != lo) e = s < hi ? ids[s] : -1;
         const bool ok = (unsigned)e < (unsigned)E;
         // Lanes of this wave holding the same expert: filter by each id bit.
         uint64_t peers = __ballot(ok);
@@ -212,6 +229,7 @@ __device__ __forceinline__ void align_scatter_block(
         } else if (s < hi) {
             slot_to_sorted[s] = -1;
         }
+        if (it + kAlignThreads >= hi) break;  // the last pass needs no hand-over
         __syncthreads();
         if (ok && rank == 0) {
             atomicAdd(&run[e], cnt);
