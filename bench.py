@@ -33,6 +33,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
     "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
+    # route_hist_kernel + align_scatter_kernel (the routing rows of moe_route_align)
+    "route_align": ["mixture_experts_routing_moe_amd/csrc/align.hip",
+                    "mixture_experts_routing_moe_amd/csrc/moe_internal.h"],
     "ffn_backward": ["mixture_experts_routing_moe_amd/csrc/backward.hip",
                      "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip"],
 }
@@ -80,7 +83,7 @@ def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; otherwise None."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path):
+    if kernel not in KERNEL_SRC or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -591,7 +594,7 @@ def main():
         achieved = nb[dom] / (phase_ms[dom] * 1e-3) / 1e9
         roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": None}
+                    "traffic": measured_traffic(dom, w.name)}
         cfg["path_bytes"] = sum(nb.values())
         cfg["path_gbs_eager_phases"] = round(sum(nb.values()) / (sum(phase_ms.values()) * 1e-3) / 1e9, 1)
         cfg["path_gbs_step"] = round(sum(nb.values()) / (ms_per_step * 1e-3) / 1e9, 1)
