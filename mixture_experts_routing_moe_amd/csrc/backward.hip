@@ -19,8 +19,11 @@
 //   G = dy . w2, d_hidden = [d_gate ; d_up] . w13) run on the forward's tuned
 //   grouped kernel (the FC2 variant: A rows in the aligned order, one weight
 //   matrix per expert, float32 out).  Its A rows are the tokens' rows gathered
-//   into the aligned order, and its weights for G and d_hidden are w2 and w13
-//   transposed per expert ([E, I, H] and [E, H, 2I], written each call).
+//   into the aligned order.  G and d_hidden contract over the rows of w2 and
+//   w13; they take the kernel's K-major variant, which loads the weights as
+//   stored and transposes them in its LDS fragment reads (gfx950's
+//   ds_read_b64_tr_b16), so the weights are not copied (operands too large
+//   for buffer addressing fall back to per-expert transposed copies).
 // * The two weight gradients contract over each expert's rows.  Their
 //   operands (dy, x, w act, [d_gate ; d_up]) are transposed into [columns,
 //   positions] with every expert's segment padded to a whole number of
@@ -30,6 +33,8 @@
 //   of 64 in two LDS stages (144 KB).  Measured against 128 x 128 tiles and
 //   32-wide k-tiles: 4 % (Mixtral shape) and 10 % (fine-grained) faster
 //   backward.
+#include <cstdlib>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -569,6 +574,18 @@ int64_t padded_positions(int64_t T, int E, int k) {
     return (T * k + (int64_t)kSegPad * E + 63) / 64 * 64;
 }
 
+// G = dy . w2 and d_hidden = [d_gate ; d_up] . w13 contract over the weights'
+// rows.  They read w2 and w13 as stored (the grouped kernel's K-major variant,
+// which transposes in its LDS fragment reads) unless an operand is too large
+// for its buffer addressing; then w2 and w13 are transposed per expert into
+// the workspace first.  MOE_BWD_TRANSPOSED_WEIGHTS=1 in the environment takes
+// the transposing path at any size (tests compare the two).
+bool kmajor_weights(int64_t T, int H, int I, int k) {
+    const char *v = std::getenv("MOE_BWD_TRANSPOSED_WEIGHTS");  // read per call (host only)
+    if (v != nullptr && v[0] == '1') return false;
+    return down_kmajor_ok(T, I, H, k) && down_kmajor_ok(T, H, 2 * I, k);
+}
+
 size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
     const size_t P = (size_t)T * (size_t)k;
     const size_t Pp = (size_t)padded_positions(T, E, k);
@@ -581,8 +598,12 @@ size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
         case 4: b = P * H * 4; break;                   // dxs    f32  [P, H]
         case 5: b = P * H * 2; break;                   // xs     bf16 [P, H]
         case 6: b = P * H * 2; break;                   // dys    bf16 [P, H]
-        case 7: b = (size_t)E * 2 * I * H * 2; break;   // w13t   bf16 [E, H, 2I]
-        case 8: b = (size_t)E * H * I * 2; break;       // w2t    bf16 [E, I, H]
+        case 7:  // w13t bf16 [E, H, 2I], only on the transposing path
+            b = kmajor_weights(T, H, I, k) ? 0 : (size_t)E * 2 * I * H * 2;
+            break;
+        case 8:  // w2t bf16 [E, I, H], only on the transposing path
+            b = kmajor_weights(T, H, I, k) ? 0 : (size_t)E * H * I * 2;
+            break;
         case 9: b = (size_t)H * Pp * 2; break;          // dyT    bf16 [H, Pp]
         case 10: b = (size_t)I * Pp * 2; break;         // wactT  bf16 [I, Pp]
         case 11: b = (size_t)2 * I * Pp * 2; break;     // dh13T  bf16 [2I, Pp]
@@ -663,9 +684,12 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
     hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)P), dim3(256), 0, s, x, dy, sorted_tok,
                        offsets, E, H, xs, dys);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(transpose(w13, H, (int64_t)2 * I * H, nullptr, 2 * I, H, w13t, 2 * I,
-                      (int64_t)2 * I * H, E, s));
-    MOE_TRY(transpose(w2, I, (int64_t)H * I, nullptr, H, I, w2t, H, (int64_t)H * I, E, s));
+    const bool km = kmajor_weights(T, H, I, k);
+    if (!km) {
+        MOE_TRY(transpose(w13, H, (int64_t)2 * I * H, nullptr, 2 * I, H, w13t, 2 * I,
+                          (int64_t)2 * I * H, E, s));
+        MOE_TRY(transpose(w2, I, (int64_t)H * I, nullptr, H, I, w2t, H, (int64_t)H * I, E, s));
+    }
     hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, E, poff);
     MOE_TRY(hipGetLastError());
     hipLaunchKernelGGL(seg_src_kernel, dim3((unsigned)((Pp + 255) / 256)), dim3(256), 0, s,
@@ -674,11 +698,13 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
 
     // Row-segment products on the forward's grouped kernel (FC2 form).
     MOE_TRY(launch_down_bf16(xs, w13, offsets, T, 2 * I, H, E, k, 1, h13, s));  // gate/up
-    MOE_TRY(launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));       // G
+    MOE_TRY(km ? launch_down_kmajor_bf16(dys, w2, offsets, T, I, H, E, k, G, s)   // G
+               : launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));
     hipLaunchKernelGGL(bwd_act_kernel, dim3((unsigned)P), dim3(256), 0, s, h13, G, topk_w,
                        offsets, sorted_slot, E, I, wact, dh13, dw);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(launch_down_bf16(dh13, w13t, offsets, T, H, 2 * I, E, k, 1, dxs, s));  // d_hidden
+    MOE_TRY(km ? launch_down_kmajor_bf16(dh13, w13, offsets, T, H, 2 * I, E, k, dxs, s)
+               : launch_down_bf16(dh13, w13t, offsets, T, H, 2 * I, E, k, 1, dxs, s));  // d_hidden
     hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
                        H, dx, dw);
     MOE_TRY(hipGetLastError());

@@ -36,6 +36,7 @@
 // clamped the same way.
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -207,6 +208,24 @@ struct Ops<false> {
     int na;                           // token loads that hold a row of the tile
 };
 
+// Buffer-addressed operands with the weight stored K-major (per expert
+// [K, N], N contiguous: w2 and w13 as stored, for the backward's products that
+// contract over their rows).  A stage's weight tile holds its BK k-rows of BN
+// columns as 16-byte chunks of 8 columns; chunk c of k-row k sits at slot
+// 32 k + (c ^ 4 (k % 4)) of the stage, so one DMA instruction fills two whole
+// k-rows (64 consecutive slots, lane-linear as the DMA writes) and the
+// transposing fragment reads (load_frags below) hit 16 distinct 16-byte bank
+// groups per half-wave.
+struct OpsKm {
+    __amdgpu_buffer_rsrc_t a, b;    // token / weight operand (this expert)
+    int kb;                         // first k of this K slice
+    int na;                         // token loads that hold a row of the tile
+    int ldw;                        // N, elements per weight k-row
+    uint32_t aoff[NLA], boff[NLB];  // byte offsets of this lane's token rows / weight chunks
+};
+static_assert(BN == 256 && BK == 64 && NLB * kWaves * 2 == BK,
+              "the K-major weight layout: 32 chunks per k-row, two k-rows per DMA instruction");
+
 // Token load i of a wave is issued only if its rows reach into the tile
 // (i < na, wave-uniform): rows past the expert's segment are never stored, so
 // their LDS rows may hold anything, and skipping them cuts the load traffic
@@ -241,6 +260,24 @@ __device__ __forceinline__ void issue_stage(uint16_t *smem, const Ops<true> &op,
             uint16_t *db =
                 smem + kWOff + S * kWStage + (wave * kWRowsPerWave + i * kRowsPerLoad) * BK;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], so, 0,
+                                                     0);
+        }
+    }
+}
+template <int S>
+__device__ __forceinline__ void issue_stage(uint16_t *smem, const OpsKm &op, int k0, int wave) {
+    const uint32_t so = 2u * (uint32_t)(op.kb + k0);
+    const uint32_t sow = so * (uint32_t)op.ldw;  // k-tile start of the K-major weight
+#pragma unroll
+    for (int i = 0; i < (NLA > NLB ? NLA : NLB); ++i) {
+        if (tok_load(op, i)) {
+            uint16_t *da = smem + S * kTokStage + (wave * kTokRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0,
+                                                     0);
+        }
+        if (i < NLB) {
+            uint16_t *db = smem + kWOff + S * kWStage + (wave * NLB + i) * 512;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], sow, 0,
                                                      0);
         }
     }
@@ -314,6 +351,35 @@ __device__ __forceinline__ void load_frags(Frags<MV> &fr, const char *lds, const
         fr.x[g] = *reinterpret_cast<const bf16x8 *>(lds + fa.x[J] + (S * kTokStage + g * 32 * BK) * 2);
 }
 
+// K-major weights: per lane, the LDS byte address of its first transposing
+// read for each weight fragment of the wave (stage 0, k-step 0); the stage,
+// the k-step and the second read are compile-time offsets on top.
+struct FragAddrKm {
+    uint32_t w[NF], x[KS];
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// A 32x32x16 A-operand fragment (lane l: weight column l % 32, k 8 (l / 32) ..
+// + 7 of the k-step) from the K-major tile: two ds_read_b64_tr_b16.  In each
+// 16-lane group the read hands lane i element i % 4 of the 8 bytes that lane
+// 4 q + i / 4 addresses, as its q-th value; so with lane s of group g
+// addressing k-row 8 (g / 2) + 4 h + s / 4, columns 16 (g % 2) + 4 (s % 4) ..
+// + 3, lane s receives column 16 (g % 2) + s at those four k-rows.
+template <int S, int J, int MV, bool kGateUp>
+__device__ __forceinline__ void load_frags(Frags<MV> &fr, const char *lds, const FragAddrKm &fa) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const char *p = lds + fa.w[f] + S * kWStage * 2 + 16 * J * 512;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 4 * 512));
+        fr.w[f] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int g = 0; g < MV; ++g)
+        fr.x[g] = *reinterpret_cast<const bf16x8 *>(lds + fa.x[J] + (S * kTokStage + g * 32 * BK) * 2);
+}
+
 template <int MV>
 __device__ __forceinline__ void mma_frags(f32x16 (&acc)[NF][MF], const Frags<MV> &fr) {
 #pragma unroll
@@ -361,9 +427,9 @@ __device__ __forceinline__ void wait_landed(int later) {
 
 // k-steps 1 .. KS-1 of stage S but the last: the reads for k-step j+1 are
 // issued during the MFMAs of k-step j (fragments double-buffered).
-template <int S, int J, int MV, bool kGateUp>
+template <int S, int J, int MV, bool kGateUp, typename FA>
 __device__ __forceinline__ void k_steps(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], const char *lds,
-                                        const FragAddr &fa) {
+                                        const FA &fa) {
     if constexpr (J + 1 < KS) {
         load_frags<S, J + 1, MV, kGateUp>(fr[(J + 1) & 1], lds, fa);
         mma_frags(acc, fr[J & 1]);
@@ -381,10 +447,9 @@ __device__ __forceinline__ void k_steps(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2
 // under the last k-step's MFMAs (after the last k-tile that stage holds data
 // nobody uses).  Stage indices are compile-time, so the loop computes no
 // addresses.
-template <int S, int MV, bool kGateUp, typename OpsT>
+template <int S, int MV, bool kGateUp, typename OpsT, typename FA>
 __device__ __forceinline__ void k_tile(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
-                                       const OpsT &op, int kt, int nk, int wv,
-                                       const FragAddr &fa) {
+                                       const OpsT &op, int kt, int nk, int wv, const FA &fa) {
     const char *lds = reinterpret_cast<const char *>(smem);
     if (!late_issue<kGateUp>() && kt + NS - 1 < nk)
         issue_stage<(S + NS - 1) % NS>(smem, op, (kt + NS - 1) * BK, wv);
@@ -400,10 +465,9 @@ __device__ __forceinline__ void k_tile(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2]
     interleave<MV>();
 }
 
-template <int S, int MV, bool kGateUp, typename OpsT>
+template <int S, int MV, bool kGateUp, typename OpsT, typename FA>
 __device__ __forceinline__ void k_tiles(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2], uint16_t *smem,
-                                        const OpsT &op, int kt, int nk, int wv,
-                                        const FragAddr &fa) {
+                                        const OpsT &op, int kt, int nk, int wv, const FA &fa) {
     if constexpr (S < NS) {
         if (kt < nk) {
             k_tile<S, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
@@ -412,18 +476,17 @@ __device__ __forceinline__ void k_tiles(f32x16 (&acc)[NF][MF], Frags<MV> (&fr)[2
     }
 }
 
-template <int S, bool kBuf>
-__device__ __forceinline__ void issue_first(uint16_t *smem, const Ops<kBuf> &op, int nk,
-                                            int wv) {
+template <int S, typename OpsT>
+__device__ __forceinline__ void issue_first(uint16_t *smem, const OpsT &op, int nk, int wv) {
     if constexpr (S + 1 < NS) {
         if (S < nk) issue_stage<S>(smem, op, S * BK, wv);
         issue_first<S + 1>(smem, op, nk, wv);
     }
 }
 
-template <int MV, bool kGateUp, typename OpsT>
+template <int MV, bool kGateUp, typename OpsT, typename FA>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, const OpsT &op,
-                                       int nk, int wv, const FragAddr &fa) {
+                                       int nk, int wv, const FA &fa) {
     issue_first<0>(smem, op, nk, wv);
     wait_landed<NS - 2>(min(nk - 1, NS - 2));
     stage_barrier();
@@ -442,9 +505,9 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
 // fragments.  Each MV has its accumulators to itself: declared outside the
 // dispatch on MV, one set shared by the five loop versions measured slower
 // (the register allocator copies it between them).
-template <int MV, bool kGateUp, typename OpsT>
+template <int MV, bool kGateUp, typename OpsT, typename FA>
 __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int wv,
-                                         const FragAddr &fa, const MTile &tile, int nt, int wn,
+                                         const FA &fa, const MTile &tile, int nt, int wn,
                                          int wm, int lr, int lk, int N, int ks, int64_t plane,
                                          void *__restrict__ Cv) {
     f32x16 acc[NF][MF];
@@ -509,7 +572,8 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 //
 // kBuf selects the operand addressing (Ops); a_bytes is the token operand's
 // size in bytes (used by kBuf only).
-template <bool kGateUp, bool kBuf>
+// kKm (FC2 form, buffer addressing only): W is K-major, [E, K, N].
+template <bool kGateUp, bool kBuf, bool kKm = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
@@ -554,7 +618,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int rr = lane / kChunks;
     const int rows_w = kGateUp ? 2 * N : N;
     const uint16_t *We = W + (int64_t)tile.e * rows_w * K;
-    Ops<kBuf> op;
+    static_assert(!kKm || (kBuf && !kGateUp), "K-major weights: FC2 form, buffer addressing");
+    using OpsT = typename std::conditional<kKm, OpsKm, Ops<kBuf>>::type;
+    OpsT op;
+    if constexpr (kKm) op.ldw = N;
     if constexpr (kBuf) {
         op.a = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, a_bytes, kBufferWord3);
         op.b = __builtin_amdgcn_make_buffer_rsrc((void *)We, (short)0, rows_w * K * 2,
@@ -575,8 +642,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         else
             op.a[i] = A + (int64_t)arow * K + kbeg + c8;
     }
+    if constexpr (kKm) {
 #pragma unroll
-    for (int i = 0; i < NLB; ++i) {
+        for (int i = 0; i < NLB; ++i) {
+            // DMA instruction wv NLB + i fills k-rows kk = 2 (wv NLB + i) + lane / 32
+            // of the tile, slot lane % 32 of each: chunk (lane % 32) ^ 4 (kk % 4).
+            const int kk = 2 * (wv * NLB + i) + (lane >> 5);
+            const int c = (lane & 31) ^ (4 * (kk & 3));
+            const int n = min(nt * BN + 8 * c, N - 8);
+            op.boff[i] = ((uint32_t)kk * (uint32_t)N + (uint32_t)n) * 2u;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NLB && !kKm; ++i) {
         const int r = wv * kWRowsPerWave + i * kRowsPerLoad + rr;
         const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         int wrow;
@@ -586,9 +664,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         } else {
             wrow = min(nt * BN + r, N - 1);
         }
-        if constexpr (kBuf)
+        if constexpr (kBuf && !kKm)
             op.boff[i] = ((uint32_t)wrow * (uint32_t)K + (uint32_t)c8) * 2u;
-        else
+        else if constexpr (!kBuf)
             op.b[i] = We + (int64_t)wrow * K + kbeg + c8;
     }
 
@@ -602,12 +680,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int sw = swz(lr);
     const int wrow0 = kGateUp ? wn * (BN / 2 / WN) : wn * (BN / WN);
     const int xrow = wm * (BM / WM) + lr;
-    FragAddr fa;
+    using FA = typename std::conditional<kKm, FragAddrKm, FragAddr>::type;
+    FA fa;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
         const uint32_t ch = (uint32_t)(((2 * j + lk) ^ sw) * 16);
-        fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
+        if constexpr (!kKm) fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
         fa.x[j] = (uint32_t)(xrow * BK * 2) + ch;
+    }
+    if constexpr (kKm) {
+        // Transposing reads: lane s of 16-lane group g addresses k-row
+        // 8 (g / 2) + s / 4 (+ 16 j + 4 h), columns c = column of the fragment's
+        // first row + 16 (g % 2) + 4 (s % 4) .. + 3, i.e. the half (s % 2) of
+        // chunk c / 8; k-row % 4 = s / 4 for every j and h.
+        const int g = lane >> 4, sl = lane & 15;
+        const int krow = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int chunk = (wrow0 + 32 * f) / 8 + 2 * (g & 1) + ((sl & 3) >> 1);
+            fa.w[f] = (uint32_t)(kWOff * 2 + (krow * 32 + (chunk ^ (4 * (sl >> 2)))) * 16 +
+                                 8 * (sl & 1));
+        }
     }
 
     // Token fragments of this wave that hold at least one row of the expert
@@ -685,6 +778,26 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s,
                            hidden, sorted_tok, w13, offsets, act, E, H, I, n_tiles, 1, (int64_t)0,
                            0);
+    return hipGetLastError();
+}
+
+bool down_kmajor_ok(int64_t T, int N, int K, int k) {
+    const int64_t a_bytes = T * k * (int64_t)K * 2, w_bytes = (int64_t)K * N * 2;
+    return use_buffer_path(a_bytes, w_bytes);
+}
+
+hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const int32_t *offsets,
+                                   int64_t T, int N, int K, int E, int k, float *y,
+                                   hipStream_t s) {
+    const int64_t rows = T * k;
+    if (rows == 0) return hipSuccess;
+    if (!down_kmajor_ok(T, N, K, k)) return hipErrorInvalidValue;
+    const int m_slots = m_slot_bound(rows, E);
+    const int n_tiles = (N + BN - 1) / BN;
+    const int64_t a_bytes = rows * K * 2;
+    const dim3 grid(grid_of(m_slots, n_tiles));
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true>), grid, dim3(kThreads), 0, s,
+                       a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes);
     return hipGetLastError();
 }
 

@@ -290,6 +290,13 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
 hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32_t *offsets,
                             int64_t T, int H, int I, int E, int k, int ksplit, float *y,
                             hipStream_t s);
+// The FC2-form grouped product with a K-major weight w [E, K, N] (N
+// contiguous): y[p, n] = sum_k a[p, k] w[e, k, n] for the rows p of expert e,
+// float32 [T k, N].  Needs buffer addressing (down_kmajor_ok).
+bool down_kmajor_ok(int64_t T, int N, int K, int k);
+hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const int32_t *offsets,
+                                   int64_t T, int N, int K, int E, int k, float *y,
+                                   hipStream_t s);
 // K slices the prefill FC2 uses for this shape (1 .. 4).
 int down_splits(int64_t T, int H, int I, int E, int k);
 

@@ -162,6 +162,26 @@ def test_ffn_backward_f32(T, H, I, E, k, inv):
     assert np.all(got["grad_topk_w"].cpu().numpy()[ids < 0] == 0)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,skew,inv", [(300, 128, 192, 8, 2, 0.0, 0.0),
+                                                (513, 192, 320, 16, 4, 0.5, 0.1),
+                                                (700, 64, 1408, 4, 2, 1.0, 0.0),
+                                                (90, 320, 64, 3, 3, 0.0, 0.0)])
+def test_ffn_backward_kmajor_weights(monkeypatch, T, H, I, E, k, skew, inv):
+    """G = dy . w2 and d_hidden = [d_gate ; d_up] . w13 read w2 and w13 as
+    stored (the grouped kernel transposes in its LDS reads): the same products,
+    term for term and in the same order, as the path that first copies the
+    weights transposed, so every gradient is bit-identical to it."""
+    x, w13, w2, w32, ids, dy = _rand_case(T * 3 + I, T, H, I, E, k, skew, inv)
+    print(f"kmajor backward T={T} H={H} I={I} E={E} k={k}", flush=True)
+    got = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.setenv("MOE_BWD_TRANSPOSED_WEIGHTS", "1")
+    ref = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.delenv("MOE_BWD_TRANSPOSED_WEIGHTS")
+    for name in got:
+        np.testing.assert_array_equal(got[name].view(np.uint32), ref[name].view(np.uint32),
+                                      err_msg=name)
+
+
 def test_ffn_backward_deterministic():
     x, w13, w2, w32, ids, dy = _rand_case(5, 300, 128, 192, 8, 2)
     a = _bwd_gpu(x, w13, w2, w32, ids, dy)
