@@ -714,8 +714,13 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
     MOE_TRY(transpose(wact, I, 0, src, Pp, I, wactT, Pp, 0, 1, s));
     MOE_TRY(transpose(dh13, 2 * I, 0, src, Pp, 2 * I, dh13T, Pp, 0, 1, s));
     MOE_TRY(transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
-    MOE_TRY(wgrad(dyT, wactT, Pp, poff, E, H, I, dw2, s));       // dw2[e]  [H, I]
-    MOE_TRY(wgrad(dh13T, xT, Pp, poff, E, 2 * I, H, dw13, s));   // dw13[e] [2I, H]
+    // On the grouped kernel's machinery where the operands fit its buffer
+    // addressing, else on wgrad_kernel.
+    MOE_TRY(wgrad_grouped_ok(H, I, Pp) ? launch_wgrad_bf16(dyT, wactT, Pp, poff, E, H, I, dw2, s)
+                                       : wgrad(dyT, wactT, Pp, poff, E, H, I, dw2, s));  // dw2[e] [H, I]
+    MOE_TRY(wgrad_grouped_ok(2 * I, H, Pp)
+                ? launch_wgrad_bf16(dh13T, xT, Pp, poff, E, 2 * I, H, dw13, s)
+                : wgrad(dh13T, xT, Pp, poff, E, 2 * I, H, dw13, s));  // dw13[e] [2I, H]
 #undef MOE_TRY
     return hipSuccess;
 }

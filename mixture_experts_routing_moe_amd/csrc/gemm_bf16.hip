@@ -103,6 +103,20 @@ struct MTile {
     int e, row0, row_end;
 };
 
+// Tile j of an expert with mt m-tiles (0 <= j < mt * n_tiles) -> (m-tile i,
+// n-tile nt): bands of a m-tiles, each band's tiles n-tile-major, so the
+// kXcdChunk tiles an XCD runs together span about a m-tiles x kXcdChunk / a
+// n-tiles and share both operands in its L2 (with all m-tiles of a big expert
+// under one n-tile, its token rows were re-read for every n-tile).
+__device__ __forceinline__ void band_tile(int j, int mt, int n_tiles, int &i, int &nt) {
+    const int a = min(mt, max(kBandMTiles, kXcdChunk / n_tiles));
+    const int b = j / (a * n_tiles);
+    const int r = j - b * a * n_tiles;
+    const int ab = min(a, mt - b * a);
+    nt = r / ab;
+    i = b * a + (r - nt * ab);
+}
+
 // Tile index -> (expert, rows, n-tile).  Expert e owns mt_e = ceil(count_e /
 // BM) m-tiles, and its mt_e * n_tiles tiles form one contiguous range of the
 // tile index, in bands of m-tiles (below).  The segment is dealt to the
@@ -139,18 +153,8 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             const int mt = readlane_i(tiles, src);
             const int o0 = readlane_i(off, src);
             const int cn = readlane_i(cnt, src);
-            // Tile j of the expert: bands of a m-tiles, each band's tiles
-            // n-tile-major, so the kXcdChunk tiles an XCD runs together span
-            // about a m-tiles x kXcdChunk / a n-tiles and share both operands
-            // in its L2 (with all m-tiles of a big expert under one n-tile,
-            // its token rows were re-read for every n-tile).
-            const int j = L - ex * n_tiles;
-            const int a = min(mt, max(kBandMTiles, kXcdChunk / n_tiles));
-            const int b = j / (a * n_tiles);
-            const int r = j - b * a * n_tiles;
-            const int ab = min(a, mt - b * a);
-            nt = r / ab;
-            const int i = b * a + (r - nt * ab);
+            int i;
+            band_tile(L - ex * n_tiles, mt, n_tiles, i, nt);
             t.e = c + src;
             // Rows per m-tile: the expert's rows dealt in equal shares
             // rounded up to whole 32-row fragments (at most BM; never an
@@ -736,6 +740,105 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     }
 }
 
+// Weight gradients on the same machinery: C_e [M, N] float32 (at C + e M N)
+// = sum over k in expert e's padded segment [poff[e], poff[e+1]) of
+// A[m, k] B[n, k], A [M, ld] and B [N, ld] bf16 with k contiguous (the
+// backward's operands transposed to [columns, positions], each segment padded
+// to whole k-tiles with zeros).  Every expert has ceil(M / BM) x ceil(N / BN)
+// tiles, numbered expert by expert in the banded order; m rows play the token
+// rows' part, n rows the weight rows'.  An expert with no rows runs no k-tile
+// and writes zeros.  A tile's cost is its expert's row count, so with
+// `chunked` (experts with at least a chunk of tiles for every XCD) tiles go
+// to the XCDs in chunks as in the forward, sharing operands in each L2;
+// otherwise block b takes tile b, spreading every expert over all XCDs (a
+// chunk would put most of a skewed expert's work on one XCD).
+__global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_bf16_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int ld,
+    const int32_t *__restrict__ poff, int E, int M, int N, int m_tiles, int n_tiles,
+    float *__restrict__ C, int a_bytes, int b_bytes, int chunked) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
+    const int bid = blockIdx.x;
+    const int slot = bid >> 3;
+    const int L = chunked ? ((slot / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + slot % kXcdChunk
+                          : bid;
+    const int per_e = m_tiles * n_tiles;
+    if (L >= E * per_e) return;
+    const int e = L / per_e;
+    int mi, nt;
+    band_tile(L - e * per_e, m_tiles, n_tiles, mi, nt);
+    MTile tile;
+    tile.e = e;
+    tile.row0 = mi * BM;
+    tile.row_end = min(M, tile.row0 + BM);
+    const int kbeg = poff[e];
+    const int nk = (poff[e + 1] - kbeg) / BK;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int rr = lane / kChunks;
+    Ops<true> op;
+    op.a = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, a_bytes, kBufferWord3);
+    op.b = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, b_bytes, kBufferWord3);
+    op.kb = __builtin_amdgcn_readfirstlane(kbeg);
+    op.na = __builtin_amdgcn_readfirstlane(
+        min(NLA, max(0, (tile.row_end - tile.row0 - wv * kTokRowsPerWave + kRowsPerLoad - 1) /
+                            kRowsPerLoad)));
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+        const int r = wv * kTokRowsPerWave + i * kRowsPerLoad + rr;
+        const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
+        const int m = min(tile.row0 + r, tile.row_end - 1);
+        op.aoff[i] = ((uint32_t)m * (uint32_t)ld + (uint32_t)c8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+        const int r = wv * kWRowsPerWave + i * kRowsPerLoad + rr;
+        const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
+        const int n = min(nt * BN + r, N - 1);
+        op.boff[i] = ((uint32_t)n * (uint32_t)ld + (uint32_t)c8) * 2u;
+    }
+
+    const int wn = wave % WN;
+    const int wm = wave / WN;
+    const int lr = lane & 31;
+    const int lk = lane >> 5;
+    const int sw = swz(lr);
+    const int wrow0 = wn * (BN / WN);
+    const int xrow = wm * (BM / WM) + lr;
+    FragAddr fa;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const uint32_t ch = (uint32_t)(((2 * j + lk) ^ sw) * 16);
+        fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
+        fa.x[j] = (uint32_t)(xrow * BK * 2) + ch;
+    }
+    float *Ce = C + (int64_t)e * M * N;
+    const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
+    switch (mvalid) {
+        case 5:
+            if constexpr (MF >= 5)
+                run_tile<5, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+        case 4:
+            run_tile<4, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+        case 3:
+            run_tile<3, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+        case 2:
+            run_tile<2, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+        case 1:
+            run_tile<1, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+        default:
+            run_tile<0, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            break;
+    }
+}
+
 int m_slot_bound(int64_t rows, int E) {
     const int64_t nz = rows < E ? rows : E;
     return (int)((rows + BM - 1) / BM + nz);
@@ -798,6 +901,23 @@ hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const i
     const dim3 grid(grid_of(m_slots, n_tiles));
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true>), grid, dim3(kThreads), 0, s,
                        a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes);
+    return hipGetLastError();
+}
+
+bool wgrad_grouped_ok(int M, int N, int64_t ld) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)M * ld * 2 < lim && (int64_t)N * ld * 2 < lim && ld % BK == 0;
+}
+
+hipError_t launch_wgrad_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
+                             const int32_t *poff, int E, int M, int N, float *c, hipStream_t s) {
+    if (!wgrad_grouped_ok(M, N, ld)) return hipErrorInvalidValue;
+    const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+    const dim3 grid(grid_of(m_tiles * E, n_tiles));
+    const int chunked = m_tiles * n_tiles >= 8 * kXcdChunk;
+    hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, grid, dim3(kThreads), 0, s, a, b, (int)ld, poff,
+                       E, M, N, m_tiles, n_tiles, c, (int)(M * ld * 2), (int)(N * ld * 2),
+                       chunked);
     return hipGetLastError();
 }
 

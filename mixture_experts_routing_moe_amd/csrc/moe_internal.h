@@ -297,6 +297,13 @@ bool down_kmajor_ok(int64_t T, int N, int K, int k);
 hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const int32_t *offsets,
                                    int64_t T, int N, int K, int E, int k, float *y,
                                    hipStream_t s);
+// Weight gradients C_e [M, N] f32 = sum over k in [poff[e], poff[e+1]) of
+// a[m, k] b[n, k] (a [M, ld], b [N, ld] bf16, segments padded to whole
+// 64-wide k-tiles) on the grouped kernel's machinery; needs buffer
+// addressing (wgrad_grouped_ok).
+bool wgrad_grouped_ok(int M, int N, int64_t ld);
+hipError_t launch_wgrad_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
+                             const int32_t *poff, int E, int M, int N, float *c, hipStream_t s);
 // K slices the prefill FC2 uses for this shape (1 .. 4).
 int down_splits(int64_t T, int H, int I, int E, int k);
 
