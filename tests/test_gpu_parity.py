@@ -623,6 +623,7 @@ def _full_layer(name, decode, sample=None):
     print(f"{name}: oracle on {len(toks)} of {w.T} tokens", flush=True)
     ref = oracle.expert_ffn(inp["hidden"], inp["w13"], inp["w2"], ow, oids, "bf16", tokens=toks)
     rel = assert_bf16_layer(got[toks], got32[toks], ref)
+    print(f"{name}: max |error| / RMS = {rel:.3g}", flush=True)
     assert np.all(np.isfinite(got))
     return got, rel
 
