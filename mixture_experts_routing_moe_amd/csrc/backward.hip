@@ -586,6 +586,19 @@ bool kmajor_weights(int64_t T, int H, int I, int k) {
     return down_kmajor_ok(T, I, H, k) && down_kmajor_ok(T, H, 2 * I, k);
 }
 
+// The weight gradients read w act and [d_gate ; d_up] as stored, per position
+// (the grouped weight-gradient kernel's K-major variant; dw13 is stored
+// through its transposing epilogue), and only dy and x are transposed,
+// unless an operand is too large for its buffer addressing.
+// MOE_BWD_TRANSPOSED_OPERANDS=1 in the environment transposes all four at any
+// size (tests compare the two).
+bool kmajor_wgrad(int64_t T, int H, int I, int E, int k) {
+    const char *v = std::getenv("MOE_BWD_TRANSPOSED_OPERANDS");  // read per call (host only)
+    if (v != nullptr && v[0] == '1') return false;
+    const int64_t Pp = padded_positions(T, E, k);
+    return wgrad_km_ok(H, I, Pp) && wgrad_km_ok(H, 2 * I, Pp);
+}
+
 size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
     const size_t P = (size_t)T * (size_t)k;
     const size_t Pp = (size_t)padded_positions(T, E, k);
@@ -605,8 +618,12 @@ size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
             b = kmajor_weights(T, H, I, k) ? 0 : (size_t)E * H * I * 2;
             break;
         case 9: b = (size_t)H * Pp * 2; break;          // dyT    bf16 [H, Pp]
-        case 10: b = (size_t)I * Pp * 2; break;         // wactT  bf16 [I, Pp]
-        case 11: b = (size_t)2 * I * Pp * 2; break;     // dh13T  bf16 [2I, Pp]
+        case 10:  // wactT bf16 [I, Pp], only on the transposing path
+            b = kmajor_wgrad(T, H, I, E, k) ? 0 : (size_t)I * Pp * 2;
+            break;
+        case 11:  // dh13T bf16 [2I, Pp], only on the transposing path
+            b = kmajor_wgrad(T, H, I, E, k) ? 0 : (size_t)2 * I * Pp * 2;
+            break;
         case 12: b = (size_t)H * Pp * 2; break;         // xT     bf16 [H, Pp]
         case 13: b = (size_t)(E + 1) * 4; break;        // poff   int32 [E+1]
         case 14: b = Pp * 4; break;                     // src    int32 [Pp]
@@ -709,11 +726,18 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
                        H, dx, dw);
     MOE_TRY(hipGetLastError());
 
-    // Weight gradients over the padded, transposed segments.
+    // Weight gradients over the padded, transposed segments of dy and x.
     MOE_TRY(transpose(dys, H, 0, src, Pp, H, dyT, Pp, 0, 1, s));
+    MOE_TRY(transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
+    if (kmajor_wgrad(T, H, I, E, k)) {
+        // dw2[e] [H, I]: dy^T (w act); dw13[e] [2I, H]: ([d_gate ; d_up]^T x),
+        // computed as x^T [d_gate ; d_up] and stored transposed.
+        MOE_TRY(launch_wgrad_km_bf16(dyT, wact, Pp, poff, offsets, E, H, I, false, dw2, s));
+        MOE_TRY(launch_wgrad_km_bf16(xT, dh13, Pp, poff, offsets, E, H, 2 * I, true, dw13, s));
+        return hipSuccess;
+    }
     MOE_TRY(transpose(wact, I, 0, src, Pp, I, wactT, Pp, 0, 1, s));
     MOE_TRY(transpose(dh13, 2 * I, 0, src, Pp, 2 * I, dh13T, Pp, 0, 1, s));
-    MOE_TRY(transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
     // On the grouped kernel's machinery where the operands fit its buffer
     // addressing, else on wgrad_kernel.
     MOE_TRY(wgrad_grouped_ok(H, I, Pp) ? launch_wgrad_bf16(dyT, wactT, Pp, poff, E, H, I, dw2, s)

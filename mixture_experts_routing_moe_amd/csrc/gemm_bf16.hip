@@ -230,6 +230,22 @@ struct OpsKm {
 static_assert(BN == 256 && BK == 64 && NLB * kWaves * 2 == BK,
               "the K-major weight layout: 32 chunks per k-row, two k-rows per DMA instruction");
 
+// The same K-major weight-side layout for an operand whose k-rows are a
+// ragged range of rows of a row-major [rows, ldw] matrix (the backward's
+// per-position operands, one expert's segment): each k-tile's loads go
+// through a buffer resource that starts at the k-tile's first row and ends
+// at the range's end, so k-rows past the range read as zeros.  The token
+// operand is addressed as in Ops<true>.
+struct OpsKmR {
+    __amdgpu_buffer_rsrc_t a;       // token operand
+    const uint16_t *bp;             // first row of the range
+    int kb;                         // first k of the token operand
+    int na;                         // token loads that hold a row of the tile
+    int ldw;                        // elements per row of the ranged operand
+    int rows;                       // rows in the range
+    uint32_t aoff[NLA], boff[NLB];  // byte offsets of this lane's token rows / chunks
+};
+
 // Token load i of a wave is issued only if its rows reach into the tile
 // (i < na, wave-uniform): rows past the expert's segment are never stored, so
 // their LDS rows may hold anything, and skipping them cuts the load traffic
@@ -283,6 +299,26 @@ __device__ __forceinline__ void issue_stage(uint16_t *smem, const OpsKm &op, int
             uint16_t *db = smem + kWOff + S * kWStage + (wave * NLB + i) * 512;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, (lds_void *)db, 16, op.boff[i], sow, 0,
                                                      0);
+        }
+    }
+}
+template <int S>
+__device__ __forceinline__ void issue_stage(uint16_t *smem, const OpsKmR &op, int k0, int wave) {
+    const uint32_t so = 2u * (uint32_t)(op.kb + k0);
+    // At most BK rows of the range from k0 on (a 32-bit record count).
+    const int left = min(BK, max(0, op.rows - k0));
+    const __amdgpu_buffer_rsrc_t b = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(op.bp + (int64_t)k0 * op.ldw), (short)0, left * op.ldw * 2, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < (NLA > NLB ? NLA : NLB); ++i) {
+        if (tok_load(op, i)) {
+            uint16_t *da = smem + S * kTokStage + (wave * kTokRowsPerWave + i * kRowsPerLoad) * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op.a, (lds_void *)da, 16, op.aoff[i], so, 0,
+                                                     0);
+        }
+        if (i < NLB) {
+            uint16_t *db = smem + kWOff + S * kWStage + (wave * NLB + i) * 512;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(b, (lds_void *)db, 16, op.boff[i], 0, 0, 0);
         }
     }
 }
@@ -509,7 +545,10 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
 // fragments.  Each MV has its accumulators to itself: declared outside the
 // dispatch on MV, one set shared by the five loop versions measured slower
 // (the register allocator copies it between them).
-template <int MV, bool kGateUp, typename OpsT, typename FA>
+//
+// kTrans (FC2 form): C is stored transposed, element (token-side row p,
+// weight-side row n) at C[n * plane + p]; p's extent must be a multiple of 4.
+template <int MV, bool kGateUp, bool kTrans = false, typename OpsT, typename FA>
 __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int wv,
                                          const FA &fa, const MTile &tile, int nt, int wn,
                                          int wm, int lr, int lk, int N, int ks, int64_t plane,
@@ -573,7 +612,7 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
         // conflict-free writes.
         constexpr int kP = 36;
         float *ep = reinterpret_cast<float *>(smem) + wv * 32 * kP;
-        float *C = static_cast<float *>(Cv) + ks * plane;
+        float *C = static_cast<float *>(Cv) + (kTrans ? 0 : ks * plane);
         const int lane = lr + 32 * lk;
         const int rl = lane >> 3, cl = (lane & 7) * 4;
 #pragma unroll
@@ -586,13 +625,29 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
                     *reinterpret_cast<float4 *>(ep + lr * kP + rg * 8 + lk * 4) =
                         make_float4(a[rg * 4], a[rg * 4 + 1], a[rg * 4 + 2], a[rg * 4 + 3]);
                 const int p0 = tile.row0 + wm * (BM / WM) + g * 32;
-                const int n = nt * BN + wn * (BN / WN) + f * 32 + cl;
+                if constexpr (kTrans) {
+                    // Lane l: weight-side row 8 i + l / 8 of the fragment,
+                    // token-side rows 4 (l % 8) .. + 3 (a column of the slice).
+                    const int p = p0 + cl;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 v = *reinterpret_cast<const float4 *>(ep + (8 * i + rl) * kP + cl);
-                    const int p = p0 + 8 * i + rl;
-                    if (p < tile.row_end && n < N)
-                        *reinterpret_cast<float4 *>(C + (int64_t)p * N + n) = v;
+                    for (int i = 0; i < 4; ++i) {
+                        const int w = 8 * i + rl;
+                        const float4 v = make_float4(ep[cl * kP + w], ep[(cl + 1) * kP + w],
+                                                     ep[(cl + 2) * kP + w], ep[(cl + 3) * kP + w]);
+                        const int n = nt * BN + wn * (BN / WN) + f * 32 + w;
+                        if (p < tile.row_end && n < N)
+                            *reinterpret_cast<float4 *>(C + (int64_t)n * plane + p) = v;
+                    }
+                } else {
+                    const int n = nt * BN + wn * (BN / WN) + f * 32 + cl;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 v =
+                            *reinterpret_cast<const float4 *>(ep + (8 * i + rl) * kP + cl);
+                        const int p = p0 + 8 * i + rl;
+                        if (p < tile.row_end && n < N)
+                            *reinterpret_cast<float4 *>(C + (int64_t)p * N + n) = v;
+                    }
                 }
             }
         }
@@ -773,21 +828,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 }
 
 // Weight gradients on the same machinery: C_e [M, N] float32 (at C + e M N)
-// = sum over k in expert e's padded segment [poff[e], poff[e+1]) of
-// A[m, k] B[n, k], A [M, ld] and B [N, ld] bf16 with k contiguous (the
-// backward's operands transposed to [columns, positions], each segment padded
-// to whole k-tiles with zeros).  Every expert has ceil(M / BM) x ceil(N / BN)
-// tiles, numbered expert by expert in the banded order; m rows play the token
-// rows' part, n rows the weight rows'.  An expert with no rows runs no k-tile
-// and writes zeros.  A tile's cost is its expert's row count, so with
-// `chunked` (experts with at least a chunk of tiles for every XCD) tiles go
-// to the XCDs in chunks as in the forward, sharing operands in each L2;
-// otherwise block b takes tile b, spreading every expert over all XCDs (a
-// chunk would put most of a skewed expert's work on one XCD).
+// = sum over the k of expert e of A[m, k] B[n, k].  A [M, ld] bf16 has k
+// contiguous: the backward's operand transposed to [columns, positions], each
+// expert's segment padded to whole k-tiles with zeros, k in [poff[e],
+// poff[e+1]).  B is either the same kind of operand ([N, ld], kKmB false) or
+// (kKmB) the per-position operand as stored, [positions, N] with N contiguous:
+// its k-rows are expert e's positions [offs[e], offs[e+1]), read K-major
+// through the transposing fragment reads, the rows past the segment read as
+// zeros (OpsKmR).  kTrans stores C_e transposed, as [N, M].  Every expert has
+// ceil(M / BM) x ceil(N / BN) tiles, numbered expert by expert in the banded
+// order; m rows play the token rows' part, n rows the weight rows'.  An
+// expert with no rows runs no k-tile and writes zeros.  A tile's cost is its
+// expert's row count, so with `chunked` (experts with at least a chunk of
+// tiles for every XCD) tiles go to the XCDs in chunks as in the forward,
+// sharing operands in each L2; otherwise block b takes tile b, spreading
+// every expert over all XCDs (a chunk would put most of a skewed expert's
+// work on one XCD).
+template <bool kKmB, bool kTrans>
 __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int ld,
-    const int32_t *__restrict__ poff, int E, int M, int N, int m_tiles, int n_tiles,
-    float *__restrict__ C, int a_bytes, int b_bytes, int chunked) {
+    const int32_t *__restrict__ poff, const int32_t *__restrict__ offs, int E, int M, int N,
+    int m_tiles, int n_tiles, float *__restrict__ C, int a_bytes, int b_bytes, int chunked) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
     const int bid = blockIdx.x;
     const int slot = bid >> 3;
@@ -810,9 +871,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_bf16_kernel(
     const int wave = tid >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int rr = lane / kChunks;
-    Ops<true> op;
+    using OpsT = typename std::conditional<kKmB, OpsKmR, Ops<true>>::type;
+    OpsT op;
     op.a = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, a_bytes, kBufferWord3);
-    op.b = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, b_bytes, kBufferWord3);
+    if constexpr (kKmB) {
+        const int r0 = __builtin_amdgcn_readfirstlane(offs[e]);
+        op.bp = B + (int64_t)r0 * N;
+        op.rows = __builtin_amdgcn_readfirstlane(offs[e + 1] - r0);
+        op.ldw = N;
+    } else {
+        op.b = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, b_bytes, kBufferWord3);
+    }
     op.kb = __builtin_amdgcn_readfirstlane(kbeg);
     op.na = __builtin_amdgcn_readfirstlane(
         min(NLA, max(0, (tile.row_end - tile.row0 - wv * kTokRowsPerWave + kRowsPerLoad - 1) /
@@ -826,10 +895,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_bf16_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NLB; ++i) {
-        const int r = wv * kWRowsPerWave + i * kRowsPerLoad + rr;
-        const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
-        const int n = min(nt * BN + r, N - 1);
-        op.boff[i] = ((uint32_t)n * (uint32_t)ld + (uint32_t)c8) * 2u;
+        if constexpr (kKmB) {
+            // As for OpsKm: DMA instruction wv NLB + i fills k-rows
+            // kk = 2 (wv NLB + i) + lane / 32 of the stage, chunk
+            // (lane % 32) ^ 4 (kk % 4) of each.
+            const int kk = 2 * (wv * NLB + i) + (lane >> 5);
+            const int c = (lane & 31) ^ (4 * (kk & 3));
+            const int n = min(nt * BN + 8 * c, N - 8);
+            op.boff[i] = ((uint32_t)kk * (uint32_t)N + (uint32_t)n) * 2u;
+        } else {
+            const int r = wv * kWRowsPerWave + i * kRowsPerLoad + rr;
+            const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
+            const int n = min(nt * BN + r, N - 1);
+            op.boff[i] = ((uint32_t)n * (uint32_t)ld + (uint32_t)c8) * 2u;
+        }
     }
 
     const int wn = wave % WN;
@@ -839,34 +918,47 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_bf16_kernel(
     const int sw = swz(lr);
     const int wrow0 = wn * (BN / WN);
     const int xrow = wm * (BM / WM) + lr;
-    FragAddr fa;
+    using FA = typename std::conditional<kKmB, FragAddrKm, FragAddr>::type;
+    FA fa;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
         const uint32_t ch = (uint32_t)(((2 * j + lk) ^ sw) * 16);
-        fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
+        if constexpr (!kKmB) fa.w[j] = (uint32_t)((kWOff + (wrow0 + lr) * BK) * 2) + ch;
         fa.x[j] = (uint32_t)(xrow * BK * 2) + ch;
+    }
+    if constexpr (kKmB) {
+        // The transposing reads' addresses, as in the forward kernel.
+        const int g = lane >> 4, sl = lane & 15;
+        const int krow = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int chunk = (wrow0 + 32 * f) / 8 + 2 * (g & 1) + ((sl & 3) >> 1);
+            fa.w[f] = (uint32_t)(kWOff * 2 + (krow * 32 + (chunk ^ (4 * (sl >> 2)))) * 16 +
+                                 8 * (sl & 1));
+        }
     }
     float *Ce = C + (int64_t)e * M * N;
     const int mvalid = min(MF, max(0, (tile.row_end - tile.row0 - wm * (BM / WM) + 31) / 32));
     switch (mvalid) {
         case 5:
             if constexpr (MF >= 5)
-                run_tile<5, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+                run_tile<5, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M,
+                                           Ce);
             break;
         case 4:
-            run_tile<4, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            run_tile<4, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M, Ce);
             break;
         case 3:
-            run_tile<3, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            run_tile<3, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M, Ce);
             break;
         case 2:
-            run_tile<2, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            run_tile<2, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M, Ce);
             break;
         case 1:
-            run_tile<1, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            run_tile<1, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M, Ce);
             break;
         default:
-            run_tile<0, false>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, 0, Ce);
+            run_tile<0, false, kTrans>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, 0, M, Ce);
             break;
     }
 }
@@ -947,9 +1039,33 @@ hipError_t launch_wgrad_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const dim3 grid(grid_of(m_tiles * E, n_tiles));
     const int chunked = m_tiles * n_tiles >= 8 * kXcdChunk;
-    hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, grid, dim3(kThreads), 0, s, a, b, (int)ld, poff,
-                       E, M, N, m_tiles, n_tiles, c, (int)(M * ld * 2), (int)(N * ld * 2),
-                       chunked);
+    hipLaunchKernelGGL((grouped_wgrad_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, a, b,
+                       (int)ld, poff, nullptr, E, M, N, m_tiles, n_tiles, c, (int)(M * ld * 2),
+                       (int)(N * ld * 2), chunked);
+    return hipGetLastError();
+}
+
+bool wgrad_km_ok(int M, int N, int64_t ld) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)M * ld * 2 < lim && (int64_t)BK * N * 2 < lim && ld % BK == 0 && N % 8 == 0 &&
+           M % 4 == 0;
+}
+
+hipError_t launch_wgrad_km_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
+                                const int32_t *poff, const int32_t *offs, int E, int M, int N,
+                                bool trans, float *c, hipStream_t s) {
+    if (!wgrad_km_ok(M, N, ld)) return hipErrorInvalidValue;
+    const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+    const dim3 grid(grid_of(m_tiles * E, n_tiles));
+    const int chunked = m_tiles * n_tiles >= 8 * kXcdChunk;
+    if (trans)
+        hipLaunchKernelGGL((grouped_wgrad_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, a,
+                           b, (int)ld, poff, offs, E, M, N, m_tiles, n_tiles, c,
+                           (int)(M * ld * 2), 0, chunked);
+    else
+        hipLaunchKernelGGL((grouped_wgrad_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, a,
+                           b, (int)ld, poff, offs, E, M, N, m_tiles, n_tiles, c,
+                           (int)(M * ld * 2), 0, chunked);
     return hipGetLastError();
 }
 

@@ -304,6 +304,14 @@ hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const i
 bool wgrad_grouped_ok(int M, int N, int64_t ld);
 hipError_t launch_wgrad_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
                              const int32_t *poff, int E, int M, int N, float *c, hipStream_t s);
+// The same with b the per-position operand as stored, [positions, N] (N
+// contiguous), expert e's k-rows being its positions [offs[e], offs[e+1])
+// (read past the segment as zeros); `trans` stores C_e transposed, [N, M].
+// Needs wgrad_km_ok (buffer addressing for a, N % 8 == 0, M % 4 == 0).
+bool wgrad_km_ok(int M, int N, int64_t ld);
+hipError_t launch_wgrad_km_bf16(const uint16_t *a, const uint16_t *b, int64_t ld,
+                                const int32_t *poff, const int32_t *offs, int E, int M, int N,
+                                bool trans, float *c, hipStream_t s);
 // K slices the prefill FC2 uses for this shape (1 .. 4).
 int down_splits(int64_t T, int H, int I, int E, int k);
 

@@ -182,6 +182,28 @@ def test_ffn_backward_kmajor_weights(monkeypatch, T, H, I, E, k, skew, inv):
                                       err_msg=name)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,skew,inv", [(300, 128, 192, 8, 2, 0.0, 0.0),
+                                                (513, 192, 320, 16, 4, 0.5, 0.1),
+                                                (700, 64, 1408, 4, 2, 1.0, 0.0),
+                                                (90, 320, 64, 3, 3, 0.0, 0.0),
+                                                (1000, 448, 128, 5, 1, 2.0, 0.0)])
+def test_ffn_backward_kmajor_wgrad(monkeypatch, T, H, I, E, k, skew, inv):
+    """The weight gradients read w act and [d_gate ; d_up] as stored, per
+    position (the K-major weight-gradient kernel, each expert's segment tail
+    read as zeros; dw13 stored through the transposing epilogue): the same
+    products over the same k order as the path that transposes all four
+    operands first, so every gradient is bit-identical to it."""
+    x, w13, w2, w32, ids, dy = _rand_case(T * 7 + H, T, H, I, E, k, skew, inv)
+    print(f"kmajor wgrad T={T} H={H} I={I} E={E} k={k}", flush=True)
+    got = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.setenv("MOE_BWD_TRANSPOSED_OPERANDS", "1")
+    ref = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.delenv("MOE_BWD_TRANSPOSED_OPERANDS")
+    for name in got:
+        np.testing.assert_array_equal(got[name].view(np.uint32), ref[name].view(np.uint32),
+                                      err_msg=name)
+
+
 def test_ffn_backward_deterministic():
     x, w13, w2, w32, ids, dy = _rand_case(5, 300, 128, 192, 8, 2)
     a = _bwd_gpu(x, w13, w2, w32, ids, dy)
