@@ -425,9 +425,10 @@ moe_status_t moe_router_backward(moe_dtype_t dt, const void *hidden, const void 
  * slot names gets zero weight gradients (every element of every output is
  * written).  gate/up are recomputed.  MOE_BF16: five grouped bf16 products
  * on the matrix cores; w act and d_gate/d_up are rounded to bfloat16 as the
- * inputs of those products, everything else accumulates in float32, and the
- * call writes w13 and w2 transposed per expert into the workspace (weights
- * change between training steps, so nothing is cached).  MOE_F32 (small
+ * inputs of those products, everything else accumulates in float32; w13 and
+ * w2 are read as stored (a weight past 2 GiB is first transposed per expert
+ * into the workspace; weights change between training steps, so nothing is
+ * cached).  MOE_F32 (small
  * layers): float32 throughout, one thread per output element.  Results are
  * deterministic.
  *
@@ -437,8 +438,9 @@ moe_status_t moe_router_backward(moe_dtype_t dt, const void *hidden, const void 
  * moe_align for the forward's ids.  Outputs float32: grad_hidden [T, H],
  * grad_w13 [E, 2I, H], grad_w2 [E, H, I], grad_topk_w [T, k].
  * workspace >= moe_expert_ffn_backward_workspace_size(T, H, I, E, k) bytes
- * (about T*k*(24 I + 12 H) + 6 E H I: the bfloat16 path's need, which also
- * covers the float32 path's T*k*(6 I + H)*4), 16-byte aligned, clobbered.
+ * (the larger of the bfloat16 path's need, about T*k*(10 I + 12 H) +
+ * 256 E H, and the float32 path's T*k*(6 I + H)*4), 16-byte aligned,
+ * clobbered.
  * Requires H % 64 == 0, I % 64 == 0; hidden, weights, grad_out and the
  * gradients 16-byte aligned.  T = 0 enqueues nothing, as for every call, so
  * the weight gradients are then left as they were.

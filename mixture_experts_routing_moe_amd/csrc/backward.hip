@@ -328,13 +328,27 @@ __global__ __launch_bounds__(256) void bwd_act_kernel(const float *__restrict__ 
 
 // grad_hidden[t] = sum over slots j = 0..k-1 (in order) of dx[slot_to_sorted[t,
 // j]]; slots with no position (invalid id) add nothing and get grad_topk_w 0.
+// With gw_part, a valid slot's grad_topk_w is also written here: the sum of
+// its position's gw_tiles partial sums, in tile order.
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ dxs,
                                                      const int32_t *__restrict__ slot_to_sorted,
                                                      int k, int H, float *__restrict__ dx,
-                                                     float *__restrict__ grad_w) {
+                                                     float *__restrict__ grad_w,
+                                                     const float *__restrict__ gw_part,
+                                                     int gw_tiles) {
     const int64_t t = blockIdx.x;
     const int32_t *s2s = slot_to_sorted + t * k;
-    if ((int)threadIdx.x < k && s2s[threadIdx.x] < 0) grad_w[t * k + threadIdx.x] = 0.f;
+    if ((int)threadIdx.x < k) {
+        const int p = s2s[threadIdx.x];
+        if (p < 0) {
+            grad_w[t * k + threadIdx.x] = 0.f;
+        } else if (gw_part != nullptr) {
+            const float *g = gw_part + (int64_t)p * gw_tiles;
+            float sum = 0.f;
+            for (int i = 0; i < gw_tiles; ++i) sum += g[i];
+            grad_w[t * k + threadIdx.x] = sum;
+        }
+    }
     for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
@@ -599,12 +613,25 @@ bool kmajor_wgrad(int64_t T, int H, int I, int E, int k) {
     return wgrad_km_ok(H, I, Pp) && wgrad_km_ok(H, 2 * I, Pp);
 }
 
+// The SiLU-and-mul backward runs in the epilogue of the gate/up recompute
+// (launch_gate_up_bwd_bf16), so gate/up are never stored, unless the
+// operands are too large for its buffer addressing; then the recompute writes
+// them (float32) and bwd_act_kernel follows.  MOE_BWD_UNFUSED_ACT=1 in the
+// environment takes the separate path at any size (tests compare the two).
+bool fused_act(int64_t T, int H, int I) {
+    const char *v = std::getenv("MOE_BWD_UNFUSED_ACT");  // read per call (host only)
+    if (v != nullptr && v[0] == '1') return false;
+    return gate_up_bwd_ok(T, H, I);
+}
+
 size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
     const size_t P = (size_t)T * (size_t)k;
     const size_t Pp = (size_t)padded_positions(T, E, k);
     size_t b = 0;
     switch (part) {
-        case 0: b = P * 2 * I * 4; break;               // h13    f32  [P, 2I]
+        case 0:  // h13 f32 [P, 2I], or with the fused epilogue gw_part f32 [P, tiles]
+            b = fused_act(T, H, I) ? P * gate_up_bwd_tiles(I) * 4 : P * 2 * I * 4;
+            break;
         case 1: b = P * I * 4; break;                   // G      f32  [P, I]
         case 2: b = P * I * 2; break;                   // wact   bf16 [P, I]
         case 3: b = P * 2 * I * 2; break;               // dh13   bf16 [P, 2I]
@@ -676,6 +703,7 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
         base += part_bytes(T, H, I, E, k, i);
     }
     float *h13 = reinterpret_cast<float *>(part[0]);
+    float *gw_part = h13;  // the same part on the fused path
     float *G = reinterpret_cast<float *>(part[1]);
     uint16_t *wact = reinterpret_cast<uint16_t *>(part[2]);
     uint16_t *dh13 = reinterpret_cast<uint16_t *>(part[3]);
@@ -713,17 +741,25 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
                        offsets, poff, E, Pp, src);
     MOE_TRY(hipGetLastError());
 
-    // Row-segment products on the forward's grouped kernel (FC2 form).
-    MOE_TRY(launch_down_bf16(xs, w13, offsets, T, 2 * I, H, E, k, 1, h13, s));  // gate/up
+    // Row-segment products on the forward's grouped kernel: G (FC2 form),
+    // then gate/up recomputed (FC1 form) with the SiLU-and-mul backward in
+    // its epilogue, or (FC2 form) stored for bwd_act_kernel.
+    const bool fused = fused_act(T, H, I);
     MOE_TRY(km ? launch_down_kmajor_bf16(dys, w2, offsets, T, I, H, E, k, G, s)   // G
                : launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));
-    hipLaunchKernelGGL(bwd_act_kernel, dim3((unsigned)P), dim3(256), 0, s, h13, G, topk_w,
-                       offsets, sorted_slot, E, I, wact, dh13, dw);
-    MOE_TRY(hipGetLastError());
+    if (fused) {
+        MOE_TRY(launch_gate_up_bwd_bf16(x, w13, offsets, sorted_tok, sorted_slot, topk_w, G, T, H,
+                                        I, E, k, wact, dh13, gw_part, s));
+    } else {
+        MOE_TRY(launch_down_bf16(xs, w13, offsets, T, 2 * I, H, E, k, 1, h13, s));  // gate/up
+        hipLaunchKernelGGL(bwd_act_kernel, dim3((unsigned)P), dim3(256), 0, s, h13, G, topk_w,
+                           offsets, sorted_slot, E, I, wact, dh13, dw);
+        MOE_TRY(hipGetLastError());
+    }
     MOE_TRY(km ? launch_down_kmajor_bf16(dh13, w13, offsets, T, H, 2 * I, E, k, dxs, s)
                : launch_down_bf16(dh13, w13t, offsets, T, H, 2 * I, E, k, 1, dxs, s));  // d_hidden
     hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
-                       H, dx, dw);
+                       H, dx, dw, fused ? gw_part : nullptr, gate_up_bwd_tiles(I));
     MOE_TRY(hipGetLastError());
 
     // Weight gradients over the padded, transposed segments of dy and x.
@@ -774,7 +810,7 @@ hipError_t launch_ffn_backward_f32(const float *x, const float *w13, const float
                        0, s, d13, w13, offsets, H, I, E, dxs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
-                       H, dx, dw);
+                       H, dx, dw, nullptr, 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(f32_wgrad_kernel, dim3((unsigned)(E * H), (unsigned)((I + 255) / 256)),
                        dim3(256), 0, s, x, dy, act, d13, topk_w, offsets, sorted_tok, sorted_slot,

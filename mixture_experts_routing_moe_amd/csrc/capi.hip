@@ -607,7 +607,9 @@ moe_status_t moe_route_grouped_backward(const float *scores, const int32_t *topk
 size_t moe_expert_ffn_backward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E,
                                               int32_t k) {
     if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-    return moe::ffn_backward_scratch_bytes(T, H, I, E, k);
+    const size_t b16 = moe::ffn_backward_scratch_bytes(T, H, I, E, k);
+    const size_t f32 = moe::ffn_backward_f32_scratch_bytes(T, H, I, k);
+    return b16 > f32 ? b16 : f32;
 }
 
 moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const void *w13,

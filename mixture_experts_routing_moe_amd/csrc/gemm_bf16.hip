@@ -541,6 +541,25 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
     k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
 }
 
+// Operands of the FC1-form epilogue that applies the SiLU-and-mul backward
+// to the recomputed gate/up (kBwd): per aligned position p and column c < N,
+// from gate z and up u (the accumulators), G[p, c] and the slot's routing
+// weight w = topk_w[sorted_slot[p]], with s = sigmoid(z) and a = z s u:
+//   wact[p, c]       = bf16(w a)
+//   dh13[p, c]       = bf16(w G u s (1 + z (1 - s)))      (d_gate)
+//   dh13[p, N + c]   = bf16(w G z s)                      (d_up)
+//   gw_part[p, nt]   = sum over the tile's columns c of G[p, c] a
+// (n-tile nt of the launch; the routing-weight gradient is the sum of a
+// row's parts in n-tile order, taken later).
+struct BwdAct {
+    const float *G;
+    const float *topk_w;
+    const int32_t *sorted_slot;
+    uint16_t *wact, *dh13;
+    float *gw_part;
+    int n_tiles;
+};
+
 // The k loop and the epilogue of one tile whose waves hold MV valid token
 // fragments.  Each MV has its accumulators to itself: declared outside the
 // dispatch on MV, one set shared by the five loop versions measured slower
@@ -548,11 +567,12 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
 //
 // kTrans (FC2 form): C is stored transposed, element (token-side row p,
 // weight-side row n) at C[n * plane + p]; p's extent must be a multiple of 4.
-template <int MV, bool kGateUp, bool kTrans = false, typename OpsT, typename FA>
+template <int MV, bool kGateUp, bool kTrans = false, bool kBwd = false, typename OpsT,
+          typename FA>
 __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int wv,
                                          const FA &fa, const MTile &tile, int nt, int wn,
                                          int wm, int lr, int lk, int N, int ks, int64_t plane,
-                                         void *__restrict__ Cv) {
+                                         void *__restrict__ Cv, const BwdAct &bw = BwdAct{}) {
     f32x16 acc[NF][MF];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
@@ -563,7 +583,67 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
     // the weight side and column lr of the token side.
-    if (kGateUp) {
+    if constexpr (kGateUp && kBwd) {
+        // SiLU-and-mul backward (BwdAct).  Lane (lr, lk) of the wave holds,
+        // for token row lr of fragment g, gate and up at columns
+        // c0 + 8 rg + 4 lk .. + 3 (rg = 0..3); it reads G there (16 bytes),
+        // writes its three bf16 results (8 bytes each) and sums G a.  The
+        // row sums of the 4 waves sharing the rows meet in LDS and are added
+        // in wave order.
+        float *red = reinterpret_cast<float *>(smem);  // [WM][MF][32][WN]
+        const int c0 = nt * (BN / 2) + wn * (BN / 2 / WN);
+#pragma unroll
+        for (int g = 0; g < MV; ++g) {
+            const int p = tile.row0 + wm * (BM / WM) + g * 32 + lr;
+            const bool prow = p < tile.row_end;
+            const float w = prow ? bw.topk_w[bw.sorted_slot[p]] : 0.f;
+            float sum = 0.f;
+#pragma unroll
+            for (int f = 0; f < NF / 2; ++f) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int c = c0 + f * 32 + rg * 8 + lk * 4;
+                    if (!prow || c >= N) continue;
+                    const f32x4 gg = *reinterpret_cast<const f32x4 *>(bw.G + (int64_t)p * N + c);
+                    uint16_t a16[4], dg16[4], du16[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float z = acc[f][g][rg * 4 + q], u = acc[f + NF / 2][g][rg * 4 + q];
+                        const float sg = 1.0f / (1.0f + __expf(-z));
+                        const float a = z * sg * u;
+                        a16[q] = __builtin_bit_cast(uint16_t, to_bf16(w * a));
+                        sum += gg[q] * a;
+                        const float da = w * gg[q];
+                        dg16[q] = __builtin_bit_cast(uint16_t,
+                                                     to_bf16(da * u * sg * (1.0f + z * (1.0f - sg))));
+                        du16[q] = __builtin_bit_cast(uint16_t, to_bf16(da * z * sg));
+                    }
+                    const int64_t o = (int64_t)p * N + c, o2 = (int64_t)p * 2 * N + c;
+                    *reinterpret_cast<uint2 *>(bw.wact + o) =
+                        uint2{a16[0] | ((uint32_t)a16[1] << 16), a16[2] | ((uint32_t)a16[3] << 16)};
+                    *reinterpret_cast<uint2 *>(bw.dh13 + o2) = uint2{
+                        dg16[0] | ((uint32_t)dg16[1] << 16), dg16[2] | ((uint32_t)dg16[3] << 16)};
+                    *reinterpret_cast<uint2 *>(bw.dh13 + o2 + N) = uint2{
+                        du16[0] | ((uint32_t)du16[1] << 16), du16[2] | ((uint32_t)du16[3] << 16)};
+                }
+            }
+            sum += __shfl_xor(sum, 32);
+            if (lk == 0) red[((wm * MF + g) * 32 + lr) * WN + wn] = sum;
+        }
+        __syncthreads();
+        const int tid = threadIdx.x;
+        if (tid < BM) {
+            const int p = tile.row0 + tid;
+            if (p < tile.row_end) {
+                const float *r = red + ((tid / (BM / WM)) * MF + (tid % (BM / WM)) / 32) * 32 * WN +
+                                 (tid % 32) * WN;
+                float t = r[0];
+#pragma unroll
+                for (int i = 1; i < WN; ++i) t += r[i];
+                bw.gw_part[(int64_t)p * bw.n_tiles + nt] = t;
+            }
+        }
+    } else if (kGateUp) {
         // The block's activation tile (BM rows x BN / 2 columns, bf16) is
         // gathered in LDS from all waves, then stored as whole rows: each
         // instruction writes 4 rows x 256 bytes (straight from the
@@ -664,11 +744,13 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 // kBuf selects the operand addressing (Ops); a_bytes is the token operand's
 // size in bytes (used by kBuf only).
 // kKm (FC2 form, buffer addressing only): W is K-major, [E, K, N].
-template <bool kGateUp, bool kBuf, bool kKm = false>
+// kBwd (FC1 form): the epilogue applies the SiLU-and-mul backward (BwdAct)
+// instead of writing act.
+template <bool kGateUp, bool kBuf, bool kKm = false, bool kBwd = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
-    int E, int K, int N, int n_tiles, int ksplit, int64_t plane, int a_bytes) {
+    int E, int K, int N, int n_tiles, int ksplit, int64_t plane, int a_bytes, BwdAct bw) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
 
     // Block -> tile.  Workgroups are dealt round-robin to the 8 XCDs (block b
@@ -801,28 +883,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     switch (mvalid) {
         case 5:
             if constexpr (MF >= 5)
-                run_tile<5, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks, plane,
-                                     Cv);
+                run_tile<5, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks, plane,
+                                     Cv, bw);
             break;
         case 4:
-            run_tile<4, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv);
+            run_tile<4, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv, bw);
             break;
         case 3:
-            run_tile<3, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv);
+            run_tile<3, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv, bw);
             break;
         case 2:
-            run_tile<2, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv);
+            run_tile<2, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv, bw);
             break;
         case 1:
-            run_tile<1, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv);
+            run_tile<1, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv, bw);
             break;
         default:
-            run_tile<0, kGateUp>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv);
+            run_tile<0, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
+                                 plane, Cv, bw);
             break;
     }
 }
@@ -1000,13 +1082,45 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
     if (use_buffer_path(a_bytes, w_bytes))
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s,
                            hidden, sorted_tok, w13, offsets, act, E, H, I, n_tiles, 1, (int64_t)0,
-                           (int)a_bytes);
+                           (int)a_bytes, BwdAct{});
     else
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s,
                            hidden, sorted_tok, w13, offsets, act, E, H, I, n_tiles, 1, (int64_t)0,
-                           0);
+                           0, BwdAct{});
     return hipGetLastError();
 }
+
+bool gate_up_bwd_ok(int64_t T, int H, int I) {
+    return use_buffer_path(T * H * 2, (int64_t)2 * I * H * 2);
+}
+
+hipError_t launch_gate_up_bwd_bf16(const uint16_t *hidden, const uint16_t *w13,
+                                   const int32_t *offsets, const int32_t *sorted_tok,
+                                   const int32_t *sorted_slot, const float *topk_w,
+                                   const float *G, int64_t T, int H, int I, int E, int k,
+                                   uint16_t *wact, uint16_t *dh13, float *gw_part,
+                                   hipStream_t s) {
+    const int64_t rows = T * k;
+    if (rows == 0) return hipSuccess;
+    if (!gate_up_bwd_ok(T, H, I)) return hipErrorInvalidValue;
+    const int m_slots = m_slot_bound(rows, E);
+    const int n_tiles = gate_up_bwd_tiles(I);
+    const dim3 grid(grid_of(m_slots, n_tiles));
+    BwdAct bw;
+    bw.G = G;
+    bw.topk_w = topk_w;
+    bw.sorted_slot = sorted_slot;
+    bw.wact = wact;
+    bw.dh13 = dh13;
+    bw.gw_part = gw_part;
+    bw.n_tiles = n_tiles;
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true, false, true>), grid, dim3(kThreads),
+                       0, s, hidden, sorted_tok, w13, offsets, nullptr, E, H, I, n_tiles, 1,
+                       (int64_t)0, (int)(T * H * 2), bw);
+    return hipGetLastError();
+}
+
+int gate_up_bwd_tiles(int I) { return (I + BN / 2 - 1) / (BN / 2); }
 
 bool down_kmajor_ok(int64_t T, int N, int K, int k) {
     const int64_t a_bytes = T * k * (int64_t)K * 2, w_bytes = (int64_t)K * N * 2;
@@ -1024,7 +1138,8 @@ hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const i
     const int64_t a_bytes = rows * K * 2;
     const dim3 grid(grid_of(m_slots, n_tiles));
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true>), grid, dim3(kThreads), 0, s,
-                       a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes);
+                       a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes,
+                       BwdAct{});
     return hipGetLastError();
 }
 
@@ -1105,10 +1220,11 @@ hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32
     if (use_buffer_path(a_bytes, w_bytes))
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s,
                            act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H,
-                           (int)a_bytes);
+                           (int)a_bytes, BwdAct{});
     else
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s,
-                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H, 0);
+                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H, 0,
+                           BwdAct{});
     return hipGetLastError();
 }
 

@@ -290,6 +290,20 @@ hipError_t launch_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
 hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32_t *offsets,
                             int64_t T, int H, int I, int E, int k, int ksplit, float *y,
                             hipStream_t s);
+// The backward's gate/up recompute (x . w13^T on the FC1 kernel) with the
+// SiLU-and-mul backward in its epilogue: from G [T k, I] f32 and the routing
+// weights it writes wact [T k, I] and dh13 [T k, 2I] (bf16, aligned order)
+// and gw_part [T k, gate_up_bwd_tiles(I)] f32, each row's partial sums of
+// G . act per column tile (the routing-weight gradient is their sum in tile
+// order).  Needs buffer addressing (gate_up_bwd_ok).
+bool gate_up_bwd_ok(int64_t T, int H, int I);
+int gate_up_bwd_tiles(int I);
+hipError_t launch_gate_up_bwd_bf16(const uint16_t *hidden, const uint16_t *w13,
+                                   const int32_t *offsets, const int32_t *sorted_tok,
+                                   const int32_t *sorted_slot, const float *topk_w,
+                                   const float *G, int64_t T, int H, int I, int E, int k,
+                                   uint16_t *wact, uint16_t *dh13, float *gw_part,
+                                   hipStream_t s);
 // The FC2-form grouped product with a K-major weight w [E, K, N] (N
 // contiguous): y[p, n] = sum_k a[p, k] w[e, k, n] for the rows p of expert e,
 // float32 [T k, N].  Needs buffer addressing (down_kmajor_ok).

@@ -204,6 +204,34 @@ def test_ffn_backward_kmajor_wgrad(monkeypatch, T, H, I, E, k, skew, inv):
                                       err_msg=name)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,skew,inv", [(300, 128, 192, 8, 2, 0.0, 0.0),
+                                                (513, 192, 320, 16, 4, 0.5, 0.1),
+                                                (700, 64, 1408, 4, 2, 1.0, 0.0),
+                                                (90, 320, 64, 3, 3, 0.0, 0.0),
+                                                (1000, 448, 128, 5, 1, 2.0, 0.0)])
+def test_ffn_backward_fused_act(monkeypatch, T, H, I, E, k, skew, inv):
+    """The SiLU-and-mul backward in the gate/up recompute's epilogue (the FC1
+    kernel's accumulators, the same products in the same k order as the FC2
+    form that stores gate/up for bwd_act_kernel): gradients of hidden, w13 and
+    w2 bit-identical to the separate path; the routing-weight gradient is the
+    same sum over a row's columns in another order (per column tile, then the
+    tiles in order)."""
+    x, w13, w2, w32, ids, dy = _rand_case(T * 11 + I, T, H, I, E, k, skew, inv)
+    print(f"fused act backward T={T} H={H} I={I} E={E} k={k}", flush=True)
+    got = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.setenv("MOE_BWD_UNFUSED_ACT", "1")
+    ref = _bwd_gpu(x, w13, w2, w32, ids, dy)
+    monkeypatch.delenv("MOE_BWD_UNFUSED_ACT")
+    for name in got:
+        if name == "grad_topk_w":
+            scale = float(np.abs(ref[name]).max())
+            np.testing.assert_allclose(got[name], ref[name], rtol=0, atol=1e-5 * scale)
+            assert np.all(got[name][ids < 0] == 0)
+        else:
+            np.testing.assert_array_equal(got[name].view(np.uint32), ref[name].view(np.uint32),
+                                          err_msg=name)
+
+
 def test_ffn_backward_deterministic():
     x, w13, w2, w32, ids, dy = _rand_case(5, 300, 128, 192, 8, 2)
     a = _bwd_gpu(x, w13, w2, w32, ids, dy)
