@@ -584,47 +584,72 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
     // Accumulator r of a 32x32 tile holds row 8 (r / 4) + 4 lk + (r % 4) of
     // the weight side and column lr of the token side.
     if constexpr (kGateUp && kBwd) {
-        // SiLU-and-mul backward (BwdAct).  Lane (lr, lk) of the wave holds,
-        // for token row lr of fragment g, gate and up at columns
-        // c0 + 8 rg + 4 lk .. + 3 (rg = 0..3); it reads G there (16 bytes),
-        // writes its three bf16 results (8 bytes each) and sums G a.  The
-        // row sums of the 4 waves sharing the rows meet in LDS and are added
-        // in wave order.
-        float *red = reinterpret_cast<float *>(smem);  // [WM][MF][32][WN]
-        const int c0 = nt * (BN / 2) + wn * (BN / 2 / WN);
+        // SiLU-and-mul backward (BwdAct), fragment by fragment through this
+        // wave's LDS slice: G's 32 x 32 block is loaded as whole 128-byte rows
+        // and read back in the accumulators' layout (lane (lr, lk): row lr,
+        // columns 8 rg + 4 lk .. + 3); the three bf16 results go the other
+        // way and are stored as 64-byte rows.  The row sums of G . act of the
+        // 4 waves sharing the rows meet in LDS and are added in wave order.
+        static_assert(NF == 2, "one gate and one up fragment per wave");
+        constexpr int kGP = 36;  // G slice pitch (floats)
+        constexpr int kOP = 40;  // result slice pitch (bf16)
+        constexpr int kSlice = 32 * kGP + 3 * 32 * kOP / 2;  // floats per wave
+        float *gs = reinterpret_cast<float *>(smem) + wv * kSlice;
+        uint16_t *os = reinterpret_cast<uint16_t *>(gs + 32 * kGP);
+        float *red = reinterpret_cast<float *>(smem) + kWaves * kSlice;  // [WM][MF][32][WN]
+        static_assert((kWaves * kSlice + WM * MF * 32 * WN) * 4 <= kLds * 2, "epilogue LDS");
+        const int lane = lr + 32 * lk;
+        const int c0 = nt * (BN / 2) + wn * (BN / 2 / WN);  // the wave's first column
+        const bool cval = c0 < N;  // N % 32 == 0: the wave's 32 columns all valid or none
+        uint16_t *const dst[3] = {bw.wact, bw.dh13, bw.dh13 + N};
+        const int64_t ld[3] = {N, 2 * (int64_t)N, 2 * (int64_t)N};
 #pragma unroll
         for (int g = 0; g < MV; ++g) {
-            const int p = tile.row0 + wm * (BM / WM) + g * 32 + lr;
-            const bool prow = p < tile.row_end;
-            const float w = prow ? bw.topk_w[bw.sorted_slot[p]] : 0.f;
+            const int pb = tile.row0 + wm * (BM / WM) + g * 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 8 * i + (lane >> 3), cc = 4 * (lane & 7);
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (pb + rr < tile.row_end && cval)
+                    v = *reinterpret_cast<const f32x4 *>(bw.G + (int64_t)(pb + rr) * N + c0 + cc);
+                *reinterpret_cast<f32x4 *>(gs + rr * kGP + cc) = v;
+            }
+            const int p = pb + lr;
+            const bool ok = p < tile.row_end && cval;
+            const float w = p < tile.row_end ? bw.topk_w[bw.sorted_slot[p]] : 0.f;
             float sum = 0.f;
 #pragma unroll
-            for (int f = 0; f < NF / 2; ++f) {
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = rg * 8 + lk * 4;
+                const f32x4 gg = *reinterpret_cast<const f32x4 *>(gs + lr * kGP + c);
+                uint16_t r16[3][4];
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int c = c0 + f * 32 + rg * 8 + lk * 4;
-                    if (!prow || c >= N) continue;
-                    const f32x4 gg = *reinterpret_cast<const f32x4 *>(bw.G + (int64_t)p * N + c);
-                    uint16_t a16[4], dg16[4], du16[4];
+                for (int q = 0; q < 4; ++q) {
+                    const float z = acc[0][g][rg * 4 + q], u = acc[1][g][rg * 4 + q];
+                    const float sg = 1.0f / (1.0f + __expf(-z));
+                    const float a = z * sg * u;
+                    r16[0][q] = __builtin_bit_cast(uint16_t, to_bf16(w * a));
+                    sum += ok ? gg[q] * a : 0.f;
+                    const float da = w * gg[q];
+                    r16[1][q] = __builtin_bit_cast(uint16_t,
+                                                   to_bf16(da * u * sg * (1.0f + z * (1.0f - sg))));
+                    r16[2][q] = __builtin_bit_cast(uint16_t, to_bf16(da * z * sg));
+                }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float z = acc[f][g][rg * 4 + q], u = acc[f + NF / 2][g][rg * 4 + q];
-                        const float sg = 1.0f / (1.0f + __expf(-z));
-                        const float a = z * sg * u;
-                        a16[q] = __builtin_bit_cast(uint16_t, to_bf16(w * a));
-                        sum += gg[q] * a;
-                        const float da = w * gg[q];
-                        dg16[q] = __builtin_bit_cast(uint16_t,
-                                                     to_bf16(da * u * sg * (1.0f + z * (1.0f - sg))));
-                        du16[q] = __builtin_bit_cast(uint16_t, to_bf16(da * z * sg));
-                    }
-                    const int64_t o = (int64_t)p * N + c, o2 = (int64_t)p * 2 * N + c;
-                    *reinterpret_cast<uint2 *>(bw.wact + o) =
-                        uint2{a16[0] | ((uint32_t)a16[1] << 16), a16[2] | ((uint32_t)a16[3] << 16)};
-                    *reinterpret_cast<uint2 *>(bw.dh13 + o2) = uint2{
-                        dg16[0] | ((uint32_t)dg16[1] << 16), dg16[2] | ((uint32_t)dg16[3] << 16)};
-                    *reinterpret_cast<uint2 *>(bw.dh13 + o2 + N) = uint2{
-                        du16[0] | ((uint32_t)du16[1] << 16), du16[2] | ((uint32_t)du16[3] << 16)};
+                for (int o = 0; o < 3; ++o)
+                    *reinterpret_cast<uint2 *>(os + (o * 32 + lr) * kOP + c) =
+                        uint2{r16[o][0] | ((uint32_t)r16[o][1] << 16),
+                              r16[o][2] | ((uint32_t)r16[o][3] << 16)};
+            }
+#pragma unroll
+            for (int o = 0; o < 3; ++o) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int rr = 16 * j + (lane >> 2), cc = 8 * (lane & 3);
+                    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(os + (o * 32 + rr) * kOP + cc);
+                    if (pb + rr < tile.row_end && cval)
+                        *reinterpret_cast<bf16x8 *>(dst[o] + (int64_t)(pb + rr) * ld[o] + c0 + cc) =
+                            v;
                 }
             }
             sum += __shfl_xor(sum, 32);
