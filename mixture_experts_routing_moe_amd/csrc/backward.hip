@@ -329,7 +329,9 @@ __global__ __launch_bounds__(256) void bwd_act_kernel(const float *__restrict__ 
 // grad_hidden[t] = sum over slots j = 0..k-1 (in order) of dx[slot_to_sorted[t,
 // j]]; slots with no position (invalid id) add nothing and get grad_topk_w 0.
 // With gw_part, a valid slot's grad_topk_w is also written here: the sum of
-// its position's gw_tiles partial sums, in tile order.
+// its position's gw_tiles partial sums, wave w taking slots w, w + 4, ...:
+// lane l adds tiles l, l + 64, ... in order, then the lanes' sums meet in a
+// fixed butterfly.
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ dxs,
                                                      const int32_t *__restrict__ slot_to_sorted,
                                                      int k, int H, float *__restrict__ dx,
@@ -338,15 +340,16 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
                                                      int gw_tiles) {
     const int64_t t = blockIdx.x;
     const int32_t *s2s = slot_to_sorted + t * k;
-    if ((int)threadIdx.x < k) {
-        const int p = s2s[threadIdx.x];
-        if (p < 0) {
-            grad_w[t * k + threadIdx.x] = 0.f;
-        } else if (gw_part != nullptr) {
+    if ((int)threadIdx.x < k && s2s[threadIdx.x] < 0) grad_w[t * k + threadIdx.x] = 0.f;
+    if (gw_part != nullptr) {
+        for (int j = threadIdx.x / kWave; j < k; j += blockDim.x / kWave) {
+            const int p = s2s[j];
+            if (p < 0) continue;  // wave-uniform
             const float *g = gw_part + (int64_t)p * gw_tiles;
             float sum = 0.f;
-            for (int i = 0; i < gw_tiles; ++i) sum += g[i];
-            grad_w[t * k + threadIdx.x] = sum;
+            for (int i = lane_id(); i < gw_tiles; i += kWave) sum += g[i];
+            sum = wave_sum_f(sum);
+            if (lane_id() == 0) grad_w[t * k + j] = sum;
         }
     }
     for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
