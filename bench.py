@@ -3,9 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
 
 One step is one pass of the whole path over one batch of synthetic input:
-route + indices->multihot + align (one call, moe_route_align: one kernel for
-at most 512 routing slots, else a route kernel that also counts the
-alignment's histograms plus the scatter kernel) -> multihot->indices ->
+route + indices->multihot + align + multihot->indices (one call,
+moe_route_align_inverse: one kernel for at most 512 routing slots, else a
+route kernel that also counts the alignment's histograms plus the scatter
+kernel, whose launch also carries the inverse conversion's blocks) ->
 grouped FC1 + SiLU-and-mul -> grouped FC2 -> combine (decode workloads use
 the decode FFN kernels).  Inputs are resident in HBM before timing starts; nothing is
 allocated inside the timed region.  Each phase is bracketed by HIP events on
@@ -33,9 +34,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
     "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
-    # route_hist_kernel + align_scatter_kernel (the routing rows of moe_route_align)
-    "route_align": ["mixture_experts_routing_moe_amd/csrc/align.hip",
-                    "mixture_experts_routing_moe_amd/csrc/moe_internal.h"],
+    # route_hist_kernel + align_scatter_kernel with the inverse's blocks (the
+    # routing rows of moe_route_align_inverse)
+    "route_align_inverse": ["mixture_experts_routing_moe_amd/csrc/align.hip",
+                            "mixture_experts_routing_moe_amd/csrc/moe_internal.h"],
     "ffn_backward": ["mixture_experts_routing_moe_amd/csrc/backward.hip",
                      "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip"],
 }
@@ -413,11 +415,13 @@ def main():
         y = torch.empty((splits, T * k, H), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    # Route, the indices->multihot conversion of its output and the alignment
-    # run as one call (moe_route_align; its launches are in config).
-    phases = ["route_align", "to_indices"]
+    # Route, the indices->multihot conversion of its output, the alignment and
+    # the multihot->indices conversion of the maps run as one call
+    # (moe_route_align_inverse; its launches are in config).
+    phases = ["route_align_inverse"]
     ra_out = {"topk_w": topk_w, "topk_ids": topk_ids, "multihot": mh, "probs_in_multihot": pim,
-              "position_map": pos, **aligned}
+              "position_map": pos, **aligned, "probs_indices": back_p,
+              "ids_from_multihot": back_i}
     if grouped:  # group-limited selection (+ indices->multihot), then align and the inverse
         phases = ["route_grouped", "align", "to_indices"]
     if has_ffn:
@@ -426,9 +430,8 @@ def main():
     cur = {"logits": logits_draws[0]}
 
     def run_phase(name):
-        if name == "route_align":
-            moe.moe_route_align(cur["logits"], k, w.norm, with_multihot=True, out=ra_out,
-                                workspace=align_ws)
+        if name == "route_align_inverse":
+            moe.moe_route_align_inverse(cur["logits"], k, w.norm, out=ra_out, workspace=align_ws)
         elif name == "route_grouped":
             moe.moe_route_grouped(cur["logits"], k, w.n_group, w.topk_group, w.method, bias_d,
                                   w.renorm, topk_w, topk_ids, multihot=(mh, pim, pos))
@@ -505,7 +508,7 @@ def main():
         # Distinct experts per routing draw (outside the timed region).
         for r in range(min(draws, args.steps)):
             cur["logits"] = logits_draws[r]
-            run_phase("route_align")
+            run_phase("route_align_inverse")
             n_distinct.append(int((aligned["counts"] > 0).sum().item()))
 
     phase_ms = {ph: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) /
@@ -533,8 +536,8 @@ def main():
                     "renormalize": w.renorm})
     else:
         cfg.update({"norm_topk_prob": w.norm,
-                    "route_align_launches": (1 if T * k <= 512 else 2)
-                    if moe.moe_route_align_fused(T, E, k) else 3})
+                    "route_align_inverse_launches": (1 if T * k <= 512 else 2)
+                    if moe.moe_route_align_fused(T, E, k) else 4})
     if has_ffn:
         cfg.update({"H": w.H, "I": w.I, "fc2_k_slices": splits})
         n_valid = int(aligned["offsets"][-1].item())
@@ -576,8 +579,8 @@ def main():
         # Algorithmic HBM bytes per phase: every input read once, every output
         # written once.
         nb = {"route_multihot": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
-              "route_align": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4) + T * k * 12 +
-              (2 * E + 1) * 4,
+              "route_align_inverse": T * E * 4 + T * k * 8 + T * E * (1 + 4 + 4) + T * k * 12 +
+              (2 * E + 1) * 4 + T * E * 8 + T * k * 8,
               "route_grouped": T * E * 4 + E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
               "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
@@ -585,8 +588,8 @@ def main():
         nb = {ph: nb[ph] for ph in phases}
         dom = max(phase_ms, key=phase_ms.get)
         names = {"route_multihot": "route_rows16_kernel (route + multihot)",
-                 "route_align": "route_hist_kernel + align_scatter_kernel (route + multihot "
-                                "+ align)",
+                 "route_align_inverse": "route_hist_kernel + align_scatter_kernel (route + "
+                                        "multihot + align + inverse)",
                  "route_grouped": "route_grouped_rows16_kernel (selection + multihot)",
                  "to_multihot": "to_multihot kernel",
                  "align": "align_hist_kernel + align_scatter_kernel",

@@ -9,6 +9,7 @@
  *   moe_route_grouped         group-limited top-k (group_limited_greedy, noaux_tc)
  *   moe_router_route          router GEMM (hidden . w_gate^T) + moe_route, one pass
  *   moe_route_align           moe_route(_multihot) + moe_align in fewer launches
+ *   moe_route_align_inverse   moe_route_align + moe_multihot_to_indices on its maps
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
@@ -244,6 +245,29 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
                              void *stream);
 /* 1 if moe_route_align takes the fused launches for this T, E and k. */
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_route_align_inverse -- moe_route_align with the multihot outputs
+ * (required here), followed by moe_multihot_to_indices on the maps it wrote:
+ * probs_indices [T, k] float32 and ids_from_multihot [T, k] int32 (may be
+ * NULL) are that call's outputs.  [mgt] _multihot_to_indices_kernel, after
+ * the sources of moe_route_align.
+ *
+ * Every output is bit-identical to the separate calls.  Where
+ * moe_route_align_fused(T, E, k) is 1 the conversion runs in moe_route_align's
+ * last launch, reading the maps back from memory: in the one-wave or
+ * one-block kernel after it has aligned, or (more slots) as extra blocks of
+ * the scatter launch, which does not depend on it; otherwise it is a launch
+ * of its own.  Same workspace as moe_route_align.
+ */
+moe_status_t moe_route_align_inverse(const float *logits, int64_t T, int32_t E, int32_t k,
+                                     int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                     uint8_t *multihot, float *probs_in_multihot,
+                                     int32_t *position_map, int32_t *expert_counts,
+                                     int32_t *expert_offsets, int32_t *sorted_token_ids,
+                                     int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                                     float *probs_indices, int32_t *ids_from_multihot,
+                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * moe_route_align_noalloc -- moe_route_align for callers that cannot allocate

@@ -24,6 +24,7 @@ from .moe import (  # noqa: F401
     moe_route,
     moe_route_align,
     moe_route_align_fused,
+    moe_route_align_inverse,
     moe_route_align_noalloc,
     moe_route_backward,
     moe_route_grouped_backward,

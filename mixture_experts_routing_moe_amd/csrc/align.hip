@@ -23,6 +23,8 @@
 //
 // Only integer LDS atomics on private counters are used, and no result
 // depends on their order, so the output is identical on every run.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -239,12 +241,27 @@ __device__ __forceinline__ void align_scatter_block(
     }
 }
 
+// Blocks nb and up (launched only with inv_w) convert the [T, E] multihot
+// maps to indices instead (E <= 64, E % 4 == 0, k <= 16: 16 lanes per row,
+// 4 rows per wave), the work of moe_multihot_to_indices, in the same launch
+// as the scatter it does not depend on.
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
     int fused_hist, const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
-    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted,
+    const float *__restrict__ pim, const int32_t *__restrict__ pos, float *__restrict__ inv_w,
+    int32_t *__restrict__ inv_ids) {
     extern __shared__ int32_t sm[];
+    if ((int)blockIdx.x >= nb) {
+        const int lane = lane_id();
+        const int64_t T = n / k;
+        const int wave = ((int)blockIdx.x - nb) * kAlignWaves + (int)threadIdx.x / kWave;
+        const int nwaves = ((int)gridDim.x - nb) * kAlignWaves;
+        for (int64_t t0 = (int64_t)wave * 4; t0 < T; t0 += (int64_t)nwaves * 4)
+            to_indices_row16<4>(pim, pos, T, t0 + (lane >> 4), E, k, inv_w, inv_ids, lane & 15);
+        return;
+    }
     align_scatter_block(blockIdx.x, ids, n, k, E, chunk, nbits, nb, fused_hist, partial, counts,
                         offsets, sorted_tok, sorted_slot, slot_to_sorted, sm);
 }
@@ -259,7 +276,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_small_kernel(
     float *__restrict__ pim, int32_t *__restrict__ pos, int chunk, int nbits,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_tok, int32_t *__restrict__ sorted_slot,
-    int32_t *__restrict__ slot_to_sorted) {
+    int32_t *__restrict__ slot_to_sorted, float *__restrict__ inv_w,
+    int32_t *__restrict__ inv_ids) {
     extern __shared__ int32_t sm[];
     const int lane = lane_id();
     const int g = lane >> 4;
@@ -268,9 +286,14 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_small_kernel(
     for (int t0 = wave * 4; t0 < T; t0 += kAlignWaves * 4)
         route16_row(logits, T, t0 + g, E, k, norm, vec4, topk_w, topk_ids, multihot, pim, pos, g,
                     q);
-    __syncthreads();  // every id of the batch is written before the block reads them
+    __syncthreads();  // every id and map row of the batch is written before the block reads them
     align_scatter_block(0, topk_ids, T * k, k, E, chunk, nbits, 1, 1, nullptr, counts, offsets,
                         sorted_tok, sorted_slot, slot_to_sorted, sm);
+    // With inv_w: the multihot maps back to indices (moe_multihot_to_indices),
+    // read from the rows written above.
+    if (inv_w != nullptr)
+        for (int t0 = wave * 4; t0 < T; t0 += kAlignWaves * 4)
+            to_indices_row16<4>(pim, pos, T, t0 + g, E, k, inv_w, inv_ids, q);
 }
 
 // Route + align in one wave (at most 64 slots, E <= 64, k <= 16: decode
@@ -284,7 +307,8 @@ __global__ __launch_bounds__(kWave) void route_align_wave_kernel(
     float *__restrict__ topk_w, int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot,
     float *__restrict__ pim, int32_t *__restrict__ pos, int nbits, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
-    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted) {
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted,
+    float *__restrict__ inv_w, int32_t *__restrict__ inv_ids) {
     __shared__ int32_t s_ids[kWave];
     __shared__ int32_t s_cnt[kWave];
     __shared__ int32_t s_off[kWave];
@@ -344,6 +368,13 @@ __global__ __launch_bounds__(kWave) void route_align_wave_kernel(
     for (int p = total + lane; p < n; p += kWave) {
         sorted_tok[p] = -1;
         sorted_slot[p] = -1;
+    }
+    // With inv_w: the multihot maps back to indices (moe_multihot_to_indices),
+    // read from the rows this wave wrote.
+    if (inv_w != nullptr) {
+        __threadfence_block();
+        for (int t0 = 0; t0 < T; t0 += 4)
+            to_indices_row16<4>(pim, pos, T, t0 + g, E, k, inv_w, inv_ids, q);
     }
 }
 
@@ -419,7 +450,7 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
     const size_t lds = scatter_lds_bytes(E);
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
                        k, E, (int)chunk, nbits, nb, fused, ws, counts, offsets, sorted_tok,
-                       sorted_slot, slot_to_sorted);
+                       sorted_slot, slot_to_sorted, nullptr, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -441,14 +472,17 @@ hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int 
                               int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
                               int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
                               int32_t *sorted_slot, int32_t *slot_to_sorted, int32_t *ws,
-                              hipStream_t s) {
+                              float *inv_w, int32_t *inv_ids, hipStream_t s) {
+    if (inv_w != nullptr && mh == nullptr) return hipErrorInvalidValue;
     if (!route_align_fused(T, E, k, mh, pim, pos)) {
         hipError_t err = mh != nullptr
                              ? launch_route_multihot(logits, T, E, k, norm, w, ids, mh, pim, pos, s)
                              : launch_route(logits, T, E, k, norm, w, ids, s);
         if (err != hipSuccess) return err;
-        return launch_align(ids, T, k, E, counts, offsets, sorted_tok, sorted_slot,
-                            slot_to_sorted, ws, s);
+        err = launch_align(ids, T, k, E, counts, offsets, sorted_tok, sorted_slot, slot_to_sorted,
+                           ws, s);
+        if (err != hipSuccess || inv_w == nullptr) return err;
+        return launch_to_indices(pim, pos, T, E, k, inv_w, inv_ids, s);
     }
     const int64_t n = T * k;
     const int nb = align_num_blocks(n, E);
@@ -459,23 +493,27 @@ hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int 
     if (n <= kWave) {
         hipLaunchKernelGGL(route_align_wave_kernel, dim3(1), dim3(kWave), 0, s, logits, (int)T, E,
                            k, norm, vec4, w, ids, mh, pim, pos, nbits, counts, offsets, sorted_tok,
-                           sorted_slot, slot_to_sorted);
+                           sorted_slot, slot_to_sorted, inv_w, inv_ids);
         return hipGetLastError();
     }
     if (nb == 1) {
         hipLaunchKernelGGL(route_align_small_kernel, dim3(1), dim3(kAlignThreads),
                            scatter_lds_bytes(E), s, logits, (int)T, E, k, norm, vec4, w, ids, mh,
                            pim, pos, (int)chunk, nbits, counts, offsets, sorted_tok, sorted_slot,
-                           slot_to_sorted);
+                           slot_to_sorted, inv_w, inv_ids);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(kRouteHistThreads), E * sizeof(int32_t), s,
                        logits, T, E, k, norm, vec4, chunk / k, w, ids, mh, pim, pos, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), scatter_lds_bytes(E),
-                       s, ids, (int)n, k, E, (int)chunk, nbits, nb, 0, ws, counts, offsets,
-                       sorted_tok, sorted_slot, slot_to_sorted);
+    // With inv_w the launch also carries the inverse conversion's blocks
+    // (32 rows per block per pass), after the scatter's.
+    const int64_t inv_blocks = inv_w == nullptr ? 0 : std::min<int64_t>((T + 31) / 32, 4096);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)(nb + inv_blocks)),
+                       dim3(kAlignThreads), scatter_lds_bytes(E), s, ids, (int)n, k, E,
+                       (int)chunk, nbits, nb, 0, ws, counts, offsets, sorted_tok, sorted_slot,
+                       slot_to_sorted, pim, pos, inv_w, inv_ids);
     return hipGetLastError();
 }
 

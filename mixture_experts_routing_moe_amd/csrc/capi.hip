@@ -283,7 +283,8 @@ moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, in
                               int32_t *position_map, int32_t *expert_counts,
                               int32_t *expert_offsets, int32_t *sorted_token_ids,
                               int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
-                              void *workspace, size_t workspace_bytes, void *stream) {
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              float *inv_probs = nullptr, int32_t *inv_ids = nullptr) {
     moe_status_t st = check_routing_dims(T, E, k, fn);
     if (st != MOE_OK) return st;
     CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
@@ -291,6 +292,10 @@ moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, in
                      (position_map != nullptr);
     CHECK(n_mh == 0 || n_mh == 3, MOE_ERR_INVALID_ARG,
           "%s: give all three multihot outputs or none", fn);
+    CHECK(inv_ids == nullptr || inv_probs != nullptr, MOE_ERR_INVALID_ARG,
+          "%s: ids of the inverse conversion without its probs", fn);
+    CHECK(inv_probs == nullptr || n_mh == 3, MOE_ERR_INVALID_ARG,
+          "%s: the inverse conversion needs the multihot outputs", fn);
     CHECK(expert_counts && expert_offsets, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     CHECK(T == 0 || (logits && topk_w && topk_ids && sorted_token_ids && sorted_slot_ids &&
                      slot_to_sorted),
@@ -302,8 +307,8 @@ moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, in
                                               topk_ids, multihot, probs_in_multihot,
                                               position_map, expert_counts, expert_offsets,
                                               sorted_token_ids, sorted_slot_ids, slot_to_sorted,
-                                              static_cast<int32_t *>(workspace),
-                                              static_cast<hipStream_t>(stream)),
+                                              static_cast<int32_t *>(workspace), inv_probs,
+                                              inv_ids, static_cast<hipStream_t>(stream)),
                       fn);
 }
 
@@ -356,6 +361,28 @@ moe_status_t moe_route_align(const float *logits, int64_t T, int32_t E, int32_t 
                             multihot, probs_in_multihot, position_map, expert_counts,
                             expert_offsets, sorted_token_ids, sorted_slot_ids, slot_to_sorted,
                             workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_route_align_inverse(const float *logits, int64_t T, int32_t E, int32_t k,
+                                     int32_t norm_topk_prob, float *topk_w, int32_t *topk_ids,
+                                     uint8_t *multihot, float *probs_in_multihot,
+                                     int32_t *position_map, int32_t *expert_counts,
+                                     int32_t *expert_offsets, int32_t *sorted_token_ids,
+                                     int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                                     float *probs_indices, int32_t *ids_from_multihot,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "moe_route_align_inverse";
+    CHECK(T == 0 || (multihot && probs_in_multihot && position_map && probs_indices),
+          MOE_ERR_INVALID_ARG, "%s: null pointer (the multihot outputs are required)", fn);
+    if (T == 0)  // no rows to convert: moe_route_align's zero counts and offsets
+        return route_align_impl(fn, logits, T, E, k, norm_topk_prob, topk_w, topk_ids, nullptr,
+                                nullptr, nullptr, expert_counts, expert_offsets,
+                                sorted_token_ids, sorted_slot_ids, slot_to_sorted, workspace,
+                                workspace_bytes, stream);
+    return route_align_impl(fn, logits, T, E, k, norm_topk_prob, topk_w, topk_ids, multihot,
+                            probs_in_multihot, position_map, expert_counts, expert_offsets,
+                            sorted_token_ids, sorted_slot_ids, slot_to_sorted, workspace,
+                            workspace_bytes, stream, probs_indices, ids_from_multihot);
 }
 
 moe_status_t moe_route_align_noalloc(const float *logits, int64_t T, int32_t E, int32_t k,

@@ -153,6 +153,56 @@ __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, i
     return (float)(ex / sum);
 }
 
+// Largest k served by the 16-lanes-per-row converters.
+constexpr int kKMax16 = 16;
+
+// multihot -> indices for row t (T rows; the 16-lane group's lane q, CPL
+// columns per lane, E <= 16 CPL, k <= kKMax16): slot j of the row is filled
+// from the highest expert naming it -- each lane proposes 1 + its highest
+// expert per slot, a 16-lane DPP max per slot picks the row's, and lane j
+// fetches that expert's probability ([mgt] _multihot_to_indices_kernel).
+// Every lane of the group must call it (rows t >= T write nothing).
+template <int CPL>
+__device__ __forceinline__ void to_indices_row16(const float *__restrict__ pim,
+                                                 const int32_t *__restrict__ pos, int64_t T,
+                                                 int64_t t, int E, int k,
+                                                 float *__restrict__ probs,
+                                                 int32_t *__restrict__ ids, int q) {
+    const int c0 = CPL * q;
+    const bool row_ok = t < T;
+    int pp[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL / 4; ++c) {
+        int4 p4 = make_int4(-1, -1, -1, -1);
+        if (row_ok && c0 + 4 * c < E) p4 = *reinterpret_cast<const int4 *>(pos + t * E + c0 + 4 * c);
+        pp[4 * c] = p4.x;
+        pp[4 * c + 1] = p4.y;
+        pp[4 * c + 2] = p4.z;
+        pp[4 * c + 3] = p4.w;
+    }
+    uint32_t best[kKMax16];
+#pragma unroll
+    for (int j = 0; j < kKMax16; ++j) {
+        best[j] = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            if (pp[i] == j) best[j] = (uint32_t)(c0 + i + 1);
+    }
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kKMax16; ++j) {
+        if (j < k) {
+            const uint32_t b = row16_max_u32(best[j]);
+            if (q == j) mine = b;
+        }
+    }
+    if (row_ok && q < k) {
+        const int e = (int)mine - 1;
+        probs[t * k + q] = e >= 0 ? pim[t * E + e] : 0.0f;
+        if (ids) ids[t * k + q] = e;
+    }
+}
+
 // One routing row on a 16-lane DPP row (g = lane / 16, q = lane % 16): row
 // t of logits [T, E] (E <= 64, k <= 16; rows t >= T write nothing), the
 // selection of route_row16, topk_w / topk_ids written by lanes q < k, and
@@ -270,14 +320,16 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
 
 // Route (+ indices->multihot when mh != nullptr) and align in fewer launches
 // where route_align_fused holds; otherwise the separate launches.  Outputs
-// are those of the separate calls, bit for bit.
+// are those of the separate calls, bit for bit.  With inv_w (which needs the
+// multihot outputs), the maps are also converted back to indices
+// (launch_to_indices: inv_w, inv_ids) in the last launch where fused.
 bool route_align_fused(int64_t T, int E, int k, const uint8_t *mh, const float *pim,
                        const int32_t *pos);
 hipError_t launch_route_align(const float *logits, int64_t T, int E, int k, int norm, float *w,
                               int32_t *ids, uint8_t *mh, float *pim, int32_t *pos,
                               int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
                               int32_t *sorted_slot, int32_t *slot_to_sorted, int32_t *ws,
-                              hipStream_t s);
+                              float *inv_w, int32_t *inv_ids, hipStream_t s);
 
 hipError_t launch_to_multihot(const int32_t *ids, const float *probs, int64_t T, int k, int E,
                               uint8_t *mh, float *pim, int32_t *pos, hipStream_t s);

@@ -92,7 +92,6 @@ __global__ __launch_bounds__(kThreads) void to_indices_kernel(
 // per row, lane q owning experts CPL q .. CPL q + CPL - 1, so each lane
 // writes its columns in groups of 4 with one 4-byte, one 16-byte and one
 // 16-byte store.
-constexpr int kKMax16 = 16;
 
 template <int CPL>
 __global__ __launch_bounds__(kThreads) void to_multihot_rows16_kernel(
@@ -140,9 +139,6 @@ __global__ __launch_bounds__(kThreads) void to_multihot_rows16_kernel(
     }
 }
 
-// Slot j of a row is filled from the highest expert naming it: each lane
-// proposes 1 + its highest expert per slot, a 16-lane DPP max per slot picks
-// the row's, and lane j fetches that expert's probability.
 template <int CPL>
 __global__ __launch_bounds__(kThreads) void to_indices_rows16_kernel(
     const float *__restrict__ pim, const int32_t *__restrict__ pos, int64_t T, int E, int k,
@@ -150,45 +146,10 @@ __global__ __launch_bounds__(kThreads) void to_indices_rows16_kernel(
     const int lane = lane_id();
     const int g = lane >> 4;
     const int q = lane & 15;
-    const int c0 = CPL * q;
     const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
-    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4) {
-        const int64_t t = t0 + g;
-        const bool row_ok = t < T;
-        int pp[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL / 4; ++c) {
-            int4 p4 = make_int4(-1, -1, -1, -1);
-            if (row_ok && c0 + 4 * c < E)
-                p4 = *reinterpret_cast<const int4 *>(pos + t * E + c0 + 4 * c);
-            pp[4 * c] = p4.x;
-            pp[4 * c + 1] = p4.y;
-            pp[4 * c + 2] = p4.z;
-            pp[4 * c + 3] = p4.w;
-        }
-        uint32_t best[kKMax16];
-#pragma unroll
-        for (int j = 0; j < kKMax16; ++j) {
-            best[j] = 0;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                if (pp[i] == j) best[j] = (uint32_t)(c0 + i + 1);
-        }
-        uint32_t mine = 0;
-#pragma unroll
-        for (int j = 0; j < kKMax16; ++j) {
-            if (j < k) {
-                const uint32_t b = row16_max_u32(best[j]);
-                if (q == j) mine = b;
-            }
-        }
-        if (row_ok && q < k) {
-            const int e = (int)mine - 1;
-            probs[t * k + q] = e >= 0 ? pim[t * E + e] : 0.0f;
-            if (ids) ids[t * k + q] = e;
-        }
-    }
+    for (int64_t t0 = wave * 4; t0 < T; t0 += nwaves * 4)
+        to_indices_row16<CPL>(pim, pos, T, t0 + g, E, k, probs, ids, q);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -226,6 +226,28 @@ def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
     return out
 
 
+def moe_route_align_inverse(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
+                            out: dict | None = None,
+                            workspace: torch.Tensor | None = None) -> dict:
+    """moe_route_align with the multihot outputs, then moe_multihot_to_indices on
+    its maps, in one call -> the dict of moe_route_align(with_multihot=True)
+    plus probs_indices [T, k] f32 and ids_from_multihot [T, k] i32."""
+    T, E, out = _route_align_outputs(logits, k, True, out)
+    if "probs_indices" not in out:
+        out["probs_indices"] = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+        out["ids_from_multihot"] = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                                device=logits.device)
+    _dev(logits, workspace, *out.values())
+    check(lib().moe_route_align_inverse(_ptr(logits), T, E, k, int(bool(norm_topk_prob)),
+                                        *_route_align_ptrs(out), _ptr(out["probs_indices"]),
+                                        _ptr(out["ids_from_multihot"]), _ptr(workspace),
+                                        workspace.numel(), _stream()),
+          "moe_route_align_inverse")
+    return out
+
+
 def moe_route_align_noalloc(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
                             with_multihot: bool = False, out: dict | None = None) -> dict:
     """moe_route_align without a workspace: the library's own device scratch

@@ -118,6 +118,23 @@ def test_route_align_validation(lib):
     assert lib.moe_route_align_fused(100, 64, 20) == 0
 
 
+def test_route_align_inverse_validation(lib):
+    I, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE
+    ws_need = lib.moe_align_workspace_size(100, 8, 64)
+    M3 = (FAKE, FAKE, FAKE)
+
+    def rai(T=100, mh=M3, probs=FAKE, ids=FAKE, ws=FAKE, wsb=None):
+        return lib.moe_route_align_inverse(FAKE, T, 64, 8, 1, FAKE, FAKE, *mh, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, probs, ids, ws,
+                                           ws_need if wsb is None else wsb, None)
+
+    assert rai(mh=(None, None, None)) == I  # the multihot outputs are required
+    assert rai(mh=(FAKE, None, FAKE)) == I
+    assert rai(probs=None) == I
+    assert rai(wsb=ws_need - 1) == W
+    assert rai(ws=None) == W
+
+
 def test_route_grouped_validation(lib):
     I = _lib.MOE_ERR_INVALID_ARG
     G, N = _lib.MOE_GROUP_LIMITED_GREEDY, _lib.MOE_NOAUX_TC

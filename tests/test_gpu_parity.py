@@ -426,6 +426,39 @@ def test_route_align_matches_separate_calls(T, E, k, mh):
         np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (32, 64, 8), (64, 64, 8), (0, 64, 8), (5, 8, 2),
+                                   (100, 60, 5), (16384, 64, 8), (4096, 8, 2), (3000, 64, 6),
+                                   (777, 100, 4), (300, 64, 20), (9000, 36, 4),
+                                   (4096, 64, 16), (12000, 62, 8), (8192, 64, 8),
+                                   (8, 64, 8), (64, 16, 1), (3, 64, 16), (9, 20, 7),
+                                   (40000, 64, 8)])
+def test_route_align_inverse_matches_separate_calls(T, E, k):
+    """moe_route_align_inverse (the multihot maps converted back to indices in
+    the route + align launches where they are fused) equals moe_route_multihot,
+    moe_align and moe_multihot_to_indices called one after the other, bit for
+    bit, and the conversion returns the routing's own ids and weights."""
+    g = np.random.Generator(np.random.PCG64(T * 5 + E + k))
+    x = g.standard_normal((T, E)).astype(np.float32)
+    if T > 0:
+        x[:, : min(E, 5)] = np.round(x[:, : min(E, 5)])  # some equal logits
+    xd = dev(x)
+    print(f"route_align_inverse T={T} E={E} k={k} fused={moe.moe_route_align_fused(T, E, k)}",
+          flush=True)
+    got = moe.moe_route_align_inverse(xd, k, True)
+    sep = dict(zip(("topk_w", "topk_ids", "multihot", "probs_in_multihot", "position_map"),
+                   moe.moe_route_multihot(xd, k, True)))
+    sep.update(moe.moe_align(sep["topk_ids"], E))
+    sep["probs_indices"], sep["ids_from_multihot"] = moe.moe_multihot_to_indices(
+        sep["probs_in_multihot"], sep["position_map"], k)
+    torch.cuda.synchronize()
+    for key in sep:
+        a, b = got[key], sep[key]
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), key
+    assert torch.equal(got["ids_from_multihot"], got["topk_ids"])
+    assert torch.equal(got["probs_indices"].view(torch.int32), got["topk_w"].view(torch.int32))
+
+
 def test_route_align_routing_workload():
     w = mi.WORKLOADS["routing"]
     x = mi.gating_logits(w)
