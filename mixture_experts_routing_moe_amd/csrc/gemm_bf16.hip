@@ -541,6 +541,22 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[NF][MF], uint16_t *smem, co
     k_tiles<0, MV, kGateUp>(acc, fr, smem, op, kt, nk, wv, fa);
 }
 
+// A float32 epilogue store, non-temporal (streamed past the caches) with kNT:
+// for outputs larger than the caches or not read again soon (fine-grained
+// FC2 -3 %, the backward's products and weight gradients -1.5 to -2.3 %; the
+// Mixtral-shaped FC2 output, which the combine reads back from the Infinity
+// Cache, keeps plain stores: its combine ran 5 us slower after non-temporal
+// ones).
+// (A compile-time choice: a runtime one let the compiler merge the two
+// stores into a plain one.)
+template <bool kNT>
+__device__ __forceinline__ void store_f32x4(float *p, const float4 &v) {
+    if constexpr (kNT)
+        __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
+    else
+        *reinterpret_cast<float4 *>(p) = v;
+}
+
 // Operands of the FC1-form epilogue that applies the SiLU-and-mul backward
 // to the recomputed gate/up (kBwd): per aligned position p and column c < N,
 // from gate z and up u (the accumulators), G[p, c] and the slot's routing
@@ -567,8 +583,8 @@ struct BwdAct {
 //
 // kTrans (FC2 form): C is stored transposed, element (token-side row p,
 // weight-side row n) at C[n * plane + p]; p's extent must be a multiple of 4.
-template <int MV, bool kGateUp, bool kTrans = false, bool kBwd = false, typename OpsT,
-          typename FA>
+template <int MV, bool kGateUp, bool kTrans = false, bool kBwd = false, bool kStream = true,
+          typename OpsT, typename FA>
 __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk, int wv,
                                          const FA &fa, const MTile &tile, int nt, int wn,
                                          int wm, int lr, int lk, int N, int ks, int64_t plane,
@@ -741,7 +757,7 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
                                                      ep[(cl + 2) * kP + w], ep[(cl + 3) * kP + w]);
                         const int n = nt * BN + wn * (BN / WN) + f * 32 + w;
                         if (p < tile.row_end && n < N)
-                            *reinterpret_cast<float4 *>(C + (int64_t)n * plane + p) = v;
+                            store_f32x4<kStream>(C + (int64_t)n * plane + p, v);
                     }
                 } else {
                     const int n = nt * BN + wn * (BN / WN) + f * 32 + cl;
@@ -751,7 +767,7 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
                             *reinterpret_cast<const float4 *>(ep + (8 * i + rl) * kP + cl);
                         const int p = p0 + 8 * i + rl;
                         if (p < tile.row_end && n < N)
-                            *reinterpret_cast<float4 *>(C + (int64_t)p * N + n) = v;
+                            store_f32x4<kStream>(C + (int64_t)p * N + n, v);
                     }
                 }
             }
@@ -770,8 +786,8 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 // size in bytes (used by kBuf only).
 // kKm (FC2 form, buffer addressing only): W is K-major, [E, K, N].
 // kBwd (FC1 form): the epilogue applies the SiLU-and-mul backward (BwdAct)
-// instead of writing act.
-template <bool kGateUp, bool kBuf, bool kKm = false, bool kBwd = false>
+// instead of writing act.  kStream (FC2 form): y is stored non-temporally.
+template <bool kGateUp, bool kBuf, bool kKm = false, bool kBwd = false, bool kStream = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
     const uint16_t *__restrict__ W, const int32_t *__restrict__ offsets, void *__restrict__ Cv,
@@ -908,28 +924,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     switch (mvalid) {
         case 5:
             if constexpr (MF >= 5)
-                run_tile<5, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks, plane,
-                                     Cv, bw);
+                run_tile<5, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm,
+                                                           lr, lk, N, ks, plane, Cv, bw);
             break;
         case 4:
-            run_tile<4, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv, bw);
+            run_tile<4, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr,
+                                                       lk, N, ks, plane, Cv, bw);
             break;
         case 3:
-            run_tile<3, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv, bw);
+            run_tile<3, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr,
+                                                       lk, N, ks, plane, Cv, bw);
             break;
         case 2:
-            run_tile<2, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv, bw);
+            run_tile<2, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr,
+                                                       lk, N, ks, plane, Cv, bw);
             break;
         case 1:
-            run_tile<1, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv, bw);
+            run_tile<1, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr,
+                                                       lk, N, ks, plane, Cv, bw);
             break;
         default:
-            run_tile<0, kGateUp, false, kBwd>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr, lk, N, ks,
-                                 plane, Cv, bw);
+            run_tile<0, kGateUp, false, kBwd, kStream>(smem, op, nk, wv, fa, tile, nt, wn, wm, lr,
+                                                       lk, N, ks, plane, Cv, bw);
             break;
     }
 }
@@ -1162,7 +1178,7 @@ hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const i
     const int n_tiles = (N + BN - 1) / BN;
     const int64_t a_bytes = rows * K * 2;
     const dim3 grid(grid_of(m_slots, n_tiles));
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true>), grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true, false, true>), grid, dim3(kThreads), 0, s,
                        a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes,
                        BwdAct{});
     return hipGetLastError();
@@ -1242,14 +1258,20 @@ hipError_t launch_down_bf16(const uint16_t *act, const uint16_t *w2, const int32
     const int n_tiles = (H + BN - 1) / BN;
     const int64_t a_bytes = rows * I * 2, w_bytes = (int64_t)H * I * 2;
     const dim3 grid(grid_of(m_slots * ksplit, n_tiles));
-    if (use_buffer_path(a_bytes, w_bytes))
-        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s,
-                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H,
-                           (int)a_bytes, BwdAct{});
-    else
+    // y streams past the caches when it is larger than the Infinity Cache.
+    const bool stream_y = (int64_t)ksplit * rows * H * 4 > ((int64_t)256 << 20);
+    if (!use_buffer_path(a_bytes, w_bytes))
         hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s,
                            act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H, 0,
                            BwdAct{});
+    else if (stream_y)
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, false, false, true>), grid,
+                           dim3(kThreads), 0, s, act, nullptr, w2, offsets, y, E, I, H, n_tiles,
+                           ksplit, rows * H, (int)a_bytes, BwdAct{});
+    else
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s,
+                           act, nullptr, w2, offsets, y, E, I, H, n_tiles, ksplit, rows * H,
+                           (int)a_bytes, BwdAct{});
     return hipGetLastError();
 }
 
