@@ -546,7 +546,8 @@ def main():
         # Algorithmic FLOPs of FC1 per launch: 2 * rows * (2I) * H.
         flops = 2.0 * n_valid * 2 * w.I * w.H
         achieved = flops / (phase_ms["gate_up"] * 1e-3) / 1e12
-        roofline = {"kernel": "grouped_gemm_bf16_kernel<true, true, false> (FC1)", "bound": "mfma",
+        roofline = {"kernel": "grouped_gemm_bf16_kernel<true, true, false, false, false> (FC1)",
+                    "bound": "mfma",
                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic("gate_up", w.name)}
