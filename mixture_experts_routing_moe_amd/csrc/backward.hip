@@ -12,27 +12,27 @@
 //   grad_w2[e]  = sum over slots of dy^T (w act)
 //   grad_w13[e] = sum over slots of [d_gate ; d_up]^T x
 //
-// Layout for the matrix cores.  Every product is arranged so that both of its
-// operands are stored with the contracted index contiguous ("NT"), which is
-// what the MFMA fragments read:
-// * The three row-segment products (gate/up recomputed = x . w13^T,
-//   G = dy . w2, d_hidden = [d_gate ; d_up] . w13) run on the forward's tuned
-//   grouped kernel (the FC2 variant: A rows in the aligned order, one weight
-//   matrix per expert, float32 out).  Its A rows are the tokens' rows gathered
-//   into the aligned order.  G and d_hidden contract over the rows of w2 and
-//   w13; they take the kernel's K-major variant, which loads the weights as
+// Layout for the matrix cores.  Every product runs on the forward's grouped
+// GEMM machinery, with the contracted index contiguous in LDS:
+// * G = dy . w2 and d_hidden = [d_gate ; d_up] . w13 contract over the rows
+//   of w2 and w13: the FC2-form kernel's K-major variant loads the weights as
 //   stored and transposes them in its LDS fragment reads (gfx950's
-//   ds_read_b64_tr_b16), so the weights are not copied (operands too large
-//   for buffer addressing fall back to per-expert transposed copies).
-// * The two weight gradients contract over each expert's rows.  Their
-//   operands (dy, x, w act, [d_gate ; d_up]) are transposed into [columns,
-//   positions] with every expert's segment padded to a whole number of
-//   k-tiles (zeros in the padding), so the k loop of a segment runs over
-//   whole, aligned tiles; one block computes a 256 x 256 tile of one expert's
-//   gradient (zero for an expert with no rows), 8 waves of 64 x 128, k-tiles
-//   of 64 in two LDS stages (144 KB).  Measured against 128 x 128 tiles and
-//   32-wide k-tiles: 4 % (Mixtral shape) and 10 % (fine-grained) faster
-//   backward.
+//   ds_read_b64_tr_b16), so they are not copied; its A rows are dy and
+//   [d_gate ; d_up] in the aligned order.
+// * gate/up = x . w13^T is recomputed on the FC1 kernel, whose epilogue
+//   applies the SiLU-and-mul backward from the accumulators and G (writing
+//   w act, [d_gate ; d_up] and per-tile partial sums of grad_w), so gate/up
+//   are never stored.
+// * The two weight gradients contract over each expert's rows: dy and x are
+//   transposed into [columns, positions] with every expert's segment padded
+//   to a whole number of k-tiles (zeros in the padding), and w act and
+//   [d_gate ; d_up] are read as stored, K-major, each k-tile's rows past the
+//   segment reading as zeros; dw13 is computed as x^T [d_gate ; d_up] and
+//   stored transposed.
+// Operands too large for the buffer addressing take the older paths: the
+// weights and all four weight-gradient operands transposed into the
+// workspace, gate/up stored for bwd_act_kernel, and wgrad_kernel (256 x 256
+// tiles, 8 waves of 64 x 128, two LDS stages of 64-wide k-tiles).
 #include <cstdlib>
 
 #include "moe_internal.h"
