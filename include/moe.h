@@ -12,6 +12,7 @@
  *   moe_route_align_inverse   moe_route_align + moe_multihot_to_indices on its maps
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
+ *   moe_tile_schedule         the grouped GEMMs' m-tile list from the offsets
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
  *   moe_multihot_to_indices   the inverse conversion
  *   moe_expert_ffn            grouped w13 GEMM + SiLU-and-mul, grouped w2 GEMM,
@@ -218,6 +219,33 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                        int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
                        int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * moe_tile_schedule -- the m-tile list of the grouped GEMMs (A3's tile
+ * schedule) from moe_align's expert_offsets.  [mlc] get_indptr (exclusive
+ * form) gives the segments; the tiles are this library's: an expert with
+ * c = offsets[e+1] - offsets[e] rows has ceil(c / 320) m-tiles, and its rows
+ * are dealt to them in equal shares rounded up to whole 32-row fragments,
+ * q = ceil(c / (32 mt)) * 32, so m-tile i covers rows
+ * [offsets[e] + min(i q, c), offsets[e] + min((i + 1) q, c)).  The grouped
+ * GEMMs derive the same tiles from the offsets on the device; this call
+ * writes them out for callers that want the list (a persistent or external
+ * GEMM, a dispatch plan).
+ *
+ * expert_offsets [E+1] int32 in (device).
+ * tile_expert, tile_row_start, tile_row_end [max_tiles] int32 out: tile j's
+ *                  expert and row range, expert order then m-tile order;
+ *                  entries j >= *num_tiles are left as they were.
+ * num_tiles        [1] int32 out (device): the number of tiles; if it
+ *                  exceeds max_tiles only the first max_tiles are written.
+ * max_tiles >= moe_tile_schedule_max(T, k, E) (ceil(T k / 320) + min(E, T k))
+ * always holds every tile.  Requires 1 <= E <= MOE_MAX_EXPERTS; the outputs
+ * may be NULL when max_tiles = 0.  One single-block launch.
+ */
+int64_t moe_tile_schedule_max(int64_t T, int32_t k, int32_t E);
+moe_status_t moe_tile_schedule(const int32_t *expert_offsets, int32_t E, int64_t max_tiles,
+                               int32_t *tile_expert, int32_t *tile_row_start,
+                               int32_t *tile_row_end, int32_t *num_tiles, void *stream);
 
 /*
  * moe_route_align -- moe_route (moe_route_multihot when multihot,

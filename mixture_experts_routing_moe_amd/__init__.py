@@ -26,6 +26,8 @@ from .moe import (  # noqa: F401
     moe_route_align_fused,
     moe_route_align_inverse,
     moe_route_align_noalloc,
+    moe_tile_schedule,
+    moe_tile_schedule_max,
     moe_route_backward,
     moe_route_grouped_backward,
     moe_route_grouped,

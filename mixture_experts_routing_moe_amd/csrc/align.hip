@@ -413,7 +413,41 @@ __global__ __launch_bounds__(kRouteHistThreads) void route_hist_kernel(
         partial[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
+// The grouped GEMMs' m-tile list (A3's tile schedule): thread e takes expert
+// e (up to 4 per thread), the block scans the tile counts, and each expert
+// writes its tiles at its base.  One block of kAlignThreads (E <= 1024).
+__global__ __launch_bounds__(kAlignThreads) void tile_schedule_kernel(
+    const int32_t *__restrict__ offsets, int E, int64_t max_tiles,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ tile_row_start,
+    int32_t *__restrict__ tile_row_end, int32_t *__restrict__ num_tiles) {
+    __shared__ int32_t cnt_tiles[4 * kAlignThreads], base[4 * kAlignThreads], wsum[kAlignWaves];
+    for (int e = threadIdx.x; e < E; e += kAlignThreads)
+        cnt_tiles[e] = expert_mtiles(offsets[e + 1] - offsets[e]);
+    __syncthreads();
+    const int total = block_exclusive_scan(cnt_tiles, base, E, wsum);
+    for (int e = threadIdx.x; e < E; e += kAlignThreads) {
+        const int o0 = offsets[e], cnt = offsets[e + 1] - o0, mt = cnt_tiles[e];
+        const int q = mtile_share(cnt, mt);
+        for (int i = 0; i < mt; ++i) {
+            const int64_t j = (int64_t)base[e] + i;
+            if (j >= max_tiles) break;
+            tile_expert[j] = e;
+            tile_row_start[j] = o0 + min(i * q, cnt);
+            tile_row_end[j] = o0 + min((i + 1) * q, cnt);
+        }
+    }
+    if (threadIdx.x == 0) num_tiles[0] = total;
+}
+
 }  // namespace
+
+hipError_t launch_tile_schedule(const int32_t *offsets, int E, int64_t max_tiles,
+                                int32_t *tile_expert, int32_t *tile_row_start,
+                                int32_t *tile_row_end, int32_t *num_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(kAlignThreads), 0, s, offsets, E,
+                       max_tiles, tile_expert, tile_row_start, tile_row_end, num_tiles);
+    return hipGetLastError();
+}
 
 size_t scatter_lds_bytes(int E) {
     const int parts = E < kAlignThreads ? kAlignThreads / E : 1;

@@ -408,6 +408,28 @@ moe_status_t moe_route_align_noalloc(const float *logits, int64_t T, int32_t E, 
                             kStaticScratchBytes, stream);
 }
 
+int64_t moe_tile_schedule_max(int64_t T, int32_t k, int32_t E) {
+    if (T <= 0 || k < 1 || E < 1) return 0;
+    const int64_t rows = T * k;
+    return (rows + moe::kGemmBM - 1) / moe::kGemmBM + (rows < E ? rows : E);
+}
+
+moe_status_t moe_tile_schedule(const int32_t *expert_offsets, int32_t E, int64_t max_tiles,
+                               int32_t *tile_expert, int32_t *tile_row_start,
+                               int32_t *tile_row_end, int32_t *num_tiles, void *stream) {
+    const char *fn = "moe_tile_schedule";
+    CHECK(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "%s: E = %d outside [1, %d]", fn,
+          E, MOE_MAX_EXPERTS);
+    CHECK(max_tiles >= 0, MOE_ERR_INVALID_ARG, "%s: max_tiles < 0", fn);
+    CHECK(expert_offsets && num_tiles &&
+              (max_tiles == 0 || (tile_expert && tile_row_start && tile_row_end)),
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    return hip_status(moe::launch_tile_schedule(expert_offsets, E, max_tiles, tile_expert,
+                                                tile_row_start, tile_row_end, num_tiles,
+                                                static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 int32_t moe_route_align_fused(int64_t T, int32_t E, int32_t k) {
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK) return 0;
     return moe::route_align_fused(T, E, k, nullptr, nullptr, nullptr);

@@ -43,10 +43,7 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_GEMM_BM
-#define MOE_GEMM_BM 320
-#endif
-constexpr int BM = MOE_GEMM_BM;  // token rows per tile
+constexpr int BM = kGemmBM;  // token rows per tile (moe_internal.h)
 constexpr int BN = 256;  // weight rows per tile
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
@@ -136,7 +133,7 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             off = offsets[e];
             cnt = offsets[e + 1] - off;
         }
-        const int tiles = (cnt + BM - 1) / BM;
+        const int tiles = expert_mtiles(cnt);
         int incl = tiles;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -156,10 +153,7 @@ __device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int L, int
             int i;
             band_tile(L - ex * n_tiles, mt, n_tiles, i, nt);
             t.e = c + src;
-            // Rows per m-tile: the expert's rows dealt in equal shares
-            // rounded up to whole 32-row fragments (at most BM; never an
-            // empty tile: (mt - 1) q < cn, checked for every cn < 200000).
-            const int q = (cn + 32 * mt - 1) / (32 * mt) * 32;
+            const int q = mtile_share(cn, mt);  // rows per m-tile
             t.row0 = o0 + min(i * q, cn);
             t.row_end = o0 + min((i + 1) * q, cn);
             return t.row0 < t.row_end;
@@ -176,7 +170,7 @@ __device__ int count_mtiles(const int32_t *__restrict__ offsets, int E) {
     for (int c = 0; c < E; c += kWave) {
         const int e = c + lane;
         const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-        int tiles = (cnt + BM - 1) / BM;
+        int tiles = expert_mtiles(cnt);
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) tiles += __shfl_xor(tiles, o, kWave);
         total += tiles;

@@ -10,6 +10,21 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// The grouped GEMMs' token rows per tile (m-tile) and how an expert's rows
+// are dealt to its m-tiles; the alignment's tile schedule follows the same
+// rule.  An expert with cnt rows has ceil(cnt / BM) m-tiles; its rows go to
+// them in equal shares rounded up to whole 32-row fragments (at most BM;
+// never an empty tile: (mt - 1) q < cnt, checked for every cnt < 200000), so
+// the tiles that share a weight tile do similar work.
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 320
+#endif
+constexpr int kGemmBM = MOE_GEMM_BM;
+__host__ __device__ inline int expert_mtiles(int cnt) { return (cnt + kGemmBM - 1) / kGemmBM; }
+__host__ __device__ inline int mtile_share(int cnt, int mt) {
+    return (cnt + 32 * mt - 1) / (32 * mt) * 32;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -314,6 +329,13 @@ hipError_t launch_router_backward(const uint16_t *hidden, const uint16_t *wg, co
                                   hipStream_t s);
 
 int align_num_blocks(int64_t n_slots, int E);
+// The m-tile list of the grouped GEMMs from the aligned offsets (expert
+// order, then m-tile order): tile i covers rows [row_start, row_end) of
+// expert tile_expert; num_tiles gets the count (entries past max_tiles are
+// not written).  E <= 1024.
+hipError_t launch_tile_schedule(const int32_t *offsets, int E, int64_t max_tiles,
+                                int32_t *tile_expert, int32_t *tile_row_start,
+                                int32_t *tile_row_end, int32_t *num_tiles, hipStream_t s);
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
                         int32_t *slot_to_sorted, int32_t *ws, hipStream_t s);

@@ -226,6 +226,26 @@ def moe_route_align(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
     return out
 
 
+def moe_tile_schedule_max(T: int, k: int, E: int) -> int:
+    return int(lib().moe_tile_schedule_max(T, k, E))
+
+
+def moe_tile_schedule(expert_offsets: torch.Tensor, max_tiles: int, out=None):
+    """The grouped GEMMs' m-tile list from moe_align's offsets -> (tile_expert,
+    tile_row_start, tile_row_end [max_tiles] int32, num_tiles [1] int32)."""
+    if expert_offsets.dtype != torch.int32 or expert_offsets.dim() != 1:
+        raise ValueError("expert_offsets must be [E+1] int32")
+    E = expert_offsets.numel() - 1
+    dev = expert_offsets.device
+    if out is None:
+        out = tuple(torch.empty(max(1, max_tiles), dtype=torch.int32, device=dev)
+                    for _ in range(3)) + (torch.empty(1, dtype=torch.int32, device=dev),)
+    _dev(expert_offsets, *out)
+    check(lib().moe_tile_schedule(_ptr(expert_offsets), E, max_tiles, *(_ptr(t) for t in out),
+                                  _stream()), "moe_tile_schedule")
+    return out
+
+
 def moe_route_align_inverse(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
                             out: dict | None = None,
                             workspace: torch.Tensor | None = None) -> dict:

@@ -118,6 +118,24 @@ def test_route_align_validation(lib):
     assert lib.moe_route_align_fused(100, 64, 20) == 0
 
 
+def test_tile_schedule_validation(lib):
+    I, U = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_tile_schedule_max(4096, 2, 8) == 26 + 8  # ceil(8192 / 320) + E
+    assert lib.moe_tile_schedule_max(1, 8, 64) == 1 + 8  # min(E, T k) experts can hold a row
+    assert lib.moe_tile_schedule_max(0, 8, 64) == 0
+
+    def ts(E=8, mx=10, off=FAKE, out=FAKE, num=FAKE):
+        return lib.moe_tile_schedule(off, E, mx, out, out, out, num, None)
+
+    assert ts(E=0) == U
+    assert ts(E=1025) == U
+    assert ts(mx=-1) == I
+    assert ts(off=None) == I
+    assert ts(num=None) == I
+    assert ts(out=None) == I
+    assert b"null pointer" in lib.moe_last_error()
+
+
 def test_route_align_inverse_validation(lib):
     I, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE
     ws_need = lib.moe_align_workspace_size(100, 8, 64)

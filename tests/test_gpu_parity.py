@@ -459,6 +459,46 @@ def test_route_align_inverse_matches_separate_calls(T, E, k):
     assert torch.equal(got["probs_indices"].view(torch.int32), got["topk_w"].view(torch.int32))
 
 
+@pytest.mark.parametrize("T,E,k,skew,inv", [(4096, 8, 2, 0.0, 0.0), (8192, 64, 8, 1.1, 0.0),
+                                            (16384, 64, 8, 0.0, 0.0), (300, 128, 4, 2.0, 0.1),
+                                            (1, 64, 8, 0.0, 0.0), (5000, 1024, 6, 0.5, 0.0),
+                                            (0, 16, 2, 0.0, 0.0), (2000, 2, 1, 3.0, 0.0)])
+def test_tile_schedule(T, E, k, skew, inv):
+    """moe_tile_schedule lists every expert's m-tiles in expert order: each
+    expert with c rows has ceil(c / 320) tiles of equal 32-row-fragment
+    shares that cover its segment exactly, in order, none empty or over 320
+    rows; and the list fits moe_tile_schedule_max."""
+    g = np.random.Generator(np.random.PCG64(T + E + 7))
+    score = g.random((T, E)) + skew * np.linspace(1.0, 0.0, E)  # skew: low ids favoured
+    ids = np.argsort(-score, axis=1)[:, :k].astype(np.int32)
+    if inv > 0:
+        ids = np.where(g.random(ids.shape) < inv, -1, ids).astype(np.int32)
+    a = moe.moe_align(dev(ids), E)
+    mx = moe.moe_tile_schedule_max(T, k, E)
+    te, trs, tre, num = moe.moe_tile_schedule(a["offsets"], mx)
+    torch.cuda.synchronize()
+    off = oracle.align(ids, E)["offsets"] if T else np.zeros(E + 1, np.int64)
+    n = int(num.item())
+    got = list(zip(te.cpu().numpy()[:n], trs.cpu().numpy()[:n], tre.cpu().numpy()[:n]))
+    want = []
+    for e in range(E):
+        c = int(off[e + 1] - off[e])
+        mt = -(-c // 320)
+        q = -(-c // (32 * mt)) * 32 if mt else 0
+        want += [(e, int(off[e]) + min(i * q, c), int(off[e]) + min((i + 1) * q, c))
+                 for i in range(mt)]
+    assert n == len(want) <= mx
+    assert [tuple(int(v) for v in t) for t in got] == want
+    # Coverage: the tiles of each expert tile its segment [off[e], off[e+1]).
+    for e in range(E):
+        rows = [(s, t) for x, s, t in want if x == e]
+        assert all(0 < t - s <= 320 for s, t in rows)
+        assert all(rows[i][1] == rows[i + 1][0] for i in range(len(rows) - 1))
+        if rows:
+            assert rows[0][0] == off[e] and rows[-1][1] == off[e + 1]
+            assert max(t - s for s, t in rows) - min(t - s for s, t in rows) <= 32 * len(rows)
+
+
 def test_route_align_routing_workload():
     w = mi.WORKLOADS["routing"]
     x = mi.gating_logits(w)
