@@ -422,8 +422,9 @@ def main():
     ra_out = {"topk_w": topk_w, "topk_ids": topk_ids, "multihot": mh, "probs_in_multihot": pim,
               "position_map": pos, **aligned, "probs_indices": back_p,
               "ids_from_multihot": back_i}
-    if grouped:  # group-limited selection (+ indices->multihot), then align and the inverse
-        phases = ["route_grouped", "align", "to_indices"]
+    if grouped:  # group-limited selection (+ indices->multihot), then align + the inverse
+        phases = ["route_grouped", "align_inverse"]
+    ai_out = {**aligned, "probs_indices": back_p, "ids_from_multihot": back_i}
     if has_ffn:
         phases += ["gate_up", "down", "combine"]
 
@@ -439,6 +440,8 @@ def main():
             moe.moe_indices_to_multihot(topk_ids, topk_w, E, out=(mh, pim, pos))
         elif name == "align":
             moe.moe_align(topk_ids, E, aligned, align_ws)
+        elif name == "align_inverse":
+            moe.moe_align_inverse(topk_ids, E, pim, pos, ai_out, align_ws)
         elif name == "to_indices":
             moe.moe_multihot_to_indices(pim, pos, k, out=(back_p, back_i))
         elif name == "gate_up":
@@ -585,6 +588,7 @@ def main():
               "route_grouped": T * E * 4 + E * 4 + T * k * 8 + T * E * (1 + 4 + 4),
               "to_multihot": T * k * 8 + T * E * (1 + 4 + 4),
               "align": T * k * 4 + T * k * 12 + (2 * E + 1) * 4,
+              "align_inverse": T * k * 4 + T * k * 12 + (2 * E + 1) * 4 + T * E * 8 + T * k * 8,
               "to_indices": T * E * 8 + T * k * 8}
         nb = {ph: nb[ph] for ph in phases}
         dom = max(phase_ms, key=phase_ms.get)
@@ -594,6 +598,8 @@ def main():
                  "route_grouped": "route_grouped_rows16_kernel (selection + multihot)",
                  "to_multihot": "to_multihot kernel",
                  "align": "align_hist_kernel + align_scatter_kernel",
+                 "align_inverse": "align_hist_kernel + align_scatter_kernel (with the inverse's "
+                                  "blocks)",
                  "to_indices": "to_indices kernel"}
         achieved = nb[dom] / (phase_ms[dom] * 1e-3) / 1e9
         roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),

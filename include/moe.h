@@ -12,6 +12,7 @@
  *   moe_route_align_inverse   moe_route_align + moe_multihot_to_indices on its maps
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
+ *   moe_align_inverse         moe_align + moe_multihot_to_indices on given maps
  *   moe_tile_schedule         the grouped GEMMs' m-tile list from the offsets
  *   moe_indices_to_multihot   [T,k] routing -> [T,E] multihot / probs / position map
  *   moe_multihot_to_indices   the inverse conversion
@@ -219,6 +220,28 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                        int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
                        int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * moe_align_inverse -- moe_align, then moe_multihot_to_indices on the given
+ * [T, E] maps (the multihot outputs of the routing that produced topk_ids),
+ * in one call.  [mlc] moe_cumsum, get_indices, get_indptr; [mgt]
+ * _multihot_to_indices_kernel.
+ *
+ * Arguments as the two calls: probs_in_multihot and position_map [T, E] in;
+ * probs_indices [T, k] float32 and ids_from_multihot [T, k] int32 (may be
+ * NULL) out.  Every output is bit-identical to the separate calls.  Where the
+ * conversion's 16-lanes-per-row form applies (E <= 256, E % 4 == 0,
+ * k <= 16, position_map 16-byte aligned) its blocks ride in the alignment
+ * scatter's launch, which does not depend on them; otherwise it is a launch
+ * of its own.  Same workspace as moe_align.
+ */
+moe_status_t moe_align_inverse(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                               int32_t *slot_to_sorted, const float *probs_in_multihot,
+                               const int32_t *position_map, float *probs_indices,
+                               int32_t *ids_from_multihot, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * moe_tile_schedule -- the m-tile list of the grouped GEMMs (A3's tile

@@ -7,6 +7,7 @@ include/moe.h); this package only binds it to torch tensors.
 from ._lib import MOE_BF16, MOE_F32, MoeError, lib  # noqa: F401
 from .moe import (  # noqa: F401
     moe_align,
+    moe_align_inverse,
     moe_align_workspace_size,
     moe_combine,
     moe_expert_ffn,

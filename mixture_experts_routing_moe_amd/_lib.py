@@ -54,6 +54,8 @@ SIGNATURES = {
     "moe_route_align_noalloc": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp]),
     "moe_align": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_align_inverse": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _sz, _vp]),
     "moe_indices_to_multihot": (_st, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_multihot_to_indices": (_st, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_st, _i64, _i32, _i32, _i32, _i32]),

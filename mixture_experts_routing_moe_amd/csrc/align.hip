@@ -242,9 +242,10 @@ __device__ __forceinline__ void align_scatter_block(
 }
 
 // Blocks nb and up (launched only with inv_w) convert the [T, E] multihot
-// maps to indices instead (E <= 64, E % 4 == 0, k <= 16: 16 lanes per row,
-// 4 rows per wave), the work of moe_multihot_to_indices, in the same launch
-// as the scatter it does not depend on.
+// maps to indices instead (E <= 256, E % 4 == 0, k <= 16: 16 lanes per row,
+// 4 rows per wave, 4, 8 or 16 columns per lane), the work of
+// moe_multihot_to_indices, in the same launch as the scatter it does not
+// depend on.
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const int32_t *__restrict__ ids, int n, int k, int E, int chunk, int nbits, int nb,
     int fused_hist, const int32_t *__restrict__ partial, int32_t *__restrict__ counts,
@@ -258,8 +259,15 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
         const int64_t T = n / k;
         const int wave = ((int)blockIdx.x - nb) * kAlignWaves + (int)threadIdx.x / kWave;
         const int nwaves = ((int)gridDim.x - nb) * kAlignWaves;
-        for (int64_t t0 = (int64_t)wave * 4; t0 < T; t0 += (int64_t)nwaves * 4)
-            to_indices_row16<4>(pim, pos, T, t0 + (lane >> 4), E, k, inv_w, inv_ids, lane & 15);
+        for (int64_t t0 = (int64_t)wave * 4; t0 < T; t0 += (int64_t)nwaves * 4) {
+            const int64_t t = t0 + (lane >> 4);
+            if (E <= 64)
+                to_indices_row16<4>(pim, pos, T, t, E, k, inv_w, inv_ids, lane & 15);
+            else if (E <= 128)
+                to_indices_row16<8>(pim, pos, T, t, E, k, inv_w, inv_ids, lane & 15);
+            else
+                to_indices_row16<16>(pim, pos, T, t, E, k, inv_w, inv_ids, lane & 15);
+        }
         return;
     }
     align_scatter_block(blockIdx.x, ids, n, k, E, chunk, nbits, nb, fused_hist, partial, counts,
@@ -465,7 +473,8 @@ int align_num_blocks(int64_t n, int E) {
 
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
-                        int32_t *slot_to_sorted, int32_t *ws, hipStream_t s) {
+                        int32_t *slot_to_sorted, int32_t *ws, hipStream_t s, const float *pim,
+                        const int32_t *pos, float *inv_w, int32_t *inv_ids) {
     const int64_t n = T * k;
     const int nb = align_num_blocks(n, E);
     const int64_t chunk = align_chunk(n, nb);
@@ -482,10 +491,18 @@ hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *co
         if (err != hipSuccess) return err;
     }
     const size_t lds = scatter_lds_bytes(E);
-    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(kAlignThreads), lds, s, ids, (int)n,
-                       k, E, (int)chunk, nbits, nb, fused, ws, counts, offsets, sorted_tok,
-                       sorted_slot, slot_to_sorted, nullptr, nullptr, nullptr, nullptr);
-    return hipGetLastError();
+    // With inv_w the launch also carries the inverse conversion's blocks
+    // where its 16-lanes-per-row form applies, else the conversion follows.
+    const bool inv_in = inv_w != nullptr && E <= 256 && E % 4 == 0 && k <= kKMax16 &&
+                        (reinterpret_cast<uintptr_t>(pos) & 15u) == 0;
+    const int64_t inv_blocks = inv_in ? std::min<int64_t>((T + 31) / 32, 4096) : 0;
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)(nb + inv_blocks)),
+                       dim3(kAlignThreads), lds, s, ids, (int)n, k, E, (int)chunk, nbits, nb,
+                       fused, ws, counts, offsets, sorted_tok, sorted_slot, slot_to_sorted, pim,
+                       pos, inv_in ? inv_w : nullptr, inv_ids);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || inv_w == nullptr || inv_in) return err;
+    return launch_to_indices(pim, pos, T, E, k, inv_w, inv_ids, s);
 }
 
 bool route_align_fused(int64_t T, int E, int k, const uint8_t *mh, const float *pim,

@@ -271,6 +271,32 @@ moe_status_t moe_align(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                       "moe_align");
 }
 
+moe_status_t moe_align_inverse(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                               int32_t *slot_to_sorted, const float *probs_in_multihot,
+                               const int32_t *position_map, float *probs_indices,
+                               int32_t *ids_from_multihot, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    const char *fn = "moe_align_inverse";
+    moe_status_t st = check_routing_dims(T, E, k, fn);
+    if (st != MOE_OK) return st;
+    CHECK(expert_counts && expert_offsets, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    CHECK(T == 0 || (topk_ids && sorted_token_ids && sorted_slot_ids && slot_to_sorted &&
+                     probs_in_multihot && position_map && probs_indices),
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    const size_t need = moe_align_workspace_size(T, k, E);
+    CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    return hip_status(moe::launch_align(topk_ids, T, k, E, expert_counts, expert_offsets,
+                                        sorted_token_ids, sorted_slot_ids, slot_to_sorted,
+                                        static_cast<int32_t *>(workspace),
+                                        static_cast<hipStream_t>(stream), probs_in_multihot,
+                                        position_map, T == 0 ? nullptr : probs_indices,
+                                        ids_from_multihot),
+                      fn);
+}
+
 }  // extern "C"
 
 namespace {

@@ -336,9 +336,13 @@ int align_num_blocks(int64_t n_slots, int E);
 hipError_t launch_tile_schedule(const int32_t *offsets, int E, int64_t max_tiles,
                                 int32_t *tile_expert, int32_t *tile_row_start,
                                 int32_t *tile_row_end, int32_t *num_tiles, hipStream_t s);
+// With inv_w, also the [T, E] maps (pim, pos) back to indices (inv_w,
+// inv_ids), in the scatter's launch where the 16-lanes-per-row form applies.
 hipError_t launch_align(const int32_t *ids, int64_t T, int k, int E, int32_t *counts,
                         int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
-                        int32_t *slot_to_sorted, int32_t *ws, hipStream_t s);
+                        int32_t *slot_to_sorted, int32_t *ws, hipStream_t s,
+                        const float *pim = nullptr, const int32_t *pos = nullptr,
+                        float *inv_w = nullptr, int32_t *inv_ids = nullptr);
 
 // Route (+ indices->multihot when mh != nullptr) and align in fewer launches
 // where route_align_fused holds; otherwise the separate launches.  Outputs

@@ -175,6 +175,45 @@ def moe_align(topk_ids: torch.Tensor, E: int, out: dict | None = None,
     return out
 
 
+def moe_align_inverse(topk_ids: torch.Tensor, E: int, probs_in_multihot: torch.Tensor,
+                      position_map: torch.Tensor, out: dict | None = None,
+                      workspace: torch.Tensor | None = None) -> dict:
+    """moe_align, then moe_multihot_to_indices on the given maps, in one call ->
+    the dict of moe_align plus probs_indices [T, k] f32 and ids_from_multihot
+    [T, k] i32."""
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k] int32")
+    T, k = topk_ids.shape
+    if (probs_in_multihot.dtype != torch.float32 or position_map.dtype != torch.int32
+            or tuple(probs_in_multihot.shape) != (T, E)
+            or tuple(position_map.shape) != (T, E)):
+        raise ValueError("probs_in_multihot [T, E] float32 and position_map [T, E] int32")
+    dev = topk_ids.device
+    n = T * k
+    if out is None:
+        out = {
+            "counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_token_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "sorted_slot_ids": torch.empty(n, dtype=torch.int32, device=dev),
+            "slot_to_sorted": torch.empty(n, dtype=torch.int32, device=dev),
+            "probs_indices": torch.empty((T, k), dtype=torch.float32, device=dev),
+            "ids_from_multihot": torch.empty((T, k), dtype=torch.int32, device=dev),
+        }
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                                device=dev)
+    _dev(topk_ids, probs_in_multihot, position_map, workspace, *out.values())
+    check(lib().moe_align_inverse(_ptr(topk_ids), T, k, E, _ptr(out["counts"]),
+                                  _ptr(out["offsets"]), _ptr(out["sorted_token_ids"]),
+                                  _ptr(out["sorted_slot_ids"]), _ptr(out["slot_to_sorted"]),
+                                  _ptr(probs_in_multihot), _ptr(position_map),
+                                  _ptr(out["probs_indices"]), _ptr(out["ids_from_multihot"]),
+                                  _ptr(workspace), workspace.numel(), _stream()),
+          "moe_align_inverse")
+    return out
+
+
 def moe_route_align_fused(T: int, E: int, k: int) -> bool:
     return bool(lib().moe_route_align_fused(T, E, k))
 

@@ -118,6 +118,21 @@ def test_route_align_validation(lib):
     assert lib.moe_route_align_fused(100, 64, 20) == 0
 
 
+def test_align_inverse_validation(lib):
+    I, W = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE
+    ws_need = lib.moe_align_workspace_size(100, 8, 64)
+
+    def ai(k=8, pim=FAKE, pos=FAKE, probs=FAKE, ws=FAKE, wsb=None):
+        return lib.moe_align_inverse(FAKE, 100, k, 64, FAKE, FAKE, FAKE, FAKE, FAKE, pim, pos,
+                                     probs, FAKE, ws, ws_need if wsb is None else wsb, None)
+
+    assert ai(k=65) == I
+    assert ai(pim=None) == I
+    assert ai(pos=None) == I
+    assert ai(probs=None) == I
+    assert ai(wsb=ws_need - 1) == W
+
+
 def test_tile_schedule_validation(lib):
     I, U = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED
     assert lib.moe_tile_schedule_max(4096, 2, 8) == 26 + 8  # ceil(8192 / 320) + E

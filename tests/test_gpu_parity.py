@@ -459,6 +459,41 @@ def test_route_align_inverse_matches_separate_calls(T, E, k):
     assert torch.equal(got["probs_indices"].view(torch.int32), got["topk_w"].view(torch.int32))
 
 
+@pytest.mark.parametrize("T,E,k,method", [(16384, 256, 8, "noaux_tc"),
+                                          (16384, 160, 6, "group_limited_greedy"),
+                                          (1000, 64, 8, "noaux_tc"), (1, 256, 8, "noaux_tc"),
+                                          (300, 128, 4, "group_limited_greedy"),
+                                          (0, 64, 8, "noaux_tc"), (777, 96, 20, "noaux_tc")])
+def test_align_inverse_matches_separate_calls(T, E, k, method):
+    """moe_align_inverse (the conversion's blocks in the alignment scatter's
+    launch where they fit) equals moe_align and moe_multihot_to_indices one
+    after the other, bit for bit, on a group-limited routing's ids and maps;
+    the conversion returns the routing's own ids and weights."""
+    g = np.random.Generator(np.random.PCG64(T + E * 3 + k))
+    scores = (1.0 / (1.0 + np.exp(-g.standard_normal((T, E))))).astype(np.float32)
+    bias = (0.1 * g.standard_normal(E)).astype(np.float32)
+    n_group = 8 if E % 8 == 0 else 4
+    kk = min(k, E // n_group * 4)
+    print(f"align_inverse T={T} E={E} k={kk} {method}", flush=True)
+    tw = torch.empty((T, kk), dtype=torch.float32, device=DEV)
+    ti = torch.empty((T, kk), dtype=torch.int32, device=DEV)
+    mh = torch.empty((T, E), dtype=torch.uint8, device=DEV)
+    pim = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    pos = torch.empty((T, E), dtype=torch.int32, device=DEV)
+    moe.moe_route_grouped(dev(scores), kk, n_group, 4, method, dev(bias), True, tw, ti,
+                          multihot=(mh, pim, pos))
+    got = moe.moe_align_inverse(ti, E, pim, pos)
+    sep = moe.moe_align(ti, E)
+    sep["probs_indices"], sep["ids_from_multihot"] = moe.moe_multihot_to_indices(pim, pos, kk)
+    torch.cuda.synchronize()
+    for key in sep:
+        a, b = got[key], sep[key]
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), key
+    assert torch.equal(got["ids_from_multihot"], ti)
+    assert torch.equal(got["probs_indices"].view(torch.int32), tw.view(torch.int32))
+
+
 @pytest.mark.parametrize("T,E,k,skew,inv", [(4096, 8, 2, 0.0, 0.0), (8192, 64, 8, 1.1, 0.0),
                                             (16384, 64, 8, 0.0, 0.0), (300, 128, 4, 2.0, 0.1),
                                             (1, 64, 8, 0.0, 0.0), (5000, 1024, 6, 0.5, 0.0),
