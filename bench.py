@@ -425,7 +425,9 @@ def main():
     if grouped:  # group-limited selection (+ indices->multihot), then align + the inverse
         phases = ["route_grouped", "align_inverse"]
     ai_out = {**aligned, "probs_indices": back_p, "ids_from_multihot": back_i}
-    if has_ffn:
+    if has_ffn and decode:  # FC2 and the combine through one call (one launch where fused)
+        phases += ["gate_up", "down_combine"]
+    elif has_ffn:
         phases += ["gate_up", "down", "combine"]
 
     cur = {"logits": logits_draws[0]}
@@ -450,6 +452,8 @@ def main():
             moe.moe_ffn_down(act, w2, aligned, T, k, decode, y, splits)
         elif name == "combine":
             moe.moe_combine(y, topk_w, aligned["slot_to_sorted"], torch.bfloat16, out)
+        elif name == "down_combine":
+            moe.moe_ffn_down_combine(act, w2, topk_w, aligned, T, k, decode, y, out)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
           for _ in range(args.steps)]
@@ -567,9 +571,14 @@ def main():
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic("decode_gate_up", w.name)}
         cfg["distinct_experts_mean"] = round(n_exp, 2)
-        w2_bytes = n_exp * w.H * w.I * 2
-        cfg["down_hbm_gbs"] = round((w2_bytes + n_valid * w.I * 2 + n_valid * w.H * 4) /
-                                    (phase_ms["down"] * 1e-3) / 1e9, 1)
+        # FC2 + combine: the selected experts' w2, the activations and the
+        # output (and y written and read back where the two are not fused).
+        fused = moe.moe_ffn_down_combine_fused(moe.MOE_BF16, T, w.H, w.I, E, k, decode)
+        dc_bytes = n_exp * w.H * w.I * 2 + n_valid * w.I * 2 + T * w.H * 2 + \
+            (0 if fused else n_valid * w.H * 4 * 2)
+        cfg["down_combine_fused"] = fused
+        cfg["down_combine_hbm_gbs"] = round(dc_bytes / (phase_ms["down_combine"] * 1e-3) / 1e9,
+                                            1)
         # The whole step against HBM: its algorithmic bytes (every selected
         # expert's w13 and w2 once, the logits, the routing and multihot
         # outputs, the inverse's reads and writes, the token rows and the

@@ -553,7 +553,8 @@ moe_status_t moe_expert_ffn_backward(moe_dtype_t dt, const void *hidden, const v
  *   plane order, then weighted and summed over j = 0..k-1 in float32.
  * `decode` != 0 selects the decode kernels (T <= MOE_DECODE_MAX_T).
  * moe_expert_ffn runs the three with splits = moe_ffn_down_splits(dt, decode,
- * ...), and its workspace holds act and the y planes.
+ * ...) (the last two through moe_ffn_down_combine, below), and its workspace
+ * holds act and the y planes.
  */
 int32_t moe_ffn_down_splits(moe_dtype_t dt, int32_t decode, int64_t T, int32_t H, int32_t I,
                             int32_t E, int32_t k);
@@ -567,6 +568,27 @@ moe_status_t moe_ffn_down(moe_dtype_t dt, int32_t decode, const void *act, const
 moe_status_t moe_combine(moe_dtype_t dt, const float *y, int32_t splits, const float *topk_w,
                          const int32_t *slot_to_sorted, int64_t T, int32_t H, int32_t k,
                          void *out, void *stream);
+
+/*
+ * moe_ffn_down_combine -- moe_ffn_down (with moe_ffn_down_splits' slice
+ * count) followed by moe_combine; moe_expert_ffn and moe_expert_ffn_decode
+ * run their last two phases through it.  [p6] moe_decode_experts,
+ * moe_prefill_experts (the down projection and the weighted sum).
+ *
+ * Where moe_ffn_down_combine_fused(...) is 1 (bf16 decode with at most 32
+ * routing slots and I <= 1536) the two run as one launch: each block owns 8
+ * output columns of every token and every selected expert, and the token's
+ * slots are summed in slot order from LDS, so y is not written (it may then
+ * be NULL) and, for finite activations, out is bit-identical to the two
+ * calls.  Otherwise y [splits, T*k, H] float32 is the intermediate.
+ */
+moe_status_t moe_ffn_down_combine(moe_dtype_t dt, int32_t decode, const void *act,
+                                  const void *w2, const float *topk_w,
+                                  const int32_t *expert_offsets, const int32_t *slot_to_sorted,
+                                  int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  float *y, void *out, void *stream);
+int32_t moe_ffn_down_combine_fused(moe_dtype_t dt, int32_t decode, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,8 @@ from .moe import (  # noqa: F401
     moe_align_inverse,
     moe_align_workspace_size,
     moe_combine,
+    moe_ffn_down_combine,
+    moe_ffn_down_combine_fused,
     moe_expert_ffn,
     moe_expert_ffn_backward,
     moe_expert_ffn_backward_workspace_size,

@@ -47,6 +47,9 @@ SIGNATURES = {
     "moe_route_align": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_align_fused": (_i32, [_i64, _i32, _i32]),
+    "moe_ffn_down_combine": (_st, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                   _i32, _vp, _vp, _vp]),
+    "moe_ffn_down_combine_fused": (_i32, [_i32, _i32, _i64, _i32, _i32, _i32, _i32]),
     "moe_tile_schedule_max": (_i64, [_i64, _i32, _i32]),
     "moe_tile_schedule": (_st, [_vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_align_inverse": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -590,6 +590,43 @@ moe_status_t moe_combine(moe_dtype_t dt, const float *y, int32_t splits, const f
                       fn);
 }
 
+moe_status_t moe_ffn_down_combine(moe_dtype_t dt, int32_t decode, const void *act,
+                                  const void *w2, const float *topk_w,
+                                  const int32_t *expert_offsets, const int32_t *slot_to_sorted,
+                                  int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  float *y, void *out, void *stream) {
+    const char *fn = "moe_ffn_down_combine";
+    moe_status_t st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    if (decode)
+        CHECK(T <= MOE_DECODE_MAX_T, MOE_ERR_UNSUPPORTED, "%s: decode needs T <= %d", fn,
+              MOE_DECODE_MAX_T);
+    if (T == 0) return MOE_OK;
+    const bool fused = dt == MOE_BF16 && decode && moe::decode_down_combine_fused(T, H, I, E, k);
+    CHECK(act && w2 && expert_offsets && topk_w && slot_to_sorted && out && (fused || y),
+          MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (fused) {
+        CHECK(aligned16(act) && aligned16(w2) && aligned16(out), MOE_ERR_INVALID_ARG,
+              "%s: act, w2 and out must be 16-byte aligned", fn);
+        return hip_status(moe::launch_decode_down_combine_bf16(
+                              static_cast<const uint16_t *>(act),
+                              static_cast<const uint16_t *>(w2), expert_offsets, topk_w,
+                              slot_to_sorted, T, H, I, E, k, static_cast<uint16_t *>(out),
+                              static_cast<hipStream_t>(stream)),
+                          fn);
+    }
+    const int32_t splits = decode ? 1 : prefill_splits(dt, T, H, I, E, k);
+    st = moe_ffn_down(dt, decode, act, w2, expert_offsets, T, H, I, E, k, splits, y, stream);
+    if (st != MOE_OK) return st;
+    return moe_combine(dt, y, splits, topk_w, slot_to_sorted, T, H, k, out, stream);
+}
+
+int32_t moe_ffn_down_combine_fused(moe_dtype_t dt, int32_t decode, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k) {
+    return dt == MOE_BF16 && decode && T >= 1 && T <= MOE_DECODE_MAX_T && H >= 1 && I >= 1 &&
+           k >= 1 && moe::decode_down_combine_fused(T, H, I, E, k);
+}
+
 static moe_status_t expert_ffn_impl(int32_t decode, moe_dtype_t dt, const void *hidden,
                                     const void *w13, const void *w2, const float *topk_w,
                                     const int32_t *expert_offsets,
@@ -617,9 +654,8 @@ static moe_status_t expert_ffn_impl(int32_t decode, moe_dtype_t dt, const void *
     st = moe_ffn_gate_up(dt, decode, hidden, w13, expert_offsets, sorted_token_ids, T, H, I, E,
                          k, act, stream);
     if (st != MOE_OK) return st;
-    st = moe_ffn_down(dt, decode, act, w2, expert_offsets, T, H, I, E, k, splits, y, stream);
-    if (st != MOE_OK) return st;
-    return moe_combine(dt, y, splits, topk_w, slot_to_sorted, T, H, k, out, stream);
+    return moe_ffn_down_combine(dt, decode, act, w2, topk_w, expert_offsets, slot_to_sorted, T, H,
+                                I, E, k, y, out, stream);
 }
 
 moe_status_t moe_expert_ffn(moe_dtype_t dt, const void *hidden, const void *w13,

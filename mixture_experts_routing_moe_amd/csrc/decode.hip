@@ -362,6 +362,235 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
         down_rows<MCmax, RT>(act, w2, H, I, e, base, cnt, y);
 }
 
+// FC2 and the combine in one launch, for the smallest batches (at most
+// kFusedSlots routing slots, I <= 64 kFusedPairs): block b owns output
+// columns [8 b, 8 b + 8) of every token, and wave w takes the non-empty
+// experts w, w + 8, ... in id order.  Each wave finds its first expert,
+// issues its first activation-chunk loads, then all of that expert's
+// weight loads (the 8 rows' whole lines, one 16-byte piece per lane per
+// 64-wide k-step pair; rows 8-15 of the MFMA operand are zero); the block
+// stages the activation rows in LDS (row pitch I + 8, so the 16 token
+// columns' reads fall on distinct banks) and meets at a barrier that waits
+// for LDS only, so the products start as the first pairs land.  Pair j's
+// registers are refilled with the next expert's pair j as soon as they are
+// consumed.  The k-steps are summed in the four quarters decode_down_kernel's
+// four waves take, in the same order, and the quarter sums are added in that
+// kernel's order (its batching only appends zero terms), so each y value is
+// that kernel's bit pattern; y goes to LDS, and the block sums each token's
+// k slots in slot order as combine_kernel does (fmaf, one rounding to bf16),
+// so `out` equals the two launches' for finite activations.
+constexpr int kFusedSlots = 32;
+constexpr int kFusedPairs = 24;
+constexpr int kFusedRows = 8;
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kStageLoads = 4;  // activation chunks per thread loaded ahead of the weights
+
+__device__ __forceinline__ int fused_pitch(int I) { return I + 8; }
+
+// One expert's products for the fused kernel: quarters of PER k-step pairs
+// (w = 0..3 covers pairs [w PER, w PER + PER) clipped to npairs; steps past
+// the last pair multiply zero weights, which adds exact zeros), quarter
+// sums added in order.  kTwo: a second block of token columns (16-31).
+// kRefill: each step reloads its pair's registers from wn (the next expert).
+// Straight-line code, so every wait counts the loads in flight exactly.
+template <int PER, bool kTwo, bool kRefill>
+__device__ __forceinline__ void fused_products(bf16x8 (&P)[4 * PER], int npairs, bool lo,
+                                               const uint16_t *ar0, const uint16_t *ar1,
+                                               const uint16_t *wn, f32x4 &t0, f32x4 &t1) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f32x4 c0{}, c1{};
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int j = w * PER + s;
+            // npairs >= 4 PER - 3: only the last three steps can fall past
+            // the last pair (a constant per unrolled step).
+            const bool tail = j >= 4 * PER - 3;
+            const int jc = tail ? min(j, npairs - 1) : j;
+            bf16x8 w0, w1;
+            unpair(lo, tail ? zero_unless(j < npairs, P[j]) : P[j], bf16x8{}, w0, w1);
+            const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(ar0 + jc * 64);
+            const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(ar0 + jc * 64 + 32);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, c0, 0, 0, 0);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, c0, 0, 0, 0);
+            if constexpr (kTwo) {
+                const bf16x8 z0 = *reinterpret_cast<const bf16x8 *>(ar1 + jc * 64);
+                const bf16x8 z1 = *reinterpret_cast<const bf16x8 *>(ar1 + jc * 64 + 32);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, z0, c1, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, z1, c1, 0, 0, 0);
+            }
+            if constexpr (kRefill) P[j] = ld_stream(wn + jc * 64);
+        }
+        if (w == 0) {
+            t0 = c0;
+            t1 = c1;
+        } else {
+            t0 += c0;
+            t1 += c1;
+        }
+    }
+}
+
+template <int PER>
+__device__ __forceinline__ void fused_products_any(bool two, bool refill,
+                                                   bf16x8 (&P)[4 * PER], int npairs,
+                                                   bool lo, const uint16_t *ar0,
+                                                   const uint16_t *ar1, const uint16_t *wn,
+                                                   f32x4 &t0, f32x4 &t1) {
+    if (two) {
+        if (refill)
+            fused_products<PER, true, true>(P, npairs, lo, ar0, ar1, wn, t0, t1);
+        else
+            fused_products<PER, true, false>(P, npairs, lo, ar0, ar1, wn, t0, t1);
+    } else {
+        if (refill)
+            fused_products<PER, false, true>(P, npairs, lo, ar0, ar1, wn, t0, t1);
+        else
+            fused_products<PER, false, false>(P, npairs, lo, ar0, ar1, wn, t0, t1);
+    }
+}
+
+// PER: k-step pairs per quarter, ceil(I / 256) (1..6).
+template <int PER>
+__global__ __launch_bounds__(kFusedThreads) void decode_down_combine_kernel(
+    const uint16_t *__restrict__ act, const uint16_t *__restrict__ w2,
+    const int32_t *__restrict__ offsets, const float *__restrict__ topk_w,
+    const int32_t *__restrict__ s2s, int T, int H, int I, int E, int k,
+    uint16_t *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t sact[];  // [rows][I + 8]
+    __shared__ int32_t le[kFusedSlots], lb[kFusedSlots], lc[kFusedSlots];
+    __shared__ int32_t lslot[kFusedSlots];
+    __shared__ float lw[kFusedSlots];
+    __shared__ float ys[kFusedSlots][kFusedRows];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int h0 = blockIdx.x * kFusedRows;
+    const int rows = min(offsets[E], T * k);  // valid positions (LDS holds T k rows)
+    // The combine's slot map and weights, read now rather than after the
+    // products (and put in LDS once the weight loads are on their way).
+    int my_slot = -1;
+    float my_w = 0.0f;
+    if (tid < T * k) {
+        my_slot = s2s[tid];
+        my_w = topk_w[tid];
+    }
+    const int npairs = I / 64;
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+    const bool lo = i < 8;
+
+    // The non-empty experts in id order (listed in LDS by wave 0); every
+    // wave finds its own first one.
+    int nd = 0, e0 = -1;
+    for (int c = 0; c < E; c += kWave) {
+        const int e = c + lane;
+        int off = 0, cn = 0;
+        if (e < E) {
+            off = offsets[e];
+            cn = offsets[e + 1] - off;
+        }
+        const uint64_t nz = __ballot(cn > 0);
+        const int d = nd + __popcll(nz & lanemask_lt());
+        if (wave == 0 && cn > 0 && d < kFusedSlots) {
+            le[d] = e;
+            lb[d] = off;
+            lc[d] = cn;
+        }
+        const uint64_t hit = __ballot(cn > 0 && d == wave);
+        if (hit) e0 = c + __ffsll((unsigned long long)hit) - 1;
+        nd += __popcll(nz);
+    }
+    nd = min(nd, kFusedSlots);
+
+    // The first kStageLoads activation chunks per thread, then the first
+    // expert's weights (paired loads of rows 0-7: row i & 7, half i >> 3 of
+    // each line).  Every load is issued unconditionally (indexes clamped
+    // into range), so the waits below count them exactly: the staging waits
+    // only for its own chunks, and pair j's products wait only for pair j.
+    const int chunks = I / 8;  // 16-byte chunks per row
+    const int pitch = fused_pitch(I);
+    const int nch = rows * chunks;
+    const int last = max(nch - 1, 0);
+    bf16x8 v[kStageLoads];
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u)
+        v[u] = *reinterpret_cast<const bf16x8 *>(
+            act + (int64_t)min(tid + u * kFusedThreads, last) * 8);
+    // A wave with no expert reads one 16-byte activation chunk instead.
+    const uint16_t *wrow = w2 + ((int64_t)h0 + (i & 7)) * I + (i >> 3) * 32 + kq * 8;
+    const uint16_t *wp = e0 >= 0 ? wrow + (int64_t)e0 * H * I : act;
+    const int pstep = e0 >= 0 ? 64 : 0;
+    constexpr int NP = 4 * PER;  // pair registers (quarters of PER pairs)
+    bf16x8 P[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) P[j] = ld_stream(wp + min(j, npairs - 1) * pstep);
+    if (tid < T * k) {
+        lslot[tid] = my_slot;
+        lw[tid] = my_w;
+    }
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u) {
+        const int c = tid + u * kFusedThreads;
+        if (c < nch) {
+            const int r = c / chunks;
+            *reinterpret_cast<bf16x8 *>(sact + r * pitch + (c - r * chunks) * 8) = v[u];
+        }
+    }
+    for (int c = tid + kStageLoads * kFusedThreads; c < nch; c += kFusedThreads) {
+        const int r = c / chunks;
+        *reinterpret_cast<bf16x8 *>(sact + r * pitch + (c - r * chunks) * 8) =
+            *reinterpret_cast<const bf16x8 *>(act + (int64_t)c * 8);
+    }
+    // LDS written (lists, slot map, activations); the weight loads stay in
+    // flight across the barrier (__syncthreads would drain them).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+
+    for (int d = wave; d < nd; d += kFusedWaves) {
+        const int base = lb[d], cnt = lc[d];
+        const bool two = cnt > 16;  // token columns 16-31 as a second MFMA column block
+        const int dn = d + kFusedWaves;
+        const bool more = dn < nd;
+        const uint16_t *wn = wrow + (int64_t)(more ? le[dn] : 0) * H * I;
+        const uint16_t *ar0 = sact + (base + min(i, cnt - 1)) * pitch + kq * 8;
+        const uint16_t *ar1 = sact + (base + min(16 + i, cnt - 1)) * pitch + kq * 8;
+        f32x4 tot0, tot1;
+        fused_products_any<PER>(two, more, P, npairs, lo, ar0, ar1, wn, tot0, tot1);
+        // Accumulator r holds weight row 4 kq + r (rows 0-7: kq < 2) of
+        // token column i (16 + i for the second block).
+        if (kq < 2) {
+            if (i < cnt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ys[base + i][4 * kq + r] = tot0[r];
+            }
+            if (16 + i < cnt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ys[base + 16 + i][4 * kq + r] = tot1[r];
+            }
+        }
+    }
+    __syncthreads();
+    // out[t, h0 .. h0 + 7]: the token's slots in order, as combine_kernel.
+    for (int t = tid; t < T; t += kFusedThreads) {
+        float o[kFusedRows];
+#pragma unroll
+        for (int r = 0; r < kFusedRows; ++r) o[r] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int p = lslot[t * k + j];
+            if (p < 0 || p >= rows) continue;
+            const float wj = lw[t * k + j];
+#pragma unroll
+            for (int r = 0; r < kFusedRows; ++r) o[r] = fmaf(wj, ys[p][r], o[r]);
+        }
+        bf16x8 v;
+#pragma unroll
+        for (int r = 0; r < kFusedRows; ++r) v[r] = to_bf16(o[r]);
+        *reinterpret_cast<bf16x8 *>(out + (int64_t)t * H + h0) = v;
+    }
+}
+
 int token_chunks(int64_t T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
 unsigned expert_rows(int64_t T, int E, int k) {
@@ -370,6 +599,64 @@ unsigned expert_rows(int64_t T, int E, int k) {
 }
 
 }  // namespace
+
+bool decode_down_combine_fused(int64_t T, int H, int I, int E, int k) {
+    return T * k <= kFusedSlots && I <= 64 * kFusedPairs && H % kFusedRows == 0 && E >= 1;
+}
+
+template <int PER>
+static hipError_t launch_fused(const uint16_t *act, const uint16_t *w2, const int32_t *offsets,
+                        const float *topk_w, const int32_t *slot_to_sorted, int T, int H, int I,
+                        int E, int k, uint16_t *out, size_t lds, hipStream_t s) {
+    hipLaunchKernelGGL(decode_down_combine_kernel<PER>, dim3(H / kFusedRows),
+                       dim3(kFusedThreads), lds, s, act, w2, offsets, topk_w, slot_to_sorted, T,
+                       H, I, E, k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_down_combine_bf16(const uint16_t *act, const uint16_t *w2,
+                                           const int32_t *offsets, const float *topk_w,
+                                           const int32_t *slot_to_sorted, int64_t T, int H,
+                                           int I, int E, int k, uint16_t *out, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (!decode_down_combine_fused(T, H, I, E, k)) return hipErrorInvalidValue;
+    // Past 64 KB of dynamic LDS a kernel's limit must be raised: once, for
+    // every instantiation, to the largest staging buffer the eligibility
+    // rule allows.
+    static const hipError_t raised = [] {
+        const void *fns[] = {reinterpret_cast<const void *>(decode_down_combine_kernel<1>),
+                             reinterpret_cast<const void *>(decode_down_combine_kernel<2>),
+                             reinterpret_cast<const void *>(decode_down_combine_kernel<3>),
+                             reinterpret_cast<const void *>(decode_down_combine_kernel<4>),
+                             reinterpret_cast<const void *>(decode_down_combine_kernel<5>),
+                             reinterpret_cast<const void *>(decode_down_combine_kernel<6>)};
+        for (const void *fn : fns) {
+            const hipError_t e = hipFuncSetAttribute(
+                fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                kFusedSlots * (64 * kFusedPairs + 8) * 2);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
+    if (raised != hipSuccess) return raised;
+    const size_t lds = (size_t)T * k * (I + 8) * 2;
+    const int Ti = (int)T;
+    switch ((I / 64 + 3) / 4) {  // k-step pairs per quarter
+        case 1: return launch_fused<1>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                       out, lds, s);
+        case 2: return launch_fused<2>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                       out, lds, s);
+        case 3: return launch_fused<3>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                       out, lds, s);
+        case 4: return launch_fused<4>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                       out, lds, s);
+        case 5: return launch_fused<5>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                       out, lds, s);
+        default: return launch_fused<6>(act, w2, offsets, topk_w, slot_to_sorted, Ti, H, I, E, k,
+                                        out, lds, s);
+    }
+}
+
 
 hipError_t launch_decode_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
                                       const int32_t *offsets, const int32_t *sorted_tok,

@@ -420,6 +420,14 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t *hidden, const uint16_t *w1
 hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
                                    const int32_t *offsets, int64_t T, int H, int I, int E, int k,
                                    float *y, hipStream_t s);
+// Decode FC2 + combine in one launch (bf16 out) where
+// decode_down_combine_fused holds (T k <= 32, I <= 1536, T k I <= 48 Ki
+// elements): the same out as launch_decode_down_bf16 + launch_combine.
+bool decode_down_combine_fused(int64_t T, int H, int I, int E, int k);
+hipError_t launch_decode_down_combine_bf16(const uint16_t *act, const uint16_t *w2,
+                                           const int32_t *offsets, const float *topk_w,
+                                           const int32_t *slot_to_sorted, int64_t T, int H,
+                                           int I, int E, int k, uint16_t *out, hipStream_t s);
 
 hipError_t launch_combine(moe_dtype_t dt, const float *y, int splits, const float *w,
                           const int32_t *slot_to_sorted, int64_t T, int H, int k, void *out,

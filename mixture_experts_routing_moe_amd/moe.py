@@ -466,6 +466,33 @@ def moe_combine(y, topk_w, slot_to_sorted, out_dtype=torch.bfloat16, out=None):
     return out
 
 
+def moe_ffn_down_combine_fused(dtype: int, T: int, H: int, I: int, E: int, k: int,
+                               decode: bool = False) -> bool:
+    return bool(lib().moe_ffn_down_combine_fused(dtype, int(decode), T, H, I, E, k))
+
+
+def moe_ffn_down_combine(act, w2, topk_w, aligned: dict, T: int, k: int, decode: bool = False,
+                         y=None, out=None, out_dtype=torch.bfloat16):
+    """moe_ffn_down + moe_combine in one call (one launch for small bf16 decode
+    batches, where y is not used) -> out [T, H]."""
+    E, H, I = w2.shape
+    dt = _dtype_code(act)
+    fused = moe_ffn_down_combine_fused(dt, T, H, I, E, k, decode)
+    if y is None and not fused:
+        splits = moe_ffn_down_splits(dt, T, H, I, E, k, decode)
+        shape = (T * k, H) if splits == 1 else (splits, T * k, H)
+        y = torch.empty(shape, dtype=torch.float32, device=act.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=act.device)
+    _dev(act, w2, topk_w, aligned["offsets"], aligned["slot_to_sorted"], out,
+         *([y] if y is not None else []))
+    check(lib().moe_ffn_down_combine(dt, int(decode), _ptr(act), _ptr(w2), _ptr(topk_w),
+                                     _ptr(aligned["offsets"]), _ptr(aligned["slot_to_sorted"]),
+                                     T, H, I, E, k, _ptr(y), _ptr(out), _stream()),
+          "moe_ffn_down_combine")
+    return out
+
+
 def moe_layer(hidden, w13, w2, logits, k: int, norm_topk_prob: bool = True,
               decode: bool | None = None):
     """route -> align -> expert FFN + combine.  Returns (out, topk_w, topk_ids, aligned)."""

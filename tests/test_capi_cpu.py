@@ -295,6 +295,40 @@ def test_down_split_validation(lib):
                   None) == _lib.MOE_ERR_INVALID_ARG
 
 
+def test_down_combine_validation(lib):
+    bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
+    f = lib.moe_ffn_down_combine_fused
+    # one launch for bf16 decode with at most 32 slots and I <= 1536
+    assert f(bf, 1, 1, 2048, 1408, 64, 8) == 1
+    assert f(bf, 1, 4, 2048, 1408, 64, 8) == 1
+    assert f(bf, 1, 8, 128, 1536, 8, 4) == 1
+    assert f(bf, 1, 32, 2048, 1408, 64, 8) == 0  # 256 slots
+    assert f(bf, 1, 1, 2048, 1600, 8, 2) == 0
+    assert f(bf, 0, 1, 2048, 1408, 64, 8) == 0  # prefill
+    assert f(f32, 1, 1, 2048, 1408, 64, 8) == 0
+    assert f(bf, 1, 0, 2048, 1408, 64, 8) == 0
+    call = "moe_ffn_down_combine"
+    a = (FAKE, FAKE, FAKE, FAKE, FAKE)  # act, w2, topk_w, offsets, slot_to_sorted
+    # y may be NULL only where the call is fused
+    assert status(lib, call, bf, 1, *a, 33, 128, 128, 8, 1, None, FAKE,
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, call, bf, 0, *a, 1, 128, 128, 8, 2, None, FAKE,
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, call, bf, 1, *a, 1, 128, 128, 8, 2, FAKE, None,
+                  None) == _lib.MOE_ERR_INVALID_ARG  # no out
+    # fused: 16-byte aligned act, w2 and out
+    assert status(lib, call, bf, 1, ctypes.c_void_p(0x1002), *a[1:], 1, 128, 128, 8, 2, None,
+                  FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, call, bf, 1, *a, 1, 128, 128, 8, 2, None, ctypes.c_void_p(0x1008),
+                  None) == _lib.MOE_ERR_INVALID_ARG
+    assert status(lib, call, bf, 1, *a, 65, 128, 128, 8, 2, FAKE, FAKE,
+                  None) == _lib.MOE_ERR_UNSUPPORTED  # decode T limit
+    assert status(lib, call, bf, 1, *a, 1, 100, 128, 8, 2, FAKE, FAKE,
+                  None) == _lib.MOE_ERR_UNSUPPORTED  # H % 64
+    assert status(lib, call, bf, 1, None, None, None, None, None, 0, 128, 128, 8, 2, None,
+                  None, None) == _lib.MOE_OK  # T = 0
+
+
 def test_last_error_is_thread_local(lib):
     import threading
     status(lib, "moe_route", FAKE, 4, 8, 9, 1, FAKE, FAKE, None)

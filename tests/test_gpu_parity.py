@@ -698,6 +698,44 @@ def test_ffn_bf16_decode(T, H, I, E, k):
     assert_bf16_layer(out, out32, ref)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,inv,skew", [
+    (1, 2048, 1408, 64, 8, 0.0, 0.0), (1, 128, 128, 8, 2, 0.0, 0.0),
+    (2, 512, 1536, 16, 8, 0.0, 0.0), (4, 256, 192, 64, 8, 0.0, 0.0),
+    (3, 192, 320, 6, 2, 0.3, 0.0), (16, 128, 192, 4, 2, 0.0, 0.0),
+    (32, 64, 64, 40, 1, 0.5, 0.0), (1, 64, 64, 1, 1, 0.0, 0.0), (6, 320, 1024, 6, 5, 0.0, 0.0),
+    (8, 128, 1536, 8, 4, 0.0, 0.0),  # both limits
+    # experts with more than 16 tokens (a second block of token columns)
+    (32, 128, 320, 4, 1, 0.0, 3.0), (28, 256, 448, 2, 1, 0.0, 1.0),
+    (24, 192, 704, 2, 1, 0.1, 2.0), (32, 64, 1536, 1, 1, 0.0, 0.0),
+    # not fused: more than 32 slots, I past the limit
+    (33, 128, 128, 8, 1, 0.0, 0.0), (1, 128, 1600, 4, 2, 0.0, 0.0)])
+def test_ffn_down_combine_decode(T, H, I, E, k, inv, skew):
+    """moe_ffn_down_combine equals moe_ffn_down + moe_combine bit for bit on
+    the decode path, fused (one launch, no y) or not, with ids dropped."""
+    x, w13, w2, w32, ids = _rand_layer(T * 7 + H + I + E, T, H, I, E, k, skew=skew, inv=inv)
+    cnt = np.bincount(ids[ids >= 0], minlength=E)
+    xd, w13d, w2d, twd = dev_bf16(x), dev_bf16(w13), dev_bf16(w2), dev(w32)
+    a = moe.moe_align(dev(ids), E)
+    fused = moe.moe_ffn_down_combine_fused(moe.MOE_BF16, T, H, I, E, k, decode=True)
+    assert fused == (T * k <= 32 and I <= 1536)
+    if T >= 20 and k == 1 and E <= 4:
+        assert cnt.max() > 16  # the case is meant to reach the second column block
+    act = moe.moe_ffn_gate_up(xd, w13d, a, k, decode=True)
+    y = moe.moe_ffn_down(act, w2d, a, T, k, decode=True)
+    two = moe.moe_combine(y, twd, a["slot_to_sorted"], torch.bfloat16,
+                          out=_nan_filled((T, H), torch.bfloat16))
+    one = moe.moe_ffn_down_combine(act, w2d, twd, a, T, k, decode=True,
+                                   out=_nan_filled((T, H), torch.bfloat16))
+    again = moe.moe_ffn_down_combine(act, w2d, twd, a, T, k, decode=True)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), two.view(torch.int16))
+    ref = oracle.expert_ffn(x, w13, w2, w32.astype(np.float64), ids, "bf16")
+    out32 = moe.moe_combine(y, twd, a["slot_to_sorted"], torch.float32)
+    torch.cuda.synchronize()
+    assert_bf16_layer(host(one), host(out32), ref)
+
+
 @pytest.mark.parametrize("T,H,I,E,k", [(4, 64, 128, 8, 2), (50, 128, 64, 5, 3), (1, 64, 64, 1, 1)])
 def test_ffn_f32(T, H, I, E, k):
     x, w13, w2, w32, ids = _rand_layer(T + 3 * H, T, H, I, E, k, dtype="f32")
@@ -844,6 +882,10 @@ def _layer_into(bufs, logits, x, w13, w2, k, decode, fused=False):
         moe.moe_route(logits, k, True, bufs["tw"], bufs["ids"])
         moe.moe_align(bufs["ids"], E, bufs["aligned"], bufs["ws"])
     moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
+    if fused:  # FC2 + combine in one call (one launch for the smallest decode batches)
+        moe.moe_ffn_down_combine(bufs["act"], w2, bufs["tw"], bufs["aligned"], T, k, decode,
+                                 bufs["y"], bufs["out"])
+        return
     moe.moe_ffn_down(bufs["act"], w2, bufs["aligned"], T, k, decode, bufs["y"])
     moe.moe_combine(bufs["y"], bufs["tw"], bufs["aligned"]["slot_to_sorted"], torch.bfloat16,
                     bufs["out"])
