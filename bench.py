@@ -34,6 +34,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
     "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
+    # decode FC2 + combine (one launch for the smallest batches, else two)
+    "decode_down_combine": ["mixture_experts_routing_moe_amd/csrc/decode.hip",
+                            "mixture_experts_routing_moe_amd/csrc/combine.hip"],
     # route_hist_kernel + align_scatter_kernel with the inverse's blocks (the
     # routing rows of moe_route_align_inverse)
     "route_align_inverse": ["mixture_experts_routing_moe_amd/csrc/align.hip",
@@ -579,6 +582,7 @@ def main():
         cfg["down_combine_fused"] = fused
         cfg["down_combine_hbm_gbs"] = round(dc_bytes / (phase_ms["down_combine"] * 1e-3) / 1e9,
                                             1)
+        cfg["down_combine_traffic"] = measured_traffic("decode_down_combine", w.name)
         # The whole step against HBM: its algorithmic bytes (every selected
         # expert's w13 and w2 once, the logits, the routing and multihot
         # outputs, the inverse's reads and writes, the token rows and the
