@@ -8,7 +8,9 @@ moe_route_align_inverse: one kernel for at most 512 routing slots, else a
 route kernel that also counts the alignment's histograms plus the scatter
 kernel, whose launch also carries the inverse conversion's blocks) ->
 grouped FC1 + SiLU-and-mul -> grouped FC2 -> combine (decode workloads use
-the decode FFN kernels).  Inputs are resident in HBM before timing starts; nothing is
+the decode FFN kernels: FC2 and the combine through moe_ffn_down_combine and,
+for the smallest batches, the routing calls and FC1 as one call,
+moe_route_align_gate_up, one launch each).  Inputs are resident in HBM before timing starts; nothing is
 allocated inside the timed region.  Each phase is bracketed by HIP events on
 the stream the library launches on (torch's current stream), so per-kernel
 durations are measured live.  Prints one JSON line.
@@ -34,6 +36,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "gate_up": "mixture_experts_routing_moe_amd/csrc/gemm_bf16.hip",
     "decode_gate_up": "mixture_experts_routing_moe_amd/csrc/decode.hip",
+    # route + align + the maps and their inverse + decode FC1 in one launch
+    "decode_route_gate_up": ["mixture_experts_routing_moe_amd/csrc/decode.hip",
+                             "mixture_experts_routing_moe_amd/csrc/moe_internal.h"],
     # decode FC2 + combine (one launch for the smallest batches, else two)
     "decode_down_combine": ["mixture_experts_routing_moe_amd/csrc/decode.hip",
                             "mixture_experts_routing_moe_amd/csrc/combine.hip"],
@@ -428,7 +433,13 @@ def main():
     if grouped:  # group-limited selection (+ indices->multihot), then align + the inverse
         phases = ["route_grouped", "align_inverse"]
     ai_out = {**aligned, "probs_indices": back_p, "ids_from_multihot": back_i}
-    if has_ffn and decode:  # FC2 and the combine through one call (one launch where fused)
+    # Decode: FC2 and the combine through one call (one launch where fused);
+    # for the smallest batches the routing call and FC1 are one call as well.
+    route_fc1 = has_ffn and decode and moe.moe_route_align_gate_up_fused(
+        T, E, k, moe.MOE_BF16, decode, w.H, w.I)
+    if route_fc1:
+        phases = ["route_align_gate_up", "down_combine"]
+    elif has_ffn and decode:
         phases += ["gate_up", "down_combine"]
     elif has_ffn:
         phases += ["gate_up", "down", "combine"]
@@ -438,6 +449,9 @@ def main():
     def run_phase(name):
         if name == "route_align_inverse":
             moe.moe_route_align_inverse(cur["logits"], k, w.norm, out=ra_out, workspace=align_ws)
+        elif name == "route_align_gate_up":
+            moe.moe_route_align_gate_up(cur["logits"], k, hidden, w13, w.norm, decode=True,
+                                        inverse=True, out=ra_out, act=act, workspace=align_ws)
         elif name == "route_grouped":
             moe.moe_route_grouped(cur["logits"], k, w.n_group, w.topk_group, w.method, bias_d,
                                   w.renorm, topk_w, topk_ids, multihot=(mh, pim, pos))
@@ -568,12 +582,22 @@ def main():
         # (mean over the routing draws) + the token rows + the activations.
         n_exp = sum(n_distinct) / len(n_distinct)
         nbytes = n_exp * 2 * w.I * w.H * 2 + T * w.H * 2 + n_valid * w.I * 2
-        achieved = nbytes / (phase_ms["gate_up"] * 1e-3) / 1e9
-        roofline = {"kernel": "decode_gate_up_kernel", "bound": "hbm",
+        if route_fc1:
+            # The same launch routes: + the logits, the weights and ids, the
+            # multihot maps, the alignment and the inverse's reads and writes.
+            nbytes += T * E * 4 + T * k * 8 + T * E * 9 + T * k * 12 + (2 * E + 1) * 4 + \
+                T * E * 8 + T * k * 8
+            achieved = nbytes / (phase_ms["route_align_gate_up"] * 1e-3) / 1e9
+            kname, tkey = "decode_route_gate_up_kernel (route + align + FC1)", "decode_route_gate_up"
+        else:
+            achieved = nbytes / (phase_ms["gate_up"] * 1e-3) / 1e9
+            kname, tkey = "decode_gate_up_kernel", "decode_gate_up"
+        roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": measured_traffic("decode_gate_up", w.name)}
+                    "traffic": measured_traffic(tkey, w.name)}
         cfg["distinct_experts_mean"] = round(n_exp, 2)
+        cfg["route_align_gate_up_fused"] = bool(route_fc1)
         # FC2 + combine: the selected experts' w2, the activations and the
         # output (and y written and read back where the two are not fused).
         fused = moe.moe_ffn_down_combine_fused(moe.MOE_BF16, T, w.H, w.I, E, k, decode)

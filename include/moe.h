@@ -10,6 +10,8 @@
  *   moe_router_route          router GEMM (hidden . w_gate^T) + moe_route, one pass
  *   moe_route_align           moe_route(_multihot) + moe_align in fewer launches
  *   moe_route_align_inverse   moe_route_align + moe_multihot_to_indices on its maps
+ *   moe_route_align_gate_up   moe_route_align(_inverse) + moe_ffn_gate_up (one launch
+ *                             for the smallest decode batches)
  *   moe_align                 per-expert histogram, exclusive offsets, stable
  *                             expert-major order of the (token, slot) pairs
  *   moe_align_inverse         moe_align + moe_multihot_to_indices on given maps
@@ -319,6 +321,34 @@ moe_status_t moe_route_align_inverse(const float *logits, int64_t T, int32_t E, 
                                      int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
                                      float *probs_indices, int32_t *ids_from_multihot,
                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_route_align_gate_up -- moe_route_align (moe_route_align_inverse when
+ * probs_indices is given; the multihot outputs may then not be NULL, and
+ * without probs_indices they are optional as in moe_route_align) followed by
+ * moe_ffn_gate_up (dt, decode, hidden [T, H], w13 [E, 2I, H], act [T*k, I]:
+ * that call's arguments and conditions) on the alignment it wrote.  [p6]
+ * moe_decode_experts (the FC1 of the selected experts), after the sources of
+ * moe_route_align.
+ *
+ * Where moe_route_align_gate_up_fused(T, E, k, dt, decode, H, I) is 1 (bf16
+ * decode, T < 16, T k <= 64, E <= 64, k <= 16, and when the multihot maps
+ * are given, 16-byte aligned rows of them) the whole call is one launch:
+ * every FC1 block routes and aligns the batch in its own shared memory and
+ * reads its tokens from there, and one block also writes every routing
+ * output; otherwise it is the separate calls' launches.  Every output is
+ * bit-identical to the separate calls.  Same workspace as moe_route_align.
+ */
+moe_status_t moe_route_align_gate_up(
+    const float *logits, int64_t T, int32_t E, int32_t k, int32_t norm_topk_prob, float *topk_w,
+    int32_t *topk_ids, uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
+    int32_t *expert_counts, int32_t *expert_offsets, int32_t *sorted_token_ids,
+    int32_t *sorted_slot_ids, int32_t *slot_to_sorted, float *probs_indices,
+    int32_t *ids_from_multihot, moe_dtype_t dt, int32_t decode, const void *hidden,
+    const void *w13, int32_t H, int32_t I, void *act, void *workspace, size_t workspace_bytes,
+    void *stream);
+int32_t moe_route_align_gate_up_fused(int64_t T, int32_t E, int32_t k, moe_dtype_t dt,
+                                      int32_t decode, int32_t H, int32_t I);
 
 /*
  * moe_route_align_noalloc -- moe_route_align for callers that cannot allocate

@@ -28,6 +28,8 @@ from .moe import (  # noqa: F401
     moe_route_align,
     moe_route_align_fused,
     moe_route_align_inverse,
+    moe_route_align_gate_up,
+    moe_route_align_gate_up_fused,
     moe_route_align_noalloc,
     moe_tile_schedule,
     moe_tile_schedule_max,

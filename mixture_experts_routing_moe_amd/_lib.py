@@ -56,6 +56,10 @@ SIGNATURES = {
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_align_noalloc": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_align_gate_up": (_st, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32,
+                                      _i32, _vp, _vp, _sz, _vp]),
+    "moe_route_align_gate_up_fused": (_i32, [_i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_align": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_align_inverse": (_st, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _sz, _vp]),

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kWave) void route_align_wave_kernel(
     float *__restrict__ inv_w, int32_t *__restrict__ inv_ids) {
     __shared__ int32_t s_ids[kWave];
     __shared__ int32_t s_cnt[kWave];
-    __shared__ int32_t s_off[kWave];
+    __shared__ int32_t s_off[kWave + 1];
     const int lane = lane_id();
     const int g = lane >> 4;
     const int q = lane & 15;
@@ -338,45 +338,8 @@ __global__ __launch_bounds__(kWave) void route_align_wave_kernel(
         }
     }
     __syncthreads();
-    const int s = lane;
-    const int e = s < n ? s_ids[s] : -1;
-    const bool ok = (unsigned)e < (unsigned)E;
-    uint64_t peers = __ballot(ok);
-    for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = (e >> bit) & 1;
-        const uint64_t m = __ballot(ok && set);
-        peers &= set ? m : ~m;
-    }
-    const int rank = __popcll(peers & lanemask_lt());
-    if (ok && rank == 0) s_cnt[e] = __popcll(peers);
-    __syncthreads();
-    const int c = lane < E ? s_cnt[lane] : 0;
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    s_off[lane] = incl - c;
-    if (lane < E) {
-        counts[lane] = c;
-        offsets[lane] = incl - c;
-    }
-    if (lane == 0) offsets[E] = total;
-    __syncthreads();
-    if (ok) {
-        const int p = s_off[e] + rank;
-        sorted_tok[p] = s / k;
-        sorted_slot[p] = s;
-        slot_to_sorted[s] = p;
-    } else if (s < n) {
-        slot_to_sorted[s] = -1;
-    }
-    for (int p = total + lane; p < n; p += kWave) {
-        sorted_tok[p] = -1;
-        sorted_slot[p] = -1;
-    }
+    align_slots_wave(s_ids, n, k, E, nbits, s_cnt, s_off, counts, offsets, sorted_tok,
+                     sorted_slot, slot_to_sorted, nullptr);
     // With inv_w: the multihot maps back to indices (moe_multihot_to_indices),
     // read from the rows this wave wrote.
     if (inv_w != nullptr) {

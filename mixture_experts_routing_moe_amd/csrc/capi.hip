@@ -303,14 +303,13 @@ namespace {
 
 // moe_route_align's checks and launches, with the alignment scratch given as
 // a device pointer (the caller's workspace, or the library's static array).
-moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, int32_t E,
-                              int32_t k, int32_t norm_topk_prob, float *topk_w,
-                              int32_t *topk_ids, uint8_t *multihot, float *probs_in_multihot,
-                              int32_t *position_map, int32_t *expert_counts,
-                              int32_t *expert_offsets, int32_t *sorted_token_ids,
-                              int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
-                              void *workspace, size_t workspace_bytes, void *stream,
-                              float *inv_probs = nullptr, int32_t *inv_ids = nullptr) {
+moe_status_t route_align_check(const char *fn, const float *logits, int64_t T, int32_t E,
+                               int32_t k, float *topk_w, int32_t *topk_ids, uint8_t *multihot,
+                               float *probs_in_multihot, int32_t *position_map,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *sorted_token_ids, int32_t *sorted_slot_ids,
+                               int32_t *slot_to_sorted, void *workspace, size_t workspace_bytes,
+                               float *inv_probs, int32_t *inv_ids) {
     moe_status_t st = check_routing_dims(T, E, k, fn);
     if (st != MOE_OK) return st;
     CHECK(k <= E, MOE_ERR_INVALID_ARG, "%s: k = %d > E = %d", fn, k, E);
@@ -329,6 +328,23 @@ moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, in
     const size_t need = moe_align_workspace_size(T, k, E);
     CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    return MOE_OK;
+}
+
+moe_status_t route_align_impl(const char *fn, const float *logits, int64_t T, int32_t E,
+                              int32_t k, int32_t norm_topk_prob, float *topk_w,
+                              int32_t *topk_ids, uint8_t *multihot, float *probs_in_multihot,
+                              int32_t *position_map, int32_t *expert_counts,
+                              int32_t *expert_offsets, int32_t *sorted_token_ids,
+                              int32_t *sorted_slot_ids, int32_t *slot_to_sorted,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              float *inv_probs = nullptr, int32_t *inv_ids = nullptr) {
+    moe_status_t st = route_align_check(fn, logits, T, E, k, topk_w, topk_ids, multihot,
+                                        probs_in_multihot, position_map, expert_counts,
+                                        expert_offsets, sorted_token_ids, sorted_slot_ids,
+                                        slot_to_sorted, workspace, workspace_bytes, inv_probs,
+                                        inv_ids);
+    if (st != MOE_OK) return st;
     return hip_status(moe::launch_route_align(logits, T, E, k, norm_topk_prob != 0, topk_w,
                                               topk_ids, multihot, probs_in_multihot,
                                               position_map, expert_counts, expert_offsets,
@@ -409,6 +425,65 @@ moe_status_t moe_route_align_inverse(const float *logits, int64_t T, int32_t E, 
                             probs_in_multihot, position_map, expert_counts, expert_offsets,
                             sorted_token_ids, sorted_slot_ids, slot_to_sorted, workspace,
                             workspace_bytes, stream, probs_indices, ids_from_multihot);
+}
+
+int32_t moe_route_align_gate_up_fused(int64_t T, int32_t E, int32_t k, moe_dtype_t dt,
+                                      int32_t decode, int32_t H, int32_t I) {
+    return dt == MOE_BF16 && decode && H >= 1 && I >= 1 && H % 64 == 0 && I % 64 == 0 &&
+           moe::decode_route_gate_up_fused(T, E, k, H, I);
+}
+
+moe_status_t moe_route_align_gate_up(
+    const float *logits, int64_t T, int32_t E, int32_t k, int32_t norm_topk_prob, float *topk_w,
+    int32_t *topk_ids, uint8_t *multihot, float *probs_in_multihot, int32_t *position_map,
+    int32_t *expert_counts, int32_t *expert_offsets, int32_t *sorted_token_ids,
+    int32_t *sorted_slot_ids, int32_t *slot_to_sorted, float *probs_indices,
+    int32_t *ids_from_multihot, moe_dtype_t dt, int32_t decode, const void *hidden,
+    const void *w13, int32_t H, int32_t I, void *act, void *workspace, size_t workspace_bytes,
+    void *stream) {
+    const char *fn = "moe_route_align_gate_up";
+    moe_status_t st = route_align_check(fn, logits, T, E, k, topk_w, topk_ids, multihot,
+                                        probs_in_multihot, position_map, expert_counts,
+                                        expert_offsets, sorted_token_ids, sorted_slot_ids,
+                                        slot_to_sorted, workspace, workspace_bytes, probs_indices,
+                                        ids_from_multihot);
+    if (st != MOE_OK) return st;
+    st = check_ffn_dims(dt, T, H, I, E, k, fn);
+    if (st != MOE_OK) return st;
+    if (decode)
+        CHECK(T <= MOE_DECODE_MAX_T, MOE_ERR_UNSUPPORTED, "%s: decode needs T <= %d", fn,
+              MOE_DECODE_MAX_T);
+    if (T > 0) {
+        CHECK(hidden && w13 && act, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+        CHECK(aligned16(hidden) && aligned16(w13) && aligned16(act), MOE_ERR_INVALID_ARG,
+              "%s: hidden, w13 and act must be 16-byte aligned", fn);
+    }
+    const bool fused = T > 0 && moe_route_align_gate_up_fused(T, E, k, dt, decode, H, I) &&
+                       (multihot == nullptr ||
+                        moe::route_multihot_fused(E, k, multihot, probs_in_multihot,
+                                                  position_map));
+    if (T == 0)  // no rows: the alignment's zero counts and offsets only
+        return route_align_impl(fn, logits, T, E, k, norm_topk_prob, topk_w, topk_ids, nullptr,
+                                nullptr, nullptr, expert_counts, expert_offsets,
+                                sorted_token_ids, sorted_slot_ids, slot_to_sorted, workspace,
+                                workspace_bytes, stream);
+    if (!fused) {
+        st = route_align_impl(fn, logits, T, E, k, norm_topk_prob, topk_w, topk_ids, multihot,
+                              probs_in_multihot, position_map, expert_counts, expert_offsets,
+                              sorted_token_ids, sorted_slot_ids, slot_to_sorted, workspace,
+                              workspace_bytes, stream, probs_indices, ids_from_multihot);
+        if (st != MOE_OK) return st;
+        return moe_ffn_gate_up(dt, decode, hidden, w13, expert_offsets, sorted_token_ids, T, H, I,
+                               E, k, act, stream);
+    }
+    return hip_status(moe::launch_decode_route_gate_up_bf16(
+                          logits, T, E, k, norm_topk_prob != 0, topk_w, topk_ids, multihot,
+                          probs_in_multihot, position_map, expert_counts, expert_offsets,
+                          sorted_token_ids, sorted_slot_ids, slot_to_sorted, probs_indices,
+                          ids_from_multihot, static_cast<const uint16_t *>(hidden),
+                          static_cast<const uint16_t *>(w13), H, I, static_cast<uint16_t *>(act),
+                          static_cast<hipStream_t>(stream)),
+                      fn);
 }
 
 moe_status_t moe_route_align_noalloc(const float *logits, int64_t T, int32_t E, int32_t k,

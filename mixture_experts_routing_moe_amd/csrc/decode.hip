@@ -347,6 +347,64 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
         gate_up_rows<MCmax, RT>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
 }
 
+// Route + align + FC1 in one launch for the smallest decode batches (T < 16,
+// T k <= kWave slots, E <= 64, k <= 16): every block routes the batch's rows
+// itself (route16_row, the moe_route selection; wave w takes rows 4w .. 4w +
+// 3) and aligns them (align_slots_wave, the moe_align order) in LDS, then
+// runs FC1 for the blockIdx.y-th non-empty expert from the LDS copy of the
+// aligned token ids, so no block waits for another launch's writes.  Block
+// (0, 0) also writes every routing output (weights, ids, the multihot maps
+// when given, the alignment) and, after its FC1 rows, converts the maps back
+// to indices: the outputs of moe_route_align(_inverse) bit for bit.
+__global__ __launch_bounds__(kThreads) void decode_route_gate_up_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int norm, int vec4, int nbits,
+    float *__restrict__ topk_w, int32_t *__restrict__ topk_ids, uint8_t *__restrict__ multihot,
+    float *__restrict__ pim, int32_t *__restrict__ pos, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_tok,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_to_sorted,
+    float *__restrict__ inv_w, int32_t *__restrict__ inv_ids, const uint16_t *__restrict__ hidden,
+    const uint16_t *__restrict__ w13, int H, int I, uint16_t *__restrict__ act) {
+    __shared__ int32_t s_ids[kWave];
+    __shared__ int32_t s_cnt[kWave];
+    __shared__ int32_t s_off[kWave + 1];
+    __shared__ int32_t s_tok[kWave];
+    __shared__ float s_w[kWave];     // weights and ids of the blocks that do not
+    __shared__ int32_t s_tid[kWave];  // write them out
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int g = lane >> 4;
+    const int q = lane & 15;
+    const int n = T * k;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    if (threadIdx.x < kWave) {
+        s_ids[lane] = -1;
+        s_cnt[lane] = 0;
+    }
+    __syncthreads();
+    const int t = 4 * wave + g;  // T < 16: one row per 16-lane group
+    const uint32_t slot_of =
+        route16_row(logits, T, t, E, k, norm, vec4, writer ? topk_w : s_w,
+                    writer ? topk_ids : s_tid, writer ? multihot : nullptr, pim, pos, g, q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t r = (slot_of >> (8 * i)) & 0xFFu;
+        if (r != 0xFFu) s_ids[t * k + (int)r] = 4 * q + i;
+    }
+    __syncthreads();
+    if (wave == 0)
+        align_slots_wave(s_ids, n, k, E, nbits, s_cnt, s_off, writer ? counts : nullptr, offsets,
+                         sorted_tok, sorted_slot, slot_to_sorted, s_tok);
+    __syncthreads();
+    int e, base, cnt;
+    if (nth_nonempty_expert(s_off, E, blockIdx.y, e, base, cnt))
+        gate_up_rows<1, 1>(hidden, w13, s_tok, H, I, e, base, cnt, act);
+    // With inv_w: block (0, 0) converts the maps it wrote back to indices.
+    if (writer && inv_w != nullptr) {
+        __syncthreads();
+        to_indices_row16<4>(pim, pos, T, t, E, k, inv_w, inv_ids, q);
+    }
+}
+
 // One block per (RT x 16 weight rows, non-empty expert).
 template <int MCmax, int RT>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
@@ -657,6 +715,29 @@ hipError_t launch_decode_down_combine_bf16(const uint16_t *act, const uint16_t *
     }
 }
 
+
+bool decode_route_gate_up_fused(int64_t T, int E, int k, int H, int I) {
+    return T >= 1 && T < 16 && T * k <= kWave && E >= 1 && E <= 64 && k >= 1 && k <= 16 &&
+           k <= E && H % 64 == 0 && I % kRows == 0;
+}
+
+hipError_t launch_decode_route_gate_up_bf16(
+    const float *logits, int64_t T, int E, int k, int norm, float *topk_w, int32_t *topk_ids,
+    uint8_t *multihot, float *pim, int32_t *pos, int32_t *counts, int32_t *offsets,
+    int32_t *sorted_tok, int32_t *sorted_slot, int32_t *slot_to_sorted, float *inv_w,
+    int32_t *inv_ids, const uint16_t *hidden, const uint16_t *w13, int H, int I, uint16_t *act,
+    hipStream_t s) {
+    if (!decode_route_gate_up_fused(T, E, k, H, I)) return hipErrorInvalidValue;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int vec4 = E == 64 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+    const dim3 grid(I / kRows, expert_rows(T, E, k));
+    hipLaunchKernelGGL(decode_route_gate_up_kernel, grid, dim3(kThreads), 0, s, logits, (int)T, E,
+                       k, norm, vec4, nbits, topk_w, topk_ids, multihot, pim, pos, counts, offsets,
+                       sorted_tok, sorted_slot, slot_to_sorted, inv_w, inv_ids, hidden, w13, H, I,
+                       act);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_gate_up_bf16(const uint16_t *hidden, const uint16_t *w13,
                                       const int32_t *offsets, const int32_t *sorted_tok,

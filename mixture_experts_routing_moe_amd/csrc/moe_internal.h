@@ -168,6 +168,78 @@ __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, i
     return (float)(ex / sum);
 }
 
+// Stable alignment of at most kWave routing slots by one wave: slot s = lane
+// holds expert s_ids[s] (LDS; -1 or >= E: dropped).  A slot's rank among the
+// earlier slots of its expert comes from ceil(log2 E) ballots + popcount,
+// the expert leaders record the counts in s_cnt (LDS, E entries, zero on
+// entry), and lane e scans them into the exclusive offsets s_off (LDS, E + 1
+// entries).  The wave's own LDS accesses are ordered, so it needs no block
+// barrier; it must be the only wave touching s_cnt and s_off.  When
+// `counts` is not null, also writes counts, offsets, sorted_tok, sorted_slot
+// and slot_to_sorted to memory (positions past the valid slots read -1);
+// when `l_sorted_tok` is not null, sorted_tok also goes there (LDS, n
+// entries).  E <= kWave.
+__device__ __forceinline__ void align_slots_wave(const int32_t *s_ids, int n, int k, int E,
+                                                 int nbits, int32_t *s_cnt, int32_t *s_off,
+                                                 int32_t *__restrict__ counts,
+                                                 int32_t *__restrict__ offsets,
+                                                 int32_t *__restrict__ sorted_tok,
+                                                 int32_t *__restrict__ sorted_slot,
+                                                 int32_t *__restrict__ slot_to_sorted,
+                                                 int32_t *l_sorted_tok) {
+    const int lane = lane_id();
+    const int s = lane;
+    const int e = s < n ? s_ids[s] : -1;
+    const bool ok = (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t m = __ballot(ok && set);
+        peers &= set ? m : ~m;
+    }
+    const int rank = __popcll(peers & lanemask_lt());
+    if (ok && rank == 0) s_cnt[e] = __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int c = lane < E ? s_cnt[lane] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    s_off[lane] = incl - c;
+    if (lane == 0) s_off[E] = total;
+    if (counts != nullptr) {
+        if (lane < E) {
+            counts[lane] = c;
+            offsets[lane] = incl - c;
+        }
+        if (lane == 0) offsets[E] = total;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+        const int p = s_off[e] + rank;
+        if (l_sorted_tok != nullptr) l_sorted_tok[p] = s / k;
+        if (counts != nullptr) {
+            sorted_tok[p] = s / k;
+            sorted_slot[p] = s;
+            slot_to_sorted[s] = p;
+        }
+    } else if (s < n && counts != nullptr) {
+        slot_to_sorted[s] = -1;
+    }
+    for (int p = total + lane; p < n; p += kWave) {
+        if (l_sorted_tok != nullptr) l_sorted_tok[p] = -1;
+        if (counts != nullptr) {
+            sorted_tok[p] = -1;
+            sorted_slot[p] = -1;
+        }
+    }
+}
+
 // Largest k served by the 16-lanes-per-row converters.
 constexpr int kKMax16 = 16;
 
@@ -423,6 +495,15 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
 // Decode FC2 + combine in one launch (bf16 out) where
 // decode_down_combine_fused holds (T k <= 32, I <= 1536, T k I <= 48 Ki
 // elements): the same out as launch_decode_down_bf16 + launch_combine.
+// Route + align (+ the multihot maps and their inverse) + decode FC1 in one
+// launch; eligibility (T < 16, T k <= 64, E <= 64, k <= 16) and launch.
+bool decode_route_gate_up_fused(int64_t T, int E, int k, int H, int I);
+hipError_t launch_decode_route_gate_up_bf16(
+    const float *logits, int64_t T, int E, int k, int norm, float *topk_w, int32_t *topk_ids,
+    uint8_t *multihot, float *pim, int32_t *pos, int32_t *counts, int32_t *offsets,
+    int32_t *sorted_tok, int32_t *sorted_slot, int32_t *slot_to_sorted, float *inv_w,
+    int32_t *inv_ids, const uint16_t *hidden, const uint16_t *w13, int H, int I, uint16_t *act,
+    hipStream_t s);
 bool decode_down_combine_fused(int64_t T, int H, int I, int E, int k);
 hipError_t launch_decode_down_combine_bf16(const uint16_t *act, const uint16_t *w2,
                                            const int32_t *offsets, const float *topk_w,

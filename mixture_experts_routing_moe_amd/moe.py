@@ -307,6 +307,40 @@ def moe_route_align_inverse(logits: torch.Tensor, k: int, norm_topk_prob: bool =
     return out
 
 
+def moe_route_align_gate_up_fused(T: int, E: int, k: int, dtype: int, decode: bool, H: int,
+                                  I: int) -> bool:
+    return bool(lib().moe_route_align_gate_up_fused(T, E, k, dtype, int(decode), H, I))
+
+
+def moe_route_align_gate_up(logits: torch.Tensor, k: int, hidden: torch.Tensor,
+                            w13: torch.Tensor, norm_topk_prob: bool = True, decode: bool = True,
+                            inverse: bool = True, out: dict | None = None, act=None,
+                            workspace: torch.Tensor | None = None):
+    """moe_route_align_inverse (moe_route_align without `inverse`) + moe_ffn_gate_up
+    in one call -> (the routing dict, act [T*k, I]); one launch for the smallest
+    bf16 decode batches (moe_route_align_gate_up_fused)."""
+    T, E, out = _route_align_outputs(logits, k, inverse, out)
+    if inverse and "probs_indices" not in out:
+        out["probs_indices"] = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+        out["ids_from_multihot"] = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    E2, I2, H = w13.shape
+    if E2 != E or hidden.shape != (T, H):
+        raise ValueError("hidden must be [T, H] and w13 [E, 2I, H]")
+    I = I2 // 2
+    if act is None:
+        act = torch.empty((T * k, I), dtype=hidden.dtype, device=hidden.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_align_workspace_size(T, k, E)), dtype=torch.uint8,
+                                device=logits.device)
+    _dev(logits, workspace, hidden, w13, act, *out.values())
+    check(lib().moe_route_align_gate_up(
+        _ptr(logits), T, E, k, int(bool(norm_topk_prob)), *_route_align_ptrs(out),
+        _ptr(out.get("probs_indices")), _ptr(out.get("ids_from_multihot")),
+        _dtype_code(hidden), int(decode), _ptr(hidden), _ptr(w13), H, I, _ptr(act),
+        _ptr(workspace), workspace.numel(), _stream()), "moe_route_align_gate_up")
+    return out, act
+
+
 def moe_route_align_noalloc(logits: torch.Tensor, k: int, norm_topk_prob: bool = True,
                             with_multihot: bool = False, out: dict | None = None) -> dict:
     """moe_route_align without a workspace: the library's own device scratch

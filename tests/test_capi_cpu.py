@@ -168,6 +168,40 @@ def test_route_align_inverse_validation(lib):
     assert rai(ws=None) == W
 
 
+def test_route_align_gate_up_validation(lib):
+    I, W, U = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE, _lib.MOE_ERR_UNSUPPORTED
+    bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
+    f = lib.moe_route_align_gate_up_fused
+    # one launch: bf16 decode, T < 16, T k <= 64, E <= 64, k <= 16
+    assert f(1, 64, 8, bf, 1, 2048, 1408) == 1
+    assert f(8, 64, 8, bf, 1, 2048, 1408) == 1
+    assert f(15, 8, 4, bf, 1, 128, 128) == 1
+    assert f(16, 8, 2, bf, 1, 128, 128) == 0  # 16 rows
+    assert f(9, 64, 8, bf, 1, 128, 128) == 0  # 72 slots
+    assert f(2, 128, 4, bf, 1, 128, 128) == 0  # E > 64
+    assert f(1, 64, 8, bf, 0, 2048, 1408) == 0  # prefill
+    assert f(1, 64, 8, f32, 1, 2048, 1408) == 0
+    assert f(0, 64, 8, bf, 1, 2048, 1408) == 0
+    ws_need = lib.moe_align_workspace_size(4, 8, 64)
+    M3 = (FAKE, FAKE, FAKE)
+
+    def rag(T=4, mh=M3, probs=FAKE, ids=FAKE, dt=bf, decode=1, hidden=FAKE, w13=FAKE, H=128,
+            I_=128, act=FAKE, ws=FAKE, wsb=None):
+        return lib.moe_route_align_gate_up(FAKE, T, 64, 8, 1, FAKE, FAKE, *mh, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, probs, ids, dt, decode, hidden, w13, H,
+                                           I_, act, ws, ws_need if wsb is None else wsb, None)
+
+    assert rag(mh=(FAKE, None, FAKE)) == I  # all three maps or none
+    assert rag(mh=(None, None, None)) == I  # the inverse needs the maps
+    assert rag(wsb=ws_need - 1) == W
+    assert rag(H=100) == U  # H % 64
+    assert rag(dt=7) == I
+    assert rag(hidden=None) == I
+    assert rag(act=ctypes.c_void_p(0x1008)) == I  # 16-byte alignment
+    assert rag(T=65, wsb=1 << 40) == U  # decode T limit
+    assert b"decode" in lib.moe_last_error()
+
+
 def test_route_grouped_validation(lib):
     I = _lib.MOE_ERR_INVALID_ARG
     G, N = _lib.MOE_GROUP_LIMITED_GREEDY, _lib.MOE_NOAUX_TC

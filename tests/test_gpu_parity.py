@@ -459,6 +459,61 @@ def test_route_align_inverse_matches_separate_calls(T, E, k):
     assert torch.equal(got["probs_indices"].view(torch.int32), got["topk_w"].view(torch.int32))
 
 
+@pytest.mark.parametrize("T,E,k,H,I,inverse,norm", [
+    (1, 64, 8, 2048, 1408, True, True), (1, 8, 2, 128, 128, True, True),
+    (2, 64, 8, 256, 192, True, False), (3, 16, 4, 192, 320, True, True),
+    (8, 64, 8, 128, 256, True, True),  # 64 slots
+    (15, 12, 4, 64, 128, True, True), (7, 60, 6, 128, 64, True, True),
+    (5, 61, 3, 128, 128, False, True),  # E % 4 != 0: no maps
+    (4, 1, 1, 64, 64, False, True), (9, 32, 7, 256, 128, False, False),
+    # the separate calls: 16 rows, more than 64 slots, E > 64
+    (16, 8, 2, 128, 128, True, True), (9, 64, 8, 128, 128, True, True),
+    (2, 128, 4, 128, 128, True, True)])
+def test_route_align_gate_up_matches_separate_calls(T, E, k, H, I, inverse, norm):
+    """moe_route_align_gate_up (one launch for the smallest decode batches:
+    every FC1 block routes and aligns the batch itself) equals
+    moe_route_align(_inverse) + moe_ffn_gate_up bit for bit: every routing
+    output, the conversion back to indices and the activation rows; the
+    activations also meet the oracle bar."""
+    g = np.random.Generator(np.random.PCG64(T * 13 + E * 3 + k + H + I))
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    logits[:, : min(E, 3)] = np.round(logits[:, : min(E, 3)])  # some equal logits
+    x = mi.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    w13 = mi.f32_to_bf16_bits((g.standard_normal((E, 2 * I, H)) / math.sqrt(H)).astype(np.float32))
+    ld, xd, w13d = dev(logits), dev_bf16(x), dev_bf16(w13)
+    fused = moe.moe_route_align_gate_up_fused(T, E, k, moe.MOE_BF16, True, H, I)
+    assert fused == (T < 16 and T * k <= 64 and E <= 64 and k <= 16)
+    print(f"route_align_gate_up T={T} E={E} k={k} H={H} I={I} fused={fused}", flush=True)
+    got, act = moe.moe_route_align_gate_up(ld, k, xd, w13d, norm, decode=True, inverse=inverse,
+                                           act=_nan_filled((T * k, I), torch.bfloat16))
+    if inverse:
+        sep = moe.moe_route_align_inverse(ld, k, norm)
+    else:
+        sep = moe.moe_route_align(ld, k, norm)
+    ref_act = moe.moe_ffn_gate_up(xd, w13d, sep, k, True, act=_nan_filled((T * k, I),
+                                                                          torch.bfloat16))
+    torch.cuda.synchronize()
+    assert set(got) == set(sep)
+    for key in sep:
+        a, b = got[key], sep[key]
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), key
+    rows = int(sep["offsets"][-1])
+    assert torch.equal(act[:rows].view(torch.int16), ref_act[:rows].view(torch.int16))
+    # the whole decode layer on the fused call's routing and activations,
+    # against the oracle
+    w2 = mi.f32_to_bf16_bits((g.standard_normal((E, H, I)) / math.sqrt(I)).astype(np.float32))
+    w2d = dev_bf16(w2)
+    y = moe.moe_ffn_down(act, w2d, got, T, k, True)
+    out = moe.moe_combine(y, got["topk_w"], got["slot_to_sorted"], torch.bfloat16)
+    out32 = moe.moe_combine(y, got["topk_w"], got["slot_to_sorted"], torch.float32)
+    torch.cuda.synchronize()
+    ow, oids = oracle.route(logits, k, norm)
+    np.testing.assert_array_equal(host(got["topk_ids"]), oids)
+    ref = oracle.expert_ffn(x, w13, w2, ow.astype(np.float64), oids, "bf16")
+    assert_bf16_layer(host(out), host(out32), ref)
+
+
 @pytest.mark.parametrize("T,E,k,method", [(16384, 256, 8, "noaux_tc"),
                                           (16384, 160, 6, "group_limited_greedy"),
                                           (1000, 64, 8, "noaux_tc"), (1, 256, 8, "noaux_tc"),
@@ -877,11 +932,17 @@ def _layer_into(bufs, logits, x, w13, w2, k, decode, fused=False):
         out = {"topk_w": bufs["tw"], "topk_ids": bufs["ids"], **bufs["aligned"],
                "multihot": bufs["mh"], "probs_in_multihot": bufs["pim"],
                "position_map": bufs["pos"]}
-        moe.moe_route_align(logits, k, True, with_multihot=True, out=out, workspace=bufs["ws"])
+        if decode:  # with FC1 in the same call (one launch for the smallest batches)
+            moe.moe_route_align_gate_up(logits, k, x, w13, True, decode=True, inverse=False,
+                                        out=out, act=bufs["act"], workspace=bufs["ws"])
+        else:
+            moe.moe_route_align(logits, k, True, with_multihot=True, out=out,
+                                workspace=bufs["ws"])
+            moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
     else:
         moe.moe_route(logits, k, True, bufs["tw"], bufs["ids"])
         moe.moe_align(bufs["ids"], E, bufs["aligned"], bufs["ws"])
-    moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
+        moe.moe_ffn_gate_up(x, w13, bufs["aligned"], k, decode, bufs["act"])
     if fused:  # FC2 + combine in one call (one launch for the smallest decode batches)
         moe.moe_ffn_down_combine(bufs["act"], w2, bufs["tw"], bufs["aligned"], T, k, decode,
                                  bufs["y"], bufs["out"])
