@@ -112,41 +112,62 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // One routing row held by a 16-lane DPP row (g = lane / 16, q = lane % 16):
 // lane q holds the logits v[0..3] of experts 4q .. 4q+3, `avail` marks which
 // of them exist.  Selects the row's top k (value descending, the lower expert
-// id first among equal values) in k rounds: a lane-local best, a 4-step DPP
-// maximum over the row on order-preserving keys, and one ballot (the lowest
-// lane holding the maximum wins).  Returns the weight of slot q (lanes q < k;
-// softmax over the k selected logits if norm, else the full softmax at the
-// selected expert), computed in double and rounded once.  Byte i of slot_of
-// = the round (= slot) that picked local expert i (0xFF if none): the lane
-// that owns an expert writes its id, so no round broadcasts the winner's
-// local index.  Rows with no available expert (past T) select nothing.
+// id first among equal values) in k rounds.  Each lane first sorts its four
+// order-preserving keys (descending, the lower local index first among equal
+// keys; missing experts key 0, last), so its best is always the head of its
+// list; a round is a 4-step DPP maximum of the heads over the row and one
+// ballot (the lowest lane holding the maximum wins, i.e. the lower expert id),
+// and the winning lane pops its head.  Returns the weight of slot q (lanes
+// q < k; softmax over the k selected logits if norm, else the full softmax at
+// the selected expert), computed in double and rounded once.  Byte i of
+// slot_of = the round (= slot) that picked local expert i (0xFF if none): the
+// lane that owns an expert writes its id, so no round broadcasts the winner's
+// local index.  Rows with no available expert (past T) select nothing; a key
+// of 0 is never selected.
 __device__ __forceinline__ float route_row16(const float v[4], uint32_t avail, int k, int norm,
                                              int g, int q, uint32_t &slot_of) {
     const uint32_t valid = avail;
     uint32_t key[4];
+    int idx[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = float_key(v[i]);
+    for (int i = 0; i < 4; ++i) {
+        key[i] = ((avail >> i) & 1u) ? float_key(v[i]) : 0u;
+        idx[i] = i;
+    }
+    // Sorting network on (key descending, index ascending): a total order,
+    // so the result is that order whatever the comparators' sequence.
+    auto cswap = [&](int a, int b) {
+        const bool sw = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
+        const uint32_t ka = key[a], kb = key[b];
+        const int ia = idx[a], ib = idx[b];
+        key[a] = sw ? kb : ka;
+        key[b] = sw ? ka : kb;
+        idx[a] = sw ? ib : ia;
+        idx[b] = sw ? ia : ib;
+    };
+    cswap(0, 1);
+    cswap(2, 3);
+    cswap(0, 2);
+    cswap(1, 3);
+    cswap(1, 2);
 
     uint32_t sel_key = 0, kmax = 0;
     slot_of = 0xFFFFFFFFu;
     for (int r = 0; r < k; ++r) {
-        // Lane-local best; strict > keeps the lowest local slot on ties.
-        uint32_t bk = 0;
-        int bi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (((avail >> i) & 1u) && key[i] > bk) {
-                bk = key[i];
-                bi = i;
-            }
-        }
+        const uint32_t bk = key[0];
         const uint32_t rmax = row16_max_u32(bk);
         const uint64_t cand = __ballot(bk != 0 && bk == rmax);
         const uint32_t mrow = (uint32_t)(cand >> (g * 16)) & 0xFFFFu;
         const int wl = __ffs((int)mrow) - 1;  // -1 only for rows without experts
         if (q == wl) {
-            avail &= ~(1u << bi);
-            slot_of = (slot_of & ~(0xFFu << (8 * bi))) | ((uint32_t)r << (8 * bi));
+            slot_of = (slot_of & ~(0xFFu << (8 * idx[0]))) | ((uint32_t)r << (8 * idx[0]));
+            key[0] = key[1];
+            key[1] = key[2];
+            key[2] = key[3];
+            key[3] = 0u;
+            idx[0] = idx[1];
+            idx[1] = idx[2];
+            idx[2] = idx[3];
         }
         if (q == r) sel_key = rmax;
         if (r == 0) kmax = rmax;
