@@ -332,11 +332,12 @@ moe_status_t moe_route_align_inverse(const float *logits, int64_t T, int32_t E, 
  * moe_route_align.
  *
  * Where moe_route_align_gate_up_fused(T, E, k, dt, decode, H, I) is 1 (bf16
- * decode, T < 16, T k <= 64, E <= 64, k <= 16, and when the multihot maps
- * are given, 16-byte aligned rows of them) the whole call is one launch:
- * every FC1 block routes and aligns the batch in its own shared memory and
- * reads its tokens from there, and one block also writes every routing
- * output; otherwise it is the separate calls' launches.  Every output is
+ * decode, T k <= 16, E <= 64, k <= 16, and when the multihot maps are given,
+ * 16-byte aligned rows of them) the whole call is one launch: every FC1 block
+ * routes and aligns the batch in its own shared memory and reads its tokens
+ * from there, and one block also writes every routing output; otherwise it
+ * is the separate calls' launches.  (Every block routing the whole batch
+ * pays off only while the batch is this small.)  Every output is
  * bit-identical to the separate calls.  Same workspace as moe_route_align.
  */
 moe_status_t moe_route_align_gate_up(

@@ -347,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
         gate_up_rows<MCmax, RT>(hidden, w13, sorted_tok, H, I, e, base, cnt, act);
 }
 
-// Route + align + FC1 in one launch for the smallest decode batches (T < 16,
-// T k <= kWave slots, E <= 64, k <= 16): every block routes the batch's rows
+// Route + align + FC1 in one launch for the smallest decode batches (T k <=
+// kRouteGateUpSlots, E <= 64, k <= 16): every block routes the batch's rows
 // itself (route16_row, the moe_route selection; wave w takes rows 4w .. 4w +
 // 3) and aligns them (align_slots_wave, the moe_align order) in LDS, then
 // runs FC1 for the blockIdx.y-th non-empty expert from the LDS copy of the
@@ -716,8 +716,15 @@ hipError_t launch_decode_down_combine_bf16(const uint16_t *act, const uint16_t *
 }
 
 
+// Every block routes the whole batch, so the redundant routing grows with the
+// blocks (I / 16 x the selected experts) times the rows: measured at E = 64,
+// k = 8, H = 2048, I = 1408 (event-timed, caches flushed) one launch beats the
+// two at T = 1 (23.7 against 26.2 us), ties at T = 2 and loses from T = 3
+// (T = 8: 93.3 against 87.5 us; T = 32: 146 against 118 us).
+constexpr int kRouteGateUpSlots = 16;
+
 bool decode_route_gate_up_fused(int64_t T, int E, int k, int H, int I) {
-    return T >= 1 && T < 16 && T * k <= kWave && E >= 1 && E <= 64 && k >= 1 && k <= 16 &&
+    return T >= 1 && T * k <= kRouteGateUpSlots && E >= 1 && E <= 64 && k >= 1 && k <= 16 &&
            k <= E && H % 64 == 0 && I % kRows == 0;
 }
 

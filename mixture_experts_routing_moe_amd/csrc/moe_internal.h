@@ -517,7 +517,7 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
 // decode_down_combine_fused holds (T k <= 32, I <= 1536, T k I <= 48 Ki
 // elements): the same out as launch_decode_down_bf16 + launch_combine.
 // Route + align (+ the multihot maps and their inverse) + decode FC1 in one
-// launch; eligibility (T < 16, T k <= 64, E <= 64, k <= 16) and launch.
+// launch; eligibility (T k <= 16, E <= 64, k <= 16) and launch.
 bool decode_route_gate_up_fused(int64_t T, int E, int k, int H, int I);
 hipError_t launch_decode_route_gate_up_bf16(
     const float *logits, int64_t T, int E, int k, int norm, float *topk_w, int32_t *topk_ids,

@@ -172,12 +172,12 @@ def test_route_align_gate_up_validation(lib):
     I, W, U = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_WORKSPACE, _lib.MOE_ERR_UNSUPPORTED
     bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
     f = lib.moe_route_align_gate_up_fused
-    # one launch: bf16 decode, T < 16, T k <= 64, E <= 64, k <= 16
+    # one launch: bf16 decode, T k <= 16, E <= 64, k <= 16
     assert f(1, 64, 8, bf, 1, 2048, 1408) == 1
-    assert f(8, 64, 8, bf, 1, 2048, 1408) == 1
-    assert f(15, 8, 4, bf, 1, 128, 128) == 1
-    assert f(16, 8, 2, bf, 1, 128, 128) == 0  # 16 rows
-    assert f(9, 64, 8, bf, 1, 128, 128) == 0  # 72 slots
+    assert f(2, 64, 8, bf, 1, 2048, 1408) == 1
+    assert f(16, 8, 1, bf, 1, 128, 128) == 1
+    assert f(3, 64, 8, bf, 1, 2048, 1408) == 0  # 24 slots
+    assert f(32, 64, 8, bf, 1, 2048, 1408) == 0
     assert f(2, 128, 4, bf, 1, 128, 128) == 0  # E > 64
     assert f(1, 64, 8, bf, 0, 2048, 1408) == 0  # prefill
     assert f(1, 64, 8, f32, 1, 2048, 1408) == 0
