@@ -29,33 +29,19 @@
 namespace moe {
 namespace {
 
-// Waves per block, each a contiguous share of H, and k-steps of 32 per load
-// batch.  Two token chunks (the large batches): 8 waves with batches as large
-// as the registers hold, so that at H = 2048 (E = 64) each wave's share is
-// one batch, one memory round trip (fine-grained router 30.4 -> 28.5 us);
-// one chunk: 4 waves of batches of 4 (8 waves of one batch measured no
-// faster at H = 4096, E = 8).
-template <int MC>
-constexpr int router_waves() {
-    return MC > 1 ? 8 : 4;
-}
-template <int MC, int EB>
-constexpr int router_kb() {
-    return MC > 1 ? (48 / (MC + EB) < 16 ? 48 / (MC + EB) : 16) : 4;
-}
+constexpr int kRouterThreads = 256;
+constexpr int kRouterKB = 4;  // k-steps of 32 per load batch
 
 __device__ __forceinline__ bf16x8 zero_unless(bool keep, bf16x8 v) {
     return keep ? v : bf16x8{};
 }
 
 template <int MC, int EB>
-__global__ __launch_bounds__(router_waves<MC>() * kWave) void router_route_kernel(
+__global__ __launch_bounds__(kRouterThreads) void router_route_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ wg, int64_t T, int H, int E,
     int k, int norm, int do_route, float *__restrict__ logits, float *__restrict__ topk_w,
     int32_t *__restrict__ topk_ids) {
-    constexpr int KB = router_kb<MC, EB>();
-    constexpr int kRouterWaves = router_waves<MC>();
-    __shared__ f32x4 red[kRouterWaves - 1][MC][EB][kWave];
+    __shared__ f32x4 red[3][MC][EB][kWave];
     __shared__ float s_log[MC * 16][EB * 16];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -84,13 +70,13 @@ __global__ __launch_bounds__(router_waves<MC>() * kWave) void router_route_kerne
         for (int eb = 0; eb < EB; ++eb) acc[mc][eb] = f32x4{};
 
     const int ksteps = H / 32;
-    const int per = (ksteps + kRouterWaves - 1) / kRouterWaves;
+    const int per = (ksteps + 3) / 4;
     const int s0 = wave * per;
     const int s1 = min(ksteps, s0 + per);
-    for (int s = s0; s < s1; s += KB) {
-        bf16x8 xa[KB][MC], wa[KB][EB];
+    for (int s = s0; s < s1; s += kRouterKB) {
+        bf16x8 xa[kRouterKB][MC], wa[kRouterKB][EB];
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
+        for (int j = 0; j < kRouterKB; ++j) {
             const int ss = min(s + j, s1 - 1) * 32;
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc)
@@ -101,7 +87,7 @@ __global__ __launch_bounds__(router_waves<MC>() * kWave) void router_route_kerne
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
+        for (int j = 0; j < kRouterKB; ++j) {
             const bool in = s + j < s1;
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb) {
@@ -132,7 +118,7 @@ __global__ __launch_bounds__(router_waves<MC>() * kWave) void router_route_kerne
             for (int eb = 0; eb < EB; ++eb) {
                 f32x4 a = acc[mc][eb];
 #pragma unroll
-                for (int w = 0; w < kRouterWaves - 1; ++w) a += red[w][mc][eb][lane];
+                for (int w = 0; w < 3; ++w) a += red[w][mc][eb][lane];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int el = eb * 16 + kq * 4 + r;
@@ -148,11 +134,9 @@ __global__ __launch_bounds__(router_waves<MC>() * kWave) void router_route_kerne
 
     const int g = lane >> 4;
     const int q = lane & 15;
-    // 4 rows per wave per pass; a wave whose rows are all past the block's
-    // skips the pass as a whole.
-    for (int p = 0; p * kRouterWaves * 4 < MC * 16; ++p) {
-        const int rl = p * kRouterWaves * 4 + wave * 4 + g;
-        if (wave * 4 + p * kRouterWaves * 4 >= MC * 16) break;
+#pragma unroll
+    for (int p = 0; p < MC; ++p) {
+        const int rl = p * 16 + wave * 4 + g;
         const int64_t t = t0 + rl;
         float v[4];
         uint32_t avail = 0;
@@ -185,8 +169,8 @@ hipError_t launch_mc_eb(const uint16_t *hidden, const uint16_t *wg, int64_t T, i
     const int64_t bx = (T + MC * 16 - 1) / (MC * 16);
     const int by = (E + EB * 16 - 1) / (EB * 16);
     hipLaunchKernelGGL((router_route_kernel<MC, EB>), dim3((unsigned)bx, (unsigned)by),
-                       dim3(router_waves<MC>() * kWave), 0, s, hidden, wg, T, H, E, k, norm,
-                       do_route, logits, w, ids);
+                       dim3(kRouterThreads), 0, s, hidden, wg, T, H, E, k, norm, do_route, logits,
+                       w, ids);
     return hipGetLastError();
 }
 
