@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void decode_route_gate_up_kernel(
         s_cnt[lane] = 0;
     }
     __syncthreads();
-    const int t = 4 * wave + g;  // T < 16: one row per 16-lane group
+    const int t = 4 * wave + g;  // T <= 16 (T k <= 16): one row per 16-lane group
     const uint32_t slot_of =
         route16_row(logits, T, t, E, k, norm, vec4, writer ? topk_w : s_w,
                     writer ? topk_ids : s_tid, writer ? multihot : nullptr, pim, pos, g, q);

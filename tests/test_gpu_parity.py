@@ -514,6 +514,26 @@ def test_route_align_gate_up_matches_separate_calls(T, E, k, H, I, inverse, norm
     assert_bf16_layer(host(out), host(out32), ref)
 
 
+def test_route_align_gate_up_empty():
+    """T = 0: zero counts and offsets, nothing else written."""
+    E, k, H, I = 16, 4, 128, 128
+    ld = torch.empty((0, E), dtype=torch.float32, device=DEV)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    w13 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16, device=DEV)
+    out = {"topk_w": torch.empty((0, k), dtype=torch.float32, device=DEV),
+           "topk_ids": torch.empty((0, k), dtype=torch.int32, device=DEV),
+           "counts": torch.full((E,), 7, dtype=torch.int32, device=DEV),
+           "offsets": torch.full((E + 1,), 7, dtype=torch.int32, device=DEV),
+           "sorted_token_ids": torch.empty(0, dtype=torch.int32, device=DEV),
+           "sorted_slot_ids": torch.empty(0, dtype=torch.int32, device=DEV),
+           "slot_to_sorted": torch.empty(0, dtype=torch.int32, device=DEV)}
+    got, act = moe.moe_route_align_gate_up(ld, k, x, w13, True, decode=True, inverse=False,
+                                           out=out)
+    torch.cuda.synchronize()
+    assert act.shape == (0, I)
+    assert int(got["counts"].abs().sum()) == 0 and int(got["offsets"].abs().sum()) == 0
+
+
 @pytest.mark.parametrize("T,E,k,method", [(16384, 256, 8, "noaux_tc"),
                                           (16384, 160, 6, "group_limited_greedy"),
                                           (1000, 64, 8, "noaux_tc"), (1, 256, 8, "noaux_tc"),
