@@ -229,15 +229,16 @@ __device__ __forceinline__ void gate_up_rows(const uint16_t *__restrict__ hidden
 // FC2.  y[p, h] (float32) for h in this block's RT x 16 rows and every
 // position p of expert e's segment, in MC chunks of 16 token columns.  KP
 // pairs per batch: with one row tile, 6 for up to 32 tokens (one batch covers
-// each wave's share of k = 1408), 4 for more; with two row tiles, 3.  Two row
-// tiles per block (used from 16 tokens on) read the expert's activation rows
-// once for 32 weight rows: at T = 32 those rows are otherwise close to half
-// of a block's bytes.
+// each wave's share of k = 1408), 4 for more; with two row tiles 3, with four
+// 2.  Several row tiles per block (from 16 tokens on: four up to 32 tokens,
+// two past that, where four token chunks leave registers for two) read the
+// expert's activation rows once for 64 or 32 weight rows: at T = 32 those
+// rows are otherwise close to half of a block's bytes.
 template <int MC, int RT>
 __device__ __forceinline__ void down_rows(const uint16_t *__restrict__ act,
                                           const uint16_t *__restrict__ w2, int H, int I, int e,
                                           int base, int cnt, float *__restrict__ y) {
-    constexpr int KP = RT == 1 ? (MC <= 2 ? 6 : 4) : 3;
+    constexpr int KP = RT == 1 ? (MC <= 2 ? 6 : 4) : (RT == 2 ? 3 : 2);
     __shared__ f32x4 red[3][RT][MC][kWave];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -780,27 +781,30 @@ hipError_t launch_decode_down_bf16(const uint16_t *act, const uint16_t *w2,
                                    const int32_t *offsets, int64_t T, int H, int I, int E, int k,
                                    float *y, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    // Two row tiles per block once the experts hold enough tokens for their
-    // activation rows to matter (H % 64 == 0, so H / 32 blocks cover H).
-    const bool two = T >= 16;
-    const dim3 grid(H / (kRows * (two ? 2 : 1)), expert_rows(T, E, k));
-    switch (token_chunks(T) * (two ? 10 : 1)) {
-        case 1:
+    // Several row tiles per block once the experts hold enough tokens for
+    // their activation rows to matter: four for 16 to 32 tokens, two past
+    // that (H % 64 == 0, so H / 64 or H / 32 blocks cover H).
+    const int rt = T < 16 ? 1 : (T <= 32 ? 4 : 2);
+    const dim3 grid(H / (kRows * rt), expert_rows(T, E, k));
+    switch (token_chunks(T) * 10 + rt) {
+        case 11:
             hipLaunchKernelGGL((decode_down_kernel<1, 1>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
-        case 10:
-            hipLaunchKernelGGL((decode_down_kernel<1, 2>), grid, dim3(kThreads), 0, s, act, w2,
+        case 14:
+            hipLaunchKernelGGL((decode_down_kernel<1, 4>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
-        case 20:
-            hipLaunchKernelGGL((decode_down_kernel<2, 2>), grid, dim3(kThreads), 0, s, act, w2,
+        case 24:
+            hipLaunchKernelGGL((decode_down_kernel<2, 4>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
-        default:
+        case 42:
             hipLaunchKernelGGL((decode_down_kernel<4, 2>), grid, dim3(kThreads), 0, s, act, w2,
                                offsets, H, I, E, y);
             break;
+        default:
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
