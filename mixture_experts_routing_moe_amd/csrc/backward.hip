@@ -176,7 +176,7 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
 }
 
 // dst[p] = src[tok[p]] (rows of L bf16) for every aligned position p, for
-// two sources at once (x and grad_out).  One block per position.
+// grad_out and, when xs is given, x.  One block per position.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ dy,
                                                           const int32_t *__restrict__ tok,
@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
     if (p >= offsets[E]) return;
     const int64_t t = tok[p];
     for (int c = threadIdx.x; c < L / 8; c += blockDim.x) {
-        *reinterpret_cast<uint4 *>(xs + (int64_t)p * L + 8 * c) =
-            *reinterpret_cast<const uint4 *>(x + t * L + 8 * c);
+        if (xs != nullptr)
+            *reinterpret_cast<uint4 *>(xs + (int64_t)p * L + 8 * c) =
+                *reinterpret_cast<const uint4 *>(x + t * L + 8 * c);
         *reinterpret_cast<uint4 *>(dys + (int64_t)p * L + 8 * c) =
             *reinterpret_cast<const uint4 *>(dy + t * L + 8 * c);
     }
@@ -209,10 +210,13 @@ __global__ void seg_offsets_kernel(const int32_t *__restrict__ offsets, int E,
 }
 
 // For each padded position q < nq: the aligned position it holds, or -1 for
-// padding (and for q past the last segment).
+// padding (and for q past the last segment), and that position's token (-1
+// likewise).
 __global__ __launch_bounds__(256) void seg_src_kernel(const int32_t *__restrict__ offsets,
-                                                      const int32_t *__restrict__ poff, int E,
-                                                      int nq, int32_t *__restrict__ src) {
+                                                      const int32_t *__restrict__ poff,
+                                                      const int32_t *__restrict__ sorted_tok,
+                                                      int E, int nq, int32_t *__restrict__ src,
+                                                      int32_t *__restrict__ tsrc) {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nq) return;
     int r = -1;
@@ -227,6 +231,7 @@ __global__ __launch_bounds__(256) void seg_src_kernel(const int32_t *__restrict_
         if (local < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + local;
     }
     src[q] = r;
+    tsrc[q] = r >= 0 ? sorted_tok[r] : -1;
 }
 
 // Batched bf16 transpose through LDS: for batch b = blockIdx.y / (L / 64),
@@ -627,6 +632,14 @@ bool fused_act(int64_t T, int H, int I) {
     return gate_up_bwd_ok(T, H, I);
 }
 
+// With K-major weights and the fused SiLU-and-mul backward, no product reads
+// x or grad_out in the aligned order: G reads grad_out through sorted_tok and
+// the transposes read both through each padded position's token, so nothing
+// is gathered.
+bool direct_rows(int64_t T, int H, int I, int k) {
+    return kmajor_weights(T, H, I, k) && fused_act(T, H, I);
+}
+
 size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
     const size_t P = (size_t)T * (size_t)k;
     const size_t Pp = (size_t)padded_positions(T, E, k);
@@ -639,8 +652,12 @@ size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
         case 2: b = P * I * 2; break;                   // wact   bf16 [P, I]
         case 3: b = P * 2 * I * 2; break;               // dh13   bf16 [P, 2I]
         case 4: b = P * H * 4; break;                   // dxs    f32  [P, H]
-        case 5: b = P * H * 2; break;                   // xs     bf16 [P, H]
-        case 6: b = P * H * 2; break;                   // dys    bf16 [P, H]
+        case 5:  // xs bf16 [P, H], only for the separate gate/up path
+            b = fused_act(T, H, I) ? 0 : P * H * 2;
+            break;
+        case 6:  // dys bf16 [P, H], unless the rows are read in place
+            b = direct_rows(T, H, I, k) ? 0 : P * H * 2;
+            break;
         case 7:  // w13t bf16 [E, H, 2I], only on the transposing path
             b = kmajor_weights(T, H, I, k) ? 0 : (size_t)E * 2 * I * H * 2;
             break;
@@ -657,10 +674,11 @@ size_t part_bytes(int64_t T, int H, int I, int E, int k, int part) {
         case 12: b = (size_t)H * Pp * 2; break;         // xT     bf16 [H, Pp]
         case 13: b = (size_t)(E + 1) * 4; break;        // poff   int32 [E+1]
         case 14: b = Pp * 4; break;                     // src    int32 [Pp]
+        case 15: b = Pp * 4; break;                     // tsrc   int32 [Pp]
     }
     return (b + 255) / 256 * 256;
 }
-constexpr int kParts = 15;
+constexpr int kParts = 16;
 
 hipError_t transpose(const uint16_t *in, int64_t ld_in, int64_t in_bs, const int32_t *src,
                      int nq, int L, uint16_t *out, int64_t ld_out, int64_t out_bs, int batch,
@@ -721,17 +739,24 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
     uint16_t *xT = reinterpret_cast<uint16_t *>(part[12]);
     int32_t *poff = reinterpret_cast<int32_t *>(part[13]);
     int32_t *src = reinterpret_cast<int32_t *>(part[14]);
+    int32_t *tsrc = reinterpret_cast<int32_t *>(part[15]);
+    const bool fused = fused_act(T, H, I);
+    const bool direct = direct_rows(T, H, I, k);
     hipError_t err;
 #define MOE_TRY(x)                                   \
     do {                                             \
         if ((err = (x)) != hipSuccess) return err;   \
     } while (0)
 
-    // Layout preparation: gathered rows, per-expert transposed weights, the
-    // padded segment map.
-    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)P), dim3(256), 0, s, x, dy, sorted_tok,
-                       offsets, E, H, xs, dys);
-    MOE_TRY(hipGetLastError());
+    // Layout preparation: gathered rows where a product reads them in the
+    // aligned order (grad_out for G on the transposed-weight path, x for the
+    // separate gate/up path), per-expert transposed weights, the padded
+    // segment map.
+    if (!direct) {
+        hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)P), dim3(256), 0, s, x, dy,
+                           sorted_tok, offsets, E, H, fused ? nullptr : xs, dys);
+        MOE_TRY(hipGetLastError());
+    }
     const bool km = kmajor_weights(T, H, I, k);
     if (!km) {
         MOE_TRY(transpose(w13, H, (int64_t)2 * I * H, nullptr, 2 * I, H, w13t, 2 * I,
@@ -741,14 +766,14 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
     hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, E, poff);
     MOE_TRY(hipGetLastError());
     hipLaunchKernelGGL(seg_src_kernel, dim3((unsigned)((Pp + 255) / 256)), dim3(256), 0, s,
-                       offsets, poff, E, Pp, src);
+                       offsets, poff, sorted_tok, E, Pp, src, tsrc);
     MOE_TRY(hipGetLastError());
 
     // Row-segment products on the forward's grouped kernel: G (FC2 form),
     // then gate/up recomputed (FC1 form) with the SiLU-and-mul backward in
     // its epilogue, or (FC2 form) stored for bwd_act_kernel.
-    const bool fused = fused_act(T, H, I);
-    MOE_TRY(km ? launch_down_kmajor_bf16(dys, w2, offsets, T, I, H, E, k, G, s)   // G
+    MOE_TRY(km ? (direct ? launch_down_kmajor_bf16(dy, sorted_tok, w2, offsets, T, I, H, E, k, G, s)
+                         : launch_down_kmajor_bf16(dys, nullptr, w2, offsets, T, I, H, E, k, G, s))  // G
                : launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));
     if (fused) {
         MOE_TRY(launch_gate_up_bwd_bf16(x, w13, offsets, sorted_tok, sorted_slot, topk_w, G, T, H,
@@ -759,15 +784,19 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
                            offsets, sorted_slot, E, I, wact, dh13, dw);
         MOE_TRY(hipGetLastError());
     }
-    MOE_TRY(km ? launch_down_kmajor_bf16(dh13, w13, offsets, T, H, 2 * I, E, k, dxs, s)
+    MOE_TRY(km ? launch_down_kmajor_bf16(dh13, nullptr, w13, offsets, T, H, 2 * I, E, k, dxs, s)
                : launch_down_bf16(dh13, w13t, offsets, T, H, 2 * I, E, k, 1, dxs, s));  // d_hidden
     hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)T), dim3(256), 0, s, dxs, slot_to_sorted, k,
                        H, dx, dw, fused ? gw_part : nullptr, gate_up_bwd_tiles(I));
     MOE_TRY(hipGetLastError());
 
     // Weight gradients over the padded, transposed segments of dy and x.
-    MOE_TRY(transpose(dys, H, 0, src, Pp, H, dyT, Pp, 0, 1, s));
-    MOE_TRY(transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
+    MOE_TRY(direct ? transpose(dy, H, 0, tsrc, Pp, H, dyT, Pp, 0, 1, s)
+                   : transpose(dys, H, 0, src, Pp, H, dyT, Pp, 0, 1, s));
+    // x^T straight from x through each padded position's token where x was
+    // not gathered.
+    MOE_TRY(fused ? transpose(x, H, 0, tsrc, Pp, H, xT, Pp, 0, 1, s)
+                  : transpose(xs, H, 0, src, Pp, H, xT, Pp, 0, 1, s));
     if (kmajor_wgrad(T, H, I, E, k)) {
         // dw2[e] [H, I]: dy^T (w act); dw13[e] [2I, H]: ([d_gate ; d_up]^T x),
         // computed as x^T [d_gate ; d_up] and stored transposed.

@@ -781,6 +781,8 @@ __device__ __forceinline__ void run_tile(uint16_t *smem, const OpsT &op, int nk,
 // kKm (FC2 form, buffer addressing only): W is K-major, [E, K, N].
 // kBwd (FC1 form): the epilogue applies the SiLU-and-mul backward (BwdAct)
 // instead of writing act.  kStream (FC2 form): y is stored non-temporally.
+// With kKm, a non-null `gather` makes A one row per token, position p
+// reading row gather[p] as the FC1 form does.
 template <bool kGateUp, bool kBuf, bool kKm = false, bool kBwd = false, bool kStream = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ gather,
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         const int r = wv * kTokRowsPerWave + i * kRowsPerLoad + rr;
         const int c8 = ((lane % kChunks) ^ swz(r)) * 8;
         const int p = min(tile.row0 + r, tile.row_end - 1);
-        const int arow = kGateUp ? gather[p] : p;
+        const int arow = (kGateUp || (kKm && gather != nullptr)) ? gather[p] : p;
         if constexpr (kBuf)
             op.aoff[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)c8) * 2u;
         else
@@ -1162,19 +1164,19 @@ bool down_kmajor_ok(int64_t T, int N, int K, int k) {
     return use_buffer_path(a_bytes, w_bytes);
 }
 
-hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const int32_t *offsets,
-                                   int64_t T, int N, int K, int E, int k, float *y,
-                                   hipStream_t s) {
+hipError_t launch_down_kmajor_bf16(const uint16_t *a, const int32_t *gather, const uint16_t *w,
+                                   const int32_t *offsets, int64_t T, int N, int K, int E, int k,
+                                   float *y, hipStream_t s) {
     const int64_t rows = T * k;
     if (rows == 0) return hipSuccess;
     if (!down_kmajor_ok(T, N, K, k)) return hipErrorInvalidValue;
     const int m_slots = m_slot_bound(rows, E);
     const int n_tiles = (N + BN - 1) / BN;
-    const int64_t a_bytes = rows * K * 2;
     const dim3 grid(grid_of(m_slots, n_tiles));
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true, false, true>), grid, dim3(kThreads), 0, s,
-                       a, nullptr, w, offsets, y, E, K, N, n_tiles, 1, rows * N, (int)a_bytes,
-                       BwdAct{});
+    const int64_t a_bytes = (gather != nullptr ? T : rows) * K * 2;
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true, true, false, true>), grid,
+                       dim3(kThreads), 0, s, a, gather, w, offsets, y, E, K, N, n_tiles, 1,
+                       rows * N, (int)a_bytes, BwdAct{});
     return hipGetLastError();
 }
 

@@ -476,12 +476,13 @@ hipError_t launch_gate_up_bwd_bf16(const uint16_t *hidden, const uint16_t *w13,
                                    uint16_t *wact, uint16_t *dh13, float *gw_part,
                                    hipStream_t s);
 // The FC2-form grouped product with a K-major weight w [E, K, N] (N
-// contiguous): y[p, n] = sum_k a[p, k] w[e, k, n] for the rows p of expert e,
-// float32 [T k, N].  Needs buffer addressing (down_kmajor_ok).
+// contiguous): y[p, n] = sum_k a[row(p), k] w[e, k, n] for the rows p of
+// expert e, float32 [T k, N], with row(p) = p (a [T k, K]) or, given
+// `gather`, gather[p] (a [T, K]).  Needs buffer addressing (down_kmajor_ok).
 bool down_kmajor_ok(int64_t T, int N, int K, int k);
-hipError_t launch_down_kmajor_bf16(const uint16_t *a, const uint16_t *w, const int32_t *offsets,
-                                   int64_t T, int N, int K, int E, int k, float *y,
-                                   hipStream_t s);
+hipError_t launch_down_kmajor_bf16(const uint16_t *a, const int32_t *gather, const uint16_t *w,
+                                   const int32_t *offsets, int64_t T, int N, int K, int E, int k,
+                                   float *y, hipStream_t s);
 // Weight gradients C_e [M, N] f32 = sum over k in [poff[e], poff[e+1]) of
 // a[m, k] b[n, k] (a [M, ld], b [N, ld] bf16, segments padded to whole
 // 64-wide k-tiles) on the grouped kernel's machinery; needs buffer
