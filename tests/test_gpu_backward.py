@@ -168,9 +168,11 @@ def test_ffn_backward_f32(T, H, I, E, k, inv):
                                                 (90, 320, 64, 3, 3, 0.0, 0.0)])
 def test_ffn_backward_kmajor_weights(monkeypatch, T, H, I, E, k, skew, inv):
     """G = dy . w2 and d_hidden = [d_gate ; d_up] . w13 read w2 and w13 as
-    stored (the grouped kernel transposes in its LDS reads): the same products,
-    term for term and in the same order, as the path that first copies the
-    weights transposed, so every gradient is bit-identical to it."""
+    stored (the grouped kernel transposes in its LDS reads) and G reads
+    grad_out's rows in place through the token ids: the same products, term
+    for term and in the same order, as the path that first copies the weights
+    transposed and gathers grad_out, so every gradient is bit-identical to
+    it."""
     x, w13, w2, w32, ids, dy = _rand_case(T * 3 + I, T, H, I, E, k, skew, inv)
     print(f"kmajor backward T={T} H={H} I={I} E={E} k={k}", flush=True)
     got = _bwd_gpu(x, w13, w2, w32, ids, dy)
@@ -212,10 +214,11 @@ def test_ffn_backward_kmajor_wgrad(monkeypatch, T, H, I, E, k, skew, inv):
 def test_ffn_backward_fused_act(monkeypatch, T, H, I, E, k, skew, inv):
     """The SiLU-and-mul backward in the gate/up recompute's epilogue (the FC1
     kernel's accumulators, the same products in the same k order as the FC2
-    form that stores gate/up for bwd_act_kernel): gradients of hidden, w13 and
-    w2 bit-identical to the separate path; the routing-weight gradient is the
-    same sum over a row's columns in another order (per column tile, then the
-    tiles in order)."""
+    form that stores gate/up for bwd_act_kernel, and x^T transposed from x
+    through each padded position's token rather than from a gathered copy):
+    gradients of hidden, w13 and w2 bit-identical to the separate path; the
+    routing-weight gradient is the same sum over a row's columns in another
+    order (per column tile, then the tiles in order)."""
     x, w13, w2, w32, ids, dy = _rand_case(T * 11 + I, T, H, I, E, k, skew, inv)
     print(f"fused act backward T={T} H={H} I={I} E={E} k={k}", flush=True)
     got = _bwd_gpu(x, w13, w2, w32, ids, dy)
