@@ -769,12 +769,16 @@ hipError_t launch_ffn_backward_bf16(const uint16_t *x, const uint16_t *w13, cons
                        offsets, poff, sorted_tok, E, Pp, src, tsrc);
     MOE_TRY(hipGetLastError());
 
-    // Row-segment products on the forward's grouped kernel: G (FC2 form),
-    // then gate/up recomputed (FC1 form) with the SiLU-and-mul backward in
-    // its epilogue, or (FC2 form) stored for bwd_act_kernel.
-    MOE_TRY(km ? (direct ? launch_down_kmajor_bf16(dy, sorted_tok, w2, offsets, T, I, H, E, k, G, s)
-                         : launch_down_kmajor_bf16(dys, nullptr, w2, offsets, T, I, H, E, k, G, s))  // G
-               : launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));
+    // Row-segment products on the forward's grouped kernel: G (FC2 form;
+    // grad_out's rows read in place through the token ids where nothing was
+    // gathered), then gate/up recomputed (FC1 form) with the SiLU-and-mul
+    // backward in its epilogue, or (FC2 form) stored for bwd_act_kernel.
+    if (!km)
+        MOE_TRY(launch_down_bf16(dys, w2t, offsets, T, I, H, E, k, 1, G, s));
+    else if (direct)
+        MOE_TRY(launch_down_kmajor_bf16(dy, sorted_tok, w2, offsets, T, I, H, E, k, G, s));
+    else
+        MOE_TRY(launch_down_kmajor_bf16(dys, nullptr, w2, offsets, T, I, H, E, k, G, s));
     if (fused) {
         MOE_TRY(launch_gate_up_bwd_bf16(x, w13, offsets, sorted_tok, sorted_slot, topk_w, G, T, H,
                                         I, E, k, wact, dh13, gw_part, s));
