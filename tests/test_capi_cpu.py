@@ -402,6 +402,32 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in msg["error"]
 
 
+def test_traffic_records_match_their_sources():
+    """Every committed HBM-traffic record (profiles/traffic_*.json: the
+    copy-calibrated FETCH_SIZE / WRITE_SIZE counter runs that bench.py reports
+    as roofline.traffic) holds the hash of the kernel sources it was taken on.
+    bench.py reports null for a record whose sources changed since, so none
+    may be stale; each names one of bench.py's kernel source sets, positive
+    bytes, its calibration and the commands that made it."""
+    import glob
+    import json
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")))
+    assert paths
+    for path in paths:
+        with open(path) as f:
+            rec = json.load(f)
+        assert rec["source"] in list(bench.KERNEL_SRC.values()), path
+        assert rec["source_sha256_16"] == bench.source_hash(rec["source"]), f"stale: {path}"
+        assert rec["hbm_bytes_per_launch"] > 0 and rec["algorithmic_bytes_per_launch"] > 0, path
+        cal = rec["copy_calibration"]
+        assert cal["fetch_factor"] > 0 and cal["write_factor"] > 0, path
+        assert any("FETCH_SIZE" in c for c in rec["commands"]), path
+        assert any("WRITE_SIZE" in c for c in rec["commands"]), path
+
+
 def test_route_backward_validation(lib):
     I = _lib.MOE_ERR_INVALID_ARG
 
